@@ -1,0 +1,248 @@
+"""Python access to the plain CPU oracle (``oracle.cpp``).
+
+TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The HIP library
+never calls it, and it never calls the HIP library.
+
+Arrays here are numpy, lane-major: u0 [n, d], p [n, P], h [n, max_steps],
+save_idx [n, S], y_save [n, S, d] with S = max(1, len(save_times)).  The
+dtype of ``u0`` (float64 or float32) selects the precision.  ``fused=True``
+evaluates every multiply-add as one correctly rounded fma; ``fused=False``
+rounds each multiply and add separately.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# status codes of a lane
+LANE_OK, LANE_MAX_STEPS, LANE_DT_UNDERFLOW, LANE_NONFINITE, LANE_MAX_ATTEMPTS = range(5)
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.cpp into liboracle.so (g++, -O2, no fp contraction, OpenMP)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+               "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("rhs", ctypes.c_int32), ("dim", ctypes.c_int32), ("n_params", ctypes.c_int32),
+        ("method", ctypes.c_int32),
+        ("t0", ctypes.c_double), ("t1", ctypes.c_double), ("rtol", ctypes.c_double),
+        ("atol", ctypes.c_double), ("dt0", ctypes.c_double),
+        ("max_steps", ctypes.c_int32), ("max_attempts", ctypes.c_int32),
+        ("n_save", ctypes.c_int32), ("save_times", ctypes.POINTER(ctypes.c_double)),
+        ("safety", ctypes.c_double), ("fac_min", ctypes.c_double), ("fac_max", ctypes.c_double),
+    ]
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB)
+        _lib.orc_ros2_gamma.restype = ctypes.c_double
+    return _lib
+
+
+def _swap_library(path: Optional[str]):
+    """Point this module at another build of oracle.cpp (None restores the
+    default).  Used by the test that plants mistakes in copies of the source."""
+    global _lib
+    _lib = None
+    if path is not None:
+        _lib = ctypes.CDLL(path)
+        _lib.orc_ros2_gamma.restype = ctypes.c_double
+
+
+def _cprob(prob):
+    st = np.ascontiguousarray(np.asarray(prob.save_times, dtype=np.float64))
+    P = _Problem(prob.rhs, prob.dim, prob.n_params, prob.method, prob.t0, prob.t1, prob.rtol,
+                 prob.atol, prob.dt0, prob.max_steps, prob.max_attempts, len(prob.save_times),
+                 st.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if len(st) else None,
+                 prob.safety, prob.fac_min, prob.fac_max)
+    return P, st  # keep st alive
+
+
+def _ptr(a):
+    return None if a is None else ctypes.c_void_p(a.ctypes.data)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"oracle {what} failed with code {rc}")
+
+
+def _sfx(dt):
+    if dt == np.float64:
+        return "f64"
+    if dt == np.float32:
+        return "f32"
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def max_threads(nthreads: int = 0) -> int:
+    return _load().orc_max_threads(ctypes.c_int(nthreads))
+
+
+def ros2_gamma() -> float:
+    return _load().orc_ros2_gamma()
+
+
+def tableau(method: int) -> dict:
+    """Tableau of Tsit5 (0) or Dopri5 (1): c[7], a[7,7], b[7], e = b - bhat."""
+    c = np.zeros(7); a = np.zeros((7, 7)); b = np.zeros(7); e = np.zeros(7)
+    info = np.zeros(2, dtype=np.int32)
+    _check(_load().orc_tableau(method, _ptr(c), _ptr(a), _ptr(b), _ptr(e), _ptr(info)),
+           "tableau")
+    return {"c": c, "a": a, "b": b, "e": e, "order": int(info[0]), "err_order": int(info[1])}
+
+
+def record(prob, u0, p, fused: bool = False, nthreads: int = 0, with_h: bool = True) -> dict:
+    """Adaptive solve per lane; returns the mesh and saved states."""
+    u0 = np.ascontiguousarray(u0)
+    dt = u0.dtype.type
+    p = np.ascontiguousarray(p, dtype=dt)
+    n = u0.shape[0]
+    S = prob.n_save_eff
+    h = np.zeros((n, prob.max_steps), dtype=dt) if with_h else None
+    ns = np.zeros(n, dtype=np.int32)
+    sidx = np.zeros((n, S), dtype=np.int32)
+    status = np.zeros(n, dtype=np.int32)
+    ysave = np.zeros((n, S, prob.dim), dtype=dt)
+    natt = np.zeros(n, dtype=np.int32)
+    P, keep = _cprob(prob)
+    fn = getattr(_load(), "orc_record_" + _sfx(dt))
+    _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(status), _ptr(ysave), _ptr(natt),
+              ctypes.c_int32(nthreads)), "record")
+    return {"h": h, "n_steps": ns, "save_idx": sidx, "status": status, "y_save": ysave,
+            "n_attempts": natt}
+
+
+def replay(prob, u0, p, mesh, fused: bool = False, nthreads: int = 0):
+    """Fixed-step replay of ``mesh``; returns (y_save [n,S,d], y_final [n,d])."""
+    u0 = np.ascontiguousarray(u0)
+    dt = u0.dtype.type
+    p = np.ascontiguousarray(p, dtype=dt)
+    n = u0.shape[0]
+    S = prob.n_save_eff
+    h = np.ascontiguousarray(mesh["h"], dtype=dt)
+    ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
+    sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    ysave = np.zeros((n, S, prob.dim), dtype=dt)
+    yfin = np.zeros((n, prob.dim), dtype=dt)
+    P, keep = _cprob(prob)
+    fn = getattr(_load(), "orc_replay_" + _sfx(dt))
+    _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(ysave), _ptr(yfin), ctypes.c_int32(nthreads)),
+           "replay")
+    return ysave, yfin
+
+
+def replay_grad(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray] = None,
+                scale: float = 1.0, fused: bool = False, nthreads: int = 0):
+    """Replay + exact discrete adjoint; returns (loss [n], grad_u0 [n,d], grad_p [n,P]).
+
+    ``aux`` is [n, S, d]: targets (MSE_SAVE) or cotangents (COTANGENT)."""
+    u0 = np.ascontiguousarray(u0)
+    dt = u0.dtype.type
+    p = np.ascontiguousarray(p, dtype=dt)
+    n = u0.shape[0]
+    h = np.ascontiguousarray(mesh["h"], dtype=dt)
+    ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
+    sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    status = np.ascontiguousarray(mesh["status"], dtype=np.int32)
+    ax = None if aux is None else np.ascontiguousarray(aux, dtype=dt)
+    loss = np.zeros(n, dtype=dt)
+    gu0 = np.zeros((n, prob.dim), dtype=dt)
+    gp = np.zeros((n, prob.n_params), dtype=dt)
+    P, keep = _cprob(prob)
+    fn = getattr(_load(), "orc_replay_grad_" + _sfx(dt))
+    _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(status), ctypes.c_int32(loss_kind), _ptr(ax),
+              ctypes.c_double(scale), _ptr(loss), _ptr(gu0), _ptr(gp), ctypes.c_int32(nthreads)),
+           "replay_grad")
+    return loss, gu0, gp
+
+
+def replay_jvp(prob, u0, p, du0, dp, mesh, loss_kind: int = 0,
+               aux: Optional[np.ndarray] = None, scale: float = 1.0):
+    """Forward-mode (dual number) derivative of the replayed loss along (du0, dp).
+
+    Returns (loss [n], dloss [n], y_save [n,S,d], dy_save [n,S,d]); float64 only."""
+    u0 = np.ascontiguousarray(u0, dtype=np.float64)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    du0 = np.ascontiguousarray(du0, dtype=np.float64)
+    dp = np.ascontiguousarray(dp, dtype=np.float64)
+    n = u0.shape[0]
+    S = prob.n_save_eff
+    h = np.ascontiguousarray(mesh["h"], dtype=np.float64)
+    ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
+    sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    ax = None if aux is None else np.ascontiguousarray(aux, dtype=np.float64)
+    loss = np.zeros(n); dloss = np.zeros(n)
+    ys = np.zeros((n, S, prob.dim)); dys = np.zeros((n, S, prob.dim))
+    P, keep = _cprob(prob)
+    _check(_load().orc_replay_jvp_f64(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p),
+                                      _ptr(du0), _ptr(dp), _ptr(h), _ptr(ns), _ptr(sidx),
+                                      ctypes.c_int32(loss_kind), _ptr(ax), ctypes.c_double(scale),
+                                      _ptr(loss), _ptr(dloss), _ptr(ys), _ptr(dys)), "replay_jvp")
+    return loss, dloss, ys, dys
+
+
+def mesh_max_err(prob, u0, p, mesh, fused: bool = False, nthreads: int = 0):
+    """Largest embedded error norm E over the steps of ``mesh``, per lane."""
+    u0 = np.ascontiguousarray(u0)
+    dt = u0.dtype.type
+    p = np.ascontiguousarray(p, dtype=dt)
+    n = u0.shape[0]
+    h = np.ascontiguousarray(mesh["h"], dtype=dt)
+    ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
+    out = np.zeros(n, dtype=dt)
+    P, keep = _cprob(prob)
+    fn = getattr(_load(), "orc_mesh_max_err_" + _sfx(dt))
+    _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
+              _ptr(h), _ptr(ns), _ptr(out), ctypes.c_int32(nthreads)), "mesh_max_err")
+    return out
+
+
+def initial_step(prob, y0, p) -> float:
+    y0 = np.ascontiguousarray(y0, dtype=np.float64)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    h0 = np.zeros(1)
+    P, keep = _cprob(prob)
+    _check(_load().orc_initial_step_f64(ctypes.byref(P), _ptr(y0), _ptr(p), _ptr(h0)),
+           "initial_step")
+    return float(h0[0])
+
+
+def rhs(kind: int, y, p, v):
+    """f(y), J(y)^T v, J_p(y)^T v and (d <= 3) the Jacobian, float64."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    d = y.shape[0]
+    f = np.zeros(d); wy = np.zeros(d); gp = np.zeros(p.shape[0]); J = np.zeros(d * d)
+    _check(_load().orc_rhs_f64(ctypes.c_int32(kind), ctypes.c_int32(d), _ptr(y), _ptr(p),
+                               _ptr(v), _ptr(f), _ptr(wy), _ptr(gp),
+                               _ptr(J) if d <= 3 else None), "rhs")
+    return f, wy, gp, J.reshape(d, d) if d <= 3 else None

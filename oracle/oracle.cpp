@@ -1,0 +1,1209 @@
+/*
+ * Plain CPU oracle for the record-and-replay discrete adjoint of ODE ensembles.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+ * benchmark's CPU-baseline leg are the only users of this library.  It shares
+ * no code, header, table or constant with the HIP library: every tableau,
+ * right-hand side, controller rule, replay and adjoint below is written here
+ * from the method's definition, one lane at a time, in plain loops.
+ *
+ * What it computes (pages, by title and section):
+ *  - "GRADSOLVE: fast exact gradients for ODE ensembles on GPUs"
+ *    (gptget.net summary), Methodology: an adaptive solve per trajectory
+ *    records the accepted step sizes; the gradient is taken through a
+ *    fixed-step replay of those steps.  Abstract: explicit and Rosenbrock
+ *    integrators; the result is the exact discrete adjoint of the replay.
+ *  - same paper, evolve.pub review, Summary: the record is a zero-padded,
+ *    fixed-length step mesh per trajectory; the replay is a branch-free chain
+ *    and its reverse sweep gives the discrete adjoint.  Strengths (paper
+ *    section 3.1) and FAQ "Is gradsolve's gradient really exact?": the mesh is
+ *    held fixed (stop-gradient); no derivative of the step-size choices.
+ *  - "Using GPU-accelerated Ensembles with Automatic Differentiation"
+ *    (DiffEqGPU docs): the Lorenz right-hand side and parameter order
+ *    (forward-mode example); per-trajectory parameters; the Enzyme example
+ *    (fixed-step Tsit5 gradient of a final-state sum) used as a test pin.
+ * Not from the pages (published methods, restated here):
+ *  - Tsit5 tableau: Ch. Tsitouras, Comput. Math. Appl. 62 (2011) 770-775.
+ *  - Dopri5 tableau: J. R. Dormand, P. J. Prince, J. Comput. Appl. Math. 6
+ *    (1980) 19-26.
+ *  - ROS2: J. G. Verwer, E. J. Spee, J. G. Blom, W. Hundsdorfer, SIAM J. Sci.
+ *    Comput. 20 (1999) 1456-1480, with gamma = 1 + 1/sqrt(2).
+ *  - Starting step: Hairer, Norsett, Wanner, Solving ODEs I, section II.4.
+ *
+ * Rounding modes.  Every sum of products is evaluated left to right as a
+ * chain "first product, then multiply-add".  With fused = 0 each multiply and
+ * add rounds separately (built with -ffp-contract=off); with fused = 1 each
+ * multiply-add is one correctly rounded fma().  Nothing else changes between
+ * the two modes.
+ *
+ * Layout here is lane-major: u0[n][d], p[n][P], h[n][max_steps],
+ * save_idx[n][S], y_save[n][S][d] with S = max(1, n_save).
+ */
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <limits>
+#include <omp.h>
+
+namespace {
+
+constexpr int MAXD = 64;  // largest state dimension handled
+constexpr int MAXP = 3;   // largest parameter count
+
+enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2 };
+enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3 };
+enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
+       S_MAX_ATTEMPTS = 4 };
+enum { L_SUMSQ_FINAL = 0, L_MSE_SAVE = 1, L_COTANGENT = 2 };
+enum { E_OK = 0, E_INVAL = -1, E_UNSUPPORTED = -2 };
+
+}  // namespace
+
+extern "C" {
+/* Problem description (the oracle's own struct). */
+typedef struct {
+  int32_t rhs, dim, n_params, method;
+  double t0, t1, rtol, atol, dt0;
+  int32_t max_steps, max_attempts;
+  int32_t n_save;
+  const double *save_times; /* host, strictly increasing in (t0, t1] */
+  double safety, fac_min, fac_max;
+} orc_problem;
+}
+
+namespace {
+
+/* ------------------------------------------------------------------ */
+/* Scalars                                                             */
+/* ------------------------------------------------------------------ */
+
+/* Forward-mode dual number (value, one tangent) for the JVP check. */
+struct Dual {
+  double v, d;
+  Dual() : v(0), d(0) {}
+  Dual(double x) : v(x), d(0) {}
+  Dual(double x, double dx) : v(x), d(dx) {}
+};
+inline Dual operator+(Dual a, Dual b) { return Dual(a.v + b.v, a.d + b.d); }
+inline Dual operator-(Dual a, Dual b) { return Dual(a.v - b.v, a.d - b.d); }
+inline Dual operator-(Dual a) { return Dual(-a.v, -a.d); }
+inline Dual operator*(Dual a, Dual b) { return Dual(a.v * b.v, a.d * b.v + a.v * b.d); }
+inline Dual operator/(Dual a, Dual b) {
+  return Dual(a.v / b.v, (a.d * b.v - a.v * b.d) / (b.v * b.v));
+}
+inline bool fin(Dual a) { return std::isfinite(a.v); }
+inline bool fin(double a) { return std::isfinite(a); }
+inline bool fin(float a) { return std::isfinite(a); }
+inline double val(Dual a) { return a.v; }
+inline double val(double a) { return a; }
+inline double val(float a) { return a; }
+inline double absval(double a) { return std::fabs(a); }
+inline float absval(float a) { return std::fabs(a); }
+inline Dual absval(Dual a) { return a.v < 0 ? -a : a; }
+
+/* The one multiply-add of this file: a*b + c. */
+template <bool F> inline double mac(double a, double b, double c) {
+  return F ? std::fma(a, b, c) : a * b + c;
+}
+template <bool F> inline float mac(float a, float b, float c) {
+  return F ? std::fma(a, b, c) : a * b + c;
+}
+template <bool F> inline Dual mac(Dual a, Dual b, Dual c) { return a * b + c; }
+
+/* Chain sum_k coef[k]*x[k] over nonzero coefficients: first a product, then
+ * multiply-adds.  Returns 0 when every coefficient is zero. */
+template <class T, bool F>
+inline T chain(int m, const double *coef, const T *const *x, int c) {
+  T acc = T(0.0);
+  bool first = true;
+  for (int k = 0; k < m; ++k) {
+    if (coef[k] == 0.0) continue;
+    if (first) { acc = T(coef[k]) * x[k][c]; first = false; }
+    else acc = mac<F>(T(coef[k]), x[k][c], acc);
+  }
+  return acc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Tableaux (explicit, 7 stages, first-same-as-last)                   */
+/* ------------------------------------------------------------------ */
+
+struct Tableau {
+  double c[7];
+  double a[7][7];  /* a[i][j], j < i; row 6 equals b */
+  double b[7];     /* 5th-order weights, b[6] = 0 */
+  double e[7];     /* error weights b - bhat (4th-order embedded) */
+  int order;       /* order of the propagated solution */
+  int err_order;   /* order of the embedded solution */
+};
+
+Tableau make_tsit5() {
+  /* Tsitouras (2011), decimal coefficients as published. */
+  Tableau t;
+  std::memset(&t, 0, sizeof t);
+  t.c[1] = 0.161; t.c[2] = 0.327; t.c[3] = 0.9; t.c[4] = 0.9800255409045097;
+  t.c[5] = 1.0; t.c[6] = 1.0;
+  t.a[1][0] = 0.161;
+  t.a[2][0] = -0.008480655492356989; t.a[2][1] = 0.335480655492357;
+  t.a[3][0] = 2.897153057105493; t.a[3][1] = -6.359448489975075;
+  t.a[3][2] = 4.3622954328695815;
+  t.a[4][0] = 5.325864828439257; t.a[4][1] = -11.748883564062828;
+  t.a[4][2] = 7.4955393428898365; t.a[4][3] = -0.09249506636175525;
+  t.a[5][0] = 5.86145544294642; t.a[5][1] = -12.92096931784711;
+  t.a[5][2] = 8.159367898576159; t.a[5][3] = -0.071584973281401;
+  t.a[5][4] = -0.028269050394068383;
+  t.a[6][0] = 0.09646076681806523; t.a[6][1] = 0.01;
+  t.a[6][2] = 0.4798896504144996; t.a[6][3] = 1.379008574103742;
+  t.a[6][4] = -3.290069515436081; t.a[6][5] = 2.324710524099774;
+  for (int j = 0; j < 7; ++j) t.b[j] = t.a[6][j];
+  t.e[0] = -0.00178001105222577714; t.e[1] = -0.0008164344596567469;
+  t.e[2] = 0.007880878010261995; t.e[3] = -0.1447110071732629;
+  t.e[4] = 0.5823571654525552; t.e[5] = -0.45808210592918697;
+  t.e[6] = 0.015151515151515152;
+  t.order = 5; t.err_order = 4;
+  return t;
+}
+
+Tableau make_dopri5() {
+  /* Dormand & Prince (1980), rational coefficients. */
+  Tableau t;
+  std::memset(&t, 0, sizeof t);
+  t.c[1] = 1.0 / 5.0; t.c[2] = 3.0 / 10.0; t.c[3] = 4.0 / 5.0; t.c[4] = 8.0 / 9.0;
+  t.c[5] = 1.0; t.c[6] = 1.0;
+  t.a[1][0] = 1.0 / 5.0;
+  t.a[2][0] = 3.0 / 40.0; t.a[2][1] = 9.0 / 40.0;
+  t.a[3][0] = 44.0 / 45.0; t.a[3][1] = -56.0 / 15.0; t.a[3][2] = 32.0 / 9.0;
+  t.a[4][0] = 19372.0 / 6561.0; t.a[4][1] = -25360.0 / 2187.0;
+  t.a[4][2] = 64448.0 / 6561.0; t.a[4][3] = -212.0 / 729.0;
+  t.a[5][0] = 9017.0 / 3168.0; t.a[5][1] = -355.0 / 33.0;
+  t.a[5][2] = 46732.0 / 5247.0; t.a[5][3] = 49.0 / 176.0;
+  t.a[5][4] = -5103.0 / 18656.0;
+  t.a[6][0] = 35.0 / 384.0; t.a[6][1] = 0.0; t.a[6][2] = 500.0 / 1113.0;
+  t.a[6][3] = 125.0 / 192.0; t.a[6][4] = -2187.0 / 6784.0; t.a[6][5] = 11.0 / 84.0;
+  for (int j = 0; j < 7; ++j) t.b[j] = t.a[6][j];
+  /* b - bhat, bhat = (5179/57600, 0, 7571/16695, 393/640, -92097/339200,
+   * 187/2100, 1/40). */
+  t.e[0] = 71.0 / 57600.0; t.e[1] = 0.0; t.e[2] = -71.0 / 16695.0;
+  t.e[3] = 71.0 / 1920.0; t.e[4] = -17253.0 / 339200.0; t.e[5] = 22.0 / 525.0;
+  t.e[6] = -1.0 / 40.0;
+  t.order = 5; t.err_order = 4;
+  return t;
+}
+
+const Tableau TSIT5 = make_tsit5();
+const Tableau DOPRI5 = make_dopri5();
+
+/* ROS2 constant gamma = 1 + 1/sqrt(2). */
+const double ROS2_GAMMA = 1.0 + 1.0 / std::sqrt(2.0);
+
+/* ------------------------------------------------------------------ */
+/* Right-hand sides: f, Jacobian, vector-Jacobian products             */
+/* ------------------------------------------------------------------ */
+/* Conventions:
+ *  vjp_y: w[j] = sum_i J[i][j] v[i], rows i in the order listed per system.
+ *  vjp_p_acc: g[q] += sum_i (df_i/dp_q) v[i], each term a multiply-add into g.
+ *  jac_contract_acc: gy[c] += sum_ab Jbar[a][b] dJ[a][b]/dy_c and likewise
+ *  gp[q], each term a multiply-add into the accumulator, entries (a,b) in
+ *  row-major order. */
+
+template <class T, bool F>
+void rhs_f(int kind, int d, const T *y, const T *p, T *out) {
+  switch (kind) {
+    case R_LINEAR:  /* y' = p0 y */
+      out[0] = p[0] * y[0];
+      break;
+    case R_LORENZ63: {  /* sigma (u2-u1), u1 (rho-u3) - u2, u1 u2 - beta u3 */
+      const T s = p[0], r = p[1], b = p[2];
+      out[0] = s * (y[1] - y[0]);
+      out[1] = mac<F>(y[0], r - y[2], -y[1]);
+      out[2] = mac<F>(y[0], y[1], -(b * y[2]));
+      break;
+    }
+    case R_ROBERTSON: {
+      /* y1' = -k1 y1 + k3 y2 y3
+       * y2' =  k1 y1 - k2 y2^2 - k3 y2 y3
+       * y3' =  k2 y2^2 */
+      const T k1 = p[0], k2 = p[1], k3 = p[2];
+      out[0] = mac<F>(k3 * y[1], y[2], (-k1) * y[0]);
+      T s = k1 * y[0];
+      s = mac<F>(-(k2 * y[1]), y[1], s);
+      s = mac<F>(-(k3 * y[1]), y[2], s);
+      out[1] = s;
+      out[2] = (k2 * y[1]) * y[1];
+      break;
+    }
+    case R_LORENZ96: {  /* x_i' = (x_{i+1} - x_{i-2}) x_{i-1} - x_i + F */
+      const T Fc = p[0];
+      for (int i = 0; i < d; ++i) {
+        const T xp1 = y[(i + 1) % d], xm1 = y[(i + d - 1) % d], xm2 = y[(i + d - 2) % d];
+        const T a = xp1 - xm2;
+        out[i] = mac<F>(a, xm1, -y[i]) + Fc;
+      }
+      break;
+    }
+  }
+}
+
+/* Explicit Jacobian J[a*d+b] = df_a/dy_b (small systems; Rosenbrock only). */
+template <class T, bool F>
+void rhs_jac(int kind, int d, const T *y, const T *p, T *J) {
+  for (int i = 0; i < d * d; ++i) J[i] = T(0.0);
+  switch (kind) {
+    case R_LINEAR:
+      J[0] = p[0];
+      break;
+    case R_LORENZ63: {
+      const T s = p[0], r = p[1], b = p[2];
+      J[0] = -s;        J[1] = s;          J[2] = T(0.0);
+      J[3] = r - y[2];  J[4] = T(-1.0);    J[5] = -y[0];
+      J[6] = y[1];      J[7] = y[0];       J[8] = -b;
+      break;
+    }
+    case R_ROBERTSON: {
+      const T k1 = p[0], k2 = p[1], k3 = p[2];
+      J[0] = -k1;  J[1] = k3 * y[2];  J[2] = k3 * y[1];
+      /* J22 = -2 k2 y2 - k3 y3 */
+      J[3] = k1;   J[4] = mac<F>(-k3, y[2], -(T(2.0) * k2) * y[1]);  J[5] = -(k3 * y[1]);
+      J[6] = T(0.0); J[7] = T(2.0) * k2 * y[1]; J[8] = T(0.0);
+      break;
+    }
+  }
+}
+
+template <class T, bool F>
+void rhs_vjp_y(int kind, int d, const T *y, const T *p, const T *v, T *w) {
+  switch (kind) {
+    case R_LINEAR:
+      w[0] = p[0] * v[0];
+      break;
+    case R_LORENZ63: {
+      /* J = [[-s, s, 0], [r-u3, -1, -u1], [u2, u1, -b]]; rows 1,2,3 in order. */
+      const T s = p[0], r = p[1], b = p[2];
+      w[0] = mac<F>(y[1], v[2], mac<F>(r - y[2], v[1], (-s) * v[0]));
+      w[1] = mac<F>(y[0], v[2], mac<F>(s, v[0], -v[1]));
+      w[2] = mac<F>(-b, v[2], (-y[0]) * v[1]);
+      break;
+    }
+    case R_ROBERTSON: {
+      const T k1 = p[0], k2 = p[1], k3 = p[2];
+      /* column 1: J11 = -k1, J21 = k1 */
+      w[0] = mac<F>(k1, v[1], (-k1) * v[0]);
+      /* column 2: J12 = k3 y3, J22 = -2 k2 y2 - k3 y3, J32 = 2 k2 y2 */
+      const T j22 = mac<F>(-k3, y[2], -(T(2.0) * k2) * y[1]);
+      T s = (k3 * y[2]) * v[0];
+      s = mac<F>(j22, v[1], s);
+      s = mac<F>(T(2.0) * k2 * y[1], v[2], s);
+      w[1] = s;
+      /* column 3: J13 = k3 y2, J23 = -k3 y2 */
+      w[2] = mac<F>(-(k3 * y[1]), v[1], (k3 * y[1]) * v[0]);
+      break;
+    }
+    case R_LORENZ96: {
+      /* Column j has entries from rows j-1 (x_{j-2}), j (-1), j+1
+       * (x_{j+2} - x_{j-1}) and j+2 (-x_{j+1}), taken in that order. */
+      for (int j = 0; j < d; ++j) {
+        const T xm2 = y[(j + d - 2) % d], xm1 = y[(j + d - 1) % d];
+        const T xp1 = y[(j + 1) % d], xp2 = y[(j + 2) % d];
+        const T vm1 = v[(j + d - 1) % d], vp1 = v[(j + 1) % d], vp2 = v[(j + 2) % d];
+        T s = xm2 * vm1;
+        s = s - v[j];
+        s = mac<F>(xp2 - xm1, vp1, s);
+        s = mac<F>(-xp1, vp2, s);
+        w[j] = s;
+      }
+      break;
+    }
+  }
+}
+
+template <class T, bool F>
+void rhs_vjp_p_acc(int kind, int d, const T *y, const T *p, const T *v, T *g) {
+  switch (kind) {
+    case R_LINEAR:  /* df/dp0 = y */
+      g[0] = mac<F>(y[0], v[0], g[0]);
+      break;
+    case R_LORENZ63:  /* df/ds = (u2-u1,0,0), df/dr = (0,u1,0), df/db = (0,0,-u3) */
+      g[0] = mac<F>(y[1] - y[0], v[0], g[0]);
+      g[1] = mac<F>(y[0], v[1], g[1]);
+      g[2] = mac<F>(-y[2], v[2], g[2]);
+      break;
+    case R_ROBERTSON: {
+      /* df/dk1 = (-y1, y1, 0); df/dk2 = (0, -y2^2, y2^2);
+       * df/dk3 = (y2 y3, -y2 y3, 0) */
+      g[0] = mac<F>(-y[0], v[0], g[0]);
+      g[0] = mac<F>(y[0], v[1], g[0]);
+      const T y22 = y[1] * y[1];
+      g[1] = mac<F>(-y22, v[1], g[1]);
+      g[1] = mac<F>(y22, v[2], g[1]);
+      const T y23 = y[1] * y[2];
+      g[2] = mac<F>(y23, v[0], g[2]);
+      g[2] = mac<F>(-y23, v[1], g[2]);
+      break;
+    }
+    case R_LORENZ96:  /* df_i/dF = 1 */
+      for (int i = 0; i < d; ++i) g[0] = g[0] + v[i];
+      break;
+  }
+}
+
+/* Second-derivative contraction needed by the Rosenbrock adjoint. */
+template <class T, bool F>
+void rhs_jac_contract_acc(int kind, int d, const T *y, const T *p, const T *Jb,
+                          T *gy, T *gp) {
+  switch (kind) {
+    case R_LINEAR:  /* J = p0: dJ/dp0 = 1 */
+      gp[0] = gp[0] + Jb[0];
+      break;
+    case R_LORENZ63:
+      /* J11=-s, J12=s, J21=r-u3, J23=-u1, J31=u2, J32=u1, J33=-b */
+      gp[0] = gp[0] - Jb[0];
+      gp[0] = gp[0] + Jb[1];
+      gp[1] = gp[1] + Jb[3];
+      gy[2] = gy[2] - Jb[3];
+      gy[0] = gy[0] - Jb[5];
+      gy[1] = gy[1] + Jb[6];
+      gy[0] = gy[0] + Jb[7];
+      gp[2] = gp[2] - Jb[8];
+      break;
+    case R_ROBERTSON: {
+      const T k1 = p[0], k2 = p[1], k3 = p[2];
+      (void)k1;
+      /* entries in row-major order:
+       * J11=-k1: d/dk1=-1
+       * J12=k3 y3: d/dy3=k3, d/dk3=y3
+       * J13=k3 y2: d/dy2=k3, d/dk3=y2
+       * J21=k1: d/dk1=1
+       * J22=-2k2y2-k3y3: d/dy2=-2k2, d/dy3=-k3, d/dk2=-2y2, d/dk3=-y3
+       * J23=-k3 y2: d/dy2=-k3, d/dk3=-y2
+       * J32=2k2y2: d/dy2=2k2, d/dk2=2y2 */
+      const T two_k2 = T(2.0) * k2, two_y2 = T(2.0) * y[1];
+      gp[0] = gp[0] - Jb[0];
+      gy[2] = mac<F>(k3, Jb[1], gy[2]);
+      gp[2] = mac<F>(y[2], Jb[1], gp[2]);
+      gy[1] = mac<F>(k3, Jb[2], gy[1]);
+      gp[2] = mac<F>(y[1], Jb[2], gp[2]);
+      gp[0] = gp[0] + Jb[3];
+      gy[1] = mac<F>(-two_k2, Jb[4], gy[1]);
+      gy[2] = mac<F>(-k3, Jb[4], gy[2]);
+      gp[1] = mac<F>(-two_y2, Jb[4], gp[1]);
+      gp[2] = mac<F>(-y[2], Jb[4], gp[2]);
+      gy[1] = mac<F>(-k3, Jb[5], gy[1]);
+      gp[2] = mac<F>(-y[1], Jb[5], gp[2]);
+      gy[1] = mac<F>(two_k2, Jb[7], gy[1]);
+      gp[1] = mac<F>(two_y2, Jb[7], gp[1]);
+      break;
+    }
+  }
+}
+
+bool rhs_shape_ok(int kind, int d, int P) {
+  switch (kind) {
+    case R_LINEAR: return d == 1 && P == 1;
+    case R_LORENZ63: return d == 3 && P == 3;
+    case R_ROBERTSON: return d == 3 && P == 3;
+    case R_LORENZ96: return d >= 4 && d <= MAXD && P == 1;
+  }
+  return false;
+}
+
+/* ------------------------------------------------------------------ */
+/* Explicit RK step                                                    */
+/* ------------------------------------------------------------------ */
+
+/* Stages of one step from y with size h.  Stage 0 is y itself; K[0] must hold
+ * f(y) on entry.  Computes Y[1..last] and K[1..kl] where kl = last when
+ * with_last_k, else last-1.  Y[i][c] = y[c] + h * sum_{j<i} a[i][j] K[j][c]. */
+template <class T, bool F>
+void erk_stages(const Tableau &tb, int kind, int d, const T *y, const T *p, T h,
+                int last, bool with_last_k, T (*Y)[MAXD], T (*K)[MAXD]) {
+  const T *Kp[7];
+  for (int j = 0; j < 7; ++j) Kp[j] = K[j];
+  for (int c = 0; c < d; ++c) Y[0][c] = y[c];
+  for (int i = 1; i <= last; ++i) {
+    for (int c = 0; c < d; ++c) {
+      const T acc = chain<T, F>(i, tb.a[i], Kp, c);
+      Y[i][c] = mac<F>(h, acc, y[c]);
+    }
+    if (i < last || with_last_k) rhs_f<T, F>(kind, d, Y[i], p, K[i]);
+  }
+}
+
+/* Replay step: y <- y + h sum_j b_j k_j (the 7th stage state). */
+template <class T, bool F>
+void erk_step(const Tableau &tb, int kind, int d, T *y, const T *p, T h) {
+  T Y[7][MAXD], K[7][MAXD];
+  rhs_f<T, F>(kind, d, y, p, K[0]);
+  erk_stages<T, F>(tb, kind, d, y, p, h, 6, false, Y, K);
+  for (int c = 0; c < d; ++c) y[c] = Y[6][c];
+}
+
+/* Reverse of erk_step: lam holds dL/dy_{k+1} on entry, dL/dy_k on exit;
+ * gp accumulates dL/dp.  Stage states are recomputed from y = y_k. */
+template <class T, bool F>
+void erk_step_adjoint(const Tableau &tb, int kind, int d, const T *y, const T *p,
+                      T h, T *lam, T *gp) {
+  T Y[7][MAXD], K[7][MAXD], Wv[7][MAXD], kb[MAXD], lacc[MAXD];
+  rhs_f<T, F>(kind, d, y, p, K[0]);
+  erk_stages<T, F>(tb, kind, d, y, p, h, 5, false, Y, K);
+  for (int c = 0; c < d; ++c) lacc[c] = lam[c];
+  for (int i = 5; i >= 0; --i) {
+    /* kbar_i = h (b_i lam + sum_{l>i} a[l][i] w_l), terms in that order */
+    for (int c = 0; c < d; ++c) {
+      T acc = T(0.0);
+      bool first = true;
+      if (tb.b[i] != 0.0) { acc = T(tb.b[i]) * lam[c]; first = false; }
+      for (int l = i + 1; l <= 5; ++l) {
+        if (tb.a[l][i] == 0.0) continue;
+        if (first) { acc = T(tb.a[l][i]) * Wv[l][c]; first = false; }
+        else acc = mac<F>(T(tb.a[l][i]), Wv[l][c], acc);
+      }
+      kb[c] = h * acc;
+    }
+    rhs_vjp_y<T, F>(kind, d, Y[i], p, kb, Wv[i]);
+    rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);
+    for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];
+  }
+  for (int c = 0; c < d; ++c) lam[c] = lacc[c];
+}
+
+/* ------------------------------------------------------------------ */
+/* ROS2 step                                                           */
+/* ------------------------------------------------------------------ */
+
+/* LU with partial pivoting of the d x d matrix A (row-major, in place);
+ * perm[i] = original row now in position i.  Ties keep the lowest row. */
+template <class T, bool F>
+void lu_factor(int d, T *A, int *perm) {
+  for (int i = 0; i < d; ++i) perm[i] = i;
+  for (int k = 0; k < d; ++k) {
+    int piv = k;
+    double best = std::fabs(val(A[k * d + k]));
+    for (int i = k + 1; i < d; ++i) {
+      const double v = std::fabs(val(A[i * d + k]));
+      if (v > best) { best = v; piv = i; }
+    }
+    if (piv != k) {
+      for (int j = 0; j < d; ++j) std::swap(A[k * d + j], A[piv * d + j]);
+      std::swap(perm[k], perm[piv]);
+    }
+    for (int i = k + 1; i < d; ++i) {
+      const T l = A[i * d + k] / A[k * d + k];
+      A[i * d + k] = l;
+      for (int j = k + 1; j < d; ++j) A[i * d + j] = mac<F>(-l, A[k * d + j], A[i * d + j]);
+    }
+  }
+}
+
+/* Solve A x = b from the factors. */
+template <class T, bool F>
+void lu_solve(int d, const T *LU, const int *perm, const T *b, T *x) {
+  for (int i = 0; i < d; ++i) x[i] = b[perm[i]];
+  for (int i = 0; i < d; ++i)
+    for (int j = 0; j < i; ++j) x[i] = mac<F>(-LU[i * d + j], x[j], x[i]);
+  for (int i = d - 1; i >= 0; --i) {
+    for (int j = i + 1; j < d; ++j) x[i] = mac<F>(-LU[i * d + j], x[j], x[i]);
+    x[i] = x[i] / LU[i * d + i];
+  }
+}
+
+/* Solve A^T x = b from the factors of A (P A = L U, so A^T = U^T L^T P). */
+template <class T, bool F>
+void lu_solve_t(int d, const T *LU, const int *perm, const T *b, T *x) {
+  T z[MAXD];
+  for (int i = 0; i < d; ++i) {
+    z[i] = b[i];
+    for (int j = 0; j < i; ++j) z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);
+    z[i] = z[i] / LU[i * d + i];
+  }
+  for (int i = d - 1; i >= 0; --i)
+    for (int j = i + 1; j < d; ++j) z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);
+  for (int i = 0; i < d; ++i) x[perm[i]] = z[i];
+}
+
+/* Everything one ROS2 step computes from (y, h). */
+template <class T>
+struct Ros2Step {
+  T J[9], LU[9];
+  int perm[3];
+  T f1[3], k1[3], Y2[3], f2[3], r2[3], k2[3], ynew[3], err[3];
+};
+
+/* W = I - gamma h J; k1 = W^-1 f(y); Y2 = y + h k1;
+ * k2 = W^-1 (f(Y2) - 2 k1); y+ = y + h (3/2 k1 + 1/2 k2);
+ * err = h (1/2 k1 + 1/2 k2)  (difference to the first-order y + h k1). */
+template <class T, bool F>
+void ros2_forward(int kind, int d, const T *y, const T *p, T h, Ros2Step<T> &s) {
+  rhs_jac<T, F>(kind, d, y, p, s.J);
+  const T gh = T(ROS2_GAMMA) * h;
+  for (int a = 0; a < d; ++a)
+    for (int b = 0; b < d; ++b)
+      s.LU[a * d + b] = (a == b) ? mac<F>(-gh, s.J[a * d + b], T(1.0)) : (-gh) * s.J[a * d + b];
+  lu_factor<T, F>(d, s.LU, s.perm);
+  rhs_f<T, F>(kind, d, y, p, s.f1);
+  lu_solve<T, F>(d, s.LU, s.perm, s.f1, s.k1);
+  for (int c = 0; c < d; ++c) s.Y2[c] = mac<F>(h, s.k1[c], y[c]);
+  rhs_f<T, F>(kind, d, s.Y2, p, s.f2);
+  for (int c = 0; c < d; ++c) s.r2[c] = mac<F>(T(-2.0), s.k1[c], s.f2[c]);
+  lu_solve<T, F>(d, s.LU, s.perm, s.r2, s.k2);
+  for (int c = 0; c < d; ++c) {
+    const T acc = mac<F>(T(0.5), s.k2[c], T(1.5) * s.k1[c]);
+    s.ynew[c] = mac<F>(h, acc, y[c]);
+    const T e = mac<F>(T(0.5), s.k2[c], T(0.5) * s.k1[c]);
+    s.err[c] = h * e;
+  }
+}
+
+template <class T, bool F>
+void ros2_step(int kind, int d, T *y, const T *p, T h) {
+  Ros2Step<T> s;
+  ros2_forward<T, F>(kind, d, y, p, h, s);
+  for (int c = 0; c < d; ++c) y[c] = s.ynew[c];
+}
+
+/* Reverse of ros2_step (mesh fixed): transposed solves with the same factors
+ * and the contraction of Jbar with the derivative of J. */
+template <class T, bool F>
+void ros2_step_adjoint(int kind, int d, const T *y, const T *p, T h, T *lam, T *gp) {
+  Ros2Step<T> s;
+  ros2_forward<T, F>(kind, d, y, p, h, s);
+  T yb[3], kb1[3], kb2[3], rb1[3], rb2[3], Y2b[3], w[3], Wb[9], Jb[9];
+  for (int c = 0; c < d; ++c) {
+    const T ab = h * lam[c];      /* adjoint of the weighted stage sum */
+    kb1[c] = T(1.5) * ab;
+    kb2[c] = T(0.5) * ab;
+    yb[c] = lam[c];
+  }
+  lu_solve_t<T, F>(d, s.LU, s.perm, kb2, rb2);
+  for (int a = 0; a < d; ++a)
+    for (int b = 0; b < d; ++b) Wb[a * d + b] = (-rb2[a]) * s.k2[b];
+  rhs_vjp_y<T, F>(kind, d, s.Y2, p, rb2, Y2b);
+  rhs_vjp_p_acc<T, F>(kind, d, s.Y2, p, rb2, gp);
+  for (int c = 0; c < d; ++c) {
+    kb1[c] = mac<F>(T(-2.0), rb2[c], kb1[c]);
+    kb1[c] = mac<F>(h, Y2b[c], kb1[c]);
+    yb[c] = yb[c] + Y2b[c];
+  }
+  lu_solve_t<T, F>(d, s.LU, s.perm, kb1, rb1);
+  for (int a = 0; a < d; ++a)
+    for (int b = 0; b < d; ++b) Wb[a * d + b] = mac<F>(-rb1[a], s.k1[b], Wb[a * d + b]);
+  rhs_vjp_y<T, F>(kind, d, y, p, rb1, w);
+  rhs_vjp_p_acc<T, F>(kind, d, y, p, rb1, gp);
+  for (int c = 0; c < d; ++c) yb[c] = yb[c] + w[c];
+  const T gh = T(ROS2_GAMMA) * h;
+  for (int i = 0; i < d * d; ++i) Jb[i] = (-gh) * Wb[i];
+  rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);
+  for (int c = 0; c < d; ++c) lam[c] = yb[c];
+}
+
+/* ------------------------------------------------------------------ */
+/* Problem helpers                                                     */
+/* ------------------------------------------------------------------ */
+
+struct Opts {
+  double safety, fac_min, fac_max;
+  int max_attempts;
+  int S;               /* save slots: max(1, n_save) */
+  const double *saves; /* S times; the last save of n_save = 0 is t1 */
+  double t1_only[1];
+};
+
+Opts make_opts(const orc_problem *P) {
+  Opts o;
+  o.safety = P->safety > 0 ? P->safety : 0.9;
+  o.fac_min = P->fac_min > 0 ? P->fac_min : 0.2;
+  o.fac_max = P->fac_max > 0 ? P->fac_max : 10.0;
+  o.max_attempts = P->max_attempts > 0 ? P->max_attempts : 4 * P->max_steps;
+  o.t1_only[0] = P->t1;
+  if (P->n_save > 0) { o.S = P->n_save; o.saves = P->save_times; }
+  else { o.S = 1; o.saves = nullptr; }
+  return o;
+}
+
+int validate(const orc_problem *P) {
+  if (!P) return E_INVAL;
+  if (P->method < 0 || P->method > 2) return E_INVAL;
+  if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
+  if (P->method == M_ROS2 && P->dim > 3) return E_UNSUPPORTED;
+  if (!(P->t1 > P->t0)) return E_INVAL;
+  if (!(P->rtol >= 0) || !(P->atol >= 0) || !(P->rtol + P->atol > 0)) return E_INVAL;
+  if (P->max_steps < 1) return E_INVAL;
+  if (P->n_save < 0) return E_INVAL;
+  if (P->n_save > 0) {
+    if (!P->save_times) return E_INVAL;
+    double prev = P->t0;
+    for (int s = 0; s < P->n_save; ++s) {
+      if (!(P->save_times[s] > prev) || P->save_times[s] > P->t1) return E_INVAL;
+      prev = P->save_times[s];
+    }
+  }
+  return E_OK;
+}
+
+/* RMS norm of v / sc over d components. */
+template <class T, bool F>
+T rms(int d, const T *v, const T *sc) {
+  T s = T(0.0);
+  for (int c = 0; c < d; ++c) {
+    const T q = v[c] / sc[c];
+    s = (c == 0) ? q * q : mac<F>(q, q, s);
+  }
+  return std::sqrt(s / T(d));
+}
+
+/* Error norm: RMS of err / (atol + rtol max(|y|, |y+|)). */
+template <class T, bool F>
+T err_norm(int d, const T *err, const T *y, const T *yn, T atol, T rtol) {
+  T sc[MAXD];
+  for (int c = 0; c < d; ++c)
+    sc[c] = mac<F>(rtol, std::max(absval(y[c]), absval(yn[c])), atol);
+  return rms<T, F>(d, err, sc);
+}
+
+/* Starting step (HNW I, II.4) for a method of order q. */
+template <class T, bool F>
+T initial_step(int kind, int d, const T *y0, const T *f0, const T *p, T atol, T rtol,
+               int q) {
+  T sc[MAXD] = {}, y1[MAXD] = {}, f1[MAXD] = {}, df[MAXD] = {};
+  for (int c = 0; c < d; ++c) sc[c] = mac<F>(rtol, absval(y0[c]), atol);
+  const T d0 = rms<T, F>(d, y0, sc);
+  const T d1 = rms<T, F>(d, f0, sc);
+  T h0 = (d0 < T(1e-5) || d1 < T(1e-5)) ? T(1e-6) : T(0.01) * (d0 / d1);
+  for (int c = 0; c < d; ++c) y1[c] = mac<F>(h0, f0[c], y0[c]);
+  rhs_f<T, F>(kind, d, y1, p, f1);
+  for (int c = 0; c < d; ++c) df[c] = f1[c] - f0[c];
+  const T d2 = rms<T, F>(d, df, sc) / h0;
+  const T dm = std::max(d1, d2);
+  T h1;
+  if (dm <= T(1e-15)) h1 = std::max(T(1e-6), h0 * T(1e-3));
+  else h1 = std::pow(T(0.01) / dm, T(1.0) / T(q + 1));
+  return std::min(T(100.0) * h0, h1);
+}
+
+/* ------------------------------------------------------------------ */
+/* Record (adaptive solve logging accepted steps)                      */
+/* ------------------------------------------------------------------ */
+
+template <class T>
+struct LaneOut {
+  T *h;            /* [max_steps] or null */
+  int32_t *nsteps;
+  int32_t *sidx;   /* [S] */
+  int32_t *status;
+  T *ysave;        /* [S][d] or null */
+  int32_t *natt;   /* or null */
+};
+
+/* One adaptive integration.  Steps are clipped to land exactly on every save
+ * time and on t1; t accumulates in double.  Controller: accept iff E <= 1;
+ * h_next = h_used * clamp(safety E^(-1/(q+1)), fac_min, fac_max), no growth on
+ * the step after a reject, fac_max when E == 0, fac_min on a non-finite E.
+ * Stop times are the save times followed by t1 when the last save is earlier
+ * (with no save times, t1 is the one save slot). */
+template <class T, bool F>
+void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
+                 const LaneOut<T> &out) {
+  const int d = P->dim, kind = P->rhs;
+  const bool ros = P->method == M_ROS2;
+  const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
+  const int qerr = ros ? 1 : tb.err_order;
+  const int qord = ros ? 2 : tb.order;
+  const T atol = T(P->atol), rtol = T(P->rtol);
+  const T expo = T(-1.0) / T(qerr + 1);
+  const T safety = T(o.safety), fmin = T(o.fac_min), fmax = T(o.fac_max);
+  const int n_stops = o.S + ((o.saves && o.saves[o.S - 1] < P->t1) ? 1 : 0);
+
+  T y[MAXD], ynew[MAXD], err[MAXD];
+  T Y[7][MAXD], K[7][MAXD];
+  for (int c = 0; c < d; ++c) y[c] = u0[c];
+  for (int s = 0; s < o.S; ++s) {
+    out.sidx[s] = -1;
+    if (out.ysave)
+      for (int c = 0; c < d; ++c) out.ysave[s * d + c] = T(NAN);
+  }
+  int nacc = 0, natt = 0, st = S_OK;
+  bool finite = true;
+  for (int c = 0; c < d; ++c) finite = finite && fin(y[c]);
+  for (int q = 0; q < P->n_params; ++q) finite = finite && fin(p[q]);
+  if (!finite) {
+    st = S_NONFINITE;
+  } else {
+    rhs_f<T, F>(kind, d, y, p, K[0]);
+    T h = P->dt0 > 0 ? T(P->dt0) : initial_step<T, F>(kind, d, y, K[0], p, atol, rtol, qord);
+    double t = P->t0;
+    int j = 0;  /* next stop */
+    bool after_reject = false;
+    for (;;) {
+      const double t_stop = (o.saves && j < o.S) ? o.saves[j] : P->t1;
+      const T rem = T(t_stop - t);
+      const bool land = !(h < rem);
+      const T hs = land ? rem : h;
+      if (nacc >= P->max_steps) { st = S_MAX_STEPS; break; }
+      if (natt >= o.max_attempts) { st = S_MAX_ATTEMPTS; break; }
+      if (!(hs > T(0.0)) || t + double(hs) == t) { st = S_DT_UNDERFLOW; break; }
+      ++natt;
+      if (ros) {
+        Ros2Step<T> rs;
+        ros2_forward<T, F>(kind, d, y, p, hs, rs);
+        for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+      } else {
+        erk_stages<T, F>(tb, kind, d, y, p, hs, 6, true, Y, K);
+        const T *Kp[7];
+        for (int i = 0; i < 7; ++i) Kp[i] = K[i];
+        for (int c = 0; c < d; ++c) {
+          ynew[c] = Y[6][c];
+          err[c] = hs * chain<T, F>(7, tb.e, Kp, c);
+        }
+      }
+      const T E = err_norm<T, F>(d, err, y, ynew, atol, rtol);
+      if (E <= T(1.0)) {
+        if (out.h) out.h[nacc] = hs;
+        ++nacc;
+        for (int c = 0; c < d; ++c) y[c] = ynew[c];
+        if (!ros)
+          for (int c = 0; c < d; ++c) K[0][c] = K[6][c];  /* first same as last */
+        t = land ? t_stop : t + double(hs);
+        T fac = (E == T(0.0)) ? fmax
+                              : std::min(fmax, std::max(fmin, safety * std::pow(E, expo)));
+        if (after_reject) fac = std::min(fac, T(1.0));
+        h = hs * fac;
+        after_reject = false;
+        if (land) {
+          if (j < o.S) {
+            out.sidx[j] = nacc;
+            if (out.ysave)
+              for (int c = 0; c < d; ++c) out.ysave[j * d + c] = y[c];
+          }
+          if (++j == n_stops) break;
+        }
+      } else {
+        const T fac = fin(E) ? std::max(fmin, safety * std::pow(E, expo)) : fmin;
+        h = hs * fac;
+        after_reject = true;
+      }
+    }
+  }
+  if (out.h)
+    for (int k = nacc; k < P->max_steps; ++k) out.h[k] = T(0.0);
+  *out.nsteps = nacc;
+  *out.status = st;
+  if (out.natt) *out.natt = natt;
+}
+
+/* ------------------------------------------------------------------ */
+/* Replay, loss, adjoint                                               */
+/* ------------------------------------------------------------------ */
+
+template <class T, bool F>
+inline void one_step(const orc_problem *P, T *y, const T *p, T h) {
+  if (P->method == M_ROS2) ros2_step<T, F>(P->rhs, P->dim, y, p, h);
+  else erk_step<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p, h);
+}
+
+template <class T, bool F>
+inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, T *lam, T *gp) {
+  if (P->method == M_ROS2) ros2_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
+  else erk_step_adjoint<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p,
+                              h, lam, gp);
+}
+
+/* Fixed-step replay of a recorded mesh: writes y at every save index. */
+template <class T, bool F>
+void replay_lane(const orc_problem *P, int S, const T *u0, const T *p, const T *h, int N,
+                 const int32_t *sidx, T *ysave, T *yfinal) {
+  const int d = P->dim;
+  T y[MAXD];
+  for (int c = 0; c < d; ++c) y[c] = u0[c];
+  for (int s = 0; s < S; ++s)
+    if (sidx[s] == 0)
+      for (int c = 0; c < d; ++c) ysave[s * d + c] = y[c];
+  for (int k = 0; k < N; ++k) {
+    one_step<T, F>(P, y, p, h[k]);
+    for (int s = 0; s < S; ++s)
+      if (sidx[s] == k + 1)
+        for (int c = 0; c < d; ++c) ysave[s * d + c] = y[c];
+  }
+  for (int s = 0; s < S; ++s)
+    if (sidx[s] < 0 || sidx[s] > N)
+      for (int c = 0; c < d; ++c) ysave[s * d + c] = T(NAN);
+  if (yfinal)
+    for (int c = 0; c < d; ++c) yfinal[c] = y[c];
+}
+
+/* Loss term of one save slot (MSE / cotangent kinds), accumulated into ss. */
+template <class T, bool F>
+void save_loss(int kind, int d, const T *y, const T *aux, T &ss, bool &first) {
+  for (int c = 0; c < d; ++c) {
+    if (kind == L_MSE_SAVE) {
+      const T r = y[c] - aux[c];
+      ss = first ? r * r : mac<F>(r, r, ss);
+    } else {
+      ss = first ? aux[c] * y[c] : mac<F>(aux[c], y[c], ss);
+    }
+    first = false;
+  }
+}
+
+/* Seed of one save slot added to the adjoint: 2 scale (y - target) for MSE,
+ * scale * cotangent otherwise. */
+template <class T, bool F>
+void save_seed(int kind, int d, const T *y, const T *aux, double scale, T *lam) {
+  for (int c = 0; c < d; ++c) {
+    if (kind == L_MSE_SAVE) lam[c] = mac<F>(T(2.0 * scale), y[c] - aux[c], lam[c]);
+    else lam[c] = mac<F>(T(scale), aux[c], lam[c]);
+  }
+}
+
+/* Replay + reverse sweep for one lane.  Loss kinds:
+ *  SUMSQ_FINAL: L = scale sum_c y_N[c]^2
+ *  MSE_SAVE:    L = scale sum_s sum_c (y_{idx_s}[c] - target[s][c])^2
+ *  COTANGENT:   L = scale sum_s sum_c cot[s][c] y_{idx_s}[c]
+ * The oracle keeps every forward state y_k, then runs the reverse sweep and
+ * adds each save's seed once the adjoint has reached that save's index. */
+template <class T, bool F>
+void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, const T *h, int N,
+                      const int32_t *sidx, int status, int loss_kind, const T *aux,
+                      double scale, T *loss, T *gu0, T *gp, T *ybuf /*[(N+1)*d]*/) {
+  const int d = P->dim, Pn = P->n_params;
+  if (status != S_OK) {
+    *loss = T(NAN);
+    for (int c = 0; c < d; ++c) gu0[c] = T(NAN);
+    for (int q = 0; q < Pn; ++q) gp[q] = T(NAN);
+    return;
+  }
+  for (int c = 0; c < d; ++c) ybuf[c] = u0[c];
+  for (int k = 0; k < N; ++k) {
+    for (int c = 0; c < d; ++c) ybuf[(k + 1) * d + c] = ybuf[k * d + c];
+    one_step<T, F>(P, &ybuf[(k + 1) * d], p, h[k]);
+  }
+  T lam[MAXD], g[MAXP];
+  for (int c = 0; c < d; ++c) lam[c] = T(0.0);
+  for (int q = 0; q < Pn; ++q) g[q] = T(0.0);
+  T ss = T(0.0);
+  const T *yN = &ybuf[N * d];
+  if (loss_kind == L_SUMSQ_FINAL) {
+    for (int c = 0; c < d; ++c) ss = (c == 0) ? yN[c] * yN[c] : mac<F>(yN[c], yN[c], ss);
+    for (int c = 0; c < d; ++c) lam[c] = T(2.0 * scale) * yN[c];
+  } else {
+    bool first = true;
+    for (int s = 0; s < S; ++s)
+      save_loss<T, F>(loss_kind, d, &ybuf[sidx[s] * d], &aux[s * d], ss, first);
+  }
+  *loss = T(scale) * ss;
+  int s_hi = S - 1;  /* highest save slot not yet seeded */
+  if (loss_kind != L_SUMSQ_FINAL)
+    for (; s_hi >= 0 && sidx[s_hi] == N; --s_hi)
+      save_seed<T, F>(loss_kind, d, yN, &aux[s_hi * d], scale, lam);
+  for (int k = N - 1; k >= 0; --k) {
+    one_step_adjoint<T, F>(P, &ybuf[k * d], p, h[k], lam, g);
+    if (loss_kind != L_SUMSQ_FINAL)
+      for (; s_hi >= 0 && sidx[s_hi] == k; --s_hi)
+        save_seed<T, F>(loss_kind, d, &ybuf[k * d], &aux[s_hi * d], scale, lam);
+  }
+  for (int c = 0; c < d; ++c) gu0[c] = lam[c];
+  for (int q = 0; q < Pn; ++q) gp[q] = g[q];
+}
+
+/* Re-evaluate the embedded error of every step of a given mesh along the
+ * replayed states (GPU-recorded mesh check): largest E per lane. */
+template <class T, bool F>
+T mesh_max_err_lane(const orc_problem *P, const T *u0, const T *p, const T *h, int N) {
+  const int d = P->dim, kind = P->rhs;
+  const bool ros = P->method == M_ROS2;
+  const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
+  const T atol = T(P->atol), rtol = T(P->rtol);
+  T y[MAXD], ynew[MAXD], err[MAXD], Y[7][MAXD], K[7][MAXD];
+  for (int c = 0; c < d; ++c) y[c] = u0[c];
+  T worst = T(0.0);
+  for (int k = 0; k < N; ++k) {
+    if (ros) {
+      Ros2Step<T> rs;
+      ros2_forward<T, F>(kind, d, y, p, h[k], rs);
+      for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+    } else {
+      rhs_f<T, F>(kind, d, y, p, K[0]);
+      erk_stages<T, F>(tb, kind, d, y, p, h[k], 6, true, Y, K);
+      const T *Kp[7];
+      for (int j = 0; j < 7; ++j) Kp[j] = K[j];
+      for (int c = 0; c < d; ++c) {
+        ynew[c] = Y[6][c];
+        err[c] = h[k] * chain<T, F>(7, tb.e, Kp, c);
+      }
+    }
+    const T E = err_norm<T, F>(d, err, y, ynew, atol, rtol);
+    if (!(E <= worst)) worst = E;
+    for (int c = 0; c < d; ++c) y[c] = ynew[c];
+  }
+  return worst;
+}
+
+int set_threads(int nthreads) {
+  if (nthreads > 0) omp_set_num_threads(nthreads);
+  return omp_get_max_threads();
+}
+
+template <class T>
+int record_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused, T *h,
+               int32_t *nsteps, int32_t *sidx, int32_t *status, T *ysave, int32_t *natt,
+               int nthreads) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!u0 || !p || !nsteps || !sidx || !status))) return E_INVAL;
+  const Opts o = make_opts(P);
+  const int d = P->dim, Pn = P->n_params;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n; ++i) {
+    LaneOut<T> out;
+    out.h = h ? h + i * P->max_steps : nullptr;
+    out.nsteps = nsteps + i;
+    out.sidx = sidx + i * o.S;
+    out.status = status + i;
+    out.ysave = ysave ? ysave + i * o.S * d : nullptr;
+    out.natt = natt ? natt + i : nullptr;
+    if (fused) record_lane<T, true>(P, o, u0 + i * d, p + i * Pn, out);
+    else record_lane<T, false>(P, o, u0 + i * d, p + i * Pn, out);
+  }
+  return E_OK;
+}
+
+template <class T>
+int replay_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused, const T *h,
+               const int32_t *nsteps, const int32_t *sidx, T *ysave, T *yfinal, int nthreads) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!u0 || !p || !h || !nsteps || !sidx || !ysave))) return E_INVAL;
+  const Opts o = make_opts(P);
+  const int d = P->dim, Pn = P->n_params;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n; ++i) {
+    const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+    T *yf = yfinal ? yfinal + i * d : nullptr;
+    if (fused)
+      replay_lane<T, true>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                           sidx + i * o.S, ysave + i * o.S * d, yf);
+    else
+      replay_lane<T, false>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                            sidx + i * o.S, ysave + i * o.S * d, yf);
+  }
+  return E_OK;
+}
+
+template <class T>
+int replay_grad_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused,
+                    const T *h, const int32_t *nsteps, const int32_t *sidx,
+                    const int32_t *status, int loss_kind, const T *aux, double scale, T *loss,
+                    T *gu0, T *gp, int nthreads) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  if (loss_kind < 0 || loss_kind > 2) return E_INVAL;
+  if (loss_kind != L_SUMSQ_FINAL && !aux) return E_INVAL;
+  if (n < 0 || (n > 0 && (!u0 || !p || !h || !nsteps || !sidx || !status || !loss || !gu0 || !gp)))
+    return E_INVAL;
+  const Opts o = make_opts(P);
+  const int d = P->dim, Pn = P->n_params;
+  set_threads(nthreads);
+#pragma omp parallel
+  {
+    T *ybuf = new T[(size_t)(P->max_steps + 1) * d];
+#pragma omp for schedule(dynamic, 64)
+    for (int64_t i = 0; i < n; ++i) {
+      const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+      const T *ax = aux ? aux + i * o.S * d : nullptr;
+      if (fused)
+        replay_grad_lane<T, true>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                                  sidx + i * o.S, status[i], loss_kind, ax, scale, loss + i,
+                                  gu0 + i * d, gp + i * Pn, ybuf);
+      else
+        replay_grad_lane<T, false>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                                   sidx + i * o.S, status[i], loss_kind, ax, scale, loss + i,
+                                   gu0 + i * d, gp + i * Pn, ybuf);
+    }
+    delete[] ybuf;
+  }
+  return E_OK;
+}
+
+}  // namespace
+
+/* ------------------------------------------------------------------ */
+/* C entry points (ctypes)                                             */
+/* ------------------------------------------------------------------ */
+extern "C" {
+
+/* Tableau of an explicit method: c[7], a[7*7] row-major, b[7], e[7],
+ * info[2] = {order, embedded order}. */
+int orc_tableau(int method, double *c, double *a, double *b, double *e, int32_t *info) {
+  if (method != M_TSIT5 && method != M_DOPRI5) return E_INVAL;
+  const Tableau &t = method == M_TSIT5 ? TSIT5 : DOPRI5;
+  for (int i = 0; i < 7; ++i) {
+    c[i] = t.c[i]; b[i] = t.b[i]; e[i] = t.e[i];
+    for (int j = 0; j < 7; ++j) a[i * 7 + j] = t.a[i][j];
+  }
+  info[0] = t.order; info[1] = t.err_order;
+  return E_OK;
+}
+
+double orc_ros2_gamma(void) { return ROS2_GAMMA; }
+
+int orc_max_threads(int nthreads) { return set_threads(nthreads); }
+
+int orc_record_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                   int32_t fused, double *h, int32_t *nsteps, int32_t *sidx, int32_t *status,
+                   double *ysave, int32_t *natt, int32_t nthreads) {
+  return record_all<double>(P, n, u0, p, fused, h, nsteps, sidx, status, ysave, natt, nthreads);
+}
+int orc_record_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
+                   int32_t fused, float *h, int32_t *nsteps, int32_t *sidx, int32_t *status,
+                   float *ysave, int32_t *natt, int32_t nthreads) {
+  return record_all<float>(P, n, u0, p, fused, h, nsteps, sidx, status, ysave, natt, nthreads);
+}
+
+int orc_replay_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                   int32_t fused, const double *h, const int32_t *nsteps, const int32_t *sidx,
+                   double *ysave, double *yfinal, int32_t nthreads) {
+  return replay_all<double>(P, n, u0, p, fused, h, nsteps, sidx, ysave, yfinal, nthreads);
+}
+int orc_replay_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
+                   int32_t fused, const float *h, const int32_t *nsteps, const int32_t *sidx,
+                   float *ysave, float *yfinal, int32_t nthreads) {
+  return replay_all<float>(P, n, u0, p, fused, h, nsteps, sidx, ysave, yfinal, nthreads);
+}
+
+int orc_replay_grad_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                        int32_t fused, const double *h, const int32_t *nsteps,
+                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
+                        const double *aux, double scale, double *loss, double *gu0,
+                        double *gp, int32_t nthreads) {
+  return replay_grad_all<double>(P, n, u0, p, fused, h, nsteps, sidx, status, loss_kind, aux,
+                                 scale, loss, gu0, gp, nthreads);
+}
+int orc_replay_grad_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
+                        int32_t fused, const float *h, const int32_t *nsteps,
+                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
+                        const float *aux, double scale, float *loss, float *gu0, float *gp,
+                        int32_t nthreads) {
+  return replay_grad_all<float>(P, n, u0, p, fused, h, nsteps, sidx, status, loss_kind, aux,
+                                scale, loss, gu0, gp, nthreads);
+}
+
+/* Forward-mode derivative of the replayed loss along (du0, dp): one dual
+ * number per value, plain rounding.  Outputs the loss and its directional
+ * derivative per lane, and the saved states with their tangents. */
+int orc_replay_jvp_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                       const double *du0, const double *dp, const double *h,
+                       const int32_t *nsteps, const int32_t *sidx, int32_t loss_kind,
+                       const double *aux, double scale, double *loss, double *dloss,
+                       double *ysave, double *dysave) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  if (loss_kind < 0 || loss_kind > 2 || (loss_kind != L_SUMSQ_FINAL && !aux)) return E_INVAL;
+  const Opts o = make_opts(P);
+  const int d = P->dim, Pn = P->n_params, S = o.S;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < n; ++i) {
+    Dual yv[MAXD], pv[MAXP], ys[16 * MAXD];
+    const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+    for (int c = 0; c < d; ++c) yv[c] = Dual(u0[i * d + c], du0[i * d + c]);
+    for (int q = 0; q < Pn; ++q) pv[q] = Dual(p[i * Pn + q], dp[i * Pn + q]);
+    Dual *ysl = (S <= 16) ? ys : new Dual[(size_t)S * d];
+    for (int s = 0; s < S; ++s)
+      for (int c = 0; c < d; ++c) ysl[s * d + c] = Dual(NAN);
+    const int32_t *si = sidx + i * S;
+    for (int s = 0; s < S; ++s)
+      if (si[s] == 0)
+        for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+    for (int k = 0; k < N; ++k) {
+      one_step<Dual, false>(P, yv, pv, Dual(h[i * P->max_steps + k]));
+      for (int s = 0; s < S; ++s)
+        if (si[s] == k + 1)
+          for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+    }
+    Dual ss(0.0);
+    bool first = true;
+    if (loss_kind == L_SUMSQ_FINAL) {
+      for (int c = 0; c < d; ++c) { ss = first ? yv[c] * yv[c] : yv[c] * yv[c] + ss; first = false; }
+    } else {
+      for (int s = 0; s < S; ++s)
+        for (int c = 0; c < d; ++c) {
+          const Dual a(aux[(i * S + s) * d + c]);
+          const Dual y = ysl[s * d + c];
+          const Dual term = (loss_kind == L_MSE_SAVE) ? (y - a) * (y - a) : a * y;
+          ss = first ? term : term + ss;
+          first = false;
+        }
+    }
+    const Dual L = Dual(scale) * ss;
+    loss[i] = L.v;
+    dloss[i] = L.d;
+    if (ysave)
+      for (int s = 0; s < S; ++s)
+        for (int c = 0; c < d; ++c) {
+          ysave[(i * S + s) * d + c] = ysl[s * d + c].v;
+          dysave[(i * S + s) * d + c] = ysl[s * d + c].d;
+        }
+    if (ysl != ys) delete[] ysl;
+  }
+  return E_OK;
+}
+
+int orc_mesh_max_err_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                         int32_t fused, const double *h, const int32_t *nsteps,
+                         double *max_err, int32_t nthreads) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  const int d = P->dim, Pn = P->n_params;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n; ++i) {
+    const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+    max_err[i] = fused ? mesh_max_err_lane<double, true>(P, u0 + i * d, p + i * Pn,
+                                                          h + i * P->max_steps, N)
+                       : mesh_max_err_lane<double, false>(P, u0 + i * d, p + i * Pn,
+                                                           h + i * P->max_steps, N);
+  }
+  return E_OK;
+}
+int orc_mesh_max_err_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
+                         int32_t fused, const float *h, const int32_t *nsteps,
+                         float *max_err, int32_t nthreads) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  const int d = P->dim, Pn = P->n_params;
+  set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+  for (int64_t i = 0; i < n; ++i) {
+    const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+    max_err[i] = fused ? mesh_max_err_lane<float, true>(P, u0 + i * d, p + i * Pn,
+                                                         h + i * P->max_steps, N)
+                       : mesh_max_err_lane<float, false>(P, u0 + i * d, p + i * Pn,
+                                                          h + i * P->max_steps, N);
+  }
+  return E_OK;
+}
+
+/* Starting step of the record for one lane (for checks against the textbook). */
+int orc_initial_step_f64(const orc_problem *P, const double *y0, const double *p, double *h0) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  double f0[MAXD];
+  rhs_f<double, false>(P->rhs, P->dim, y0, p, f0);
+  const int q = P->method == M_ROS2 ? 2 : 5;
+  *h0 = initial_step<double, false>(P->rhs, P->dim, y0, f0, p, P->atol, P->rtol, q);
+  return E_OK;
+}
+
+/* One right-hand-side evaluation and its products (for direct checks). */
+int orc_rhs_f64(int32_t kind, int32_t d, const double *y, const double *p, const double *v,
+                double *f, double *wy, double *gp, double *J) {
+  if (!rhs_shape_ok(kind, d, kind == R_LORENZ96 ? 1 : (kind == R_LINEAR ? 1 : 3)))
+    return E_INVAL;
+  rhs_f<double, false>(kind, d, y, p, f);
+  rhs_vjp_y<double, false>(kind, d, y, p, v, wy);
+  rhs_vjp_p_acc<double, false>(kind, d, y, p, v, gp);
+  if (J && d <= 3) rhs_jac<double, false>(kind, d, y, p, J);
+  return E_OK;
+}
+
+}  // extern "C"

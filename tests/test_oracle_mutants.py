@@ -1,0 +1,102 @@
+"""The oracle's pins are sharp enough to catch plausible mistakes.
+
+Each mutant below is a copy of ``oracle/oracle.cpp`` with one planted error
+(a dropped term, a flipped sign, a transposed operand, a wrong index, a
+mistyped tableau digit, a missing contraction, a wrong seed).  It is built on
+the CPU into a temporary library and the pin battery of
+``test_oracle_pins`` is run against it; at least one pin must fail.
+"""
+import os
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as W
+import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
+                   "oracle.cpp")
+
+MUTANTS = {
+    "drop_first_stage_adjoint": ("for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];",
+                                 "for (int c = 0; c < d; ++c) if (i > 0) lacc[c] = lacc[c] + Wv[i][c];"),
+    "lorenz_vjp_sign": ("w[2] = mac<F>(-b, v[2], (-y[0]) * v[1]);",
+                        "w[2] = mac<F>(b, v[2], (-y[0]) * v[1]);"),
+    "lorenz_vjp_index": ("w[1] = mac<F>(y[0], v[2], mac<F>(s, v[0], -v[1]));",
+                         "w[1] = mac<F>(y[1], v[2], mac<F>(s, v[0], -v[1]));"),
+    "lorenz_param_vjp": ("g[0] = mac<F>(y[1] - y[0], v[0], g[0]);",
+                         "g[0] = mac<F>(y[0] - y[1], v[0], g[0]);"),
+    "transposed_tableau_in_adjoint": ("if (tb.a[l][i] == 0.0) continue;\n        if (first) { acc = T(tb.a[l][i]) * Wv[l][c];",
+                                      "if (tb.a[l][i] == 0.0) continue;\n        if (first) { acc = T(tb.a[i][l]) * Wv[l][c];"),
+    "tsit5_digit": ("t.a[4][2] = 7.4955393428898365;", "t.a[4][2] = 7.4955393428988365;"),
+    "dopri5_weight": ("t.a[6][3] = 125.0 / 192.0;", "t.a[6][3] = 125.0 / 191.0;"),
+    "lu_transposed_solve": ("z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);\n    z[i] = z[i] / LU[i * d + i];",
+                            "z[i] = mac<F>(-LU[i * d + j], z[j], z[i]);\n    z[i] = z[i] / LU[i * d + i];"),
+    "ros2_no_jac_contraction": ("rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);", ""),
+    "ros2_wrong_weight": ("const T acc = mac<F>(T(0.5), s.k2[c], T(1.5) * s.k1[c]);",
+                          "const T acc = mac<F>(T(0.5), s.k2[c], T(1.0) * s.k1[c]);"),
+    "robertson_contraction_sign": ("gy[1] = mac<F>(-two_k2, Jb[4], gy[1]);",
+                                   "gy[1] = mac<F>(two_k2, Jb[4], gy[1]);"),
+    "lorenz96_vjp_index": ("const T vm1 = v[(j + d - 1) % d]", "const T vm1 = v[(j + d - 2) % d]"),
+    "mse_seed_factor": ("lam[c] = mac<F>(T(2.0 * scale), y[c] - aux[c], lam[c]);",
+                        "lam[c] = mac<F>(T(scale), y[c] - aux[c], lam[c]);"),
+    "save_seed_off_by_one": ("for (; s_hi >= 0 && sidx[s_hi] == k; --s_hi)",
+                             "for (; s_hi >= 0 && sidx[s_hi] == k + 1; --s_hi)"),
+    "controller_growth_after_reject": ("if (after_reject) fac = std::min(fac, T(1.0));", ""),
+    "error_norm_scale": ("sc[c] = mac<F>(rtol, std::max(absval(y[c]), absval(yn[c])), atol);",
+                         "sc[c] = mac<F>(rtol, absval(y[c]), atol);"),
+}
+
+
+def _battery():
+    out = []
+    for m in (W.TSIT5, W.DOPRI5):
+        out.append((pins.test_tableau_order_conditions, dict(method=m)))
+    out += [(pins.test_dopri5_rationals, {}), (pins.test_dopri5_stability_polynomial, {}),
+            (pins.test_page5_enzyme_fixed_step_tsit5, {})]
+    for m in (W.TSIT5, W.DOPRI5, W.ROS2):
+        out.append((pins.test_linear_decay_closed_form, dict(method=m, fused=False)))
+        out.append((pins.test_lorenz63_origin_linearisation, dict(method=m)))
+    for m in (W.TSIT5, W.DOPRI5):
+        out.append((pins.test_lorenz96_fixed_point, dict(method=m)))
+    out += [(pins.test_robertson_ros2_conservation, {}),
+            (pins.test_dopri5_record_matches_scipy_rk45, {}),
+            (pins.test_loss_values_match_their_definitions, {}),
+            (pins.test_rhs_vjp_against_dense_jacobian, {})]
+    for case in pins.CASES:
+        out.append((pins.test_adjoint_matches_dual_numbers, dict(case=case)))
+    for case in pins.CASES:
+        out.append((pins.test_adjoint_matches_finite_differences, dict(case=case)))
+    return out
+
+
+def _killed(orc):
+    for fn, kw in _battery():
+        try:
+            fn(orc, **kw)
+        except Exception:          # an assertion (or a numerical failure) kills it
+            return fn.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(orc, tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site of {name} not unique/found"
+    mutated = tmp_path / "oracle_mutant.cpp"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["g++", "-O1", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-fPIC",
+                    "-shared", "-w", "-o", str(lib), str(mutated)], check=True)
+    try:
+        orc._swap_library(str(lib))
+        killer = _killed(orc)
+    finally:
+        orc._swap_library(None)
+    assert killer is not None, f"no pin catches mutant {name}"
+
+
+def test_unmutated_oracle_passes_battery(orc):
+    assert _killed(orc) is None

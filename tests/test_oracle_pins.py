@@ -1,0 +1,532 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test names what fixes the expected value: order conditions of the
+published tableaux, closed forms of the replayed map on linear problems, the
+gradient values printed on the DiffEqGPU page (Enzyme section), SciPy's RK45
+(the same Dormand-Prince controller), dual-number forward mode, central finite
+differences on the frozen mesh, and invariants of the Robertson and Lorenz-96
+systems.  These run on the CPU only.
+"""
+import json
+import math
+import os
+from fractions import Fraction as Fr
+
+import numpy as np
+import pytest
+
+import workloads as W
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Tableaux
+# ---------------------------------------------------------------------------
+
+def _order_conditions(b, A, c, order):
+    """Residuals of the Butcher order conditions up to ``order`` (<= 5)."""
+    one = np.ones_like(c)
+    r = [b @ one - 1, b @ c - 1 / 2]
+    if order >= 3:
+        r += [b @ c**2 - 1 / 3, b @ A @ c - 1 / 6]
+    if order >= 4:
+        r += [b @ c**3 - 1 / 4, b @ (c * (A @ c)) - 1 / 8, b @ A @ c**2 - 1 / 12,
+              b @ A @ A @ c - 1 / 24]
+    if order >= 5:
+        r += [b @ c**4 - 1 / 5, b @ (c**2 * (A @ c)) - 1 / 10, b @ (c * (A @ c**2)) - 1 / 15,
+              b @ (c * (A @ A @ c)) - 1 / 30, b @ ((A @ c) ** 2) - 1 / 20,
+              b @ A @ c**3 - 1 / 20, b @ A @ (c * (A @ c)) - 1 / 40,
+              b @ A @ A @ c**2 - 1 / 60, b @ A @ A @ A @ c - 1 / 120]
+    return np.abs(np.array(r))
+
+
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5])
+def test_tableau_order_conditions(orc, method):
+    t = orc.tableau(method)
+    A, b, c, e = t["a"], t["b"], t["c"], t["e"]
+    assert np.allclose(A.sum(axis=1), c, rtol=0, atol=2e-15)      # row sums
+    assert np.array_equal(A[6], b) and b[6] == 0.0                  # first same as last
+    assert _order_conditions(b, A, c, 5).max() < 2e-15              # 5th order
+    bh = b - e
+    assert _order_conditions(bh, A, c, 4).max() < 3e-15             # embedded 4th order
+    assert _order_conditions(bh, A, c, 5).max() > 1e-5              # ... and not 5th
+    assert t["order"] == 5 and t["err_order"] == 4
+
+
+def test_dopri5_rationals(orc):
+    """Dormand-Prince coefficients are the published rationals, to the last bit."""
+    t = orc.tableau(W.DOPRI5)
+    exact = {
+        (1, 0): Fr(1, 5), (2, 0): Fr(3, 40), (2, 1): Fr(9, 40), (3, 0): Fr(44, 45),
+        (3, 1): Fr(-56, 15), (3, 2): Fr(32, 9), (4, 0): Fr(19372, 6561),
+        (4, 1): Fr(-25360, 2187), (4, 2): Fr(64448, 6561), (4, 3): Fr(-212, 729),
+        (5, 0): Fr(9017, 3168), (5, 1): Fr(-355, 33), (5, 2): Fr(46732, 5247),
+        (5, 3): Fr(49, 176), (5, 4): Fr(-5103, 18656), (6, 0): Fr(35, 384),
+        (6, 2): Fr(500, 1113), (6, 3): Fr(125, 192), (6, 4): Fr(-2187, 6784),
+        (6, 5): Fr(11, 84)}
+    for (i, j), v in exact.items():
+        assert t["a"][i, j] == float(v), (i, j)
+    bhat = [Fr(5179, 57600), 0, Fr(7571, 16695), Fr(393, 640), Fr(-92097, 339200),
+            Fr(187, 2100), Fr(1, 40)]
+    b = [exact.get((6, j), Fr(0)) for j in range(7)]
+    for j in range(7):
+        assert t["e"][j] == float(b[j] - bhat[j]), j
+    # exact order conditions in rationals
+    A = [[exact.get((i, j), Fr(0)) for j in range(7)] for i in range(7)]
+    c = [sum(row) for row in A]
+    assert sum(b) == 1 and sum(bi * ci for bi, ci in zip(b, c)) == Fr(1, 2)
+    assert sum(bi * ci**4 for bi, ci in zip(b, c)) == Fr(1, 5)
+
+
+def _stability_poly(t):
+    """Coefficients of R(z) = 1 + z b^T (I - zA)^{-1} 1 = sum_j (b^T A^{j-1} 1) z^j."""
+    A, b = t["a"], t["b"]
+    one = np.ones(7)
+    coef = [1.0]
+    v = one.copy()
+    for _ in range(7):
+        coef.append(b @ v)
+        v = A @ v
+    return np.array(coef)
+
+
+def test_dopri5_stability_polynomial(orc):
+    """Textbook: R(z) = sum_{j<=5} z^j/j! + z^6/600 for Dormand-Prince."""
+    coef = _stability_poly(orc.tableau(W.DOPRI5))
+    expect = [1 / math.factorial(j) for j in range(6)] + [1 / 600, 0.0]
+    assert np.allclose(coef, expect, rtol=1e-14, atol=1e-17)
+
+
+# ---------------------------------------------------------------------------
+# Pages' printed values
+# ---------------------------------------------------------------------------
+
+def test_page5_enzyme_fixed_step_tsit5(orc):
+    """Fixed-step Tsit5 gradient printed in the DiffEqGPU Enzyme example."""
+    g = json.load(open(os.path.join(GOLDEN, "diffeqgpu_enzyme_tsit5.json")))
+    pr = g["problem"]
+    n = len(g["p"])
+    N = pr["steps"]
+    prob = W.Problem(W.LINEAR, 1, 1, W.TSIT5, pr["t0"], pr["t1"], 1e-6, 1e-6, N)
+    mesh = {"h": np.full((n, N), pr["dt"]), "n_steps": np.full(n, N),
+            "save_idx": np.full((n, 1), N), "status": np.zeros(n)}
+    u0 = np.full((n, 1), pr["y0"])
+    p = np.array(g["p"])[:, None]
+    for fused in (False, True):
+        loss, gu0, gp = orc.replay_grad(prob, u0, p, mesh, W.COTANGENT,
+                                        aux=np.ones((n, 1, 1)), fused=fused)
+        assert np.allclose(gp[:, 0], g["dloss_dp"], rtol=0, atol=5e-15), gp[:, 0]
+        # the loss is the final state itself and its u0-gradient is R(z)^N
+        assert np.allclose(gu0[:, 0], loss, rtol=1e-15)
+    # the page's values fix the z^6 coefficient of Tsit5's stability polynomial
+    coef = _stability_poly(orc.tableau(W.TSIT5))
+    assert abs(coef[6] - 1.4328e-3) < 1e-6 and coef[7] == 0.0
+
+
+# ---------------------------------------------------------------------------
+# Closed forms on linear problems
+# ---------------------------------------------------------------------------
+
+def _R_erk(coef, z):
+    return sum(cj * z**j for j, cj in enumerate(coef))
+
+
+def _R_ros2(gamma, z):
+    w = 1.0 / (1.0 - gamma * z)
+    return 1 + 2 * z * w + 0.5 * z * z * w * w - z * w * w
+
+
+def _complex_step(fn, z):
+    eps = 1e-30
+    return (fn(z + 1j * eps)).imag / eps
+
+
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+@pytest.mark.parametrize("fused", [False, True])
+def test_linear_decay_closed_form(orc, method, fused):
+    """y' = -k y on an arbitrary mesh: y_N = y0 prod R(-k h_n); exact derivative
+    d y_N / dk from R'(z) (complex step on the closed form)."""
+    rng = np.random.default_rng(7)
+    N = 37
+    n = 4
+    ks = np.array([0.5, 3.0, 11.0, 0.01])
+    h = rng.uniform(0.01, 0.2, size=(n, N))
+    y0 = np.array([1.7, -0.3, 2.0, 1.0])
+    if method == W.ROS2:
+        g = orc.ros2_gamma()
+        assert g == 1.0 + 1.0 / math.sqrt(2.0)
+        assert abs(_R_ros2(g, -1e12)) < 1e-11            # L-stable: R(-inf) = 0
+        R = lambda z: _R_ros2(g, z)
+    else:
+        coef = _stability_poly(orc.tableau(method))
+        R = lambda z: _R_erk(coef, z)
+    prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, 1e-6, 1e-6, N)
+    mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
+            "status": np.zeros(n)}
+    p = -ks[:, None]
+    _, yN = orc.replay(prob, y0[:, None], p, mesh, fused=fused)
+    loss, gu0, gp = orc.replay_grad(prob, y0[:, None], p, mesh, W.COTANGENT,
+                                    aux=np.ones((n, 1, 1)), fused=fused)
+    for i in range(n):
+        z = -ks[i] * h[i]
+        Rz = np.array([R(zz) for zz in z])
+        prod = np.prod(Rz)
+        assert yN[i, 0] == pytest.approx(y0[i] * prod, rel=2e-14)
+        assert gu0[i, 0] == pytest.approx(prod, rel=2e-14)
+        dR = np.array([_complex_step(R, zz) for zz in z])
+        # d/dp of prod R(p h_n) with p = -k
+        dprod = prod * np.sum(h[i] * dR / Rz)
+        assert gp[i, 0] == pytest.approx(y0[i] * dprod, rel=2e-13, abs=1e-300)
+
+
+def _matrix_R(method, orc, Z):
+    I = np.eye(Z.shape[0])
+    if method == W.ROS2:
+        g = orc.ros2_gamma()
+        Wm = np.linalg.inv(I - g * Z)
+        return I + 2 * Z @ Wm + 0.5 * Z @ Z @ Wm @ Wm - Z @ Wm @ Wm
+    coef = _stability_poly(orc.tableau(method))
+    out = np.zeros_like(Z)
+    Zp = I.copy()
+    for cj in coef:
+        out = out + cj * Zp
+        Zp = Zp @ Z
+    return out
+
+
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+def test_lorenz63_origin_linearisation(orc, method):
+    """At the origin Lorenz-63 is a fixed point; the replay's Jacobian is the
+    product of R(h_n A) with A = [[-s, s, 0], [r, -1, 0], [0, 0, -b]].  A
+    cotangent w at the end must come back as (prod R)^T w."""
+    rng = np.random.default_rng(11)
+    N, n = 25, 3
+    h = rng.uniform(0.005, 0.05, size=(n, N))
+    p = np.array([[10.0, 28.0, 8 / 3], [6.0, 15.0, 1.5], [8.0, 22.0, 2.2]])
+    w = rng.standard_normal((n, 1, 3))
+    prob = W.Problem(W.LORENZ63, 3, 3, method, 0.0, 1.0, 1e-6, 1e-6, N)
+    mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
+            "status": np.zeros(n)}
+    u0 = np.zeros((n, 3))
+    loss, gu0, gp = orc.replay_grad(prob, u0, p, mesh, W.COTANGENT, aux=w)
+    for i in range(n):
+        s, r, b = p[i]
+        A = np.array([[-s, s, 0], [r, -1, 0], [0, 0, -b]])
+        M = np.eye(3)
+        for k in range(N):
+            M = _matrix_R(method, orc, h[i, k] * A) @ M
+        expect = M.T @ w[i, 0]
+        assert np.allclose(gu0[i], expect, rtol=1e-12, atol=1e-12 * np.abs(expect).max())
+        assert np.all(gp[i] == 0.0)
+
+
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5])
+def test_lorenz96_fixed_point(orc, method):
+    """x = F 1 is an exact fixed point of Lorenz-96 (f == 0 bitwise).  The
+    replay's Jacobian is prod R(h_n A) with the circulant linearisation A, and
+    d x_N / dF follows the linear inhomogeneous recursion
+    e_{n+1} = R(h A) e_n + h Phi(h A) 1, Phi(Z) = (R(Z) - I) Z^{-1}."""
+    d, N, n = 64, 20, 2
+    rng = np.random.default_rng(5)
+    F = np.array([8.0, 7.3])
+    h = rng.uniform(0.01, 0.05, size=(n, N))
+    u0 = F[:, None] * np.ones((n, d))
+    w = rng.standard_normal((n, 1, d))
+    prob = W.Problem(W.LORENZ96, d, 1, method, 0.0, 1.0, 1e-6, 1e-6, N)
+    mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
+            "status": np.zeros(n)}
+    _, yN = orc.replay(prob, u0, F[:, None], mesh)
+    assert np.array_equal(yN, u0)
+    loss, gu0, gp = orc.replay_grad(prob, u0, F[:, None], mesh, W.COTANGENT, aux=w)
+    coef = _stability_poly(orc.tableau(method))
+    I = np.eye(d)
+    for i in range(n):
+        A = np.zeros((d, d))
+        for r in range(d):
+            A[r, (r + 1) % d] += F[i]
+            A[r, (r - 2) % d] -= F[i]
+            A[r, (r - 1) % d] += 0.0     # x_{i+1} - x_{i-2} = 0 at the fixed point
+            A[r, r] -= 1.0
+        M = I.copy()
+        e = np.zeros(d)
+        for k in range(N):
+            Z = h[i, k] * A
+            Rm = np.zeros((d, d)); Phi = np.zeros((d, d)); Zp = I.copy()
+            for j, cj in enumerate(coef):
+                Rm += cj * Zp
+                if j >= 1:
+                    Phi += cj * (Zp @ np.linalg.inv(Z))
+                Zp = Zp @ Z
+            e = Rm @ e + h[i, k] * (Phi @ np.ones(d))
+            M = Rm @ M
+        assert np.allclose(gu0[i], M.T @ w[i, 0], rtol=1e-11, atol=1e-12)
+        assert gp[i, 0] == pytest.approx(w[i, 0] @ e, rel=1e-11)
+
+
+# ---------------------------------------------------------------------------
+# Invariants
+# ---------------------------------------------------------------------------
+
+def test_robertson_ros2_conservation(orc):
+    """1^T f = 0 for Robertson, so 1^T J = 0 and ROS2 keeps y1+y2+y3 fixed for
+    any k and h; the adjoint of the linear functional 1^T y_N is 1 for u0 and
+    0 for k."""
+    inp = W.make_inputs(4, 64)
+    prob = W.WORKLOADS[4].problem()
+    m = orc.record(prob, inp["u0"], inp["p"])
+    assert np.all(m["status"] == 0)
+    ys, yN = orc.replay(prob, inp["u0"], inp["p"], m)
+    assert np.allclose(yN.sum(1), inp["u0"].sum(1), rtol=0, atol=1e-13)
+    n = inp["u0"].shape[0]
+    loss, gu0, gp = orc.replay_grad(prob, inp["u0"], inp["p"], m, W.COTANGENT,
+                                    aux=np.ones((n, 1, 3)))
+    assert np.allclose(gu0, 1.0, rtol=0, atol=1e-11)
+    # scale of each k-gradient term: |dL/dk| would be O(y/k) for a generic functional
+    assert np.all(np.abs(gp * inp["p"]) < 1e-9)
+
+
+def test_record_equals_replay_bitwise(orc):
+    """The replay reproduces the recorded states bit for bit (both roundings)."""
+    for wid, n in [(1, 64), (2, 32), (3, 32), (4, 8), (5, 8)]:
+        w = W.WORKLOADS[wid]
+        inp = W.make_inputs(wid, n)
+        prob = w.problem()
+        for fused in (False, True):
+            m = orc.record(prob, inp["u0"], inp["p"], fused=fused)
+            assert np.all(m["status"] == 0)
+            ys, _ = orc.replay(prob, inp["u0"], inp["p"], m, fused=fused)
+            assert np.array_equal(ys, m["y_save"]), (wid, fused)
+
+
+def test_record_accepts_only_small_errors(orc):
+    """Re-evaluating every recorded step gives E <= 1 (the accept test)."""
+    for wid, n in [(1, 128), (3, 64), (4, 16)]:
+        w = W.WORKLOADS[wid]
+        inp = W.make_inputs(wid, n)
+        prob = w.problem()
+        m = orc.record(prob, inp["u0"], inp["p"])
+        E = orc.mesh_max_err(prob, inp["u0"], inp["p"], m)
+        assert np.all(E <= 1.0) and np.all(E > 0.01)
+
+
+def test_save_times_are_mesh_points(orc):
+    """Steps are clipped onto save times: the partial sums of h hit them."""
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(3, 64)
+    prob = w.problem()
+    u0 = inp["u0"].astype(np.float64); p = inp["p"].astype(np.float64)
+    m = orc.record(prob, u0, p)
+    for i in range(64):
+        cs = np.concatenate([[0.0], np.cumsum(m["h"][i])])
+        for s, ts in enumerate(prob.save_times):
+            assert cs[m["save_idx"][i, s]] == pytest.approx(ts, rel=1e-13)
+        assert m["save_idx"][i, -1] == m["n_steps"][i]
+
+
+def test_global_error_tracks_tolerance(orc):
+    """y' = -y on [0, 1]: the recorded solve's error at t=1 stays below the
+    tolerance scale and shrinks as the tolerance does."""
+    for method in (W.TSIT5, W.DOPRI5, W.ROS2):
+        errs = []
+        for tol in (1e-4, 1e-6, 1e-8):
+            prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, tol, tol, 100000)
+            m = orc.record(prob, np.ones((1, 1)), -np.ones((1, 1)))
+            err = abs(m["y_save"][0, 0, 0] - math.exp(-1.0))
+            errs.append(err)
+            assert err < 20 * tol, (method, tol, err)
+        assert errs[2] < errs[0]
+
+
+def test_status_codes(orc):
+    w = W.WORKLOADS[1]
+    inp = W.make_inputs(1, 4)
+    u0, p = inp["u0"], inp["p"].copy()
+    m = orc.record(w.problem(max_steps=3), u0, p)
+    assert np.all(m["status"] == orc.LANE_MAX_STEPS) and np.all(m["n_steps"] == 3)
+    p[1, 0] = np.nan
+    m = orc.record(w.problem(), u0, p)
+    assert m["status"][1] == orc.LANE_NONFINITE and m["n_steps"][1] == 0
+    assert np.all(m["status"][[0, 2, 3]] == 0)
+    # an overflowing right-hand side makes every error estimate non-finite:
+    # each attempt is rejected with the smallest factor until h underflows
+    m = orc.record(w.problem(), np.full((4, 3), 1e200), inp["p"])
+    assert np.all(m["status"] == orc.LANE_DT_UNDERFLOW) and np.all(m["n_steps"] == 0)
+    # a tolerance far below rounding cannot reach t1 within max_steps
+    m = orc.record(w.problem(rtol=1e-300, atol=1e-300), u0, inp["p"])
+    assert np.all(m["status"] != 0)
+    m = orc.record(w.problem(max_attempts=5), u0, inp["p"])
+    assert np.all(m["status"] == orc.LANE_MAX_ATTEMPTS) and np.all(m["n_attempts"] == 5)
+    # failed lanes give NaN gradients
+    m = orc.record(w.problem(max_steps=3), u0, inp["p"])
+    loss, gu0, gp = orc.replay_grad(w.problem(max_steps=3), u0, inp["p"], m)
+    assert np.all(np.isnan(gp)) and np.all(np.isnan(loss))
+
+
+# ---------------------------------------------------------------------------
+# Textbook / library routines
+# ---------------------------------------------------------------------------
+
+def _lorenz(p):
+    s, r, b = p
+    return lambda t, u: np.array([s * (u[1] - u[0]), u[0] * (r - u[2]) - u[1],
+                                  u[0] * u[1] - b * u[2]])
+
+
+def test_dopri5_record_matches_scipy_rk45(orc):
+    """SciPy's RK45 is Dormand-Prince with the same RMS error norm and
+    I-controller (safety 0.9, factors in [0.2, 10], no growth right after a
+    reject).  Given the same first step, the accepted steps coincide."""
+    from scipy.integrate import solve_ivp
+    inp = W.make_inputs(2, 6)
+    for i in range(6):
+        prob = W.Problem(W.LORENZ63, 3, 3, W.DOPRI5, 0.0, 2.0, 1e-8, 1e-8, 4096, dt0=1e-3)
+        m = orc.record(prob, inp["u0"][i:i + 1], inp["p"][i:i + 1])
+        sol = solve_ivp(_lorenz(inp["p"][i]), (0.0, 2.0), inp["u0"][i], method="RK45",
+                        rtol=1e-8, atol=1e-8, first_step=1e-3)
+        hs = np.diff(sol.t)
+        N = m["n_steps"][0]
+        assert N == len(hs)
+        assert np.allclose(m["h"][0, :N], hs, rtol=1e-8)
+        assert np.allclose(m["y_save"][0, 0], sol.y[:, -1], rtol=1e-6, atol=1e-8)
+
+
+def test_initial_step_matches_textbook(orc):
+    """Starting step of Hairer-Norsett-Wanner I.II.4 (SciPy's select_initial_step
+    implements the same algorithm), with the method order 5."""
+    from scipy.integrate._ivp.common import select_initial_step
+    inp = W.make_inputs(2, 8)
+    prob = W.WORKLOADS[2].problem()
+    for i in range(8):
+        f = _lorenz(inp["p"][i])
+        y0 = inp["u0"][i]
+        ref = select_initial_step(f, 0.0, y0, 10.0, np.inf, f(0.0, y0), 1, 5, 1e-8, 1e-8)
+        assert orc.initial_step(prob, y0, inp["p"][i]) == pytest.approx(ref, rel=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Adjoint vs forward mode and finite differences
+# ---------------------------------------------------------------------------
+
+def _cases():
+    # (problem, u0, p, loss, aux, scale)
+    out = []
+    inp = W.make_inputs(1, 6)
+    out.append(("lorenz63_tsit5", W.WORKLOADS[1].problem(), inp["u0"], inp["p"],
+                W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(2, 6)
+    out.append(("lorenz63_dopri5_saves", W.WORKLOADS[2].problem(t1=1.5, save_times=(0.5, 1.0, 1.5)),
+                inp["u0"], inp["p"], W.COTANGENT,
+                np.random.default_rng(1).standard_normal((6, 3, 3))))
+    inp = W.make_inputs(3, 6)
+    out.append(("lorenz63_mse", W.WORKLOADS[3].problem(t1=2.0, save_times=(0.5, 1.0, 2.0)),
+                inp["u0"].astype(np.float64), inp["p"].astype(np.float64), W.MSE_SAVE,
+                np.random.default_rng(2).standard_normal((6, 3, 3))))
+    inp = W.make_inputs(4, 4)
+    out.append(("robertson_ros2", W.WORKLOADS[4].problem(t1=30.0), inp["u0"], inp["p"],
+                W.SUMSQ_FINAL, None))
+    out.append(("robertson_tsit5", W.WORKLOADS[4].problem(t1=0.5, method=W.TSIT5, max_steps=8192),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(5, 3)
+    out.append(("lorenz96", W.WORKLOADS[5].problem(t1=0.5), inp["u0"], inp["p"],
+                W.SUMSQ_FINAL, None))
+    out.append(("lorenz96_dopri5", W.WORKLOADS[5].problem(t1=0.5, method=W.DOPRI5), inp["u0"],
+                inp["p"], W.COTANGENT, np.random.default_rng(3).standard_normal((3, 1, 64))))
+    out.append(("linear_ros2", W.Problem(W.LINEAR, 1, 1, W.ROS2, 0.0, 2.0, 1e-6, 1e-6, 20000),
+                np.array([[1.0], [2.0]]), np.array([[-0.7], [0.4]]), W.SUMSQ_FINAL, None))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_adjoint_matches_dual_numbers(orc, case):
+    """<grad, v> equals the forward-mode derivative along v (dot-product test)."""
+    name, prob, u0, p, lk, aux = case
+    m = orc.record(prob, u0, p)
+    assert np.all(m["status"] == 0)
+    loss, gu0, gp = orc.replay_grad(prob, u0, p, m, lk, aux=aux, scale=0.7)
+    rng = np.random.default_rng(4)
+    for _ in range(3):
+        du0 = rng.standard_normal(u0.shape)
+        dp = rng.standard_normal(p.shape) * p
+        l2, dl, _, _ = orc.replay_jvp(prob, u0, p, du0, dp, m, lk, aux=aux, scale=0.7)
+        assert np.allclose(l2, loss, rtol=1e-14)
+        adj = (gu0 * du0).sum(1) + (gp * dp).sum(1)
+        assert np.allclose(adj, dl, rtol=1e-11, atol=1e-11 * np.abs(dl).max()), name
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_adjoint_matches_finite_differences(orc, case):
+    """Central differences of the replayed loss on the frozen mesh."""
+    name, prob, u0, p, lk, aux = case
+    m = orc.record(prob, u0, p)
+    loss, gu0, gp = orc.replay_grad(prob, u0, p, m, lk, aux=aux)
+    for q in range(p.shape[1]):
+        eps = 1e-6 * np.abs(p[:, q])
+        pp = p.copy(); pp[:, q] += eps
+        pm = p.copy(); pm[:, q] -= eps
+        lp = orc.replay_grad(prob, u0, pp, m, lk, aux=aux)[0]
+        lm = orc.replay_grad(prob, u0, pm, m, lk, aux=aux)[0]
+        fd = (lp - lm) / (2 * eps)
+        assert np.allclose(gp[:, q], fd, rtol=2e-5, atol=1e-6 * np.abs(fd).max()), (name, q)
+    for c in range(min(u0.shape[1], 4)):
+        eps = 1e-6
+        up = u0.copy(); up[:, c] += eps
+        um = u0.copy(); um[:, c] -= eps
+        fd = (orc.replay_grad(prob, up, p, m, lk, aux=aux)[0] -
+              orc.replay_grad(prob, um, p, m, lk, aux=aux)[0]) / (2 * eps)
+        assert np.allclose(gu0[:, c], fd, rtol=2e-5, atol=1e-6 * np.abs(fd).max()), (name, c)
+
+
+def test_loss_values_match_their_definitions(orc):
+    """Loss kinds against their formulas evaluated on the replayed states."""
+    prob = W.WORKLOADS[3].problem(t1=2.0, save_times=(0.5, 1.0, 2.0))
+    inp = W.make_inputs(3, 8)
+    u0 = inp["u0"].astype(np.float64); p = inp["p"].astype(np.float64)
+    m = orc.record(prob, u0, p)
+    ys, yN = orc.replay(prob, u0, p, m)
+    tg = np.random.default_rng(0).standard_normal((8, 3, 3))
+    L = orc.replay_grad(prob, u0, p, m, W.MSE_SAVE, aux=tg, scale=0.25)[0]
+    assert np.allclose(L, 0.25 * ((ys - tg) ** 2).sum((1, 2)), rtol=1e-13)
+    L = orc.replay_grad(prob, u0, p, m, W.COTANGENT, aux=tg, scale=2.0)[0]
+    assert np.allclose(L, 2.0 * (ys * tg).sum((1, 2)), rtol=1e-12)
+    L = orc.replay_grad(prob, u0, p, m, W.SUMSQ_FINAL, scale=3.0)[0]
+    assert np.allclose(L, 3.0 * (yN**2).sum(1), rtol=1e-13)
+
+
+def test_rhs_vjp_against_dense_jacobian(orc):
+    """J^T v and J_p^T v of each system against finite-difference Jacobians."""
+    rng = np.random.default_rng(9)
+    for kind, d, P in [(W.LORENZ63, 3, 3), (W.ROBERTSON, 3, 3), (W.LORENZ96, 8, 1),
+                       (W.LINEAR, 1, 1)]:
+        y = rng.standard_normal(d)
+        p = rng.uniform(0.5, 2.0, P)
+        v = rng.standard_normal(d)
+        f, wy, gp, J = orc.rhs(kind, y, p, v)
+        Jfd = np.zeros((d, d)); Jpfd = np.zeros((d, P))
+        for j in range(d):
+            e = np.zeros(d); e[j] = 1e-6
+            Jfd[:, j] = (orc.rhs(kind, y + e, p, v)[0] - orc.rhs(kind, y - e, p, v)[0]) / 2e-6
+        for q in range(P):
+            e = np.zeros(P); e[q] = 1e-6
+            Jpfd[:, q] = (orc.rhs(kind, y, p + e, v)[0] - orc.rhs(kind, y, p - e, v)[0]) / 2e-6
+        assert np.allclose(wy, Jfd.T @ v, rtol=1e-7, atol=1e-8)
+        assert np.allclose(gp, Jpfd.T @ v, rtol=1e-7, atol=1e-8)
+        if J is not None:
+            assert np.allclose(J, Jfd, rtol=1e-7, atol=1e-8)
+
+
+def test_fp32_oracle_tracks_fp64(orc):
+    """The FP32 oracle stays close to the FP64 oracle on its own mesh."""
+    w = W.WORKLOADS[3]
+    inp = W.make_inputs(3, 32)
+    prob = w.problem(t1=1.0, save_times=(0.5, 1.0))
+    m32 = orc.record(prob, inp["u0"], inp["p"])
+    m64 = {k: (v.astype(np.float64) if v is not None and v.dtype == np.float32 else v)
+           for k, v in m32.items()}
+    l32, g32, p32 = orc.replay_grad(prob, inp["u0"], inp["p"], m32)
+    l64, g64, p64 = orc.replay_grad(prob, inp["u0"].astype(np.float64),
+                                    inp["p"].astype(np.float64), m64)
+    assert np.allclose(p32, p64, rtol=1e-3, atol=1e-3 * np.abs(p64).max())
