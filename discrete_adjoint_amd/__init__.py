@@ -1,0 +1,303 @@
+"""MI355X record-and-replay discrete adjoint for ODE ensembles.
+
+Thin Python binding of ``libdadj.so`` (declared in ``include/dadj.h``): it
+checks and marshals torch tensors (device pointers, the current HIP stream)
+and calls the C ABI.  Every step of the computation runs in the library's HIP
+kernels; there is no fallback.  Importing fails loudly if the library has not
+been built (``python -m discrete_adjoint_amd._build`` or
+``__graft_entry__.build()``).
+
+Layout: per-trajectory tensors are component-major, shape [C, n] (trajectory
+index last and contiguous): u0 [d, n], p [P, n], y_save [S, d, n], grad_u0
+[d, n], grad_p [P, n], with S = max(1, len(problem.save_times)).  The mesh is
+h [max_steps, n], n_steps [n], save_idx [S, n], status [n], perm [n] or None.
+
+The problem description is ``workloads.Problem`` (or any object with the same
+fields) plus a dtype taken from the tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdadj.so")
+
+DA_F64, DA_F32 = 0, 1
+TSIT5, DOPRI5, ROS2 = 0, 1, 2
+LINEAR, LORENZ63, ROBERTSON, LORENZ96 = 0, 1, 2, 3
+SUMSQ_FINAL, MSE_SAVE, COTANGENT = 0, 1, 2
+LANE_OK, LANE_MAX_STEPS, LANE_DT_UNDERFLOW, LANE_NONFINITE, LANE_MAX_ATTEMPTS = range(5)
+DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EHIP, DA_EWORKSPACE = 0, -1, -2, -3, -4
+MAX_SAVES = 128
+
+EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_sort_workspace", "da_mesh_sort",
+           "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
+           "da_last_error", "da_version")
+
+
+class DadjError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"dadj error {code}: {msg}")
+        self.code = code
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [
+        ("rhs", ctypes.c_int32), ("dim", ctypes.c_int32), ("n_params", ctypes.c_int32),
+        ("method", ctypes.c_int32), ("dtype", ctypes.c_int32),
+        ("t0", ctypes.c_double), ("t1", ctypes.c_double),
+        ("rtol", ctypes.c_double), ("atol", ctypes.c_double), ("dt0", ctypes.c_double),
+        ("max_steps", ctypes.c_int32), ("max_attempts", ctypes.c_int32),
+        ("n_save", ctypes.c_int32), ("save_times", ctypes.POINTER(ctypes.c_double)),
+        ("safety", ctypes.c_double), ("fac_min", ctypes.c_double), ("fac_max", ctypes.c_double),
+    ]
+
+
+class _Mesh(ctypes.Structure):
+    _fields_ = [("h", ctypes.c_void_p), ("n_steps", ctypes.c_void_p),
+                ("save_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
+                ("perm", ctypes.c_void_p)]
+
+
+class _Loss(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int32), ("aux", ctypes.c_void_p), ("scale", ctypes.c_double)]
+
+
+def _load_library() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
+                          "(python -m discrete_adjoint_amd._build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    P = ctypes.POINTER(_Problem)
+    M = ctypes.POINTER(_Mesh)
+    lib.da_record.argtypes = [P, i64, vp, vp, M, vp, vp]
+    lib.da_solve_fwd.argtypes = [P, i64, vp, vp, vp, vp, vp, vp]
+    lib.da_mesh_sort_workspace.argtypes = [P, i64]
+    lib.da_mesh_sort_workspace.restype = ctypes.c_size_t
+    lib.da_mesh_sort.argtypes = [P, i64, M, M, vp, ctypes.c_size_t, vp]
+    lib.da_mesh_max_steps.argtypes = [i64, M, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.da_replay_fwd.argtypes = [P, i64, vp, vp, M, vp, vp]
+    lib.da_replay_grad_workspace.argtypes = [P, i64, i32]
+    lib.da_replay_grad_workspace.restype = ctypes.c_size_t
+    lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
+                                   ctypes.c_size_t, vp]
+    lib.da_last_error.restype = ctypes.c_char_p
+    for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps",
+                 "da_replay_fwd", "da_replay_grad", "da_version"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_lib = _load_library()
+
+
+def library() -> ctypes.CDLL:
+    return _lib
+
+
+def version() -> int:
+    return _lib.da_version()
+
+
+def last_error() -> str:
+    return _lib.da_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != DA_OK:
+        raise DadjError(rc, last_error())
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float64:
+        return DA_F64
+    if dt == torch.float32:
+        return DA_F32
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def cproblem(prob, dtype) -> tuple:
+    """ctypes problem struct (and the array that backs save_times)."""
+    st = (ctypes.c_double * max(1, len(prob.save_times)))(*prob.save_times)
+    P = _Problem(prob.rhs, prob.dim, prob.n_params, prob.method, _dtype_code(dtype),
+                 prob.t0, prob.t1, prob.rtol, prob.atol, prob.dt0, prob.max_steps,
+                 prob.max_attempts, len(prob.save_times),
+                 ctypes.cast(st, ctypes.POINTER(ctypes.c_double)) if len(prob.save_times) else None,
+                 prob.safety, prob.fac_min, prob.fac_max)
+    return P, st
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, shape, dtype, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclasses.dataclass
+class Mesh:
+    """The record: step sizes [max_steps, n], n_steps [n], save_idx [S, n],
+    status [n] and the slot -> trajectory permutation [n] (None = identity)."""
+    h: torch.Tensor
+    n_steps: torch.Tensor
+    save_idx: torch.Tensor
+    status: torch.Tensor
+    perm: Optional[torch.Tensor] = None
+
+    @property
+    def n(self) -> int:
+        return self.n_steps.shape[0]
+
+    def c(self) -> _Mesh:
+        return _Mesh(self.h.data_ptr(), self.n_steps.data_ptr(), self.save_idx.data_ptr(),
+                     self.status.data_ptr(), None if self.perm is None else self.perm.data_ptr())
+
+
+def empty_mesh(prob, n: int, dtype, device="cuda", with_perm: bool = False) -> Mesh:
+    S = max(1, len(prob.save_times))
+    return Mesh(torch.empty((prob.max_steps, n), dtype=dtype, device=device),
+                torch.empty(n, dtype=torch.int32, device=device),
+                torch.empty((S, n), dtype=torch.int32, device=device),
+                torch.empty(n, dtype=torch.int32, device=device),
+                torch.empty(n, dtype=torch.int32, device=device) if with_perm else None)
+
+
+def _inputs(prob, u0: torch.Tensor, p: torch.Tensor):
+    n = u0.shape[-1]
+    _need(u0, (prob.dim, n), u0.dtype, "u0")
+    _need(p, (prob.n_params, n), u0.dtype, "p")
+    return n, u0.dtype
+
+
+def record(prob, u0, p, mesh: Optional[Mesh] = None, save: bool = True, stream=None):
+    """Adaptive solve per trajectory; returns (mesh, y_save or None)."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    if mesh is None:
+        mesh = empty_mesh(prob, n, dt, u0.device)
+    ys = torch.empty((S, prob.dim, n), dtype=dt, device=u0.device) if save else None
+    P, keep = cproblem(prob, dt)
+    cm = mesh.c()
+    _check(_lib.da_record(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm), _ptr(ys),
+                          _stream(stream)))
+    return mesh, ys
+
+
+def solve_fwd(prob, u0, p, stream=None):
+    """Forward-only adaptive solve: (y_save [S, d, n], n_steps [n], status [n])."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    ys = torch.empty((S, prob.dim, n), dtype=dt, device=u0.device)
+    ns = torch.empty(n, dtype=torch.int32, device=u0.device)
+    st = torch.empty(n, dtype=torch.int32, device=u0.device)
+    P, keep = cproblem(prob, dt)
+    _check(_lib.da_solve_fwd(ctypes.byref(P), n, _ptr(u0), _ptr(p), _ptr(ys), _ptr(ns), _ptr(st),
+                             _stream(stream)))
+    return ys, ns, st
+
+
+def mesh_sort_workspace(prob, n: int, dtype=torch.float64) -> int:
+    P, keep = cproblem(prob, dtype)
+    return int(_lib.da_mesh_sort_workspace(ctypes.byref(P), n))
+
+
+def mesh_sort(prob, mesh: Mesh, out: Optional[Mesh] = None, workspace=None, stream=None) -> Mesh:
+    """Mesh with slots reordered by decreasing step count (and its permutation)."""
+    n = mesh.n
+    dt = mesh.h.dtype
+    if out is None:
+        out = empty_mesh(prob, n, dt, mesh.h.device, with_perm=True)
+    need = mesh_sort_workspace(prob, n, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=mesh.h.device)
+    P, keep = cproblem(prob, dt)
+    ci, co = mesh.c(), out.c()
+    _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(ci), ctypes.byref(co),
+                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out
+
+
+def mesh_max_steps(mesh: Mesh, stream=None) -> int:
+    out = ctypes.c_int32(0)
+    cm = mesh.c()
+    _check(_lib.da_mesh_max_steps(mesh.n, ctypes.byref(cm), ctypes.byref(out), _stream(stream)))
+    return int(out.value)
+
+
+def replay_fwd(prob, u0, p, mesh: Mesh, stream=None) -> torch.Tensor:
+    """Fixed-step replay; returns y_save [S, d, n] (trajectory order)."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    ys = torch.empty((S, prob.dim, n), dtype=dt, device=u0.device)
+    P, keep = cproblem(prob, dt)
+    cm = mesh.c()
+    _check(_lib.da_replay_fwd(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm), _ptr(ys),
+                              _stream(stream)))
+    return ys
+
+
+def replay_grad_workspace(prob, n: int, max_n_steps: int, dtype=torch.float64) -> int:
+    P, keep = cproblem(prob, dtype)
+    return int(_lib.da_replay_grad_workspace(ctypes.byref(P), n, max_n_steps))
+
+
+class ReplayGrad:
+    """Reusable replay-gradient call: holds outputs and workspace so that
+    repeated passes against one record allocate nothing."""
+
+    def __init__(self, prob, u0, p, mesh: Mesh, loss_kind: int = SUMSQ_FINAL, aux=None,
+                 scale: float = 1.0, max_n_steps: Optional[int] = None,
+                 ws_bytes: Optional[int] = None):
+        n, dt = _inputs(prob, u0, p)
+        S = max(1, len(prob.save_times))
+        if aux is not None:
+            _need(aux, (S, prob.dim, n), dt, "aux")
+        self.prob, self.u0, self.p, self.mesh, self.aux = prob, u0, p, mesh, aux
+        self.n = n
+        self.max_n_steps = mesh_max_steps(mesh) if max_n_steps is None else int(max_n_steps)
+        need = replay_grad_workspace(prob, n, self.max_n_steps, dt)
+        nb = need if ws_bytes is None else int(ws_bytes)
+        self.ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=u0.device)
+        self.loss = torch.empty(n, dtype=dt, device=u0.device)
+        self.grad_u0 = torch.empty((prob.dim, n), dtype=dt, device=u0.device)
+        self.grad_p = torch.empty((prob.n_params, n), dtype=dt, device=u0.device)
+        self._P, self._keep = cproblem(prob, dt)
+        self._cm = mesh.c()
+        self._loss = _Loss(loss_kind, None if aux is None else aux.data_ptr(), scale)
+
+    def __call__(self, stream=None):
+        _check(_lib.da_replay_grad(ctypes.byref(self._P), self.n, _ptr(self.u0), _ptr(self.p),
+                                   ctypes.byref(self._cm), ctypes.byref(self._loss),
+                                   _ptr(self.loss), _ptr(self.grad_u0), _ptr(self.grad_p),
+                                   self.max_n_steps, _ptr(self.ws), self.ws.numel(),
+                                   _stream(stream)))
+        return self.loss, self.grad_u0, self.grad_p
+
+
+def replay_grad(prob, u0, p, mesh: Mesh, loss_kind: int = SUMSQ_FINAL, aux=None,
+                scale: float = 1.0, max_n_steps: Optional[int] = None,
+                ws_bytes: Optional[int] = None, stream=None):
+    """Replay + reverse sweep: (loss [n], grad_u0 [d, n], grad_p [P, n])."""
+    call = ReplayGrad(prob, u0, p, mesh, loss_kind, aux, scale, max_n_steps, ws_bytes)
+    return call(stream)

@@ -1,0 +1,307 @@
+// C ABI of libdadj: argument checks, defaults, dispatch and error reporting.
+// The operations and their sources are described in include/dadj.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "dadj.h"
+#include "dadj_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DA_OK;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DA_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool shape_ok(int rhs, int d, int P) {
+  switch (rhs) {
+    case DA_RHS_LINEAR: return d == 1 && P == 1;
+    case DA_RHS_LORENZ63: return d == 3 && P == 3;
+    case DA_RHS_ROBERTSON: return d == 3 && P == 3;
+    case DA_RHS_LORENZ96: return d >= 4 && d <= 64 && P == 1;
+  }
+  return false;
+}
+
+size_t dsize(int dtype) { return dtype == DA_F64 ? 8 : 4; }
+
+// Validates the problem and resolves defaults.
+int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::SaveTimes *st) {
+  if (!pb) return fail(DA_EINVAL, "problem is NULL");
+  if (n < 0 || n > (int64_t)0x7fffffff) return fail(DA_EINVAL, "n = %lld out of range", (long long)n);
+  if (pb->dtype != DA_F64 && pb->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", pb->dtype);
+  if (pb->method < DA_TSIT5 || pb->method > DA_ROS2)
+    return fail(DA_EINVAL, "bad method %d", pb->method);
+  if (pb->rhs < DA_RHS_LINEAR || pb->rhs > DA_RHS_LORENZ96)
+    return fail(DA_EINVAL, "bad rhs %d", pb->rhs);
+  if (!shape_ok(pb->rhs, pb->dim, pb->n_params))
+    return fail(DA_EINVAL, "rhs %d does not take dim=%d, n_params=%d", pb->rhs, pb->dim,
+                pb->n_params);
+  if (pb->rhs == DA_RHS_LORENZ96)
+    return fail(DA_EUNSUPPORTED, "LORENZ96 is not available in this build");
+  if (!(isfinite(pb->t0) && isfinite(pb->t1) && pb->t1 > pb->t0))
+    return fail(DA_EINVAL, "need finite t0 < t1");
+  if (!(pb->rtol >= 0) || !(pb->atol >= 0) || !(pb->rtol + pb->atol > 0) || !isfinite(pb->rtol) ||
+      !isfinite(pb->atol))
+    return fail(DA_EINVAL, "tolerances must be finite, >= 0 and not both 0");
+  if (pb->max_steps < 1) return fail(DA_EINVAL, "max_steps must be >= 1");
+  if (pb->max_steps > (1 << 24)) return fail(DA_EINVAL, "max_steps above 2^24");
+  if (pb->n_save < 0 || pb->n_save > DA_MAX_SAVES)
+    return fail(DA_EINVAL, "n_save must be in [0, %d]", DA_MAX_SAVES);
+  if (pb->n_save > 0 && !pb->save_times) return fail(DA_EINVAL, "save_times is NULL");
+  double prev = pb->t0;
+  for (int s = 0; s < pb->n_save; ++s) {
+    const double ts = pb->save_times[s];
+    if (!(ts > prev) || ts > pb->t1)
+      return fail(DA_EINVAL, "save_times must increase strictly within (t0, t1]");
+    prev = ts;
+  }
+  if (!(pb->safety >= 0 && pb->fac_min >= 0 && pb->fac_max >= 0) || pb->max_attempts < 0)
+    return fail(DA_EINVAL, "negative controller option");
+  pr.rhs = pb->rhs;
+  pr.dim = pb->dim;
+  pr.n_params = pb->n_params;
+  pr.method = pb->method;
+  pr.dtype = pb->dtype;
+  pr.max_steps = pb->max_steps;
+  pr.max_attempts = pb->max_attempts > 0 ? pb->max_attempts : 4 * pb->max_steps;
+  pr.n_save = pb->n_save;
+  pr.S = pb->n_save > 0 ? pb->n_save : 1;
+  pr.t0 = pb->t0;
+  pr.t1 = pb->t1;
+  pr.rtol = pb->rtol;
+  pr.atol = pb->atol;
+  pr.dt0 = pb->dt0;
+  pr.safety = pb->safety > 0 ? pb->safety : 0.9;
+  pr.fac_min = pb->fac_min > 0 ? pb->fac_min : 0.2;
+  pr.fac_max = pb->fac_max > 0 ? pb->fac_max : 10.0;
+  if (st) {
+    memset(st, 0, sizeof *st);
+    for (int s = 0; s < pb->n_save; ++s) st->t[s] = pb->save_times[s];
+  }
+  return DA_OK;
+}
+
+int check_mesh(const da_mesh *m, bool need_status) {
+  if (!m) return fail(DA_EINVAL, "mesh is NULL");
+  if (!m->h || !m->n_steps || !m->save_idx || (need_status && !m->status))
+    return fail(DA_EINVAL, "mesh arrays must not be NULL");
+  return DA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int da_version(void) { return 100; }
+
+const char *da_last_error(void) { return g_err; }
+
+int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, da_mesh *mesh,
+              void *y_save, void *stream) {
+  dadj::ProbArgs pr;
+  dadj::SaveTimes st;
+  int rc = check_problem(prob, n, pr, &st);
+  if (rc) return rc;
+  if ((rc = check_mesh(mesh, true))) return rc;
+  if (mesh->perm) return fail(DA_EINVAL, "da_record writes trajectory order: mesh->perm must be NULL");
+  if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
+  if (n == 0) return ok();
+  dadj::RecordArgs a;
+  a.pr = pr;
+  a.n = n;
+  a.u0 = u0;
+  a.p = p;
+  a.h = mesh->h;
+  a.nsteps = mesh->n_steps;
+  a.sidx = mesh->save_idx;
+  a.status = mesh->status;
+  a.y_save = y_save;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_record(a, st, s)
+                                            : dadj::launch_erk_record(a, st, s);
+  if (e != hipSuccess) return hip_fail(e, "record launch");
+  return ok();
+}
+
+int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p, void *y_save,
+                 int32_t *n_steps, int32_t *status, void *stream) {
+  dadj::ProbArgs pr;
+  dadj::SaveTimes st;
+  int rc = check_problem(prob, n, pr, &st);
+  if (rc) return rc;
+  if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
+  if (n == 0) return ok();
+  dadj::RecordArgs a;
+  a.pr = pr;
+  a.n = n;
+  a.u0 = u0;
+  a.p = p;
+  a.h = nullptr;
+  a.nsteps = n_steps;
+  a.sidx = nullptr;
+  a.status = status;
+  a.y_save = y_save;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_record(a, st, s)
+                                            : dadj::launch_erk_record(a, st, s);
+  if (e != hipSuccess) return hip_fail(e, "solve_fwd launch");
+  return ok();
+}
+
+size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n) {
+  if (!prob || n <= 0) return 0;
+  return dadj::sort_workspace_bytes(n, prob->max_steps);
+}
+
+int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *out,
+                 void *workspace, size_t ws_bytes, void *stream) {
+  dadj::ProbArgs pr;
+  int rc = check_problem(prob, n, pr, nullptr);
+  if (rc) return rc;
+  if ((rc = check_mesh(in, true))) return rc;
+  if ((rc = check_mesh(out, true))) return rc;
+  if (!out->perm) return fail(DA_EINVAL, "out->perm must not be NULL");
+  if (out->h == in->h || out->n_steps == in->n_steps || out->save_idx == in->save_idx ||
+      out->status == in->status || (in->perm && out->perm == in->perm))
+    return fail(DA_EINVAL, "out must not alias in");
+  if (n == 0) return ok();
+  const size_t need = dadj::sort_workspace_bytes(n, pr.max_steps);
+  if (!workspace || ws_bytes < need)
+    return fail(DA_EWORKSPACE, "mesh sort needs %zu bytes of workspace, got %zu", need, ws_bytes);
+  da_mesh o = *out;
+  const hipError_t e = dadj::launch_mesh_sort(pr, n, *in, o, workspace, ws_bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mesh sort launch");
+  return ok();
+}
+
+int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *stream) {
+  if (!mesh || !mesh->n_steps || !host_max) return fail(DA_EINVAL, "NULL argument");
+  if (n < 0) return fail(DA_EINVAL, "n < 0");
+  if (n == 0) {
+    *host_max = 0;
+    return ok();
+  }
+  hipStream_t s = (hipStream_t)stream;
+  int32_t *d = nullptr;
+  hipError_t e = hipMalloc((void **)&d, sizeof(int32_t));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc");
+  e = dadj::launch_max_steps(n, mesh->n_steps, d, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_max, d, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  const hipError_t e2 = hipFree(d);
+  if (e != hipSuccess) return hip_fail(e, "max steps");
+  if (e2 != hipSuccess) return hip_fail(e2, "hipFree");
+  return ok();
+}
+
+int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                  const da_mesh *mesh, void *y_save, void *stream) {
+  dadj::ProbArgs pr;
+  int rc = check_problem(prob, n, pr, nullptr);
+  if (rc) return rc;
+  if ((rc = check_mesh(mesh, false))) return rc;
+  if (n > 0 && (!u0 || !p || !y_save)) return fail(DA_EINVAL, "u0, p and y_save must not be NULL");
+  if (n == 0) return ok();
+  dadj::ReplayArgs a;
+  memset(&a, 0, sizeof a);
+  a.pr = pr;
+  a.n = n;
+  a.u0 = u0;
+  a.p = p;
+  a.h = mesh->h;
+  a.nsteps = mesh->n_steps;
+  a.sidx = mesh->save_idx;
+  a.status = mesh->status;
+  a.perm = mesh->perm;
+  a.y_save = y_save;
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_replay_fwd(a, s)
+                                            : dadj::launch_erk_replay_fwd(a, s);
+  if (e != hipSuccess) return hip_fail(e, "replay_fwd launch");
+  return ok();
+}
+
+size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps) {
+  if (!prob || n <= 0 || max_n_steps <= 0) return 0;
+  return (size_t)n * (size_t)max_n_steps * (size_t)prob->dim * dsize(prob->dtype);
+}
+
+int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                   void *grad_p, int32_t max_n_steps, void *workspace, size_t ws_bytes,
+                   void *stream) {
+  dadj::ProbArgs pr;
+  int rc = check_problem(prob, n, pr, nullptr);
+  if (rc) return rc;
+  if ((rc = check_mesh(mesh, true))) return rc;
+  if (!loss) return fail(DA_EINVAL, "loss is NULL");
+  if (loss->kind < DA_LOSS_SUMSQ_FINAL || loss->kind > DA_LOSS_COTANGENT)
+    return fail(DA_EINVAL, "bad loss kind %d", loss->kind);
+  if (loss->kind != DA_LOSS_SUMSQ_FINAL && !loss->aux)
+    return fail(DA_EINVAL, "loss kind %d needs aux", loss->kind);
+  if (!isfinite(loss->scale)) return fail(DA_EINVAL, "loss scale must be finite");
+  if (max_n_steps < 0 || max_n_steps > pr.max_steps)
+    return fail(DA_EINVAL, "max_n_steps must be in [0, max_steps]");
+  if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
+  if (n == 0) return ok();
+  const size_t per_lane = (size_t)max_n_steps * pr.dim * dsize(pr.dtype);
+  int64_t C = n;
+  if (per_lane > 0) {
+    if (!workspace) return fail(DA_EWORKSPACE, "workspace is NULL");
+    const size_t fit = ws_bytes / per_lane;
+    if (fit < (size_t)n) {
+      C = (int64_t)(fit / dadj::BLOCK) * dadj::BLOCK;
+      if (C < dadj::BLOCK)
+        return fail(DA_EWORKSPACE, "workspace %zu bytes holds fewer than %d trajectories", ws_bytes,
+                    dadj::BLOCK);
+    }
+  }
+  dadj::ReplayArgs a;
+  memset(&a, 0, sizeof a);
+  a.pr = pr;
+  a.n = n;
+  a.u0 = u0;
+  a.p = p;
+  a.h = mesh->h;
+  a.nsteps = mesh->n_steps;
+  a.sidx = mesh->save_idx;
+  a.status = mesh->status;
+  a.perm = mesh->perm;
+  a.loss_kind = loss->kind;
+  a.aux = loss->aux;
+  a.scale = loss->scale;
+  a.loss_out = loss_out;
+  a.gu0 = grad_u0;
+  a.gp = grad_p;
+  a.ws = workspace;
+  a.ws_lanes = C;
+  a.max_n_steps = max_n_steps;
+  hipStream_t s = (hipStream_t)stream;
+  for (int64_t slot0 = 0; slot0 < n; slot0 += C) {
+    a.slot0 = slot0;
+    a.nslots = (n - slot0) < C ? (n - slot0) : C;
+    const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_replay_grad(a, s)
+                                              : dadj::launch_erk_replay_grad(a, s);
+    if (e != hipSuccess) return hip_fail(e, "replay_grad launch");
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,260 @@
+// Device building blocks of libdadj: multiply-add, wave64 helpers, the
+// explicit Runge-Kutta tableaux and the built-in right-hand sides.
+//
+// Arithmetic schedule.  Every sum of products is a chain "first product, then
+// fused multiply-adds", evaluated left to right in the order written below,
+// and the sources are built with -ffp-contract=off so that no other operation
+// is fused.  The order is fixed so that results are reproducible and can be
+// compared element by element with an independent CPU evaluation of the same
+// formulas.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dadj {
+
+// ---------------------------------------------------------------------------
+// scalars
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double mac(double a, double b, double c) { return __builtin_fma(a, b, c); }
+__device__ __forceinline__ float mac(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
+
+__device__ __forceinline__ bool finite(double x) { return __builtin_isfinite(x); }
+__device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
+
+template <class T> __device__ __forceinline__ T nanv() { return T(__builtin_nan("")); }
+
+// Largest value of x over the active lanes of the wavefront, broadcast to all.
+__device__ __forceinline__ int wave_max(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int o = __shfl_xor(x, off, 64);
+    x = o > x ? o : x;
+  }
+  return __builtin_amdgcn_readfirstlane(x);
+}
+
+// ---------------------------------------------------------------------------
+// Explicit 7-stage first-same-as-last tableaux.  Row 6 of A equals b and
+// b[6] = 0, so the 7th stage state is the propagated 5th-order solution and
+// only its right-hand side (for the error estimate) is extra.
+// ---------------------------------------------------------------------------
+struct Tsit5Tab {
+  // Ch. Tsitouras, "Runge-Kutta pairs of order 5(4) satisfying only the first
+  // column simplifying assumption", Comput. Math. Appl. 62 (2011) 770-775.
+  static constexpr int order = 5, err_order = 4;
+  static constexpr double a[7][7] = {
+      {0, 0, 0, 0, 0, 0, 0},
+      {0.161, 0, 0, 0, 0, 0, 0},
+      {-0.008480655492356989, 0.335480655492357, 0, 0, 0, 0, 0},
+      {2.897153057105493, -6.359448489975075, 4.3622954328695815, 0, 0, 0, 0},
+      {5.325864828439257, -11.748883564062828, 7.4955393428898365, -0.09249506636175525, 0, 0, 0},
+      {5.86145544294642, -12.92096931784711, 8.159367898576159, -0.071584973281401,
+       -0.028269050394068383, 0, 0},
+      {0.09646076681806523, 0.01, 0.4798896504144996, 1.379008574103742, -3.290069515436081,
+       2.324710524099774, 0}};
+  // error weights b - bhat
+  static constexpr double e[7] = {-0.00178001105222577714, -0.0008164344596567469,
+                                  0.007880878010261995,    -0.1447110071732629,
+                                  0.5823571654525552,      -0.45808210592918697,
+                                  0.015151515151515152};
+};
+
+struct Dopri5Tab {
+  // J. R. Dormand, P. J. Prince, "A family of embedded Runge-Kutta formulae",
+  // J. Comput. Appl. Math. 6 (1980) 19-26.
+  static constexpr int order = 5, err_order = 4;
+  static constexpr double a[7][7] = {
+      {0, 0, 0, 0, 0, 0, 0},
+      {1.0 / 5.0, 0, 0, 0, 0, 0, 0},
+      {3.0 / 40.0, 9.0 / 40.0, 0, 0, 0, 0, 0},
+      {44.0 / 45.0, -56.0 / 15.0, 32.0 / 9.0, 0, 0, 0, 0},
+      {19372.0 / 6561.0, -25360.0 / 2187.0, 64448.0 / 6561.0, -212.0 / 729.0, 0, 0, 0},
+      {9017.0 / 3168.0, -355.0 / 33.0, 46732.0 / 5247.0, 49.0 / 176.0, -5103.0 / 18656.0, 0, 0},
+      {35.0 / 384.0, 0, 500.0 / 1113.0, 125.0 / 192.0, -2187.0 / 6784.0, 11.0 / 84.0, 0}};
+  // b - bhat with bhat = (5179/57600, 0, 7571/16695, 393/640, -92097/339200,
+  // 187/2100, 1/40)
+  static constexpr double e[7] = {71.0 / 57600.0,       0.0,           -71.0 / 16695.0,
+                                  71.0 / 1920.0,        -17253.0 / 339200.0, 22.0 / 525.0,
+                                  -1.0 / 40.0};
+};
+
+// ROS2 (Verwer, Spee, Blom, Hundsdorfer 1999): gamma = 1 + 1/sqrt(2) rounded
+// to double.
+constexpr double ROS2_GAMMA = 1.7071067811865475;
+
+// ---------------------------------------------------------------------------
+// Right-hand sides.  vjp_y: w_j = sum_i J_ij v_i over the rows listed;
+// vjp_p_acc: g_q += each (df_i/dp_q) v_i as a multiply-add into g_q;
+// jac_contract_acc: gy_c (gp_q) += Jbar_ab dJ_ab/dy_c (dp_q), entries (a, b)
+// in row-major order.
+// ---------------------------------------------------------------------------
+struct Linear {
+  static constexpr int D = 1, P = 1;
+  template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
+    o[0] = p[0] * y[0];
+  }
+  template <class T>
+  __device__ static __forceinline__ void vjp_y(const T *y, const T *p, const T *v, T *w) {
+    w[0] = p[0] * v[0];
+  }
+  template <class T>
+  __device__ static __forceinline__ void vjp_p_acc(const T *y, const T *p, const T *v, T *g) {
+    g[0] = mac(y[0], v[0], g[0]);
+  }
+  template <class T> __device__ static __forceinline__ void jac(const T *y, const T *p, T *J) {
+    J[0] = p[0];
+  }
+  template <class T>
+  __device__ static __forceinline__ void jac_contract_acc(const T *y, const T *p, const T *Jb,
+                                                          T *gy, T *gp) {
+    gp[0] = gp[0] + Jb[0];
+  }
+};
+
+struct Lorenz63 {
+  // p = (sigma, rho, beta)
+  static constexpr int D = 3, P = 3;
+  template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
+    o[0] = p[0] * (y[1] - y[0]);
+    o[1] = mac(y[0], p[1] - y[2], -y[1]);
+    o[2] = mac(y[0], y[1], -(p[2] * y[2]));
+  }
+  // J = [[-s, s, 0], [r - y3, -1, -y1], [y2, y1, -b]]
+  template <class T>
+  __device__ static __forceinline__ void vjp_y(const T *y, const T *p, const T *v, T *w) {
+    w[0] = mac(y[1], v[2], mac(p[1] - y[2], v[1], (-p[0]) * v[0]));
+    w[1] = mac(y[0], v[2], mac(p[0], v[0], -v[1]));
+    w[2] = mac(-p[2], v[2], (-y[0]) * v[1]);
+  }
+  template <class T>
+  __device__ static __forceinline__ void vjp_p_acc(const T *y, const T *p, const T *v, T *g) {
+    g[0] = mac(y[1] - y[0], v[0], g[0]);
+    g[1] = mac(y[0], v[1], g[1]);
+    g[2] = mac(-y[2], v[2], g[2]);
+  }
+  template <class T> __device__ static __forceinline__ void jac(const T *y, const T *p, T *J) {
+    J[0] = -p[0];        J[1] = p[0];   J[2] = T(0);
+    J[3] = p[1] - y[2];  J[4] = T(-1);  J[5] = -y[0];
+    J[6] = y[1];         J[7] = y[0];   J[8] = -p[2];
+  }
+  template <class T>
+  __device__ static __forceinline__ void jac_contract_acc(const T *y, const T *p, const T *Jb,
+                                                          T *gy, T *gp) {
+    gp[0] = gp[0] - Jb[0];  // J11 = -s
+    gp[0] = gp[0] + Jb[1];  // J12 = s
+    gp[1] = gp[1] + Jb[3];  // J21 = r - y3
+    gy[2] = gy[2] - Jb[3];
+    gy[0] = gy[0] - Jb[5];  // J23 = -y1
+    gy[1] = gy[1] + Jb[6];  // J31 = y2
+    gy[0] = gy[0] + Jb[7];  // J32 = y1
+    gp[2] = gp[2] - Jb[8];  // J33 = -b
+  }
+};
+
+struct Robertson {
+  // p = (k1, k2, k3)
+  static constexpr int D = 3, P = 3;
+  template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
+    o[0] = mac(p[2] * y[1], y[2], (-p[0]) * y[0]);
+    T s = p[0] * y[0];
+    s = mac(-(p[1] * y[1]), y[1], s);
+    s = mac(-(p[2] * y[1]), y[2], s);
+    o[1] = s;
+    o[2] = (p[1] * y[1]) * y[1];
+  }
+  // J = [[-k1, k3 y3, k3 y2], [k1, -2 k2 y2 - k3 y3, -k3 y2], [0, 2 k2 y2, 0]]
+  template <class T>
+  __device__ static __forceinline__ void vjp_y(const T *y, const T *p, const T *v, T *w) {
+    w[0] = mac(p[0], v[1], (-p[0]) * v[0]);
+    const T j22 = mac(-p[2], y[2], -(T(2) * p[1]) * y[1]);
+    T s = (p[2] * y[2]) * v[0];
+    s = mac(j22, v[1], s);
+    s = mac(T(2) * p[1] * y[1], v[2], s);
+    w[1] = s;
+    w[2] = mac(-(p[2] * y[1]), v[1], (p[2] * y[1]) * v[0]);
+  }
+  template <class T>
+  __device__ static __forceinline__ void vjp_p_acc(const T *y, const T *p, const T *v, T *g) {
+    g[0] = mac(-y[0], v[0], g[0]);
+    g[0] = mac(y[0], v[1], g[0]);
+    const T y22 = y[1] * y[1];
+    g[1] = mac(-y22, v[1], g[1]);
+    g[1] = mac(y22, v[2], g[1]);
+    const T y23 = y[1] * y[2];
+    g[2] = mac(y23, v[0], g[2]);
+    g[2] = mac(-y23, v[1], g[2]);
+  }
+  template <class T> __device__ static __forceinline__ void jac(const T *y, const T *p, T *J) {
+    J[0] = -p[0];  J[1] = p[2] * y[2];  J[2] = p[2] * y[1];
+    J[3] = p[0];   J[4] = mac(-p[2], y[2], -(T(2) * p[1]) * y[1]);  J[5] = -(p[2] * y[1]);
+    J[6] = T(0);   J[7] = T(2) * p[1] * y[1];  J[8] = T(0);
+  }
+  template <class T>
+  __device__ static __forceinline__ void jac_contract_acc(const T *y, const T *p, const T *Jb,
+                                                          T *gy, T *gp) {
+    const T k3 = p[2], two_k2 = T(2) * p[1], two_y2 = T(2) * y[1];
+    gp[0] = gp[0] - Jb[0];              // J11 = -k1
+    gy[2] = mac(k3, Jb[1], gy[2]);      // J12 = k3 y3
+    gp[2] = mac(y[2], Jb[1], gp[2]);
+    gy[1] = mac(k3, Jb[2], gy[1]);      // J13 = k3 y2
+    gp[2] = mac(y[1], Jb[2], gp[2]);
+    gp[0] = gp[0] + Jb[3];              // J21 = k1
+    gy[1] = mac(-two_k2, Jb[4], gy[1]); // J22 = -2 k2 y2 - k3 y3
+    gy[2] = mac(-k3, Jb[4], gy[2]);
+    gp[1] = mac(-two_y2, Jb[4], gp[1]);
+    gp[2] = mac(-y[2], Jb[4], gp[2]);
+    gy[1] = mac(-k3, Jb[5], gy[1]);     // J23 = -k3 y2
+    gp[2] = mac(-y[1], Jb[5], gp[2]);
+    gy[1] = mac(two_k2, Jb[7], gy[1]);  // J32 = 2 k2 y2
+    gp[1] = mac(two_y2, Jb[7], gp[1]);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Explicit RK stage machinery (one trajectory per lane, state in registers)
+// ---------------------------------------------------------------------------
+
+// Y = y + h * sum_{j<I} a[I][j] K[j]  (zero coefficients skipped)
+template <class Tab, int I, int D, class T>
+__device__ __forceinline__ void stage_state(const T (&y)[D], const T (&K)[7][D], T h,
+                                            T (&Y)[D]) {
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    T acc = T(0);
+    bool first = true;
+#pragma unroll
+    for (int j = 0; j < I; ++j) {
+      if (Tab::a[I][j] != 0.0) {
+        if (first) { acc = T(Tab::a[I][j]) * K[j][c]; first = false; }
+        else acc = mac(T(Tab::a[I][j]), K[j][c], acc);
+      }
+    }
+    Y[c] = mac(h, acc, y[c]);
+  }
+}
+
+template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
+struct StageLoop {
+  __device__ static __forceinline__ void run(const T (&y)[Rhs::D], const T *p, T h,
+                                             T (&Y)[7][Rhs::D], T (&K)[7][Rhs::D]) {
+    stage_state<Tab, I>(y, K, h, Y[I]);
+    if (I < LAST || LASTK) Rhs::f(Y[I], p, K[I]);
+    StageLoop<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, p, h, Y, K);
+  }
+};
+template <class Tab, class Rhs, int LAST, bool LASTK, class T>
+struct StageLoop<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
+  __device__ static __forceinline__ void run(const T (&)[Rhs::D], const T *, T, T (&)[7][Rhs::D],
+                                             T (&)[7][Rhs::D]) {}
+};
+
+// Stages 1..LAST from y with K[0] = f(y) given; K[LAST] too when LASTK.
+template <class Tab, class Rhs, int LAST, bool LASTK, class T>
+__device__ __forceinline__ void erk_stages(const T (&y)[Rhs::D], const T *p, T h,
+                                           T (&Y)[7][Rhs::D], T (&K)[7][Rhs::D]) {
+  StageLoop<Tab, Rhs, 1, LAST, LASTK, T>::run(y, p, h, Y, K);
+}
+
+}  // namespace dadj

@@ -1,0 +1,68 @@
+// Host/device interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dadj.h"
+
+namespace dadj {
+
+constexpr int BLOCK = 256;  // threads per workgroup of the lane-per-trajectory kernels
+
+enum { LANE_OK = 0, LANE_MAX_STEPS = 1, LANE_DT_UNDERFLOW = 2, LANE_NONFINITE = 3,
+       LANE_MAX_ATTEMPTS = 4 };
+
+// Problem, flattened, defaults resolved.
+struct ProbArgs {
+  int32_t rhs, dim, n_params, method, dtype;
+  int32_t max_steps, max_attempts, n_save, S;  // S = max(1, n_save)
+  double t0, t1, rtol, atol, dt0, safety, fac_min, fac_max;
+};
+
+// Save times by value (kernel argument); t[n_save - 1] <= t1.
+struct SaveTimes {
+  double t[DA_MAX_SAVES];
+};
+
+struct RecordArgs {
+  ProbArgs pr;
+  int64_t n;
+  const void *u0, *p;
+  void *h;              // [max_steps][n] or null (forward solve)
+  int32_t *nsteps;      // [n] or null
+  int32_t *sidx;        // [S][n] or null
+  int32_t *status;      // [n] or null
+  void *y_save;         // [S][d][n] or null
+};
+
+struct ReplayArgs {
+  ProbArgs pr;
+  int64_t n;
+  const void *u0, *p;
+  const void *h;
+  const int32_t *nsteps, *sidx, *status, *perm;
+  void *y_save;                // replay_fwd output [S][d][n]
+  int32_t loss_kind;
+  const void *aux;             // [S][d][n]
+  double scale;
+  void *loss_out, *gu0, *gp;   // [n], [d][n], [P][n]
+  void *ws;                    // [max_n_steps][d][ws_lanes]
+  int64_t slot0, nslots, ws_lanes;
+  int32_t max_n_steps;
+};
+
+hipError_t launch_erk_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
+hipError_t launch_erk_replay_fwd(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_erk_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_ros2_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
+hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s);
+
+// Mesh utilities
+size_t sort_workspace_bytes(int64_t n, int32_t max_steps);
+hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const da_mesh &in, da_mesh &out,
+                            void *ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s);
+
+}  // namespace dadj

@@ -1,0 +1,256 @@
+// Second-order Rosenbrock method ROS2 (Verwer, Spee, Blom, Hundsdorfer 1999,
+// gamma = 1 + 1/sqrt(2)) for the lane-per-trajectory kernels, the stiff
+// integrator of the record-and-replay path ("GRADSOLVE: fast exact gradients
+// for ODE ensembles on GPUs", gptget.net summary, Abstract: Rosenbrock
+// integrators; evolve.pub review, Summary: default second-order Rosenbrock).
+// Per lane: the d x d Jacobian (d <= 3), W = I - gamma h J, its LU factors
+// with partial pivoting (ties keep the lower row), two solves per step; the
+// reverse sweep uses transposed solves with the same factors and contracts
+// Jbar = -gamma h Wbar with the derivative of J.
+#include "lane_kernels.hpp"
+
+namespace dadj {
+namespace {
+
+template <int D, class T> struct Ros2Step {
+  T J[D * D], LU[D * D];
+  int perm[D];
+  T f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
+};
+
+// In-place LU of A (row-major) with partial pivoting; perm[i] = original row
+// now in position i.  Row exchanges are register selects.
+template <int D, class T>
+__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D]) {
+#pragma unroll
+  for (int i = 0; i < D; ++i) perm[i] = i;
+#pragma unroll
+  for (int k = 0; k < D; ++k) {
+    int piv = k;
+    T best = dabs(A[k * D + k]);
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      const T v = dabs(A[i * D + k]);
+      if (v > best) { best = v; piv = i; }
+    }
+#pragma unroll
+    for (int r = k + 1; r < D; ++r) {
+      const bool sw = piv == r;
+#pragma unroll
+      for (int j = 0; j < D; ++j) {
+        const T top = A[k * D + j], oth = A[r * D + j];
+        A[k * D + j] = sw ? oth : top;
+        A[r * D + j] = sw ? top : oth;
+      }
+      const int pt = perm[k], po = perm[r];
+      perm[k] = sw ? po : pt;
+      perm[r] = sw ? pt : po;
+    }
+#pragma unroll
+    for (int i = k + 1; i < D; ++i) {
+      const T l = A[i * D + k] / A[k * D + k];
+      A[i * D + k] = l;
+#pragma unroll
+      for (int j = k + 1; j < D; ++j) A[i * D + j] = mac(-l, A[k * D + j], A[i * D + j]);
+    }
+  }
+}
+
+// Solve A x = b from the factors (P A = L U).  The right-hand side is copied
+// into a private array first so that the permutation stays a register select
+// (a select between loads through the argument would become an indexed load
+// and keep the caller's arrays out of registers).
+template <int D, class T>
+__device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const int (&perm)[D],
+                                         const T (&b_in)[D], T (&x)[D]) {
+  T b[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) b[i] = b_in[i];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    T v = b[0];
+#pragma unroll
+    for (int q = 1; q < D; ++q) v = (perm[i] == q) ? b[q] : v;
+    x[i] = v;
+  }
+#pragma unroll
+  for (int i = 0; i < D; ++i)
+#pragma unroll
+    for (int j = 0; j < i; ++j) x[i] = mac(-LU[i * D + j], x[j], x[i]);
+#pragma unroll
+  for (int i = D - 1; i >= 0; --i) {
+#pragma unroll
+    for (int j = i + 1; j < D; ++j) x[i] = mac(-LU[i * D + j], x[j], x[i]);
+    x[i] = x[i] / LU[i * D + i];
+  }
+}
+
+// Solve A^T x = b from the factors of A (A^T = U^T L^T P).
+template <int D, class T>
+__device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const int (&perm)[D],
+                                           const T (&b)[D], T (&x)[D]) {
+  T z[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    z[i] = b[i];
+#pragma unroll
+    for (int j = 0; j < i; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
+    z[i] = z[i] / LU[i * D + i];
+  }
+#pragma unroll
+  for (int i = D - 1; i >= 0; --i)
+#pragma unroll
+    for (int j = i + 1; j < D; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
+  // x[perm[i]] = z[i]
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    T v = z[0];
+#pragma unroll
+    for (int i = 1; i < D; ++i) v = (perm[i] == c) ? z[i] : v;
+    x[c] = v;
+  }
+}
+
+// One ROS2 step from y with size h:
+//   k1 = W^-1 f(y);  Y2 = y + h k1;  k2 = W^-1 (f(Y2) - 2 k1);
+//   y+ = y + h (3/2 k1 + 1/2 k2);  err = h (1/2 k1 + 1/2 k2).
+template <class Rhs, class T>
+__device__ __forceinline__ void ros2_forward(const T (&y)[Rhs::D], const T *p, T h,
+                                             Ros2Step<Rhs::D, T> &s) {
+  constexpr int D = Rhs::D;
+  Rhs::jac(y, p, s.J);
+  const T gh = T(ROS2_GAMMA) * h;
+#pragma unroll
+  for (int a = 0; a < D; ++a)
+#pragma unroll
+    for (int b = 0; b < D; ++b)
+      s.LU[a * D + b] = (a == b) ? mac(-gh, s.J[a * D + b], T(1)) : (-gh) * s.J[a * D + b];
+  lu_factor<D>(s.LU, s.perm);
+  Rhs::f(y, p, s.f1);
+  lu_solve<D>(s.LU, s.perm, s.f1, s.k1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) s.Y2[c] = mac(h, s.k1[c], y[c]);
+  Rhs::f(s.Y2, p, s.f2);
+#pragma unroll
+  for (int c = 0; c < D; ++c) s.r2[c] = mac(T(-2), s.k1[c], s.f2[c]);
+  lu_solve<D>(s.LU, s.perm, s.r2, s.k2);
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    const T acc = mac(T(0.5), s.k2[c], T(1.5) * s.k1[c]);
+    s.ynew[c] = mac(h, acc, y[c]);
+    const T e = mac(T(0.5), s.k2[c], T(0.5) * s.k1[c]);
+    s.err[c] = h * e;
+  }
+}
+
+template <class R>
+struct Ros2 {
+  using Rhs = R;
+  static constexpr int D = R::D;
+  static constexpr int order = 2, err_order = 1;
+  template <class T> struct Cache {};
+
+  template <class T>
+  __device__ static __forceinline__ void begin(const T (&)[D], const T *, const T (&)[D],
+                                               Cache<T> &) {}
+
+  template <class T>
+  __device__ static __forceinline__ void attempt(const T (&y)[D], const T *p, T h, Cache<T> &,
+                                                 T (&ynew)[D], T (&err)[D]) {
+    Ros2Step<D, T> s;
+    ros2_forward<Rhs>(y, p, h, s);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      ynew[c] = s.ynew[c];
+      err[c] = s.err[c];
+    }
+  }
+
+  template <class T> __device__ static __forceinline__ void accepted(Cache<T> &) {}
+
+  template <class T> __device__ static __forceinline__ void fwd(T (&y)[D], const T *p, T h) {
+    Ros2Step<D, T> s;
+    ros2_forward<Rhs>(y, p, h, s);
+#pragma unroll
+    for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
+  }
+
+  // Reverse with the mesh fixed:
+  //   kbar1 = 3/2 h lam, kbar2 = 1/2 h lam, ybar = lam
+  //   rbar2 = W^-T kbar2, Wbar = -rbar2 k2^T
+  //   Y2bar = J(Y2)^T rbar2, g += J_p(Y2)^T rbar2
+  //   kbar1 += -2 rbar2 + h Y2bar, ybar += Y2bar
+  //   rbar1 = W^-T kbar1, Wbar += -rbar1 k1^T
+  //   ybar += J(y)^T rbar1, g += J_p(y)^T rbar1
+  //   Jbar = -gamma h Wbar; ybar, g += contraction of Jbar with dJ
+  template <class T>
+  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
+    Ros2Step<D, T> s;
+    ros2_forward<Rhs>(y, p, h, s);
+    T yb[D], kb1[D], kb2[D], rb1[D], rb2[D], Y2b[D], w[D], Wb[D * D], Jb[D * D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      const T ab = h * lam[c];
+      kb1[c] = T(1.5) * ab;
+      kb2[c] = T(0.5) * ab;
+      yb[c] = lam[c];
+    }
+    lu_solve_t<D>(s.LU, s.perm, kb2, rb2);
+#pragma unroll
+    for (int a = 0; a < D; ++a)
+#pragma unroll
+      for (int b = 0; b < D; ++b) Wb[a * D + b] = (-rb2[a]) * s.k2[b];
+    Rhs::vjp_y(s.Y2, p, rb2, Y2b);
+    Rhs::vjp_p_acc(s.Y2, p, rb2, g);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      kb1[c] = mac(T(-2), rb2[c], kb1[c]);
+      kb1[c] = mac(h, Y2b[c], kb1[c]);
+      yb[c] = yb[c] + Y2b[c];
+    }
+    lu_solve_t<D>(s.LU, s.perm, kb1, rb1);
+#pragma unroll
+    for (int a = 0; a < D; ++a)
+#pragma unroll
+      for (int b = 0; b < D; ++b) Wb[a * D + b] = mac(-rb1[a], s.k1[b], Wb[a * D + b]);
+    Rhs::vjp_y(y, p, rb1, w);
+    Rhs::vjp_p_acc(y, p, rb1, g);
+#pragma unroll
+    for (int c = 0; c < D; ++c) yb[c] = yb[c] + w[c];
+    const T gh = T(ROS2_GAMMA) * h;
+#pragma unroll
+    for (int q = 0; q < D * D; ++q) Jb[q] = (-gh) * Wb[q];
+    Rhs::jac_contract_acc(y, p, Jb, yb, g);
+#pragma unroll
+    for (int c = 0; c < D; ++c) lam[c] = yb[c];
+  }
+};
+
+#define DADJ_ROS2_DISPATCH(FN, ARGS)                                                  \
+  do {                                                                                \
+    const bool f64 = a.pr.dtype == DA_F64;                                            \
+    switch (a.pr.rhs) {                                                               \
+      case DA_RHS_LINEAR:                                                             \
+        return f64 ? FN<double, Ros2<Linear>> ARGS : FN<float, Ros2<Linear>> ARGS;    \
+      case DA_RHS_LORENZ63:                                                           \
+        return f64 ? FN<double, Ros2<Lorenz63>> ARGS : FN<float, Ros2<Lorenz63>> ARGS; \
+      case DA_RHS_ROBERTSON:                                                          \
+        return f64 ? FN<double, Ros2<Robertson>> ARGS : FN<float, Ros2<Robertson>> ARGS; \
+      default:                                                                        \
+        return hipErrorInvalidValue;                                                  \
+    }                                                                                 \
+  } while (0)
+
+}  // namespace
+
+hipError_t launch_ros2_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  DADJ_ROS2_DISPATCH(record_t, (a, st, s));
+}
+hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s) {
+  DADJ_ROS2_DISPATCH(replay_fwd_t, (a, s));
+}
+hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s) {
+  DADJ_ROS2_DISPATCH(replay_grad_t, (a, s));
+}
+
+}  // namespace dadj

@@ -1,0 +1,222 @@
+// Mesh utilities: lane ordering by step count and the largest step count.
+//
+// Lane ordering.  Trajectories of one ensemble need different numbers of
+// accepted steps (the GRADSOLVE review, Strengths, quotes a max/mean of
+// 1.33-1.34 from the paper's Table 5).  A wavefront replays for as many steps
+// as its longest lane needs, so slots are reordered by decreasing n_steps:
+// neighbouring lanes then carry nearly equal work.  The sort is a stable LSD
+// radix sort over 8-bit digits of key = max_steps - n_steps (deterministic:
+// no atomics), followed by a gather of the mesh into the new slot order.
+#include "dadj_internal.hpp"
+
+namespace dadj {
+namespace {
+
+constexpr int SORT_THREADS = 256;
+constexpr int SORT_ITEMS = 4;                 // per thread
+constexpr int SORT_TILE = SORT_THREADS * SORT_ITEMS;
+constexpr int RADIX = 256;
+
+__device__ __forceinline__ unsigned digit_of(unsigned key, int shift) {
+  return (key >> shift) & (RADIX - 1);
+}
+
+// keys from n_steps; values = source slot
+__global__ __launch_bounds__(SORT_THREADS) void k_init_keys(int64_t n, int32_t max_steps,
+                                                            const int32_t *__restrict__ nsteps,
+                                                            unsigned *__restrict__ keys,
+                                                            int32_t *__restrict__ vals) {
+  const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
+  if (j >= n) return;
+  int s = nsteps[j];
+  s = s < 0 ? 0 : (s > max_steps ? max_steps : s);
+  keys[j] = (unsigned)(max_steps - s);
+  vals[j] = (int32_t)j;
+}
+
+// counts[d * ntiles + tile] = number of keys of the tile with digit d
+__global__ __launch_bounds__(SORT_THREADS) void k_hist(int64_t n, int shift,
+                                                       const unsigned *__restrict__ keys,
+                                                       unsigned *__restrict__ counts,
+                                                       int64_t ntiles) {
+  __shared__ unsigned h[RADIX];
+  h[threadIdx.x] = 0;
+  __syncthreads();
+  const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+  for (int r = 0; r < SORT_ITEMS; ++r) {
+    const int64_t e = base + r * SORT_THREADS + threadIdx.x;
+    if (e < n) atomicAdd(&h[digit_of(keys[e], shift)], 1u);
+  }
+  __syncthreads();
+  counts[(int64_t)threadIdx.x * ntiles + blockIdx.x] = h[threadIdx.x];
+}
+
+// exclusive scan of counts[0..m) in place, one workgroup
+__global__ __launch_bounds__(SORT_THREADS) void k_scan(unsigned *__restrict__ counts, int64_t m) {
+  __shared__ unsigned part[SORT_THREADS];
+  __shared__ unsigned carry;
+  if (threadIdx.x == 0) carry = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < m; base += SORT_THREADS) {
+    const int64_t e = base + threadIdx.x;
+    const unsigned v = e < m ? counts[e] : 0u;
+    part[threadIdx.x] = v;
+    __syncthreads();
+    for (int off = 1; off < SORT_THREADS; off <<= 1) {
+      const unsigned add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0u;
+      __syncthreads();
+      part[threadIdx.x] += add;
+      __syncthreads();
+    }
+    if (e < m) counts[e] = carry + part[threadIdx.x] - v;
+    __syncthreads();
+    if (threadIdx.x == SORT_THREADS - 1) carry += part[SORT_THREADS - 1];
+    __syncthreads();
+  }
+}
+
+// stable scatter of one tile: rank among equal digits of earlier elements
+__global__ __launch_bounds__(SORT_THREADS) void k_scatter(int64_t n, int shift, int64_t ntiles,
+                                                          const unsigned *__restrict__ counts,
+                                                          const unsigned *__restrict__ kin,
+                                                          const int32_t *__restrict__ vin,
+                                                          unsigned *__restrict__ kout,
+                                                          int32_t *__restrict__ vout) {
+  constexpr int NW = SORT_THREADS / 64;
+  __shared__ unsigned run[RADIX];          // running count per digit within the tile
+  __shared__ unsigned wcnt[NW][RADIX];     // per-wave counts of the current round
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  run[threadIdx.x] = 0;
+  const int64_t base = (int64_t)blockIdx.x * SORT_TILE;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = 0; r < SORT_ITEMS; ++r) {
+    for (int q = 0; q < NW; ++q) wcnt[q][threadIdx.x] = 0;
+    __syncthreads();
+    const int64_t e = base + r * SORT_THREADS + threadIdx.x;
+    const bool valid = e < n;
+    const unsigned key = valid ? kin[e] : 0u;
+    const unsigned d = digit_of(key, shift);
+    // lanes of this wave holding the same digit
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (d >> b) & 1u;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const unsigned rank_w = (unsigned)__popcll(same & lt);
+    if (valid && rank_w == 0) wcnt[w][d] = (unsigned)__popcll(same);
+    __syncthreads();
+    if (valid) {
+      unsigned pre = run[d];
+      for (int q = 0; q < w; ++q) pre += wcnt[q][d];
+      const unsigned pos = counts[(int64_t)d * ntiles + blockIdx.x] + pre + rank_w;
+      kout[pos] = key;
+      vout[pos] = vin[e];
+    }
+    __syncthreads();
+    unsigned tot = 0;
+    for (int q = 0; q < NW; ++q) tot += wcnt[q][threadIdx.x];
+    run[threadIdx.x] += tot;
+    __syncthreads();
+  }
+}
+
+// out slot j takes in slot src = order[j]
+__global__ __launch_bounds__(SORT_THREADS) void k_gather_meta(int64_t n, int S,
+                                                              const int32_t *__restrict__ order,
+                                                              da_mesh in, da_mesh out) {
+  const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
+  if (j >= n) return;
+  const int64_t src = order[j];
+  out.n_steps[j] = in.n_steps[src];
+  out.status[j] = in.status[src];
+  out.perm[j] = in.perm ? in.perm[src] : (int32_t)src;
+  for (int s = 0; s < S; ++s) out.save_idx[(int64_t)s * n + j] = in.save_idx[(int64_t)s * n + src];
+}
+
+template <class T>
+__global__ __launch_bounds__(SORT_THREADS) void k_gather_h(int64_t n, int32_t max_steps,
+                                                           const int32_t *__restrict__ order,
+                                                           const int32_t *__restrict__ ns_out,
+                                                           const T *__restrict__ hin,
+                                                           T *__restrict__ hout) {
+  const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
+  const bool live = j < n;
+  const int64_t src = live ? order[j] : 0;
+  int N = live ? ns_out[j] : 0;
+  N = N < 0 ? 0 : (N > max_steps ? max_steps : N);
+  for (int k = 0; k < max_steps; ++k)
+    if (live) hout[(int64_t)k * n + j] = k < N ? hin[(int64_t)k * n + src] : T(0);
+}
+
+__global__ __launch_bounds__(1024) void k_max_steps(int64_t n, const int32_t *__restrict__ ns,
+                                                    int32_t *__restrict__ out) {
+  __shared__ int part[1024];
+  int m = 0;
+  for (int64_t j = threadIdx.x; j < n; j += 1024) m = ns[j] > m ? ns[j] : m;
+  part[threadIdx.x] = m;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off && part[threadIdx.x + off] > part[threadIdx.x])
+      part[threadIdx.x] = part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[0] = part[0];
+}
+
+size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int key_bits(int32_t max_steps) {
+  int b = 1;
+  while (b < 31 && (1u << b) <= (unsigned)max_steps) ++b;
+  return b;
+}
+
+}  // namespace
+
+size_t sort_workspace_bytes(int64_t n, int32_t max_steps) {
+  (void)max_steps;
+  const int64_t ntiles = (n + SORT_TILE - 1) / SORT_TILE;
+  return 2 * align_up((size_t)n * 4) + 2 * align_up((size_t)n * 4) +
+         align_up((size_t)ntiles * RADIX * 4);
+}
+
+hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const da_mesh &in, da_mesh &out,
+                            void *ws, size_t ws_bytes, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (ws_bytes < sort_workspace_bytes(n, pr.max_steps)) return hipErrorInvalidValue;
+  const int64_t ntiles = (n + SORT_TILE - 1) / SORT_TILE;
+  char *p = (char *)ws;
+  unsigned *kA = (unsigned *)p; p += align_up((size_t)n * 4);
+  unsigned *kB = (unsigned *)p; p += align_up((size_t)n * 4);
+  int32_t *vA = (int32_t *)p; p += align_up((size_t)n * 4);
+  int32_t *vB = (int32_t *)p; p += align_up((size_t)n * 4);
+  unsigned *counts = (unsigned *)p;
+  const unsigned g1 = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
+  hipLaunchKernelGGL(k_init_keys, g1, SORT_THREADS, 0, s, n, pr.max_steps, in.n_steps, kA, vA);
+  const int bits = key_bits(pr.max_steps);
+  for (int shift = 0; shift < bits; shift += 8) {
+    hipLaunchKernelGGL(k_hist, (unsigned)ntiles, SORT_THREADS, 0, s, n, shift, kA, counts, ntiles);
+    hipLaunchKernelGGL(k_scan, 1, SORT_THREADS, 0, s, counts, ntiles * RADIX);
+    hipLaunchKernelGGL(k_scatter, (unsigned)ntiles, SORT_THREADS, 0, s, n, shift, ntiles, counts,
+                       kA, vA, kB, vB);
+    unsigned *tk = kA; kA = kB; kB = tk;
+    int32_t *tv = vA; vA = vB; vB = tv;
+  }
+  hipLaunchKernelGGL(k_gather_meta, g1, SORT_THREADS, 0, s, n, pr.S, vA, in, out);
+  if (pr.dtype == DA_F64)
+    hipLaunchKernelGGL(k_gather_h<double>, g1, SORT_THREADS, 0, s, n, pr.max_steps, vA,
+                       out.n_steps, (const double *)in.h, (double *)out.h);
+  else
+    hipLaunchKernelGGL(k_gather_h<float>, g1, SORT_THREADS, 0, s, n, pr.max_steps, vA,
+                       out.n_steps, (const float *)in.h, (float *)out.h);
+  return hipGetLastError();
+}
+
+hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_max_steps, 1, 1024, 0, s, n, nsteps, dev_out);
+  return hipGetLastError();
+}
+
+}  // namespace dadj

@@ -1,0 +1,210 @@
+/*
+ * dadj.h - C ABI of the MI355X record-and-replay discrete-adjoint library
+ * (libdadj.so, HIP kernels for gfx950).
+ *
+ * The problem (DiffEqGPU page "Using GPU-accelerated Ensembles with Automatic
+ * Differentiation", ensemble examples): an ensemble of n independent initial
+ * value problems y' = f(y, p_i), y(t0) = u0_i, each trajectory with its own
+ * parameters p_i and initial state u0_i, one trajectory per GPU lane (gist.science
+ * page "Differentiable astrophysics at scale", Methodology: per-thread
+ * integration).
+ *
+ * The path ("GRADSOLVE: fast exact gradients for ODE ensembles on GPUs",
+ * gptget.net summary, Methodology, and the evolve.pub review, Summary):
+ *   1. da_record      - one adaptive solve per trajectory; the accepted step
+ *                       sizes form a zero-padded fixed-length mesh.
+ *   2. da_replay_grad - fixed-step replay of that mesh and its reverse sweep:
+ *                       the exact discrete adjoint with the mesh held fixed
+ *                       (review, Strengths: paper section 3.1; FAQ on
+ *                       exactness), repeated for many passes against one record.
+ *   3. da_solve_fwd   - the forward-only adaptive solve (summary, Key results).
+ * plus da_replay_fwd (forward replay only) and da_mesh_sort (lane ordering by
+ * step count so that each wavefront's lanes carry similar work).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers unless marked "host"; all memory is
+ *    owned by the caller.  The library allocates no device memory and keeps no
+ *    state apart from a thread-local error message.
+ *  - Per-trajectory arrays are component-major: element (c, i) of an array
+ *    with C components lives at index c * n + i (trajectory index fastest), so
+ *    a wavefront reads and writes contiguous memory.
+ *  - Floating-point buffers use the problem's dtype (double or float);
+ *    t0, t1, save times and tolerances are host doubles.
+ *  - Argument checks run synchronously before any launch; on failure the call
+ *    returns a negative da_err, launches nothing and leaves outputs untouched.
+ *    Everything else is asynchronous on `stream` (a hipStream_t; NULL is the
+ *    default stream).  A failed launch returns DA_EHIP.
+ *  - A trajectory that fails (see da_lane_status) never fails the call; its
+ *    status says why and its gradients and loss are NaN.
+ *  - Outputs are overwritten, not accumulated.  Results are deterministic:
+ *    the same inputs give bitwise identical outputs on the same device.
+ */
+#ifndef DADJ_H
+#define DADJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { DA_F64 = 0, DA_F32 = 1 } da_dtype;
+
+/* Integrators: explicit Tsitouras 5(4) and Dormand-Prince 5(4) (both 7
+ * stages, first-same-as-last, 5th-order solution propagated), and the
+ * second-order Rosenbrock method ROS2 with gamma = 1 + 1/sqrt(2) (summary,
+ * Abstract: explicit and Rosenbrock integrators). */
+typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2 } da_method;
+
+/* Built-in right-hand sides (dimension d, parameter count P):
+ *  DA_RHS_LINEAR    d=1, P=1: y' = p0 y
+ *  DA_RHS_LORENZ63  d=3, P=3: (s (y2-y1), y1 (r-y3) - y2, y1 y2 - b y3),
+ *                   p = (s, r, b) (DiffEqGPU page, forward-mode example)
+ *  DA_RHS_ROBERTSON d=3, P=3: (-k1 y1 + k3 y2 y3, k1 y1 - k2 y2^2 - k3 y2 y3,
+ *                   k2 y2^2), p = (k1, k2, k3)
+ *  DA_RHS_LORENZ96  4<=d<=64, P=1: x_i' = (x_{i+1} - x_{i-2}) x_{i-1} - x_i + F,
+ *                   indices cyclic, p = (F).  Explicit methods only.       */
+typedef enum {
+  DA_RHS_LINEAR = 0,
+  DA_RHS_LORENZ63 = 1,
+  DA_RHS_ROBERTSON = 2,
+  DA_RHS_LORENZ96 = 3
+} da_rhs;
+
+typedef enum {
+  DA_OK = 0,
+  DA_EINVAL = -1,       /* invalid argument                                 */
+  DA_EUNSUPPORTED = -2, /* valid but not implemented (e.g. ROS2 on LORENZ96) */
+  DA_EHIP = -3,         /* a HIP call or kernel launch failed               */
+  DA_EWORKSPACE = -4    /* workspace too small                              */
+} da_err;
+
+/* Per-trajectory outcome of a record (or forward solve). */
+typedef enum {
+  DA_LANE_OK = 0,
+  DA_LANE_MAX_STEPS = 1,    /* max_steps accepted steps did not reach t1     */
+  DA_LANE_DT_UNDERFLOW = 2, /* the step no longer advances t                 */
+  DA_LANE_NONFINITE = 3,    /* u0 or p holds a NaN or infinity               */
+  DA_LANE_MAX_ATTEMPTS = 4  /* max_attempts step attempts did not reach t1   */
+} da_lane_status;
+
+#define DA_MAX_SAVES 128
+
+/* Problem and solver options.  Zero for dt0, max_attempts, safety, fac_min,
+ * fac_max selects the default: Hairer-Norsett-Wanner starting step,
+ * 4*max_steps attempts, 0.9, 0.2, 10.
+ * Adaptive control (record and forward solve): error norm = RMS over
+ * components of err / (atol + rtol max(|y_n|, |y_{n+1}|)); accept iff it is
+ * <= 1; next step = used step * clamp(safety E^(-1/(q+1)), fac_min, fac_max)
+ * with q the embedded order (4 for the explicit pairs, 1 for ROS2), no growth
+ * on the step after a rejection.  Steps are shortened to land exactly on each
+ * save time and on t1. */
+typedef struct {
+  int32_t rhs;         /* da_rhs                                              */
+  int32_t dim;         /* state dimension d                                   */
+  int32_t n_params;    /* parameter count P                                   */
+  int32_t method;      /* da_method                                           */
+  int32_t dtype;       /* da_dtype of every floating buffer                   */
+  double t0, t1;       /* integration interval, t1 > t0                       */
+  double rtol, atol;   /* >= 0, rtol + atol > 0                               */
+  double dt0;          /* > 0: first trial step; <= 0: automatic              */
+  int32_t max_steps;   /* mesh length = largest number of accepted steps      */
+  int32_t max_attempts;
+  int32_t n_save;      /* 0..DA_MAX_SAVES; 0 = the final state is the only save */
+  const double *save_times; /* host, n_save values strictly increasing in (t0, t1] */
+  double safety, fac_min, fac_max;
+} da_problem;
+
+/* The record: one zero-padded step mesh per trajectory, reused by every
+ * replay until the next record.  S = max(1, n_save) save slots.
+ * Arrays are indexed by SLOT j in [0, n).  Without a permutation (perm ==
+ * NULL) slot j holds trajectory j.  With one, slot j holds trajectory perm[j]
+ * and the replay entry points gather inputs and scatter outputs through it;
+ * inputs and outputs of every entry point stay in trajectory order. */
+typedef struct {
+  void *h;           /* [max_steps][n]: accepted step sizes of each slot,
+                        zeros after its n_steps-th step                       */
+  int32_t *n_steps;  /* [n] accepted steps                                    */
+  int32_t *save_idx; /* [S][n] mesh index k at which save time s is reached
+                        (the state after k steps); -1 if never reached        */
+  int32_t *status;   /* [n] da_lane_status                                    */
+  int32_t *perm;     /* [n] slot -> trajectory, or NULL for the identity      */
+} da_mesh;
+
+/* Scalar loss of the replayed states; the gradient is of the sum over
+ * trajectories, i.e. per trajectory of its own term:
+ *  DA_LOSS_SUMSQ_FINAL: L_i = scale * sum_c y_{N_i}[c]^2 (final state)
+ *  DA_LOSS_MSE_SAVE:    L_i = scale * sum_s sum_c (y_{idx_s}[c] - aux[s][c][i])^2
+ *  DA_LOSS_COTANGENT:   L_i = scale * sum_s sum_c aux[s][c][i] * y_{idx_s}[c]
+ * aux is [S][d][n] in trajectory order (NULL for SUMSQ_FINAL).  The MSE of
+ * the calibration workload uses scale = 1 / (n S d). */
+typedef enum {
+  DA_LOSS_SUMSQ_FINAL = 0,
+  DA_LOSS_MSE_SAVE = 1,
+  DA_LOSS_COTANGENT = 2
+} da_loss_kind;
+
+typedef struct {
+  int32_t kind;      /* da_loss_kind */
+  const void *aux;   /* device [S][d][n] or NULL */
+  double scale;
+} da_loss;
+
+/* Record: one adaptive solve per trajectory (summary, Methodology: record the
+ * accepted steps; review, Summary: zero-padded fixed-length mesh).
+ * u0 [d][n], p [P][n]; fills mesh->h, n_steps, save_idx, status in trajectory
+ * order (mesh->perm must be NULL) and, if y_save is not NULL, y_save
+ * [S][d][n] with the state at each save time (NaN where not reached). */
+int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p,
+              da_mesh *mesh, void *y_save, void *stream);
+
+/* Forward-only adaptive solve (summary, Key results: the forward kernel):
+ * the same integration as da_record without the mesh.  y_save [S][d][n],
+ * n_steps [n] and status [n] (either may be NULL). */
+int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                 void *y_save, int32_t *n_steps, int32_t *status, void *stream);
+
+/* Lane ordering: writes into `out` the mesh of `in` with slots reordered by
+ * decreasing n_steps (stable, so deterministic), and out->perm (required).
+ * `in` may itself be permuted.  `out` must not alias `in`.  Work space of
+ * da_mesh_sort_workspace bytes is required. */
+size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n);
+int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *out,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/* Largest n_steps over the mesh, returned to the host (synchronises the
+ * stream).  Used to size the replay workspace. */
+int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *stream);
+
+/* Fixed-step replay of the mesh (review, Summary: branch-free fixed-length
+ * chain): y_save [S][d][n] at each save index; reproduces the record's
+ * states bit for bit. */
+int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                  const da_mesh *mesh, void *y_save, void *stream);
+
+/* Replay plus reverse sweep through the replayed stages, mesh held fixed:
+ * exact gradient of the loss with respect to every trajectory's u0 and p
+ * (review, Strengths and FAQ).  Outputs (each may be NULL): loss_out [n],
+ * grad_u0 [d][n], grad_p [P][n].  The forward states are kept in the
+ * workspace; da_replay_grad_workspace gives the size for all n trajectories
+ * at once given the largest n_steps.  A smaller workspace (at least enough
+ * for 256 trajectories) makes the call process the ensemble in consecutive
+ * chunks; less returns DA_EWORKSPACE. */
+size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps);
+int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out,
+                   void *grad_u0, void *grad_p, int32_t max_n_steps, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/* Message of the last non-zero return on this thread ("" if none). */
+const char *da_last_error(void);
+
+/* Library version (major*10000 + minor*100 + patch). */
+int da_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DADJ_H */

@@ -1,0 +1,62 @@
+"""Shared helpers of the tests: layout conversion and error measures."""
+import numpy as np
+
+import workloads as W
+
+
+def to_dev(x, torch, dev="cuda"):
+    """Lane-major numpy [n, C] -> component-major device tensor [C, n]."""
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(x).T)).to(dev)
+
+
+def aux_to_dev(a, torch, dev="cuda"):
+    """[n, S, d] -> [S, d, n]."""
+    return torch.from_numpy(np.ascontiguousarray(np.transpose(a, (1, 2, 0)))).to(dev)
+
+
+def mesh_to_host(mesh, N=None):
+    """Device mesh (slot order) -> oracle dict (lane-major) in trajectory order."""
+    ns = mesh.n_steps.cpu().numpy()
+    if N is None:
+        N = mesh.h.shape[0]
+    h = mesh.h[:N].cpu().numpy().T.copy()
+    out = {"h": h, "n_steps": ns, "save_idx": mesh.save_idx.cpu().numpy().T.copy(),
+           "status": mesh.status.cpu().numpy()}
+    if mesh.perm is not None:
+        perm = mesh.perm.cpu().numpy()
+        inv = np.empty_like(perm)
+        inv[perm] = np.arange(len(perm))
+        out = {k: v[inv] for k, v in out.items()}
+    return out
+
+
+def mesh_to_dev(m, max_steps, torch, dev="cuda"):
+    import discrete_adjoint_amd as da
+    n, N = m["h"].shape
+    h = np.zeros((max_steps, n), dtype=m["h"].dtype)
+    h[:N] = m["h"].T
+    return da.Mesh(torch.from_numpy(h).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(m["n_steps"].astype(np.int32))).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(m["save_idx"].T.astype(np.int32))).to(dev),
+                   torch.from_numpy(np.ascontiguousarray(m["status"].astype(np.int32))).to(dev))
+
+
+def rel_err(g, ref):
+    """Per-lane ||g - ref||_inf / max(||ref||_inf, 1e-300) over the last axis."""
+    num = np.max(np.abs(g - ref), axis=-1)
+    den = np.maximum(np.max(np.abs(ref), axis=-1), 1e-300)
+    return num / den
+
+
+def grad_rel_err(gu0, gp, gu0_ref, gp_ref):
+    """Per-lane max of the relative errors of the two gradient vectors."""
+    return np.maximum(rel_err(gu0, gu0_ref), rel_err(gp, gp_ref))
+
+
+def mse_targets(orc, wid, n, inp):
+    """Targets of the calibration workload: FP64 oracle record with the perturbed
+    parameters at the save times, cast to the workload dtype; [n, S, d]."""
+    w = W.WORKLOADS[wid]
+    prob = w.problem()
+    m = orc.record(prob, inp["u0"].astype(np.float64), inp["p_true"], with_h=False)
+    return m["y_save"].astype(w.np_dtype), m["status"]

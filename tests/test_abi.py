@@ -1,0 +1,102 @@
+"""The C ABI library: it loads without a GPU, exports every entry point that
+include/dadj.h declares, and rejects invalid arguments before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dadj.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(da_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def da():
+    import discrete_adjoint_amd as da
+    return da
+
+
+def test_library_exports_every_declared_symbol(da):
+    names = _declared()
+    assert "da_record" in names and "da_replay_grad" in names and "da_solve_fwd" in names
+    lib = ctypes.CDLL(da.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(da.EXPORTS)
+    assert da.version() >= 100
+
+
+def _call_record(da, prob, n=4, dtype_code=0, **kw):
+    P, keep = da.cproblem(prob, __import__("torch").float64)
+    P.dtype = dtype_code
+    m = da._Mesh(1, 1, 1, 1, None)
+    return da.library().da_record(ctypes.byref(P), n, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                                  ctypes.byref(m), None, None)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(t1=0.0), -1), (dict(rtol=0.0, atol=0.0), -1), (dict(max_steps=0), -1),
+    (dict(dim=4), -1), (dict(method=7), -1), (dict(rhs=9), -1),
+    (dict(save_times=(0.5, 0.4)), -1), (dict(save_times=(0.5, 2.0)), -1),
+    (dict(rtol=-1.0), -1), (dict(safety=-0.5), -1),
+])
+def test_invalid_problems_rejected(da, change, code):
+    prob = W.WORKLOADS[1].problem(**change)
+    assert _call_record(da, prob) == code
+    assert da.last_error() != ""
+
+
+def test_unsupported_combinations(da):
+    prob = W.Problem(W.LORENZ96, 64, 1, W.ROS2, 0.0, 1.0, 1e-6, 1e-6, 100)
+    assert _call_record(da, prob) in (-1, -2)
+
+
+def test_bad_dtype_and_sizes(da):
+    prob = W.WORKLOADS[1].problem()
+    assert _call_record(da, prob, dtype_code=5) == -1
+    assert _call_record(da, prob, n=-1) == -1
+    assert _call_record(da, prob, n=2**33) == -1
+
+
+def test_null_pointers_rejected(da):
+    prob = W.WORKLOADS[1].problem()
+    P, keep = da.cproblem(prob, __import__("torch").float64)
+    lib = da.library()
+    assert lib.da_record(ctypes.byref(P), 4, None, None, None, None, None) == -1
+    m = da._Mesh(1, 1, 1, 1, None)
+    assert lib.da_record(ctypes.byref(P), 4, None, ctypes.c_void_p(8), ctypes.byref(m), None,
+                         None) == -1
+    loss = da._Loss(1, None, 1.0)   # MSE without targets
+    assert lib.da_replay_grad(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
+                              ctypes.c_void_p(8), 1 << 20, None) == -1
+    loss = da._Loss(0, None, 1.0)
+    # workspace for fewer than 256 trajectories
+    assert lib.da_replay_grad(ctypes.byref(P), 4096, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
+                              ctypes.c_void_p(8), 100, None) == -4
+    assert lib.da_replay_grad(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                              ctypes.byref(m), ctypes.byref(loss), None, None, None, 10**6,
+                              ctypes.c_void_p(8), 1 << 30, None) == -1
+    # sorting needs an output permutation and workspace
+    mo = da._Mesh(2, 2, 2, 2, None)
+    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(m), ctypes.byref(mo),
+                            ctypes.c_void_p(8), 1 << 20, None) == -1
+    mo = da._Mesh(2, 2, 2, 2, 2)
+    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(m), ctypes.byref(mo),
+                            ctypes.c_void_p(8), 4, None) == -4
+
+
+def test_workspace_sizes(da):
+    import torch
+    prob = W.WORKLOADS[2].problem()
+    assert da.replay_grad_workspace(prob, 1000, 700) == 1000 * 700 * 3 * 8
+    assert da.replay_grad_workspace(prob, 1000, 700, torch.float32) == 1000 * 700 * 3 * 4
+    assert da.mesh_sort_workspace(prob, 1 << 20) > 4 * 4 * (1 << 20)

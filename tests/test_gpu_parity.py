@@ -1,0 +1,293 @@
+"""GPU (HIP library, through the C ABI) against the CPU oracle.
+
+Gates (relative error per lane = max over grad_u0, grad_p of
+||g_gpu - g_orc||_inf / ||g_orc||_inf):
+ - gradients on a shared (oracle-recorded) mesh: <= 1e-12 in FP64 against the
+   oracle's fused-rounding mode, <= 1e-4 in FP32 against the FP32 oracle;
+ - a GPU-recorded mesh: every step's re-evaluated error norm <= 1 + 1e-6,
+   |N_gpu - N_orc| <= max(2, 1% of N_orc), same statuses;
+ - the GPU record and the GPU replay give bitwise equal states;
+ - results do not depend on the slot order, the workspace chunking or the run.
+"""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import (aux_to_dev, grad_rel_err, mesh_to_dev, mesh_to_host, mse_targets,
+                     rel_err, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+# (workload, lanes) small enough for the oracle, several tiles and a ragged tail
+SMALL = [(1, 1024), (2, 1000), (3, 1500), (4, 300)]
+TOL = {"f64": 1e-12, "f32": 1e-4}
+
+
+@pytest.fixture(scope="module")
+def da():
+    import discrete_adjoint_amd as da
+    assert torch.cuda.is_available()
+    return da
+
+
+def _setup(orc, wid, n):
+    w = W.WORKLOADS[wid]
+    inp = W.make_inputs(wid, n)
+    prob = w.problem()
+    aux = None
+    scale = 1.0
+    if w.loss == W.MSE_SAVE:
+        aux, st = mse_targets(orc, wid, n, inp)
+        assert np.all(st == 0)
+        scale = 1.0 / (n * w.n_save_eff * w.dim)
+    return w, prob, inp, aux, scale
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("wid,n", SMALL)
+def test_gradient_on_oracle_mesh(da, orc, wid, n):
+    """Shared mesh: the GPU replays the oracle's record."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: gradient on oracle mesh, workload {wid}, n={n}")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    assert np.all(m["status"] == 0)
+    lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, w.loss, aux=aux, scale=scale,
+                                 fused=True)
+    mesh = mesh_to_dev(m, prob.max_steps, torch)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale)
+    torch.cuda.synchronize()
+    g1, g2, L = gu0.cpu().numpy().T, gp.cpu().numpy().T, loss.cpu().numpy()
+    err = grad_rel_err(g1, g2, go, po)
+    _print(f"  max rel err {err.max():.3e}, p99.9 {np.percentile(err, 99.9):.3e}, "
+           f"bitwise equal lanes {np.mean(err == 0):.4f}")
+    assert err.max() <= TOL[w.dtype]
+    assert np.max(np.abs(L - lo) / np.abs(lo)) <= TOL[w.dtype]
+    # against the plain-rounding oracle: reported, loose gate
+    lp, gop, pop = orc.replay_grad(prob, inp["u0"], inp["p"], m, w.loss, aux=aux, scale=scale,
+                                   fused=False)
+    errp = grad_rel_err(g1, g2, gop, pop)
+    _print(f"  vs plain-rounding oracle: max {errp.max():.3e}, median {np.median(errp):.3e}")
+    assert np.median(errp) < (1e-9 if w.dtype == "f64" else 1e-3)
+
+
+@pytest.mark.parametrize("wid,n", SMALL)
+def test_record_within_tolerance_of_oracle(da, orc, wid, n):
+    """GPU-recorded mesh: accepted steps pass the oracle's own error test and the
+    step counts agree with the oracle's record."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: GPU record vs oracle, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, ys = da.record(prob, u0, p)
+    torch.cuda.synchronize()
+    mg = mesh_to_host(mesh)
+    mo = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    assert np.array_equal(mg["status"], mo["status"])
+    ng, no = mg["n_steps"], mo["n_steps"]
+    assert np.all(np.abs(ng - no) <= np.maximum(2, 0.01 * no))
+    same = np.array([np.array_equal(mg["h"][i, :ng[i]], mo["h"][i, :no[i]]) and ng[i] == no[i]
+                     for i in range(n)])
+    _print(f"  bitwise-equal meshes: {same.mean():.4f}; mean steps gpu {ng.mean():.2f} "
+           f"oracle {no.mean():.2f}")
+    # zero padding after the last step
+    hg = mg["h"]
+    pad = np.arange(prob.max_steps)[None, :] >= ng[:, None]
+    assert np.all(hg[pad] == 0)
+    E = orc.mesh_max_err(prob, inp["u0"], inp["p"], mg, fused=True)
+    assert np.all(E <= 1 + 1e-6), E.max()
+    # save indices land on the save times
+    for i in range(0, n, max(1, n // 50)):
+        cs = np.concatenate([[0.0], np.cumsum(hg[i].astype(np.float64))])
+        times = prob.save_times if prob.save_times else (prob.t1,)
+        for s, ts in enumerate(times):
+            assert cs[mg["save_idx"][i, s]] == pytest.approx(ts - prob.t0, rel=1e-6 if w.dtype == "f32" else 1e-12)
+    if wid in (1, 4):
+        # short or non-chaotic: final states agree to the tolerance scale
+        yg = ys.cpu().numpy()[-1].T
+        yo = mo["y_save"][:, -1, :]
+        tol = 10 * (prob.atol + prob.rtol * np.abs(yo))
+        assert np.all(np.abs(yg - yo) <= tol)
+
+
+@pytest.mark.parametrize("wid,n", SMALL)
+def test_gpu_record_equals_gpu_replay(da, orc, wid, n):
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: record == replay, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, ys = da.record(prob, u0, p)
+    yr = da.replay_fwd(prob, u0, p, mesh)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, yr)
+    # and the oracle replays the GPU mesh to the same states (fused rounding)
+    mg = mesh_to_host(mesh)
+    yo, _ = orc.replay(prob, inp["u0"], inp["p"], mg, fused=True)
+    yg = ys.cpu().numpy().transpose(2, 0, 1)
+    err = rel_err(yg.reshape(n, -1), yo.reshape(n, -1))
+    _print(f"  replay of GPU mesh vs oracle: max rel {err.max():.3e}")
+    assert err.max() <= TOL[w.dtype]
+
+
+@pytest.mark.parametrize("wid,n", [(1, 1024), (2, 1000), (3, 777), (4, 300)])
+def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
+    """Lane ordering changes the slot order only: every output is bitwise the
+    same, the permutation is valid and step counts are non-increasing."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: sorted mesh, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    mesh, _ = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    r1 = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale)
+    r2 = da.replay_grad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)
+    y1 = da.replay_fwd(prob, u0, p, mesh)
+    y2 = da.replay_fwd(prob, u0, p, sm)
+    torch.cuda.synchronize()
+    perm = sm.perm.cpu().numpy()
+    assert np.array_equal(np.sort(perm), np.arange(n))
+    ns_sorted = sm.n_steps.cpu().numpy()
+    assert np.all(np.diff(ns_sorted) <= 0)
+    ns = mesh.n_steps.cpu().numpy()
+    assert np.array_equal(ns_sorted, ns[perm])
+    # stable: equal step counts keep their original order
+    for v in np.unique(ns_sorted):
+        sel = perm[ns_sorted == v]
+        assert np.all(np.diff(sel) > 0)
+    assert np.array_equal(mesh_to_host(sm)["h"], mesh_to_host(mesh)["h"])
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+    assert torch.equal(y1, y2)
+
+
+def test_determinism_and_chunking(da, orc):
+    w, prob, inp, aux, scale = _setup(orc, 2, 3000)
+    _print("case: determinism and chunked workspace, workload 2, n=3000")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p)
+    mesh2, _ = da.record(prob, u0, p)
+    torch.cuda.synchronize()
+    assert torch.equal(mesh.h, mesh2.h) and torch.equal(mesh.n_steps, mesh2.n_steps)
+    call = da.ReplayGrad(prob, u0, p, mesh)
+    a = [t.clone() for t in call()]
+    b = [t.clone() for t in call()]
+    N = call.max_n_steps
+    small = da.replay_grad(prob, u0, p, mesh, ws_bytes=512 * N * 3 * 8)   # 6 chunks
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, small):
+        assert torch.equal(x, y) and torch.equal(x, z)
+
+
+def test_loss_kinds_and_cotangents(da, orc):
+    """Cotangent and MSE losses at several save times (FP64)."""
+    w = W.WORKLOADS[2]
+    n = 700
+    prob = w.problem(t1=2.0, save_times=(0.3, 0.9, 1.5, 2.0))
+    inp = W.make_inputs(2, n)
+    _print("case: loss kinds, workload 2 with 4 save times, n=700")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    mesh = mesh_to_dev(m, prob.max_steps, torch)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    aux = np.random.default_rng(0).standard_normal((n, 4, 3))
+    for lk, sc in ((W.COTANGENT, 0.5), (W.MSE_SAVE, 1.0 / 3.0)):
+        lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, lk, aux=aux, scale=sc,
+                                     fused=True)
+        loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, lk, aux=aux_to_dev(aux, torch),
+                                       scale=sc)
+        torch.cuda.synchronize()
+        err = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+        assert err.max() <= 1e-12, (lk, err.max())
+        assert np.allclose(loss.cpu().numpy(), lo, rtol=1e-12)
+
+
+def test_failed_lanes_and_edge_sizes(da, orc):
+    """Lanes that fail report the oracle's status and NaN gradients; n = 1 and
+    n = 0 work; max_steps bounds the record."""
+    w = W.WORKLOADS[1]
+    n = 130
+    inp = W.make_inputs(1, n)
+    inp["p"][5, 0] = np.nan
+    inp["u0"][7, :] = 1e200
+    prob = w.problem(max_steps=30)
+    _print("case: failed lanes, n=130, max_steps=30")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, ys = da.record(prob, u0, p)
+    loss, gu0, gp = da.replay_grad(prob, u0, p, mesh)
+    torch.cuda.synchronize()
+    mo = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    st = mesh.status.cpu().numpy()
+    assert np.array_equal(st, mo["status"])
+    assert st[5] == da.LANE_NONFINITE and st[7] == da.LANE_DT_UNDERFLOW
+    bad = st != 0
+    assert bad.sum() >= 3
+    assert np.all(np.isnan(gp.cpu().numpy()[:, bad])) and np.all(np.isnan(loss.cpu().numpy()[bad]))
+    assert not np.any(np.isnan(gp.cpu().numpy()[:, ~bad]))
+    # n = 1
+    _print("case: n = 1")
+    m1, _ = da.record(w.problem(), u0[:, :1].contiguous(), p[:, :1].contiguous())
+    l1, g1, q1 = da.replay_grad(w.problem(), u0[:, :1].contiguous(), p[:, :1].contiguous(), m1)
+    torch.cuda.synchronize()
+    assert m1.status.item() == 0 and np.isfinite(q1.cpu().numpy()).all()
+    # n = 0: nothing to do, no error
+    _print("case: n = 0")
+    e = torch.empty((3, 0), dtype=torch.float64, device="cuda")
+    m0, _ = da.record(w.problem(), e, e)
+    r0 = da.replay_grad(w.problem(), e, e, m0, max_n_steps=0)
+    assert r0[0].numel() == 0
+
+
+def test_solve_fwd_matches_record(da, orc):
+    for wid, n in ((1, 1000), (3, 500), (4, 200)):
+        w, prob, inp, aux, scale = _setup(orc, wid, n)
+        _print(f"case: solve_fwd, workload {wid}, n={n}")
+        u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+        mesh, ys = da.record(prob, u0, p)
+        yf, ns, st = da.solve_fwd(prob, u0, p)
+        torch.cuda.synchronize()
+        assert torch.equal(ys, yf) and torch.equal(ns, mesh.n_steps) and torch.equal(st, mesh.status)
+
+
+def test_full_size_lorenz_dopri5_sampled(da, orc):
+    """Workload 2 at its full size (2^20 lanes), in the launch configuration of
+    the benchmark (record, lane ordering, replay gradient); a sample of lanes
+    is checked against the oracle on the GPU's own mesh and record."""
+    w = W.WORKLOADS[2]
+    prob = w.problem()
+    inp = W.make_inputs(2)
+    n = w.n
+    _print(f"case: full size workload 2, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p, save=False)
+    sm = da.mesh_sort(prob, mesh)
+    del mesh
+    call = da.ReplayGrad(prob, u0, p, sm)
+    loss, gu0, gp = call()
+    torch.cuda.synchronize()
+    st = sm.status.cpu().numpy()
+    assert np.all(st == 0)
+    perm = sm.perm.cpu().numpy()
+    rng = np.random.default_rng(123)
+    slots = np.sort(rng.choice(n, 512, replace=False))
+    slots = np.unique(np.concatenate([slots, [0, 1, n - 2, n - 1]]))   # longest and shortest
+    tr = perm[slots]
+    idx = torch.from_numpy(slots.astype(np.int64)).cuda()
+    N = int(sm.n_steps.max().item())
+    h = sm.h[:N].index_select(1, idx).cpu().numpy().T.copy()
+    sub = {"h": h, "n_steps": sm.n_steps.cpu().numpy()[slots],
+           "save_idx": sm.save_idx.cpu().numpy()[:, slots].T.copy(), "status": st[slots]}
+    pn = prob.replace(max_steps=N)
+    lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
+    g1 = gu0.cpu().numpy()[:, tr].T
+    g2 = gp.cpu().numpy()[:, tr].T
+    err = grad_rel_err(g1, g2, go, po)
+    _print(f"  sampled {len(slots)} lanes: max rel err {err.max():.3e}, "
+           f"max steps {N}, mean steps {sm.n_steps.float().mean().item():.1f}")
+    assert err.max() <= 1e-12
+    E = orc.mesh_max_err(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
+    assert np.all(E <= 1 + 1e-6)
+    mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
+    no = mo["n_steps"]
+    assert np.all(np.abs(sub["n_steps"] - no) <= np.maximum(2, 0.01 * no))
