@@ -119,6 +119,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   dadj::SaveTimes st;
   int rc = check_problem(prob, n, pr, &st);
   if (rc) return rc;
+  if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true))) return rc;
   if (mesh->perm) return fail(DA_EINVAL, "da_record writes trajectory order: mesh->perm must be NULL");
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
@@ -175,6 +176,7 @@ int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
+  if (n == 0) return ok();
   if ((rc = check_mesh(in, true))) return rc;
   if ((rc = check_mesh(out, true))) return rc;
   if (!out->perm) return fail(DA_EINVAL, "out->perm must not be NULL");
@@ -192,12 +194,13 @@ int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *
 }
 
 int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *stream) {
-  if (!mesh || !mesh->n_steps || !host_max) return fail(DA_EINVAL, "NULL argument");
+  if (!host_max) return fail(DA_EINVAL, "host_max is NULL");
   if (n < 0) return fail(DA_EINVAL, "n < 0");
   if (n == 0) {
     *host_max = 0;
     return ok();
   }
+  if (!mesh || !mesh->n_steps) return fail(DA_EINVAL, "mesh is NULL");
   hipStream_t s = (hipStream_t)stream;
   int32_t *d = nullptr;
   hipError_t e = hipMalloc((void **)&d, sizeof(int32_t));
@@ -216,6 +219,7 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
+  if (n == 0) return ok();
   if ((rc = check_mesh(mesh, false))) return rc;
   if (n > 0 && (!u0 || !p || !y_save)) return fail(DA_EINVAL, "u0, p and y_save must not be NULL");
   if (n == 0) return ok();
@@ -250,6 +254,7 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
+  if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true))) return rc;
   if (!loss) return fail(DA_EINVAL, "loss is NULL");
   if (loss->kind < DA_LOSS_SUMSQ_FINAL || loss->kind > DA_LOSS_COTANGENT)
