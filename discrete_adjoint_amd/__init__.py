@@ -4,7 +4,7 @@ Thin Python binding of ``libdadj.so`` (declared in ``include/dadj.h``): it
 checks and marshals torch tensors (device pointers, the current HIP stream)
 and calls the C ABI.  Every step of the computation runs in the library's HIP
 kernels; there is no fallback.  Importing fails loudly if the library has not
-been built (``python -m discrete_adjoint_amd._build`` or
+been built (``python discrete_adjoint_amd/_build.py`` or
 ``__graft_entry__.build()``).
 
 Layout: per-trajectory tensors are component-major, shape [C, n] (trajectory
@@ -71,7 +71,7 @@ class _Loss(ctypes.Structure):
 def _load_library() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build the HIP library first "
-                          "(python -m discrete_adjoint_amd._build)")
+                          "(python discrete_adjoint_amd/_build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
     P = ctypes.POINTER(_Problem)
