@@ -142,8 +142,7 @@ def main():
     u0 = torch.from_numpy(np.ascontiguousarray(inp["u0"].T)).to(dev)
     p = torch.from_numpy(np.ascontiguousarray(inp["p"].T)).to(dev)
     dt = u0.dtype
-    mesh = da.empty_mesh(prob, n, dt, dev)
-    smesh = da.empty_mesh(prob, n, dt, dev, with_perm=True)
+    mesh = da.empty_mesh(prob, n, dt, dev, with_perm=True)
     sort_ws = torch.empty(da.mesh_sort_workspace(prob, n, dt), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     state = {"call": None, "N": -1}
@@ -153,11 +152,11 @@ def main():
         if e: e["rec0"].record(stream)
         da.record(prob, u0, p, mesh=mesh, save=False)
         if e: e["rec1"].record(stream)
-        da.mesh_sort(prob, mesh, out=smesh, workspace=sort_ws)
+        da.mesh_sort(prob, mesh, perm=mesh.perm, workspace=sort_ws)
         if e: e["sort1"].record(stream)
-        N = da.mesh_max_steps(smesh)          # sizes the workspace (host sync)
+        N = da.mesh_max_steps(mesh)           # sizes the workspace (host sync)
         if N != state["N"]:
-            state["call"] = da.ReplayGrad(prob, u0, p, smesh, W.SUMSQ_FINAL, max_n_steps=N)
+            state["call"] = da.ReplayGrad(prob, u0, p, mesh, W.SUMSQ_FINAL, max_n_steps=N)
             state["N"] = N
         for k in range(passes):
             if e: e["p0"][k].record(stream)
@@ -184,7 +183,7 @@ def main():
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
     pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
                              for k in range(passes)]))
-    ns = smesh.n_steps.double()
+    ns = mesh.n_steps.double()
     total_steps = float(ns.sum().item())
     mean_steps = total_steps / n
     flop_step = FLOP_PER_STEP[(W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs])]

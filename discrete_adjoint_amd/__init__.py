@@ -10,7 +10,11 @@ been built (``python discrete_adjoint_amd/_build.py`` or
 Layout: per-trajectory tensors are component-major, shape [C, n] (trajectory
 index last and contiguous): u0 [d, n], p [P, n], y_save [S, d, n], grad_u0
 [d, n], grad_p [P, n], with S = max(1, len(problem.save_times)).  The mesh is
-h [max_steps, n], n_steps [n], save_idx [S, n], status [n], perm [n] or None.
+h [T, n, B] (tiled step log: B = 8 steps per 64-byte chunk in float64, 16 in
+float32, T = ceil(max_steps / B); ``Mesh.steps()`` gives the [n, max_steps]
+view), n_steps [n], save_idx [S, n], status [n], perm [n] or None (a
+replay order) and h_rows [rows, n] or None (the replay table: step k of the
+trajectory of lane j at [k, j]); ``mesh_sort`` fills the last two.
 
 The problem description is ``workloads.Problem`` (or any object with the same
 fields) plus a dtype taken from the tensors.
@@ -25,7 +29,9 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdadj.so")
+# DADJ_LIBRARY may name another build of the same sources (e.g. one made
+# with different build options); the default is the in-tree libdadj.so.
+LIB_PATH = os.environ.get("DADJ_LIBRARY") or os.path.join(_HERE, "libdadj.so")
 
 DA_F64, DA_F32 = 0, 1
 TSIT5, DOPRI5, ROS2 = 0, 1, 2
@@ -35,7 +41,7 @@ LANE_OK, LANE_MAX_STEPS, LANE_DT_UNDERFLOW, LANE_NONFINITE, LANE_MAX_ATTEMPTS = 
 DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EHIP, DA_EWORKSPACE = 0, -1, -2, -3, -4
 MAX_SAVES = 128
 
-EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_sort_workspace", "da_mesh_sort",
+EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
            "da_last_error", "da_version")
 
@@ -55,13 +61,15 @@ class _Problem(ctypes.Structure):
         ("max_steps", ctypes.c_int32), ("max_attempts", ctypes.c_int32),
         ("n_save", ctypes.c_int32), ("save_times", ctypes.POINTER(ctypes.c_double)),
         ("safety", ctypes.c_double), ("fac_min", ctypes.c_double), ("fac_max", ctypes.c_double),
+        ("checkpoint", ctypes.c_int32),
     ]
 
 
 class _Mesh(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("n_steps", ctypes.c_void_p),
                 ("save_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
-                ("perm", ctypes.c_void_p)]
+                ("perm", ctypes.c_void_p), ("h_rows", ctypes.c_void_p),
+                ("rows", ctypes.c_int32)]
 
 
 class _Loss(ctypes.Structure):
@@ -78,9 +86,11 @@ def _load_library() -> ctypes.CDLL:
     M = ctypes.POINTER(_Mesh)
     lib.da_record.argtypes = [P, i64, vp, vp, M, vp, vp]
     lib.da_solve_fwd.argtypes = [P, i64, vp, vp, vp, vp, vp, vp]
+    lib.da_mesh_h_elems.argtypes = [P, i64]
+    lib.da_mesh_h_elems.restype = ctypes.c_int64
     lib.da_mesh_sort_workspace.argtypes = [P, i64]
     lib.da_mesh_sort_workspace.restype = ctypes.c_size_t
-    lib.da_mesh_sort.argtypes = [P, i64, M, M, vp, ctypes.c_size_t, vp]
+    lib.da_mesh_sort.argtypes = [P, i64, M, vp, ctypes.c_size_t, vp]
     lib.da_mesh_max_steps.argtypes = [i64, M, ctypes.POINTER(ctypes.c_int32), vp]
     lib.da_replay_fwd.argtypes = [P, i64, vp, vp, M, vp, vp]
     lib.da_replay_grad_workspace.argtypes = [P, i64, i32]
@@ -129,7 +139,7 @@ def cproblem(prob, dtype) -> tuple:
                  prob.t0, prob.t1, prob.rtol, prob.atol, prob.dt0, prob.max_steps,
                  prob.max_attempts, len(prob.save_times),
                  ctypes.cast(st, ctypes.POINTER(ctypes.c_double)) if len(prob.save_times) else None,
-                 prob.safety, prob.fac_min, prob.fac_max)
+                 prob.safety, prob.fac_min, prob.fac_max, getattr(prob, "checkpoint", 0))
     return P, st
 
 
@@ -155,28 +165,51 @@ def _need(t: torch.Tensor, shape, dtype, name: str):
         raise ValueError(f"{name} must be contiguous")
 
 
+def chunk_steps(dtype) -> int:
+    """Steps per 64-byte chunk of the step log."""
+    return 8 if dtype == torch.float64 else 16
+
+
 @dataclasses.dataclass
 class Mesh:
-    """The record: step sizes [max_steps, n], n_steps [n], save_idx [S, n],
-    status [n] and the slot -> trajectory permutation [n] (None = identity)."""
+    """The record: tiled step log h [T, n, B], n_steps [n], save_idx [S, n],
+    status [n]; an optional replay order perm [n] (None = identity) and
+    replay table h_rows [rows, n]."""
     h: torch.Tensor
     n_steps: torch.Tensor
     save_idx: torch.Tensor
     status: torch.Tensor
     perm: Optional[torch.Tensor] = None
+    h_rows: Optional[torch.Tensor] = None
 
     @property
     def n(self) -> int:
         return self.n_steps.shape[0]
 
+    def steps(self, max_steps: Optional[int] = None) -> torch.Tensor:
+        """Step sizes as an [n, K] tensor (a copy), K = max_steps or T * B."""
+        T, n, B = self.h.shape
+        out = self.h.permute(1, 0, 2).reshape(n, T * B)
+        return (out if max_steps is None else out[:, :max_steps]).contiguous()
+
     def c(self) -> _Mesh:
         return _Mesh(self.h.data_ptr(), self.n_steps.data_ptr(), self.save_idx.data_ptr(),
-                     self.status.data_ptr(), None if self.perm is None else self.perm.data_ptr())
+                     self.status.data_ptr(), None if self.perm is None else self.perm.data_ptr(),
+                     None if self.h_rows is None else self.h_rows.data_ptr(),
+                     0 if self.h_rows is None else self.h_rows.shape[0])
+
+
+def mesh_h_shape(prob, n: int, dtype) -> tuple:
+    B = chunk_steps(dtype)
+    return ((prob.max_steps + B - 1) // B, n, B)
 
 
 def empty_mesh(prob, n: int, dtype, device="cuda", with_perm: bool = False) -> Mesh:
     S = max(1, len(prob.save_times))
-    return Mesh(torch.empty((prob.max_steps, n), dtype=dtype, device=device),
+    h = torch.empty(mesh_h_shape(prob, n, dtype), dtype=dtype, device=device)
+    P, keep = cproblem(prob, dtype)
+    assert h.numel() == _lib.da_mesh_h_elems(ctypes.byref(P), n) or n == 0
+    return Mesh(h,
                 torch.empty(n, dtype=torch.int32, device=device),
                 torch.empty((S, n), dtype=torch.int32, device=device),
                 torch.empty(n, dtype=torch.int32, device=device),
@@ -222,19 +255,32 @@ def mesh_sort_workspace(prob, n: int, dtype=torch.float64) -> int:
     return int(_lib.da_mesh_sort_workspace(ctypes.byref(P), n))
 
 
-def mesh_sort(prob, mesh: Mesh, out: Optional[Mesh] = None, workspace=None, stream=None) -> Mesh:
-    """Mesh with slots reordered by decreasing step count (and its permutation)."""
+def mesh_sort(prob, mesh: Mesh, perm: Optional[torch.Tensor] = None, table: bool = True,
+              rows: Optional[int] = None, h_rows: Optional[torch.Tensor] = None,
+              workspace=None, stream=None) -> Mesh:
+    """The same record with a replay order by decreasing step count and, with
+    ``table``, the replay table of ``rows`` rows (default: the largest step
+    count, read back from the GPU).  Returns a new Mesh that shares the
+    record's arrays; ``perm`` and ``h_rows`` may be given to reuse storage."""
     n = mesh.n
     dt = mesh.h.dtype
-    if out is None:
-        out = empty_mesh(prob, n, dt, mesh.h.device, with_perm=True)
+    dev = mesh.h.device
+    if perm is None:
+        perm = torch.empty(n, dtype=torch.int32, device=dev)
+    if table and h_rows is None:
+        if rows is None:
+            rows = max(1, mesh_max_steps(mesh, stream))
+        h_rows = torch.empty((rows, n), dtype=dt, device=dev)
+    if not table:
+        h_rows = None
     need = mesh_sort_workspace(prob, n, dt)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=mesh.h.device)
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    out = Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, perm, h_rows)
     P, keep = cproblem(prob, dt)
-    ci, co = mesh.c(), out.c()
-    _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(ci), ctypes.byref(co),
-                             _ptr(workspace), workspace.numel(), _stream(stream)))
+    co = out.c()
+    _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(co), _ptr(workspace),
+                             workspace.numel(), _stream(stream)))
     return out
 
 

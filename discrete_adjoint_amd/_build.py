@@ -27,21 +27,23 @@ def _obj_dir() -> str:
     return d
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(_obj_dir(), os.path.splitext(src)[0] + ".o")
-    subprocess.run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj], check=True)
+def _compile(src: str, extra=(), tag: str = "") -> str:
+    obj = os.path.join(_obj_dir(), os.path.splitext(src)[0] + tag + ".o")
+    subprocess.run([HIPCC, *CFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj], check=True)
     return obj
 
 
-def build(jobs: int = 4) -> str:
-    """Compile every source and link libdadj.so; returns its path."""
+def build(jobs: int = 4, out: str = LIB, extra=()) -> str:
+    """Compile every source and link libdadj.so (or `out`, with extra compiler
+    flags such as -D build options); returns its path."""
+    tag = "" if out == LIB else "_" + os.path.basename(out).replace(".", "_")
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra, tag), SOURCES))
+    tmp = out + ".tmp"
     subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs],
                    check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

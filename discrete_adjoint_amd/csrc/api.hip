@@ -41,6 +41,17 @@ bool shape_ok(int rhs, int d, int P) {
 
 size_t dsize(int dtype) { return dtype == DA_F64 ? 8 : 4; }
 
+// Checkpoint interval of the reverse sweep when the caller leaves it to the
+// library.
+int default_checkpoint(const da_problem &pb) {
+  (void)pb;
+  return 1;
+}
+
+int resolved_checkpoint(const da_problem &pb) {
+  return pb.checkpoint > 0 ? pb.checkpoint : default_checkpoint(pb);
+}
+
 // Validates the problem and resolves defaults.
 int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::SaveTimes *st) {
   if (!pb) return fail(DA_EINVAL, "problem is NULL");
@@ -74,6 +85,9 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   }
   if (!(pb->safety >= 0 && pb->fac_min >= 0 && pb->fac_max >= 0) || pb->max_attempts < 0)
     return fail(DA_EINVAL, "negative controller option");
+  if (pb->checkpoint != 0 && pb->checkpoint != 1 && pb->checkpoint != 2 && pb->checkpoint != 4 &&
+      pb->checkpoint != 8)
+    return fail(DA_EINVAL, "checkpoint must be 0, 1, 2, 4 or 8");
   pr.rhs = pb->rhs;
   pr.dim = pb->dim;
   pr.n_params = pb->n_params;
@@ -91,6 +105,9 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   pr.safety = pb->safety > 0 ? pb->safety : 0.9;
   pr.fac_min = pb->fac_min > 0 ? pb->fac_min : 0.2;
   pr.fac_max = pb->fac_max > 0 ? pb->fac_max : 10.0;
+  const int B = dadj::chunk_steps(pb->dtype);
+  pr.n_chunks = (pb->max_steps + B - 1) / B;
+  pr.checkpoint = pb->checkpoint > 0 ? pb->checkpoint : default_checkpoint(*pb);
   if (st) {
     memset(st, 0, sizeof *st);
     for (int s = 0; s < pb->n_save; ++s) st->t[s] = pb->save_times[s];
@@ -98,11 +115,31 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   return DA_OK;
 }
 
-int check_mesh(const da_mesh *m, bool need_status) {
+int check_mesh(const da_mesh *m, bool need_status, int32_t max_steps) {
   if (!m) return fail(DA_EINVAL, "mesh is NULL");
   if (!m->h || !m->n_steps || !m->save_idx || (need_status && !m->status))
     return fail(DA_EINVAL, "mesh arrays must not be NULL");
+  if ((uintptr_t)m->h % dadj::CHUNK_BYTES != 0)
+    return fail(DA_EINVAL, "mesh->h must be %d-byte aligned", dadj::CHUNK_BYTES);
+  if (m->h_rows && (m->rows < 1 || m->rows > max_steps))
+    return fail(DA_EINVAL, "mesh->rows = %d must be in [1, max_steps] with h_rows", m->rows);
   return DA_OK;
+}
+
+void fill_replay_args(dadj::ReplayArgs &a, const dadj::ProbArgs &pr, int64_t n, const void *u0,
+                      const void *p, const da_mesh *mesh) {
+  memset(&a, 0, sizeof a);
+  a.pr = pr;
+  a.n = n;
+  a.u0 = u0;
+  a.p = p;
+  a.h = mesh->h;
+  a.h_rows = mesh->h_rows;
+  a.rows = mesh->h_rows ? mesh->rows : 0;
+  a.nsteps = mesh->n_steps;
+  a.sidx = mesh->save_idx;
+  a.status = mesh->status;
+  a.perm = mesh->perm;
 }
 
 }  // namespace
@@ -120,8 +157,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   int rc = check_problem(prob, n, pr, &st);
   if (rc) return rc;
   if (n == 0) return ok();
-  if ((rc = check_mesh(mesh, true))) return rc;
-  if (mesh->perm) return fail(DA_EINVAL, "da_record writes trajectory order: mesh->perm must be NULL");
+  if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
   if (n == 0) return ok();
   dadj::RecordArgs a;
@@ -166,29 +202,34 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
   return ok();
 }
 
-size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n) {
-  if (!prob || n <= 0) return 0;
-  return dadj::sort_workspace_bytes(n, prob->max_steps);
+int64_t da_mesh_h_elems(const da_problem *prob, int64_t n) {
+  if (!prob || n <= 0 || prob->max_steps < 1 || (prob->dtype != DA_F64 && prob->dtype != DA_F32))
+    return 0;
+  const int B = dadj::chunk_steps(prob->dtype);
+  return (int64_t)((prob->max_steps + B - 1) / B) * n * B;
 }
 
-int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *out,
-                 void *workspace, size_t ws_bytes, void *stream) {
+size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n) {
+  if (!prob || n <= 0) return 0;
+  return dadj::sort_workspace_bytes(n);
+}
+
+int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspace,
+                 size_t ws_bytes, void *stream) {
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
   if (n == 0) return ok();
-  if ((rc = check_mesh(in, true))) return rc;
-  if ((rc = check_mesh(out, true))) return rc;
-  if (!out->perm) return fail(DA_EINVAL, "out->perm must not be NULL");
-  if (out->h == in->h || out->n_steps == in->n_steps || out->save_idx == in->save_idx ||
-      out->status == in->status || (in->perm && out->perm == in->perm))
-    return fail(DA_EINVAL, "out must not alias in");
-  if (n == 0) return ok();
-  const size_t need = dadj::sort_workspace_bytes(n, pr.max_steps);
+  if ((rc = check_mesh(mesh, false, pr.max_steps))) return rc;
+  if (!mesh->perm) return fail(DA_EINVAL, "mesh->perm must not be NULL");
+  const size_t need = dadj::sort_workspace_bytes(n);
   if (!workspace || ws_bytes < need)
     return fail(DA_EWORKSPACE, "mesh sort needs %zu bytes of workspace, got %zu", need, ws_bytes);
-  da_mesh o = *out;
-  const hipError_t e = dadj::launch_mesh_sort(pr, n, *in, o, workspace, ws_bytes, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = dadj::launch_mesh_sort(pr, n, mesh->n_steps, mesh->perm, workspace, ws_bytes, s);
+  if (e == hipSuccess && mesh->h_rows)
+    e = dadj::launch_replay_table(pr, n, mesh->h, mesh->n_steps, mesh->perm, mesh->h_rows,
+                                  mesh->rows, s);
   if (e != hipSuccess) return hip_fail(e, "mesh sort launch");
   return ok();
 }
@@ -220,20 +261,11 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
   if (n == 0) return ok();
-  if ((rc = check_mesh(mesh, false))) return rc;
+  if ((rc = check_mesh(mesh, false, pr.max_steps))) return rc;
   if (n > 0 && (!u0 || !p || !y_save)) return fail(DA_EINVAL, "u0, p and y_save must not be NULL");
   if (n == 0) return ok();
   dadj::ReplayArgs a;
-  memset(&a, 0, sizeof a);
-  a.pr = pr;
-  a.n = n;
-  a.u0 = u0;
-  a.p = p;
-  a.h = mesh->h;
-  a.nsteps = mesh->n_steps;
-  a.sidx = mesh->save_idx;
-  a.status = mesh->status;
-  a.perm = mesh->perm;
+  fill_replay_args(a, pr, n, u0, p, mesh);
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_replay_fwd(a, s)
@@ -243,8 +275,11 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
 }
 
 size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps) {
-  if (!prob || n <= 0 || max_n_steps <= 0) return 0;
-  return (size_t)n * (size_t)max_n_steps * (size_t)prob->dim * dsize(prob->dtype);
+  if (!prob || n <= 0 || max_n_steps <= 0 || prob->dim <= 0) return 0;
+  const int ck = resolved_checkpoint(*prob);
+  if (ck <= 0 || ck > 8) return 0;
+  return (size_t)n * (size_t)((max_n_steps + ck - 1) / ck) * (size_t)prob->dim *
+         dsize(prob->dtype);
 }
 
 int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
@@ -255,7 +290,7 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
   if (n == 0) return ok();
-  if ((rc = check_mesh(mesh, true))) return rc;
+  if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
   if (!loss) return fail(DA_EINVAL, "loss is NULL");
   if (loss->kind < DA_LOSS_SUMSQ_FINAL || loss->kind > DA_LOSS_COTANGENT)
     return fail(DA_EINVAL, "bad loss kind %d", loss->kind);
@@ -266,7 +301,8 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
     return fail(DA_EINVAL, "max_n_steps must be in [0, max_steps]");
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
   if (n == 0) return ok();
-  const size_t per_lane = (size_t)max_n_steps * pr.dim * dsize(pr.dtype);
+  const size_t per_lane =
+      (size_t)((max_n_steps + pr.checkpoint - 1) / pr.checkpoint) * pr.dim * dsize(pr.dtype);
   int64_t C = n;
   if (per_lane > 0) {
     if (!workspace) return fail(DA_EWORKSPACE, "workspace is NULL");
@@ -279,16 +315,7 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
     }
   }
   dadj::ReplayArgs a;
-  memset(&a, 0, sizeof a);
-  a.pr = pr;
-  a.n = n;
-  a.u0 = u0;
-  a.p = p;
-  a.h = mesh->h;
-  a.nsteps = mesh->n_steps;
-  a.sidx = mesh->save_idx;
-  a.status = mesh->status;
-  a.perm = mesh->perm;
+  fill_replay_args(a, pr, n, u0, p, mesh);
   a.loss_kind = loss->kind;
   a.aux = loss->aux;
   a.scale = loss->scale;

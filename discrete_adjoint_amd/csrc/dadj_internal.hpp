@@ -9,6 +9,10 @@
 namespace dadj {
 
 constexpr int BLOCK = 256;  // threads per workgroup of the lane-per-trajectory kernels
+constexpr int CHUNK_BYTES = 64;  // step-log chunk owned by one trajectory
+
+// Steps per chunk of the tiled step log.
+constexpr int chunk_steps(int dtype) { return dtype == DA_F64 ? 8 : 16; }
 
 enum { LANE_OK = 0, LANE_MAX_STEPS = 1, LANE_DT_UNDERFLOW = 2, LANE_NONFINITE = 3,
        LANE_MAX_ATTEMPTS = 4 };
@@ -17,6 +21,8 @@ enum { LANE_OK = 0, LANE_MAX_STEPS = 1, LANE_DT_UNDERFLOW = 2, LANE_NONFINITE = 
 struct ProbArgs {
   int32_t rhs, dim, n_params, method, dtype;
   int32_t max_steps, max_attempts, n_save, S;  // S = max(1, n_save)
+  int32_t n_chunks;                             // T = ceil(max_steps / B)
+  int32_t checkpoint;                           // resolved: 1, 2, 4 or 8
   double t0, t1, rtol, atol, dt0, safety, fac_min, fac_max;
 };
 
@@ -29,7 +35,7 @@ struct RecordArgs {
   ProbArgs pr;
   int64_t n;
   const void *u0, *p;
-  void *h;              // [max_steps][n] or null (forward solve)
+  void *h;              // [T][n][B] or null (forward solve)
   int32_t *nsteps;      // [n] or null
   int32_t *sidx;        // [S][n] or null
   int32_t *status;      // [n] or null
@@ -40,14 +46,16 @@ struct ReplayArgs {
   ProbArgs pr;
   int64_t n;
   const void *u0, *p;
-  const void *h;
+  const void *h;               // tiled step log [T][n][B]
+  const void *h_rows;          // replay table [rows][n] in lane order, or null
+  int32_t rows;
   const int32_t *nsteps, *sidx, *status, *perm;
   void *y_save;                // replay_fwd output [S][d][n]
   int32_t loss_kind;
   const void *aux;             // [S][d][n]
   double scale;
   void *loss_out, *gu0, *gp;   // [n], [d][n], [P][n]
-  void *ws;                    // [max_n_steps][d][ws_lanes]
+  void *ws;                    // [ceil(max_n_steps / checkpoint)][d][ws_lanes]
   int64_t slot0, nslots, ws_lanes;
   int32_t max_n_steps;
 };
@@ -60,9 +68,12 @@ hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s);
 
 // Mesh utilities
-size_t sort_workspace_bytes(int64_t n, int32_t max_steps);
-hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const da_mesh &in, da_mesh &out,
+size_t sort_workspace_bytes(int64_t n);
+hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps, int32_t *perm,
                             void *ws, size_t ws_bytes, hipStream_t s);
+hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
+                               const int32_t *nsteps, const int32_t *perm, void *h_rows,
+                               int32_t rows, hipStream_t s);
 hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s);
 
 }  // namespace dadj

@@ -61,17 +61,19 @@ struct Erk {
   // Reverse of fwd at y = y_k: lam (dL/dy_{k+1} -> dL/dy_k), g += dL/dp.
   //   kbar_i = h (b_i lam + sum_{l>i} a[l][i] w_l),  w_i = J(Y_i)^T kbar_i,
   //   g += J_p(Y_i)^T kbar_i,  lam <- lam + w_5 + w_4 + ... + w_0.
-  // Stage states Y_1..Y_5 are recomputed from y_k.
+  // Stage states Y_1..Y_5 are recomputed from y_k; the stage slopes are dead
+  // once the states are formed, and the w_i are summed into lam at the end
+  // in the order of the formula.
   template <class T>
   __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
-    T Y[7][D], K[7][D], Wv[7][D], kb[D], lacc[D];
-    Rhs::f(y, p, K[0]);
-    erk_stages<Tab, Rhs, 5, false>(y, p, h, Y, K);
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      Y[0][c] = y[c];
-      lacc[c] = lam[c];
+    T Y[7][D], Wv[7][D], kb[D];
+    {
+      T K[7][D];
+      Rhs::f(y, p, K[0]);
+      erk_stages<Tab, Rhs, 5, false>(y, p, h, Y, K);
     }
+#pragma unroll
+    for (int c = 0; c < D; ++c) Y[0][c] = y[c];
 #pragma unroll
     for (int i = 5; i >= 0; --i) {
 #pragma unroll
@@ -93,11 +95,14 @@ struct Erk {
       }
       Rhs::vjp_y(Y[i], p, kb, Wv[i]);
       Rhs::vjp_p_acc(Y[i], p, kb, g);
-#pragma unroll
-      for (int c = 0; c < D; ++c) lacc[c] = lacc[c] + Wv[i][c];
     }
 #pragma unroll
-    for (int c = 0; c < D; ++c) lam[c] = lacc[c];
+    for (int c = 0; c < D; ++c) {
+      T s = lam[c];
+#pragma unroll
+      for (int i = 5; i >= 0; --i) s = s + Wv[i][c];
+      lam[c] = s;
+    }
   }
 };
 

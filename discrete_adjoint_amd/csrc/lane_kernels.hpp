@@ -1,17 +1,18 @@
 // Lane-per-trajectory kernels, generic over the integration method M.
 //
-//  k_record<T, M, LOG>   adaptive solve of one trajectory per lane; with LOG it
-//                        writes every accepted step size into the mesh
-//                        ("GRADSOLVE: fast exact gradients for ODE ensembles on
-//                        GPUs", gptget.net summary, Methodology; evolve.pub
-//                        review, Summary: zero-padded fixed-length mesh), without
-//                        it it is the forward-only solve (summary, Key results).
-//  k_replay_fwd<T, M>    fixed-step replay of a mesh (review, Summary).
-//  k_replay_grad<T, M>   replay that keeps each y_k in the workspace, then the
-//                        reverse sweep through the recomputed stages with the
-//                        mesh held fixed (review, Strengths (paper section 3.1)
-//                        and FAQ: the exact discrete adjoint, no derivative of
-//                        the step-size choices).
+//  k_record<T, M, LOG>    adaptive solve of one trajectory per lane; with LOG
+//                         it writes every accepted step size into the tiled
+//                         step log ("GRADSOLVE: fast exact gradients for ODE
+//                         ensembles on GPUs", gptget.net summary, Methodology;
+//                         evolve.pub review, Summary: zero-padded fixed-length
+//                         mesh), without it it is the forward-only solve
+//                         (summary, Key results).
+//  k_replay_fwd<T, M>     fixed-step replay of a mesh (review, Summary).
+//  k_replay_grad<T, M, C> replay that keeps every C-th state in the workspace,
+//                         then the reverse sweep through the recomputed stages
+//                         with the mesh held fixed (review, Strengths (paper
+//                         section 3.1) and FAQ: the exact discrete adjoint, no
+//                         derivative of the step-size choices).
 //
 // A method M provides:
 //   using Rhs; order (for the starting step); err_order (controller exponent)
@@ -21,12 +22,26 @@
 //   accepted(cache)                                  after an accepted trial
 //   fwd(y, p, h)                                     one replay step
 //   adj(y, p, h, lam, g)                             its reverse
+//
+// Memory: per-trajectory arrays are component-major ([c][n], trajectory
+// fastest).  The step log is tiled [T][n][B]: each trajectory owns one 64-byte
+// chunk of B steps per tile, so the record writes whole chunks and a replay
+// in any lane order reads whole chunks.  The replays read step k + 1 (and the
+// reverse sweep its checkpoint) while step k computes.
 #pragma once
 
 #include <math.h>
 
 #include "dadj_device.hpp"
 #include "dadj_internal.hpp"
+
+// Build option: DADJ_GRAD_WAVES_PER_EU=w asks the compiler to fit the
+// gradient kernel into the registers of w wavefronts per SIMD.
+#ifdef DADJ_GRAD_WAVES_PER_EU
+#define DADJ_GRAD_OCCUPANCY __attribute__((amdgpu_waves_per_eu(DADJ_GRAD_WAVES_PER_EU)))
+#else
+#define DADJ_GRAD_OCCUPANCY
+#endif
 
 namespace dadj {
 
@@ -38,6 +53,32 @@ __device__ __forceinline__ double dsqrt(double a) { return sqrt(a); }
 __device__ __forceinline__ float dsqrt(float a) { return sqrtf(a); }
 __device__ __forceinline__ double dabs(double a) { return fabs(a); }
 __device__ __forceinline__ float dabs(float a) { return fabsf(a); }
+
+// ---------------------------------------------------------------------------
+// Tiled step log
+// ---------------------------------------------------------------------------
+template <class T> struct Log {
+  static constexpr int B = CHUNK_BYTES / (int)sizeof(T);
+  // offset of step k from the lane's first element H + tr * B
+  __device__ static __forceinline__ int64_t at(int k, int64_t n) {
+    return (int64_t)(k / B) * n * B + (k % B);
+  }
+};
+
+typedef double dvec2 __attribute__((ext_vector_type(2)));
+typedef float fvec4 __attribute__((ext_vector_type(4)));
+
+// One 64-byte chunk from registers to memory as four 16-byte stores.
+__device__ __forceinline__ void store_chunk(double *dst, const double (&v)[8]) {
+  dvec2 *d = (dvec2 *)dst;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = dvec2{v[2 * q], v[2 * q + 1]};
+}
+__device__ __forceinline__ void store_chunk(float *dst, const float (&v)[16]) {
+  fvec4 *d = (fvec4 *)dst;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q] = fvec4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
 
 // RMS of v / sc over D components.
 template <int D, class T>
@@ -89,12 +130,15 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // Record / forward solve.  Controller: accept iff E <= 1; next step = used
 // step * clamp(safety E^(-1/(q+1)), fac_min, fac_max), no growth right after
 // a rejection, fac_max when E == 0, fac_min when E is not finite.  Steps land
-// exactly on every save time and on t1; t accumulates in double.
+// exactly on every save time and on t1; t accumulates in double.  Accepted
+// steps collect in a register chunk that is written when full; after the
+// last step the partial chunk and zero chunks up to the end of the log follow.
 // ---------------------------------------------------------------------------
 template <class T, class M, bool LOG>
 __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
+  constexpr int B = Log<T>::B;
   const int64_t n = a.n;
   const int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
   const bool live = i < n;
@@ -111,6 +155,9 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   T *ysave = (T *)a.y_save;
 
   int nacc = 0, natt = 0, st = LANE_OK;
+  T hb[B];
+#pragma unroll
+  for (int b = 0; b < B; ++b) hb[b] = T(0);
   if (live) {
     T y[D], p[P], ynew[D], err[D];
     typename M::template Cache<T> cache;
@@ -153,7 +200,16 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         M::attempt(y, p, hs, cache, ynew, err);
         const T E = err_norm<D>(err, y, ynew, atol, rtol);
         if (E <= T(1)) {
-          if (LOG) H[(int64_t)nacc * n + i] = hs;
+          if (LOG) {
+            const int pos = nacc % B;
+#pragma unroll
+            for (int b = 0; b < B; ++b) hb[b] = (b == pos) ? hs : hb[b];
+            if (pos == B - 1) {
+              store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
+#pragma unroll
+              for (int b = 0; b < B; ++b) hb[b] = T(0);
+            }
+          }
           ++nacc;
 #pragma unroll
           for (int c = 0; c < D; ++c) y[c] = ynew[c];
@@ -181,27 +237,88 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     }
     if (a.nsteps) a.nsteps[i] = nacc;
     if (a.status) a.status[i] = st;
+    if (LOG && nacc % B != 0) store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
   }
   if (LOG) {
-    // zero padding after each lane's last step, written row by row across the wave
-    const int mine = live ? nacc : pr.max_steps;
-    int kmin = mine;
+    // zero chunks after each lane's last one, chunk row by chunk row across
+    // the wavefront (hb is all zero here except for lanes that still hold a
+    // partial chunk, which start one chunk later)
+    const int Tn = pr.n_chunks;
+    const int mine = live ? (nacc + B - 1) / B : Tn;
+    int tmin = mine;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
-      const int o = __shfl_xor(kmin, off, 64);
-      kmin = o < kmin ? o : kmin;
+      const int o = __shfl_xor(tmin, off, 64);
+      tmin = o < tmin ? o : tmin;
     }
-    kmin = __builtin_amdgcn_readfirstlane(kmin);
-    for (int k = kmin; k < pr.max_steps; ++k)
-      if (k >= mine) H[(int64_t)k * n + i] = T(0);
+    tmin = __builtin_amdgcn_readfirstlane(tmin);
+    T zb[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) zb[b] = T(0);
+    for (int t = tmin; t < Tn; ++t)
+      if (t >= mine) store_chunk(H + ((int64_t)t * n + i) * B, zb);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Replay forward: the state after save_idx[s] steps goes to y_save[s]; save
-// slots whose index lies outside [0, n_steps] get NaN.
+// Where a replay lane finds its step sizes: a row of the replay table (one
+// contiguous row segment per wavefront and step) or its trajectory's chunks
+// of the tiled log.  `cap` is the number of steps the source holds; loads
+// are clamped to it so that prefetches past the end stay in bounds.
 // ---------------------------------------------------------------------------
-template <class T, class M>
+template <class T, bool ROWS> struct StepSrc {
+  typedef __attribute__((address_space(1))) const T GT;  // global memory
+  GT *base;
+  int64_t n;
+  int cap;
+  __device__ __forceinline__ void init(const ReplayArgs &a, int64_t j, int64_t tr) {
+    n = a.n;
+    if constexpr (ROWS) {
+      base = (GT *)a.h_rows + j;
+      cap = a.rows;
+    } else {
+      base = (GT *)a.h + tr * Log<T>::B;
+      cap = a.pr.n_chunks * Log<T>::B;
+    }
+  }
+  __device__ __forceinline__ T load(int k) const {
+    k = k < cap ? k : cap - 1;
+    k = k < 0 ? 0 : k;
+    if constexpr (ROWS) return base[(int64_t)k * n];
+    else return base[Log<T>::at(k, n)];
+  }
+};
+
+// Lane j of a replay: its trajectory, step count and whether it replays.
+// Lanes that need more steps than the step source holds (or than `limit`),
+// and with `need_ok` lanes whose record failed, replay nothing and report
+// NaN.
+struct LaneInfo {
+  int64_t tr;
+  int N;
+  bool ok;
+};
+__device__ __forceinline__ LaneInfo lane_info(const ReplayArgs &a, int64_t j, bool live,
+                                              int limit, bool need_ok) {
+  LaneInfo L{0, 0, false};
+  if (live) {
+    L.tr = a.perm ? a.perm[j] : j;
+    const int N = a.nsteps[L.tr];
+    const int cap = a.h_rows ? a.rows : a.pr.max_steps;
+    L.ok = (!need_ok || a.status[L.tr] == LANE_OK) && N >= 0 && N <= cap && N <= limit;
+    L.N = L.ok ? N : 0;
+  }
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Replay forward: the state after save_idx[s] steps goes to y_save[s]; save
+// slots whose index lies outside [0, n_steps], and every slot of a lane that
+// does not replay, get NaN.  Two steps per loop trip so that the step size of
+// the next step is loaded into the register the next step reads (no copy,
+// so no wait on the load until that step).
+// ---------------------------------------------------------------------------
+template <class T, class M, bool ROWS>
 __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
@@ -209,46 +326,49 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
   const int64_t j = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
   const bool live = j < n;
   const int S = a.pr.S;
-  const T *H = (const T *)a.h;
   T *ysave = (T *)a.y_save;
-  int N = 0;
-  int64_t tr = j;
+  const LaneInfo L = lane_info(a, j, live, a.pr.max_steps, false);
+  const int64_t tr = L.tr;
+  const int N = L.N;
+  StepSrc<T, ROWS> src;
+  src.init(a, live ? j : 0, tr);
   T y[D], p[P];
   if (live) {
-    tr = a.perm ? a.perm[j] : j;
-    N = a.nsteps[j];
-    N = N < 0 ? 0 : (N > a.pr.max_steps ? a.pr.max_steps : N);
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = ((const T *)a.u0)[c * n + tr];
 #pragma unroll
     for (int q = 0; q < P; ++q) p[q] = ((const T *)a.p)[q * n + tr];
     for (int q = 0; q < S; ++q) {
-      const int ix = a.sidx[q * n + j];
-      if (ix < 0 || ix > N)
+      const int ix = a.sidx[q * n + tr];
+      if (!L.ok || ix < 0 || ix > N)
 #pragma unroll
         for (int c = 0; c < D; ++c) ysave[(q * D + c) * n + tr] = nanv<T>();
     }
   }
   const int Nw = wave_max(N);
   int s = 0;
-  int nxt = live ? a.sidx[j] : -1;
-  while (live && s < S && nxt == 0) {
+  int nxt = L.ok ? a.sidx[tr] : -1;
+  auto save = [&](int k) {
+    while (s < S && nxt == k) {
 #pragma unroll
-    for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = y[c];
-    ++s;
-    nxt = s < S ? a.sidx[s * n + j] : -1;
-  }
-  for (int k = 0; k < Nw; ++k) {
-    if (k < N) {
-      const T hk = H[(int64_t)k * n + j];
-      M::fwd(y, p, hk);
-      while (s < S && nxt == k + 1) {
-#pragma unroll
-        for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = y[c];
-        ++s;
-        nxt = s < S ? a.sidx[s * n + j] : -1;
-      }
+      for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = y[c];
+      ++s;
+      nxt = s < S ? a.sidx[s * n + tr] : -1;
     }
+  };
+  save(0);
+  auto step = [&](int k, T hk) {
+    if (k < N) {
+      M::fwd(y, p, hk);
+      save(k + 1);
+    }
+  };
+  T hA = src.load(0);
+  for (int k = 0; k < Nw; k += 2) {
+    const T hB = src.load(k + 1);
+    step(k, hA);
+    hA = src.load(k + 2);
+    if (k + 1 < Nw) step(k + 1, hB);
   }
 }
 
@@ -282,9 +402,19 @@ __device__ __forceinline__ void seed_terms(int lk, const T (&y)[D], const T *aux
   }
 }
 
-// Workspace layout: y_k of local slot jl at ws[(k * D + c) * ws_lanes + jl].
-template <class T, class M>
-__global__ __launch_bounds__(BLOCK) void k_replay_grad(ReplayArgs a) {
+// Workspace: checkpoint m (the state before step m * CK) of local lane jl at
+// ws[(m * D + c) * ws_lanes + jl].  The forward replay writes the
+// checkpoints; the reverse sweep walks the segments of CK steps from the
+// last, recomputes the segment's states from its checkpoint in registers and
+// runs the adjoint of its steps in reverse.  Segments are taken two per loop
+// trip from two register sets (A, B): while one segment computes, the loads
+// of the next one (its checkpoint and step sizes) are in flight.
+template <class T, int D, int CK> struct Seg {
+  T cp[D], h[CK];
+};
+
+template <class T, class M, int CK, bool ROWS>
+__global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(ReplayArgs a) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
   const int64_t n = a.n;
@@ -294,47 +424,57 @@ __global__ __launch_bounds__(BLOCK) void k_replay_grad(ReplayArgs a) {
   const int64_t C = a.ws_lanes;
   const int S = a.pr.S;
   const int lk = a.loss_kind;
-  const T *H = (const T *)a.h;
+  const bool saves = lk != DA_LOSS_SUMSQ_FINAL;  // loss terms at save indices
   const T *aux = (const T *)a.aux;
-  T *ws = (T *)a.ws;
-  int N = 0;
-  bool ok = false;
-  int64_t tr = j;
+  // lanes past the end read (and never use) lane 0's workspace column, so
+  // that the unconditional prefetches below stay inside the workspace
+  T *ws = (T *)a.ws + (live ? jl : 0);
+  const LaneInfo L = lane_info(a, j, live, a.max_n_steps, true);
+  const int64_t tr = L.tr;
+  const int N = L.N;
+  const bool ok = L.ok;
+  StepSrc<T, ROWS> src;
+  src.init(a, live ? j : a.slot0, tr);
   T y[D], p[P];
   if (live) {
-    tr = a.perm ? a.perm[j] : j;
-    N = a.nsteps[j];
-    ok = a.status[j] == LANE_OK && N >= 0 && N <= a.max_n_steps;
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = ((const T *)a.u0)[c * n + tr];
 #pragma unroll
     for (int q = 0; q < P; ++q) p[q] = ((const T *)a.p)[q * n + tr];
   }
-  if (!ok) N = 0;
   const int Nw = wave_max(N);
 
-  // ---- forward replay, keeping y_k; loss terms at the save indices ----
+  // ---- forward replay, keeping every CK-th state; loss terms at the saves ----
   T ss = T(0);
   bool first = true;
   int s = 0;
-  int nxt = (ok && lk != DA_LOSS_SUMSQ_FINAL) ? a.sidx[j] : -1;
-  while (s < S && nxt == 0) {
-    loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
-    ++s;
-    nxt = s < S ? a.sidx[s * n + j] : -1;
-  }
-  for (int k = 0; k < Nw; ++k) {
+  int nxt = (ok && saves) ? a.sidx[tr] : -1;
+  auto terms = [&](int k) {
+    while (s < S && nxt == k) {
+      loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
+      ++s;
+      nxt = s < S ? a.sidx[s * n + tr] : -1;
+    }
+  };
+  if (saves) terms(0);
+  auto fstep = [&](int k, T hk) {
     if (k < N) {
-      T *wk = ws + (int64_t)k * D * C + jl;
+      if (k % CK == 0) {
+        T *wk = ws + (int64_t)(k / CK) * D * C;
 #pragma unroll
-      for (int c = 0; c < D; ++c) wk[c * C] = y[c];
-      const T hk = H[(int64_t)k * n + j];
-      M::fwd(y, p, hk);
-      if (nxt == k + 1) {
-        loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
-        ++s;
-        nxt = s < S ? a.sidx[s * n + j] : -1;
+        for (int c = 0; c < D; ++c) wk[c * C] = y[c];
       }
+      M::fwd(y, p, hk);
+      if (saves) terms(k + 1);
+    }
+  };
+  {
+    T hA = src.load(0);
+    for (int k = 0; k < Nw; k += 2) {
+      const T hB = src.load(k + 1);
+      fstep(k, hA);
+      hA = src.load(k + 2);
+      if (k + 1 < Nw) fstep(k + 1, hB);
     }
   }
 
@@ -342,7 +482,7 @@ __global__ __launch_bounds__(BLOCK) void k_replay_grad(ReplayArgs a) {
   T lam[D], g[P];
 #pragma unroll
   for (int q = 0; q < P; ++q) g[q] = T(0);
-  if (lk == DA_LOSS_SUMSQ_FINAL) {
+  if (!saves) {
 #pragma unroll
     for (int c = 0; c < D; ++c) ss = (c == 0) ? y[c] * y[c] : mac(y[c], y[c], ss);
 #pragma unroll
@@ -352,33 +492,61 @@ __global__ __launch_bounds__(BLOCK) void k_replay_grad(ReplayArgs a) {
     for (int c = 0; c < D; ++c) lam[c] = T(0);
   }
   int sh = S - 1;
-  int hidx = (ok && lk != DA_LOSS_SUMSQ_FINAL) ? a.sidx[(int64_t)sh * n + j] : -1;
-  while (sh >= 0 && hidx == N) {
-    seed_terms<T, D>(lk, y, aux, n, sh, tr, a.scale, lam);
-    --sh;
-    hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + j] : -1;
-  }
+  int hidx = (ok && saves) ? a.sidx[(int64_t)sh * n + tr] : -1;
+  auto seeds = [&](int k, const T (&yk)[D]) {
+    while (sh >= 0 && hidx == k) {
+      seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
+      --sh;
+      hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+    }
+  };
+  if (saves) seeds(N, y);
 
-  // ---- reverse sweep ----
-  for (int k = Nw - 1; k >= 0; --k) {
-    if (k < N) {
-      const T *wk = ws + (int64_t)k * D * C + jl;
-      T yk[D];
+  // ---- reverse sweep, one segment of CK steps at a time ----
+  // Every index stays inside the buffers: segments m < Mw = ceil(Nw / CK);
+  // the workspace holds ceil(max_n_steps / CK) >= Mw checkpoints; step loads
+  // are clamped to the step source.
+  const int Mw = (Nw + CK - 1) / CK;
+  auto fetch = [&](int m, Seg<T, D, CK> &sg) {
+    m = m < 0 ? 0 : m;
 #pragma unroll
-      for (int c = 0; c < D; ++c) yk[c] = wk[c * C];
-      const T hk = H[(int64_t)k * n + j];
-      M::adj(yk, p, hk, lam, g);
-      while (sh >= 0 && hidx == k) {
-        seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
-        --sh;
-        hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + j] : -1;
+    for (int c = 0; c < D; ++c) sg.cp[c] = ws[((int64_t)m * D + c) * C];
+#pragma unroll
+    for (int b = 0; b < CK; ++b) sg.h[b] = src.load(m * CK + b);
+  };
+  auto rseg = [&](int m, const Seg<T, D, CK> &sg) {
+    T ys[CK][D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) ys[0][c] = sg.cp[c];
+#pragma unroll
+    for (int b = 1; b < CK; ++b) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) ys[b][c] = ys[b - 1][c];
+      if (m * CK + b - 1 < N) M::fwd(ys[b], p, sg.h[b - 1]);
+    }
+#pragma unroll
+    for (int b = CK - 1; b >= 0; --b) {
+      const int k = m * CK + b;
+      if (k < N) {
+        M::adj(ys[b], p, sg.h[b], lam, g);
+        if (saves) seeds(k, ys[b]);
       }
+    }
+  };
+  if (Mw > 0) {
+    Seg<T, D, CK> A, B;
+    fetch(Mw - 1, A);
+    for (int m = Mw - 1; m >= 0; m -= 2) {
+      fetch(m - 1, B);
+      rseg(m, A);
+      fetch(m - 2, A);
+      if (m - 1 >= 0) rseg(m - 1, B);
     }
   }
 
   if (live) {
-    const T L = ok ? T(a.scale) * ss : nanv<T>();
-    if (a.loss_out) ((T *)a.loss_out)[tr] = L;
+    const T Lv = ok ? T(a.scale) * ss : nanv<T>();
+    if (a.loss_out) ((T *)a.loss_out)[tr] = Lv;
     if (a.gu0)
 #pragma unroll
       for (int c = 0; c < D; ++c) ((T *)a.gu0)[c * n + tr] = ok ? lam[c] : nanv<T>();
@@ -402,15 +570,27 @@ hipError_t record_t(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
 template <class T, class M>
 hipError_t replay_fwd_t(const ReplayArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.n + BLOCK - 1) / BLOCK);
-  hipLaunchKernelGGL((k_replay_fwd<T, M>), grid, BLOCK, 0, s, a);
+  if (a.h_rows) hipLaunchKernelGGL((k_replay_fwd<T, M, true>), grid, BLOCK, 0, s, a);
+  else hipLaunchKernelGGL((k_replay_fwd<T, M, false>), grid, BLOCK, 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, class M, bool ROWS>
+hipError_t replay_grad_ck(const ReplayArgs &a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.nslots + BLOCK - 1) / BLOCK);
+  switch (a.pr.checkpoint) {
+    case 1: hipLaunchKernelGGL((k_replay_grad<T, M, 1, ROWS>), grid, BLOCK, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_replay_grad<T, M, 2, ROWS>), grid, BLOCK, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_replay_grad<T, M, 4, ROWS>), grid, BLOCK, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_replay_grad<T, M, 8, ROWS>), grid, BLOCK, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 template <class T, class M>
 hipError_t replay_grad_t(const ReplayArgs &a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.nslots + BLOCK - 1) / BLOCK);
-  hipLaunchKernelGGL((k_replay_grad<T, M>), grid, BLOCK, 0, s, a);
-  return hipGetLastError();
+  return a.h_rows ? replay_grad_ck<T, M, true>(a, s) : replay_grad_ck<T, M, false>(a, s);
 }
 
 }  // namespace dadj

@@ -1,4 +1,4 @@
-// Mesh utilities: lane ordering by step count and the largest step count.
+// Mesh utilities: replay order by step count and the largest step count.
 //
 // Lane ordering.  Trajectories of one ensemble need different numbers of
 // accepted steps (the GRADSOLVE review, Strengths, quotes a max/mean of
@@ -6,7 +6,9 @@
 // as its longest lane needs, so slots are reordered by decreasing n_steps:
 // neighbouring lanes then carry nearly equal work.  The sort is a stable LSD
 // radix sort over 8-bit digits of key = max_steps - n_steps (deterministic:
-// no atomics), followed by a gather of the mesh into the new slot order.
+// no atomics) of (key, trajectory) pairs; the sorted trajectories are the
+// replay order.  The mesh itself is not moved: with the tiled step log a lane
+// reads whole 64-byte chunks of its trajectory wherever they lie.
 #include "dadj_internal.hpp"
 
 namespace dadj {
@@ -122,32 +124,58 @@ __global__ __launch_bounds__(SORT_THREADS) void k_scatter(int64_t n, int shift, 
   }
 }
 
-// out slot j takes in slot src = order[j]
-__global__ __launch_bounds__(SORT_THREADS) void k_gather_meta(int64_t n, int S,
-                                                              const int32_t *__restrict__ order,
-                                                              da_mesh in, da_mesh out) {
-  const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
-  if (j >= n) return;
-  const int64_t src = order[j];
-  out.n_steps[j] = in.n_steps[src];
-  out.status[j] = in.status[src];
-  out.perm[j] = in.perm ? in.perm[src] : (int32_t)src;
-  for (int s = 0; s < S; ++s) out.save_idx[(int64_t)s * n + j] = in.save_idx[(int64_t)s * n + src];
+// Replay table: lane j (trajectory perm[j]) reads its trajectory's 64-byte
+// chunks of the tiled log whole and writes them as B consecutive rows, each
+// store a contiguous row segment across the wavefront; zeros after n_steps.
+typedef double dvec2 __attribute__((ext_vector_type(2)));
+typedef float fvec4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void load_chunk(const double *src, double (&v)[8]) {
+  const dvec2 *s = (const dvec2 *)src;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const dvec2 x = s[q];
+    v[2 * q] = x.x;
+    v[2 * q + 1] = x.y;
+  }
+}
+__device__ __forceinline__ void load_chunk(const float *src, float (&v)[16]) {
+  const fvec4 *s = (const fvec4 *)src;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const fvec4 x = s[q];
+    v[4 * q] = x.x;
+    v[4 * q + 1] = x.y;
+    v[4 * q + 2] = x.z;
+    v[4 * q + 3] = x.w;
+  }
 }
 
 template <class T>
-__global__ __launch_bounds__(SORT_THREADS) void k_gather_h(int64_t n, int32_t max_steps,
-                                                           const int32_t *__restrict__ order,
-                                                           const int32_t *__restrict__ ns_out,
-                                                           const T *__restrict__ hin,
-                                                           T *__restrict__ hout) {
+__global__ __launch_bounds__(SORT_THREADS) void k_replay_table(
+    int64_t n, int32_t max_steps, const T *__restrict__ h, const int32_t *__restrict__ nsteps,
+    const int32_t *__restrict__ perm, T *__restrict__ out, int32_t rows) {
+  constexpr int B = 64 / (int)sizeof(T);
   const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
-  const bool live = j < n;
-  const int64_t src = live ? order[j] : 0;
-  int N = live ? ns_out[j] : 0;
+  if (j >= n) return;
+  const int64_t tr = perm ? perm[j] : j;
+  int N = nsteps[tr];
   N = N < 0 ? 0 : (N > max_steps ? max_steps : N);
-  for (int k = 0; k < max_steps; ++k)
-    if (live) hout[(int64_t)k * n + j] = k < N ? hin[(int64_t)k * n + src] : T(0);
+  const int tmax = (rows + B - 1) / B;
+  for (int t = 0; t < tmax; ++t) {
+    T c[B];
+    if (t * B < N) {
+      load_chunk(h + ((int64_t)t * n + tr) * B, c);
+    } else {
+#pragma unroll
+      for (int b = 0; b < B; ++b) c[b] = T(0);
+    }
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+      const int k = t * B + b;
+      if (k < rows) out[(int64_t)k * n + j] = k < N ? c[b] : T(0);
+    }
+  }
 }
 
 __global__ __launch_bounds__(1024) void k_max_steps(int64_t n, const int32_t *__restrict__ ns,
@@ -175,27 +203,30 @@ int key_bits(int32_t max_steps) {
 
 }  // namespace
 
-size_t sort_workspace_bytes(int64_t n, int32_t max_steps) {
-  (void)max_steps;
+size_t sort_workspace_bytes(int64_t n) {
   const int64_t ntiles = (n + SORT_TILE - 1) / SORT_TILE;
-  return 2 * align_up((size_t)n * 4) + 2 * align_up((size_t)n * 4) +
-         align_up((size_t)ntiles * RADIX * 4);
+  return 3 * align_up((size_t)n * 4) + align_up((size_t)ntiles * RADIX * 4);
 }
 
-hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const da_mesh &in, da_mesh &out,
+// Radix passes ping-pong between (kA, vA) and (kB, vB); the values of the
+// last pass land in `perm`, which serves as one of the two value buffers.
+hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps, int32_t *perm,
                             void *ws, size_t ws_bytes, hipStream_t s) {
   if (n == 0) return hipSuccess;
-  if (ws_bytes < sort_workspace_bytes(n, pr.max_steps)) return hipErrorInvalidValue;
+  if (ws_bytes < sort_workspace_bytes(n)) return hipErrorInvalidValue;
   const int64_t ntiles = (n + SORT_TILE - 1) / SORT_TILE;
-  char *p = (char *)ws;
-  unsigned *kA = (unsigned *)p; p += align_up((size_t)n * 4);
-  unsigned *kB = (unsigned *)p; p += align_up((size_t)n * 4);
-  int32_t *vA = (int32_t *)p; p += align_up((size_t)n * 4);
-  int32_t *vB = (int32_t *)p; p += align_up((size_t)n * 4);
-  unsigned *counts = (unsigned *)p;
-  const unsigned g1 = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
-  hipLaunchKernelGGL(k_init_keys, g1, SORT_THREADS, 0, s, n, pr.max_steps, in.n_steps, kA, vA);
   const int bits = key_bits(pr.max_steps);
+  const int passes = (bits + 7) / 8;
+  char *q = (char *)ws;
+  unsigned *kA = (unsigned *)q; q += align_up((size_t)n * 4);
+  unsigned *kB = (unsigned *)q; q += align_up((size_t)n * 4);
+  int32_t *vX = (int32_t *)q; q += align_up((size_t)n * 4);
+  unsigned *counts = (unsigned *)q;
+  // choose the initial value buffer so that the last pass writes `perm`
+  int32_t *vA = (passes % 2 == 0) ? perm : vX;
+  int32_t *vB = (passes % 2 == 0) ? vX : perm;
+  const unsigned g1 = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
+  hipLaunchKernelGGL(k_init_keys, g1, SORT_THREADS, 0, s, n, pr.max_steps, nsteps, kA, vA);
   for (int shift = 0; shift < bits; shift += 8) {
     hipLaunchKernelGGL(k_hist, (unsigned)ntiles, SORT_THREADS, 0, s, n, shift, kA, counts, ntiles);
     hipLaunchKernelGGL(k_scan, 1, SORT_THREADS, 0, s, counts, ntiles * RADIX);
@@ -204,13 +235,20 @@ hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const da_mesh &in, da
     unsigned *tk = kA; kA = kB; kB = tk;
     int32_t *tv = vA; vA = vB; vB = tv;
   }
-  hipLaunchKernelGGL(k_gather_meta, g1, SORT_THREADS, 0, s, n, pr.S, vA, in, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
+                               const int32_t *nsteps, const int32_t *perm, void *h_rows,
+                               int32_t rows, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const unsigned g1 = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
   if (pr.dtype == DA_F64)
-    hipLaunchKernelGGL(k_gather_h<double>, g1, SORT_THREADS, 0, s, n, pr.max_steps, vA,
-                       out.n_steps, (const double *)in.h, (double *)out.h);
+    hipLaunchKernelGGL(k_replay_table<double>, g1, SORT_THREADS, 0, s, n, pr.max_steps,
+                       (const double *)h, nsteps, perm, (double *)h_rows, rows);
   else
-    hipLaunchKernelGGL(k_gather_h<float>, g1, SORT_THREADS, 0, s, n, pr.max_steps, vA,
-                       out.n_steps, (const float *)in.h, (float *)out.h);
+    hipLaunchKernelGGL(k_replay_table<float>, g1, SORT_THREADS, 0, s, n, pr.max_steps,
+                       (const float *)h, nsteps, perm, (float *)h_rows, rows);
   return hipGetLastError();
 }
 

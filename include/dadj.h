@@ -18,8 +18,9 @@
  *                       (review, Strengths: paper section 3.1; FAQ on
  *                       exactness), repeated for many passes against one record.
  *   3. da_solve_fwd   - the forward-only adaptive solve (summary, Key results).
- * plus da_replay_fwd (forward replay only) and da_mesh_sort (lane ordering by
- * step count so that each wavefront's lanes carry similar work).
+ * plus da_replay_fwd (forward replay only) and da_mesh_sort (a replay order of
+ * the trajectories by step count so that each wavefront's lanes carry similar
+ * work).
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers unless marked "host"; all memory is
@@ -114,23 +115,51 @@ typedef struct {
   int32_t n_save;      /* 0..DA_MAX_SAVES; 0 = the final state is the only save */
   const double *save_times; /* host, n_save values strictly increasing in (t0, t1] */
   double safety, fac_min, fac_max;
+  int32_t checkpoint;  /* reverse sweep of da_replay_grad: the forward replay
+                          keeps every checkpoint-th state in the workspace and
+                          the sweep recomputes the states in between in
+                          registers; 1 = keep every state; 0 = the library's
+                          choice for the right-hand side.  1, 2, 4 or 8 (or
+                          0).  The result does not depend on it.             */
 } da_problem;
 
 /* The record: one zero-padded step mesh per trajectory, reused by every
- * replay until the next record.  S = max(1, n_save) save slots.
- * Arrays are indexed by SLOT j in [0, n).  Without a permutation (perm ==
- * NULL) slot j holds trajectory j.  With one, slot j holds trajectory perm[j]
- * and the replay entry points gather inputs and scatter outputs through it;
- * inputs and outputs of every entry point stay in trajectory order. */
+ * replay until the next record.  S = max(1, n_save) save slots.  Every array
+ * is in trajectory order.
+ *
+ * The step log is tiled so that each trajectory owns 64-byte chunks of B
+ * consecutive steps, B = 8 (F64) or 16 (F32), and a wavefront's chunks are
+ * adjacent: step k of trajectory i is element ((k / B) * n + i) * B + k % B,
+ * for k < T * B with T = ceil(max_steps / B) chunks.  Steps at and after
+ * n_steps[i] are zero (a zero step leaves the state unchanged).  h must be
+ * 64-byte aligned; da_mesh_h_elems gives its length.
+ *
+ * perm is a replay order: NULL replays trajectory j on lane j; otherwise lane
+ * j replays trajectory perm[j] (da_mesh_sort makes one).  It only schedules
+ * work: inputs and outputs stay in trajectory order and results do not
+ * depend on it.  da_record neither reads nor writes it.
+ *
+ * h_rows is an optional replay table, the same step sizes laid out for the
+ * replay: row k holds step k of the trajectory of every lane,
+ * h_rows[k * n + j] = step k of trajectory perm[j] (of j without perm), zero
+ * at and after its n_steps, for k < rows.  A wavefront then reads one
+ * contiguous row segment per step.  da_mesh_sort fills it; the replays read
+ * it instead of h when it is not NULL, and report a trajectory with more than
+ * `rows` steps as failed (NaN outputs). */
 typedef struct {
-  void *h;           /* [max_steps][n]: accepted step sizes of each slot,
-                        zeros after its n_steps-th step                       */
+  void *h;           /* [T][n][B] accepted step sizes, zero padded            */
   int32_t *n_steps;  /* [n] accepted steps                                    */
   int32_t *save_idx; /* [S][n] mesh index k at which save time s is reached
                         (the state after k steps); -1 if never reached        */
   int32_t *status;   /* [n] da_lane_status                                    */
-  int32_t *perm;     /* [n] slot -> trajectory, or NULL for the identity      */
+  int32_t *perm;     /* [n] lane -> trajectory replay order, or NULL          */
+  void *h_rows;      /* [rows][n] replay table, or NULL                       */
+  int32_t rows;      /* rows of h_rows (1..max_steps when h_rows is set)      */
 } da_mesh;
+
+/* Elements (of the problem's dtype) of the step log of n trajectories:
+ * T * n * B.  0 for a NULL problem or n <= 0. */
+int64_t da_mesh_h_elems(const da_problem *prob, int64_t n);
 
 /* Scalar loss of the replayed states; the gradient is of the sum over
  * trajectories, i.e. per trajectory of its own term:
@@ -153,9 +182,9 @@ typedef struct {
 
 /* Record: one adaptive solve per trajectory (summary, Methodology: record the
  * accepted steps; review, Summary: zero-padded fixed-length mesh).
- * u0 [d][n], p [P][n]; fills mesh->h, n_steps, save_idx, status in trajectory
- * order (mesh->perm must be NULL) and, if y_save is not NULL, y_save
- * [S][d][n] with the state at each save time (NaN where not reached). */
+ * u0 [d][n], p [P][n]; fills mesh->h (every chunk, padding included),
+ * n_steps, save_idx and status, and, if y_save is not NULL, y_save [S][d][n]
+ * with the state at each save time (NaN where not reached). */
 int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p,
               da_mesh *mesh, void *y_save, void *stream);
 
@@ -165,13 +194,18 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p,
 int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p,
                  void *y_save, int32_t *n_steps, int32_t *status, void *stream);
 
-/* Lane ordering: writes into `out` the mesh of `in` with slots reordered by
- * decreasing n_steps (stable, so deterministic), and out->perm (required).
- * `in` may itself be permuted.  `out` must not alias `in`.  Work space of
+/* Lane ordering: fills mesh->perm (required, [n]) with the trajectories in
+ * order of decreasing n_steps; equal counts keep their index order, so the
+ * order is deterministic.  Replaying in this order gives each wavefront
+ * lanes of nearly equal step counts (the GRADSOLVE review, Strengths, quotes
+ * the paper's Table 5: max/mean step count 1.33-1.34 across an ensemble).
+ * When mesh->h_rows is not NULL it also writes the replay table in that
+ * order (mesh->rows rows; da_mesh_max_steps gives the smallest that holds
+ * every trajectory).  Reads n_steps and h.  Work space of
  * da_mesh_sort_workspace bytes is required. */
 size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n);
-int da_mesh_sort(const da_problem *prob, int64_t n, const da_mesh *in, da_mesh *out,
-                 void *workspace, size_t ws_bytes, void *stream);
+int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspace,
+                 size_t ws_bytes, void *stream);
 
 /* Largest n_steps over the mesh, returned to the host (synchronises the
  * stream).  Used to size the replay workspace. */
@@ -186,11 +220,13 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
 /* Replay plus reverse sweep through the replayed stages, mesh held fixed:
  * exact gradient of the loss with respect to every trajectory's u0 and p
  * (review, Strengths and FAQ).  Outputs (each may be NULL): loss_out [n],
- * grad_u0 [d][n], grad_p [P][n].  The forward states are kept in the
- * workspace; da_replay_grad_workspace gives the size for all n trajectories
- * at once given the largest n_steps.  A smaller workspace (at least enough
- * for 256 trajectories) makes the call process the ensemble in consecutive
- * chunks; less returns DA_EWORKSPACE. */
+ * grad_u0 [d][n], grad_p [P][n].  Checkpoint states of the forward replay
+ * (see da_problem.checkpoint) are kept in the workspace;
+ * da_replay_grad_workspace gives the size for all n trajectories at once
+ * given max_n_steps, an upper bound of n_steps over the trajectories (the
+ * trajectories above it are reported as failed, NaN).  A smaller workspace
+ * (at least enough for 256 trajectories) makes the call process the
+ * ensemble in consecutive chunks; less returns DA_EWORKSPACE. */
 size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps);
 int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
                    const da_mesh *mesh, const da_loss *loss, void *loss_out,

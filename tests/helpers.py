@@ -14,27 +14,29 @@ def aux_to_dev(a, torch, dev="cuda"):
     return torch.from_numpy(np.ascontiguousarray(np.transpose(a, (1, 2, 0)))).to(dev)
 
 
-def mesh_to_host(mesh, N=None):
-    """Device mesh (slot order) -> oracle dict (lane-major) in trajectory order."""
+def mesh_to_host(mesh, N):
+    """Device mesh (tiled log, trajectory order) -> oracle dict (lane-major)
+    with the first N steps of every trajectory (the oracle's row length is its
+    problem's max_steps); the replay order, if any, is not part of it."""
     ns = mesh.n_steps.cpu().numpy()
-    if N is None:
-        N = mesh.h.shape[0]
-    h = mesh.h[:N].cpu().numpy().T.copy()
-    out = {"h": h, "n_steps": ns, "save_idx": mesh.save_idx.cpu().numpy().T.copy(),
-           "status": mesh.status.cpu().numpy()}
-    if mesh.perm is not None:
-        perm = mesh.perm.cpu().numpy()
-        inv = np.empty_like(perm)
-        inv[perm] = np.arange(len(perm))
-        out = {k: v[inv] for k, v in out.items()}
-    return out
+    h = mesh.steps(N).cpu().numpy()
+    return {"h": h, "n_steps": ns, "save_idx": mesh.save_idx.cpu().numpy().T.copy(),
+            "status": mesh.status.cpu().numpy()}
+
+
+def tile_steps(h_rows, max_steps, B):
+    """[n, N] step sizes -> tiled [T, n, B] log with zero padding."""
+    n, N = h_rows.shape
+    T = (max_steps + B - 1) // B
+    full = np.zeros((n, T * B), dtype=h_rows.dtype)
+    full[:, :N] = h_rows
+    return np.ascontiguousarray(full.reshape(n, T, B).transpose(1, 0, 2))
 
 
 def mesh_to_dev(m, max_steps, torch, dev="cuda"):
     import discrete_adjoint_amd as da
-    n, N = m["h"].shape
-    h = np.zeros((max_steps, n), dtype=m["h"].dtype)
-    h[:N] = m["h"].T
+    B = 8 if m["h"].dtype == np.float64 else 16
+    h = tile_steps(m["h"], max_steps, B)
     return da.Mesh(torch.from_numpy(h).to(dev),
                    torch.from_numpy(np.ascontiguousarray(m["n_steps"].astype(np.int32))).to(dev),
                    torch.from_numpy(np.ascontiguousarray(m["save_idx"].T.astype(np.int32))).to(dev),

@@ -78,6 +78,7 @@ def test_null_pointers_rejected(da):
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
                               ctypes.c_void_p(8), 1 << 20, None) == -1
     loss = da._Loss(0, None, 1.0)
+    m = da._Mesh(64, 8, 8, 8, None)   # plausible (aligned) addresses; nothing is launched
     # workspace for fewer than 256 trajectories
     assert lib.da_replay_grad(ctypes.byref(P), 4096, ctypes.c_void_p(8), ctypes.c_void_p(8),
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
@@ -85,18 +86,53 @@ def test_null_pointers_rejected(da):
     assert lib.da_replay_grad(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10**6,
                               ctypes.c_void_p(8), 1 << 30, None) == -1
-    # sorting needs an output permutation and workspace
-    mo = da._Mesh(2, 2, 2, 2, None)
-    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(m), ctypes.byref(mo),
-                            ctypes.c_void_p(8), 1 << 20, None) == -1
-    mo = da._Mesh(2, 2, 2, 2, 2)
-    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(m), ctypes.byref(mo),
-                            ctypes.c_void_p(8), 4, None) == -4
+    # sorting needs a permutation array and workspace
+    mo = da._Mesh(64, 8, 8, 8, None)
+    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(mo), ctypes.c_void_p(8), 1 << 20,
+                            None) == -1
+    mo = da._Mesh(64, 8, 8, 8, 8)
+    assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(mo), ctypes.c_void_p(8), 4,
+                            None) == -4
+    # a replay table needs 1 <= rows <= max_steps
+    mr = da._Mesh(64, 8, 8, 8, 8, 64, 0)
+    assert lib.da_replay_fwd(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                             ctypes.byref(mr), ctypes.c_void_p(8), None) == -1
+    mr = da._Mesh(64, 8, 8, 8, 8, 64, prob.max_steps + 1)
+    assert lib.da_replay_fwd(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                             ctypes.byref(mr), ctypes.c_void_p(8), None) == -1
+    assert "rows" in da.last_error()
+    # the record writes 64-byte chunks: an unaligned step log is refused
+    mu = da._Mesh(72, 8, 8, 8, None)
+    assert lib.da_record(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
+                         ctypes.byref(mu), None, None) == -1
+    assert "aligned" in da.last_error()
+
+
+@pytest.mark.parametrize("ck", [3, 5, 16, -1])
+def test_bad_checkpoint_rejected(da, ck):
+    prob = W.WORKLOADS[1].problem(checkpoint=ck)
+    assert _call_record(da, prob) == -1
+    assert "checkpoint" in da.last_error()
 
 
 def test_workspace_sizes(da):
     import torch
-    prob = W.WORKLOADS[2].problem()
+    prob = W.WORKLOADS[2].problem(checkpoint=1)
     assert da.replay_grad_workspace(prob, 1000, 700) == 1000 * 700 * 3 * 8
     assert da.replay_grad_workspace(prob, 1000, 700, torch.float32) == 1000 * 700 * 3 * 4
-    assert da.mesh_sort_workspace(prob, 1 << 20) > 4 * 4 * (1 << 20)
+    for ck in (2, 4, 8):
+        assert da.replay_grad_workspace(prob.replace(checkpoint=ck), 1000, 700) == \
+            1000 * ((700 + ck - 1) // ck) * 3 * 8
+    assert da.replay_grad_workspace(prob.replace(checkpoint=0), 1000, 700) > 0
+    assert da.mesh_sort_workspace(prob, 1 << 20) >= 3 * 4 * (1 << 20)
+
+
+def test_step_log_length(da):
+    import torch
+    lib = da.library()
+    for wid, dt, B in ((2, torch.float64, 8), (3, torch.float32, 16)):
+        prob = W.WORKLOADS[wid].problem(max_steps=1001)
+        P, keep = da.cproblem(prob, dt)
+        assert lib.da_mesh_h_elems(ctypes.byref(P), 300) == ((1001 + B - 1) // B) * 300 * B
+        assert da.mesh_h_shape(prob, 300, dt) == ((1001 + B - 1) // B, 300, B)
+        assert lib.da_mesh_h_elems(ctypes.byref(P), 0) == 0

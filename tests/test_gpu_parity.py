@@ -87,7 +87,7 @@ def test_record_within_tolerance_of_oracle(da, orc, wid, n):
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     mesh, ys = da.record(prob, u0, p)
     torch.cuda.synchronize()
-    mg = mesh_to_host(mesh)
+    mg = mesh_to_host(mesh, prob.max_steps)
     mo = orc.record(prob, inp["u0"], inp["p"], fused=True)
     assert np.array_equal(mg["status"], mo["status"])
     ng, no = mg["n_steps"], mo["n_steps"]
@@ -106,10 +106,12 @@ def test_record_within_tolerance_of_oracle(da, orc, wid, n):
                      for i in range(n)])
     _print(f"  bitwise-equal meshes: {same.mean():.4f}; mean steps gpu {ng.mean():.2f} "
            f"oracle {no.mean():.2f}")
-    # zero padding after the last step
+    # zero padding after the last step, to the end of the tiled log
     hg = mg["h"]
-    pad = np.arange(prob.max_steps)[None, :] >= ng[:, None]
-    assert np.all(hg[pad] == 0)
+    hall = mesh.steps().cpu().numpy()
+    pad = np.arange(hall.shape[1])[None, :] >= ng[:, None]
+    assert np.all(hall[pad] == 0)
+    assert np.all(hall[~pad] > 0)
     E = orc.mesh_max_err(prob, inp["u0"], inp["p"], mg, fused=True)
     assert np.all(E <= 1 + 1e-6), E.max()
     # save indices land on the save times
@@ -136,7 +138,7 @@ def test_gpu_record_equals_gpu_replay(da, orc, wid, n):
     torch.cuda.synchronize()
     assert torch.equal(ys, yr)
     # and the oracle replays the GPU mesh to the same states (fused rounding)
-    mg = mesh_to_host(mesh)
+    mg = mesh_to_host(mesh, prob.max_steps)
     yo, _ = orc.replay(prob, inp["u0"], inp["p"], mg, fused=True)
     yg = ys.cpu().numpy().transpose(2, 0, 1)
     err = rel_err(yg.reshape(n, -1), yo.reshape(n, -1))
@@ -146,33 +148,70 @@ def test_gpu_record_equals_gpu_replay(da, orc, wid, n):
 
 @pytest.mark.parametrize("wid,n", [(1, 1024), (2, 1000), (3, 777), (4, 300)])
 def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
-    """Lane ordering changes the slot order only: every output is bitwise the
-    same, the permutation is valid and step counts are non-increasing."""
+    """A replay order changes the lane schedule only: every output is bitwise
+    the same; the order is a valid permutation with non-increasing step
+    counts that keeps equal counts in index order."""
     w, prob, inp, aux, scale = _setup(orc, wid, n)
     _print(f"case: sorted mesh, workload {wid}, n={n}")
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     auxd = None if aux is None else aux_to_dev(aux, torch)
     mesh, _ = da.record(prob, u0, p)
+    h_before = mesh.h.clone()
     sm = da.mesh_sort(prob, mesh)
     r1 = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale)
     r2 = da.replay_grad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)
     y1 = da.replay_fwd(prob, u0, p, mesh)
     y2 = da.replay_fwd(prob, u0, p, sm)
+    # a reversed order as well (longest trajectories last)
+    rev = da.Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, sm.perm.flip(0).contiguous())
+    r3 = da.replay_grad(prob, u0, p, rev, w.loss, aux=auxd, scale=scale)
     torch.cuda.synchronize()
+    assert torch.equal(mesh.h, h_before)
     perm = sm.perm.cpu().numpy()
     assert np.array_equal(np.sort(perm), np.arange(n))
-    ns_sorted = sm.n_steps.cpu().numpy()
-    assert np.all(np.diff(ns_sorted) <= 0)
     ns = mesh.n_steps.cpu().numpy()
-    assert np.array_equal(ns_sorted, ns[perm])
+    ns_sorted = ns[perm]
+    assert np.all(np.diff(ns_sorted) <= 0)
     # stable: equal step counts keep their original order
     for v in np.unique(ns_sorted):
         sel = perm[ns_sorted == v]
         assert np.all(np.diff(sel) > 0)
-    assert np.array_equal(mesh_to_host(sm)["h"], mesh_to_host(mesh)["h"])
-    for a, b in zip(r1, r2):
-        assert torch.equal(a, b)
+    for a, b, c in zip(r1, r2, r3):
+        assert torch.equal(a, b) and torch.equal(a, c)
     assert torch.equal(y1, y2)
+    # the replay table holds the record's steps in replay order, zero padded
+    rows = sm.h_rows.shape[0]
+    assert rows == ns.max()
+    steps = mesh.steps().cpu().numpy()
+    assert np.array_equal(sm.h_rows.cpu().numpy(), steps[perm, :rows].T)
+    # a table shorter than the longest trajectory: those lanes report NaN
+    short = da.mesh_sort(prob, mesh, rows=int(ns.max()) - 1)
+    l4, g4, q4 = da.replay_grad(prob, u0, p, short, w.loss, aux=auxd, scale=scale)
+    torch.cuda.synchronize()
+    longest = ns == ns.max()
+    assert np.all(np.isnan(q4.cpu().numpy()[:, longest]))
+    assert torch.equal(q4[:, torch.from_numpy(~longest).cuda()],
+                       r1[2][:, torch.from_numpy(~longest).cuda()])
+
+
+@pytest.mark.parametrize("wid,n", [(2, 1000), (3, 600), (4, 300)])
+def test_checkpoint_intervals_give_identical_gradients(da, orc, wid, n):
+    """The reverse sweep's checkpoint interval changes what is stored and what
+    is recomputed, never the arithmetic: all intervals agree bitwise."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: checkpoint intervals, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    mesh, _ = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    ref = [t.clone() for t in da.replay_grad(prob.replace(checkpoint=1), u0, p, sm, w.loss,
+                                             aux=auxd, scale=scale)]
+    for ck in (2, 4, 8, 0):
+        out = da.replay_grad(prob.replace(checkpoint=ck), u0, p, sm, w.loss, aux=auxd,
+                             scale=scale)
+        torch.cuda.synchronize()
+        for a, b in zip(ref, out):
+            assert torch.equal(a, b), ck
 
 
 def test_determinism_and_chunking(da, orc):
@@ -274,7 +313,6 @@ def test_full_size_lorenz_dopri5_sampled(da, orc):
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     mesh, _ = da.record(prob, u0, p, save=False)
     sm = da.mesh_sort(prob, mesh)
-    del mesh
     call = da.ReplayGrad(prob, u0, p, sm)
     loss, gu0, gp = call()
     torch.cuda.synchronize()
@@ -285,11 +323,11 @@ def test_full_size_lorenz_dopri5_sampled(da, orc):
     slots = np.sort(rng.choice(n, 512, replace=False))
     slots = np.unique(np.concatenate([slots, [0, 1, n - 2, n - 1]]))   # longest and shortest
     tr = perm[slots]
-    idx = torch.from_numpy(slots.astype(np.int64)).cuda()
+    idx = torch.from_numpy(tr.astype(np.int64)).cuda()
     N = int(sm.n_steps.max().item())
-    h = sm.h[:N].index_select(1, idx).cpu().numpy().T.copy()
-    sub = {"h": h, "n_steps": sm.n_steps.cpu().numpy()[slots],
-           "save_idx": sm.save_idx.cpu().numpy()[:, slots].T.copy(), "status": st[slots]}
+    h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
+    sub = {"h": np.ascontiguousarray(h), "n_steps": sm.n_steps.cpu().numpy()[tr],
+           "save_idx": sm.save_idx.cpu().numpy()[:, tr].T.copy(), "status": st[tr]}
     pn = prob.replace(max_steps=N)
     lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
     g1 = gu0.cpu().numpy()[:, tr].T

@@ -52,7 +52,7 @@ class Problem:
 
     Zero for ``dt0``, ``max_attempts``, ``safety``, ``fac_min`` and ``fac_max``
     selects the default (automatic starting step, 4 * max_steps attempts,
-    0.9, 0.2, 10).  ``save_times`` must be strictly increasing in (t0, t1];
+    0.9, 0.2, 10).  ``checkpoint`` only schedules the GPU reverse sweep.  ``save_times`` must be strictly increasing in (t0, t1];
     empty means the final state is the only save.
     """
     rhs: int
@@ -70,6 +70,7 @@ class Problem:
     safety: float = 0.0
     fac_min: float = 0.0
     fac_max: float = 0.0
+    checkpoint: int = 0     # reverse-sweep checkpoint interval (0 = automatic)
 
     @property
     def n_save_eff(self) -> int:
