@@ -1,23 +1,26 @@
 """Benchmark of the record-and-replay discrete adjoint on one MI355X.
 
-Workload: Lorenz-63 ensemble of 2^20 trajectories in FP64, Dopri5,
+Default workload: Lorenz-63 ensemble of 2^20 trajectories in FP64, Dopri5,
 rtol = atol = 1e-8, t in [0, 10], at most 4096 steps, loss = sum of squared
 final states; one record then 10 replay-gradient passes against it.  Inputs
 are synthetic (seeded, see workloads/) and resident on the GPU before the
-timed region.
+timed region.  --workload selects one of the other ensembles.
 
-One timed step is that whole job: record, lane ordering, 10 gradient passes.
+One timed step is that whole job: record, lane ordering with the replay
+table, and the gradient passes.
 value = trajectories * passes / step time (trajectory-gradients/s).
 
 Printed on one JSON line, besides the driver's fields:
-  roofline      the gradient kernel (k_replay_grad) against the FP64 vector
-                ALU peak: algorithmic FLOPs per launch (exact count of the
-                replay step and its adjoint per populated step, times the
+  roofline      the gradient kernel (k_replay_grad) against the vector ALU
+                peak of its dtype: algorithmic FLOPs per launch (the exact
+                operation count of the replay step and its adjoint per
+                populated step, stage recomputation excluded, times the
                 populated steps of the record) / mean launch time from HIP
                 events on the launch stream; traffic = HBM bytes per launch
-                from rocprofv3 FETCH_SIZE + WRITE_SIZE counters (scaled by a
-                copy-kernel calibration), when the kernel sources match the
-                ones the counters were taken with, else null;
+                from rocprofv3 FETCH_SIZE and WRITE_SIZE counters, each scaled
+                by what the counter reads for a copy of known size, when the
+                kernel sources match the ones the counters were taken with,
+                else null;
   cpu_baseline  the CPU oracle (plain C++, OpenMP) on a bounded sample of the
                 same workload, as trajectory-gradients/s of the same job.
 
@@ -33,51 +36,87 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-# FP64 vector peak of MI355X: 256 CUs x 128 FP64 flop/clock (64 FMA lanes) x 2.4 GHz
-PEAK_FP64_TFLOPS = 78.6
-# Algorithmic FLOPs per populated step (FMA = 2, add/sub/mul = 1, negation = 0)
-# of the replay step plus its adjoint (stage recomputation excluded), counted
-# from the arithmetic schedule of the kernel:
-#   forward: 6 right-hand sides x 8 + stage sums 46 per component x 3 = 186
-#   adjoint: stage cotangent sums 40 per component x 3 = 120
-#            + 6 stages x (J^T v 13 + J_p^T v 7 + accumulate 3) = 138
-FLOP_PER_STEP = {("dopri5", "lorenz63"): 186 + 258, ("tsit5", "lorenz63"): 192 + 264}
-COUNTERS_FILE = os.path.join(ROOT, "profiles", "replay_grad_lorenz63_dopri5_n1048576_counters.md")
-KERNEL_SOURCES = ["lane_kernels.hpp", "erk.hip", "dadj_device.hpp", "dadj_internal.hpp"]
+# Vector ALU peaks of MI355X (256 CUs x 2.4 GHz): FP64 128 flop/clock/CU;
+# FP32 256 flop/clock/CU (packed; unpacked FP32 runs at the FP64 rate).
+PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
+
+# Algorithmic FLOPs per populated step (FMA = 2, add/sub/mul/div = 1,
+# negation = 0) of the replay step plus its adjoint, stage recomputation
+# excluded, counted from the arithmetic schedule of the kernels:
+#  Dopri5 / Lorenz-63: forward 6 right-hand sides x 8 + stage sums 46 per
+#    component x 3 = 186; adjoint stage cotangent sums 40 x 3 = 120 + 6 stages
+#    x (J^T v 13 + J_p^T v 7 + accumulate 3) = 138; total 444.
+#  Tsit5 / Lorenz-63: forward 48 + 48 x 3 = 192; adjoint 42 x 3 + 138 = 264.
+#  ROS2 / Robertson: forward (Jacobian 9, W 13, LU 13, two right-hand sides
+#    26, two solves 30, stage and solution combinations 27) = 118; adjoint
+#    (two transposed solves 30, J^T v and J_p^T v at both stages 66, Wbar 27,
+#    cotangent combinations 36, dJ contraction 29) = 188; total 306.
+#  Tsit5 / Lorenz-96 (d components): forward 6 x 4d + 48d = 72d; adjoint
+#    42d + 6 x (J^T v 7d + J_p^T v d + accumulate d) = 96d; total 168d.
+def flop_per_step(method: str, rhs: str, dim: int) -> int:
+    table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
+             ("ros2", "robertson"): 306}
+    if rhs == "lorenz96" and method == "tsit5":
+        return 168 * dim
+    return table[(method, rhs)]
 
 
-def kernel_source_hash() -> str:
+COUNTERS_DIR = os.path.join(ROOT, "profiles")
+# Sources of the gradient kernel of each method family.
+KERNEL_SOURCES = {
+    "erk": ["lane_kernels.hpp", "erk.hip", "dadj_device.hpp", "dadj_internal.hpp"],
+    "ros2": ["lane_kernels.hpp", "ros2.hip", "dadj_device.hpp", "dadj_internal.hpp"],
+    "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
+}
+
+
+def kernel_family(method: str, rhs: str) -> str:
+    if rhs == "lorenz96":
+        return "wave"
+    return "ros2" if method == "ros2" else "erk"
+
+
+def kernel_source_hash(family: str = "erk") -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "discrete_adjoint_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in KERNEL_SOURCES[family]:
+        path = os.path.join(ROOT, "discrete_adjoint_amd", "csrc", f)
+        if os.path.exists(path):
+            with open(path, "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per launch from the committed counter summary, if it was taken
-    with the current kernel sources."""
-    if not os.path.exists(COUNTERS_FILE):
+def read_traffic(workload_name: str, family: str):
+    """HBM bytes per gradient launch from the committed counter summary of the
+    workload, if it was taken with the current kernel sources."""
+    path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}_counters.md")
+    if not os.path.exists(path):
         return None
     src_hash, traffic = None, None
-    for line in open(COUNTERS_FILE):
+    for line in open(path):
         if line.startswith("kernel_source_hash:"):
             src_hash = line.split(":", 1)[1].strip()
         if line.startswith("hbm_bytes_per_launch:"):
             traffic = float(line.split(":", 1)[1].strip())
-    return traffic if src_hash == kernel_source_hash() else None
+    return traffic if src_hash == kernel_source_hash(family) else None
 
 
-def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 20.0):
+def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0):
     """Oracle as it stands, plain rounding, all OpenMP threads: record + passes
     on the first `lanes` trajectories of the workload."""
     import numpy as np
     import oracle
     import workloads as W
     w = W.WORKLOADS[wid]
+    lanes = min(lanes, w.n)
     inp = W.make_inputs(wid, lanes)
     prob = w.problem()
     cores = oracle.max_threads()
+    aux, scale = None, 1.0
+    if w.loss == W.MSE_SAVE:
+        t = oracle.record(prob, inp["u0"].astype(np.float64), inp["p_true"], with_h=False)
+        aux = t["y_save"].astype(w.np_dtype)
+        scale = 1.0 / (lanes * w.n_save_eff * w.dim)
     t0 = time.perf_counter()
     m = oracle.record(prob, inp["u0"], inp["p"])
     t_rec = time.perf_counter() - t0
@@ -85,16 +124,16 @@ def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 20.0):
     m["h"] = np.ascontiguousarray(m["h"][:, :N])
     pn = prob.replace(max_steps=N)
     t_pass = []
-    while len(t_pass) < 2 or (sum(t_pass) + t_rec < max_seconds and len(t_pass) < passes):
+    while len(t_pass) < 1 or (sum(t_pass) + t_rec < max_seconds and len(t_pass) < passes):
         t0 = time.perf_counter()
-        oracle.replay_grad(pn, inp["u0"], inp["p"], m)
+        oracle.replay_grad(pn, inp["u0"], inp["p"], m, w.loss, aux=aux, scale=scale)
         t_pass.append(time.perf_counter() - t0)
     t_job = t_rec + passes * float(np.mean(t_pass))
     return {"value": lanes * passes / t_job, "unit": "trajectory-gradients/s", "cores": cores,
             "kind": "oracle",
-            "sample": f"first {lanes} trajectories of the workload: record {t_rec:.2f} s + "
-                      f"{len(t_pass)} timed gradient passes (mean {np.mean(t_pass):.3f} s), "
-                      f"job time = record + {passes} passes"}
+            "sample": f"first {lanes} of {w.n} trajectories of the workload: record "
+                      f"{t_rec:.2f} s + {len(t_pass)} timed gradient passes (mean "
+                      f"{np.mean(t_pass):.3f} s); job time = record + {passes} passes"}
 
 
 def copy_probe(gib: float = 1.0):
@@ -115,8 +154,10 @@ def main():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", type=int, default=2)
+    ap.add_argument("--checkpoint", type=int, default=0,
+                    help="reverse-sweep checkpoint interval (0 = library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-lanes", type=int, default=65536)
+    ap.add_argument("--cpu-lanes", type=int, default=262144)
     ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -134,7 +175,7 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
-    prob = w.problem()
+    prob = w.problem(checkpoint=args.checkpoint)
     n = w.n
     passes = w.passes
     dev = torch.device("cuda:0")
@@ -142,21 +183,32 @@ def main():
     u0 = torch.from_numpy(np.ascontiguousarray(inp["u0"].T)).to(dev)
     p = torch.from_numpy(np.ascontiguousarray(inp["p"].T)).to(dev)
     dt = u0.dtype
+    aux, scale = None, 1.0
+    if w.loss == W.MSE_SAVE:
+        # targets: the same solver on perturbed parameters (computed on the GPU,
+        # outside the timed region; only their shape and scale matter here)
+        pt = torch.from_numpy(np.ascontiguousarray(inp["p_true"].T.astype(inp["p"].dtype)))
+        aux, _, _ = da.solve_fwd(prob, u0, pt.to(dev))
+        aux = torch.nan_to_num(aux)
+        scale = 1.0 / (n * w.n_save_eff * w.dim)
     mesh = da.empty_mesh(prob, n, dt, dev, with_perm=True)
     sort_ws = torch.empty(da.mesh_sort_workspace(prob, n, dt), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    state = {"call": None, "N": -1}
+    state = {"call": None, "N": -1, "rows": None}
 
     def job(events=None):
         e = events
         if e: e["rec0"].record(stream)
         da.record(prob, u0, p, mesh=mesh, save=False)
         if e: e["rec1"].record(stream)
-        da.mesh_sort(prob, mesh, perm=mesh.perm, workspace=sort_ws)
-        if e: e["sort1"].record(stream)
-        N = da.mesh_max_steps(mesh)           # sizes the workspace (host sync)
+        N = da.mesh_max_steps(mesh)           # sizes the table and workspace (host sync)
         if N != state["N"]:
-            state["call"] = da.ReplayGrad(prob, u0, p, mesh, W.SUMSQ_FINAL, max_n_steps=N)
+            state["rows"] = torch.empty((max(N, 1), n), dtype=dt, device=dev)
+        sm = da.mesh_sort(prob, mesh, perm=mesh.perm, h_rows=state["rows"], workspace=sort_ws)
+        if e: e["sort1"].record(stream)
+        if N != state["N"]:
+            state["call"] = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=aux, scale=scale,
+                                          max_n_steps=N)
             state["N"] = N
         for k in range(passes):
             if e: e["p0"][k].record(stream)
@@ -183,31 +235,36 @@ def main():
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
     pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
                              for k in range(passes)]))
+    st = mesh.status.cpu().numpy()
     ns = mesh.n_steps.double()
-    total_steps = float(ns.sum().item())
-    mean_steps = total_steps / n
-    flop_step = FLOP_PER_STEP[(W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs])]
+    ok = torch.from_numpy(st == 0).to(dev)
+    total_steps = float(ns[ok].sum().item())
+    mean_steps = float(ns.mean().item())
+    mname, rname = W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs]
+    flop_step = flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
-    traffic = read_traffic()
+    peak = PEAK_TFLOPS[w.dtype]
+    traffic = read_traffic(w.name, kernel_family(mname, rname))
     out = {
         "metric": "trajectory-gradients/s (Lorenz FP64, 1M traj) + % of FP64 vector peak",
         "value": n * passes / (ms_per_step * 1e-3),
         "unit": "trajectory-gradients/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
-        "config": {"workload": w.name, "n": n, "method": W.METHOD_NAMES[w.method],
-                   "rhs": W.RHS_NAMES[w.rhs], "t1": w.t1, "rtol": w.rtol, "atol": w.atol,
-                   "max_steps": w.max_steps, "passes_per_record": passes,
-                   "step": "record + lane ordering + 10 gradient passes"},
-        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP64_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_FP64_TFLOPS,
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "n": n, "method": mname, "rhs": rname, "dim": w.dim,
+                   "t1": w.t1, "rtol": w.rtol, "atol": w.atol, "max_steps": w.max_steps,
+                   "passes_per_record": passes, "checkpoint": args.checkpoint,
+                   "step": f"record + lane ordering and replay table + {passes} gradient "
+                           f"pass{'es' if passes > 1 else ''}"},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
+                     "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "kernel": "k_replay_grad",
                      "flop_per_step": flop_step, "populated_steps_per_launch": total_steps},
         "per_pass": {"ms": pass_ms, "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
-        "record_ms": rec_ms, "sort_ms": sort_ms,
+        "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],
-                 "max_over_mean": state["N"] / mean_steps},
+                 "max_over_mean": state["N"] / mean_steps, "failed_lanes": int((st != 0).sum())},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes)
