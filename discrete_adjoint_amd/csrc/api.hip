@@ -64,8 +64,8 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (!shape_ok(pb->rhs, pb->dim, pb->n_params))
     return fail(DA_EINVAL, "rhs %d does not take dim=%d, n_params=%d", pb->rhs, pb->dim,
                 pb->n_params);
-  if (pb->rhs == DA_RHS_LORENZ96)
-    return fail(DA_EUNSUPPORTED, "LORENZ96 is not available in this build");
+  if (pb->rhs == DA_RHS_LORENZ96 && pb->method == DA_ROS2)
+    return fail(DA_EUNSUPPORTED, "ROS2 is available for systems of dimension <= 3 only");
   if (!(isfinite(pb->t0) && isfinite(pb->t1) && pb->t1 > pb->t0))
     return fail(DA_EINVAL, "need finite t0 < t1");
   if (!(pb->rtol >= 0) || !(pb->atol >= 0) || !(pb->rtol + pb->atol > 0) || !isfinite(pb->rtol) ||
@@ -142,6 +142,24 @@ void fill_replay_args(dadj::ReplayArgs &a, const dadj::ProbArgs &pr, int64_t n, 
   a.perm = mesh->perm;
 }
 
+hipError_t launch_record(const dadj::RecordArgs &a, const dadj::SaveTimes &st, hipStream_t s) {
+  if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_record(a, st, s);
+  if (a.pr.method == DA_ROS2) return dadj::launch_ros2_record(a, st, s);
+  return dadj::launch_erk_record(a, st, s);
+}
+
+hipError_t launch_replay_fwd(const dadj::ReplayArgs &a, hipStream_t s) {
+  if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_fwd(a, s);
+  if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_fwd(a, s);
+  return dadj::launch_erk_replay_fwd(a, s);
+}
+
+hipError_t launch_replay_grad(const dadj::ReplayArgs &a, hipStream_t s) {
+  if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_grad(a, s);
+  if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_grad(a, s);
+  return dadj::launch_erk_replay_grad(a, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -171,8 +189,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   a.status = mesh->status;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_record(a, st, s)
-                                            : dadj::launch_erk_record(a, st, s);
+  const hipError_t e = launch_record(a, st, s);
   if (e != hipSuccess) return hip_fail(e, "record launch");
   return ok();
 }
@@ -196,8 +213,7 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
   a.status = status;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_record(a, st, s)
-                                            : dadj::launch_erk_record(a, st, s);
+  const hipError_t e = launch_record(a, st, s);
   if (e != hipSuccess) return hip_fail(e, "solve_fwd launch");
   return ok();
 }
@@ -268,8 +284,7 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
   fill_replay_args(a, pr, n, u0, p, mesh);
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
-  const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_replay_fwd(a, s)
-                                            : dadj::launch_erk_replay_fwd(a, s);
+  const hipError_t e = launch_replay_fwd(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_fwd launch");
   return ok();
 }
@@ -278,8 +293,8 @@ size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n
   if (!prob || n <= 0 || max_n_steps <= 0 || prob->dim <= 0) return 0;
   const int ck = resolved_checkpoint(*prob);
   if (ck <= 0 || ck > 8) return 0;
-  return (size_t)n * (size_t)((max_n_steps + ck - 1) / ck) * (size_t)prob->dim *
-         dsize(prob->dtype);
+  return (size_t)n * (size_t)((max_n_steps + ck - 1) / ck) *
+         (size_t)dadj::ws_row(prob->rhs, prob->dim) * dsize(prob->dtype);
 }
 
 int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
@@ -301,8 +316,8 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
     return fail(DA_EINVAL, "max_n_steps must be in [0, max_steps]");
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
   if (n == 0) return ok();
-  const size_t per_lane =
-      (size_t)((max_n_steps + pr.checkpoint - 1) / pr.checkpoint) * pr.dim * dsize(pr.dtype);
+  const size_t per_lane = (size_t)((max_n_steps + pr.checkpoint - 1) / pr.checkpoint) *
+                          dadj::ws_row(pr.rhs, pr.dim) * dsize(pr.dtype);
   int64_t C = n;
   if (per_lane > 0) {
     if (!workspace) return fail(DA_EWORKSPACE, "workspace is NULL");
@@ -329,8 +344,7 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   for (int64_t slot0 = 0; slot0 < n; slot0 += C) {
     a.slot0 = slot0;
     a.nslots = (n - slot0) < C ? (n - slot0) : C;
-    const hipError_t e = pr.method == DA_ROS2 ? dadj::launch_ros2_replay_grad(a, s)
-                                              : dadj::launch_erk_replay_grad(a, s);
+    const hipError_t e = launch_replay_grad(a, s);
     if (e != hipSuccess) return hip_fail(e, "replay_grad launch");
   }
   return ok();

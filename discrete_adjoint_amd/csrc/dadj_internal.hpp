@@ -14,6 +14,11 @@ constexpr int CHUNK_BYTES = 64;  // step-log chunk owned by one trajectory
 // Steps per chunk of the tiled step log.
 constexpr int chunk_steps(int dtype) { return dtype == DA_F64 ? 8 : 16; }
 
+// Values per trajectory and checkpoint in the replay-gradient workspace: the
+// state, padded to a whole wavefront for the wavefront-per-trajectory
+// systems.
+constexpr int ws_row(int rhs, int dim) { return rhs == DA_RHS_LORENZ96 ? 64 : dim; }
+
 enum { LANE_OK = 0, LANE_MAX_STEPS = 1, LANE_DT_UNDERFLOW = 2, LANE_NONFINITE = 3,
        LANE_MAX_ATTEMPTS = 4 };
 
@@ -63,6 +68,9 @@ struct ReplayArgs {
 hipError_t launch_erk_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_erk_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_erk_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_l96_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
+hipError_t launch_l96_replay_fwd(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_l96_replay_grad(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s);

@@ -1,0 +1,62 @@
+// Lorenz-96 ensembles (state dimension 4..64) on the wavefront-per-trajectory
+// kernels: explicit Tsit5 and Dopri5 in FP64 and FP32.
+#include "wave_kernels.hpp"
+
+namespace dadj {
+namespace {
+
+using wave::WAVES;
+
+template <class T, class M>
+hipError_t wrecord_t(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.n + WAVES - 1) / WAVES);
+  if (a.h) hipLaunchKernelGGL((wave::k_wrecord<T, M, true>), grid, 64 * WAVES, 0, s, a, st);
+  else hipLaunchKernelGGL((wave::k_wrecord<T, M, false>), grid, 64 * WAVES, 0, s, a, st);
+  return hipGetLastError();
+}
+
+template <class T, class M>
+hipError_t wreplay_fwd_t(const ReplayArgs &a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.n + WAVES - 1) / WAVES);
+  hipLaunchKernelGGL((wave::k_wreplay_fwd<T, M>), grid, 64 * WAVES, 0, s, a);
+  return hipGetLastError();
+}
+
+template <class T, class M>
+hipError_t wreplay_grad_t(const ReplayArgs &a, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.nslots + WAVES - 1) / WAVES);
+  switch (a.pr.checkpoint) {
+    case 1: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 1>), grid, 64 * WAVES, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 2>), grid, 64 * WAVES, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 4>), grid, 64 * WAVES, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 8>), grid, 64 * WAVES, 0, s, a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define DADJ_L96_DISPATCH(FN, ARGS)                                                    \
+  do {                                                                                 \
+    const bool f64 = a.pr.dtype == DA_F64;                                             \
+    if (a.pr.method == DA_TSIT5)                                                       \
+      return f64 ? FN<double, wave::WErk<Tsit5Tab, wave::L96>> ARGS                    \
+                 : FN<float, wave::WErk<Tsit5Tab, wave::L96>> ARGS;                    \
+    if (a.pr.method == DA_DOPRI5)                                                      \
+      return f64 ? FN<double, wave::WErk<Dopri5Tab, wave::L96>> ARGS                   \
+                 : FN<float, wave::WErk<Dopri5Tab, wave::L96>> ARGS;                   \
+    return hipErrorInvalidValue;                                                       \
+  } while (0)
+
+}  // namespace
+
+hipError_t launch_l96_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  DADJ_L96_DISPATCH(wrecord_t, (a, st, s));
+}
+hipError_t launch_l96_replay_fwd(const ReplayArgs &a, hipStream_t s) {
+  DADJ_L96_DISPATCH(wreplay_fwd_t, (a, s));
+}
+hipError_t launch_l96_replay_grad(const ReplayArgs &a, hipStream_t s) {
+  DADJ_L96_DISPATCH(wreplay_grad_t, (a, s));
+}
+
+}  // namespace dadj

@@ -1,0 +1,539 @@
+// Wavefront-per-trajectory kernels for systems of dimension up to 64 whose
+// right-hand side couples each component only to a few neighbours (the
+// cyclic Lorenz-96 stencil).  The pages' one-thread-per-trajectory design
+// ("Differentiable astrophysics at scale", Methodology) would keep about
+// 7 KB of stage state per lane at d = 64; here lane c of a wavefront owns
+// component c of one trajectory, so every lane keeps a handful of scalars and
+// the neighbours come from cross-lane shuffles.  Everything that decides the
+// control flow (error norm, accept/reject, step size, loop bounds) is reduced
+// across the wavefront and taken from one lane, so it is wavefront-uniform
+// and the shuffles always run with every lane active.
+//
+//  k_wrecord<T, M, LOG>        adaptive solve (record / forward-only solve)
+//  k_wreplay_fwd<T, M>         fixed-step replay
+//  k_wreplay_grad<T, M, CK>    replay + reverse sweep, mesh held fixed
+//
+// A method M provides, per lane (component) with a Nbr context for the
+// neighbours: fwd(x, F, h), attempt(x, F, h, k0, xnew, err) and
+// adj(x, F, h, lam, gF) (gF accumulates this lane's share of dL/dF).
+#pragma once
+
+#include <math.h>
+
+#include "dadj_device.hpp"
+#include "dadj_internal.hpp"
+
+namespace dadj {
+namespace wave {
+
+constexpr int WAVES = 4;  // trajectories (wavefronts) per workgroup
+
+// ---------------------------------------------------------------------------
+// wavefront helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double uniform(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)b);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(b >> 32));
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ float uniform(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Sum over the 64 lanes by a butterfly; every stage adds the same two values
+// in every lane (addition commutes exactly), and lane 0's result is taken.
+template <class T> __device__ __forceinline__ T wave_sum(T v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = v + __shfl_xor(v, off, 64);
+  return uniform(v);
+}
+
+__device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0ull; }
+
+// Source lanes of the cyclic neighbours of component c in dimension d.
+struct Nbr {
+  int p1, p2, m1, m2;  // c+1, c+2, c-1, c-2 (mod d)
+  __device__ __forceinline__ void init(int c, int d) {
+    const int cc = c < d ? c : 0;
+    p1 = (cc + 1) % d;
+    p2 = (cc + 2) % d;
+    m1 = (cc + d - 1) % d;
+    m2 = (cc + d - 2) % d;
+  }
+};
+
+template <class T> __device__ __forceinline__ T take(T v, int src) { return __shfl(v, src, 64); }
+
+// ---------------------------------------------------------------------------
+// Lorenz-96: x_c' = (x_{c+1} - x_{c-2}) x_{c-1} - x_c + F.  The operation
+// order per component is the same as in the per-trajectory formulas:
+// f_c = fma(x_{c+1} - x_{c-2}, x_{c-1}, -x_c) + F;
+// (J^T v)_c = x_{c-2} v_{c-1} - v_c + (x_{c+2} - x_{c-1}) v_{c+1} - x_{c+1} v_{c+2}
+// (rows c-1, c, c+1, c+2 of column c, in that order); df_c/dF = 1.
+// ---------------------------------------------------------------------------
+struct L96 {
+  template <class T>
+  __device__ static __forceinline__ T f(T x, T F, const Nbr &nb) {
+    const T xp1 = take(x, nb.p1), xm1 = take(x, nb.m1), xm2 = take(x, nb.m2);
+    return mac(xp1 - xm2, xm1, -x) + F;
+  }
+  template <class T>
+  __device__ static __forceinline__ T vjp_y(T x, T v, const Nbr &nb) {
+    const T xp1 = take(x, nb.p1), xp2 = take(x, nb.p2), xm1 = take(x, nb.m1),
+            xm2 = take(x, nb.m2);
+    const T vm1 = take(v, nb.m1), vp1 = take(v, nb.p1), vp2 = take(v, nb.p2);
+    T s = xm2 * vm1;
+    s = s - v;
+    s = mac(xp2 - xm1, vp1, s);
+    s = mac(-xp1, vp2, s);
+    return s;
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Explicit RK step per component (same arithmetic schedule as the
+// lane-per-trajectory kernels: first product, then multiply-adds, left to
+// right; Y_i = fma(h, acc, y)).
+// ---------------------------------------------------------------------------
+template <class Tab, int I, class T>
+__device__ __forceinline__ T wstage(T y, const T (&K)[7], T h) {
+  T acc = T(0);
+  bool first = true;
+#pragma unroll
+  for (int j = 0; j < I; ++j) {
+    if (Tab::a[I][j] != 0.0) {
+      if (first) { acc = T(Tab::a[I][j]) * K[j]; first = false; }
+      else acc = mac(T(Tab::a[I][j]), K[j], acc);
+    }
+  }
+  return mac(h, acc, y);
+}
+
+template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
+struct WStages {
+  __device__ static __forceinline__ void run(T y, T F, T h, const Nbr &nb, T (&Y)[7], T (&K)[7]) {
+    Y[I] = wstage<Tab, I>(y, K, h);
+    if (I < LAST || LASTK) K[I] = Rhs::f(Y[I], F, nb);
+    WStages<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, F, h, nb, Y, K);
+  }
+};
+template <class Tab, class Rhs, int LAST, bool LASTK, class T>
+struct WStages<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
+  __device__ static __forceinline__ void run(T, T, T, const Nbr &, T (&)[7], T (&)[7]) {}
+};
+
+template <class Tab, class R>
+struct WErk {
+  using Rhs = R;
+  static constexpr int order = Tab::order, err_order = Tab::err_order;
+
+  // trial step from x with K[0] = f(x) given; returns the 5th-order value
+  template <class T>
+  __device__ static __forceinline__ T attempt(T x, T F, T h, const Nbr &nb, T (&K)[7], T &err) {
+    T Y[7];
+    WStages<Tab, Rhs, 1, 6, true, T>::run(x, F, h, nb, Y, K);
+    T acc = T(0);
+    bool first = true;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      if (Tab::e[j] != 0.0) {
+        if (first) { acc = T(Tab::e[j]) * K[j]; first = false; }
+        else acc = mac(T(Tab::e[j]), K[j], acc);
+      }
+    }
+    err = h * acc;
+    return Y[6];
+  }
+
+  template <class T> __device__ static __forceinline__ T fwd(T x, T F, T h, const Nbr &nb) {
+    T Y[7], K[7];
+    K[0] = Rhs::f(x, F, nb);
+    WStages<Tab, Rhs, 1, 6, false, T>::run(x, F, h, nb, Y, K);
+    return Y[6];
+  }
+
+  // Reverse of fwd at x = x_k: lam (dL/dx_{k+1} -> dL/dx_k); gF += this
+  // component's share of dL/dF (the sum of its stage cotangents).
+  template <class T>
+  __device__ static __forceinline__ void adj(T x, T F, T h, const Nbr &nb, T &lam, T &gF) {
+    T Y[7], Wv[7];
+    {
+      T K[7];
+      K[0] = Rhs::f(x, F, nb);
+      WStages<Tab, Rhs, 1, 5, false, T>::run(x, F, h, nb, Y, K);
+    }
+    Y[0] = x;
+#pragma unroll
+    for (int i = 5; i >= 0; --i) {
+      T acc = T(0);
+      bool first = true;
+      if (Tab::a[6][i] != 0.0) {
+        acc = T(Tab::a[6][i]) * lam;
+        first = false;
+      }
+#pragma unroll
+      for (int l = i + 1; l <= 5; ++l) {
+        if (Tab::a[l][i] != 0.0) {
+          if (first) { acc = T(Tab::a[l][i]) * Wv[l]; first = false; }
+          else acc = mac(T(Tab::a[l][i]), Wv[l], acc);
+        }
+      }
+      const T kb = h * acc;
+      Wv[i] = Rhs::vjp_y(Y[i], kb, nb);
+      gF = gF + kb;
+    }
+    T s = lam;
+#pragma unroll
+    for (int i = 5; i >= 0; --i) s = s + Wv[i];
+    lam = s;
+  }
+};
+
+template <class T> __device__ __forceinline__ T wmax(T a, T b) { return (a < b) ? b : a; }
+template <class T> __device__ __forceinline__ T wmin(T a, T b) { return (b < a) ? b : a; }
+__device__ __forceinline__ double wpow(double a, double b) { return pow(a, b); }
+__device__ __forceinline__ float wpow(float a, float b) { return powf(a, b); }
+__device__ __forceinline__ double wsqrt(double a) { return sqrt(a); }
+__device__ __forceinline__ float wsqrt(float a) { return sqrtf(a); }
+__device__ __forceinline__ double wabs(double a) { return fabs(a); }
+__device__ __forceinline__ float wabs(float a) { return fabsf(a); }
+
+// RMS over the d live components of v / sc (lanes >= d contribute zero).
+template <class T> __device__ __forceinline__ T wrms(T v, T sc, bool on, int d) {
+  const T q = v / sc;
+  return wsqrt(wave_sum(on ? q * q : T(0)) / T(d));
+}
+
+// One trajectory per wavefront: trajectory index of this wavefront (uniform)
+// and this lane's component.
+struct WaveId {
+  int64_t i;
+  int c;
+  bool live;  // trajectory exists
+};
+__device__ __forceinline__ WaveId wave_id(int64_t count) {
+  WaveId w;
+  w.c = threadIdx.x & 63;
+  w.i = (int64_t)blockIdx.x * WAVES + uniform((int)(threadIdx.x >> 6));
+  w.live = w.i < count;
+  return w;
+}
+
+template <class T> struct WLog {
+  static constexpr int B = CHUNK_BYTES / (int)sizeof(T);
+};
+
+// ---------------------------------------------------------------------------
+// Record / forward solve (same controller as the lane kernels).  Lane b of
+// the wavefront holds step b of the current chunk of the step log; a full
+// chunk is written by lanes 0..B-1 as one 64-byte store.
+// ---------------------------------------------------------------------------
+template <class T, class M, bool LOG>
+__global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes stimes) {
+  using Rhs = typename M::Rhs;
+  constexpr int B = WLog<T>::B;
+  const int64_t n = a.n;
+  const WaveId w = wave_id(n);
+  if (!w.live) return;  // wavefront-uniform
+  const int64_t i = w.i;
+  const int c = w.c;
+  const ProbArgs &pr = a.pr;
+  const int d = pr.dim;
+  const bool on = c < d;
+  Nbr nb;
+  nb.init(c, d);
+  const int S = pr.S;
+  const bool has_saves = pr.n_save > 0;
+  const int n_stops = S + ((has_saves && stimes.t[pr.n_save - 1] < pr.t1) ? 1 : 0);
+  const T atol = T(pr.atol), rtol = T(pr.rtol);
+  const T expo = T(-1.0) / T(M::err_order + 1);
+  const T safety = T(pr.safety), fmin = T(pr.fac_min), fmax = T(pr.fac_max);
+  T *H = (T *)a.h;
+  T *ysave = (T *)a.y_save;
+
+  T x = on ? ((const T *)a.u0)[c * n + i] : T(0);
+  const T F = uniform(((const T *)a.p)[i]);
+  for (int s = 0; s < S; ++s) {
+    if (a.sidx && c == 0) a.sidx[s * n + i] = -1;
+    if (ysave && on) ysave[(s * d + c) * n + i] = nanv<T>();
+  }
+  int nacc = 0, natt = 0, st = LANE_OK;
+  T hb = T(0);  // lane b: step b of the current chunk
+  const bool fin = wave_all(finite(x)) && finite(F);
+  if (!fin) {
+    st = LANE_NONFINITE;
+  } else {
+    T K[7];
+    K[0] = Rhs::f(x, F, nb);
+    T h;
+    if (pr.dt0 > 0) {
+      h = T(pr.dt0);
+    } else {  // Hairer, Norsett, Wanner I, section II.4
+      const T sc = mac(rtol, wabs(x), atol);
+      const T d0 = wrms(x, sc, on, d), d1 = wrms(K[0], sc, on, d);
+      const T h0 = (d0 < T(1e-5) || d1 < T(1e-5)) ? T(1e-6) : T(0.01) * (d0 / d1);
+      const T x1 = mac(h0, K[0], x);
+      const T f1 = Rhs::f(x1, F, nb);
+      const T d2 = wrms(f1 - K[0], sc, on, d) / h0;
+      const T dm = wmax(d1, d2);
+      const T h1 = (dm <= T(1e-15)) ? wmax(T(1e-6), h0 * T(1e-3))
+                                    : wpow(T(0.01) / dm, T(1.0) / T(M::order + 1));
+      h = uniform(wmin(T(100.0) * h0, h1));
+    }
+    double t = pr.t0;
+    int js = 0;
+    bool after_reject = false;
+    for (;;) {
+      const double t_stop = (has_saves && js < S) ? stimes.t[js] : pr.t1;
+      const T rem = T(t_stop - t);
+      const bool land = !(h < rem);
+      const T hs = land ? rem : h;
+      if (nacc >= pr.max_steps) { st = LANE_MAX_STEPS; break; }
+      if (natt >= pr.max_attempts) { st = LANE_MAX_ATTEMPTS; break; }
+      if (!(hs > T(0)) || t + double(hs) == t) { st = LANE_DT_UNDERFLOW; break; }
+      ++natt;
+      T Kt[7];
+      Kt[0] = K[0];
+      T err;
+      const T xn = M::attempt(x, F, hs, nb, Kt, err);
+      const T sc = mac(rtol, wmax(wabs(x), wabs(xn)), atol);
+      const T E = wrms(err, sc, on, d);
+      if (E <= T(1)) {
+        if (LOG) {
+          const int pos = nacc % B;
+          if (c == pos) hb = hs;
+          if (pos == B - 1) {
+            if (c < B) H[((int64_t)(nacc / B) * n + i) * B + c] = hb;
+            hb = T(0);
+          }
+        }
+        ++nacc;
+        x = xn;
+        K[0] = Kt[6];
+        t = land ? t_stop : t + double(hs);
+        T fac = (E == T(0)) ? fmax : wmin(fmax, wmax(fmin, safety * wpow(E, expo)));
+        if (after_reject) fac = wmin(fac, T(1));
+        h = uniform(hs * fac);
+        after_reject = false;
+        if (land) {
+          if (js < S) {
+            if (a.sidx && c == 0) a.sidx[js * n + i] = nacc;
+            if (ysave && on) ysave[(js * d + c) * n + i] = x;
+          }
+          if (++js == n_stops) break;
+        }
+      } else {
+        const T fac = finite(E) ? wmax(fmin, safety * wpow(E, expo)) : fmin;
+        h = uniform(hs * fac);
+        after_reject = true;
+      }
+    }
+  }
+  if (c == 0) {
+    if (a.nsteps) a.nsteps[i] = nacc;
+    if (a.status) a.status[i] = st;
+  }
+  if (LOG) {
+    // the partial chunk, then zero chunks to the end of the log, B lanes per
+    // chunk (64 lanes write 64 / B chunks per store)
+    int t0 = nacc / B;
+    if (nacc % B != 0) {
+      if (c < B) H[((int64_t)t0 * n + i) * B + c] = hb;
+      ++t0;
+    }
+    const int per = 64 / B;
+    for (int t = t0; t < pr.n_chunks; t += per) {
+      const int tc = t + c / B;
+      if (tc < pr.n_chunks) H[((int64_t)tc * n + i) * B + (c % B)] = T(0);
+    }
+  }
+}
+
+// Step source of a replay wavefront: the replay table row of its lane slot,
+// or its trajectory's chunks of the tiled log (uniform addresses).
+template <class T> struct WSteps {
+  typedef __attribute__((address_space(1))) const T GT;  // global memory
+  GT *base;
+  int64_t stride_chunk;
+  int64_t n;
+  int cap;
+  bool rows;
+  __device__ __forceinline__ void init(const ReplayArgs &a, int64_t j, int64_t tr) {
+    n = a.n;
+    rows = a.h_rows != nullptr;
+    if (rows) {
+      base = (GT *)a.h_rows + j;
+      cap = a.rows;
+    } else {
+      base = (GT *)a.h + tr * WLog<T>::B;
+      cap = a.pr.n_chunks * WLog<T>::B;
+    }
+  }
+  __device__ __forceinline__ T load(int k) const {
+    k = k < cap ? k : cap - 1;
+    k = k < 0 ? 0 : k;
+    constexpr int B = WLog<T>::B;
+    return rows ? base[(int64_t)k * n] : base[(int64_t)(k / B) * n * B + (k % B)];
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Replay forward
+// ---------------------------------------------------------------------------
+template <class T, class M>
+__global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
+  const int64_t n = a.n;
+  const WaveId w = wave_id(n);
+  if (!w.live) return;
+  const int64_t j = w.i;
+  const int c = w.c;
+  const int d = a.pr.dim;
+  const bool on = c < d;
+  Nbr nb;
+  nb.init(c, d);
+  const int S = a.pr.S;
+  T *ysave = (T *)a.y_save;
+  const int64_t tr = uniform((int)(a.perm ? a.perm[j] : j));
+  int N = uniform(a.nsteps[tr]);
+  const int cap = a.h_rows ? a.rows : a.pr.max_steps;
+  const bool ok = N >= 0 && N <= cap;
+  if (!ok) N = 0;
+  WSteps<T> src;
+  src.init(a, j, tr);
+  T x = on ? ((const T *)a.u0)[c * n + tr] : T(0);
+  const T F = uniform(((const T *)a.p)[tr]);
+  for (int q = 0; q < S; ++q) {
+    const int ix = a.sidx[q * n + tr];
+    if (on && (!ok || ix < 0 || ix > N)) ysave[(q * d + c) * n + tr] = nanv<T>();
+  }
+  int s = 0;
+  int nxt = ok ? uniform(a.sidx[tr]) : -1;
+  for (int k = 0; k <= N; ++k) {
+    while (s < S && nxt == k) {
+      if (on) ysave[(s * d + c) * n + tr] = x;
+      ++s;
+      nxt = s < S ? uniform(a.sidx[s * n + tr]) : -1;
+    }
+    if (k < N) x = M::fwd(x, F, src.load(k), nb);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Replay + reverse sweep.  Workspace: checkpoint m of local slot jl is the
+// 64-component row ws[(m * ws_lanes + jl) * 64 + c] (one contiguous 512-byte
+// store per wavefront in FP64).
+// ---------------------------------------------------------------------------
+template <class T, class M, int CK>
+__global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
+  const int64_t n = a.n;
+  const WaveId w = wave_id(a.nslots);
+  if (!w.live) return;
+  const int64_t jl = w.i;
+  const int64_t j = a.slot0 + jl;
+  const int c = w.c;
+  const int d = a.pr.dim;
+  const bool on = c < d;
+  Nbr nb;
+  nb.init(c, d);
+  const int64_t C = a.ws_lanes;
+  const int S = a.pr.S;
+  const int lk = a.loss_kind;
+  const bool saves = lk != DA_LOSS_SUMSQ_FINAL;
+  const T *aux = (const T *)a.aux;
+  T *ws = (T *)a.ws + jl * 64 + c;
+  const int64_t tr = uniform((int)(a.perm ? a.perm[j] : j));
+  int N = uniform(a.nsteps[tr]);
+  const int cap = a.h_rows ? a.rows : a.pr.max_steps;
+  const bool ok = a.status[tr] == LANE_OK && N >= 0 && N <= cap && N <= a.max_n_steps;
+  if (!ok) N = 0;
+  WSteps<T> src;
+  src.init(a, j, tr);
+  T x = on ? ((const T *)a.u0)[c * n + tr] : T(0);
+  const T F = uniform(((const T *)a.p)[tr]);
+
+  // ---- forward replay, checkpoints, loss terms ----
+  T ss = T(0);   // this lane's share of the loss
+  bool first = true;
+  int s = 0;
+  int nxt = (ok && saves) ? uniform(a.sidx[tr]) : -1;
+  auto terms = [&](int k) {
+    while (s < S && nxt == k) {
+      if (on) {
+        const T av = aux[((int64_t)s * d + c) * n + tr];
+        if (lk == DA_LOSS_MSE_SAVE) {
+          const T r = x - av;
+          ss = first ? r * r : mac(r, r, ss);
+        } else {
+          ss = first ? av * x : mac(av, x, ss);
+        }
+      }
+      first = false;
+      ++s;
+      nxt = s < S ? uniform(a.sidx[s * n + tr]) : -1;
+    }
+  };
+  if (saves) terms(0);
+  T hcur = src.load(0);
+  for (int k = 0; k < N; ++k) {
+    const T hnext = src.load(k + 1);
+    if (k % CK == 0) ws[(int64_t)(k / CK) * C * 64] = x;
+    x = M::fwd(x, F, hcur, nb);
+    if (saves) terms(k + 1);
+    hcur = hnext;
+  }
+
+  // ---- loss and seeds at the final state ----
+  T lam = T(0), gF = T(0);
+  if (!saves) {
+    ss = on ? x * x : T(0);
+    lam = on ? T(2.0 * a.scale) * x : T(0);
+  }
+  int sh = S - 1;
+  int hidx = (ok && saves) ? uniform(a.sidx[(int64_t)sh * n + tr]) : -1;
+  auto seeds = [&](int k, T xk) {
+    while (sh >= 0 && hidx == k) {
+      if (on) {
+        const T av = aux[((int64_t)sh * d + c) * n + tr];
+        if (lk == DA_LOSS_MSE_SAVE) lam = mac(T(2.0 * a.scale), xk - av, lam);
+        else lam = mac(T(a.scale), av, lam);
+      }
+      --sh;
+      hidx = sh >= 0 ? uniform(a.sidx[(int64_t)sh * n + tr]) : -1;
+    }
+  };
+  if (saves) seeds(N, x);
+
+  // ---- reverse sweep by segments of CK steps ----
+  const int Mw = (N + CK - 1) / CK;
+  for (int m = Mw - 1; m >= 0; --m) {
+    T xs[CK], hs[CK];
+    xs[0] = ws[(int64_t)m * C * 64];
+#pragma unroll
+    for (int b = 0; b < CK; ++b) hs[b] = src.load(m * CK + b);
+#pragma unroll
+    for (int b = 1; b < CK; ++b)
+      xs[b] = (m * CK + b - 1 < N) ? M::fwd(xs[b - 1], F, hs[b - 1], nb) : xs[b - 1];
+#pragma unroll
+    for (int b = CK - 1; b >= 0; --b) {
+      const int k = m * CK + b;
+      if (k < N) {
+        M::adj(xs[b], F, hs[b], nb, lam, gF);
+        if (saves) seeds(k, xs[b]);
+      }
+    }
+  }
+
+  // ---- outputs ----
+  const T L = wave_sum(on ? ss : T(0));
+  const T G = wave_sum(on ? gF : T(0));
+  if (on && a.gu0) ((T *)a.gu0)[c * n + tr] = ok ? lam : nanv<T>();
+  if (c == 0) {
+    if (a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * L : nanv<T>();
+    if (a.gp) ((T *)a.gp)[tr] = ok ? G : nanv<T>();
+  }
+}
+
+}  // namespace wave
+}  // namespace dadj

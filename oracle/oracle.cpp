@@ -442,7 +442,7 @@ void erk_step(const Tableau &tb, int kind, int d, T *y, const T *p, T h) {
  * gp accumulates dL/dp.  Stage states are recomputed from y = y_k. */
 template <class T, bool F>
 void erk_step_adjoint(const Tableau &tb, int kind, int d, const T *y, const T *p,
-                      T h, T *lam, T *gp) {
+                      T h, T *lam, T *gp, T *gpc = nullptr) {
   T Y[7][MAXD], K[7][MAXD], Wv[7][MAXD], kb[MAXD], lacc[MAXD];
   rhs_f<T, F>(kind, d, y, p, K[0]);
   erk_stages<T, F>(tb, kind, d, y, p, h, 5, false, Y, K);
@@ -461,7 +461,10 @@ void erk_step_adjoint(const Tableau &tb, int kind, int d, const T *y, const T *p
       kb[c] = h * acc;
     }
     rhs_vjp_y<T, F>(kind, d, Y[i], p, kb, Wv[i]);
-    rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);
+    if (gpc)  /* Lorenz-96, df_c/dF = 1: component c contributes kb[c] */
+      for (int c = 0; c < d; ++c) gpc[c] = gpc[c] + kb[c];
+    else
+      rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);
     for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];
   }
   for (int c = 0; c < d; ++c) lam[c] = lacc[c];
@@ -801,10 +804,24 @@ inline void one_step(const orc_problem *P, T *y, const T *p, T h) {
 }
 
 template <class T, bool F>
-inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, T *lam, T *gp) {
+inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, T *lam, T *gp,
+                             T *gpc = nullptr) {
   if (P->method == M_ROS2) ros2_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
   else erk_step_adjoint<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p,
-                              h, lam, gp);
+                              h, lam, gp, gpc);
+}
+
+/* Sum of v[0..d) (d <= 64, zero beyond) by pairwise sums at offsets 32, 16,
+ * ..., 1: w[c] = v[c] + v[c ^ off] for every c, then the entry at 0. */
+template <class T>
+T pairwise64(const T *v, int d) {
+  T a[64], b[64];
+  for (int c = 0; c < 64; ++c) a[c] = c < d ? v[c] : T(0.0);
+  for (int off = 32; off >= 1; off >>= 1) {
+    for (int c = 0; c < 64; ++c) b[c] = a[c] + a[c ^ off];
+    for (int c = 0; c < 64; ++c) a[c] = b[c];
+  }
+  return a[0];
 }
 
 /* Fixed-step replay of a recorded mesh: writes y at every save index. */
@@ -894,12 +911,20 @@ void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, cons
   if (loss_kind != L_SUMSQ_FINAL)
     for (; s_hi >= 0 && sidx[s_hi] == N; --s_hi)
       save_seed<T, F>(loss_kind, d, yN, &aux[s_hi * d], scale, lam);
+  /* Fused mode follows the kernels' schedule also in its association order:
+   * the Lorenz-96 F-gradient (a sum over components, stages and steps) is kept
+   * per component over the whole sweep and the components are combined at
+   * the end by pairwise sums.  Plain mode adds every term into one sum. */
+  T gpc[MAXD];
+  for (int c = 0; c < d; ++c) gpc[c] = T(0.0);
+  T *split = (F && P->rhs == R_LORENZ96 && P->method != M_ROS2) ? gpc : nullptr;
   for (int k = N - 1; k >= 0; --k) {
-    one_step_adjoint<T, F>(P, &ybuf[k * d], p, h[k], lam, g);
+    one_step_adjoint<T, F>(P, &ybuf[k * d], p, h[k], lam, g, split);
     if (loss_kind != L_SUMSQ_FINAL)
       for (; s_hi >= 0 && sidx[s_hi] == k; --s_hi)
         save_seed<T, F>(loss_kind, d, &ybuf[k * d], &aux[s_hi * d], scale, lam);
   }
+  if (split) g[0] = pairwise64(gpc, d);
   for (int c = 0; c < d; ++c) gu0[c] = lam[c];
   for (int q = 0; q < Pn; ++q) gp[q] = g[q];
 }

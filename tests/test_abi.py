@@ -55,7 +55,17 @@ def test_invalid_problems_rejected(da, change, code):
 
 def test_unsupported_combinations(da):
     prob = W.Problem(W.LORENZ96, 64, 1, W.ROS2, 0.0, 1.0, 1e-6, 1e-6, 100)
-    assert _call_record(da, prob) in (-1, -2)
+    assert _call_record(da, prob) == -2
+    assert "ROS2" in da.last_error()
+    for dim in (3, 65):
+        prob = W.Problem(W.LORENZ96, dim, 1, W.TSIT5, 0.0, 1.0, 1e-6, 1e-6, 100)
+        assert _call_record(da, prob) == -1
+
+
+def test_lorenz96_workspace_rows(da):
+    """The wavefront kernels keep a whole 64-value row per checkpoint."""
+    prob = W.Problem(W.LORENZ96, 40, 1, W.TSIT5, 0.0, 1.0, 1e-6, 1e-6, 100, checkpoint=1)
+    assert da.replay_grad_workspace(prob, 100, 50) == 100 * 50 * 64 * 8
 
 
 def test_bad_dtype_and_sizes(da):

@@ -22,7 +22,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 # (workload, lanes) small enough for the oracle, several tiles and a ragged tail
-SMALL = [(1, 1024), (2, 1000), (3, 1500), (4, 300)]
+SMALL = [(1, 1024), (2, 1000), (3, 1500), (4, 300), (5, 200)]
 TOL = {"f64": 1e-12, "f32": 1e-4}
 
 
@@ -146,7 +146,7 @@ def test_gpu_record_equals_gpu_replay(da, orc, wid, n):
     assert err.max() <= TOL[w.dtype]
 
 
-@pytest.mark.parametrize("wid,n", [(1, 1024), (2, 1000), (3, 777), (4, 300)])
+@pytest.mark.parametrize("wid,n", [(1, 1024), (2, 1000), (3, 777), (4, 300), (5, 150)])
 def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
     """A replay order changes the lane schedule only: every output is bitwise
     the same; the order is a valid permutation with non-increasing step
@@ -194,7 +194,7 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
                        r1[2][:, torch.from_numpy(~longest).cuda()])
 
 
-@pytest.mark.parametrize("wid,n", [(2, 1000), (3, 600), (4, 300)])
+@pytest.mark.parametrize("wid,n", [(2, 1000), (3, 600), (4, 300), (5, 120)])
 def test_checkpoint_intervals_give_identical_gradients(da, orc, wid, n):
     """The reverse sweep's checkpoint interval changes what is stored and what
     is recomputed, never the arithmetic: all intervals agree bitwise."""
@@ -254,6 +254,51 @@ def test_loss_kinds_and_cotangents(da, orc):
         assert np.allclose(loss.cpu().numpy(), lo, rtol=1e-12)
 
 
+@pytest.mark.parametrize("dim", [64, 40, 5])
+def test_lorenz96_losses_and_dimensions(da, orc, dim):
+    """Lorenz-96 on the wavefront kernels: dimensions that fill a wavefront or
+    not, cotangent and MSE losses at several save times, Dopri5 as well."""
+    w = W.WORKLOADS[5]
+    n = 90
+    inp = W.make_inputs(5, n)
+    u0n = np.ascontiguousarray(inp["u0"][:, :dim])
+    pn = inp["p"]
+    _print(f"case: Lorenz-96 d={dim}, n={n}")
+    for method in (W.TSIT5, W.DOPRI5):
+        prob = W.Problem(W.LORENZ96, dim, 1, method, 0.0, 1.0, 1e-7, 1e-7, 4096,
+                         save_times=(0.25, 0.5, 1.0))
+        m = orc.record(prob, u0n, pn, fused=True)
+        assert np.all(m["status"] == 0)
+        mesh = mesh_to_dev(m, prob.max_steps, torch)
+        u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+        aux = np.random.default_rng(dim).standard_normal((n, 3, dim))
+        for lk, sc in ((W.COTANGENT, 0.5), (W.MSE_SAVE, 1.0 / 3.0), (W.SUMSQ_FINAL, 1.0)):
+            ax = None if lk == W.SUMSQ_FINAL else aux
+            lo, go, po = orc.replay_grad(prob, u0n, pn, m, lk, aux=ax, scale=sc, fused=True)
+            loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, lk,
+                                           aux=None if ax is None else aux_to_dev(ax, torch),
+                                           scale=sc)
+            torch.cuda.synchronize()
+            err = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+            _print(f"  method {method} loss {lk}: max rel err {err.max():.3e}")
+            assert err.max() <= 1e-12, (method, lk, err.max())
+            # the loss is a sum over components that the GPU adds pairwise and
+            # the oracle in sequence: both within 2 d eps of the sum of |terms|
+            ys_o, yN_o = orc.replay(prob, u0n, pn, m, fused=True)
+            if lk == W.COTANGENT:
+                mag = sc * np.abs(ys_o * aux).sum((1, 2))
+            elif lk == W.MSE_SAVE:
+                mag = sc * ((ys_o - aux) ** 2).sum((1, 2))
+            else:
+                mag = sc * (yN_o ** 2).sum(1)
+            assert np.all(np.abs(loss.cpu().numpy() - lo) <= 4 * dim * 2.3e-16 * mag)
+        # forward replay of the shared mesh equals the oracle's states
+        ys = da.replay_fwd(prob, u0, p, mesh)
+        yo, _ = orc.replay(prob, u0n, pn, m, fused=True)
+        torch.cuda.synchronize()
+        assert np.array_equal(ys.cpu().numpy().transpose(2, 0, 1), yo)
+
+
 def test_failed_lanes_and_edge_sizes(da, orc):
     """Lanes that fail report the oracle's status and NaN gradients; n = 1 and
     n = 0 work; max_steps bounds the record."""
@@ -291,7 +336,7 @@ def test_failed_lanes_and_edge_sizes(da, orc):
 
 
 def test_solve_fwd_matches_record(da, orc):
-    for wid, n in ((1, 1000), (3, 500), (4, 200)):
+    for wid, n in ((1, 1000), (3, 500), (4, 200), (5, 70)):
         w, prob, inp, aux, scale = _setup(orc, wid, n)
         _print(f"case: solve_fwd, workload {wid}, n={n}")
         u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)

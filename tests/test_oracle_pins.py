@@ -458,6 +458,27 @@ def test_adjoint_matches_dual_numbers(orc, case):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_adjoint_matches_dual_numbers(orc, case):
+    """The fused-rounding mode (the kernels' arithmetic schedule, including the
+    per-component accumulation of the Lorenz-96 F-gradient) passes the same
+    dot-product test, and stays within rounding of the plain mode."""
+    name, prob, u0, p, lk, aux = case
+    m = orc.record(prob, u0, p, fused=True)
+    assert np.all(m["status"] == 0)
+    loss, gu0, gp = orc.replay_grad(prob, u0, p, m, lk, aux=aux, scale=0.7, fused=True)
+    lp, gu0p, gpp = orc.replay_grad(prob, u0, p, m, lk, aux=aux, scale=0.7, fused=False)
+    rng = np.random.default_rng(5)
+    for _ in range(3):
+        du0 = rng.standard_normal(u0.shape)
+        dp = rng.standard_normal(p.shape) * p
+        _, dl, _, _ = orc.replay_jvp(prob, u0, p, du0, dp, m, lk, aux=aux, scale=0.7)
+        adj = (gu0 * du0).sum(1) + (gp * dp).sum(1)
+        assert np.allclose(adj, dl, rtol=1e-11, atol=1e-11 * np.abs(dl).max()), name
+    assert np.allclose(gp, gpp, rtol=1e-10, atol=1e-12 * np.abs(gpp).max()), name
+    assert np.allclose(gu0, gu0p, rtol=1e-10, atol=1e-12 * np.abs(gu0p).max()), name
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_adjoint_matches_finite_differences(orc, case):
     """Central differences of the replayed loss on the frozen mesh."""
     name, prob, u0, p, lk, aux = case
