@@ -346,6 +346,107 @@ def test_solve_fwd_matches_record(da, orc):
         assert torch.equal(ys, yf) and torch.equal(ns, mesh.n_steps) and torch.equal(st, mesh.status)
 
 
+@pytest.mark.parametrize("wid", [3, 4, 5])
+def test_full_size_workloads_sampled(da, orc, wid):
+    """Workloads 3, 4 and 5 at their full sizes in the benchmark's launch
+    configuration (record, lane ordering with the replay table, one gradient
+    pass); sampled trajectories are checked against the oracle on the GPU's own
+    mesh (gradients) and against the oracle's record (step counts, error
+    norms)."""
+    w = W.WORKLOADS[wid]
+    prob = w.problem()
+    inp = W.make_inputs(wid)
+    n = w.n
+    aux = None
+    scale = 1.0
+    if w.loss == W.MSE_SAVE:
+        aux, st = mse_targets(orc, wid, n, inp)
+        assert np.all(st == 0)
+        scale = 1.0 / (n * w.n_save_eff * w.dim)
+    _print(f"case: full size workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    mesh, _ = da.record(prob, u0, p, save=False)
+    sm = da.mesh_sort(prob, mesh)
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)()
+    torch.cuda.synchronize()
+    st = sm.status.cpu().numpy()
+    assert np.all(st == 0)
+    perm = sm.perm.cpu().numpy()
+    ns_all = sm.n_steps.cpu().numpy()
+    assert np.all(np.diff(ns_all[perm]) <= 0)
+    rng = np.random.default_rng(7 + wid)
+    k = 96
+    slots = np.unique(np.concatenate([rng.choice(n, k, replace=False), [0, n - 1]]))
+    tr = perm[slots]                                   # longest and shortest included
+    N = int(ns_all.max())
+    idx = torch.from_numpy(tr.astype(np.int64)).cuda()
+    h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
+    sub = {"h": np.ascontiguousarray(h), "n_steps": ns_all[tr],
+           "save_idx": sm.save_idx.cpu().numpy()[:, tr].T.copy(), "status": st[tr]}
+    pn = prob.replace(max_steps=N)
+    ax = None if aux is None else aux[tr]
+    lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, w.loss, aux=ax,
+                                 scale=scale, fused=True)
+    err = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
+    _print(f"  sampled {len(tr)} trajectories: max rel err {err.max():.3e}, max steps {N}")
+    assert err.max() <= TOL[w.dtype]
+    E = orc.mesh_max_err(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
+    assert np.all(E <= 1 + (1e-6 if w.dtype == "f64" else 1e-3))
+    mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
+    no = mo["n_steps"]
+    dn = np.abs(sub["n_steps"] - no)
+    if w.dtype == "f64":
+        assert np.all(dn <= np.maximum(2, 0.01 * no))
+    else:
+        assert np.mean(dn <= np.maximum(2, 0.01 * no)) >= 0.9
+        assert np.all(dn <= np.maximum(8, 0.1 * no))
+
+
+def test_degenerate_trajectories(da, orc):
+    """Fixed points and one-step solves: Lorenz-63 at the origin and Lorenz-96
+    at x = F (f == 0 exactly: zero error estimate, maximal growth), and an
+    interval shorter than the first step."""
+    _print("case: degenerate trajectories")
+    # Lorenz-63 at the origin, among ordinary trajectories
+    w = W.WORKLOADS[1]
+    prob = w.problem()
+    inp = W.make_inputs(1, 70)
+    inp["u0"][3] = 0.0
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, ys = da.record(prob, u0, p)
+    torch.cuda.synchronize()
+    mg = mesh_to_host(mesh, prob.max_steps)
+    assert mg["n_steps"][3] == m["n_steps"][3]
+    assert np.array_equal(mg["h"][3], m["h"][3])
+    lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, fused=True)
+    l1, g1, q1 = da.replay_grad(prob, u0, p, mesh_to_dev(m, prob.max_steps, torch))
+    torch.cuda.synchronize()
+    assert np.all(grad_rel_err(g1.cpu().numpy().T, q1.cpu().numpy().T, go, po)[
+        np.arange(70) != 3] <= 1e-12)
+    assert np.all(g1.cpu().numpy()[:, 3] == 0) and l1.cpu().numpy()[3] == 0
+    # Lorenz-96 at its fixed point
+    w5 = W.WORKLOADS[5]
+    inp5 = W.make_inputs(5, 6)
+    inp5["u0"][2] = inp5["p"][2, 0]
+    prob5 = w5.problem()
+    m5 = orc.record(prob5, inp5["u0"], inp5["p"], fused=True)
+    u05, p5 = to_dev(inp5["u0"], torch), to_dev(inp5["p"], torch)
+    mesh5, ys5 = da.record(prob5, u05, p5)
+    torch.cuda.synchronize()
+    mg5 = mesh_to_host(mesh5, prob5.max_steps)
+    assert mg5["n_steps"][2] == m5["n_steps"][2]
+    assert np.array_equal(ys5.cpu().numpy()[-1, :, 2], inp5["u0"][2])
+    # an interval shorter than the starting step: one clipped step
+    prob1 = w.problem(t1=1e-9)
+    m1 = orc.record(prob1, inp["u0"][:5], inp["p"][:5], fused=True)
+    mesh1, _ = da.record(prob1, u0[:, :5].contiguous(), p[:, :5].contiguous())
+    torch.cuda.synchronize()
+    assert np.array_equal(mesh1.n_steps.cpu().numpy(), m1["n_steps"])
+    assert np.all(m1["n_steps"] >= 1)
+
+
 def test_full_size_lorenz_dopri5_sampled(da, orc):
     """Workload 2 at its full size (2^20 lanes), in the launch configuration of
     the benchmark (record, lane ordering, replay gradient); a sample of lanes
