@@ -235,6 +235,16 @@ def main():
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
     pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
                              for k in range(passes)]))
+    # forward-only adaptive solve of the same ensemble (outside the job)
+    solve_ms = []
+    for r in range(3):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        da.solve_fwd(prob, u0, p)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            solve_ms.append(a0.elapsed_time(a1))
     st = mesh.status.cpu().numpy()
     ns = mesh.n_steps.double()
     ok = torch.from_numpy(st == 0).to(dev)
@@ -263,6 +273,8 @@ def main():
                      "flop_per_step": flop_step, "populated_steps_per_launch": total_steps},
         "per_pass": {"ms": pass_ms, "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
         "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
+        "solve_fwd": {"ms": float(np.mean(solve_ms)),
+                      "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],
                  "max_over_mean": state["N"] / mean_steps, "failed_lanes": int((st != 0).sum())},
     }
