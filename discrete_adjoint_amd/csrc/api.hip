@@ -260,7 +260,7 @@ int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *s
   if (!mesh || !mesh->n_steps) return fail(DA_EINVAL, "mesh is NULL");
   hipStream_t s = (hipStream_t)stream;
   int32_t *d = nullptr;
-  hipError_t e = hipMalloc((void **)&d, sizeof(int32_t));
+  hipError_t e = hipMalloc((void **)&d, dadj::max_steps_scratch_ints() * sizeof(int32_t));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc");
   e = dadj::launch_max_steps(n, mesh->n_steps, d, s);
   if (e == hipSuccess) e = hipMemcpyAsync(host_max, d, sizeof(int32_t), hipMemcpyDeviceToHost, s);

@@ -82,6 +82,7 @@ hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps
 hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
                                const int32_t *nsteps, const int32_t *perm, void *h_rows,
                                int32_t rows, hipStream_t s);
+size_t max_steps_scratch_ints();  // size of dev_out below
 hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s);
 
 }  // namespace dadj

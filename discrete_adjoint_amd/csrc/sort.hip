@@ -77,6 +77,48 @@ __global__ __launch_bounds__(SORT_THREADS) void k_scan(unsigned *__restrict__ co
   }
 }
 
+// Multi-workgroup exclusive scan of counts[0..m): each workgroup scans a
+// segment of SCAN_SEG values in place and writes the segment total; the
+// totals are scanned (k_scan) and added back (k_scan_add).
+constexpr int SCAN_SEG = SORT_THREADS * 4;
+
+__global__ __launch_bounds__(SORT_THREADS) void k_scan_seg(unsigned *__restrict__ counts,
+                                                           int64_t m,
+                                                           unsigned *__restrict__ seg_total) {
+  __shared__ unsigned part[SORT_THREADS];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_SEG + (int64_t)threadIdx.x * 4;
+  unsigned v[4], t = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[q] = (base + q < m) ? counts[base + q] : 0u;
+    t += v[q];
+  }
+  part[threadIdx.x] = t;
+  __syncthreads();
+  for (int off = 1; off < SORT_THREADS; off <<= 1) {
+    const unsigned add = threadIdx.x >= (unsigned)off ? part[threadIdx.x - off] : 0u;
+    __syncthreads();
+    part[threadIdx.x] += add;
+    __syncthreads();
+  }
+  unsigned run = part[threadIdx.x] - t;  // exclusive prefix of this thread's items
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (base + q < m) counts[base + q] = run;
+    run += v[q];
+  }
+  if (threadIdx.x == SORT_THREADS - 1) seg_total[blockIdx.x] = part[SORT_THREADS - 1];
+}
+
+__global__ __launch_bounds__(SORT_THREADS) void k_scan_add(unsigned *__restrict__ counts,
+                                                           int64_t m,
+                                                           const unsigned *__restrict__ seg_off) {
+  const unsigned add = seg_off[blockIdx.x];
+  const int64_t base = (int64_t)blockIdx.x * SCAN_SEG;
+  for (int q = threadIdx.x; q < SCAN_SEG; q += SORT_THREADS)
+    if (base + q < m) counts[base + q] += add;
+}
+
 // stable scatter of one tile: rank among equal digits of earlier elements
 __global__ __launch_bounds__(SORT_THREADS) void k_scatter(int64_t n, int shift, int64_t ntiles,
                                                           const unsigned *__restrict__ counts,
@@ -178,14 +220,32 @@ __global__ __launch_bounds__(SORT_THREADS) void k_replay_table(
   }
 }
 
+// Largest value of ns[0..n): MAX_BLOCKS workgroups each reduce a strided
+// share into out[1 + block], then one workgroup reduces those into out[0].
+constexpr int MAX_BLOCKS = 256;
+
 __global__ __launch_bounds__(1024) void k_max_steps(int64_t n, const int32_t *__restrict__ ns,
                                                     int32_t *__restrict__ out) {
   __shared__ int part[1024];
   int m = 0;
-  for (int64_t j = threadIdx.x; j < n; j += 1024) m = ns[j] > m ? ns[j] : m;
+  for (int64_t j = (int64_t)blockIdx.x * 1024 + threadIdx.x; j < n;
+       j += (int64_t)gridDim.x * 1024)
+    m = ns[j] > m ? ns[j] : m;
   part[threadIdx.x] = m;
   __syncthreads();
   for (int off = 512; off > 0; off >>= 1) {
+    if ((int)threadIdx.x < off && part[threadIdx.x + off] > part[threadIdx.x])
+      part[threadIdx.x] = part[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[1 + blockIdx.x] = part[0];
+}
+
+__global__ __launch_bounds__(MAX_BLOCKS) void k_max_final(int nb, int32_t *__restrict__ out) {
+  __shared__ int part[MAX_BLOCKS];
+  part[threadIdx.x] = (int)threadIdx.x < nb ? out[1 + threadIdx.x] : 0;
+  __syncthreads();
+  for (int off = MAX_BLOCKS / 2; off > 0; off >>= 1) {
     if ((int)threadIdx.x < off && part[threadIdx.x + off] > part[threadIdx.x])
       part[threadIdx.x] = part[threadIdx.x + off];
     __syncthreads();
@@ -205,7 +265,9 @@ int key_bits(int32_t max_steps) {
 
 size_t sort_workspace_bytes(int64_t n) {
   const int64_t ntiles = (n + SORT_TILE - 1) / SORT_TILE;
-  return 3 * align_up((size_t)n * 4) + align_up((size_t)ntiles * RADIX * 4);
+  const int64_t m = ntiles * RADIX;
+  const int64_t nseg = (m + SCAN_SEG - 1) / SCAN_SEG;
+  return 3 * align_up((size_t)n * 4) + align_up((size_t)m * 4) + align_up((size_t)nseg * 4);
 }
 
 // Radix passes ping-pong between (kA, vA) and (kB, vB); the values of the
@@ -221,7 +283,10 @@ hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps
   unsigned *kA = (unsigned *)q; q += align_up((size_t)n * 4);
   unsigned *kB = (unsigned *)q; q += align_up((size_t)n * 4);
   int32_t *vX = (int32_t *)q; q += align_up((size_t)n * 4);
-  unsigned *counts = (unsigned *)q;
+  unsigned *counts = (unsigned *)q; q += align_up((size_t)ntiles * RADIX * 4);
+  unsigned *seg_total = (unsigned *)q;
+  const int64_t m = ntiles * RADIX;
+  const unsigned nseg = (unsigned)((m + SCAN_SEG - 1) / SCAN_SEG);
   // choose the initial value buffer so that the last pass writes `perm`
   int32_t *vA = (passes % 2 == 0) ? perm : vX;
   int32_t *vB = (passes % 2 == 0) ? vX : perm;
@@ -229,7 +294,9 @@ hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps
   hipLaunchKernelGGL(k_init_keys, g1, SORT_THREADS, 0, s, n, pr.max_steps, nsteps, kA, vA);
   for (int shift = 0; shift < bits; shift += 8) {
     hipLaunchKernelGGL(k_hist, (unsigned)ntiles, SORT_THREADS, 0, s, n, shift, kA, counts, ntiles);
-    hipLaunchKernelGGL(k_scan, 1, SORT_THREADS, 0, s, counts, ntiles * RADIX);
+    hipLaunchKernelGGL(k_scan_seg, nseg, SORT_THREADS, 0, s, counts, m, seg_total);
+    hipLaunchKernelGGL(k_scan, 1, SORT_THREADS, 0, s, seg_total, (int64_t)nseg);
+    hipLaunchKernelGGL(k_scan_add, nseg, SORT_THREADS, 0, s, counts, m, seg_total);
     hipLaunchKernelGGL(k_scatter, (unsigned)ntiles, SORT_THREADS, 0, s, n, shift, ntiles, counts,
                        kA, vA, kB, vB);
     unsigned *tk = kA; kA = kB; kB = tk;
@@ -252,8 +319,13 @@ hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
   return hipGetLastError();
 }
 
+size_t max_steps_scratch_ints() { return 1 + MAX_BLOCKS; }
+
 hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s) {
-  hipLaunchKernelGGL(k_max_steps, 1, 1024, 0, s, n, nsteps, dev_out);
+  int64_t nb = (n + 1023) / 1024;
+  nb = nb < 1 ? 1 : (nb > MAX_BLOCKS ? MAX_BLOCKS : nb);
+  hipLaunchKernelGGL(k_max_steps, (unsigned)nb, 1024, 0, s, n, nsteps, dev_out);
+  hipLaunchKernelGGL(k_max_final, 1, MAX_BLOCKS, 0, s, (int)nb, dev_out);
   return hipGetLastError();
 }
 
