@@ -209,6 +209,36 @@ def replay_jvp(prob, u0, p, du0, dp, mesh, loss_kind: int = 0,
     return loss, dloss, ys, dys
 
 
+def replay_sens(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray] = None,
+                scale: float = 1.0, fused: bool = False):
+    """Forward-mode sensitivities of the replay along the d + P unit directions
+    (u0 components, then parameters), float64.
+
+    Returns (sens [n, S, d, d+P], loss [n], grad_u0 [n, d], grad_p [n, P]); the
+    gradient is the loss gradient by the chain rule through the tangents."""
+    u0 = np.ascontiguousarray(u0, dtype=np.float64)
+    p = np.ascontiguousarray(p, dtype=np.float64)
+    n = u0.shape[0]
+    S = prob.n_save_eff
+    Q = prob.dim + prob.n_params
+    h = np.ascontiguousarray(mesh["h"], dtype=np.float64)
+    ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
+    sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    status = np.ascontiguousarray(mesh["status"], dtype=np.int32)
+    ax = None if aux is None else np.ascontiguousarray(aux, dtype=np.float64)
+    sens = np.zeros((n, S, prob.dim, Q))
+    loss = np.zeros(n)
+    gu0 = np.zeros((n, prob.dim))
+    gp = np.zeros((n, prob.n_params))
+    P, keep = _cprob(prob)
+    _check(_load().orc_replay_sens_f64(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p),
+                                       ctypes.c_int32(int(fused)), _ptr(h), _ptr(ns), _ptr(sidx),
+                                       _ptr(status), ctypes.c_int32(loss_kind), _ptr(ax),
+                                       ctypes.c_double(scale), _ptr(sens), _ptr(loss), _ptr(gu0),
+                                       _ptr(gp)), "replay_sens")
+    return sens, loss, gu0, gp
+
+
 def mesh_max_err(prob, u0, p, mesh, fused: bool = False, nthreads: int = 0):
     """Largest embedded error norm E over the steps of ``mesh``, per lane."""
     u0 = np.ascontiguousarray(u0)

@@ -45,6 +45,7 @@
 #include <cstring>
 #include <limits>
 #include <omp.h>
+#include <vector>
 
 namespace {
 
@@ -92,6 +93,33 @@ inline Dual operator*(Dual a, Dual b) { return Dual(a.v * b.v, a.d * b.v + a.v *
 inline Dual operator/(Dual a, Dual b) {
   return Dual(a.v / b.v, (a.d * b.v - a.v * b.d) / (b.v * b.v));
 }
+/* Dual number of the fused-rounding mode: the tangent of every product and
+ * multiply-add is formed with fma in a fixed order (the written schedule of
+ * the GPU sensitivity kernels):
+ *   a*b        -> (a.v*b.v,        fma(a.d, b.v, a.v*b.d))
+ *   fma(a,b,c) -> (fma(a.v,b.v,c.v), fma(a.d, b.v, fma(a.v, b.d, c.d)))
+ *   a/b        -> (q = a.v/b.v,     fma(-q, b.d, a.d) / b.v)
+ * sums and differences act on both parts. */
+struct DualF {
+  double v, d;
+  DualF() : v(0), d(0) {}
+  DualF(double x) : v(x), d(0) {}
+  DualF(double x, double dx) : v(x), d(dx) {}
+};
+inline DualF operator+(DualF a, DualF b) { return DualF(a.v + b.v, a.d + b.d); }
+inline DualF operator-(DualF a, DualF b) { return DualF(a.v - b.v, a.d - b.d); }
+inline DualF operator-(DualF a) { return DualF(-a.v, -a.d); }
+inline DualF operator*(DualF a, DualF b) {
+  return DualF(a.v * b.v, std::fma(a.d, b.v, a.v * b.d));
+}
+inline DualF operator/(DualF a, DualF b) {
+  const double q = a.v / b.v;
+  return DualF(q, std::fma(-q, b.d, a.d) / b.v);
+}
+inline bool fin(DualF a) { return std::isfinite(a.v); }
+inline double val(DualF a) { return a.v; }
+inline DualF absval(DualF a) { return a.v < 0 ? -a : a; }
+
 inline bool fin(Dual a) { return std::isfinite(a.v); }
 inline bool fin(double a) { return std::isfinite(a); }
 inline bool fin(float a) { return std::isfinite(a); }
@@ -110,6 +138,9 @@ template <bool F> inline float mac(float a, float b, float c) {
   return F ? std::fma(a, b, c) : a * b + c;
 }
 template <bool F> inline Dual mac(Dual a, Dual b, Dual c) { return a * b + c; }
+template <bool F> inline DualF mac(DualF a, DualF b, DualF c) {
+  return DualF(std::fma(a.v, b.v, c.v), std::fma(a.d, b.v, std::fma(a.v, b.d, c.d)));
+}
 
 /* Chain sum_k coef[k]*x[k] over nonzero coefficients: first a product, then
  * multiply-adds.  Returns 0 when every coefficient is zero. */
@@ -1050,6 +1081,89 @@ int replay_grad_all(const orc_problem *P, int64_t n, const T *u0, const T *p, in
   return E_OK;
 }
 
+/* Forward-mode sensitivities of the replay (mesh fixed): for every direction
+ * q of the d + P unit directions (u0 components, then parameters) the replay
+ * runs in dual numbers (DualF with fused = 1, Dual with plain rounding),
+ * giving sens[i][s][c][q] = d y(save s)[c] / d theta_q, and the loss gradient
+ * by the chain rule, g_q = sum over seeds of seed . dy/dtheta_q with the
+ * terms in save-then-component order (first product, then multiply-adds):
+ *   final-state loss: seed = (2 scale) y_N  (the final state only)
+ *   MSE:              seed = (2 scale) (y_s - aux_s)
+ *   cotangent:        seed = scale aux_s.
+ * A failed lane gets NaN. */
+template <class D, bool F>
+void sens_lane(const orc_problem *P, int S, const double *u0, const double *p, const double *h,
+               int N, const int32_t *si, int status, int loss_kind, const double *aux,
+               double scale, double *sens, double *loss, double *gu0, double *gp) {
+  const int d = P->dim, Pn = P->n_params, Q = d + Pn;
+  if (status != S_OK) {
+    for (int k = 0; k < S * d * Q; ++k) sens[k] = NAN;
+    *loss = NAN;
+    for (int c = 0; c < d; ++c) gu0[c] = NAN;
+    for (int q = 0; q < Pn; ++q) gp[q] = NAN;
+    return;
+  }
+  double g[MAXD + MAXP];
+  for (int q = 0; q < Q; ++q) {
+    D yv[MAXD], pv[MAXP];
+    for (int c = 0; c < d; ++c) yv[c] = D(u0[c], q == c ? 1.0 : 0.0);
+    for (int r = 0; r < Pn; ++r) pv[r] = D(p[r], q == d + r ? 1.0 : 0.0);
+    std::vector<D> ysl((size_t)S * d, D(NAN));
+    for (int s = 0; s < S; ++s)
+      if (si[s] == 0)
+        for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+    for (int k = 0; k < N; ++k) {
+      one_step<D, F>(P, yv, pv, D(h[k]));
+      for (int s = 0; s < S; ++s)
+        if (si[s] == k + 1)
+          for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+    }
+    for (int s = 0; s < S; ++s)
+      for (int c = 0; c < d; ++c) sens[(s * d + c) * Q + q] = ysl[s * d + c].d;
+    double acc = 0.0;
+    bool first = true;
+    auto add = [&](double seed, double t) {
+      acc = first ? seed * t : mac<F>(seed, t, acc);
+      first = false;
+    };
+    if (loss_kind == L_SUMSQ_FINAL) {
+      for (int c = 0; c < d; ++c) add((2.0 * scale) * yv[c].v, yv[c].d);
+    } else {
+      for (int s = 0; s < S; ++s)
+        for (int c = 0; c < d; ++c) {
+          const double y = ysl[s * d + c].v, a = aux[s * d + c];
+          add(loss_kind == L_MSE_SAVE ? (2.0 * scale) * (y - a) : scale * a, ysl[s * d + c].d);
+        }
+    }
+    g[q] = acc;
+    if (q == 0) {  /* the loss of the replayed states */
+      double ss = 0.0;
+      bool f1 = true;
+      if (loss_kind == L_SUMSQ_FINAL) {
+        for (int c = 0; c < d; ++c) {
+          ss = f1 ? yv[c].v * yv[c].v : mac<F>(yv[c].v, yv[c].v, ss);
+          f1 = false;
+        }
+      } else {
+        for (int s = 0; s < S; ++s)
+          for (int c = 0; c < d; ++c) {
+            const double y = ysl[s * d + c].v, a = aux[s * d + c];
+            if (loss_kind == L_MSE_SAVE) {
+              const double r = y - a;
+              ss = f1 ? r * r : mac<F>(r, r, ss);
+            } else {
+              ss = f1 ? a * y : mac<F>(a, y, ss);
+            }
+            f1 = false;
+          }
+      }
+      *loss = scale * ss;
+    }
+  }
+  for (int c = 0; c < d; ++c) gu0[c] = g[c];
+  for (int r = 0; r < Pn; ++r) gp[r] = g[d + r];
+}
+
 }  // namespace
 
 /* ------------------------------------------------------------------ */
@@ -1111,6 +1225,32 @@ int orc_replay_grad_f32(const orc_problem *P, int64_t n, const float *u0, const 
                         int32_t nthreads) {
   return replay_grad_all<float>(P, n, u0, p, fused, h, nsteps, sidx, status, loss_kind, aux,
                                 scale, loss, gu0, gp, nthreads);
+}
+
+int orc_replay_sens_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
+                        int32_t fused, const double *h, const int32_t *nsteps,
+                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
+                        const double *aux, double scale, double *sens, double *loss,
+                        double *gu0, double *gp) {
+  const int rc = validate(P);
+  if (rc) return rc;
+  if (loss_kind < 0 || loss_kind > 2 || (loss_kind != L_SUMSQ_FINAL && !aux)) return E_INVAL;
+  const Opts o = make_opts(P);
+  const int d = P->dim, Pn = P->n_params, S = o.S, Q = d + Pn;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t i = 0; i < n; ++i) {
+    const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
+    const double *ax = aux ? aux + i * S * d : nullptr;
+    if (fused)
+      sens_lane<DualF, true>(P, S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                             sidx + i * S, status[i], loss_kind, ax, scale,
+                             sens + i * S * d * Q, loss + i, gu0 + i * d, gp + i * Pn);
+    else
+      sens_lane<Dual, false>(P, S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
+                             sidx + i * S, status[i], loss_kind, ax, scale,
+                             sens + i * S * d * Q, loss + i, gu0 + i * d, gp + i * Pn);
+  }
+  return E_OK;
 }
 
 /* Forward-mode derivative of the replayed loss along (du0, dp): one dual

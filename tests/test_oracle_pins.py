@@ -551,3 +551,79 @@ def test_fp32_oracle_tracks_fp64(orc):
     l64, g64, p64 = orc.replay_grad(prob, inp["u0"].astype(np.float64),
                                     inp["p"].astype(np.float64), m64)
     assert np.allclose(p32, p64, rtol=1e-3, atol=1e-3 * np.abs(p64).max())
+
+
+# ---------------------------------------------------------------------------
+# Forward-mode sensitivities (tangents carried through the replay)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+@pytest.mark.parametrize("fused", [False, True])
+def test_sensitivities_linear_closed_form(orc, method, fused):
+    """y' = p y on an arbitrary mesh: dy_N/dy0 = prod R(p h_n) and
+    dy_N/dp = y_N sum h_n R'(p h_n) / R(p h_n), from the stability function."""
+    rng = np.random.default_rng(11)
+    N, n = 29, 3
+    h = rng.uniform(0.01, 0.2, size=(n, N))
+    y0 = np.array([1.3, -0.4, 2.0])
+    pv = np.array([-0.6, -4.0, 0.35])
+    if method == W.ROS2:
+        g = orc.ros2_gamma()
+        R = lambda z: _R_ros2(g, z)
+    else:
+        coef = _stability_poly(orc.tableau(method))
+        R = lambda z: _R_erk(coef, z)
+    prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, 1e-6, 1e-6, N)
+    mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
+            "status": np.zeros(n)}
+    sens, loss, gu0, gp = orc.replay_sens(prob, y0[:, None], pv[:, None], mesh, fused=fused)
+    for i in range(n):
+        z = pv[i] * h[i]
+        Rz = np.array([R(zz) for zz in z])
+        prod = np.prod(Rz)
+        dR = np.array([_complex_step(R, zz) for zz in z])
+        assert sens[i, 0, 0, 0] == pytest.approx(prod, rel=2e-14)
+        assert sens[i, 0, 0, 1] == pytest.approx(y0[i] * prod * np.sum(h[i] * dR / Rz), rel=2e-13)
+        # final-state loss y_N^2: gradient 2 y_N dy_N/dtheta
+        yN = y0[i] * prod
+        assert gu0[i, 0] == pytest.approx(2 * yN * prod, rel=2e-13)
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+@pytest.mark.parametrize("fused", [False, True])
+def test_sensitivity_gradient_matches_adjoint(orc, case, fused):
+    """The loss gradient through forward tangents equals the reverse sweep's
+    (both are the exact derivative of the same discrete map); the tangents of
+    the final state match central differences on the frozen mesh."""
+    name, prob, u0, p, lk, aux = case
+    m = orc.record(prob, u0, p, fused=fused)
+    sens, loss, gu0, gp = orc.replay_sens(prob, u0, p, m, lk, aux=aux, scale=0.7, fused=fused)
+    la, ga, pa = orc.replay_grad(prob, u0, p, m, lk, aux=aux, scale=0.7, fused=fused)
+    assert np.allclose(loss, la, rtol=1e-13)
+    assert np.allclose(gu0, ga, rtol=1e-10, atol=1e-11 * np.abs(ga).max()), name
+    assert np.allclose(gp, pa, rtol=1e-10, atol=1e-11 * np.abs(pa).max()), name
+    # tangents of the final state against central differences in the parameters
+    d = prob.dim
+    for q in range(p.shape[1]):
+        eps = 1e-6 * np.abs(p[:, q])
+        pp = p.copy(); pp[:, q] += eps
+        pm = p.copy(); pm[:, q] -= eps
+        yp = orc.replay(prob, u0, pp, m, fused=fused)[1]
+        ym = orc.replay(prob, u0, pm, m, fused=fused)[1]
+        fd = (yp - ym) / (2 * eps[:, None])
+        last = m["save_idx"].argmax(axis=1)
+        sq = sens[np.arange(len(u0)), last, :, d + q]
+        if np.all(m["save_idx"].max(axis=1) == m["n_steps"]):
+            assert np.allclose(sq, fd, rtol=3e-5, atol=1e-6 * np.abs(fd).max()), (name, q)
+
+
+def test_fused_and_plain_sensitivities_agree(orc):
+    """The two roundings of the tangent arithmetic agree to rounding level on a
+    short horizon."""
+    prob = W.WORKLOADS[1].problem()
+    inp = W.make_inputs(1, 16)
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    sf = orc.replay_sens(prob, inp["u0"], inp["p"], m, fused=True)[0]
+    sp = orc.replay_sens(prob, inp["u0"], inp["p"], m, fused=False)[0]
+    assert np.allclose(sf, sp, rtol=1e-12, atol=1e-13 * np.abs(sp).max())
+    assert not np.array_equal(sf, sp)      # the schedules do differ
