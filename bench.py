@@ -53,6 +53,15 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 #    cotangent combinations 36, dJ contraction 29) = 188; total 306.
 #  Tsit5 / Lorenz-96 (d components): forward 6 x 4d + 48d = 72d; adjoint
 #    42d + 6 x (J^T v 7d + J_p^T v d + accumulate d) = 96d; total 168d.
+# Forward-mode sensitivities (all d + P unit directions as dual numbers, the
+# state counted once): per direction the tangent of every right-hand side
+# (Lorenz-63: 4 + 5 + 7 = 16 flop) and of the stage sums (same count as the
+# state's), so Dopri5 / Lorenz-63: 186 + 6 x (6 x 16 + 138) = 1590 and
+# Tsit5 / Lorenz-63: 192 + 6 x (6 x 16 + 144) = 1632.
+def sens_flop_per_step(method: str, rhs: str) -> int:
+    return {("dopri5", "lorenz63"): 1590, ("tsit5", "lorenz63"): 1632}.get((method, rhs), 0)
+
+
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
     table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
              ("ros2", "robertson"): 306}
@@ -235,6 +244,18 @@ def main():
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
     pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
                              for k in range(passes)]))
+    # forward-mode gradient of the same loss on the same replay order and table
+    sens_ms = []
+    if w.method != W.ROS2 and w.rhs != W.LORENZ96:
+        for r in range(3):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux, scale=scale,
+                           with_sens=False)
+            a1.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                sens_ms.append(a0.elapsed_time(a1))
     # forward-only adaptive solve of the same ensemble (outside the job)
     solve_ms = []
     for r in range(3):
@@ -273,6 +294,12 @@ def main():
                      "flop_per_step": flop_step, "populated_steps_per_launch": total_steps},
         "per_pass": {"ms": pass_ms, "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
         "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
+        "forward_mode_grad": None if not sens_ms else {
+            "ms": float(np.mean(sens_ms)),
+            "trajectory_gradients_per_s": n / (float(np.mean(sens_ms)) * 1e-3),
+            "flop_per_step": sens_flop_per_step(mname, rname),
+            "achieved_tflops": sens_flop_per_step(mname, rname) * total_steps
+            / (float(np.mean(sens_ms)) * 1e-3) / 1e12},
         "solve_fwd": {"ms": float(np.mean(solve_ms)),
                       "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],

@@ -43,7 +43,7 @@ MAX_SAVES = 128
 
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
-           "da_last_error", "da_version")
+           "da_replay_sens", "da_last_error", "da_version")
 
 
 class DadjError(RuntimeError):
@@ -97,9 +97,10 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_grad_workspace.restype = ctypes.c_size_t
     lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp]
+    lib.da_replay_sens.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, vp, vp]
     lib.da_last_error.restype = ctypes.c_char_p
     for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps",
-                 "da_replay_fwd", "da_replay_grad", "da_version"):
+                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -347,3 +348,28 @@ def replay_grad(prob, u0, p, mesh: Mesh, loss_kind: int = SUMSQ_FINAL, aux=None,
     """Replay + reverse sweep: (loss [n], grad_u0 [d, n], grad_p [P, n])."""
     call = ReplayGrad(prob, u0, p, mesh, loss_kind, aux, scale, max_n_steps, ws_bytes)
     return call(stream)
+
+
+def replay_sens(prob, u0, p, mesh: Mesh, loss_kind: Optional[int] = SUMSQ_FINAL, aux=None,
+                scale: float = 1.0, with_sens: bool = True, stream=None):
+    """Forward-mode sensitivities: (sens [S, d, d+P, n] or None, loss [n],
+    grad_u0 [d, n], grad_p [P, n]); loss_kind None computes only sens."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    Q = prob.dim + prob.n_params
+    dev = u0.device
+    if aux is not None:
+        _need(aux, (S, prob.dim, n), dt, "aux")
+    sens = torch.empty((S, prob.dim, Q, n), dtype=dt, device=dev) if with_sens else None
+    loss = torch.empty(n, dtype=dt, device=dev)
+    gu0 = torch.empty((prob.dim, n), dtype=dt, device=dev)
+    gp = torch.empty((prob.n_params, n), dtype=dt, device=dev)
+    P, keep = cproblem(prob, dt)
+    cm = mesh.c()
+    lp = None
+    if loss_kind is not None:
+        lobj = _Loss(loss_kind, None if aux is None else aux.data_ptr(), scale)
+        lp = ctypes.byref(lobj)
+    _check(_lib.da_replay_sens(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm), lp,
+                               _ptr(loss), _ptr(gu0), _ptr(gp), _ptr(sens), _stream(stream)))
+    return sens, loss, gu0, gp

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdadj.so")
-SOURCES = ["api.hip", "erk.hip", "ros2.hip", "l96.hip", "sort.hip"]
+SOURCES = ["api.hip", "erk.hip", "ros2.hip", "l96.hip", "sens.hip", "sort.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -350,4 +350,40 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   return ok();
 }
 
+int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                   void *grad_p, void *sens, void *stream) {
+  dadj::ProbArgs pr;
+  int rc = check_problem(prob, n, pr, nullptr);
+  if (rc) return rc;
+  if (pr.method == DA_ROS2 || pr.rhs == DA_RHS_LORENZ96)
+    return fail(DA_EUNSUPPORTED, "sensitivities are available for explicit methods on systems "
+                                 "of dimension <= 3");
+  if (n == 0) return ok();
+  if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
+  if (loss) {
+    if (loss->kind < DA_LOSS_SUMSQ_FINAL || loss->kind > DA_LOSS_COTANGENT)
+      return fail(DA_EINVAL, "bad loss kind %d", loss->kind);
+    if (loss->kind != DA_LOSS_SUMSQ_FINAL && !loss->aux)
+      return fail(DA_EINVAL, "loss kind %d needs aux", loss->kind);
+    if (!isfinite(loss->scale)) return fail(DA_EINVAL, "loss scale must be finite");
+  }
+  if (!u0 || !p) return fail(DA_EINVAL, "u0 and p must not be NULL");
+  dadj::ReplayArgs a;
+  fill_replay_args(a, pr, n, u0, p, mesh);
+  a.sens = sens;
+  a.has_loss = loss != nullptr;
+  if (loss) {
+    a.loss_kind = loss->kind;
+    a.aux = loss->aux;
+    a.scale = loss->scale;
+    a.loss_out = loss_out;
+    a.gu0 = grad_u0;
+    a.gp = grad_p;
+  }
+  const hipError_t e = dadj::launch_erk_replay_sens(a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "replay_sens launch");
+  return ok();
+}
+
 }  // extern "C"

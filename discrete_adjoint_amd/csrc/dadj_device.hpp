@@ -20,6 +20,16 @@ namespace dadj {
 __device__ __forceinline__ double mac(double a, double b, double c) { return __builtin_fma(a, b, c); }
 __device__ __forceinline__ float mac(float a, float b, float c) { return __builtin_fmaf(a, b, c); }
 
+// Coefficient products and the step-size update of a stage sum: c * x,
+// fma(c, x, acc) and fma(h, acc, y) (the tangent types of the sensitivity
+// kernels provide the same three forms).
+__device__ __forceinline__ double cmul(double c, double x) { return c * x; }
+__device__ __forceinline__ float cmul(double c, float x) { return float(c) * x; }
+__device__ __forceinline__ double cmac(double c, double x, double acc) { return mac(c, x, acc); }
+__device__ __forceinline__ float cmac(double c, float x, float acc) { return mac(float(c), x, acc); }
+__device__ __forceinline__ double smac(double h, double a, double y) { return mac(h, a, y); }
+__device__ __forceinline__ float smac(float h, float a, float y) { return mac(h, a, y); }
+
 __device__ __forceinline__ bool finite(double x) { return __builtin_isfinite(x); }
 __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }
 
@@ -216,9 +226,10 @@ struct Robertson {
 // Explicit RK stage machinery (one trajectory per lane, state in registers)
 // ---------------------------------------------------------------------------
 
-// Y = y + h * sum_{j<I} a[I][j] K[j]  (zero coefficients skipped)
-template <class Tab, int I, int D, class T>
-__device__ __forceinline__ void stage_state(const T (&y)[D], const T (&K)[7][D], T h,
+// Y = y + h * sum_{j<I} a[I][j] K[j]  (zero coefficients skipped).  T is the
+// state type (a float type, or a tangent type), H the step-size type.
+template <class Tab, int I, int D, class T, class H>
+__device__ __forceinline__ void stage_state(const T (&y)[D], const T (&K)[7][D], H h,
                                             T (&Y)[D]) {
 #pragma unroll
   for (int c = 0; c < D; ++c) {
@@ -227,34 +238,34 @@ __device__ __forceinline__ void stage_state(const T (&y)[D], const T (&K)[7][D],
 #pragma unroll
     for (int j = 0; j < I; ++j) {
       if (Tab::a[I][j] != 0.0) {
-        if (first) { acc = T(Tab::a[I][j]) * K[j][c]; first = false; }
-        else acc = mac(T(Tab::a[I][j]), K[j][c], acc);
+        if (first) { acc = cmul(Tab::a[I][j], K[j][c]); first = false; }
+        else acc = cmac(Tab::a[I][j], K[j][c], acc);
       }
     }
-    Y[c] = mac(h, acc, y[c]);
+    Y[c] = smac(h, acc, y[c]);
   }
 }
 
-template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
+template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T, class H>
 struct StageLoop {
-  __device__ static __forceinline__ void run(const T (&y)[Rhs::D], const T *p, T h,
+  __device__ static __forceinline__ void run(const T (&y)[Rhs::D], const T *p, H h,
                                              T (&Y)[7][Rhs::D], T (&K)[7][Rhs::D]) {
     stage_state<Tab, I>(y, K, h, Y[I]);
     if (I < LAST || LASTK) Rhs::f(Y[I], p, K[I]);
-    StageLoop<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, p, h, Y, K);
+    StageLoop<Tab, Rhs, I + 1, LAST, LASTK, T, H>::run(y, p, h, Y, K);
   }
 };
-template <class Tab, class Rhs, int LAST, bool LASTK, class T>
-struct StageLoop<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
-  __device__ static __forceinline__ void run(const T (&)[Rhs::D], const T *, T, T (&)[7][Rhs::D],
+template <class Tab, class Rhs, int LAST, bool LASTK, class T, class H>
+struct StageLoop<Tab, Rhs, LAST + 1, LAST, LASTK, T, H> {
+  __device__ static __forceinline__ void run(const T (&)[Rhs::D], const T *, H, T (&)[7][Rhs::D],
                                              T (&)[7][Rhs::D]) {}
 };
 
 // Stages 1..LAST from y with K[0] = f(y) given; K[LAST] too when LASTK.
-template <class Tab, class Rhs, int LAST, bool LASTK, class T>
-__device__ __forceinline__ void erk_stages(const T (&y)[Rhs::D], const T *p, T h,
+template <class Tab, class Rhs, int LAST, bool LASTK, class T, class H>
+__device__ __forceinline__ void erk_stages(const T (&y)[Rhs::D], const T *p, H h,
                                            T (&Y)[7][Rhs::D], T (&K)[7][Rhs::D]) {
-  StageLoop<Tab, Rhs, 1, LAST, LASTK, T>::run(y, p, h, Y, K);
+  StageLoop<Tab, Rhs, 1, LAST, LASTK, T, H>::run(y, p, h, Y, K);
 }
 
 }  // namespace dadj

@@ -61,6 +61,8 @@ struct ReplayArgs {
   double scale;
   void *loss_out, *gu0, *gp;   // [n], [d][n], [P][n]
   void *ws;                    // [ceil(max_n_steps / checkpoint)][d][ws_lanes]
+  void *sens;                  // sensitivity output [S][d][d+P][n] or null
+  int32_t has_loss;            // sensitivity call: loss outputs requested
   int64_t slot0, nslots, ws_lanes;
   int32_t max_n_steps;
 };
@@ -71,6 +73,7 @@ hipError_t launch_erk_replay_grad(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_l96_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_l96_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_l96_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_erk_replay_sens(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s);

@@ -233,6 +233,22 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
                    void *grad_u0, void *grad_p, int32_t max_n_steps, void *workspace,
                    size_t ws_bytes, void *stream);
 
+/* Forward-mode sensitivities of the replay, mesh held fixed: the d + P unit
+ * directions (u0 components first, then parameters) are carried as tangents
+ * through the same fixed-step replay as da_replay_grad ("Differentiable
+ * astrophysics at scale", Methodology: forward sensitivities integrated
+ * alongside the state in the per-trajectory kernel; "GRADSOLVE" review, FAQ:
+ * no derivative of the step sizes).  Outputs (each may be NULL):
+ * sens [S][d][d+P][n] with d y(save s)[c] / d theta_q (NaN where the save is
+ * not reached); with loss not NULL, loss_out [n], grad_u0 [d][n] and
+ * grad_p [P][n], the gradient of that loss by the chain rule through the
+ * tangents (the same quantity as da_replay_grad computes in reverse).
+ * Needs no workspace.  Explicit methods on systems of dimension <= 3
+ * (DA_EUNSUPPORTED otherwise).  Trajectories whose record failed get NaN. */
+int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                   void *grad_p, void *sens, void *stream);
+
 /* Message of the last non-zero return on this thread ("" if none). */
 const char *da_last_error(void);
 
