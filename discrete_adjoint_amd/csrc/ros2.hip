@@ -13,15 +13,17 @@ namespace dadj {
 namespace {
 
 template <int D, class T> struct Ros2Step {
-  T J[D * D], LU[D * D];
+  T J[D * D], LU[D * D], rinv[D];  // rinv[k] = 1 / U_kk
   int perm[D];
   T f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
 };
 
 // In-place LU of A (row-major) with partial pivoting; perm[i] = original row
-// now in position i.  Row exchanges are register selects.
+// now in position i.  Row exchanges are register selects.  Each pivot's
+// reciprocal is formed once (a correctly rounded 1 / u) and every division by
+// the pivot, here and in the solves, is a multiplication by it.
 template <int D, class T>
-__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D]) {
+__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rinv)[D]) {
 #pragma unroll
   for (int i = 0; i < D; ++i) perm[i] = i;
 #pragma unroll
@@ -46,9 +48,10 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D]) {
       perm[k] = sw ? po : pt;
       perm[r] = sw ? pt : po;
     }
+    rinv[k] = T(1) / A[k * D + k];
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
-      const T l = A[i * D + k] / A[k * D + k];
+      const T l = A[i * D + k] * rinv[k];
       A[i * D + k] = l;
 #pragma unroll
       for (int j = k + 1; j < D; ++j) A[i * D + j] = mac(-l, A[k * D + j], A[i * D + j]);
@@ -61,8 +64,8 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D]) {
 // (a select between loads through the argument would become an indexed load
 // and keep the caller's arrays out of registers).
 template <int D, class T>
-__device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const int (&perm)[D],
-                                         const T (&b_in)[D], T (&x)[D]) {
+__device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const T (&rinv)[D],
+                                         const int (&perm)[D], const T (&b_in)[D], T (&x)[D]) {
   T b[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) b[i] = b_in[i];
@@ -81,21 +84,21 @@ __device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const int (&perm)
   for (int i = D - 1; i >= 0; --i) {
 #pragma unroll
     for (int j = i + 1; j < D; ++j) x[i] = mac(-LU[i * D + j], x[j], x[i]);
-    x[i] = x[i] / LU[i * D + i];
+    x[i] = x[i] * rinv[i];
   }
 }
 
 // Solve A^T x = b from the factors of A (A^T = U^T L^T P).
 template <int D, class T>
-__device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const int (&perm)[D],
-                                           const T (&b)[D], T (&x)[D]) {
+__device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)[D],
+                                           const int (&perm)[D], const T (&b)[D], T (&x)[D]) {
   T z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     z[i] = b[i];
 #pragma unroll
     for (int j = 0; j < i; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
-    z[i] = z[i] / LU[i * D + i];
+    z[i] = z[i] * rinv[i];
   }
 #pragma unroll
   for (int i = D - 1; i >= 0; --i)
@@ -125,15 +128,15 @@ __device__ __forceinline__ void ros2_forward(const T (&y)[Rhs::D], const T *p, T
 #pragma unroll
     for (int b = 0; b < D; ++b)
       s.LU[a * D + b] = (a == b) ? mac(-gh, s.J[a * D + b], T(1)) : (-gh) * s.J[a * D + b];
-  lu_factor<D>(s.LU, s.perm);
+  lu_factor<D>(s.LU, s.perm, s.rinv);
   Rhs::f(y, p, s.f1);
-  lu_solve<D>(s.LU, s.perm, s.f1, s.k1);
+  lu_solve<D>(s.LU, s.rinv, s.perm, s.f1, s.k1);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.Y2[c] = mac(h, s.k1[c], y[c]);
   Rhs::f(s.Y2, p, s.f2);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.r2[c] = mac(T(-2), s.k1[c], s.f2[c]);
-  lu_solve<D>(s.LU, s.perm, s.r2, s.k2);
+  lu_solve<D>(s.LU, s.rinv, s.perm, s.r2, s.k2);
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     const T acc = mac(T(0.5), s.k2[c], T(1.5) * s.k1[c]);
@@ -195,7 +198,7 @@ struct Ros2 {
       kb2[c] = T(0.5) * ab;
       yb[c] = lam[c];
     }
-    lu_solve_t<D>(s.LU, s.perm, kb2, rb2);
+    lu_solve_t<D>(s.LU, s.rinv, s.perm, kb2, rb2);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll
@@ -208,7 +211,7 @@ struct Ros2 {
       kb1[c] = mac(h, Y2b[c], kb1[c]);
       yb[c] = yb[c] + Y2b[c];
     }
-    lu_solve_t<D>(s.LU, s.perm, kb1, rb1);
+    lu_solve_t<D>(s.LU, s.rinv, s.perm, kb1, rb1);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll

@@ -506,7 +506,10 @@ void erk_step_adjoint(const Tableau &tb, int kind, int d, const T *y, const T *p
 /* ------------------------------------------------------------------ */
 
 /* LU with partial pivoting of the d x d matrix A (row-major, in place);
- * perm[i] = original row now in position i.  Ties keep the lowest row. */
+ * perm[i] = original row now in position i.  Ties keep the lowest row.
+ * Plain mode divides by the pivot; fused mode (the kernels' schedule) forms
+ * the pivot's reciprocal 1 / u once and multiplies by it, here and in both
+ * solves. */
 template <class T, bool F>
 void lu_factor(int d, T *A, int *perm) {
   for (int i = 0; i < d; ++i) perm[i] = i;
@@ -521,8 +524,9 @@ void lu_factor(int d, T *A, int *perm) {
       for (int j = 0; j < d; ++j) std::swap(A[k * d + j], A[piv * d + j]);
       std::swap(perm[k], perm[piv]);
     }
+    const T r = T(1.0) / A[k * d + k];
     for (int i = k + 1; i < d; ++i) {
-      const T l = A[i * d + k] / A[k * d + k];
+      const T l = F ? A[i * d + k] * r : A[i * d + k] / A[k * d + k];
       A[i * d + k] = l;
       for (int j = k + 1; j < d; ++j) A[i * d + j] = mac<F>(-l, A[k * d + j], A[i * d + j]);
     }
@@ -537,7 +541,7 @@ void lu_solve(int d, const T *LU, const int *perm, const T *b, T *x) {
     for (int j = 0; j < i; ++j) x[i] = mac<F>(-LU[i * d + j], x[j], x[i]);
   for (int i = d - 1; i >= 0; --i) {
     for (int j = i + 1; j < d; ++j) x[i] = mac<F>(-LU[i * d + j], x[j], x[i]);
-    x[i] = x[i] / LU[i * d + i];
+    x[i] = F ? x[i] * (T(1.0) / LU[i * d + i]) : x[i] / LU[i * d + i];
   }
 }
 
@@ -548,7 +552,7 @@ void lu_solve_t(int d, const T *LU, const int *perm, const T *b, T *x) {
   for (int i = 0; i < d; ++i) {
     z[i] = b[i];
     for (int j = 0; j < i; ++j) z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);
-    z[i] = z[i] / LU[i * d + i];
+    z[i] = F ? z[i] * (T(1.0) / LU[i * d + i]) : z[i] / LU[i * d + i];
   }
   for (int i = d - 1; i >= 0; --i)
     for (int j = i + 1; j < d; ++j) z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);

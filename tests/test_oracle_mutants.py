@@ -31,8 +31,8 @@ MUTANTS = {
                                       "if (tb.a[l][i] == 0.0) continue;\n        if (first) { acc = T(tb.a[i][l]) * Wv[l][c];"),
     "tsit5_digit": ("t.a[4][2] = 7.4955393428898365;", "t.a[4][2] = 7.4955393428988365;"),
     "dopri5_weight": ("t.a[6][3] = 125.0 / 192.0;", "t.a[6][3] = 125.0 / 191.0;"),
-    "lu_transposed_solve": ("z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);\n    z[i] = z[i] / LU[i * d + i];",
-                            "z[i] = mac<F>(-LU[i * d + j], z[j], z[i]);\n    z[i] = z[i] / LU[i * d + i];"),
+    "lu_transposed_solve": ("z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);\n    z[i] = F ?",
+                            "z[i] = mac<F>(-LU[i * d + j], z[j], z[i]);\n    z[i] = F ?"),
     "ros2_no_jac_contraction": ("rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);", ""),
     "ros2_wrong_weight": ("const T acc = mac<F>(T(0.5), s.k2[c], T(1.5) * s.k1[c]);",
                           "const T acc = mac<F>(T(0.5), s.k2[c], T(1.0) * s.k1[c]);"),
