@@ -15,7 +15,9 @@
 //
 // A method M provides, per lane (component) with a Nbr context for the
 // neighbours: fwd(x, F, h), attempt(x, F, h, k0, xnew, err) and
-// adj(x, F, h, lam, gF) (gF accumulates this lane's share of dL/dF).
+// adj(x, F, h, lam, gF) (gF accumulates this lane's share of dL/dF).  At
+// d = 64 (FULL) the neighbours are DPP wavefront rotations; otherwise
+// cross-lane reads (ds_bpermute).
 #pragma once
 
 #include <math.h>
@@ -52,9 +54,26 @@ template <class T> __device__ __forceinline__ T wave_sum(T v) {
 
 __device__ __forceinline__ bool wave_all(bool b) { return __ballot(!b) == 0ull; }
 
-// Source lanes of the cyclic neighbours of component c in dimension d.
-struct Nbr {
-  int p1, p2, m1, m2;  // c+1, c+2, c-1, c-2 (mod d)
+template <class T> __device__ __forceinline__ T take(T v, int src) { return __shfl(v, src, 64); }
+
+// Whole-wavefront rotations by one lane (DPP): lane c receives lane c - 1
+// (ROR) or c + 1 (ROL), cyclically over the 64 lanes.
+constexpr int DPP_WAVE_ROL1 = 0x134, DPP_WAVE_ROR1 = 0x13C;
+template <int CTRL> __device__ __forceinline__ double rot(double v) {
+  const long long b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)b, CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(b >> 32), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double((long long)(((unsigned long long)(unsigned)hi << 32) | (unsigned)lo));
+}
+template <int CTRL> __device__ __forceinline__ float rot(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// The cyclic neighbours of component c in dimension d.  FULL (d = 64): the
+// neighbours are wavefront rotations; otherwise cross-lane reads from the
+// lanes of components c+1, c+2, c-1, c-2 (mod d).
+template <bool FULL> struct Nbr {
+  int p1, p2, m1, m2;
   __device__ __forceinline__ void init(int c, int d) {
     const int cc = c < d ? c : 0;
     p1 = (cc + 1) % d;
@@ -62,9 +81,24 @@ struct Nbr {
     m1 = (cc + d - 1) % d;
     m2 = (cc + d - 2) % d;
   }
+  template <class T> __device__ __forceinline__ T up1(T v) const {  // v_{c+1}
+    if constexpr (FULL) return rot<DPP_WAVE_ROL1>(v);
+    else return take(v, p1);
+  }
+  template <class T> __device__ __forceinline__ T dn1(T v) const {  // v_{c-1}
+    if constexpr (FULL) return rot<DPP_WAVE_ROR1>(v);
+    else return take(v, m1);
+  }
+  // v_{c+2} and v_{c-2}, given v and its first neighbour on that side
+  template <class T> __device__ __forceinline__ T up2(T v, T vp1) const {
+    if constexpr (FULL) return rot<DPP_WAVE_ROL1>(vp1);
+    else return take(v, p2);
+  }
+  template <class T> __device__ __forceinline__ T dn2(T v, T vm1) const {
+    if constexpr (FULL) return rot<DPP_WAVE_ROR1>(vm1);
+    else return take(v, m2);
+  }
 };
-
-template <class T> __device__ __forceinline__ T take(T v, int src) { return __shfl(v, src, 64); }
 
 // ---------------------------------------------------------------------------
 // Lorenz-96: x_c' = (x_{c+1} - x_{c-2}) x_{c-1} - x_c + F.  The operation
@@ -74,16 +108,15 @@ template <class T> __device__ __forceinline__ T take(T v, int src) { return __sh
 // (rows c-1, c, c+1, c+2 of column c, in that order); df_c/dF = 1.
 // ---------------------------------------------------------------------------
 struct L96 {
-  template <class T>
-  __device__ static __forceinline__ T f(T x, T F, const Nbr &nb) {
-    const T xp1 = take(x, nb.p1), xm1 = take(x, nb.m1), xm2 = take(x, nb.m2);
+  template <class T, class NB>
+  __device__ static __forceinline__ T f(T x, T F, const NB &nb) {
+    const T xp1 = nb.up1(x), xm1 = nb.dn1(x), xm2 = nb.dn2(x, xm1);
     return mac(xp1 - xm2, xm1, -x) + F;
   }
-  template <class T>
-  __device__ static __forceinline__ T vjp_y(T x, T v, const Nbr &nb) {
-    const T xp1 = take(x, nb.p1), xp2 = take(x, nb.p2), xm1 = take(x, nb.m1),
-            xm2 = take(x, nb.m2);
-    const T vm1 = take(v, nb.m1), vp1 = take(v, nb.p1), vp2 = take(v, nb.p2);
+  template <class T, class NB>
+  __device__ static __forceinline__ T vjp_y(T x, T v, const NB &nb) {
+    const T xp1 = nb.up1(x), xp2 = nb.up2(x, xp1), xm1 = nb.dn1(x), xm2 = nb.dn2(x, xm1);
+    const T vm1 = nb.dn1(v), vp1 = nb.up1(v), vp2 = nb.up2(v, vp1);
     T s = xm2 * vm1;
     s = s - v;
     s = mac(xp2 - xm1, vp1, s);
@@ -113,7 +146,8 @@ __device__ __forceinline__ T wstage(T y, const T (&K)[7], T h) {
 
 template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
 struct WStages {
-  __device__ static __forceinline__ void run(T y, T F, T h, const Nbr &nb, T (&Y)[7], T (&K)[7]) {
+  template <class NB>
+  __device__ static __forceinline__ void run(T y, T F, T h, const NB &nb, T (&Y)[7], T (&K)[7]) {
     Y[I] = wstage<Tab, I>(y, K, h);
     if (I < LAST || LASTK) K[I] = Rhs::f(Y[I], F, nb);
     WStages<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, F, h, nb, Y, K);
@@ -121,7 +155,8 @@ struct WStages {
 };
 template <class Tab, class Rhs, int LAST, bool LASTK, class T>
 struct WStages<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
-  __device__ static __forceinline__ void run(T, T, T, const Nbr &, T (&)[7], T (&)[7]) {}
+  template <class NB>
+  __device__ static __forceinline__ void run(T, T, T, const NB &, T (&)[7], T (&)[7]) {}
 };
 
 template <class Tab, class R>
@@ -130,8 +165,8 @@ struct WErk {
   static constexpr int order = Tab::order, err_order = Tab::err_order;
 
   // trial step from x with K[0] = f(x) given; returns the 5th-order value
-  template <class T>
-  __device__ static __forceinline__ T attempt(T x, T F, T h, const Nbr &nb, T (&K)[7], T &err) {
+  template <class T, class NB>
+  __device__ static __forceinline__ T attempt(T x, T F, T h, const NB &nb, T (&K)[7], T &err) {
     T Y[7];
     WStages<Tab, Rhs, 1, 6, true, T>::run(x, F, h, nb, Y, K);
     T acc = T(0);
@@ -147,7 +182,8 @@ struct WErk {
     return Y[6];
   }
 
-  template <class T> __device__ static __forceinline__ T fwd(T x, T F, T h, const Nbr &nb) {
+  template <class T, class NB>
+  __device__ static __forceinline__ T fwd(T x, T F, T h, const NB &nb) {
     T Y[7], K[7];
     K[0] = Rhs::f(x, F, nb);
     WStages<Tab, Rhs, 1, 6, false, T>::run(x, F, h, nb, Y, K);
@@ -156,8 +192,8 @@ struct WErk {
 
   // Reverse of fwd at x = x_k: lam (dL/dx_{k+1} -> dL/dx_k); gF += this
   // component's share of dL/dF (the sum of its stage cotangents).
-  template <class T>
-  __device__ static __forceinline__ void adj(T x, T F, T h, const Nbr &nb, T &lam, T &gF) {
+  template <class T, class NB>
+  __device__ static __forceinline__ void adj(T x, T F, T h, const NB &nb, T &lam, T &gF) {
     T Y[7], Wv[7];
     {
       T K[7];
@@ -230,7 +266,7 @@ template <class T> struct WLog {
 // the wavefront holds step b of the current chunk of the step log; a full
 // chunk is written by lanes 0..B-1 as one 64-byte store.
 // ---------------------------------------------------------------------------
-template <class T, class M, bool LOG>
+template <class T, class M, bool LOG, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
   constexpr int B = WLog<T>::B;
@@ -242,7 +278,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   const ProbArgs &pr = a.pr;
   const int d = pr.dim;
   const bool on = c < d;
-  Nbr nb;
+  Nbr<FULL> nb;
   nb.init(c, d);
   const int S = pr.S;
   const bool has_saves = pr.n_save > 0;
@@ -382,7 +418,7 @@ template <class T> struct WSteps {
 // ---------------------------------------------------------------------------
 // Replay forward
 // ---------------------------------------------------------------------------
-template <class T, class M>
+template <class T, class M, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
   const int64_t n = a.n;
   const WaveId w = wave_id(n);
@@ -391,7 +427,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
   const int c = w.c;
   const int d = a.pr.dim;
   const bool on = c < d;
-  Nbr nb;
+  Nbr<FULL> nb;
   nb.init(c, d);
   const int S = a.pr.S;
   T *ysave = (T *)a.y_save;
@@ -425,7 +461,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
 // 64-component row ws[(m * ws_lanes + jl) * 64 + c] (one contiguous 512-byte
 // store per wavefront in FP64).
 // ---------------------------------------------------------------------------
-template <class T, class M, int CK>
+template <class T, class M, int CK, bool FULL>
 __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   const int64_t n = a.n;
   const WaveId w = wave_id(a.nslots);
@@ -435,7 +471,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   const int c = w.c;
   const int d = a.pr.dim;
   const bool on = c < d;
-  Nbr nb;
+  Nbr<FULL> nb;
   nb.init(c, d);
   const int64_t C = a.ws_lanes;
   const int S = a.pr.S;
