@@ -487,3 +487,64 @@ def test_full_size_lorenz_dopri5_sampled(da, orc):
     mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
     no = mo["n_steps"]
     assert np.all(np.abs(sub["n_steps"] - no) <= np.maximum(2, 0.01 * no))
+
+
+def test_lorenz96_chunked_workspace_and_fp32(da, orc):
+    """The wavefront gradient kernel with a workspace for a few trajectories at
+    a time (several chunks) equals the one-chunk result bitwise; FP32 Lorenz-96
+    against the FP32 oracle on a shared mesh."""
+    w = W.WORKLOADS[5]
+    prob = w.problem()
+    n = 600
+    inp = W.make_inputs(5, n)
+    _print("case: Lorenz-96 chunked workspace, n=600")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    full = [t.clone() for t in da.replay_grad(prob, u0, p, sm)]
+    N = da.mesh_max_steps(sm)
+    part = da.replay_grad(prob, u0, p, sm, ws_bytes=da.replay_grad_workspace(prob, 256, N))
+    torch.cuda.synchronize()
+    for a, b in zip(full, part):
+        assert torch.equal(a, b)
+    # FP32
+    _print("case: Lorenz-96 FP32, n=150")
+    u32, p32 = inp["u0"][:150].astype(np.float32), inp["p"][:150].astype(np.float32)
+    m = orc.record(prob, u32, p32, fused=True)
+    assert np.all(m["status"] == 0)
+    lo, go, po = orc.replay_grad(prob, u32, p32, m, fused=True)
+    l, g, q = da.replay_grad(prob, to_dev(u32, torch), to_dev(p32, torch),
+                             mesh_to_dev(m, prob.max_steps, torch))
+    torch.cuda.synchronize()
+    err = grad_rel_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
+    _print(f"  FP32 max rel err {err.max():.3e}")
+    assert err.max() <= 1e-4
+
+
+def test_maximum_save_times(da, orc):
+    """DA_MAX_SAVES save times, MSE loss: shared-mesh gradient and the saved
+    states of record and replay."""
+    w = W.WORKLOADS[1]
+    S = da.MAX_SAVES
+    times = tuple(float(t) for t in np.linspace(1.0 / S, 1.0, S))
+    prob = w.problem(save_times=times)
+    n = 130
+    inp = W.make_inputs(1, n)
+    _print(f"case: {S} save times, n={n}")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    assert np.all(m["status"] == 0)
+    aux = np.random.default_rng(5).standard_normal((n, S, 3))
+    lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, W.MSE_SAVE, aux=aux,
+                                 scale=0.01, fused=True)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    l, g, q = da.replay_grad(prob, u0, p, mesh_to_dev(m, prob.max_steps, torch), W.MSE_SAVE,
+                             aux=aux_to_dev(aux, torch), scale=0.01)
+    mesh, ys = da.record(prob, u0, p)
+    yr = da.replay_fwd(prob, u0, p, mesh)
+    torch.cuda.synchronize()
+    err = grad_rel_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
+    assert err.max() <= 1e-12
+    assert torch.equal(ys, yr)
+    si = mesh.save_idx.cpu().numpy().T
+    assert np.all(np.diff(si, axis=1) > 0)
+    assert np.array_equal(si[:, -1], mesh.n_steps.cpu().numpy())

@@ -143,3 +143,27 @@ def test_full_size_sensitivities_sampled(da, orc):
     eg = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
     _print(f"  sampled {len(tr)}: max rel {eg.max():.3e}")
     assert eg.max() <= 1e-12
+
+
+def test_sensitivities_fp32(da, orc):
+    """FP32 tangents against the FP64 oracle on the FP32 mesh (the tangent
+    arithmetic in single precision)."""
+    w = W.WORKLOADS[3]
+    prob = w.problem(t1=1.0, save_times=(0.5, 1.0))
+    n = 200
+    inp = W.make_inputs(3, n)
+    _print("case: FP32 sensitivities, n=200")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    assert np.all(m["status"] == 0)
+    m64 = dict(m)
+    m64["h"] = m["h"].astype(np.float64)
+    so, lo, go, po = orc.replay_sens(prob, inp["u0"].astype(np.float64),
+                                     inp["p"].astype(np.float64), m64, fused=True)
+    sg, lg, gu0, gp = da.replay_sens(prob, to_dev(inp["u0"], torch), to_dev(inp["p"], torch),
+                                     mesh_to_dev(m, prob.max_steps, torch))
+    torch.cuda.synchronize()
+    es = _sens_err(sg.cpu().numpy().transpose(3, 0, 1, 2).astype(np.float64), so)
+    eg = grad_rel_err(gu0.cpu().numpy().T.astype(np.float64), gp.cpu().numpy().T.astype(np.float64),
+                      go, po)
+    _print(f"  FP32 sens max rel {es.max():.3e}, grad {eg.max():.3e}")
+    assert es.max() <= 1e-4 and eg.max() <= 1e-4
