@@ -73,7 +73,8 @@ def flop_per_step(method: str, rhs: str, dim: int) -> int:
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 # Sources of the gradient kernel of each method family.
 KERNEL_SOURCES = {
-    "erk": ["lane_kernels.hpp", "erk.hip", "dadj_device.hpp", "dadj_internal.hpp"],
+    "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "dadj_device.hpp",
+            "dadj_internal.hpp"],
     "ros2": ["lane_kernels.hpp", "ros2.hip", "dadj_device.hpp", "dadj_internal.hpp"],
     "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
 }
