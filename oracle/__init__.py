@@ -5,7 +5,11 @@ TEST INFRASTRUCTURE.  Only the test suite, ``__graft_entry__.smoke()`` and the
 never calls it, and it never calls the HIP library.
 
 Arrays here are numpy, lane-major: u0 [n, d], p [n, P], h [n, max_steps],
-save_idx [n, S], y_save [n, S, d] with S = max(1, len(save_times)).  The
+save_idx [n, S], save_theta [n, S], y_save [n, S, d] with
+S = max(1, len(save_times)).  With ``prob.dense`` the saves are read from the
+cubic Hermite interpolant of the step that contains them, and ``save_theta``
+(the step fraction of each save, part of the mesh) is required by the
+replays.  The
 dtype of ``u0`` (float64 or float32) selects the precision.  ``fused=True``
 evaluates every multiply-add as one correctly rounded fma; ``fused=False``
 rounds each multiply and add separately.
@@ -47,6 +51,7 @@ class _Problem(ctypes.Structure):
         ("max_steps", ctypes.c_int32), ("max_attempts", ctypes.c_int32),
         ("n_save", ctypes.c_int32), ("save_times", ctypes.POINTER(ctypes.c_double)),
         ("safety", ctypes.c_double), ("fac_min", ctypes.c_double), ("fac_max", ctypes.c_double),
+        ("dense", ctypes.c_int32),
     ]
 
 
@@ -78,7 +83,7 @@ def _cprob(prob):
     P = _Problem(prob.rhs, prob.dim, prob.n_params, prob.method, prob.t0, prob.t1, prob.rtol,
                  prob.atol, prob.dt0, prob.max_steps, prob.max_attempts, len(prob.save_times),
                  st.ctypes.data_as(ctypes.POINTER(ctypes.c_double)) if len(st) else None,
-                 prob.safety, prob.fac_min, prob.fac_max)
+                 prob.safety, prob.fac_min, prob.fac_max, int(getattr(prob, "dense", 0)))
     return P, st  # keep st alive
 
 
@@ -127,15 +132,22 @@ def record(prob, u0, p, fused: bool = False, nthreads: int = 0, with_h: bool = T
     ns = np.zeros(n, dtype=np.int32)
     sidx = np.zeros((n, S), dtype=np.int32)
     status = np.zeros(n, dtype=np.int32)
+    theta = np.zeros((n, S), dtype=dt)
     ysave = np.zeros((n, S, prob.dim), dtype=dt)
     natt = np.zeros(n, dtype=np.int32)
     P, keep = _cprob(prob)
     fn = getattr(_load(), "orc_record_" + _sfx(dt))
     _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
-              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(status), _ptr(ysave), _ptr(natt),
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(theta), _ptr(status), _ptr(ysave), _ptr(natt),
               ctypes.c_int32(nthreads)), "record")
-    return {"h": h, "n_steps": ns, "save_idx": sidx, "status": status, "y_save": ysave,
-            "n_attempts": natt}
+    return {"h": h, "n_steps": ns, "save_idx": sidx, "save_theta": theta, "status": status,
+            "y_save": ysave, "n_attempts": natt}
+
+
+def _theta(prob, mesh, dt):
+    if not getattr(prob, "dense", 0):
+        return None
+    return np.ascontiguousarray(mesh["save_theta"], dtype=dt)
 
 
 def replay(prob, u0, p, mesh, fused: bool = False, nthreads: int = 0):
@@ -148,13 +160,14 @@ def replay(prob, u0, p, mesh, fused: bool = False, nthreads: int = 0):
     h = np.ascontiguousarray(mesh["h"], dtype=dt)
     ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
     sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    th = _theta(prob, mesh, dt)
     ysave = np.zeros((n, S, prob.dim), dtype=dt)
     yfin = np.zeros((n, prob.dim), dtype=dt)
     P, keep = _cprob(prob)
     fn = getattr(_load(), "orc_replay_" + _sfx(dt))
     _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
-              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(ysave), _ptr(yfin), ctypes.c_int32(nthreads)),
-           "replay")
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(th), _ptr(ysave), _ptr(yfin),
+              ctypes.c_int32(nthreads)), "replay")
     return ysave, yfin
 
 
@@ -171,6 +184,7 @@ def replay_grad(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray]
     ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
     sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
     status = np.ascontiguousarray(mesh["status"], dtype=np.int32)
+    th = _theta(prob, mesh, dt)
     ax = None if aux is None else np.ascontiguousarray(aux, dtype=dt)
     loss = np.zeros(n, dtype=dt)
     gu0 = np.zeros((n, prob.dim), dtype=dt)
@@ -178,9 +192,9 @@ def replay_grad(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray]
     P, keep = _cprob(prob)
     fn = getattr(_load(), "orc_replay_grad_" + _sfx(dt))
     _check(fn(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p), ctypes.c_int32(int(fused)),
-              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(status), ctypes.c_int32(loss_kind), _ptr(ax),
-              ctypes.c_double(scale), _ptr(loss), _ptr(gu0), _ptr(gp), ctypes.c_int32(nthreads)),
-           "replay_grad")
+              _ptr(h), _ptr(ns), _ptr(sidx), _ptr(th), _ptr(status), ctypes.c_int32(loss_kind),
+              _ptr(ax), ctypes.c_double(scale), _ptr(loss), _ptr(gu0), _ptr(gp),
+              ctypes.c_int32(nthreads)), "replay_grad")
     return loss, gu0, gp
 
 
@@ -198,14 +212,16 @@ def replay_jvp(prob, u0, p, du0, dp, mesh, loss_kind: int = 0,
     h = np.ascontiguousarray(mesh["h"], dtype=np.float64)
     ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
     sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
+    th = _theta(prob, mesh, np.float64)
     ax = None if aux is None else np.ascontiguousarray(aux, dtype=np.float64)
     loss = np.zeros(n); dloss = np.zeros(n)
     ys = np.zeros((n, S, prob.dim)); dys = np.zeros((n, S, prob.dim))
     P, keep = _cprob(prob)
     _check(_load().orc_replay_jvp_f64(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p),
                                       _ptr(du0), _ptr(dp), _ptr(h), _ptr(ns), _ptr(sidx),
-                                      ctypes.c_int32(loss_kind), _ptr(ax), ctypes.c_double(scale),
-                                      _ptr(loss), _ptr(dloss), _ptr(ys), _ptr(dys)), "replay_jvp")
+                                      _ptr(th), ctypes.c_int32(loss_kind), _ptr(ax),
+                                      ctypes.c_double(scale), _ptr(loss), _ptr(dloss), _ptr(ys),
+                                      _ptr(dys)), "replay_jvp")
     return loss, dloss, ys, dys
 
 
@@ -225,6 +241,7 @@ def replay_sens(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray]
     ns = np.ascontiguousarray(mesh["n_steps"], dtype=np.int32)
     sidx = np.ascontiguousarray(mesh["save_idx"], dtype=np.int32)
     status = np.ascontiguousarray(mesh["status"], dtype=np.int32)
+    th = _theta(prob, mesh, np.float64)
     ax = None if aux is None else np.ascontiguousarray(aux, dtype=np.float64)
     sens = np.zeros((n, S, prob.dim, Q))
     loss = np.zeros(n)
@@ -233,7 +250,7 @@ def replay_sens(prob, u0, p, mesh, loss_kind: int = 0, aux: Optional[np.ndarray]
     P, keep = _cprob(prob)
     _check(_load().orc_replay_sens_f64(ctypes.byref(P), ctypes.c_int64(n), _ptr(u0), _ptr(p),
                                        ctypes.c_int32(int(fused)), _ptr(h), _ptr(ns), _ptr(sidx),
-                                       _ptr(status), ctypes.c_int32(loss_kind), _ptr(ax),
+                                       _ptr(th), _ptr(status), ctypes.c_int32(loss_kind), _ptr(ax),
                                        ctypes.c_double(scale), _ptr(sens), _ptr(loss), _ptr(gu0),
                                        _ptr(gp)), "replay_sens")
     return sens, loss, gu0, gp

@@ -70,6 +70,8 @@ typedef struct {
   int32_t n_save;
   const double *save_times; /* host, strictly increasing in (t0, t1] */
   double safety, fac_min, fac_max;
+  int32_t dense;            /* 0: steps land on save times; 1: saves read from
+                               the step's interpolant (explicit methods) */
 } orc_problem;
 }
 
@@ -663,6 +665,8 @@ int validate(const orc_problem *P) {
   if (P->method < 0 || P->method > 2) return E_INVAL;
   if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
   if (P->method == M_ROS2 && P->dim > 3) return E_UNSUPPORTED;
+  if (P->dense != 0 && P->dense != 1) return E_INVAL;
+  if (P->dense && P->method == M_ROS2) return E_UNSUPPORTED;
   if (!(P->t1 > P->t0)) return E_INVAL;
   if (!(P->rtol >= 0) || !(P->atol >= 0) || !(P->rtol + P->atol > 0)) return E_INVAL;
   if (P->max_steps < 1) return E_INVAL;
@@ -719,6 +723,61 @@ T initial_step(int kind, int d, const T *y0, const T *f0, const T *p, T atol, T 
 }
 
 /* ------------------------------------------------------------------ */
+/* Dense output: save times read inside a step                         */
+/* ------------------------------------------------------------------ */
+/* "Differentiable astrophysics at scale" (gist.science summary),
+ * Methodology, dense output: the solution is interpolated at observation
+ * times instead of forcing steps to end on them.  The page names no
+ * interpolant; the one used here is the cubic Hermite interpolant of an
+ * accepted step [t_k, t_k + h] through its end states and end slopes
+ * f(y_k), f(y_{k+1}) (for a first-same-as-last pair these are the step's
+ * first and last stage derivatives, so no extra stage is needed):
+ *   y(t_k + th h) = H00 y_k + H01 y_{k+1} + h (H10 f(y_k) + H11 f(y_{k+1}))
+ *   H00 = (1 - th)^2 (1 + 2 th)    H01 = th^2 (3 - 2 th)
+ *   H10 = th (1 - th)^2            H11 = -th^2 (1 - th)
+ * A save time t_s belongs to the accepted step with t_k < t_s <= t_k + h;
+ * its fraction th = (t_s - t_k) / h is taken in double, capped at 1, and is
+ * exactly 1 when t_s is the step's end (then the save is y_{k+1}).  The
+ * fraction belongs to the mesh: it is recorded once and, like the step
+ * sizes, carries no derivative. */
+
+/* Fraction of the step [t, t_end] of size h at which ts lies. */
+inline double step_fraction(double ts, double t, double t_end, double h) {
+  if (ts >= t_end) return 1.0;
+  const double th = (ts - t) / h;
+  return th < 1.0 ? th : 1.0;
+}
+
+/* Hermite basis at th: w = {H00, H01, H10, H11}. */
+template <class S, bool F>
+void hermite_weights(S th, S *w) {
+  const S u = S(1.0) - th;
+  const S u2 = u * u, t2 = th * th;
+  w[0] = u2 * mac<F>(S(2.0), th, S(1.0));
+  w[1] = t2 * mac<F>(S(-2.0), th, S(3.0));
+  w[2] = th * u2;
+  w[3] = -(t2 * u);
+}
+
+/* Interpolated state at fraction th of the step from yk to yk1 of size h:
+ * out = h (H11 f(yk1) + H10 f(yk)) + (H01 yk1 + H00 yk), each sum a chain as
+ * written.  V is the value type (a real or a dual number), S the real type of
+ * th. */
+template <class V, class S, bool F>
+void dense_value(int kind, int d, S th, V h, const V *yk, const V *yk1, const V *p, V *out) {
+  S w[4];
+  hermite_weights<S, F>(th, w);
+  const V wv[4] = {V(w[0]), V(w[1]), V(w[2]), V(w[3])};
+  V f0[MAXD], f1[MAXD];
+  rhs_f<V, F>(kind, d, yk, p, f0);
+  rhs_f<V, F>(kind, d, yk1, p, f1);
+  for (int c = 0; c < d; ++c) {
+    const V sl = mac<F>(wv[3], f1[c], wv[2] * f0[c]);
+    out[c] = mac<F>(h, sl, mac<F>(wv[1], yk1[c], wv[0] * yk[c]));
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Record (adaptive solve logging accepted steps)                      */
 /* ------------------------------------------------------------------ */
 
@@ -727,13 +786,16 @@ struct LaneOut {
   T *h;            /* [max_steps] or null */
   int32_t *nsteps;
   int32_t *sidx;   /* [S] */
+  T *theta;        /* [S] step fraction of each save, or null */
   int32_t *status;
   T *ysave;        /* [S][d] or null */
   int32_t *natt;   /* or null */
 };
 
 /* One adaptive integration.  Steps are clipped to land exactly on every save
- * time and on t1; t accumulates in double.  Controller: accept iff E <= 1;
+ * time and on t1 (with dense output only on t1, and each save is read from
+ * the interpolant of the accepted step that contains it); t accumulates in
+ * double.  Controller: accept iff E <= 1;
  * h_next = h_used * clamp(safety E^(-1/(q+1)), fac_min, fac_max), no growth on
  * the step after a reject, fac_max when E == 0, fac_min on a non-finite E.
  * Stop times are the save times followed by t1 when the last save is earlier
@@ -750,12 +812,14 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
   const T expo = T(-1.0) / T(qerr + 1);
   const T safety = T(o.safety), fmin = T(o.fac_min), fmax = T(o.fac_max);
   const int n_stops = o.S + ((o.saves && o.saves[o.S - 1] < P->t1) ? 1 : 0);
+  const bool dense = P->dense != 0;
 
   T y[MAXD], ynew[MAXD], err[MAXD];
   T Y[7][MAXD], K[7][MAXD];
   for (int c = 0; c < d; ++c) y[c] = u0[c];
   for (int s = 0; s < o.S; ++s) {
     out.sidx[s] = -1;
+    if (out.theta) out.theta[s] = T(NAN);
     if (out.ysave)
       for (int c = 0; c < d; ++c) out.ysave[s * d + c] = T(NAN);
   }
@@ -772,7 +836,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
     int j = 0;  /* next stop */
     bool after_reject = false;
     for (;;) {
-      const double t_stop = (o.saves && j < o.S) ? o.saves[j] : P->t1;
+      const double t_stop = (!dense && o.saves && j < o.S) ? o.saves[j] : P->t1;
       const T rem = T(t_stop - t);
       const bool land = !(h < rem);
       const T hs = land ? rem : h;
@@ -795,20 +859,38 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
       }
       const T E = err_norm<T, F>(d, err, y, ynew, atol, rtol);
       if (E <= T(1.0)) {
+        const double t_new = land ? t_stop : t + double(hs);
         if (out.h) out.h[nacc] = hs;
         ++nacc;
+        if (dense) /* save times inside this step */
+          for (; o.saves && j < o.S && o.saves[j] <= t_new; ++j) {
+            const T th = T(step_fraction(o.saves[j], t, t_new, double(hs)));
+            out.sidx[j] = nacc;
+            if (out.theta) out.theta[j] = th;
+            if (out.ysave) dense_value<T, T, F>(kind, d, th, hs, y, ynew, p, &out.ysave[j * d]);
+          }
         for (int c = 0; c < d; ++c) y[c] = ynew[c];
         if (!ros)
           for (int c = 0; c < d; ++c) K[0][c] = K[6][c];  /* first same as last */
-        t = land ? t_stop : t + double(hs);
+        t = t_new;
         T fac = (E == T(0.0)) ? fmax
                               : std::min(fmax, std::max(fmin, safety * std::pow(E, expo)));
         if (after_reject) fac = std::min(fac, T(1.0));
         h = hs * fac;
         after_reject = false;
+        if (land && dense) {
+          if (!o.saves) { /* the final state is the one save */
+            out.sidx[0] = nacc;
+            if (out.theta) out.theta[0] = T(1.0);
+            if (out.ysave)
+              for (int c = 0; c < d; ++c) out.ysave[c] = y[c];
+          }
+          break;
+        }
         if (land) {
           if (j < o.S) {
             out.sidx[j] = nacc;
+            if (out.theta) out.theta[j] = T(1.0);
             if (out.ysave)
               for (int c = 0; c < d; ++c) out.ysave[j * d + c] = y[c];
           }
@@ -859,21 +941,28 @@ T pairwise64(const T *v, int d) {
   return a[0];
 }
 
-/* Fixed-step replay of a recorded mesh: writes y at every save index. */
+/* Fixed-step replay of a recorded mesh: writes y at every save index (with
+ * dense output, theta != null, the interpolant of step sidx - 1 at the
+ * save's fraction; index 0 is the initial state in both modes). */
 template <class T, bool F>
 void replay_lane(const orc_problem *P, int S, const T *u0, const T *p, const T *h, int N,
-                 const int32_t *sidx, T *ysave, T *yfinal) {
+                 const int32_t *sidx, const T *theta, T *ysave, T *yfinal) {
   const int d = P->dim;
-  T y[MAXD];
+  T y[MAXD], yprev[MAXD];
   for (int c = 0; c < d; ++c) y[c] = u0[c];
   for (int s = 0; s < S; ++s)
     if (sidx[s] == 0)
       for (int c = 0; c < d; ++c) ysave[s * d + c] = y[c];
   for (int k = 0; k < N; ++k) {
+    for (int c = 0; c < d; ++c) yprev[c] = y[c];
     one_step<T, F>(P, y, p, h[k]);
     for (int s = 0; s < S; ++s)
-      if (sidx[s] == k + 1)
-        for (int c = 0; c < d; ++c) ysave[s * d + c] = y[c];
+      if (sidx[s] == k + 1) {
+        if (theta)
+          dense_value<T, T, F>(P->rhs, d, theta[s], h[k], yprev, y, p, &ysave[s * d]);
+        else
+          for (int c = 0; c < d; ++c) ysave[s * d + c] = y[c];
+      }
   }
   for (int s = 0; s < S; ++s)
     if (sidx[s] < 0 || sidx[s] > N)
@@ -906,17 +995,56 @@ void save_seed(int kind, int d, const T *y, const T *aux, double scale, T *lam) 
   }
 }
 
+/* Reverse of one dense save inside the step from yk to yk1 (size h, fraction
+ * th), given the save's seed sb = dL/dy(t_s) (save_seed from zero):
+ *   lam (dL/dy_{k+1}) += H01 sb + J(yk1)^T v1,   v1 = (h H11) sb
+ *   mu  (dL/dy_k part) += H00 sb + J(yk)^T v0,    v0 = (h H10) sb
+ *   g += J_p(yk1)^T v1, then g += J_p(yk)^T v0
+ * (with the Lorenz-96 split, df_c/dF = 1: gpc[c] += v1[c], then v0[c]). */
+template <class T, bool F>
+void dense_seed(const orc_problem *P, T th, T h, const T *yk, const T *yk1, const T *p,
+                int loss_kind, const T *aux, double scale, T *lam, T *mu, T *g, T *gpc) {
+  const int d = P->dim, kind = P->rhs;
+  T ys[MAXD], sb[MAXD], v0[MAXD], v1[MAXD], w0[MAXD], w1[MAXD], w[4];
+  dense_value<T, T, F>(kind, d, th, h, yk, yk1, p, ys);
+  for (int c = 0; c < d; ++c) sb[c] = T(0.0);
+  save_seed<T, F>(loss_kind, d, ys, aux, scale, sb);
+  hermite_weights<T, F>(th, w);
+  const T c1 = h * w[3], c0 = h * w[2];
+  for (int c = 0; c < d; ++c) {
+    v1[c] = c1 * sb[c];
+    v0[c] = c0 * sb[c];
+  }
+  rhs_vjp_y<T, F>(kind, d, yk1, p, v1, w1);
+  rhs_vjp_y<T, F>(kind, d, yk, p, v0, w0);
+  for (int c = 0; c < d; ++c) {
+    lam[c] = mac<F>(w[1], sb[c], lam[c]) + w1[c];
+    mu[c] = mac<F>(w[0], sb[c], mu[c]) + w0[c];
+  }
+  if (gpc) {
+    for (int c = 0; c < d; ++c) gpc[c] = gpc[c] + v1[c];
+    for (int c = 0; c < d; ++c) gpc[c] = gpc[c] + v0[c];
+  } else {
+    rhs_vjp_p_acc<T, F>(kind, d, yk1, p, v1, g);
+    rhs_vjp_p_acc<T, F>(kind, d, yk, p, v0, g);
+  }
+}
+
 /* Replay + reverse sweep for one lane.  Loss kinds:
  *  SUMSQ_FINAL: L = scale sum_c y_N[c]^2
  *  MSE_SAVE:    L = scale sum_s sum_c (y_{idx_s}[c] - target[s][c])^2
  *  COTANGENT:   L = scale sum_s sum_c cot[s][c] y_{idx_s}[c]
  * The oracle keeps every forward state y_k, then runs the reverse sweep and
- * adds each save's seed once the adjoint has reached that save's index. */
+ * adds each save's seed once the adjoint has reached that save's index; with
+ * dense output (theta != null) y_{idx_s} stands for the interpolated save
+ * and its seed enters through dense_seed at step idx_s - 1. */
 template <class T, bool F>
 void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, const T *h, int N,
-                      const int32_t *sidx, int status, int loss_kind, const T *aux,
-                      double scale, T *loss, T *gu0, T *gp, T *ybuf /*[(N+1)*d]*/) {
+                      const int32_t *sidx, const T *theta, int status, int loss_kind,
+                      const T *aux, double scale, T *loss, T *gu0, T *gp,
+                      T *ybuf /*[(N+1)*d]*/) {
   const int d = P->dim, Pn = P->n_params;
+  const bool dense = theta != nullptr;
   if (status != S_OK) {
     *loss = T(NAN);
     for (int c = 0; c < d; ++c) gu0[c] = T(NAN);
@@ -938,12 +1066,21 @@ void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, cons
     for (int c = 0; c < d; ++c) lam[c] = T(2.0 * scale) * yN[c];
   } else {
     bool first = true;
-    for (int s = 0; s < S; ++s)
-      save_loss<T, F>(loss_kind, d, &ybuf[sidx[s] * d], &aux[s * d], ss, first);
+    for (int s = 0; s < S; ++s) {
+      const int ix = sidx[s];
+      if (dense && ix > 0) {
+        T ys[MAXD];
+        dense_value<T, T, F>(P->rhs, d, theta[s], h[ix - 1], &ybuf[(ix - 1) * d],
+                             &ybuf[ix * d], p, ys);
+        save_loss<T, F>(loss_kind, d, ys, &aux[s * d], ss, first);
+      } else {
+        save_loss<T, F>(loss_kind, d, &ybuf[ix * d], &aux[s * d], ss, first);
+      }
+    }
   }
   *loss = T(scale) * ss;
   int s_hi = S - 1;  /* highest save slot not yet seeded */
-  if (loss_kind != L_SUMSQ_FINAL)
+  if (loss_kind != L_SUMSQ_FINAL && !dense)
     for (; s_hi >= 0 && sidx[s_hi] == N; --s_hi)
       save_seed<T, F>(loss_kind, d, yN, &aux[s_hi * d], scale, lam);
   /* Fused mode follows the kernels' schedule also in its association order:
@@ -954,8 +1091,23 @@ void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, cons
   for (int c = 0; c < d; ++c) gpc[c] = T(0.0);
   T *split = (F && P->rhs == R_LORENZ96 && P->method != M_ROS2) ? gpc : nullptr;
   for (int k = N - 1; k >= 0; --k) {
+    /* dense output: every save inside step k, the last first, seeds lam
+     * (here dL/dy_{k+1}) now and mu, the part of dL/dy_k that bypasses the
+     * step, which joins lam after the step's adjoint */
+    T mu[MAXD];
+    bool has_mu = false;
+    if (dense && loss_kind != L_SUMSQ_FINAL)
+      for (; s_hi >= 0 && sidx[s_hi] == k + 1; --s_hi) {
+        if (!has_mu)
+          for (int c = 0; c < d; ++c) mu[c] = T(0.0);
+        has_mu = true;
+        dense_seed<T, F>(P, theta[s_hi], h[k], &ybuf[k * d], &ybuf[(k + 1) * d], p, loss_kind,
+                         &aux[s_hi * d], scale, lam, mu, g, split);
+      }
     one_step_adjoint<T, F>(P, &ybuf[k * d], p, h[k], lam, g, split);
-    if (loss_kind != L_SUMSQ_FINAL)
+    if (has_mu)
+      for (int c = 0; c < d; ++c) lam[c] = lam[c] + mu[c];
+    if (loss_kind != L_SUMSQ_FINAL && (!dense || k == 0))
       for (; s_hi >= 0 && sidx[s_hi] == k; --s_hi)
         save_seed<T, F>(loss_kind, d, &ybuf[k * d], &aux[s_hi * d], scale, lam);
   }
@@ -1004,8 +1156,8 @@ int set_threads(int nthreads) {
 
 template <class T>
 int record_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused, T *h,
-               int32_t *nsteps, int32_t *sidx, int32_t *status, T *ysave, int32_t *natt,
-               int nthreads) {
+               int32_t *nsteps, int32_t *sidx, T *theta, int32_t *status, T *ysave,
+               int32_t *natt, int nthreads) {
   const int rc = validate(P);
   if (rc) return rc;
   if (n < 0 || (n > 0 && (!u0 || !p || !nsteps || !sidx || !status))) return E_INVAL;
@@ -1018,6 +1170,7 @@ int record_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fus
     out.h = h ? h + i * P->max_steps : nullptr;
     out.nsteps = nsteps + i;
     out.sidx = sidx + i * o.S;
+    out.theta = theta ? theta + i * o.S : nullptr;
     out.status = status + i;
     out.ysave = ysave ? ysave + i * o.S * d : nullptr;
     out.natt = natt ? natt + i : nullptr;
@@ -1029,10 +1182,12 @@ int record_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fus
 
 template <class T>
 int replay_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused, const T *h,
-               const int32_t *nsteps, const int32_t *sidx, T *ysave, T *yfinal, int nthreads) {
+               const int32_t *nsteps, const int32_t *sidx, const T *theta, T *ysave, T *yfinal,
+               int nthreads) {
   const int rc = validate(P);
   if (rc) return rc;
   if (n < 0 || (n > 0 && (!u0 || !p || !h || !nsteps || !sidx || !ysave))) return E_INVAL;
+  if (P->dense && !theta) return E_INVAL;
   const Opts o = make_opts(P);
   const int d = P->dim, Pn = P->n_params;
   set_threads(nthreads);
@@ -1040,23 +1195,25 @@ int replay_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fus
   for (int64_t i = 0; i < n; ++i) {
     const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
     T *yf = yfinal ? yfinal + i * d : nullptr;
+    const T *th = P->dense ? theta + i * o.S : nullptr;
     if (fused)
       replay_lane<T, true>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                           sidx + i * o.S, ysave + i * o.S * d, yf);
+                           sidx + i * o.S, th, ysave + i * o.S * d, yf);
     else
       replay_lane<T, false>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                            sidx + i * o.S, ysave + i * o.S * d, yf);
+                            sidx + i * o.S, th, ysave + i * o.S * d, yf);
   }
   return E_OK;
 }
 
 template <class T>
 int replay_grad_all(const orc_problem *P, int64_t n, const T *u0, const T *p, int fused,
-                    const T *h, const int32_t *nsteps, const int32_t *sidx,
+                    const T *h, const int32_t *nsteps, const int32_t *sidx, const T *theta,
                     const int32_t *status, int loss_kind, const T *aux, double scale, T *loss,
                     T *gu0, T *gp, int nthreads) {
   const int rc = validate(P);
   if (rc) return rc;
+  if (P->dense && !theta) return E_INVAL;
   if (loss_kind < 0 || loss_kind > 2) return E_INVAL;
   if (loss_kind != L_SUMSQ_FINAL && !aux) return E_INVAL;
   if (n < 0 || (n > 0 && (!u0 || !p || !h || !nsteps || !sidx || !status || !loss || !gu0 || !gp)))
@@ -1071,14 +1228,15 @@ int replay_grad_all(const orc_problem *P, int64_t n, const T *u0, const T *p, in
     for (int64_t i = 0; i < n; ++i) {
       const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
       const T *ax = aux ? aux + i * o.S * d : nullptr;
+      const T *th = P->dense ? theta + i * o.S : nullptr;
       if (fused)
         replay_grad_lane<T, true>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                                  sidx + i * o.S, status[i], loss_kind, ax, scale, loss + i,
+                                  sidx + i * o.S, th, status[i], loss_kind, ax, scale, loss + i,
                                   gu0 + i * d, gp + i * Pn, ybuf);
       else
         replay_grad_lane<T, false>(P, o.S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                                   sidx + i * o.S, status[i], loss_kind, ax, scale, loss + i,
-                                   gu0 + i * d, gp + i * Pn, ybuf);
+                                   sidx + i * o.S, th, status[i], loss_kind, ax, scale,
+                                   loss + i, gu0 + i * d, gp + i * Pn, ybuf);
     }
     delete[] ybuf;
   }
@@ -1097,8 +1255,9 @@ int replay_grad_all(const orc_problem *P, int64_t n, const T *u0, const T *p, in
  * A failed lane gets NaN. */
 template <class D, bool F>
 void sens_lane(const orc_problem *P, int S, const double *u0, const double *p, const double *h,
-               int N, const int32_t *si, int status, int loss_kind, const double *aux,
-               double scale, double *sens, double *loss, double *gu0, double *gp) {
+               int N, const int32_t *si, const double *theta, int status, int loss_kind,
+               const double *aux, double scale, double *sens, double *loss, double *gu0,
+               double *gp) {
   const int d = P->dim, Pn = P->n_params, Q = d + Pn;
   if (status != S_OK) {
     for (int k = 0; k < S * d * Q; ++k) sens[k] = NAN;
@@ -1117,10 +1276,16 @@ void sens_lane(const orc_problem *P, int S, const double *u0, const double *p, c
       if (si[s] == 0)
         for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
     for (int k = 0; k < N; ++k) {
+      D yprev[MAXD];
+      for (int c = 0; c < d; ++c) yprev[c] = yv[c];
       one_step<D, F>(P, yv, pv, D(h[k]));
       for (int s = 0; s < S; ++s)
-        if (si[s] == k + 1)
-          for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+        if (si[s] == k + 1) {
+          if (theta)
+            dense_value<D, double, F>(P->rhs, d, theta[s], D(h[k]), yprev, yv, pv, &ysl[s * d]);
+          else
+            for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+        }
     }
     for (int s = 0; s < S; ++s)
       for (int c = 0; c < d; ++c) sens[(s * d + c) * Q + q] = ysl[s * d + c].d;
@@ -1192,52 +1357,58 @@ double orc_ros2_gamma(void) { return ROS2_GAMMA; }
 
 int orc_max_threads(int nthreads) { return set_threads(nthreads); }
 
+/* theta ([n][S] step fraction of each save) is written by the record when
+ * not null, and read by the replays when the problem asks for dense output. */
 int orc_record_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
-                   int32_t fused, double *h, int32_t *nsteps, int32_t *sidx, int32_t *status,
-                   double *ysave, int32_t *natt, int32_t nthreads) {
-  return record_all<double>(P, n, u0, p, fused, h, nsteps, sidx, status, ysave, natt, nthreads);
+                   int32_t fused, double *h, int32_t *nsteps, int32_t *sidx, double *theta,
+                   int32_t *status, double *ysave, int32_t *natt, int32_t nthreads) {
+  return record_all<double>(P, n, u0, p, fused, h, nsteps, sidx, theta, status, ysave, natt,
+                            nthreads);
 }
 int orc_record_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
-                   int32_t fused, float *h, int32_t *nsteps, int32_t *sidx, int32_t *status,
-                   float *ysave, int32_t *natt, int32_t nthreads) {
-  return record_all<float>(P, n, u0, p, fused, h, nsteps, sidx, status, ysave, natt, nthreads);
+                   int32_t fused, float *h, int32_t *nsteps, int32_t *sidx, float *theta,
+                   int32_t *status, float *ysave, int32_t *natt, int32_t nthreads) {
+  return record_all<float>(P, n, u0, p, fused, h, nsteps, sidx, theta, status, ysave, natt,
+                           nthreads);
 }
 
 int orc_replay_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
                    int32_t fused, const double *h, const int32_t *nsteps, const int32_t *sidx,
-                   double *ysave, double *yfinal, int32_t nthreads) {
-  return replay_all<double>(P, n, u0, p, fused, h, nsteps, sidx, ysave, yfinal, nthreads);
+                   const double *theta, double *ysave, double *yfinal, int32_t nthreads) {
+  return replay_all<double>(P, n, u0, p, fused, h, nsteps, sidx, theta, ysave, yfinal,
+                            nthreads);
 }
 int orc_replay_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
                    int32_t fused, const float *h, const int32_t *nsteps, const int32_t *sidx,
-                   float *ysave, float *yfinal, int32_t nthreads) {
-  return replay_all<float>(P, n, u0, p, fused, h, nsteps, sidx, ysave, yfinal, nthreads);
+                   const float *theta, float *ysave, float *yfinal, int32_t nthreads) {
+  return replay_all<float>(P, n, u0, p, fused, h, nsteps, sidx, theta, ysave, yfinal, nthreads);
 }
 
 int orc_replay_grad_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
                         int32_t fused, const double *h, const int32_t *nsteps,
-                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
-                        const double *aux, double scale, double *loss, double *gu0,
-                        double *gp, int32_t nthreads) {
-  return replay_grad_all<double>(P, n, u0, p, fused, h, nsteps, sidx, status, loss_kind, aux,
-                                 scale, loss, gu0, gp, nthreads);
+                        const int32_t *sidx, const double *theta, const int32_t *status,
+                        int32_t loss_kind, const double *aux, double scale, double *loss,
+                        double *gu0, double *gp, int32_t nthreads) {
+  return replay_grad_all<double>(P, n, u0, p, fused, h, nsteps, sidx, theta, status, loss_kind,
+                                 aux, scale, loss, gu0, gp, nthreads);
 }
 int orc_replay_grad_f32(const orc_problem *P, int64_t n, const float *u0, const float *p,
                         int32_t fused, const float *h, const int32_t *nsteps,
-                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
-                        const float *aux, double scale, float *loss, float *gu0, float *gp,
-                        int32_t nthreads) {
-  return replay_grad_all<float>(P, n, u0, p, fused, h, nsteps, sidx, status, loss_kind, aux,
-                                scale, loss, gu0, gp, nthreads);
+                        const int32_t *sidx, const float *theta, const int32_t *status,
+                        int32_t loss_kind, const float *aux, double scale, float *loss,
+                        float *gu0, float *gp, int32_t nthreads) {
+  return replay_grad_all<float>(P, n, u0, p, fused, h, nsteps, sidx, theta, status, loss_kind,
+                                aux, scale, loss, gu0, gp, nthreads);
 }
 
 int orc_replay_sens_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
                         int32_t fused, const double *h, const int32_t *nsteps,
-                        const int32_t *sidx, const int32_t *status, int32_t loss_kind,
-                        const double *aux, double scale, double *sens, double *loss,
-                        double *gu0, double *gp) {
+                        const int32_t *sidx, const double *theta, const int32_t *status,
+                        int32_t loss_kind, const double *aux, double scale, double *sens,
+                        double *loss, double *gu0, double *gp) {
   const int rc = validate(P);
   if (rc) return rc;
+  if (P->dense && !theta) return E_INVAL;
   if (loss_kind < 0 || loss_kind > 2 || (loss_kind != L_SUMSQ_FINAL && !aux)) return E_INVAL;
   const Opts o = make_opts(P);
   const int d = P->dim, Pn = P->n_params, S = o.S, Q = d + Pn;
@@ -1245,13 +1416,14 @@ int orc_replay_sens_f64(const orc_problem *P, int64_t n, const double *u0, const
   for (int64_t i = 0; i < n; ++i) {
     const int N = std::min(std::max(nsteps[i], 0), P->max_steps);
     const double *ax = aux ? aux + i * S * d : nullptr;
+    const double *th = P->dense ? theta + i * S : nullptr;
     if (fused)
       sens_lane<DualF, true>(P, S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                             sidx + i * S, status[i], loss_kind, ax, scale,
+                             sidx + i * S, th, status[i], loss_kind, ax, scale,
                              sens + i * S * d * Q, loss + i, gu0 + i * d, gp + i * Pn);
     else
       sens_lane<Dual, false>(P, S, u0 + i * d, p + i * Pn, h + i * P->max_steps, N,
-                             sidx + i * S, status[i], loss_kind, ax, scale,
+                             sidx + i * S, th, status[i], loss_kind, ax, scale,
                              sens + i * S * d * Q, loss + i, gu0 + i * d, gp + i * Pn);
   }
   return E_OK;
@@ -1262,11 +1434,12 @@ int orc_replay_sens_f64(const orc_problem *P, int64_t n, const double *u0, const
  * derivative per lane, and the saved states with their tangents. */
 int orc_replay_jvp_f64(const orc_problem *P, int64_t n, const double *u0, const double *p,
                        const double *du0, const double *dp, const double *h,
-                       const int32_t *nsteps, const int32_t *sidx, int32_t loss_kind,
-                       const double *aux, double scale, double *loss, double *dloss,
-                       double *ysave, double *dysave) {
+                       const int32_t *nsteps, const int32_t *sidx, const double *theta,
+                       int32_t loss_kind, const double *aux, double scale, double *loss,
+                       double *dloss, double *ysave, double *dysave) {
   const int rc = validate(P);
   if (rc) return rc;
+  if (P->dense && !theta) return E_INVAL;
   if (loss_kind < 0 || loss_kind > 2 || (loss_kind != L_SUMSQ_FINAL && !aux)) return E_INVAL;
   const Opts o = make_opts(P);
   const int d = P->dim, Pn = P->n_params, S = o.S;
@@ -1284,10 +1457,18 @@ int orc_replay_jvp_f64(const orc_problem *P, int64_t n, const double *u0, const 
       if (si[s] == 0)
         for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
     for (int k = 0; k < N; ++k) {
-      one_step<Dual, false>(P, yv, pv, Dual(h[i * P->max_steps + k]));
+      Dual yprev[MAXD];
+      const Dual hk(h[i * P->max_steps + k]);
+      for (int c = 0; c < d; ++c) yprev[c] = yv[c];
+      one_step<Dual, false>(P, yv, pv, hk);
       for (int s = 0; s < S; ++s)
-        if (si[s] == k + 1)
-          for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+        if (si[s] == k + 1) {
+          if (P->dense)
+            dense_value<Dual, double, false>(P->rhs, d, theta[i * S + s], hk, yprev, yv, pv,
+                                             &ysl[s * d]);
+          else
+            for (int c = 0; c < d; ++c) ysl[s * d + c] = yv[c];
+        }
     }
     Dual ss(0.0);
     bool first = true;

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 
 import workloads as W
+import test_oracle_dense as dense
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
@@ -46,6 +47,18 @@ MUTANTS = {
     "controller_growth_after_reject": ("if (after_reject) fac = std::min(fac, T(1.0));", ""),
     "error_norm_scale": ("sc[c] = mac<F>(rtol, std::max(absval(y[c]), absval(yn[c])), atol);",
                          "sc[c] = mac<F>(rtol, absval(y[c]), atol);"),
+    "hermite_start_slope_sign": ("w[2] = th * u2;", "w[2] = -(th * u2);"),
+    "hermite_end_weight": ("w[1] = t2 * mac<F>(S(-2.0), th, S(3.0));",
+                           "w[1] = t2 * mac<F>(S(-2.0), th, S(2.0));"),
+    "dense_seed_drops_end_slope": ("lam[c] = mac<F>(w[1], sb[c], lam[c]) + w1[c];",
+                                   "lam[c] = mac<F>(w[1], sb[c], lam[c]);"),
+    "dense_seed_vjp_at_wrong_state": ("rhs_vjp_y<T, F>(kind, d, yk1, p, v1, w1);",
+                                      "rhs_vjp_y<T, F>(kind, d, yk, p, v1, w1);"),
+    "dense_bypass_not_added": ("for (int c = 0; c < d; ++c) lam[c] = lam[c] + mu[c];", ""),
+    "dense_fraction_origin": ("const double th = (ts - t) / h;",
+                              "const double th = (t_end - ts) / h;"),
+    "dense_save_in_next_step": ("out.sidx[j] = nacc;\n            if (out.theta) out.theta[j] = th;",
+                                "out.sidx[j] = nacc + 1;\n            if (out.theta) out.theta[j] = th;"),
 }
 
 
@@ -68,6 +81,12 @@ def _battery():
         out.append((pins.test_adjoint_matches_dual_numbers, dict(case=case)))
     for case in pins.CASES:
         out.append((pins.test_adjoint_matches_finite_differences, dict(case=case)))
+    out += [(dense.test_dense_hermite_remainder_on_linear_decay,
+             dict(method=W.TSIT5, fused=False)),
+            (dense.test_dense_fraction_one_is_the_clipped_save, dict(fused=False))]
+    for case in dense.DCASES:
+        out.append((dense.test_dense_record_mesh_bookkeeping, dict(case=case)))
+        out.append((dense.test_dense_adjoint_matches_dual_numbers, dict(case=case, fused=False)))
     return out
 
 

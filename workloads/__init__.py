@@ -52,8 +52,11 @@ class Problem:
 
     Zero for ``dt0``, ``max_attempts``, ``safety``, ``fac_min`` and ``fac_max``
     selects the default (automatic starting step, 4 * max_steps attempts,
-    0.9, 0.2, 10).  ``checkpoint`` only schedules the GPU reverse sweep.  ``save_times`` must be strictly increasing in (t0, t1];
-    empty means the final state is the only save.
+    0.9, 0.2, 10).  ``checkpoint`` only schedules the GPU reverse sweep.
+    ``save_times`` must be strictly increasing in (t0, t1]; empty means the
+    final state is the only save.  ``dense = 1`` reads the save times from an
+    interpolant of the accepted step that contains them instead of shortening
+    steps to land on them.
     """
     rhs: int
     dim: int
@@ -71,6 +74,7 @@ class Problem:
     fac_min: float = 0.0
     fac_max: float = 0.0
     checkpoint: int = 0     # reverse-sweep checkpoint interval (0 = automatic)
+    dense: int = 0          # 1: saves read from the step interpolant, not landed on
 
     @property
     def n_save_eff(self) -> int:
