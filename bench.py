@@ -73,8 +73,9 @@ def flop_per_step(method: str, rhs: str, dim: int) -> int:
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
 # Sources of the gradient kernel of each method family.
 KERNEL_SOURCES = {
-    "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "dadj_device.hpp",
-            "dadj_internal.hpp"],
+    "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "erk_grad_f64_dopri5.hip",
+            "erk_grad_f64_tsit5.hip", "erk_grad_f32_dopri5.hip", "erk_grad_f32_tsit5.hip",
+            "dadj_device.hpp", "dadj_internal.hpp"],
     "ros2": ["lane_kernels.hpp", "ros2.hip", "dadj_device.hpp", "dadj_internal.hpp"],
     "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
 }

@@ -13,8 +13,10 @@ index last and contiguous): u0 [d, n], p [P, n], y_save [S, d, n], grad_u0
 h [T, n, B] (tiled step log: B = 8 steps per 64-byte chunk in float64, 16 in
 float32, T = ceil(max_steps / B); ``Mesh.steps()`` gives the [n, max_steps]
 view), n_steps [n], save_idx [S, n], status [n], perm [n] or None (a
-replay order) and h_rows [rows, n] or None (the replay table: step k of the
-trajectory of lane j at [k, j]); ``mesh_sort`` fills the last two.
+replay order), h_rows [rows, n] or None (the replay table: step k of the
+trajectory of lane j at [k, j]; ``mesh_sort`` fills these two) and
+save_theta [S, n] (the step fraction of each save: 1 where steps land on the
+save times, the interpolation point with ``problem.dense = 1``).
 
 The problem description is ``workloads.Problem`` (or any object with the same
 fields) plus a dtype taken from the tensors.
@@ -61,7 +63,7 @@ class _Problem(ctypes.Structure):
         ("max_steps", ctypes.c_int32), ("max_attempts", ctypes.c_int32),
         ("n_save", ctypes.c_int32), ("save_times", ctypes.POINTER(ctypes.c_double)),
         ("safety", ctypes.c_double), ("fac_min", ctypes.c_double), ("fac_max", ctypes.c_double),
-        ("checkpoint", ctypes.c_int32),
+        ("checkpoint", ctypes.c_int32), ("dense", ctypes.c_int32),
     ]
 
 
@@ -69,7 +71,7 @@ class _Mesh(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("n_steps", ctypes.c_void_p),
                 ("save_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("h_rows", ctypes.c_void_p),
-                ("rows", ctypes.c_int32)]
+                ("rows", ctypes.c_int32), ("save_theta", ctypes.c_void_p)]
 
 
 class _Loss(ctypes.Structure):
@@ -140,7 +142,8 @@ def cproblem(prob, dtype) -> tuple:
                  prob.t0, prob.t1, prob.rtol, prob.atol, prob.dt0, prob.max_steps,
                  prob.max_attempts, len(prob.save_times),
                  ctypes.cast(st, ctypes.POINTER(ctypes.c_double)) if len(prob.save_times) else None,
-                 prob.safety, prob.fac_min, prob.fac_max, getattr(prob, "checkpoint", 0))
+                 prob.safety, prob.fac_min, prob.fac_max, getattr(prob, "checkpoint", 0),
+                 getattr(prob, "dense", 0))
     return P, st
 
 
@@ -175,13 +178,15 @@ def chunk_steps(dtype) -> int:
 class Mesh:
     """The record: tiled step log h [T, n, B], n_steps [n], save_idx [S, n],
     status [n]; an optional replay order perm [n] (None = identity) and
-    replay table h_rows [rows, n]."""
+    replay table h_rows [rows, n]; save fractions save_theta [S, n] (needed
+    with dense output)."""
     h: torch.Tensor
     n_steps: torch.Tensor
     save_idx: torch.Tensor
     status: torch.Tensor
     perm: Optional[torch.Tensor] = None
     h_rows: Optional[torch.Tensor] = None
+    save_theta: Optional[torch.Tensor] = None
 
     @property
     def n(self) -> int:
@@ -197,7 +202,8 @@ class Mesh:
         return _Mesh(self.h.data_ptr(), self.n_steps.data_ptr(), self.save_idx.data_ptr(),
                      self.status.data_ptr(), None if self.perm is None else self.perm.data_ptr(),
                      None if self.h_rows is None else self.h_rows.data_ptr(),
-                     0 if self.h_rows is None else self.h_rows.shape[0])
+                     0 if self.h_rows is None else self.h_rows.shape[0],
+                     None if self.save_theta is None else self.save_theta.data_ptr())
 
 
 def mesh_h_shape(prob, n: int, dtype) -> tuple:
@@ -214,7 +220,9 @@ def empty_mesh(prob, n: int, dtype, device="cuda", with_perm: bool = False) -> M
                 torch.empty(n, dtype=torch.int32, device=device),
                 torch.empty((S, n), dtype=torch.int32, device=device),
                 torch.empty(n, dtype=torch.int32, device=device),
-                torch.empty(n, dtype=torch.int32, device=device) if with_perm else None)
+                torch.empty(n, dtype=torch.int32, device=device) if with_perm else None,
+                None,
+                torch.empty((S, n), dtype=dtype, device=device))
 
 
 def _inputs(prob, u0: torch.Tensor, p: torch.Tensor):
@@ -277,7 +285,7 @@ def mesh_sort(prob, mesh: Mesh, perm: Optional[torch.Tensor] = None, table: bool
     need = mesh_sort_workspace(prob, n, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    out = Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, perm, h_rows)
+    out = Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, perm, h_rows, mesh.save_theta)
     P, keep = cproblem(prob, dt)
     co = out.c()
     _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(co), _ptr(workspace),

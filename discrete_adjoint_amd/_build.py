@@ -10,7 +10,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libdadj.so")
-SOURCES = ["api.hip", "erk.hip", "ros2.hip", "l96.hip", "sens.hip", "sort.hip"]
+SOURCES = ["erk_grad_f64_dopri5.hip", "erk_grad_f64_tsit5.hip", "erk_grad_f32_dopri5.hip",
+           "erk_grad_f32_tsit5.hip", "sens.hip", "erk.hip", "ros2.hip", "l96.hip", "api.hip",
+           "sort.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -33,7 +35,7 @@ def _compile(src: str, extra=(), tag: str = "") -> str:
     return obj
 
 
-def build(jobs: int = 4, out: str = LIB, extra=()) -> str:
+def build(jobs: int = 8, out: str = LIB, extra=()) -> str:
     """Compile every source and link libdadj.so (or `out`, with extra compiler
     flags such as -D build options); returns its path."""
     tag = "" if out == LIB else "_" + os.path.basename(out).replace(".", "_")

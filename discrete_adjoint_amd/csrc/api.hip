@@ -88,6 +88,11 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (pb->checkpoint != 0 && pb->checkpoint != 1 && pb->checkpoint != 2 && pb->checkpoint != 4 &&
       pb->checkpoint != 8)
     return fail(DA_EINVAL, "checkpoint must be 0, 1, 2, 4 or 8");
+  if (pb->dense != 0 && pb->dense != 1) return fail(DA_EINVAL, "dense must be 0 or 1");
+  if (pb->dense && pb->method == DA_ROS2)
+    return fail(DA_EUNSUPPORTED, "dense output is available for the explicit methods");
+  if (pb->dense && pb->rhs == DA_RHS_LORENZ96)
+    return fail(DA_EUNSUPPORTED, "dense output is not available for LORENZ96");
   pr.rhs = pb->rhs;
   pr.dim = pb->dim;
   pr.n_params = pb->n_params;
@@ -108,6 +113,7 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   const int B = dadj::chunk_steps(pb->dtype);
   pr.n_chunks = (pb->max_steps + B - 1) / B;
   pr.checkpoint = pb->checkpoint > 0 ? pb->checkpoint : default_checkpoint(*pb);
+  pr.dense = pb->dense;
   if (st) {
     memset(st, 0, sizeof *st);
     for (int s = 0; s < pb->n_save; ++s) st->t[s] = pb->save_times[s];
@@ -140,6 +146,7 @@ void fill_replay_args(dadj::ReplayArgs &a, const dadj::ProbArgs &pr, int64_t n, 
   a.sidx = mesh->save_idx;
   a.status = mesh->status;
   a.perm = mesh->perm;
+  a.theta = mesh->save_theta;
 }
 
 hipError_t launch_record(const dadj::RecordArgs &a, const dadj::SaveTimes &st, hipStream_t s) {
@@ -176,6 +183,8 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   if (rc) return rc;
   if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
+  if (pr.dense && !mesh->save_theta)
+    return fail(DA_EINVAL, "dense output needs mesh->save_theta");
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
   if (n == 0) return ok();
   dadj::RecordArgs a;
@@ -186,6 +195,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   a.h = mesh->h;
   a.nsteps = mesh->n_steps;
   a.sidx = mesh->save_idx;
+  a.theta = mesh->save_theta;
   a.status = mesh->status;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
@@ -210,6 +220,7 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
   a.h = nullptr;
   a.nsteps = n_steps;
   a.sidx = nullptr;
+  a.theta = nullptr;
   a.status = status;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
@@ -279,6 +290,8 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
   if (n == 0) return ok();
   if ((rc = check_mesh(mesh, false, pr.max_steps))) return rc;
   if (n > 0 && (!u0 || !p || !y_save)) return fail(DA_EINVAL, "u0, p and y_save must not be NULL");
+  if (pr.dense && !mesh->save_theta)
+    return fail(DA_EINVAL, "dense output needs mesh->save_theta");
   if (n == 0) return ok();
   dadj::ReplayArgs a;
   fill_replay_args(a, pr, n, u0, p, mesh);
@@ -312,6 +325,8 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   if (loss->kind != DA_LOSS_SUMSQ_FINAL && !loss->aux)
     return fail(DA_EINVAL, "loss kind %d needs aux", loss->kind);
   if (!isfinite(loss->scale)) return fail(DA_EINVAL, "loss scale must be finite");
+  if (pr.dense && loss->kind != DA_LOSS_SUMSQ_FINAL && !mesh->save_theta)
+    return fail(DA_EINVAL, "dense output needs mesh->save_theta");
   if (max_n_steps < 0 || max_n_steps > pr.max_steps)
     return fail(DA_EINVAL, "max_n_steps must be in [0, max_steps]");
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
@@ -361,6 +376,8 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
                                  "of dimension <= 3");
   if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
+  if (pr.dense && (sens || (loss && loss->kind != DA_LOSS_SUMSQ_FINAL)) && !mesh->save_theta)
+    return fail(DA_EINVAL, "dense output needs mesh->save_theta");
   if (loss) {
     if (loss->kind < DA_LOSS_SUMSQ_FINAL || loss->kind > DA_LOSS_COTANGENT)
       return fail(DA_EINVAL, "bad loss kind %d", loss->kind);

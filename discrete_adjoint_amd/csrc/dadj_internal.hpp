@@ -28,6 +28,7 @@ struct ProbArgs {
   int32_t max_steps, max_attempts, n_save, S;  // S = max(1, n_save)
   int32_t n_chunks;                             // T = ceil(max_steps / B)
   int32_t checkpoint;                           // resolved: 1, 2, 4 or 8
+  int32_t dense;                                // saves from the step interpolant
   double t0, t1, rtol, atol, dt0, safety, fac_min, fac_max;
 };
 
@@ -43,6 +44,7 @@ struct RecordArgs {
   void *h;              // [T][n][B] or null (forward solve)
   int32_t *nsteps;      // [n] or null
   int32_t *sidx;        // [S][n] or null
+  void *theta;          // [S][n] step fraction of each save, or null
   int32_t *status;      // [n] or null
   void *y_save;         // [S][d][n] or null
 };
@@ -55,6 +57,7 @@ struct ReplayArgs {
   const void *h_rows;          // replay table [rows][n] in lane order, or null
   int32_t rows;
   const int32_t *nsteps, *sidx, *status, *perm;
+  const void *theta;           // [S][n] step fraction of each save (dense output)
   void *y_save;                // replay_fwd output [S][d][n]
   int32_t loss_kind;
   const void *aux;             // [S][d][n]

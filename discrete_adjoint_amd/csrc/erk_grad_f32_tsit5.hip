@@ -1,0 +1,11 @@
+// Replay-gradient kernels of the explicit methods for float and Tsit5
+// (one file per dtype and method, see erk.hip).
+#include "erk_method.hpp"
+
+namespace dadj {
+
+hipError_t launch_erk_grad_f32_tsit5(const ReplayArgs &a, hipStream_t s) {
+  DADJ_ERK_RHS_DISPATCH(replay_grad_t, float, Tsit5Tab, (a, s));
+}
+
+}  // namespace dadj

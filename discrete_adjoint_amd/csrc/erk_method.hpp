@@ -12,6 +12,7 @@ struct Erk {
   using Rhs = R;
   static constexpr int D = R::D;
   static constexpr int order = Tab::order, err_order = Tab::err_order;
+  static constexpr bool dense_output = true;
   template <class T> struct Cache {
     T Y[7][D], K[7][D];
   };
@@ -109,29 +110,28 @@ struct Erk {
   }
 };
 
-#define DADJ_ERK_DISPATCH(FN, ARGS)                                                        \
+// FN<T, Erk<TAB, rhs>> ARGS for the problem's right-hand side.
+#define DADJ_ERK_RHS_DISPATCH(FN, T, TAB, ARGS)                                           \
   do {                                                                                     \
-    const bool f64 = a.pr.dtype == DA_F64;                                                 \
-    const bool ts = a.pr.method == DA_TSIT5;                                               \
     switch (a.pr.rhs) {                                                                    \
-      case DA_RHS_LINEAR:                                                                  \
-        if (f64) return ts ? FN<double, Erk<Tsit5Tab, Linear>> ARGS                        \
-                           : FN<double, Erk<Dopri5Tab, Linear>> ARGS;                      \
-        return ts ? FN<float, Erk<Tsit5Tab, Linear>> ARGS : FN<float, Erk<Dopri5Tab, Linear>> ARGS; \
-      case DA_RHS_LORENZ63:                                                                \
-        if (f64) return ts ? FN<double, Erk<Tsit5Tab, Lorenz63>> ARGS                      \
-                           : FN<double, Erk<Dopri5Tab, Lorenz63>> ARGS;                    \
-        return ts ? FN<float, Erk<Tsit5Tab, Lorenz63>> ARGS                                \
-                  : FN<float, Erk<Dopri5Tab, Lorenz63>> ARGS;                              \
-      case DA_RHS_ROBERTSON:                                                               \
-        if (f64) return ts ? FN<double, Erk<Tsit5Tab, Robertson>> ARGS                     \
-                           : FN<double, Erk<Dopri5Tab, Robertson>> ARGS;                   \
-        return ts ? FN<float, Erk<Tsit5Tab, Robertson>> ARGS                               \
-                  : FN<float, Erk<Dopri5Tab, Robertson>> ARGS;                             \
-      default:                                                                             \
-        return hipErrorInvalidValue;                                                       \
+      case DA_RHS_LINEAR: return FN<T, Erk<TAB, Linear>> ARGS;                             \
+      case DA_RHS_LORENZ63: return FN<T, Erk<TAB, Lorenz63>> ARGS;                         \
+      case DA_RHS_ROBERTSON: return FN<T, Erk<TAB, Robertson>> ARGS;                       \
+      default: return hipErrorInvalidValue;                                                \
     }                                                                                      \
   } while (0)
 
+// FN<T, Erk<tableau, rhs>> ARGS for the problem's dtype, method and
+// right-hand side.
+#define DADJ_ERK_DISPATCH(FN, ARGS)                                                        \
+  do {                                                                                     \
+    const bool ts = a.pr.method == DA_TSIT5;                                               \
+    if (a.pr.dtype == DA_F64) {                                                            \
+      if (ts) DADJ_ERK_RHS_DISPATCH(FN, double, Tsit5Tab, ARGS);                           \
+      DADJ_ERK_RHS_DISPATCH(FN, double, Dopri5Tab, ARGS);                                  \
+    }                                                                                      \
+    if (ts) DADJ_ERK_RHS_DISPATCH(FN, float, Tsit5Tab, ARGS);                              \
+    DADJ_ERK_RHS_DISPATCH(FN, float, Dopri5Tab, ARGS);                                     \
+  } while (0)
 
 }  // namespace dadj

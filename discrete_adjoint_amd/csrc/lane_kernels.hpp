@@ -23,6 +23,10 @@
 //   fwd(y, p, h)                                     one replay step
 //   adj(y, p, h, lam, g)                             its reverse
 //
+// With dense output (template flag DENSE) save times do not end steps: each
+// is read from the cubic Hermite interpolant of the accepted step that
+// contains it, at the step fraction the record stores in the mesh.
+//
 // Memory: per-trajectory arrays are component-major ([c][n], trajectory
 // fastest).  The step log is tiled [T][n][B]: each trajectory owns one 64-byte
 // chunk of B steps per tile, so the record writes whole chunks and a replay
@@ -102,6 +106,58 @@ __device__ __forceinline__ T err_norm(const T (&err)[D], const T (&y)[D], const 
   return rms<D>(err, sc);
 }
 
+// ---------------------------------------------------------------------------
+// Dense output ("Differentiable astrophysics at scale", Methodology: the
+// solution is interpolated at observation times instead of ending steps
+// there).  The interpolant is the cubic Hermite one of the accepted step
+// [t_k, t_k + h] through y_k, y_{k+1} and the slopes f(y_k), f(y_{k+1}):
+//   y(t_k + th h) = h (H11 f(y_{k+1}) + H10 f(y_k)) + (H01 y_{k+1} + H00 y_k)
+//   H00 = (1-th)^2 (1+2th), H01 = th^2 (3-2th), H10 = th (1-th)^2,
+//   H11 = -th^2 (1-th);  th = 1 gives y_{k+1} exactly.
+// ---------------------------------------------------------------------------
+template <class T> struct HermiteW {
+  T h00, h01, h10, h11;
+};
+template <class T> __device__ __forceinline__ HermiteW<T> hermite_w(T th) {
+  const T u = T(1) - th;
+  const T u2 = u * u, t2 = th * th;
+  HermiteW<T> w;
+  w.h00 = u2 * mac(T(2), th, T(1));
+  w.h01 = t2 * mac(T(-2), th, T(3));
+  w.h10 = th * u2;
+  w.h11 = -(t2 * u);
+  return w;
+}
+
+// Interpolated state at fraction th of the step of size h from y0 to y1.  V
+// is the value type (a real, or a tangent type whose weights and step carry
+// no tangent), T the real type of th and h.
+template <class Rhs, class V, class T>
+__device__ __forceinline__ void dense_value(T th, T h, const V (&y0)[Rhs::D],
+                                            const V (&y1)[Rhs::D], const V *p,
+                                            V (&out)[Rhs::D]) {
+  constexpr int D = Rhs::D;
+  const HermiteW<T> w = hermite_w(th);
+  const V w00(w.h00), w01(w.h01), w10(w.h10), w11(w.h11), hv(h);
+  V f0[D], f1[D];
+  Rhs::f(y0, p, f0);
+  Rhs::f(y1, p, f1);
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    const V sl = mac(w11, f1[c], w10 * f0[c]);
+    out[c] = mac(hv, sl, mac(w01, y1[c], w00 * y0[c]));
+  }
+}
+
+// Fraction of the accepted step [t, t_end] of size h at which save time ts
+// lies (t < ts <= t_end): exactly 1 at the step's end, else (ts - t) / h in
+// double, capped at 1.
+__device__ __forceinline__ double step_fraction(double ts, double t, double t_end, double h) {
+  if (ts >= t_end) return 1.0;
+  const double th = (ts - t) / h;
+  return th < 1.0 ? th : 1.0;
+}
+
 // Starting step of Hairer, Norsett, Wanner I, section II.4, method order q.
 template <class Rhs, class T>
 __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T *p, T atol,
@@ -130,11 +186,13 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // Record / forward solve.  Controller: accept iff E <= 1; next step = used
 // step * clamp(safety E^(-1/(q+1)), fac_min, fac_max), no growth right after
 // a rejection, fac_max when E == 0, fac_min when E is not finite.  Steps land
-// exactly on every save time and on t1; t accumulates in double.  Accepted
-// steps collect in a register chunk that is written when full; after the
-// last step the partial chunk and zero chunks up to the end of the log follow.
+// exactly on every save time and on t1 (DENSE: on t1 only; the save times
+// inside an accepted step are read from its interpolant); t accumulates in
+// double.  Accepted steps collect in a register chunk that is written when
+// full; after the last step the partial chunk and zero chunks up to the end
+// of the log follow.
 // ---------------------------------------------------------------------------
-template <class T, class M, bool LOG>
+template <class T, class M, bool LOG, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
@@ -153,6 +211,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   const T *pp = (const T *)a.p;
   T *H = (T *)a.h;
   T *ysave = (T *)a.y_save;
+  T *theta = (T *)a.theta;
 
   int nacc = 0, natt = 0, st = LANE_OK;
   T hb[B];
@@ -174,6 +233,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     }
     for (int s = 0; s < S; ++s) {
       if (a.sidx) a.sidx[s * n + i] = -1;
+      if (theta) theta[s * n + i] = nanv<T>();
       if (ysave)
 #pragma unroll
         for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + i] = nanv<T>();
@@ -189,7 +249,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
       int js = 0;
       bool after_reject = false;
       for (;;) {
-        const double t_stop = (has_saves && js < S) ? stimes.t[js] : pr.t1;
+        const double t_stop = (!DENSE && has_saves && js < S) ? stimes.t[js] : pr.t1;
         const T rem = T(t_stop - t);
         const bool land = !(h < rem);
         const T hs = land ? rem : h;
@@ -200,6 +260,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         M::attempt(y, p, hs, cache, ynew, err);
         const T E = err_norm<D>(err, y, ynew, atol, rtol);
         if (E <= T(1)) {
+          const double t_new = land ? t_stop : t + double(hs);
           if (LOG) {
             const int pos = nacc % B;
 #pragma unroll
@@ -211,17 +272,42 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
             }
           }
           ++nacc;
+          if constexpr (DENSE) {
+            // the save times inside this step
+            for (; has_saves && js < S && stimes.t[js] <= t_new; ++js) {
+              const T th = T(step_fraction(stimes.t[js], t, t_new, double(hs)));
+              if (a.sidx) a.sidx[js * n + i] = nacc;
+              if (theta) theta[js * n + i] = th;
+              if (ysave) {
+                T ys[D];
+                dense_value<Rhs>(th, hs, y, ynew, p, ys);
+#pragma unroll
+                for (int c = 0; c < D; ++c) ysave[(js * D + c) * n + i] = ys[c];
+              }
+            }
+          }
 #pragma unroll
           for (int c = 0; c < D; ++c) y[c] = ynew[c];
           M::accepted(cache);
-          t = land ? t_stop : t + double(hs);
+          t = t_new;
           T fac = (E == T(0)) ? fmax : dmin(fmax, dmax(fmin, safety * dpow(E, expo)));
           if (after_reject) fac = dmin(fac, T(1));
           h = hs * fac;
           after_reject = false;
+          if (DENSE && land) {
+            if (!has_saves) {  // the final state is the one save
+              if (a.sidx) a.sidx[i] = nacc;
+              if (theta) theta[i] = T(1);
+              if (ysave)
+#pragma unroll
+                for (int c = 0; c < D; ++c) ysave[c * n + i] = y[c];
+            }
+            break;
+          }
           if (land) {
             if (js < S) {
               if (a.sidx) a.sidx[js * n + i] = nacc;
+              if (theta) theta[js * n + i] = T(1);
               if (ysave)
 #pragma unroll
                 for (int c = 0; c < D; ++c) ysave[(js * D + c) * n + i] = y[c];
@@ -314,11 +400,12 @@ __device__ __forceinline__ LaneInfo lane_info(const ReplayArgs &a, int64_t j, bo
 // ---------------------------------------------------------------------------
 // Replay forward: the state after save_idx[s] steps goes to y_save[s]; save
 // slots whose index lies outside [0, n_steps], and every slot of a lane that
-// does not replay, get NaN.  Two steps per loop trip so that the step size of
-// the next step is loaded into the register the next step reads (no copy,
-// so no wait on the load until that step).
+// does not replay, get NaN.  DENSE: a save with index k >= 1 is the
+// interpolant of step k - 1 at its recorded fraction.  Two steps per loop
+// trip so that the step size of the next step is loaded into the register
+// the next step reads (no copy, so no wait on the load until that step).
 // ---------------------------------------------------------------------------
-template <class T, class M, bool ROWS>
+template <class T, class M, bool ROWS, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
@@ -357,10 +444,29 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
     }
   };
   save(0);
+  // DENSE: the saves inside step k, from the state yp before it
+  auto dsave = [&](int k, const T (&yp)[D], T hk) {
+    while (s < S && nxt == k + 1) {
+      T ys[D];
+      dense_value<Rhs>(((const T *)a.theta)[(int64_t)s * n + tr], hk, yp, y, p, ys);
+#pragma unroll
+      for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = ys[c];
+      ++s;
+      nxt = s < S ? a.sidx[s * n + tr] : -1;
+    }
+  };
   auto step = [&](int k, T hk) {
     if (k < N) {
-      M::fwd(y, p, hk);
-      save(k + 1);
+      if constexpr (DENSE) {
+        T yp[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) yp[c] = y[c];
+        M::fwd(y, p, hk);
+        dsave(k, yp, hk);
+      } else {
+        M::fwd(y, p, hk);
+        save(k + 1);
+      }
     }
   };
   T hA = src.load(0);
@@ -413,7 +519,42 @@ template <class T, int D, int CK> struct Seg {
   T cp[D], h[CK];
 };
 
-template <class T, class M, int CK, bool ROWS>
+// Reverse of one dense save inside the step from yk to yk1 (size h, fraction
+// th), with sb = dL/dy(t_s) the save's seed:
+//   lam (dL/dy_{k+1}) += H01 sb + J(yk1)^T v1,  v1 = (h H11) sb
+//   mu  (the part of dL/dy_k that bypasses the step) += H00 sb + J(yk)^T v0,
+//                                               v0 = (h H10) sb
+//   g += J_p(yk1)^T v1, then g += J_p(yk)^T v0.
+template <class Rhs, class T>
+__device__ __forceinline__ void dense_seed(int lk, T th, T h, const T (&yk)[Rhs::D],
+                                           const T (&yk1)[Rhs::D], const T *p, const T *aux,
+                                           int64_t n, int s, int64_t tr, double scale,
+                                           T (&lam)[Rhs::D], T (&mu)[Rhs::D], T *g) {
+  constexpr int D = Rhs::D;
+  T ys[D], sb[D], v0[D], v1[D], w0[D], w1[D];
+  dense_value<Rhs>(th, h, yk, yk1, p, ys);
+#pragma unroll
+  for (int c = 0; c < D; ++c) sb[c] = T(0);
+  seed_terms<T, D>(lk, ys, aux, n, s, tr, scale, sb);
+  const HermiteW<T> w = hermite_w(th);
+  const T c1 = h * w.h11, c0 = h * w.h10;
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    v1[c] = c1 * sb[c];
+    v0[c] = c0 * sb[c];
+  }
+  Rhs::vjp_y(yk1, p, v1, w1);
+  Rhs::vjp_y(yk, p, v0, w0);
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    lam[c] = mac(w.h01, sb[c], lam[c]) + w1[c];
+    mu[c] = mac(w.h00, sb[c], mu[c]) + w0[c];
+  }
+  Rhs::vjp_p_acc(yk1, p, v1, g);
+  Rhs::vjp_p_acc(yk, p, v0, g);
+}
+
+template <class T, class M, int CK, bool ROWS, bool DENSE>
 __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(ReplayArgs a) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P;
@@ -457,6 +598,17 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
     }
   };
   if (saves) terms(0);
+  const T *theta = (const T *)a.theta;
+  // DENSE: loss terms of the saves inside step k, from the state yp before it
+  auto dterms = [&](int k, const T (&yp)[D], T hk) {
+    while (s < S && nxt == k + 1) {
+      T ys[D];
+      dense_value<Rhs>(theta[(int64_t)s * n + tr], hk, yp, y, p, ys);
+      loss_terms<T, D>(lk, ys, aux, n, s, tr, ss, first);
+      ++s;
+      nxt = s < S ? a.sidx[s * n + tr] : -1;
+    }
+  };
   auto fstep = [&](int k, T hk) {
     if (k < N) {
       if (k % CK == 0) {
@@ -464,8 +616,16 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 #pragma unroll
         for (int c = 0; c < D; ++c) wk[c * C] = y[c];
       }
-      M::fwd(y, p, hk);
-      if (saves) terms(k + 1);
+      if constexpr (DENSE) {
+        T yp[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) yp[c] = y[c];
+        M::fwd(y, p, hk);
+        dterms(k, yp, hk);
+      } else {
+        M::fwd(y, p, hk);
+        if (saves) terms(k + 1);
+      }
     }
   };
   {
@@ -500,7 +660,11 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
       hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
     }
   };
-  if (saves) seeds(N, y);
+  if (saves && !DENSE) seeds(N, y);
+  // DENSE: y_{k+1} while step k is reversed (starts as the final state)
+  T yhi[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) yhi[c] = y[c];
 
   // ---- reverse sweep, one segment of CK steps at a time ----
   // Every index stays inside the buffers: segments m < Mw = ceil(Nw / CK);
@@ -528,8 +692,34 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
     for (int b = CK - 1; b >= 0; --b) {
       const int k = m * CK + b;
       if (k < N) {
-        M::adj(ys[b], p, sg.h[b], lam, g);
-        if (saves) seeds(k, ys[b]);
+        if constexpr (DENSE) {
+          // the saves inside step k, the last first: into lam now, into mu
+          // (joining lam after the step's reverse) for the y_k part
+          T mu[D];
+          bool has_mu = false;
+          while (sh >= 0 && hidx == k + 1) {
+            if (!has_mu) {
+#pragma unroll
+              for (int c = 0; c < D; ++c) mu[c] = T(0);
+            }
+            has_mu = true;
+            dense_seed<Rhs>(lk, theta[(int64_t)sh * n + tr], sg.h[b], ys[b], yhi, p, aux, n, sh,
+                            tr, a.scale, lam, mu, g);
+            --sh;
+            hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+          }
+          M::adj(ys[b], p, sg.h[b], lam, g);
+          if (has_mu) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) lam[c] = lam[c] + mu[c];
+          }
+          if (k == 0) seeds(0, ys[b]);
+#pragma unroll
+          for (int c = 0; c < D; ++c) yhi[c] = ys[b][c];
+        } else {
+          M::adj(ys[b], p, sg.h[b], lam, g);
+          if (saves) seeds(k, ys[b]);
+        }
       }
     }
   };
@@ -559,38 +749,74 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+// Methods with dense output set M::dense_output; for the others the DENSE
+// kernels are not built and a dense problem is refused before launch.
+template <class T, class M, bool DENSE>
+hipError_t record_d(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  const unsigned grid = (unsigned)((a.n + BLOCK - 1) / BLOCK);
+  if (a.h) hipLaunchKernelGGL((k_record<T, M, true, DENSE>), grid, BLOCK, 0, s, a, st);
+  else hipLaunchKernelGGL((k_record<T, M, false, DENSE>), grid, BLOCK, 0, s, a, st);
+  return hipGetLastError();
+}
+
 template <class T, class M>
 hipError_t record_t(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  if constexpr (M::dense_output) {
+    if (a.pr.dense) return record_d<T, M, true>(a, st, s);
+  } else {
+    if (a.pr.dense) return hipErrorInvalidValue;
+  }
+  return record_d<T, M, false>(a, st, s);
+}
+
+template <class T, class M, bool DENSE>
+hipError_t replay_fwd_d(const ReplayArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.n + BLOCK - 1) / BLOCK);
-  if (a.h) hipLaunchKernelGGL((k_record<T, M, true>), grid, BLOCK, 0, s, a, st);
-  else hipLaunchKernelGGL((k_record<T, M, false>), grid, BLOCK, 0, s, a, st);
+  if (a.h_rows) hipLaunchKernelGGL((k_replay_fwd<T, M, true, DENSE>), grid, BLOCK, 0, s, a);
+  else hipLaunchKernelGGL((k_replay_fwd<T, M, false, DENSE>), grid, BLOCK, 0, s, a);
   return hipGetLastError();
 }
 
 template <class T, class M>
 hipError_t replay_fwd_t(const ReplayArgs &a, hipStream_t s) {
-  const unsigned grid = (unsigned)((a.n + BLOCK - 1) / BLOCK);
-  if (a.h_rows) hipLaunchKernelGGL((k_replay_fwd<T, M, true>), grid, BLOCK, 0, s, a);
-  else hipLaunchKernelGGL((k_replay_fwd<T, M, false>), grid, BLOCK, 0, s, a);
-  return hipGetLastError();
+  if constexpr (M::dense_output) {
+    if (a.pr.dense) return replay_fwd_d<T, M, true>(a, s);
+  } else {
+    if (a.pr.dense) return hipErrorInvalidValue;
+  }
+  return replay_fwd_d<T, M, false>(a, s);
 }
 
-template <class T, class M, bool ROWS>
+template <class T, class M, bool ROWS, bool DENSE>
 hipError_t replay_grad_ck(const ReplayArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.nslots + BLOCK - 1) / BLOCK);
   switch (a.pr.checkpoint) {
-    case 1: hipLaunchKernelGGL((k_replay_grad<T, M, 1, ROWS>), grid, BLOCK, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((k_replay_grad<T, M, 2, ROWS>), grid, BLOCK, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((k_replay_grad<T, M, 4, ROWS>), grid, BLOCK, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((k_replay_grad<T, M, 8, ROWS>), grid, BLOCK, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((k_replay_grad<T, M, 1, ROWS, DENSE>), grid, BLOCK, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((k_replay_grad<T, M, 2, ROWS, DENSE>), grid, BLOCK, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((k_replay_grad<T, M, 4, ROWS, DENSE>), grid, BLOCK, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_replay_grad<T, M, 8, ROWS, DENSE>), grid, BLOCK, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <class T, class M, bool DENSE>
+hipError_t replay_grad_d(const ReplayArgs &a, hipStream_t s) {
+  return a.h_rows ? replay_grad_ck<T, M, true, DENSE>(a, s)
+                  : replay_grad_ck<T, M, false, DENSE>(a, s);
+}
+
+// The final-state loss reads no save, so a dense problem runs the plain
+// kernel for it.
 template <class T, class M>
 hipError_t replay_grad_t(const ReplayArgs &a, hipStream_t s) {
-  return a.h_rows ? replay_grad_ck<T, M, true>(a, s) : replay_grad_ck<T, M, false>(a, s);
+  const bool dense = a.pr.dense && a.loss_kind != DA_LOSS_SUMSQ_FINAL;
+  if constexpr (M::dense_output) {
+    if (dense) return replay_grad_d<T, M, true>(a, s);
+  } else {
+    if (dense) return hipErrorInvalidValue;
+  }
+  return replay_grad_d<T, M, false>(a, s);
 }
 
 }  // namespace dadj

@@ -151,6 +151,7 @@ struct Ros2 {
   using Rhs = R;
   static constexpr int D = R::D;
   static constexpr int order = 2, err_order = 1;
+  static constexpr bool dense_output = false;
   template <class T> struct Cache {};
 
   template <class T>

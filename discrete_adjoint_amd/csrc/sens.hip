@@ -19,7 +19,9 @@ constexpr int SENS_G = 2;  // tangent directions per lane
 // product, then multiply-adds), the seeds being
 //   final-state loss: (2 scale) y_N    MSE: (2 scale) (y_s - aux_s)
 //   cotangent:        scale aux_s.
-template <class T, class M, int G, bool ROWS>
+// DENSE: a save with index k >= 1 (and its tangents) is the interpolant of
+// step k - 1 at the recorded fraction.
+template <class T, class M, int G, bool ROWS, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
   using Rhs = typename M::Rhs;
   constexpr int D = Rhs::D, P = Rhs::P, Q = D + P;
@@ -77,39 +79,54 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
   };
   int s = 0;
   int nxt = ok ? a.sidx[tr] : -1;
-  auto at_saves = [&](int k) {
-    while (s < S && nxt == k) {
-      if (sens)
+  // save s has state (and tangents) ysv
+  auto emit = [&](const DT (&ysv)[D]) {
+    if (sens)
 #pragma unroll
-        for (int c = 0; c < D; ++c)
+      for (int c = 0; c < D; ++c)
 #pragma unroll
-          for (int m = 0; m < G; ++m)
-            if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = y[c].d[m];
-      if (saves) {
+        for (int m = 0; m < G; ++m)
+          if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = ysv[c].d[m];
+    if (saves) {
 #pragma unroll
-        for (int c = 0; c < D; ++c) {
-          const T av = aux[((int64_t)s * D + c) * n + tr];
-          const T yv = y[c].v;
-          if (lk == DA_LOSS_MSE_SAVE) {
-            grad_terms(T(2.0 * a.scale) * (yv - av), y[c]);
-            const T r = yv - av;
-            ss = lfirst ? r * r : mac(r, r, ss);
-          } else {
-            grad_terms(T(a.scale) * av, y[c]);
-            ss = lfirst ? av * yv : mac(av, yv, ss);
-          }
-          lfirst = false;
+      for (int c = 0; c < D; ++c) {
+        const T av = aux[((int64_t)s * D + c) * n + tr];
+        const T yv = ysv[c].v;
+        if (lk == DA_LOSS_MSE_SAVE) {
+          grad_terms(T(2.0 * a.scale) * (yv - av), ysv[c]);
+          const T r = yv - av;
+          ss = lfirst ? r * r : mac(r, r, ss);
+        } else {
+          grad_terms(T(a.scale) * av, ysv[c]);
+          ss = lfirst ? av * yv : mac(av, yv, ss);
         }
+        lfirst = false;
       }
-      ++s;
-      nxt = s < S ? a.sidx[s * n + tr] : -1;
     }
+    ++s;
+    nxt = s < S ? a.sidx[s * n + tr] : -1;
+  };
+  auto at_saves = [&](int k) {
+    while (s < S && nxt == k) emit(y);
   };
   at_saves(0);
+  const T *theta = (const T *)a.theta;
   auto step = [&](int k, T hk) {
     if (k < N) {
-      M::fwd(y, p, hk);
-      at_saves(k + 1);
+      if constexpr (DENSE) {
+        DT yp[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) yp[c] = y[c];
+        M::fwd(y, p, hk);
+        while (s < S && nxt == k + 1) {
+          DT ys[D];
+          dense_value<Rhs>(theta[(int64_t)s * n + tr], hk, yp, y, p, ys);
+          emit(ys);
+        }
+      } else {
+        M::fwd(y, p, hk);
+        at_saves(k + 1);
+      }
     }
   };
   T hA = src.load(0);
@@ -141,13 +158,24 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
   }
 }
 
-template <class T, class M>
-hipError_t replay_sens_t(const ReplayArgs &a, hipStream_t s) {
+template <class T, class M, bool DENSE>
+hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {
   constexpr int Q = M::Rhs::D + M::Rhs::P;
   const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK), (unsigned)((Q + SENS_G - 1) / SENS_G));
-  if (a.h_rows) hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true>), grid, BLOCK, 0, s, a);
-  else hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, false>), grid, BLOCK, 0, s, a);
+  if (a.h_rows)
+    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true, DENSE>), grid, BLOCK, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, false, DENSE>), grid, BLOCK, 0, s, a);
   return hipGetLastError();
+}
+
+// Dense output changes only the saves: without loss terms at the saves and
+// without sensitivity output the plain kernel computes the same.
+template <class T, class M>
+hipError_t replay_sens_t(const ReplayArgs &a, hipStream_t s) {
+  const bool at_saves = a.sens || (a.has_loss && a.loss_kind != DA_LOSS_SUMSQ_FINAL);
+  if (a.pr.dense && at_saves) return replay_sens_d<T, M, true>(a, s);
+  return replay_sens_d<T, M, false>(a, s);
 }
 
 }  // namespace

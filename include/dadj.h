@@ -100,7 +100,9 @@ typedef enum {
  * <= 1; next step = used step * clamp(safety E^(-1/(q+1)), fac_min, fac_max)
  * with q the embedded order (4 for the explicit pairs, 1 for ROS2), no growth
  * on the step after a rejection.  Steps are shortened to land exactly on each
- * save time and on t1. */
+ * save time and on t1, or, with dense = 1, on t1 only, each save time then
+ * being read from the interpolant of the accepted step that contains it
+ * (see da_mesh.save_theta). */
 typedef struct {
   int32_t rhs;         /* da_rhs                                              */
   int32_t dim;         /* state dimension d                                   */
@@ -121,6 +123,24 @@ typedef struct {
                           registers; 1 = keep every state; 0 = the library's
                           choice for the right-hand side.  1, 2, 4 or 8 (or
                           0).  The result does not depend on it.             */
+  int32_t dense;       /* 0: steps land on the save times.  1: dense output
+                          ("Differentiable astrophysics at scale",
+                          Methodology: the solution is interpolated at the
+                          observation times instead of ending steps there).
+                          The page names no interpolant; this library uses
+                          the cubic Hermite interpolant of the accepted step
+                          [t_k, t_k + h] through y_k, y_{k+1} and the slopes
+                          f(y_k), f(y_{k+1}) (the step's first and last stage
+                          derivatives):
+                            y(t_k + th h) = H00 y_k + H01 y_{k+1}
+                                          + h (H10 f(y_k) + H11 f(y_{k+1})),
+                            H00 = (1-th)^2 (1+2th), H01 = th^2 (3-2th),
+                            H10 = th (1-th)^2,      H11 = -th^2 (1-th).
+                          Save time t_s belongs to the step with
+                          t_k < t_s <= t_k + h; th = (t_s - t_k) / h in double,
+                          capped at 1, exactly 1 at the step's end.  th is part
+                          of the mesh and, like h, carries no derivative.
+                          Explicit methods only (DA_EUNSUPPORTED with ROS2).  */
 } da_problem;
 
 /* The record: one zero-padded step mesh per trajectory, reused by every
@@ -150,11 +170,20 @@ typedef struct {
   void *h;           /* [T][n][B] accepted step sizes, zero padded            */
   int32_t *n_steps;  /* [n] accepted steps                                    */
   int32_t *save_idx; /* [S][n] mesh index k at which save time s is reached
-                        (the state after k steps); -1 if never reached        */
+                        (the state after k steps; with dense output, the end
+                        of the step that contains it); -1 if never reached   */
   int32_t *status;   /* [n] da_lane_status                                    */
   int32_t *perm;     /* [n] lane -> trajectory replay order, or NULL          */
   void *h_rows;      /* [rows][n] replay table, or NULL                       */
   int32_t rows;      /* rows of h_rows (1..max_steps when h_rows is set)      */
+  void *save_theta;  /* [S][n] (problem dtype) step fraction of each save:
+                        with dense output save s is read from step
+                        save_idx[s] - 1 at fraction save_theta[s]; without it
+                        every reached save has fraction 1.  Written by
+                        da_record when not NULL; required by da_record and by
+                        the replays of a problem with dense = 1 (a replay
+                        gradient with the final-state loss reads no save and
+                        does not need it).                                   */
 } da_mesh;
 
 /* Elements (of the problem's dtype) of the step log of n trajectories:
@@ -166,8 +195,9 @@ int64_t da_mesh_h_elems(const da_problem *prob, int64_t n);
  *  DA_LOSS_SUMSQ_FINAL: L_i = scale * sum_c y_{N_i}[c]^2 (final state)
  *  DA_LOSS_MSE_SAVE:    L_i = scale * sum_s sum_c (y_{idx_s}[c] - aux[s][c][i])^2
  *  DA_LOSS_COTANGENT:   L_i = scale * sum_s sum_c aux[s][c][i] * y_{idx_s}[c]
- * aux is [S][d][n] in trajectory order (NULL for SUMSQ_FINAL).  The MSE of
- * the calibration workload uses scale = 1 / (n S d). */
+ * aux is [S][d][n] in trajectory order (NULL for SUMSQ_FINAL).  y_{idx_s} is
+ * the save s (with dense output the interpolated state).  The MSE of the
+ * calibration workload uses scale = 1 / (n S d). */
 typedef enum {
   DA_LOSS_SUMSQ_FINAL = 0,
   DA_LOSS_MSE_SAVE = 1,
@@ -183,8 +213,9 @@ typedef struct {
 /* Record: one adaptive solve per trajectory (summary, Methodology: record the
  * accepted steps; review, Summary: zero-padded fixed-length mesh).
  * u0 [d][n], p [P][n]; fills mesh->h (every chunk, padding included),
- * n_steps, save_idx and status, and, if y_save is not NULL, y_save [S][d][n]
- * with the state at each save time (NaN where not reached). */
+ * n_steps, save_idx, status and save_theta (when not NULL; required with
+ * dense output), and, if y_save is not NULL, y_save [S][d][n] with the state
+ * at each save time (NaN where not reached). */
 int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p,
               da_mesh *mesh, void *y_save, void *stream);
 
@@ -212,8 +243,9 @@ int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspa
 int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *stream);
 
 /* Fixed-step replay of the mesh (review, Summary: branch-free fixed-length
- * chain): y_save [S][d][n] at each save index; reproduces the record's
- * states bit for bit. */
+ * chain): y_save [S][d][n] at each save index (with dense output, the
+ * interpolant at the save's fraction); reproduces the record's saves bit for
+ * bit. */
 int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void *p,
                   const da_mesh *mesh, void *y_save, void *stream);
 

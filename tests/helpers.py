@@ -20,8 +20,11 @@ def mesh_to_host(mesh, N):
     problem's max_steps); the replay order, if any, is not part of it."""
     ns = mesh.n_steps.cpu().numpy()
     h = mesh.steps(N).cpu().numpy()
-    return {"h": h, "n_steps": ns, "save_idx": mesh.save_idx.cpu().numpy().T.copy(),
-            "status": mesh.status.cpu().numpy()}
+    out = {"h": h, "n_steps": ns, "save_idx": mesh.save_idx.cpu().numpy().T.copy(),
+           "status": mesh.status.cpu().numpy()}
+    if mesh.save_theta is not None:
+        out["save_theta"] = mesh.save_theta.cpu().numpy().T.copy()
+    return out
 
 
 def tile_steps(h_rows, max_steps, B):
@@ -37,10 +40,14 @@ def mesh_to_dev(m, max_steps, torch, dev="cuda"):
     import discrete_adjoint_amd as da
     B = 8 if m["h"].dtype == np.float64 else 16
     h = tile_steps(m["h"], max_steps, B)
+    th = None
+    if "save_theta" in m:
+        th = torch.from_numpy(np.ascontiguousarray(m["save_theta"].T)).to(dev)
     return da.Mesh(torch.from_numpy(h).to(dev),
                    torch.from_numpy(np.ascontiguousarray(m["n_steps"].astype(np.int32))).to(dev),
                    torch.from_numpy(np.ascontiguousarray(m["save_idx"].T.astype(np.int32))).to(dev),
-                   torch.from_numpy(np.ascontiguousarray(m["status"].astype(np.int32))).to(dev))
+                   torch.from_numpy(np.ascontiguousarray(m["status"].astype(np.int32))).to(dev),
+                   save_theta=th)
 
 
 def rel_err(g, ref):

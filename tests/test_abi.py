@@ -118,6 +118,31 @@ def test_null_pointers_rejected(da):
     assert "aligned" in da.last_error()
 
 
+def test_dense_output_checks(da):
+    """Dense output: flag 0/1, explicit methods on systems of dimension <= 3,
+    and the mesh must carry save_theta wherever a save is read."""
+    lib = da.library()
+    assert _call_record(da, W.WORKLOADS[1].problem(dense=2)) == -1
+    assert "dense" in da.last_error()
+    assert _call_record(da, W.WORKLOADS[4].problem(dense=1)) == -2
+    assert _call_record(da, W.WORKLOADS[5].problem(dense=1)) == -2
+    prob = W.WORKLOADS[3].problem(dense=1)
+    P, keep = da.cproblem(prob, __import__("torch").float32)
+    m = da._Mesh(64, 8, 8, 8, None)          # aligned fake addresses, no save_theta
+    args = (ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.byref(m))
+    assert lib.da_record(ctypes.byref(P), 4, *args, None, None) == -1
+    assert "save_theta" in da.last_error()
+    assert lib.da_replay_fwd(ctypes.byref(P), 4, *args, ctypes.c_void_p(8), None) == -1
+    assert "save_theta" in da.last_error()
+    loss = da._Loss(1, ctypes.c_void_p(8), 1.0)
+    assert lib.da_replay_grad(ctypes.byref(P), 4, *args, ctypes.byref(loss), None, None, None,
+                              10, ctypes.c_void_p(8), 1 << 20, None) == -1
+    assert "save_theta" in da.last_error()
+    assert lib.da_replay_sens(ctypes.byref(P), 4, *args, None, None, None, None,
+                              ctypes.c_void_p(8), None) == -1
+    assert "save_theta" in da.last_error()
+
+
 @pytest.mark.parametrize("ck", [3, 5, 16, -1])
 def test_bad_checkpoint_rejected(da, ck):
     prob = W.WORKLOADS[1].problem(checkpoint=ck)
