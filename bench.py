@@ -97,10 +97,12 @@ def kernel_source_hash(family: str = "erk") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str, family: str):
+def read_traffic(workload_name: str, family: str, dense: bool = False):
     """HBM bytes per gradient launch from the committed counter summary of the
-    workload, if it was taken with the current kernel sources."""
-    path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}_counters.md")
+    workload (its dense-output variant with `dense`), if it was taken with the
+    current kernel sources."""
+    sfx = "_dense" if dense else ""
+    path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}{sfx}_counters.md")
     if not os.path.exists(path):
         return None
     src_hash, traffic = None, None
@@ -112,7 +114,8 @@ def read_traffic(workload_name: str, family: str):
     return traffic if src_hash == kernel_source_hash(family) else None
 
 
-def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0):
+def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0,
+                 dense: int = 0):
     """Oracle as it stands, plain rounding, all OpenMP threads: record + passes
     on the first `lanes` trajectories of the workload."""
     import numpy as np
@@ -121,7 +124,7 @@ def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0):
     w = W.WORKLOADS[wid]
     lanes = min(lanes, w.n)
     inp = W.make_inputs(wid, lanes)
-    prob = w.problem()
+    prob = w.problem(dense=dense)
     cores = oracle.max_threads()
     aux, scale = None, 1.0
     if w.loss == W.MSE_SAVE:
@@ -170,6 +173,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-lanes", type=int, default=262144)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--dense", action="store_true",
+                    help="read the save times from the step interpolant (dense output) "
+                         "instead of landing steps on them")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU mode (trajectories "
@@ -186,7 +192,7 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
-    prob = w.problem(checkpoint=args.checkpoint)
+    prob = w.problem(checkpoint=args.checkpoint, dense=int(args.dense))
     n = w.n
     passes = w.passes
     dev = torch.device("cuda:0")
@@ -277,7 +283,7 @@ def main():
     flop_step = flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = read_traffic(w.name, kernel_family(mname, rname))
+    traffic = read_traffic(w.name, kernel_family(mname, rname), args.dense)
     out = {
         "metric": "trajectory-gradients/s (Lorenz FP64, 1M traj) + % of FP64 vector peak",
         "value": n * passes / (ms_per_step * 1e-3),
@@ -288,6 +294,7 @@ def main():
         "config": {"workload": w.name, "n": n, "method": mname, "rhs": rname, "dim": w.dim,
                    "t1": w.t1, "rtol": w.rtol, "atol": w.atol, "max_steps": w.max_steps,
                    "passes_per_record": passes, "checkpoint": args.checkpoint,
+                   "saves": "dense output" if args.dense else "steps land on save times",
                    "step": f"record + lane ordering and replay table + {passes} gradient "
                            f"pass{'es' if passes > 1 else ''}"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
@@ -308,7 +315,8 @@ def main():
                  "max_over_mean": state["N"] / mean_steps, "failed_lanes": int((st != 0).sum())},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes)
+        out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
+                                           dense=int(args.dense))
     print(json.dumps(out), flush=True)
 
 
