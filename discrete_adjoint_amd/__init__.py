@@ -45,7 +45,7 @@ MAX_SAVES = 128
 
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
-           "da_replay_sens", "da_last_error", "da_version")
+           "da_replay_sens", "da_rhs_register", "da_rhs_release", "da_last_error", "da_version")
 
 
 class DadjError(RuntimeError):
@@ -74,6 +74,11 @@ class _Mesh(ctypes.Structure):
                 ("rows", ctypes.c_int32), ("save_theta", ctypes.c_void_p)]
 
 
+class _RhsDef(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("n_params", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("method", ctypes.c_int32), ("f_body", ctypes.c_char_p)]
+
+
 class _Loss(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("aux", ctypes.c_void_p), ("scale", ctypes.c_double)]
 
@@ -100,9 +105,12 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp]
     lib.da_replay_sens.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, vp, vp]
+    lib.da_rhs_register.argtypes = [ctypes.POINTER(_RhsDef), ctypes.POINTER(ctypes.c_int32)]
+    lib.da_rhs_release.argtypes = [i32]
     lib.da_last_error.restype = ctypes.c_char_p
     for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps",
-                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_version"):
+                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_rhs_register",
+                 "da_rhs_release", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -125,6 +133,23 @@ def last_error() -> str:
 def _check(rc: int):
     if rc != DA_OK:
         raise DadjError(rc, last_error())
+
+
+def register_rhs(f_body: str, dim: int, n_params: int, dtype=torch.float64,
+                 method: int = 0) -> int:
+    """Compile the kernels for a right-hand side given as the C++ body of
+    ``template <class T> void f(const T *y, const T *p, T *dy)`` (see
+    da_rhs_register in include/dadj.h) for one dtype and explicit method
+    (0 = Tsit5, 1 = Dopri5).  Returns the rhs identifier for the problem."""
+    rid = ctypes.c_int32(0)
+    d = _RhsDef(dim, n_params, _dtype_code(dtype), method, f_body.encode())
+    _check(_lib.da_rhs_register(ctypes.byref(d), ctypes.byref(rid)))
+    return int(rid.value)
+
+
+def release_rhs(rhs_id: int) -> None:
+    """Unload the kernels of a registered right-hand side."""
+    _check(_lib.da_rhs_release(rhs_id))
 
 
 def _dtype_code(dt) -> int:

@@ -5,12 +5,14 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <string>
+
 #include "dadj.h"
 #include "dadj_internal.hpp"
 
 namespace {
 
-thread_local char g_err[512] = "";
+thread_local char g_err[4096] = "";
 
 int fail(int code, const char *fmt, ...) {
   va_list ap;
@@ -26,6 +28,8 @@ int ok() {
 }
 
 int hip_fail(hipError_t e, const char *what) {
+  const std::string rtc = dadj::rtc_take_error();  // a registered rhs that failed to compile
+  if (!rtc.empty()) return fail(DA_EHIP, "%s: %s", what, rtc.c_str());
   return fail(DA_EHIP, "%s: %s", what, hipGetErrorString(e));
 }
 
@@ -59,13 +63,19 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (pb->dtype != DA_F64 && pb->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", pb->dtype);
   if (pb->method < DA_TSIT5 || pb->method > DA_ROS2)
     return fail(DA_EINVAL, "bad method %d", pb->method);
-  if (pb->rhs < DA_RHS_LINEAR || pb->rhs > DA_RHS_LORENZ96)
-    return fail(DA_EINVAL, "bad rhs %d", pb->rhs);
-  if (!shape_ok(pb->rhs, pb->dim, pb->n_params))
-    return fail(DA_EINVAL, "rhs %d does not take dim=%d, n_params=%d", pb->rhs, pb->dim,
-                pb->n_params);
-  if (pb->rhs == DA_RHS_LORENZ96 && pb->method == DA_ROS2)
-    return fail(DA_EUNSUPPORTED, "ROS2 is available for systems of dimension <= 3 only");
+  if (pb->rhs >= DA_RHS_USER_BASE) {
+    std::string msg;
+    const int rc = dadj::rtc_check(*pb, msg);
+    if (rc) return fail(rc, "%s", msg.c_str());
+  } else {
+    if (pb->rhs < DA_RHS_LINEAR || pb->rhs > DA_RHS_LORENZ96)
+      return fail(DA_EINVAL, "bad rhs %d", pb->rhs);
+    if (!shape_ok(pb->rhs, pb->dim, pb->n_params))
+      return fail(DA_EINVAL, "rhs %d does not take dim=%d, n_params=%d", pb->rhs, pb->dim,
+                  pb->n_params);
+    if (pb->rhs == DA_RHS_LORENZ96 && pb->method == DA_ROS2)
+      return fail(DA_EUNSUPPORTED, "ROS2 is available for systems of dimension <= 3 only");
+  }
   if (!(isfinite(pb->t0) && isfinite(pb->t1) && pb->t1 > pb->t0))
     return fail(DA_EINVAL, "need finite t0 < t1");
   if (!(pb->rtol >= 0) || !(pb->atol >= 0) || !(pb->rtol + pb->atol > 0) || !isfinite(pb->rtol) ||
@@ -149,19 +159,24 @@ void fill_replay_args(dadj::ReplayArgs &a, const dadj::ProbArgs &pr, int64_t n, 
   a.theta = mesh->save_theta;
 }
 
+bool user_rhs(const dadj::ProbArgs &pr) { return pr.rhs >= DA_RHS_USER_BASE; }
+
 hipError_t launch_record(const dadj::RecordArgs &a, const dadj::SaveTimes &st, hipStream_t s) {
+  if (user_rhs(a.pr)) return dadj::launch_rtc_record(a, st, s);
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_record(a, st, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_record(a, st, s);
   return dadj::launch_erk_record(a, st, s);
 }
 
 hipError_t launch_replay_fwd(const dadj::ReplayArgs &a, hipStream_t s) {
+  if (user_rhs(a.pr)) return dadj::launch_rtc_replay_fwd(a, s);
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_fwd(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_fwd(a, s);
   return dadj::launch_erk_replay_fwd(a, s);
 }
 
 hipError_t launch_replay_grad(const dadj::ReplayArgs &a, hipStream_t s) {
+  if (user_rhs(a.pr)) return dadj::launch_rtc_replay_grad(a, s);
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_grad(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_grad(a, s);
   return dadj::launch_erk_replay_grad(a, s);
@@ -172,6 +187,28 @@ hipError_t launch_replay_grad(const dadj::ReplayArgs &a, hipStream_t s) {
 extern "C" {
 
 int da_version(void) { return 100; }
+
+int da_rhs_register(const da_rhs_def *def, int32_t *rhs_id) {
+  if (!def || !rhs_id) return fail(DA_EINVAL, "def and rhs_id must not be NULL");
+  if (def->dim < 1 || def->dim > 16) return fail(DA_EINVAL, "dim must be in [1, 16]");
+  if (def->n_params < 1 || def->n_params > 16)
+    return fail(DA_EINVAL, "n_params must be in [1, 16]");
+  if (def->dtype != DA_F64 && def->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", def->dtype);
+  if (def->method != DA_TSIT5 && def->method != DA_DOPRI5)
+    return fail(DA_EUNSUPPORTED, "registered right-hand sides run the explicit methods");
+  if (!def->f_body) return fail(DA_EINVAL, "f_body is NULL");
+  std::string msg;
+  const int rc = dadj::rtc_register(*def, rhs_id, msg);
+  if (rc) return fail(rc, "%s", msg.c_str());
+  return ok();
+}
+
+int da_rhs_release(int32_t rhs_id) {
+  std::string msg;
+  const int rc = dadj::rtc_release(rhs_id, msg);
+  if (rc) return fail(rc, "%s", msg.c_str());
+  return ok();
+}
 
 const char *da_last_error(void) { return g_err; }
 
@@ -398,7 +435,8 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
     a.gu0 = grad_u0;
     a.gp = grad_p;
   }
-  const hipError_t e = dadj::launch_erk_replay_sens(a, (hipStream_t)stream);
+  const hipError_t e = user_rhs(pr) ? dadj::launch_rtc_replay_sens(a, (hipStream_t)stream)
+                                    : dadj::launch_erk_replay_sens(a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "replay_sens launch");
   return ok();
 }

@@ -1,8 +1,12 @@
 // Host/device interface between the C ABI (api.hip) and the kernel files.
 #pragma once
 
+#ifndef __HIPCC_RTC__
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <string>
+#endif
 
 #include "dadj.h"
 
@@ -70,6 +74,7 @@ struct ReplayArgs {
   int32_t max_n_steps;
 };
 
+#ifndef __HIPCC_RTC__  // host side: launchers of the built-in kernels
 hipError_t launch_erk_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_erk_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_erk_replay_grad(const ReplayArgs &a, hipStream_t s);
@@ -90,5 +95,17 @@ hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
                                int32_t rows, hipStream_t s);
 size_t max_steps_scratch_ints();  // size of dev_out below
 hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s);
+
+// Right-hand sides compiled at run time (rtc.hip)
+int rtc_register(const da_rhs_def &def, int32_t *id, std::string &err);
+int rtc_release(int32_t id, std::string &err);
+int rtc_check(const da_problem &pb, std::string &err);
+std::string rtc_take_error();  // message of the last failed lazy compilation on this thread
+hipError_t launch_rtc_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
+hipError_t launch_rtc_replay_fwd(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_rtc_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_rtc_replay_sens(const ReplayArgs &a, hipStream_t s);
+
+#endif
 
 }  // namespace dadj

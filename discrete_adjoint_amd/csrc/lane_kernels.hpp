@@ -34,7 +34,9 @@
 // reverse sweep its checkpoint) while step k computes.
 #pragma once
 
+#ifndef __HIPCC_RTC__  // run-time compilation brings its own device math
 #include <math.h>
+#endif
 
 #include "dadj_device.hpp"
 #include "dadj_internal.hpp"
@@ -749,6 +751,7 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
+#ifndef __HIPCC_RTC__
 // Methods with dense output set M::dense_output; for the others the DENSE
 // kernels are not built and a dense problem is refused before launch.
 template <class T, class M, bool DENSE>
@@ -818,5 +821,7 @@ hipError_t replay_grad_t(const ReplayArgs &a, hipStream_t s) {
   }
   return replay_grad_d<T, M, false>(a, s);
 }
+
+#endif  // __HIPCC_RTC__
 
 }  // namespace dadj

@@ -7,156 +7,10 @@
 // of G, one group per grid row, so a group costs one replay of the state plus
 // G tangents.  Outputs: the sensitivity matrices at the save times and the
 // loss gradient by the chain rule through the tangents.
-#include "dual.hpp"
-#include "erk_method.hpp"
+#include "sens_kernel.hpp"
 
 namespace dadj {
 namespace {
-
-constexpr int SENS_G = 2;  // tangent directions per lane
-
-// Gradient terms seed . dy/dtheta_q in save-then-component order (first
-// product, then multiply-adds), the seeds being
-//   final-state loss: (2 scale) y_N    MSE: (2 scale) (y_s - aux_s)
-//   cotangent:        scale aux_s.
-// DENSE: a save with index k >= 1 (and its tangents) is the interpolant of
-// step k - 1 at the recorded fraction.
-template <class T, class M, int G, bool ROWS, bool DENSE>
-__global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
-  using Rhs = typename M::Rhs;
-  constexpr int D = Rhs::D, P = Rhs::P, Q = D + P;
-  using DT = DualN<T, G>;
-  const int64_t n = a.n;
-  const int64_t j = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
-  const bool live = j < n;
-  const int q0 = (int)blockIdx.y * G;
-  const int S = a.pr.S;
-  const int lk = a.loss_kind;
-  const bool saves = a.has_loss && lk != DA_LOSS_SUMSQ_FINAL;
-  const T *aux = (const T *)a.aux;
-  T *sens = (T *)a.sens;
-  const LaneInfo L = lane_info(a, j, live, a.pr.max_steps, true);
-  const int64_t tr = L.tr;
-  const int N = L.N;
-  const bool ok = L.ok;
-  StepSrc<T, ROWS> src;
-  src.init(a, live ? j : 0, tr);
-  DT y[D], p[P];
-  if (live) {
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      y[c] = DT(((const T *)a.u0)[c * n + tr]);
-#pragma unroll
-      for (int m = 0; m < G; ++m) y[c].d[m] = (q0 + m == c) ? T(1) : T(0);
-    }
-#pragma unroll
-    for (int r = 0; r < P; ++r) {
-      p[r] = DT(((const T *)a.p)[r * n + tr]);
-#pragma unroll
-      for (int m = 0; m < G; ++m) p[r].d[m] = (q0 + m == D + r) ? T(1) : T(0);
-    }
-    if (sens)
-      for (int s = 0; s < S; ++s) {
-        const int ix = a.sidx[s * n + tr];
-        if (!ok || ix < 0 || ix > N)
-#pragma unroll
-          for (int c = 0; c < D; ++c)
-#pragma unroll
-            for (int m = 0; m < G; ++m)
-              if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = nanv<T>();
-      }
-  }
-  const int Nw = wave_max(N);
-
-  T g[G], ss = T(0);
-#pragma unroll
-  for (int m = 0; m < G; ++m) g[m] = T(0);
-  bool gfirst = true, lfirst = true;
-  auto grad_terms = [&](T seed, const DT &yc) {
-#pragma unroll
-    for (int m = 0; m < G; ++m) g[m] = gfirst ? seed * yc.d[m] : mac(seed, yc.d[m], g[m]);
-    gfirst = false;
-  };
-  int s = 0;
-  int nxt = ok ? a.sidx[tr] : -1;
-  // save s has state (and tangents) ysv
-  auto emit = [&](const DT (&ysv)[D]) {
-    if (sens)
-#pragma unroll
-      for (int c = 0; c < D; ++c)
-#pragma unroll
-        for (int m = 0; m < G; ++m)
-          if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = ysv[c].d[m];
-    if (saves) {
-#pragma unroll
-      for (int c = 0; c < D; ++c) {
-        const T av = aux[((int64_t)s * D + c) * n + tr];
-        const T yv = ysv[c].v;
-        if (lk == DA_LOSS_MSE_SAVE) {
-          grad_terms(T(2.0 * a.scale) * (yv - av), ysv[c]);
-          const T r = yv - av;
-          ss = lfirst ? r * r : mac(r, r, ss);
-        } else {
-          grad_terms(T(a.scale) * av, ysv[c]);
-          ss = lfirst ? av * yv : mac(av, yv, ss);
-        }
-        lfirst = false;
-      }
-    }
-    ++s;
-    nxt = s < S ? a.sidx[s * n + tr] : -1;
-  };
-  auto at_saves = [&](int k) {
-    while (s < S && nxt == k) emit(y);
-  };
-  at_saves(0);
-  const T *theta = (const T *)a.theta;
-  auto step = [&](int k, T hk) {
-    if (k < N) {
-      if constexpr (DENSE) {
-        DT yp[D];
-#pragma unroll
-        for (int c = 0; c < D; ++c) yp[c] = y[c];
-        M::fwd(y, p, hk);
-        while (s < S && nxt == k + 1) {
-          DT ys[D];
-          dense_value<Rhs>(theta[(int64_t)s * n + tr], hk, yp, y, p, ys);
-          emit(ys);
-        }
-      } else {
-        M::fwd(y, p, hk);
-        at_saves(k + 1);
-      }
-    }
-  };
-  T hA = src.load(0);
-  for (int k = 0; k < Nw; k += 2) {
-    const T hB = src.load(k + 1);
-    step(k, hA);
-    hA = src.load(k + 2);
-    if (k + 1 < Nw) step(k + 1, hB);
-  }
-  if (a.has_loss && !saves) {
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      grad_terms(T(2.0 * a.scale) * y[c].v, y[c]);
-      ss = (c == 0) ? y[c].v * y[c].v : mac(y[c].v, y[c].v, ss);
-    }
-  }
-  if (live && a.has_loss) {
-#pragma unroll
-    for (int m = 0; m < G; ++m) {
-      const int q = q0 + m;
-      const T v = ok ? g[m] : nanv<T>();
-      if (q < D) {
-        if (a.gu0) ((T *)a.gu0)[q * n + tr] = v;
-      } else if (q < Q) {
-        if (a.gp) ((T *)a.gp)[(q - D) * n + tr] = v;
-      }
-    }
-    if (blockIdx.y == 0 && a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * ss : nanv<T>();
-  }
-}
 
 template <class T, class M, bool DENSE>
 hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {

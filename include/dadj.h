@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers unless marked "host"; all memory is
  *    owned by the caller.  The library allocates no device memory and keeps no
- *    state apart from a thread-local error message.
+ *    state apart from a thread-local error message and the code objects of
+ *    right-hand sides registered at run time (da_rhs_register).
  *  - Per-trajectory arrays are component-major: element (c, i) of an array
  *    with C components lives at index c * n + i (trajectory index fastest), so
  *    a wavefront reads and writes contiguous memory.
@@ -43,8 +44,15 @@
 #ifndef DADJ_H
 #define DADJ_H
 
+#ifndef __HIPCC_RTC__
 #include <stddef.h>
 #include <stdint.h>
+#else  /* run-time compilation of the kernels: the runtime's own integer types */
+typedef __hip_internal::int32_t int32_t;
+typedef __hip_internal::int64_t int64_t;
+typedef __hip_internal::uint32_t uint32_t;
+typedef __hip_internal::uint64_t uint64_t;
+#endif
 
 #ifdef __cplusplus
 extern "C" {
@@ -72,6 +80,10 @@ typedef enum {
   DA_RHS_ROBERTSON = 2,
   DA_RHS_LORENZ96 = 3
 } da_rhs;
+
+/* Identifiers of right-hand sides registered at run time (da_rhs_register)
+ * start here. */
+#define DA_RHS_USER_BASE 1024
 
 typedef enum {
   DA_OK = 0,
@@ -280,6 +292,38 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
 int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
                    const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
                    void *grad_p, void *sens, void *stream);
+
+/* Right-hand side compiled at run time ("GRADSOLVE", evolve.pub review, FAQ:
+ * registered right-hand sides of small dimension run in the fused kernels,
+ * hand-written or translated from the caller's function).  The caller gives
+ * f as C++ statements, the body of
+ *     template <class T> void f(const T *y, const T *p, T *dy)
+ * that set dy[0..dim) from y[0..dim) and p[0..n_params), for any number type
+ * T: use + - * /, constants (preferably written T(c)) and sqrt, exp, log,
+ * sin, cos, tanh, pow(x, c) with a real constant c.  The library compiles the
+ * record, forward solve, replay, replay-gradient and sensitivity kernels for
+ * it with hipRTC, for one dtype and one explicit method (DA_TSIT5 or
+ * DA_DOPRI5), and loads them on the current device.  The vector-Jacobian
+ * products of the reverse sweep come from forward-mode tangent numbers run
+ * through f (J_y^T v from the dim Jacobian columns, J_p^T v from the n_params
+ * columns).  Registration blocks for the compilation (seconds); a source that
+ * does not compile returns DA_EINVAL with the compiler's log in
+ * da_last_error().  On success *rhs_id (>= DA_RHS_USER_BASE) is the da_rhs
+ * value to put in da_problem.rhs, with the same dim, n_params, dtype and
+ * method, on the same device (DA_EINVAL / DA_EUNSUPPORTED otherwise).  Unlike
+ * the rest of the library, a registration is global state: its code object
+ * stays loaded until da_rhs_release.  Registration and release must not race
+ * with launches that use the same identifier. */
+typedef struct {
+  int32_t dim;         /* 1..16 */
+  int32_t n_params;    /* 1..16 */
+  int32_t dtype;       /* da_dtype */
+  int32_t method;      /* DA_TSIT5 or DA_DOPRI5 */
+  const char *f_body;  /* host string, NUL-terminated */
+} da_rhs_def;
+
+int da_rhs_register(const da_rhs_def *def, int32_t *rhs_id);
+int da_rhs_release(int32_t rhs_id);
 
 /* Message of the last non-zero return on this thread ("" if none). */
 const char *da_last_error(void);

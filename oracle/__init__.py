@@ -17,8 +17,10 @@ rounds each multiply and add separately.
 from __future__ import annotations
 
 import ctypes
+import hashlib
 import os
 import subprocess
+import tempfile
 from typing import Optional
 
 import numpy as np
@@ -102,6 +104,62 @@ def _sfx(dt):
     if dt == np.float32:
         return "f32"
     raise TypeError(f"unsupported dtype {dt}")
+
+
+_PLUGIN = r'''
+#include "user_types.h"
+namespace user {
+struct Src {
+  template <class T> static void f(const T *y, const T *p, T *dy) {
+#line 1 "rhs"
+%s
+  }
+};
+}  // namespace user
+typedef user::UDual<double, false> DP64;
+typedef user::UDual<double, true> DF64;
+typedef user::UDual<float, false> DP32;
+typedef user::UDual<float, true> DF32;
+extern "C" {
+#define ORC_USER_F(NAME, TYPE) \
+  void NAME(const TYPE *y, const TYPE *p, TYPE *o) { user::Src::f(y, p, o); }
+ORC_USER_F(orc_user_f64, double)
+ORC_USER_F(orc_user_f32, float)
+ORC_USER_F(orc_user_dp64, DP64)
+ORC_USER_F(orc_user_df64, DF64)
+ORC_USER_F(orc_user_dp32, DP32)
+ORC_USER_F(orc_user_df32, DF32)
+}
+'''
+_plugins = {}
+
+
+def set_user_rhs(f_body: str, dim: int, n_params: int) -> None:
+    """Make the caller's right-hand side (the body of
+    ``template <class T> void f(const T *y, const T *p, T *dy)``, the same
+    source the HIP library compiles) the oracle's right-hand side for every
+    problem whose rhs code is >= 1024.  It is built with g++ into a plugin
+    (cached by source) and evaluated on reals and dual numbers."""
+    key = hashlib.sha256(f"{dim} {n_params}\n{f_body}".encode()).hexdigest()[:16]
+    if key not in _plugins:
+        d = os.path.join(tempfile.gettempdir(), "dadj_oracle_rhs")
+        os.makedirs(d, exist_ok=True)
+        src = os.path.join(d, f"rhs_{key}.cpp")
+        lib = os.path.join(d, f"rhs_{key}.so")
+        if not os.path.exists(lib):
+            with open(src, "w") as f:
+                f.write(_PLUGIN % f_body)
+            tmp = lib + f".{os.getpid()}.tmp"
+            subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
+                            "-fPIC", "-shared", "-I", _HERE, "-o", tmp, src], check=True)
+            os.replace(tmp, lib)
+        _plugins[key] = ctypes.CDLL(lib)
+    pl = _plugins[key]
+    ptrs = [ctypes.cast(getattr(pl, n), ctypes.c_void_p)
+            for n in ("orc_user_f64", "orc_user_f32", "orc_user_dp64", "orc_user_df64",
+                      "orc_user_dp32", "orc_user_df32")]
+    _check(_load().orc_set_user_rhs(ctypes.c_int32(dim), ctypes.c_int32(n_params), *ptrs),
+           "set_user_rhs")
 
 
 def max_threads(nthreads: int = 0) -> int:

@@ -45,15 +45,19 @@
 #include <cstring>
 #include <limits>
 #include <omp.h>
+#include <type_traits>
 #include <vector>
+
+#include "user_types.h"
 
 namespace {
 
 constexpr int MAXD = 64;  // largest state dimension handled
-constexpr int MAXP = 3;   // largest parameter count
+constexpr int MAXP = 16;  // largest parameter count
 
 enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2 };
 enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3 };
+constexpr int R_USER = 1024;  /* kinds from here: the caller's right-hand side */
 enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
        S_MAX_ATTEMPTS = 4 };
 enum { L_SUMSQ_FINAL = 0, L_MSE_SAVE = 1, L_COTANGENT = 2 };
@@ -231,6 +235,108 @@ const Tableau DOPRI5 = make_dopri5();
 const double ROS2_GAMMA = 1.0 + 1.0 / std::sqrt(2.0);
 
 /* ------------------------------------------------------------------ */
+/* The caller's right-hand side                                         */
+/* ------------------------------------------------------------------ */
+/* f comes from a plugin built from the caller's source (user_types.h) and
+ * evaluated on reals and on dual numbers.  Its vector-Jacobian products are
+ * taken column by column, one dual pass per Jacobian column:
+ *   w_m = sum_i J[i][m] v_i                 (first product, then mac, i up)
+ *   g_q <- g_q + sum_i Jp[i][q] v_i         (mac into g_q, i up)
+ * Kinds >= R_USER all name the one right-hand side last set. */
+template <class S, bool F> using UD = user::UDual<S, F>;
+struct UserFns {
+  int dim = 0, np = 0;
+  void (*f64)(const double *, const double *, double *) = nullptr;
+  void (*f32)(const float *, const float *, float *) = nullptr;
+  void (*dp64)(const UD<double, false> *, const UD<double, false> *, UD<double, false> *) = nullptr;
+  void (*df64)(const UD<double, true> *, const UD<double, true> *, UD<double, true> *) = nullptr;
+  void (*dp32)(const UD<float, false> *, const UD<float, false> *, UD<float, false> *) = nullptr;
+  void (*df32)(const UD<float, true> *, const UD<float, true> *, UD<float, true> *) = nullptr;
+};
+UserFns g_user;
+
+inline void user_eval(const double *y, const double *p, double *o) { g_user.f64(y, p, o); }
+inline void user_eval(const float *y, const float *p, float *o) { g_user.f32(y, p, o); }
+inline void user_eval(const UD<double, false> *y, const UD<double, false> *p,
+                      UD<double, false> *o) { g_user.dp64(y, p, o); }
+inline void user_eval(const UD<double, true> *y, const UD<double, true> *p, UD<double, true> *o) {
+  g_user.df64(y, p, o);
+}
+inline void user_eval(const UD<float, false> *y, const UD<float, false> *p, UD<float, false> *o) {
+  g_user.dp32(y, p, o);
+}
+inline void user_eval(const UD<float, true> *y, const UD<float, true> *p, UD<float, true> *o) {
+  g_user.df32(y, p, o);
+}
+
+/* f on the oracle's own dual types (the JVP and sensitivity checks): through
+ * the plugin's dual type of the same rounding. */
+template <class DT, bool FU>
+void user_eval_dual(int d, const DT *y, const DT *p, DT *o) {
+  UD<double, FU> yu[MAXD], pu[MAXP], ou[MAXD];
+  for (int c = 0; c < d; ++c) yu[c] = UD<double, FU>(y[c].v, y[c].d);
+  for (int q = 0; q < g_user.np; ++q) pu[q] = UD<double, FU>(p[q].v, p[q].d);
+  user_eval(yu, pu, ou);
+  for (int c = 0; c < d; ++c) o[c] = DT(ou[c].v, ou[c].d);
+}
+
+template <class T, bool F>
+void user_f(int d, const T *y, const T *p, T *o);
+
+/* Jacobian columns of the caller's f at (y, p): Jy[i][m] for the states
+ * (wrt_p false) or Jp[i][q] for the parameters (wrt_p true). */
+template <class T, bool F>
+void user_jacobian(int d, const T *y, const T *p, bool wrt_p, T (*J)[MAXD > MAXP ? MAXD : MAXP]) {
+  using U = UD<T, F>;
+  const int ncol = wrt_p ? g_user.np : d;
+  for (int m = 0; m < ncol; ++m) {
+    U yd[MAXD], pd[MAXP], od[MAXD];
+    for (int c = 0; c < d; ++c) yd[c] = U(y[c], (!wrt_p && c == m) ? T(1) : T(0));
+    for (int q = 0; q < g_user.np; ++q) pd[q] = U(p[q], (wrt_p && q == m) ? T(1) : T(0));
+    user_eval(yd, pd, od);
+    for (int i = 0; i < d; ++i) J[i][m] = od[i].d;
+  }
+}
+
+template <class T, bool F>
+void user_vjp_y(int d, const T *y, const T *p, const T *v, T *w) {
+  if constexpr (std::is_same<T, double>::value || std::is_same<T, float>::value) {
+    T J[MAXD][MAXD > MAXP ? MAXD : MAXP];
+    user_jacobian<T, F>(d, y, p, false, J);
+    for (int m = 0; m < d; ++m) {
+      T acc = J[0][m] * v[0];
+      for (int i = 1; i < d; ++i) acc = mac<F>(J[i][m], v[i], acc);
+      w[m] = acc;
+    }
+  } else {
+    for (int m = 0; m < d; ++m) w[m] = T(NAN);
+  }
+}
+
+template <class T, bool F>
+void user_vjp_p_acc(int d, const T *y, const T *p, const T *v, T *g) {
+  if constexpr (std::is_same<T, double>::value || std::is_same<T, float>::value) {
+    T J[MAXD][MAXD > MAXP ? MAXD : MAXP];
+    user_jacobian<T, F>(d, y, p, true, J);
+    for (int q = 0; q < g_user.np; ++q)
+      for (int i = 0; i < d; ++i) g[q] = mac<F>(J[i][q], v[i], g[q]);
+  } else {
+    for (int q = 0; q < g_user.np; ++q) g[q] = T(NAN);
+  }
+}
+
+template <class T, bool F>
+void user_f(int d, const T *y, const T *p, T *o) {
+  if constexpr (std::is_same<T, double>::value || std::is_same<T, float>::value) {
+    user_eval(y, p, o);
+  } else if constexpr (std::is_same<T, DualF>::value) {
+    user_eval_dual<DualF, true>(d, y, p, o);
+  } else {
+    user_eval_dual<T, false>(d, y, p, o);
+  }
+}
+
+/* ------------------------------------------------------------------ */
 /* Right-hand sides: f, Jacobian, vector-Jacobian products             */
 /* ------------------------------------------------------------------ */
 /* Conventions:
@@ -242,6 +348,10 @@ const double ROS2_GAMMA = 1.0 + 1.0 / std::sqrt(2.0);
 
 template <class T, bool F>
 void rhs_f(int kind, int d, const T *y, const T *p, T *out) {
+  if (kind >= R_USER) {
+    user_f<T, F>(d, y, p, out);
+    return;
+  }
   switch (kind) {
     case R_LINEAR:  /* y' = p0 y */
       out[0] = p[0] * y[0];
@@ -306,6 +416,10 @@ void rhs_jac(int kind, int d, const T *y, const T *p, T *J) {
 
 template <class T, bool F>
 void rhs_vjp_y(int kind, int d, const T *y, const T *p, const T *v, T *w) {
+  if (kind >= R_USER) {
+    user_vjp_y<T, F>(d, y, p, v, w);
+    return;
+  }
   switch (kind) {
     case R_LINEAR:
       w[0] = p[0] * v[0];
@@ -352,6 +466,10 @@ void rhs_vjp_y(int kind, int d, const T *y, const T *p, const T *v, T *w) {
 
 template <class T, bool F>
 void rhs_vjp_p_acc(int kind, int d, const T *y, const T *p, const T *v, T *g) {
+  if (kind >= R_USER) {
+    user_vjp_p_acc<T, F>(d, y, p, v, g);
+    return;
+  }
   switch (kind) {
     case R_LINEAR:  /* df/dp0 = y */
       g[0] = mac<F>(y[0], v[0], g[0]);
@@ -431,6 +549,7 @@ void rhs_jac_contract_acc(int kind, int d, const T *y, const T *p, const T *Jb,
 }
 
 bool rhs_shape_ok(int kind, int d, int P) {
+  if (kind >= R_USER) return g_user.f64 && d == g_user.dim && P == g_user.np;
   switch (kind) {
     case R_LINEAR: return d == 1 && P == 1;
     case R_LORENZ63: return d == 3 && P == 3;
@@ -667,6 +786,7 @@ int validate(const orc_problem *P) {
   if (P->method == M_ROS2 && P->dim > 3) return E_UNSUPPORTED;
   if (P->dense != 0 && P->dense != 1) return E_INVAL;
   if (P->dense && P->method == M_ROS2) return E_UNSUPPORTED;
+  if (P->rhs >= R_USER && P->method == M_ROS2) return E_UNSUPPORTED;
   if (!(P->t1 > P->t0)) return E_INVAL;
   if (!(P->rtol >= 0) || !(P->atol >= 0) || !(P->rtol + P->atol > 0)) return E_INVAL;
   if (P->max_steps < 1) return E_INVAL;
@@ -1354,6 +1474,23 @@ int orc_tableau(int method, double *c, double *a, double *b, double *e, int32_t 
 }
 
 double orc_ros2_gamma(void) { return ROS2_GAMMA; }
+
+/* The caller's right-hand side from a plugin (see user_types.h): f on reals
+ * (double, float) and on dual numbers (plain and fused, double and float). */
+int orc_set_user_rhs(int32_t dim, int32_t n_params, void *f64, void *f32, void *dp64, void *df64,
+                     void *dp32, void *df32) {
+  if (dim < 1 || dim > MAXD || n_params < 1 || n_params > MAXP) return E_INVAL;
+  if (!f64 || !f32 || !dp64 || !df64 || !dp32 || !df32) return E_INVAL;
+  g_user.dim = dim;
+  g_user.np = n_params;
+  g_user.f64 = (decltype(g_user.f64))f64;
+  g_user.f32 = (decltype(g_user.f32))f32;
+  g_user.dp64 = (decltype(g_user.dp64))dp64;
+  g_user.df64 = (decltype(g_user.df64))df64;
+  g_user.dp32 = (decltype(g_user.dp32))dp32;
+  g_user.df32 = (decltype(g_user.df32))df32;
+  return E_OK;
+}
 
 int orc_max_threads(int nthreads) { return set_threads(nthreads); }
 

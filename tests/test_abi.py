@@ -143,6 +143,33 @@ def test_dense_output_checks(da):
     assert "save_theta" in da.last_error()
 
 
+def test_rhs_registration_checks(da):
+    """Argument checks of da_rhs_register, and compilation, which needs no
+    GPU: a source with an error is refused with the compiler's message; a
+    correct one compiles and then loads (or, without a device, says so)."""
+    import torch
+    lib = da.library()
+    rid = ctypes.c_int32(-1)
+    assert lib.da_rhs_register(None, ctypes.byref(rid)) == -1
+    good = "dy[0] = -p[0] * y[0];"
+    for dim, npar, dt, meth, body, code in [(0, 1, 0, 0, good, -1), (17, 1, 0, 0, good, -1),
+                                            (1, 0, 0, 0, good, -1), (1, 17, 0, 0, good, -1),
+                                            (1, 1, 5, 0, good, -1), (1, 1, 0, 2, good, -2),
+                                            (1, 1, 0, 0, None, -1)]:
+        d = da._RhsDef(dim, npar, dt, meth, None if body is None else body.encode())
+        assert lib.da_rhs_register(ctypes.byref(d), ctypes.byref(rid)) == code, (dim, npar, dt,
+                                                                                 meth)
+    with pytest.raises(da.DadjError) as e:
+        da.register_rhs("dy[0] = y[0] +;", 1, 1)
+    assert e.value.code == -1 and "expected expression" in str(e.value)
+    try:
+        got = da.register_rhs(good, 1, 1, torch.float64, 1)
+        da.release_rhs(got)
+    except da.DadjError as err:
+        assert err.code == -3 and "no current HIP device" in str(err)
+    assert lib.da_rhs_release(5) == -1
+
+
 @pytest.mark.parametrize("ck", [3, 5, 16, -1])
 def test_bad_checkpoint_rejected(da, ck):
     prob = W.WORKLOADS[1].problem(checkpoint=ck)

@@ -15,6 +15,7 @@ import pytest
 import workloads as W
 import test_oracle_dense as dense
 import test_oracle_pins as pins
+import test_oracle_user_rhs as user
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
                    "oracle.cpp")
@@ -57,6 +58,10 @@ MUTANTS = {
     "dense_bypass_not_added": ("for (int c = 0; c < d; ++c) lam[c] = lam[c] + mu[c];", ""),
     "dense_fraction_origin": ("const double th = (ts - t) / h;",
                               "const double th = (t_end - ts) / h;"),
+    "user_vjp_transposed": ("T acc = J[0][m] * v[0];\n      for (int i = 1; i < d; ++i) acc = mac<F>(J[i][m], v[i], acc);",
+                            "T acc = J[m][0] * v[0];\n      for (int i = 1; i < d; ++i) acc = mac<F>(J[m][i], v[i], acc);"),
+    "user_param_column": ("pd[q] = U(p[q], (wrt_p && q == m) ? T(1) : T(0));",
+                          "pd[q] = U(p[q], (wrt_p && q == 0) ? T(1) : T(0));"),
     "dense_save_in_next_step": ("out.sidx[j] = nacc;\n            if (out.theta) out.theta[j] = th;",
                                 "out.sidx[j] = nacc + 1;\n            if (out.theta) out.theta[j] = th;"),
 }
@@ -87,6 +92,10 @@ def _battery():
     for case in dense.DCASES:
         out.append((dense.test_dense_record_mesh_bookkeeping, dict(case=case)))
         out.append((dense.test_dense_adjoint_matches_dual_numbers, dict(case=case, fused=False)))
+    out += [(user.test_source_lorenz63_equals_builtin, {}),
+            (user.test_source_rhs_products_match_finite_differences, {}),
+            (user.test_source_adjoint_matches_duals_and_differences,
+             dict(src=user.ALLFN, dim=3, P=3, name="allfn", fused=False))]
     return out
 
 
@@ -108,7 +117,8 @@ def test_pins_catch_planted_mistake(orc, tmp_path, name):
     mutated.write_text(src.replace(old, new))
     lib = tmp_path / "liboracle_mutant.so"
     subprocess.run(["g++", "-O1", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-fPIC",
-                    "-shared", "-w", "-o", str(lib), str(mutated)], check=True)
+                    "-shared", "-w", "-I", os.path.dirname(SRC), "-o", str(lib), str(mutated)],
+                   check=True)
     try:
         orc._swap_library(str(lib))
         killer = _killed(orc)
