@@ -71,6 +71,15 @@ def flop_per_step(method: str, rhs: str, dim: int) -> int:
 
 
 COUNTERS_DIR = os.path.join(ROOT, "profiles")
+
+# Lorenz-63 written as the source of a run-time compiled right-hand side
+# (--rhs-source): the same system as the built-in one, with the
+# vector-Jacobian products taken by forward-mode tangents.
+LORENZ63_SOURCE = """
+    dy[0] = p[0] * (y[1] - y[0]);
+    dy[1] = y[0] * (p[1] - y[2]) - y[1];
+    dy[2] = y[0] * y[1] - p[2] * y[2];
+"""
 # Sources of the gradient kernel of each method family.
 KERNEL_SOURCES = {
     "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "erk_grad_f64_dopri5.hip",
@@ -173,6 +182,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-lanes", type=int, default=262144)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--rhs-source", action="store_true",
+                    help="Lorenz-63 workloads: run the system as a right-hand side compiled at "
+                         "run time from source instead of the built-in one")
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
@@ -193,6 +205,14 @@ def main():
 
     w = W.WORKLOADS[args.workload]
     prob = w.problem(checkpoint=args.checkpoint, dense=int(args.dense))
+    if args.rhs_source:
+        if w.rhs != W.LORENZ63:
+            sys.exit("--rhs-source is available for the Lorenz-63 workloads")
+        t_reg = time.perf_counter()
+        rid = da.register_rhs(LORENZ63_SOURCE, 3, 3, torch.float64 if w.dtype == "f64"
+                              else torch.float32, w.method)
+        t_reg = time.perf_counter() - t_reg
+        prob = prob.replace(rhs=rid)
     n = w.n
     passes = w.passes
     dev = torch.device("cuda:0")
@@ -283,7 +303,8 @@ def main():
     flop_step = flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    traffic = read_traffic(w.name, kernel_family(mname, rname), args.dense)
+    traffic = None if args.rhs_source else read_traffic(w.name, kernel_family(mname, rname),
+                                                          args.dense)
     out = {
         "metric": "trajectory-gradients/s (Lorenz FP64, 1M traj) + % of FP64 vector peak",
         "value": n * passes / (ms_per_step * 1e-3),
@@ -295,6 +316,8 @@ def main():
                    "t1": w.t1, "rtol": w.rtol, "atol": w.atol, "max_steps": w.max_steps,
                    "passes_per_record": passes, "checkpoint": args.checkpoint,
                    "saves": "dense output" if args.dense else "steps land on save times",
+                   "rhs_source": "compiled at run time from source, vector-Jacobian products by "
+                                 "forward-mode tangents" if args.rhs_source else "built in",
                    "step": f"record + lane ordering and replay table + {passes} gradient "
                            f"pass{'es' if passes > 1 else ''}"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
@@ -314,6 +337,8 @@ def main():
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],
                  "max_over_mean": state["N"] / mean_steps, "failed_lanes": int((st != 0).sum())},
     }
+    if args.rhs_source:
+        out["rhs_registration_s"] = t_reg
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
                                            dense=int(args.dense))

@@ -1,11 +1,13 @@
 // Right-hand sides compiled at run time from the caller's source (the
 // counterpart of registered right-hand sides: "GRADSOLVE" review, FAQ on
 // which systems run in the fused kernels).  The caller writes only f, as the
-// body of a function template over the number type T:
+// body of a function template that computes in the number type T:
 //
-//   template <class T> void f(const T *y, const T *p, T *dy)   // dy = f(y, p)
+//   template <class T, class TY, class TP>
+//   void f(const TY *y, const TP *p, T *dy)                    // dy = f(y, p)
 //
 // using + - * /, real constants (best written T(c)) and the functions below.
+// y and p hold numbers that convert to T (reals where no tangent is needed).
 // The kernels evaluate f on reals and, for the derivatives, on tangent numbers
 // (DualN): the vector-Jacobian products the reverse sweep needs are formed
 // from the Jacobian columns of one forward-mode pass.
@@ -155,30 +157,33 @@ __device__ __forceinline__ DualN<T, G> pow(const DualN<T, G> &x, double c) {
 
 // ---------------------------------------------------------------------------
 // A right-hand side from the caller's f: S provides D, P and
-// template <class T> f(y, p, dy).  The kernels' interface (f, vjp_y,
-// vjp_p_acc) follows, the products from the Jacobian columns:
+// template <class T, class TY, class TP> f(const TY *y, const TP *p, T *dy),
+// T being the type the body computes in (the caller's "T").  The kernels'
+// interface (f, vjp_y, vjp_p_acc) follows, the products from the Jacobian
+// columns:
 //   w_m = sum_i J[i][m] v_i          (first product, then fma, i ascending)
 //   g_q <- g_q + sum_i Jp[i][q] v_i  (fma into g_q, i ascending)
+// For J the parameters enter as reals, for Jp the states do: a tangent that
+// is zero throughout is left out instead of carried (for finite values the
+// result is the same as with zero tangents).
 // ---------------------------------------------------------------------------
 template <class S> struct AutoVjp {
   static constexpr int D = S::D, P = S::P;
 
   template <class T>
   __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
-    S::f(y, p, o);
+    S::template f<T, T, T>(y, p, o);
   }
 
   template <class T>
   __device__ static __forceinline__ void vjp_y(const T *y, const T *p, const T *v, T *w) {
-    DualN<T, D> yd[D], pd[P], od[D];
+    DualN<T, D> yd[D], od[D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       yd[c] = DualN<T, D>(y[c]);
       yd[c].d[c] = T(1);
     }
-#pragma unroll
-    for (int q = 0; q < P; ++q) pd[q] = DualN<T, D>(p[q]);
-    S::f(yd, pd, od);
+    S::template f<DualN<T, D>, DualN<T, D>, T>(yd, p, od);
 #pragma unroll
     for (int m = 0; m < D; ++m) {
       T acc = od[0].d[m] * v[0];
@@ -190,15 +195,13 @@ template <class S> struct AutoVjp {
 
   template <class T>
   __device__ static __forceinline__ void vjp_p_acc(const T *y, const T *p, const T *v, T *g) {
-    DualN<T, P> yd[D], pd[P], od[D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) yd[c] = DualN<T, P>(y[c]);
+    DualN<T, P> pd[P], od[D];
 #pragma unroll
     for (int q = 0; q < P; ++q) {
       pd[q] = DualN<T, P>(p[q]);
       pd[q].d[q] = T(1);
     }
-    S::f(yd, pd, od);
+    S::template f<DualN<T, P>, T, DualN<T, P>>(y, pd, od);
 #pragma unroll
     for (int q = 0; q < P; ++q) {
 #pragma unroll

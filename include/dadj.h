@@ -297,10 +297,14 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
  * registered right-hand sides of small dimension run in the fused kernels,
  * hand-written or translated from the caller's function).  The caller gives
  * f as C++ statements, the body of
- *     template <class T> void f(const T *y, const T *p, T *dy)
- * that set dy[0..dim) from y[0..dim) and p[0..n_params), for any number type
- * T: use + - * /, constants (preferably written T(c)) and sqrt, exp, log,
- * sin, cos, tanh, pow(x, c) with a real constant c.  The library compiles the
+ *     template <class T, class TY, class TP>
+ *     void f(const TY *y, const TP *p, T *dy)
+ * that set dy[0..dim) from y[0..dim) and p[0..n_params).  T is the number
+ * type to compute in (a real or a tangent number); y and p hold numbers
+ * that convert to T (for the derivatives, one of them holds plain reals), so
+ * declare intermediate values as T (or auto) and do not assume y[i] or p[q]
+ * is a T.  Use + - * /, constants (preferably written T(c)) and sqrt, exp,
+ * log, sin, cos, tanh, pow(x, c) with a real constant c.  The library compiles the
  * record, forward solve, replay, replay-gradient and sensitivity kernels for
  * it with hipRTC, for one dtype and one explicit method (DA_TSIT5 or
  * DA_DOPRI5), and loads them on the current device.  The vector-Jacobian
