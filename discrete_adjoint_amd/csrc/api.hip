@@ -101,8 +101,6 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (pb->dense != 0 && pb->dense != 1) return fail(DA_EINVAL, "dense must be 0 or 1");
   if (pb->dense && pb->method == DA_ROS2)
     return fail(DA_EUNSUPPORTED, "dense output is available for the explicit methods");
-  if (pb->dense && pb->rhs == DA_RHS_LORENZ96)
-    return fail(DA_EUNSUPPORTED, "dense output is not available for LORENZ96");
   pr.rhs = pb->rhs;
   pr.dim = pb->dim;
   pr.n_params = pb->n_params;

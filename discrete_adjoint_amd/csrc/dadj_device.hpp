@@ -270,4 +270,32 @@ __device__ __forceinline__ void erk_stages(const T (&y)[Rhs::D], const T *p, H h
   StageLoop<Tab, Rhs, 1, LAST, LASTK, T, H>::run(y, p, h, Y, K);
 }
 
+// ---------------------------------------------------------------------------
+// Dense output: weights of the cubic Hermite interpolant of an accepted step
+// at fraction th, {H00, H01, H10, H11} = {(1-th)^2 (1+2th), th^2 (3-2th),
+// th (1-th)^2, -th^2 (1-th)}, and the fraction of a save time in its step.
+// ---------------------------------------------------------------------------
+template <class T> struct HermiteW {
+  T h00, h01, h10, h11;
+};
+template <class T> __device__ __forceinline__ HermiteW<T> hermite_w(T th) {
+  const T u = T(1) - th;
+  const T u2 = u * u, t2 = th * th;
+  HermiteW<T> w;
+  w.h00 = u2 * mac(T(2), th, T(1));
+  w.h01 = t2 * mac(T(-2), th, T(3));
+  w.h10 = th * u2;
+  w.h11 = -(t2 * u);
+  return w;
+}
+
+// Fraction of the accepted step [t, t_end] of size h at which save time ts
+// lies (t < ts <= t_end): exactly 1 at the step's end, else (ts - t) / h in
+// double, capped at 1.
+__device__ __forceinline__ double step_fraction(double ts, double t, double t_end, double h) {
+  if (ts >= t_end) return 1.0;
+  const double th = (ts - t) / h;
+  return th < 1.0 ? th : 1.0;
+}
+
 }  // namespace dadj

@@ -8,44 +8,63 @@ namespace {
 using wave::WAVES;
 
 // FULL: the dimension fills the wavefront (neighbours by DPP rotations).
-template <class T, class M, bool FULL>
+template <class T, class M, bool FULL, bool DENSE>
 hipError_t wrecord_f(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
   const unsigned grid = (unsigned)((a.n + WAVES - 1) / WAVES);
-  if (a.h) hipLaunchKernelGGL((wave::k_wrecord<T, M, true, FULL>), grid, 64 * WAVES, 0, s, a, st);
-  else hipLaunchKernelGGL((wave::k_wrecord<T, M, false, FULL>), grid, 64 * WAVES, 0, s, a, st);
+  if (a.h)
+    hipLaunchKernelGGL((wave::k_wrecord<T, M, true, FULL, DENSE>), grid, 64 * WAVES, 0, s, a, st);
+  else
+    hipLaunchKernelGGL((wave::k_wrecord<T, M, false, FULL, DENSE>), grid, 64 * WAVES, 0, s, a, st);
   return hipGetLastError();
+}
+template <class T, class M, bool DENSE>
+hipError_t wrecord_d(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
+  return a.pr.dim == 64 ? wrecord_f<T, M, true, DENSE>(a, st, s)
+                        : wrecord_f<T, M, false, DENSE>(a, st, s);
 }
 template <class T, class M>
 hipError_t wrecord_t(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
-  return a.pr.dim == 64 ? wrecord_f<T, M, true>(a, st, s) : wrecord_f<T, M, false>(a, st, s);
+  return a.pr.dense ? wrecord_d<T, M, true>(a, st, s) : wrecord_d<T, M, false>(a, st, s);
 }
 
-template <class T, class M, bool FULL>
+template <class T, class M, bool FULL, bool DENSE>
 hipError_t wreplay_fwd_f(const ReplayArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.n + WAVES - 1) / WAVES);
-  hipLaunchKernelGGL((wave::k_wreplay_fwd<T, M, FULL>), grid, 64 * WAVES, 0, s, a);
+  hipLaunchKernelGGL((wave::k_wreplay_fwd<T, M, FULL, DENSE>), grid, 64 * WAVES, 0, s, a);
   return hipGetLastError();
+}
+template <class T, class M, bool DENSE>
+hipError_t wreplay_fwd_d(const ReplayArgs &a, hipStream_t s) {
+  return a.pr.dim == 64 ? wreplay_fwd_f<T, M, true, DENSE>(a, s)
+                        : wreplay_fwd_f<T, M, false, DENSE>(a, s);
 }
 template <class T, class M>
 hipError_t wreplay_fwd_t(const ReplayArgs &a, hipStream_t s) {
-  return a.pr.dim == 64 ? wreplay_fwd_f<T, M, true>(a, s) : wreplay_fwd_f<T, M, false>(a, s);
+  return a.pr.dense ? wreplay_fwd_d<T, M, true>(a, s) : wreplay_fwd_d<T, M, false>(a, s);
 }
 
-template <class T, class M, bool FULL>
+template <class T, class M, bool FULL, bool DENSE>
 hipError_t wreplay_grad_f(const ReplayArgs &a, hipStream_t s) {
   const unsigned grid = (unsigned)((a.nslots + WAVES - 1) / WAVES);
   switch (a.pr.checkpoint) {
-    case 1: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 1, FULL>), grid, 64 * WAVES, 0, s, a); break;
-    case 2: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 2, FULL>), grid, 64 * WAVES, 0, s, a); break;
-    case 4: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 4, FULL>), grid, 64 * WAVES, 0, s, a); break;
-    case 8: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 8, FULL>), grid, 64 * WAVES, 0, s, a); break;
+    case 1: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 1, FULL, DENSE>), grid, 64 * WAVES, 0, s, a); break;
+    case 2: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 2, FULL, DENSE>), grid, 64 * WAVES, 0, s, a); break;
+    case 4: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 4, FULL, DENSE>), grid, 64 * WAVES, 0, s, a); break;
+    case 8: hipLaunchKernelGGL((wave::k_wreplay_grad<T, M, 8, FULL, DENSE>), grid, 64 * WAVES, 0, s, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+template <class T, class M, bool DENSE>
+hipError_t wreplay_grad_d(const ReplayArgs &a, hipStream_t s) {
+  return a.pr.dim == 64 ? wreplay_grad_f<T, M, true, DENSE>(a, s)
+                        : wreplay_grad_f<T, M, false, DENSE>(a, s);
+}
+// The final-state loss reads no save: a dense problem runs the plain kernel.
 template <class T, class M>
 hipError_t wreplay_grad_t(const ReplayArgs &a, hipStream_t s) {
-  return a.pr.dim == 64 ? wreplay_grad_f<T, M, true>(a, s) : wreplay_grad_f<T, M, false>(a, s);
+  const bool dense = a.pr.dense && a.loss_kind != DA_LOSS_SUMSQ_FINAL;
+  return dense ? wreplay_grad_d<T, M, true>(a, s) : wreplay_grad_d<T, M, false>(a, s);
 }
 
 #define DADJ_L96_DISPATCH(FN, ARGS)                                                    \

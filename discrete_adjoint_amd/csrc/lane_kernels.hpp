@@ -117,20 +117,6 @@ __device__ __forceinline__ T err_norm(const T (&err)[D], const T (&y)[D], const 
 //   H00 = (1-th)^2 (1+2th), H01 = th^2 (3-2th), H10 = th (1-th)^2,
 //   H11 = -th^2 (1-th);  th = 1 gives y_{k+1} exactly.
 // ---------------------------------------------------------------------------
-template <class T> struct HermiteW {
-  T h00, h01, h10, h11;
-};
-template <class T> __device__ __forceinline__ HermiteW<T> hermite_w(T th) {
-  const T u = T(1) - th;
-  const T u2 = u * u, t2 = th * th;
-  HermiteW<T> w;
-  w.h00 = u2 * mac(T(2), th, T(1));
-  w.h01 = t2 * mac(T(-2), th, T(3));
-  w.h10 = th * u2;
-  w.h11 = -(t2 * u);
-  return w;
-}
-
 // Interpolated state at fraction th of the step of size h from y0 to y1.  V
 // is the value type (a real, or a tangent type whose weights and step carry
 // no tangent), T the real type of th and h.
@@ -149,15 +135,6 @@ __device__ __forceinline__ void dense_value(T th, T h, const V (&y0)[Rhs::D],
     const V sl = mac(w11, f1[c], w10 * f0[c]);
     out[c] = mac(hv, sl, mac(w01, y1[c], w00 * y0[c]));
   }
-}
-
-// Fraction of the accepted step [t, t_end] of size h at which save time ts
-// lies (t < ts <= t_end): exactly 1 at the step's end, else (ts - t) / h in
-// double, capped at 1.
-__device__ __forceinline__ double step_fraction(double ts, double t, double t_end, double h) {
-  if (ts >= t_end) return 1.0;
-  const double th = (ts - t) / h;
-  return th < 1.0 ? th : 1.0;
 }
 
 // Starting step of Hairer, Norsett, Wanner I, section II.4, method order q.

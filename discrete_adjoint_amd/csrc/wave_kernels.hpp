@@ -12,6 +12,9 @@
 //  k_wrecord<T, M, LOG>        adaptive solve (record / forward-only solve)
 //  k_wreplay_fwd<T, M>         fixed-step replay
 //  k_wreplay_grad<T, M, CK>    replay + reverse sweep, mesh held fixed
+// each also with DENSE: save times read from the cubic Hermite interpolant of
+// the accepted step that holds them, per component (lane_kernels.hpp gives
+// the interpolant); whether a step holds a save is the same for all lanes.
 //
 // A method M provides, per lane (component) with a Nbr context for the
 // neighbours: fwd(x, F, h), attempt(x, F, h, k0, xnew, err) and
@@ -227,6 +230,16 @@ struct WErk {
   }
 };
 
+// Dense output, per component: the interpolant at fraction th of the step of
+// size h from x0 to x1, h (H11 f(x1) + H10 f(x0)) + (H01 x1 + H00 x0).
+template <class Rhs, class T, class NB>
+__device__ __forceinline__ T wdense_value(T th, T h, T x0, T x1, T F, const NB &nb) {
+  const HermiteW<T> w = hermite_w(th);
+  const T f0 = Rhs::f(x0, F, nb), f1 = Rhs::f(x1, F, nb);
+  const T sl = mac(w.h11, f1, w.h10 * f0);
+  return mac(h, sl, mac(w.h01, x1, w.h00 * x0));
+}
+
 template <class T> __device__ __forceinline__ T wmax(T a, T b) { return (a < b) ? b : a; }
 template <class T> __device__ __forceinline__ T wmin(T a, T b) { return (b < a) ? b : a; }
 __device__ __forceinline__ double wpow(double a, double b) { return pow(a, b); }
@@ -266,7 +279,7 @@ template <class T> struct WLog {
 // the wavefront holds step b of the current chunk of the step log; a full
 // chunk is written by lanes 0..B-1 as one 64-byte store.
 // ---------------------------------------------------------------------------
-template <class T, class M, bool LOG, bool FULL>
+template <class T, class M, bool LOG, bool FULL, bool DENSE>
 __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
   constexpr int B = WLog<T>::B;
@@ -288,11 +301,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   const T safety = T(pr.safety), fmin = T(pr.fac_min), fmax = T(pr.fac_max);
   T *H = (T *)a.h;
   T *ysave = (T *)a.y_save;
+  T *theta = (T *)a.theta;
 
   T x = on ? ((const T *)a.u0)[c * n + i] : T(0);
   const T F = uniform(((const T *)a.p)[i]);
   for (int s = 0; s < S; ++s) {
     if (a.sidx && c == 0) a.sidx[s * n + i] = -1;
+    if (theta && c == 0) theta[s * n + i] = nanv<T>();
     if (ysave && on) ysave[(s * d + c) * n + i] = nanv<T>();
   }
   int nacc = 0, natt = 0, st = LANE_OK;
@@ -322,7 +337,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
     int js = 0;
     bool after_reject = false;
     for (;;) {
-      const double t_stop = (has_saves && js < S) ? stimes.t[js] : pr.t1;
+      const double t_stop = (!DENSE && has_saves && js < S) ? stimes.t[js] : pr.t1;
       const T rem = T(t_stop - t);
       const bool land = !(h < rem);
       const T hs = land ? rem : h;
@@ -346,16 +361,37 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
           }
         }
         ++nacc;
+        const double t_new = land ? t_stop : t + double(hs);
+        if constexpr (DENSE) {  // the save times inside this step
+          for (; has_saves && js < S && stimes.t[js] <= t_new; ++js) {
+            const T th = T(step_fraction(stimes.t[js], t, t_new, double(hs)));
+            if (a.sidx && c == 0) a.sidx[js * n + i] = nacc;
+            if (theta && c == 0) theta[js * n + i] = th;
+            if (ysave) {
+              const T v = wdense_value<Rhs>(th, hs, x, xn, F, nb);
+              if (on) ysave[(js * d + c) * n + i] = v;
+            }
+          }
+        }
         x = xn;
         K[0] = Kt[6];
-        t = land ? t_stop : t + double(hs);
+        t = t_new;
         T fac = (E == T(0)) ? fmax : wmin(fmax, wmax(fmin, safety * wpow(E, expo)));
         if (after_reject) fac = wmin(fac, T(1));
         h = uniform(hs * fac);
         after_reject = false;
+        if (DENSE && land) {
+          if (!has_saves) {  // the final state is the one save
+            if (a.sidx && c == 0) a.sidx[i] = nacc;
+            if (theta && c == 0) theta[i] = T(1);
+            if (ysave && on) ysave[c * n + i] = x;
+          }
+          break;
+        }
         if (land) {
           if (js < S) {
             if (a.sidx && c == 0) a.sidx[js * n + i] = nacc;
+            if (theta && c == 0) theta[js * n + i] = T(1);
             if (ysave && on) ysave[(js * d + c) * n + i] = x;
           }
           if (++js == n_stops) break;
@@ -418,8 +454,9 @@ template <class T> struct WSteps {
 // ---------------------------------------------------------------------------
 // Replay forward
 // ---------------------------------------------------------------------------
-template <class T, class M, bool FULL>
+template <class T, class M, bool FULL, bool DENSE>
 __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
+  using Rhs = typename M::Rhs;
   const int64_t n = a.n;
   const WaveId w = wave_id(n);
   if (!w.live) return;
@@ -446,13 +483,20 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
   }
   int s = 0;
   int nxt = ok ? uniform(a.sidx[tr]) : -1;
+  T xp = x, hp = T(0);  // DENSE: the state before the last step, and its size
   for (int k = 0; k <= N; ++k) {
     while (s < S && nxt == k) {
-      if (on) ysave[(s * d + c) * n + tr] = x;
+      T v = x;
+      if (DENSE && k > 0) v = wdense_value<Rhs>(((const T *)a.theta)[s * n + tr], hp, xp, x, F, nb);
+      if (on) ysave[(s * d + c) * n + tr] = v;
       ++s;
       nxt = s < S ? uniform(a.sidx[s * n + tr]) : -1;
     }
-    if (k < N) x = M::fwd(x, F, src.load(k), nb);
+    if (k < N) {
+      hp = src.load(k);
+      if (DENSE) xp = x;
+      x = M::fwd(x, F, hp, nb);
+    }
   }
 }
 
@@ -461,8 +505,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
 // 64-component row ws[(m * ws_lanes + jl) * 64 + c] (one contiguous 512-byte
 // store per wavefront in FP64).
 // ---------------------------------------------------------------------------
-template <class T, class M, int CK, bool FULL>
+template <class T, class M, int CK, bool FULL, bool DENSE>
 __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
+  using Rhs = typename M::Rhs;
   const int64_t n = a.n;
   const WaveId w = wave_id(a.nslots);
   if (!w.live) return;
@@ -490,19 +535,23 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   const T F = uniform(((const T *)a.p)[tr]);
 
   // ---- forward replay, checkpoints, loss terms ----
+  const T *theta = (const T *)a.theta;
   T ss = T(0);   // this lane's share of the loss
   bool first = true;
   int s = 0;
   int nxt = (ok && saves) ? uniform(a.sidx[tr]) : -1;
-  auto terms = [&](int k) {
+  // saves with index k; DENSE (k >= 1): interpolated in the step from xp (size hk)
+  auto terms = [&](int k, T xp, T hk) {
     while (s < S && nxt == k) {
+      T xv = x;
+      if (DENSE && k > 0) xv = wdense_value<Rhs>(theta[(int64_t)s * n + tr], hk, xp, x, F, nb);
       if (on) {
         const T av = aux[((int64_t)s * d + c) * n + tr];
         if (lk == DA_LOSS_MSE_SAVE) {
-          const T r = x - av;
+          const T r = xv - av;
           ss = first ? r * r : mac(r, r, ss);
         } else {
-          ss = first ? av * x : mac(av, x, ss);
+          ss = first ? av * xv : mac(av, xv, ss);
         }
       }
       first = false;
@@ -510,13 +559,14 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
       nxt = s < S ? uniform(a.sidx[s * n + tr]) : -1;
     }
   };
-  if (saves) terms(0);
+  if (saves) terms(0, x, T(0));
   T hcur = src.load(0);
   for (int k = 0; k < N; ++k) {
     const T hnext = src.load(k + 1);
     if (k % CK == 0) ws[(int64_t)(k / CK) * C * 64] = x;
+    const T xp = x;
     x = M::fwd(x, F, hcur, nb);
-    if (saves) terms(k + 1);
+    if (saves) terms(k + 1, xp, hcur);
     hcur = hnext;
   }
 
@@ -539,7 +589,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
       hidx = sh >= 0 ? uniform(a.sidx[(int64_t)sh * n + tr]) : -1;
     }
   };
-  if (saves) seeds(N, x);
+  if (saves && !DENSE) seeds(N, x);
+  T xhi = x;  // DENSE: x_{k+1} while step k is reversed
 
   // ---- reverse sweep by segments of CK steps ----
   const int Mw = (N + CK - 1) / CK;
@@ -555,8 +606,40 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
     for (int b = CK - 1; b >= 0; --b) {
       const int k = m * CK + b;
       if (k < N) {
-        M::adj(xs[b], F, hs[b], nb, lam, gF);
-        if (saves) seeds(k, xs[b]);
+        if constexpr (DENSE) {
+          // saves inside step k, the last first: lam (dL/dx_{k+1}) now, mu
+          // (the part of dL/dx_k that bypasses the step) after its reverse;
+          // this lane's share of dL/dF gets v1, then v0
+          T mu = T(0);
+          bool has_mu = false;
+          while (sh >= 0 && hidx == k + 1) {
+            const T th = theta[(int64_t)sh * n + tr];
+            const T xv = wdense_value<Rhs>(th, hs[b], xs[b], xhi, F, nb);
+            T sb = T(0);
+            if (on) {
+              const T av = aux[((int64_t)sh * d + c) * n + tr];
+              if (lk == DA_LOSS_MSE_SAVE) sb = mac(T(2.0 * a.scale), xv - av, sb);
+              else sb = mac(T(a.scale), av, sb);
+            }
+            const HermiteW<T> w = hermite_w(th);
+            const T v1 = (hs[b] * w.h11) * sb, v0 = (hs[b] * w.h10) * sb;
+            const T w1 = Rhs::vjp_y(xhi, v1, nb), w0 = Rhs::vjp_y(xs[b], v0, nb);
+            lam = mac(w.h01, sb, lam) + w1;
+            mu = mac(w.h00, sb, mu) + w0;
+            gF = gF + v1;
+            gF = gF + v0;
+            has_mu = true;
+            --sh;
+            hidx = sh >= 0 ? uniform(a.sidx[(int64_t)sh * n + tr]) : -1;
+          }
+          M::adj(xs[b], F, hs[b], nb, lam, gF);
+          if (has_mu) lam = lam + mu;
+          if (saves && k == 0) seeds(0, xs[b]);
+          xhi = xs[b];
+        } else {
+          M::adj(xs[b], F, hs[b], nb, lam, gF);
+          if (saves) seeds(k, xs[b]);
+        }
       }
     }
   }

@@ -119,13 +119,12 @@ def test_null_pointers_rejected(da):
 
 
 def test_dense_output_checks(da):
-    """Dense output: flag 0/1, explicit methods on systems of dimension <= 3,
-    and the mesh must carry save_theta wherever a save is read."""
+    """Dense output: flag 0/1, explicit methods only, and the mesh must carry
+    save_theta wherever a save is read."""
     lib = da.library()
     assert _call_record(da, W.WORKLOADS[1].problem(dense=2)) == -1
     assert "dense" in da.last_error()
     assert _call_record(da, W.WORKLOADS[4].problem(dense=1)) == -2
-    assert _call_record(da, W.WORKLOADS[5].problem(dense=1)) == -2
     prob = W.WORKLOADS[3].problem(dense=1)
     P, keep = da.cproblem(prob, __import__("torch").float32)
     m = da._Mesh(64, 8, 8, 8, None)          # aligned fake addresses, no save_theta

@@ -43,6 +43,10 @@ CASES = [
     # many saves per step: 40 save times inside [0.5, 0.52] and one at t1
     ("l63_tsit5_crowded", 1, dict(save_times=tuple(np.linspace(0.5, 0.52, 40)) + (1.0,)),
      W.COTANGENT, 260),
+    # Lorenz-96 on the wavefront kernels: d = 64 (DPP neighbours) and d = 40
+    ("l96_tsit5_cot", 5, dict(t1=0.5, save_times=(0.1, 0.23, 0.4)), W.COTANGENT, 200),
+    ("l96_d40_dopri5_mse", 5, dict(dim=40, method=W.DOPRI5, t1=0.5,
+                                   save_times=(0.05, 0.3, 0.5)), W.MSE_SAVE, 150),
 ]
 
 
@@ -58,7 +62,7 @@ def _case(orc, wid, kw, lk, n):
         w = W.WORKLOADS[wid]
         prob = w.problem(dense=1, **kw)
         inp = W.make_inputs(wid, n)
-        u0, p = inp["u0"], inp["p"]
+        u0, p = np.ascontiguousarray(inp["u0"][:, :prob.dim]), inp["p"]
         dt = w.np_dtype
     S, d = prob.n_save_eff, prob.dim
     if lk == W.MSE_SAVE and wid == 3:
@@ -94,7 +98,15 @@ def test_dense_on_oracle_mesh(da, orc, name, wid, kw, lk, n):
     el = np.abs(loss.cpu().numpy() - lo) / np.abs(lo)
     _print(f"  saves max rel {ey.max():.3e} (bitwise lanes {np.mean(ey == 0):.3f}), "
            f"grad max rel {eg.max():.3e}, loss max rel {el.max():.3e}")
-    assert ey.max() <= tol and eg.max() <= tol and el.max() <= tol
+    assert ey.max() <= tol and eg.max() <= tol
+    if prob.rhs == W.LORENZ96:
+        # the wavefront adds the loss over components pairwise, the oracle in
+        # sequence: both within 4 d eps of the sum of |terms|
+        mag = scale * (np.abs(yo * aux).sum((1, 2)) if lk == W.COTANGENT
+                       else ((yo - aux) ** 2).sum((1, 2)))
+        assert np.all(np.abs(loss.cpu().numpy() - lo) <= 4 * prob.dim * 2.3e-16 * mag)
+    else:
+        assert el.max() <= tol
     ref = (gu0.clone(), gp.clone())
     for ck in (2, 4, 8):
         l2, g2, q2 = da.replay_grad(prob.replace(checkpoint=ck), u0, p, mesh, lk, aux=auxd,
