@@ -270,6 +270,14 @@ __device__ __forceinline__ void erk_stages(const T (&y)[Rhs::D], const T *p, H h
   StageLoop<Tab, Rhs, 1, LAST, LASTK, T, H>::run(y, p, h, Y, K);
 }
 
+// Power E^expo of the step-size controller, in single precision: the factor
+// only scales the next trial step (the accept test E <= 1 stays in the
+// state's precision), and the double-precision power would cost about as
+// much as the rest of a trial step.
+template <class T> __device__ __forceinline__ T ctrl_pow(T E, T expo) {
+  return T(exp2f(float(expo) * log2f(float(E))));
+}
+
 // ---------------------------------------------------------------------------
 // Dense output: weights of the cubic Hermite interpolant of an accepted step
 // at fraction th, {H00, H01, H10, H11} = {(1-th)^2 (1+2th), th^2 (3-2th),

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
           for (int c = 0; c < D; ++c) y[c] = ynew[c];
           M::accepted(cache);
           t = t_new;
-          T fac = (E == T(0)) ? fmax : dmin(fmax, dmax(fmin, safety * dpow(E, expo)));
+          T fac = (E == T(0)) ? fmax : dmin(fmax, dmax(fmin, safety * ctrl_pow(E, expo)));
           if (after_reject) fac = dmin(fac, T(1));
           h = hs * fac;
           after_reject = false;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
             if (++js == n_stops) break;
           }
         } else {
-          const T fac = finite(E) ? dmax(fmin, safety * dpow(E, expo)) : fmin;
+          const T fac = finite(E) ? dmax(fmin, safety * ctrl_pow(E, expo)) : fmin;
           h = hs * fac;
           after_reject = true;
         }

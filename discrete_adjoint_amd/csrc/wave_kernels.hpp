@@ -376,7 +376,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
         x = xn;
         K[0] = Kt[6];
         t = t_new;
-        T fac = (E == T(0)) ? fmax : wmin(fmax, wmax(fmin, safety * wpow(E, expo)));
+        T fac = (E == T(0)) ? fmax : wmin(fmax, wmax(fmin, safety * ctrl_pow(E, expo)));
         if (after_reject) fac = wmin(fac, T(1));
         h = uniform(hs * fac);
         after_reject = false;
@@ -397,7 +397,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
           if (++js == n_stops) break;
         }
       } else {
-        const T fac = finite(E) ? wmax(fmin, safety * wpow(E, expo)) : fmin;
+        const T fac = finite(E) ? wmax(fmin, safety * ctrl_pow(E, expo)) : fmin;
         h = uniform(hs * fac);
         after_reject = true;
       }

@@ -822,6 +822,13 @@ T err_norm(int d, const T *err, const T *y, const T *yn, T atol, T rtol) {
   return rms<T, F>(d, err, sc);
 }
 
+/* The controller's power E^expo, in single precision: exp2(expo log2 E) with
+ * E and expo rounded to float (it only scales the next trial step). */
+template <class T>
+T ctrl_pow(T E, T expo) {
+  return T(std::exp2(float(expo) * std::log2(float(E))));
+}
+
 /* Starting step (HNW I, II.4) for a method of order q. */
 template <class T, bool F>
 T initial_step(int kind, int d, const T *y0, const T *f0, const T *p, T atol, T rtol,
@@ -994,7 +1001,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
           for (int c = 0; c < d; ++c) K[0][c] = K[6][c];  /* first same as last */
         t = t_new;
         T fac = (E == T(0.0)) ? fmax
-                              : std::min(fmax, std::max(fmin, safety * std::pow(E, expo)));
+                              : std::min(fmax, std::max(fmin, safety * ctrl_pow(E, expo)));
         if (after_reject) fac = std::min(fac, T(1.0));
         h = hs * fac;
         after_reject = false;
@@ -1017,7 +1024,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
           if (++j == n_stops) break;
         }
       } else {
-        const T fac = fin(E) ? std::max(fmin, safety * std::pow(E, expo)) : fmin;
+        const T fac = fin(E) ? std::max(fmin, safety * ctrl_pow(E, expo)) : fmin;
         h = hs * fac;
         after_reject = true;
       }
