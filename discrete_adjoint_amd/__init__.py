@@ -44,6 +44,7 @@ DA_OK, DA_EINVAL, DA_EUNSUPPORTED, DA_EHIP, DA_EWORKSPACE = 0, -1, -2, -3, -4
 MAX_SAVES = 128
 
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
+           "da_mesh_pad",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
            "da_replay_sens", "da_rhs_register", "da_rhs_release", "da_last_error", "da_version")
 
@@ -71,7 +72,8 @@ class _Mesh(ctypes.Structure):
     _fields_ = [("h", ctypes.c_void_p), ("n_steps", ctypes.c_void_p),
                 ("save_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("h_rows", ctypes.c_void_p),
-                ("rows", ctypes.c_int32), ("save_theta", ctypes.c_void_p)]
+                ("rows", ctypes.c_int32), ("save_theta", ctypes.c_void_p),
+                ("defer_pad", ctypes.c_int32)]
 
 
 class _RhsDef(ctypes.Structure):
@@ -99,6 +101,7 @@ def _load_library() -> ctypes.CDLL:
     lib.da_mesh_sort_workspace.restype = ctypes.c_size_t
     lib.da_mesh_sort.argtypes = [P, i64, M, vp, ctypes.c_size_t, vp]
     lib.da_mesh_max_steps.argtypes = [i64, M, ctypes.POINTER(ctypes.c_int32), vp]
+    lib.da_mesh_pad.argtypes = [P, i64, M, vp]
     lib.da_replay_fwd.argtypes = [P, i64, vp, vp, M, vp, vp]
     lib.da_replay_grad_workspace.argtypes = [P, i64, i32]
     lib.da_replay_grad_workspace.restype = ctypes.c_size_t
@@ -108,7 +111,7 @@ def _load_library() -> ctypes.CDLL:
     lib.da_rhs_register.argtypes = [ctypes.POINTER(_RhsDef), ctypes.POINTER(ctypes.c_int32)]
     lib.da_rhs_release.argtypes = [i32]
     lib.da_last_error.restype = ctypes.c_char_p
-    for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps",
+    for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps", "da_mesh_pad",
                  "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_rhs_register",
                  "da_rhs_release", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -257,8 +260,11 @@ def _inputs(prob, u0: torch.Tensor, p: torch.Tensor):
     return n, u0.dtype
 
 
-def record(prob, u0, p, mesh: Optional[Mesh] = None, save: bool = True, stream=None):
-    """Adaptive solve per trajectory; returns (mesh, y_save or None)."""
+def record(prob, u0, p, mesh: Optional[Mesh] = None, save: bool = True, stream=None,
+           defer_pad: bool = False):
+    """Adaptive solve per trajectory; returns (mesh, y_save or None).  With
+    ``defer_pad`` the chunks after each trajectory's last step are left for
+    ``mesh_pad`` (which nothing on the replay path waits for)."""
     n, dt = _inputs(prob, u0, p)
     S = max(1, len(prob.save_times))
     if mesh is None:
@@ -266,6 +272,7 @@ def record(prob, u0, p, mesh: Optional[Mesh] = None, save: bool = True, stream=N
     ys = torch.empty((S, prob.dim, n), dtype=dt, device=u0.device) if save else None
     P, keep = cproblem(prob, dt)
     cm = mesh.c()
+    cm.defer_pad = int(defer_pad)
     _check(_lib.da_record(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm), _ptr(ys),
                           _stream(stream)))
     return mesh, ys
@@ -316,6 +323,14 @@ def mesh_sort(prob, mesh: Mesh, perm: Optional[torch.Tensor] = None, table: bool
     _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(co), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
     return out
+
+
+def mesh_pad(prob, mesh: Mesh, stream=None) -> None:
+    """Zero padding of a record taken with ``defer_pad`` (on ``stream``,
+    which must be ordered after the record)."""
+    P, keep = cproblem(prob, mesh.h.dtype)
+    cm = mesh.c()
+    _check(_lib.da_mesh_pad(ctypes.byref(P), mesh.n, ctypes.byref(cm), _stream(stream)))
 
 
 def mesh_max_steps(mesh: Mesh, stream=None) -> int:

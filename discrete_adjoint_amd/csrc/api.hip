@@ -233,6 +233,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   a.theta = mesh->save_theta;
   a.status = mesh->status;
   a.y_save = y_save;
+  a.defer_pad = mesh->defer_pad != 0;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = launch_record(a, st, s);
   if (e != hipSuccess) return hip_fail(e, "record launch");
@@ -257,6 +258,7 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
   a.sidx = nullptr;
   a.theta = nullptr;
   a.status = status;
+  a.defer_pad = 0;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = launch_record(a, st, s);
@@ -293,6 +295,18 @@ int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspa
     e = dadj::launch_replay_table(pr, n, mesh->h, mesh->n_steps, mesh->perm, mesh->h_rows,
                                   mesh->rows, s);
   if (e != hipSuccess) return hip_fail(e, "mesh sort launch");
+  return ok();
+}
+
+int da_mesh_pad(const da_problem *prob, int64_t n, const da_mesh *mesh, void *stream) {
+  dadj::ProbArgs pr;
+  int rc = check_problem(prob, n, pr, nullptr);
+  if (rc) return rc;
+  if (n == 0) return ok();
+  if ((rc = check_mesh(mesh, false, pr.max_steps))) return rc;
+  const hipError_t e =
+      dadj::launch_mesh_pad(pr, n, mesh->n_steps, mesh->h, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mesh pad launch");
   return ok();
 }
 

@@ -51,6 +51,7 @@ struct RecordArgs {
   void *theta;          // [S][n] step fraction of each save, or null
   int32_t *status;      // [n] or null
   void *y_save;         // [S][d][n] or null
+  int32_t defer_pad;    // leave the chunks after each trajectory's last one
 };
 
 struct ReplayArgs {
@@ -93,6 +94,8 @@ hipError_t launch_mesh_sort(const ProbArgs &pr, int64_t n, const int32_t *nsteps
 hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
                                const int32_t *nsteps, const int32_t *perm, void *h_rows,
                                int32_t rows, hipStream_t s);
+hipError_t launch_mesh_pad(const ProbArgs &pr, int64_t n, const int32_t *nsteps, void *h,
+                           hipStream_t s);
 size_t max_steps_scratch_ints();  // size of dev_out below
 hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, hipStream_t s);
 

@@ -168,7 +168,8 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // exactly on every save time and on t1 (DENSE: on t1 only; the save times
 // inside an accepted step are read from its interpolant); t accumulates in
 // double.  Accepted steps collect in a register chunk that is written when
-// full; after the last step the partial chunk and zero chunks up to the end
+// full; after the last step the partial chunk and (unless the caller defers
+// them to da_mesh_pad) zero chunks up to the end
 // of the log follow.
 // ---------------------------------------------------------------------------
 template <class T, class M, bool LOG, bool DENSE>
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     if (a.status) a.status[i] = st;
     if (LOG && nacc % B != 0) store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
   }
-  if (LOG) {
+  if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)
     // zero chunks after each lane's last one, chunk row by chunk row across
     // the wavefront (hb is all zero here except for lanes that still hold a
     // partial chunk, which start one chunk later)

@@ -253,6 +253,27 @@ __global__ __launch_bounds__(MAX_BLOCKS) void k_max_final(int nb, int32_t *__res
   if (threadIdx.x == 0) out[0] = part[0];
 }
 
+// Zero chunks t >= ceil(N_i / B) of every trajectory i (the padding of a
+// record taken with deferred padding).  Thread i walks its chunk rows; a
+// wavefront writes 64 adjacent 64-byte chunks per row, as four 16-byte stores
+// per lane.
+template <class T>
+__global__ __launch_bounds__(SORT_THREADS) void k_mesh_pad(int64_t n, int32_t n_chunks,
+                                                           int32_t max_steps,
+                                                           const int32_t *__restrict__ nsteps,
+                                                           T *__restrict__ h) {
+  constexpr int B = 64 / (int)sizeof(T);
+  const int64_t i = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
+  if (i >= n) return;
+  int N = nsteps[i];
+  N = N < 0 ? 0 : (N > max_steps ? max_steps : N);
+  for (int t = (N + B - 1) / B; t < n_chunks; ++t) {
+    dvec2 *dst = (dvec2 *)(h + ((int64_t)t * n + i) * B);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) dst[q] = dvec2{0.0, 0.0};
+  }
+}
+
 size_t align_up(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int key_bits(int32_t max_steps) {
@@ -316,6 +337,18 @@ hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
   else
     hipLaunchKernelGGL(k_replay_table<float>, g1, SORT_THREADS, 0, s, n, pr.max_steps,
                        (const float *)h, nsteps, perm, (float *)h_rows, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_mesh_pad(const ProbArgs &pr, int64_t n, const int32_t *nsteps, void *h,
+                           hipStream_t s) {
+  const unsigned g = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
+  if (pr.dtype == DA_F64)
+    hipLaunchKernelGGL(k_mesh_pad<double>, g, SORT_THREADS, 0, s, n, pr.n_chunks, pr.max_steps,
+                       nsteps, (double *)h);
+  else
+    hipLaunchKernelGGL(k_mesh_pad<float>, g, SORT_THREADS, 0, s, n, pr.n_chunks, pr.max_steps,
+                       nsteps, (float *)h);
   return hipGetLastError();
 }
 

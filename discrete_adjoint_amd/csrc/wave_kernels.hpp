@@ -416,7 +416,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
       ++t0;
     }
     const int per = 64 / B;
-    for (int t = t0; t < pr.n_chunks; t += per) {
+    for (int t = a.defer_pad ? pr.n_chunks : t0; t < pr.n_chunks; t += per) {
       const int tc = t + c / B;
       if (tc < pr.n_chunks) H[((int64_t)tc * n + i) * B + (c % B)] = T(0);
     }

@@ -196,6 +196,14 @@ typedef struct {
                         the replays of a problem with dense = 1 (a replay
                         gradient with the final-state loss reads no save and
                         does not need it).                                   */
+  int32_t defer_pad; /* 1: da_record writes each trajectory's chunks only up to
+                        the one holding its last step (zero after that step)
+                        and leaves the later chunks as they are;
+                        da_mesh_pad then writes their zeros, on any stream,
+                        after the record.  The replays, the sensitivities and
+                        da_mesh_sort read no chunk past a trajectory's last
+                        step, so they need not wait for it.  0: da_record
+                        writes the zeros itself.                             */
 } da_mesh;
 
 /* Elements (of the problem's dtype) of the step log of n trajectories:
@@ -249,6 +257,12 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
 size_t da_mesh_sort_workspace(const da_problem *prob, int64_t n);
 int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspace,
                  size_t ws_bytes, void *stream);
+
+/* Zero padding of a record taken with mesh->defer_pad = 1: writes zeros to
+ * every chunk after the one that holds each trajectory's last step (reads
+ * n_steps, writes h).  Asynchronous on stream, which must be ordered after
+ * the record. */
+int da_mesh_pad(const da_problem *prob, int64_t n, const da_mesh *mesh, void *stream);
 
 /* Largest n_steps over the mesh, returned to the host (synchronises the
  * stream).  Used to size the replay workspace. */

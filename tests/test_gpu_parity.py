@@ -548,3 +548,50 @@ def test_maximum_save_times(da, orc):
     si = mesh.save_idx.cpu().numpy().T
     assert np.all(np.diff(si, axis=1) > 0)
     assert np.array_equal(si[:, -1], mesh.n_steps.cpu().numpy())
+
+
+@pytest.mark.parametrize("wid,n", [(2, 1000), (3, 777), (4, 300), (5, 120)])
+def test_deferred_padding(da, orc, wid, n):
+    """A record with deferred padding into a log filled with NaN: the saves,
+    step counts and chunks up to each trajectory's last step equal a padded
+    record's; replays, replay table, gradient and sensitivities give the same
+    results bit for bit (so none of them reads a chunk after a trajectory's
+    last step); after mesh_pad the whole log equals the padded one."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: deferred padding, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    m1, ys1 = da.record(prob, u0, p)
+    m2 = da.empty_mesh(prob, n, u0.dtype, u0.device)
+    m2.h.fill_(float("nan"))
+    m2, ys2 = da.record(prob, u0, p, mesh=m2, defer_pad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ys1, ys2)
+    for a, b in ((m1.n_steps, m2.n_steps), (m1.save_idx, m2.save_idx), (m1.status, m2.status)):
+        assert torch.equal(a, b)
+    B = m1.h.shape[2]
+    last = (m1.n_steps.cpu().numpy() + B - 1) // B
+    h1, h2 = m1.h.cpu().numpy(), m2.h.cpu().numpy()
+    written = np.arange(h1.shape[0])[:, None] < last[None, :]
+    assert np.array_equal(h1[written], h2[written])
+    assert np.all(np.isnan(h2[~written]))
+    for table in (False, True):
+        a = da.mesh_sort(prob, m1, table=table)
+        b = da.mesh_sort(prob, m2, table=table)
+        r1 = da.replay_grad(prob, u0, p, a, w.loss, aux=auxd, scale=scale)
+        r2 = da.replay_grad(prob, u0, p, b, w.loss, aux=auxd, scale=scale)
+        f1, f2 = da.replay_fwd(prob, u0, p, a), da.replay_fwd(prob, u0, p, b)
+        torch.cuda.synchronize()
+        for x, y in zip(r1 + (f1,), r2 + (f2,)):
+            assert torch.equal(x, y), table
+        if table:
+            assert torch.equal(a.h_rows, b.h_rows)
+        if prob.method != W.ROS2 and prob.rhs != W.LORENZ96:
+            s1 = da.replay_sens(prob, u0, p, a, w.loss, aux=auxd, scale=scale)
+            s2 = da.replay_sens(prob, u0, p, b, w.loss, aux=auxd, scale=scale)
+            torch.cuda.synchronize()
+            for x, y in zip(s1, s2):
+                assert torch.equal(x, y)
+    da.mesh_pad(prob, m2)
+    torch.cuda.synchronize()
+    assert torch.equal(m1.h, m2.h)
