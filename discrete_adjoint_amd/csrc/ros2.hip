@@ -15,17 +15,24 @@ namespace {
 template <int D, class T> struct Ros2Step {
   T J[D * D], LU[D * D], rinv[D];  // rinv[k] = 1 / U_kk
   int perm[D];
+  bool swapped;  // some row exchange happened (perm is not the identity)
   T f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
 };
 
 // In-place LU of A (row-major) with partial pivoting; perm[i] = original row
-// now in position i.  Row exchanges are register selects.  Each pivot's
-// reciprocal is formed once (a correctly rounded 1 / u) and every division by
-// the pivot, here and in the solves, is a multiplication by it.
+// now in position i, swapped = some row was exchanged.  Row exchanges are
+// register selects, executed only when some lane of the wavefront needs one
+// (a uniform branch: where the pivot is already on the diagonal, as with
+// diagonally dominant W, the selects are skipped; the values are the same
+// either way).  Each pivot's reciprocal is formed once (a correctly rounded
+// 1 / u) and every division by the pivot, here and in the solves, is a
+// multiplication by it.
 template <int D, class T>
-__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rinv)[D]) {
+__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rinv)[D],
+                                          bool &swapped) {
 #pragma unroll
   for (int i = 0; i < D; ++i) perm[i] = i;
+  swapped = false;
 #pragma unroll
   for (int k = 0; k < D; ++k) {
     int piv = k;
@@ -35,18 +42,21 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rin
       const T v = dabs(A[i * D + k]);
       if (v > best) { best = v; piv = i; }
     }
+    swapped = swapped || piv != k;
+    if (__ballot(piv != k) != 0ull) {
 #pragma unroll
-    for (int r = k + 1; r < D; ++r) {
-      const bool sw = piv == r;
+      for (int r = k + 1; r < D; ++r) {
+        const bool sw = piv == r;
 #pragma unroll
-      for (int j = 0; j < D; ++j) {
-        const T top = A[k * D + j], oth = A[r * D + j];
-        A[k * D + j] = sw ? oth : top;
-        A[r * D + j] = sw ? top : oth;
+        for (int j = 0; j < D; ++j) {
+          const T top = A[k * D + j], oth = A[r * D + j];
+          A[k * D + j] = sw ? oth : top;
+          A[r * D + j] = sw ? top : oth;
+        }
+        const int pt = perm[k], po = perm[r];
+        perm[k] = sw ? po : pt;
+        perm[r] = sw ? pt : po;
       }
-      const int pt = perm[k], po = perm[r];
-      perm[k] = sw ? po : pt;
-      perm[r] = sw ? pt : po;
     }
     rinv[k] = T(1) / A[k * D + k];
 #pragma unroll
@@ -65,16 +75,22 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rin
 // and keep the caller's arrays out of registers).
 template <int D, class T>
 __device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const T (&rinv)[D],
-                                         const int (&perm)[D], const T (&b_in)[D], T (&x)[D]) {
+                                         const int (&perm)[D], bool swapped, const T (&b_in)[D],
+                                         T (&x)[D]) {
   T b[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) b[i] = b_in[i];
+  if (__ballot(swapped) != 0ull) {  // uniform: some lane has a row exchange
 #pragma unroll
-  for (int i = 0; i < D; ++i) {
-    T v = b[0];
+    for (int i = 0; i < D; ++i) {
+      T v = b[0];
 #pragma unroll
-    for (int q = 1; q < D; ++q) v = (perm[i] == q) ? b[q] : v;
-    x[i] = v;
+      for (int q = 1; q < D; ++q) v = (perm[i] == q) ? b[q] : v;
+      x[i] = v;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D; ++i) x[i] = b[i];
   }
 #pragma unroll
   for (int i = 0; i < D; ++i)
@@ -91,7 +107,8 @@ __device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const T (&rinv)[D
 // Solve A^T x = b from the factors of A (A^T = U^T L^T P).
 template <int D, class T>
 __device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)[D],
-                                           const int (&perm)[D], const T (&b)[D], T (&x)[D]) {
+                                           const int (&perm)[D], bool swapped, const T (&b)[D],
+                                           T (&x)[D]) {
   T z[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) {
@@ -105,12 +122,17 @@ __device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)
 #pragma unroll
     for (int j = i + 1; j < D; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
   // x[perm[i]] = z[i]
+  if (__ballot(swapped) != 0ull) {  // uniform, as in lu_solve
 #pragma unroll
-  for (int c = 0; c < D; ++c) {
-    T v = z[0];
+    for (int c = 0; c < D; ++c) {
+      T v = z[0];
 #pragma unroll
-    for (int i = 1; i < D; ++i) v = (perm[i] == c) ? z[i] : v;
-    x[c] = v;
+      for (int i = 1; i < D; ++i) v = (perm[i] == c) ? z[i] : v;
+      x[c] = v;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < D; ++c) x[c] = z[c];
   }
 }
 
@@ -128,15 +150,15 @@ __device__ __forceinline__ void ros2_forward(const T (&y)[Rhs::D], const T *p, T
 #pragma unroll
     for (int b = 0; b < D; ++b)
       s.LU[a * D + b] = (a == b) ? mac(-gh, s.J[a * D + b], T(1)) : (-gh) * s.J[a * D + b];
-  lu_factor<D>(s.LU, s.perm, s.rinv);
+  lu_factor<D>(s.LU, s.perm, s.rinv, s.swapped);
   Rhs::f(y, p, s.f1);
-  lu_solve<D>(s.LU, s.rinv, s.perm, s.f1, s.k1);
+  lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.f1, s.k1);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.Y2[c] = mac(h, s.k1[c], y[c]);
   Rhs::f(s.Y2, p, s.f2);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.r2[c] = mac(T(-2), s.k1[c], s.f2[c]);
-  lu_solve<D>(s.LU, s.rinv, s.perm, s.r2, s.k2);
+  lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.r2, s.k2);
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     const T acc = mac(T(0.5), s.k2[c], T(1.5) * s.k1[c]);
@@ -199,7 +221,7 @@ struct Ros2 {
       kb2[c] = T(0.5) * ab;
       yb[c] = lam[c];
     }
-    lu_solve_t<D>(s.LU, s.rinv, s.perm, kb2, rb2);
+    lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, kb2, rb2);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll
@@ -212,7 +234,7 @@ struct Ros2 {
       kb1[c] = mac(h, Y2b[c], kb1[c]);
       yb[c] = yb[c] + Y2b[c];
     }
-    lu_solve_t<D>(s.LU, s.rinv, s.perm, kb1, rb1);
+    lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, kb1, rb1);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll
