@@ -24,9 +24,11 @@
  *
  * Conventions for every entry point:
  *  - All array pointers are DEVICE pointers unless marked "host"; all memory is
- *    owned by the caller.  The library allocates no device memory and keeps no
- *    state apart from a thread-local error message and the code objects of
- *    right-hand sides registered at run time (da_rhs_register).
+ *    owned by the caller.  The library allocates no device memory (except the
+ *    1 KiB scratch that da_mesh_max_steps allocates and frees within the
+ *    call) and keeps no state apart from a thread-local error message and the
+ *    code objects of right-hand sides registered at run time
+ *    (da_rhs_register).
  *  - Per-trajectory arrays are component-major: element (c, i) of an array
  *    with C components lives at index c * n + i (trajectory index fastest), so
  *    a wavefront reads and writes contiguous memory.
@@ -265,7 +267,8 @@ int da_mesh_sort(const da_problem *prob, int64_t n, da_mesh *mesh, void *workspa
 int da_mesh_pad(const da_problem *prob, int64_t n, const da_mesh *mesh, void *stream);
 
 /* Largest n_steps over the mesh, returned to the host (synchronises the
- * stream).  Used to size the replay workspace. */
+ * stream; allocates and frees a 1 KiB device scratch buffer).  Used to size
+ * the replay workspace. */
 int da_mesh_max_steps(int64_t n, const da_mesh *mesh, int32_t *host_max, void *stream);
 
 /* Fixed-step replay of the mesh (review, Summary: branch-free fixed-length
