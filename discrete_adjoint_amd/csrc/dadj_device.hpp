@@ -31,6 +31,18 @@ __device__ __forceinline__ double cmac(double c, double x, double acc) { return 
 __device__ __forceinline__ float cmac(double c, float x, float acc) { return mac(float(c), x, acc); }
 __device__ __forceinline__ double smac(double h, double a, double y) { return mac(h, a, y); }
 __device__ __forceinline__ float smac(float h, float a, float y) { return mac(h, a, y); }
+// h * x for a step-size factor h, 1 / x (correctly rounded), and the value part
+// of a number (the tangent types give their value; pivoting compares values).
+__device__ __forceinline__ double smul(double h, double x) { return h * x; }
+__device__ __forceinline__ float smul(float h, float x) { return h * x; }
+__device__ __forceinline__ double recip(double x) { return 1.0 / x; }
+__device__ __forceinline__ float recip(float x) { return 1.0f / x; }
+__device__ __forceinline__ double vpart(double x) { return x; }
+__device__ __forceinline__ float vpart(float x) { return x; }
+// c ? a : b (the tangent types select part by part, which keeps them in
+// registers)
+__device__ __forceinline__ double sel(bool c, double a, double b) { return c ? a : b; }
+__device__ __forceinline__ float sel(bool c, float a, float b) { return c ? a : b; }
 
 __device__ __forceinline__ bool finite(double x) { return __builtin_isfinite(x); }
 __device__ __forceinline__ bool finite(float x) { return __builtin_isfinite(x); }

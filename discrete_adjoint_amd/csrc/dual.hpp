@@ -7,6 +7,7 @@
 //   a * b        value a.v * b.v,         tangent fma(a.d, b.v, a.v * b.d)
 //   fma(a, b, c) value fma(a.v, b.v, c.v), tangent fma(a.d, b.v, fma(a.v, b.d, c.d))
 //   a +- b, -a   on both parts
+//   1 / b        value r = 1 / b.v,      tangent fma(-r, b.d, 0) / b.v
 // Coefficients and step sizes carry no tangent: c * x scales both parts,
 // fma(c, x, acc) and fma(h, acc, y) act on both parts with the same c or h.
 #pragma once
@@ -91,6 +92,31 @@ __device__ __forceinline__ DualN<T, G> smac(T h, const DualN<T, G> &acc, const D
   r.v = mac(h, acc.v, y.v);
 #pragma unroll
   for (int m = 0; m < G; ++m) r.d[m] = mac(h, acc.d[m], y.d[m]);
+  return r;
+}
+
+template <class T, int G>
+__device__ __forceinline__ DualN<T, G> smul(T h, const DualN<T, G> &x) {
+  DualN<T, G> r;
+  r.v = h * x.v;
+#pragma unroll
+  for (int m = 0; m < G; ++m) r.d[m] = h * x.d[m];
+  return r;
+}
+template <class T, int G> __device__ __forceinline__ DualN<T, G> recip(const DualN<T, G> &b) {
+  DualN<T, G> r;
+  r.v = T(1) / b.v;
+#pragma unroll
+  for (int m = 0; m < G; ++m) r.d[m] = mac(-r.v, b.d[m], T(0)) / b.v;
+  return r;
+}
+template <class T, int G> __device__ __forceinline__ T vpart(const DualN<T, G> &x) { return x.v; }
+template <class T, int G>
+__device__ __forceinline__ DualN<T, G> sel(bool c, const DualN<T, G> &a, const DualN<T, G> &b) {
+  DualN<T, G> r;
+  r.v = c ? a.v : b.v;
+#pragma unroll
+  for (int m = 0; m < G; ++m) r.d[m] = c ? a.d[m] : b.d[m];
   return r;
 }
 

@@ -6,17 +6,20 @@
 // Per lane: the d x d Jacobian (d <= 3), W = I - gamma h J, its LU factors
 // with partial pivoting (ties keep the lower row), two solves per step; the
 // reverse sweep uses transposed solves with the same factors and contracts
-// Jbar = -gamma h Wbar with the derivative of J.
+// Jbar = -gamma h Wbar with the derivative of J.  The forward step is written
+// once for values and for the tangent numbers of the sensitivity kernel (V is
+// either; the step size and gamma carry no tangent).
 #include "lane_kernels.hpp"
+#include "sens_kernel.hpp"
 
 namespace dadj {
 namespace {
 
-template <int D, class T> struct Ros2Step {
-  T J[D * D], LU[D * D], rinv[D];  // rinv[k] = 1 / U_kk
+template <int D, class V> struct Ros2Step {
+  V J[D * D], LU[D * D], rinv[D];  // rinv[k] = 1 / U_kk
   int perm[D];
   bool swapped;  // some row exchange happened (perm is not the identity)
-  T f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
+  V f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
 };
 
 // In-place LU of A (row-major) with partial pivoting; perm[i] = original row
@@ -26,9 +29,9 @@ template <int D, class T> struct Ros2Step {
 // diagonally dominant W, the selects are skipped; the values are the same
 // either way).  Each pivot's reciprocal is formed once (a correctly rounded
 // 1 / u) and every division by the pivot, here and in the solves, is a
-// multiplication by it.
-template <int D, class T>
-__device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rinv)[D],
+// multiplication by it.  Pivots are chosen on values.
+template <int D, class V>
+__device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rinv)[D],
                                           bool &swapped) {
 #pragma unroll
   for (int i = 0; i < D; ++i) perm[i] = i;
@@ -36,10 +39,10 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rin
 #pragma unroll
   for (int k = 0; k < D; ++k) {
     int piv = k;
-    T best = dabs(A[k * D + k]);
+    auto best = dabs(vpart(A[k * D + k]));
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
-      const T v = dabs(A[i * D + k]);
+      const auto v = dabs(vpart(A[i * D + k]));
       if (v > best) { best = v; piv = i; }
     }
     swapped = swapped || piv != k;
@@ -49,19 +52,19 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rin
         const bool sw = piv == r;
 #pragma unroll
         for (int j = 0; j < D; ++j) {
-          const T top = A[k * D + j], oth = A[r * D + j];
-          A[k * D + j] = sw ? oth : top;
-          A[r * D + j] = sw ? top : oth;
+          const V top = A[k * D + j], oth = A[r * D + j];
+          A[k * D + j] = sel(sw, oth, top);
+          A[r * D + j] = sel(sw, top, oth);
         }
         const int pt = perm[k], po = perm[r];
         perm[k] = sw ? po : pt;
         perm[r] = sw ? pt : po;
       }
     }
-    rinv[k] = T(1) / A[k * D + k];
+    rinv[k] = recip(A[k * D + k]);
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
-      const T l = A[i * D + k] * rinv[k];
+      const V l = A[i * D + k] * rinv[k];
       A[i * D + k] = l;
 #pragma unroll
       for (int j = k + 1; j < D; ++j) A[i * D + j] = mac(-l, A[k * D + j], A[i * D + j]);
@@ -73,19 +76,19 @@ __device__ __forceinline__ void lu_factor(T (&A)[D * D], int (&perm)[D], T (&rin
 // into a private array first so that the permutation stays a register select
 // (a select between loads through the argument would become an indexed load
 // and keep the caller's arrays out of registers).
-template <int D, class T>
-__device__ __forceinline__ void lu_solve(const T (&LU)[D * D], const T (&rinv)[D],
-                                         const int (&perm)[D], bool swapped, const T (&b_in)[D],
-                                         T (&x)[D]) {
-  T b[D];
+template <int D, class V>
+__device__ __forceinline__ void lu_solve(const V (&LU)[D * D], const V (&rinv)[D],
+                                         const int (&perm)[D], bool swapped, const V (&b_in)[D],
+                                         V (&x)[D]) {
+  V b[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) b[i] = b_in[i];
   if (__ballot(swapped) != 0ull) {  // uniform: some lane has a row exchange
 #pragma unroll
     for (int i = 0; i < D; ++i) {
-      T v = b[0];
+      V v = b[0];
 #pragma unroll
-      for (int q = 1; q < D; ++q) v = (perm[i] == q) ? b[q] : v;
+      for (int q = 1; q < D; ++q) v = sel(perm[i] == q, b[q], v);
       x[i] = v;
     }
   } else {
@@ -139,32 +142,32 @@ __device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)
 // One ROS2 step from y with size h:
 //   k1 = W^-1 f(y);  Y2 = y + h k1;  k2 = W^-1 (f(Y2) - 2 k1);
 //   y+ = y + h (3/2 k1 + 1/2 k2);  err = h (1/2 k1 + 1/2 k2).
-template <class Rhs, class T>
-__device__ __forceinline__ void ros2_forward(const T (&y)[Rhs::D], const T *p, T h,
-                                             Ros2Step<Rhs::D, T> &s) {
+template <class Rhs, class V, class H>
+__device__ __forceinline__ void ros2_forward(const V (&y)[Rhs::D], const V *p, H h,
+                                             Ros2Step<Rhs::D, V> &s) {
   constexpr int D = Rhs::D;
   Rhs::jac(y, p, s.J);
-  const T gh = T(ROS2_GAMMA) * h;
+  const H gh = H(ROS2_GAMMA) * h;
 #pragma unroll
   for (int a = 0; a < D; ++a)
 #pragma unroll
     for (int b = 0; b < D; ++b)
-      s.LU[a * D + b] = (a == b) ? mac(-gh, s.J[a * D + b], T(1)) : (-gh) * s.J[a * D + b];
+      s.LU[a * D + b] = (a == b) ? smac(-gh, s.J[a * D + b], V(1)) : smul(-gh, s.J[a * D + b]);
   lu_factor<D>(s.LU, s.perm, s.rinv, s.swapped);
   Rhs::f(y, p, s.f1);
   lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.f1, s.k1);
 #pragma unroll
-  for (int c = 0; c < D; ++c) s.Y2[c] = mac(h, s.k1[c], y[c]);
+  for (int c = 0; c < D; ++c) s.Y2[c] = smac(h, s.k1[c], y[c]);
   Rhs::f(s.Y2, p, s.f2);
 #pragma unroll
-  for (int c = 0; c < D; ++c) s.r2[c] = mac(T(-2), s.k1[c], s.f2[c]);
+  for (int c = 0; c < D; ++c) s.r2[c] = cmac(-2.0, s.k1[c], s.f2[c]);
   lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.r2, s.k2);
 #pragma unroll
   for (int c = 0; c < D; ++c) {
-    const T acc = mac(T(0.5), s.k2[c], T(1.5) * s.k1[c]);
-    s.ynew[c] = mac(h, acc, y[c]);
-    const T e = mac(T(0.5), s.k2[c], T(0.5) * s.k1[c]);
-    s.err[c] = h * e;
+    const V acc = cmac(0.5, s.k2[c], cmul(1.5, s.k1[c]));
+    s.ynew[c] = smac(h, acc, y[c]);
+    const V e = cmac(0.5, s.k2[c], cmul(0.5, s.k1[c]));
+    s.err[c] = smul(h, e);
   }
 }
 
@@ -194,8 +197,10 @@ struct Ros2 {
 
   template <class T> __device__ static __forceinline__ void accepted(Cache<T> &) {}
 
-  template <class T> __device__ static __forceinline__ void fwd(T (&y)[D], const T *p, T h) {
-    Ros2Step<D, T> s;
+  // V: values, or the tangent numbers of the sensitivity kernel
+  template <class V, class H>
+  __device__ static __forceinline__ void fwd(V (&y)[D], const V *p, H h) {
+    Ros2Step<D, V> s;
     ros2_forward<Rhs>(y, p, h, s);
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
@@ -277,6 +282,9 @@ hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s) {
 }
 hipError_t launch_ros2_replay_grad(const ReplayArgs &a, hipStream_t s) {
   DADJ_ROS2_DISPATCH(replay_grad_t, (a, s));
+}
+hipError_t launch_ros2_replay_sens(const ReplayArgs &a, hipStream_t s) {
+  DADJ_ROS2_DISPATCH(replay_sens_t, (a, s));
 }
 
 }  // namespace dadj

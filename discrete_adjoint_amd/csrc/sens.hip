@@ -10,29 +10,6 @@
 #include "sens_kernel.hpp"
 
 namespace dadj {
-namespace {
-
-template <class T, class M, bool DENSE>
-hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {
-  constexpr int Q = M::Rhs::D + M::Rhs::P;
-  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK), (unsigned)((Q + SENS_G - 1) / SENS_G));
-  if (a.h_rows)
-    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true, DENSE>), grid, BLOCK, 0, s, a);
-  else
-    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, false, DENSE>), grid, BLOCK, 0, s, a);
-  return hipGetLastError();
-}
-
-// Dense output changes only the saves: without loss terms at the saves and
-// without sensitivity output the plain kernel computes the same.
-template <class T, class M>
-hipError_t replay_sens_t(const ReplayArgs &a, hipStream_t s) {
-  const bool at_saves = a.sens || (a.has_loss && a.loss_kind != DA_LOSS_SUMSQ_FINAL);
-  if (a.pr.dense && at_saves) return replay_sens_d<T, M, true>(a, s);
-  return replay_sens_d<T, M, false>(a, s);
-}
-
-}  // namespace
 
 hipError_t launch_erk_replay_sens(const ReplayArgs &a, hipStream_t s) {
   DADJ_ERK_DISPATCH(replay_sens_t, (a, s));

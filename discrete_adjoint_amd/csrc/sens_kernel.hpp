@@ -1,9 +1,10 @@
-// Forward-mode sensitivity kernel (see sens.hip for its launcher): the
-// state of every lane carries G tangent directions (unit vectors in u0, then
-// in p) through the fixed-step replay, with the mesh held fixed as in the
-// reverse sweep ("Differentiable astrophysics at scale", Methodology:
+// Forward-mode sensitivity kernel and its launcher: the state of every lane
+// carries G tangent directions (unit vectors in u0, then in p) through the
+// fixed-step replay, with the mesh held fixed as in the reverse sweep ("Differentiable astrophysics at scale", Methodology:
 // forward sensitivities integrated in the same per-trajectory kernel;
 // "GRADSOLVE" review, FAQ on exactness: no derivative of the step sizes).
+// Any method whose fwd takes tangent numbers runs here (the explicit tableaux
+// and ROS2).
 #pragma once
 
 #include "dual.hpp"
@@ -155,5 +156,32 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
     if (blockIdx.y == 0 && a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * ss : nanv<T>();
   }
 }
+
+#ifndef __HIPCC_RTC__
+// Launch: one lane per trajectory, the d + P directions in groups of G on the
+// second grid dimension.
+template <class T, class M, bool DENSE>
+hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {
+  constexpr int Q = M::Rhs::D + M::Rhs::P;
+  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK), (unsigned)((Q + SENS_G - 1) / SENS_G));
+  if (a.h_rows)
+    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true, DENSE>), grid, BLOCK, 0, s, a);
+  else
+    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, false, DENSE>), grid, BLOCK, 0, s, a);
+  return hipGetLastError();
+}
+
+// Dense output changes only the saves: without loss terms at the saves and
+// without sensitivity output the plain kernel computes the same.  Methods
+// without an interpolant never take the dense kernel (the library refuses
+// dense output for them).
+template <class T, class M>
+hipError_t replay_sens_t(const ReplayArgs &a, hipStream_t s) {
+  const bool at_saves = a.sens || (a.has_loss && a.loss_kind != DA_LOSS_SUMSQ_FINAL);
+  if constexpr (M::dense_output)
+    if (a.pr.dense && at_saves) return replay_sens_d<T, M, true>(a, s);
+  return replay_sens_d<T, M, false>(a, s);
+}
+#endif
 
 }  // namespace dadj

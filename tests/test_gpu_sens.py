@@ -43,6 +43,10 @@ CASES = [
     ("lorenz63_dopri5_saves_cot", 2, dict(t1=2.0, save_times=(0.4, 1.1, 2.0)), W.COTANGENT, 400),
     ("lorenz63_tsit5_saves_mse", 1, dict(save_times=(0.25, 0.5, 0.75)), W.MSE_SAVE, 300),
     ("robertson_tsit5", 4, dict(t1=0.3, method=W.TSIT5, max_steps=8192), W.SUMSQ_FINAL, 130),
+    ("robertson_ros2", 4, dict(t1=100.0), W.SUMSQ_FINAL, 300),
+    ("robertson_ros2_saves_mse", 4, dict(t1=1e3, save_times=(1.0, 10.0, 1e3)), W.MSE_SAVE, 200),
+    ("lorenz63_ros2_saves_cot", 1, dict(method=W.ROS2, rtol=1e-4, atol=1e-4, max_steps=2048,
+                                        save_times=(0.3, 0.7, 1.0)), W.COTANGENT, 300),
 ]
 
 
@@ -107,23 +111,63 @@ def test_sensitivity_options_and_errors(da, orc):
     assert np.all(np.isnan(q1.cpu().numpy()[:, bad]))
     assert np.all(np.isnan(s1.cpu().numpy()[..., bad]))
     assert not np.any(np.isnan(q1.cpu().numpy()[:, ~bad]))
-    for prob_u in (W.WORKLOADS[4].problem(), W.WORKLOADS[5].problem()):
-        wid = 4 if prob_u.rhs == W.ROBERTSON else 5
-        iu = W.make_inputs(wid, 4)
-        with pytest.raises(da.DadjError) as e:
-            mu, _ = da.record(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch))
-            da.replay_sens(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch), mu)
-        assert e.value.code == da.DA_EUNSUPPORTED
+    prob_u = W.WORKLOADS[5].problem()
+    iu = W.make_inputs(5, 4)
+    mu, _ = da.record(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch))
+    with pytest.raises(da.DadjError) as e:
+        da.replay_sens(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch), mu)
+    assert e.value.code == da.DA_EUNSUPPORTED
 
 
-def test_full_size_sensitivities_sampled(da, orc):
-    """Workload 2 at full size (record, replay order with table, forward-mode
-    gradient); sampled trajectories against the oracle on the GPU's mesh."""
-    w = W.WORKLOADS[2]
+def test_ros2_sensitivities_with_row_exchanges(da, orc):
+    """ROS2 on Lorenz-63 over a coarse hand-made mesh (per-trajectory step
+    sizes 0.02..0.2), where the LU of W = I - gamma h J exchanges rows in some
+    lanes of every wavefront and not in others: tangents through the pivoted
+    factors and both solves against the oracle, and against the reverse sweep."""
+    n, N = 256, 10
+    inp = W.make_inputs(1, n)
+    u0n, pn = inp["u0"], inp["p"]
+    hl = 0.02 + 0.18 * np.random.default_rng(8).random(n)
+    g = orc.ros2_gamma()
+    col0 = np.abs(np.stack([1 + g * hl * pn[:, 0], -g * hl * (pn[:, 1] - u0n[:, 2]),
+                            -g * hl * u0n[:, 1]]))
+    piv = np.argmax(col0, axis=0)          # pivot row of the first column, first step
+    for w0 in range(0, n, 64):
+        assert 0 < np.count_nonzero(piv[w0:w0 + 64]) < 64
+    m = {"h": np.repeat(hl[:, None], N, 1), "n_steps": np.full(n, N, np.int32),
+         "save_idx": np.tile(np.array([3, 7, 10], np.int32), (n, 1)),
+         "status": np.zeros(n, np.int32)}
+    prob = W.Problem(W.LORENZ63, 3, 3, W.ROS2, 0.0, 2.0, 1e-6, 1e-6, N,
+                     save_times=(0.6, 1.4, 2.0))
+    aux = np.random.default_rng(5).standard_normal((n, 3, 3))
+    _print(f"case: ROS2 sensitivities with row exchanges, n={n}")
+    so, lo, go, po = orc.replay_sens(prob, u0n, pn, m, W.MSE_SAVE, aux=aux, scale=0.3, fused=True)
+    mesh = mesh_to_dev(m, N, torch)
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    sg, lg, gu0, gp = da.replay_sens(prob, u0, p, mesh, W.MSE_SAVE, aux=aux_to_dev(aux, torch),
+                                     scale=0.3)
+    la, ga, pa = da.replay_grad(prob, u0, p, mesh, W.MSE_SAVE, aux=aux_to_dev(aux, torch),
+                                scale=0.3)
+    torch.cuda.synchronize()
+    es = _sens_err(sg.cpu().numpy().transpose(3, 0, 1, 2), so)
+    eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+    ea = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, ga.cpu().numpy().T,
+                      pa.cpu().numpy().T)
+    _print(f"  sens max rel {es.max():.3e} (bitwise lanes {np.mean(es == 0):.3f}), "
+           f"grad {eg.max():.3e}, forward vs reverse {ea.max():.3e}")
+    assert es.max() <= 1e-12 and eg.max() <= 1e-12 and ea.max() <= 1e-10
+
+
+@pytest.mark.parametrize("wid", [2, 4])
+def test_full_size_sensitivities_sampled(da, orc, wid):
+    """Lorenz-63 with Dopri5 (2^20 trajectories) and Robertson with ROS2
+    (65536) at full size: record, replay order with table, forward-mode
+    gradient; sampled trajectories against the oracle on the GPU's mesh."""
+    w = W.WORKLOADS[wid]
     prob = w.problem()
-    inp = W.make_inputs(2)
+    inp = W.make_inputs(wid)
     n = w.n
-    _print(f"case: full-size sensitivities, workload 2, n={n}")
+    _print(f"case: full-size sensitivities, {w.name}, n={n}")
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     mesh, _ = da.record(prob, u0, p, save=False)
     sm = da.mesh_sort(prob, mesh)
@@ -131,7 +175,8 @@ def test_full_size_sensitivities_sampled(da, orc):
     torch.cuda.synchronize()
     perm = sm.perm.cpu().numpy()
     rng = np.random.default_rng(31)
-    tr = perm[np.unique(np.concatenate([rng.choice(n, 64, replace=False), [0, n - 1]]))]
+    k = 64 if wid == 2 else 24
+    tr = perm[np.unique(np.concatenate([rng.choice(n, k, replace=False), [0, n - 1]]))]
     N = int(sm.n_steps.max().item())
     idx = torch.from_numpy(tr.astype(np.int64)).cuda()
     h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
@@ -145,14 +190,17 @@ def test_full_size_sensitivities_sampled(da, orc):
     assert eg.max() <= 1e-12
 
 
-def test_sensitivities_fp32(da, orc):
+@pytest.mark.parametrize("wid,kw", [(3, dict(t1=1.0, save_times=(0.5, 1.0))),
+                                    (4, dict(t1=10.0, rtol=1e-4, atol=1e-8))],
+                         ids=["lorenz63_tsit5", "robertson_ros2"])
+def test_sensitivities_fp32(da, orc, wid, kw):
     """FP32 tangents against the FP64 oracle on the FP32 mesh (the tangent
     arithmetic in single precision)."""
-    w = W.WORKLOADS[3]
-    prob = w.problem(t1=1.0, save_times=(0.5, 1.0))
+    w = W.WORKLOADS[wid]
+    prob = w.problem(**kw)
     n = 200
-    inp = W.make_inputs(3, n)
-    _print("case: FP32 sensitivities, n=200")
+    inp = {k: v.astype(np.float32) for k, v in W.make_inputs(wid, n).items()}
+    _print(f"case: FP32 sensitivities, {w.name}, n=200")
     m = orc.record(prob, inp["u0"], inp["p"], fused=True)
     assert np.all(m["status"] == 0)
     m64 = dict(m)
