@@ -57,9 +57,14 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 # state counted once): per direction the tangent of every right-hand side
 # (Lorenz-63: 4 + 5 + 7 = 16 flop) and of the stage sums (same count as the
 # state's), so Dopri5 / Lorenz-63: 186 + 6 x (6 x 16 + 138) = 1590 and
-# Tsit5 / Lorenz-63: 192 + 6 x (6 x 16 + 144) = 1632.
-def sens_flop_per_step(method: str, rhs: str) -> int:
-    return {("dopri5", "lorenz63"): 1590, ("tsit5", "lorenz63"): 1632}.get((method, rhs), 0)
+# Tsit5 / Lorenz-63: 192 + 6 x (6 x 16 + 144) = 1632.  Tsit5 / Lorenz-96:
+# the state 72d, and per direction the tangents of six right-hand sides
+# (6d each: difference, tangent multiply-add, sum) and of the stage sums
+# (48d), so 72d + (d + 1) x 84d.  Not counted for ROS2 (None).
+def sens_flop_per_step(method: str, rhs: str, dim: int):
+    if (method, rhs) == ("tsit5", "lorenz96"):
+        return 72 * dim + (dim + 1) * 84 * dim
+    return {("dopri5", "lorenz63"): 1590, ("tsit5", "lorenz63"): 1632}.get((method, rhs))
 
 
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
@@ -274,16 +279,15 @@ def main():
                              for k in range(passes)]))
     # forward-mode gradient of the same loss on the same replay order and table
     sens_ms = []
-    if w.method != W.ROS2 and w.rhs != W.LORENZ96:
-        for r in range(3):
-            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a0.record(stream)
-            da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux, scale=scale,
-                           with_sens=False)
-            a1.record(stream)
-            torch.cuda.synchronize()
-            if r > 0:
-                sens_ms.append(a0.elapsed_time(a1))
+    for r in range(3):
+        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a0.record(stream)
+        da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux, scale=scale,
+                       with_sens=False)
+        a1.record(stream)
+        torch.cuda.synchronize()
+        if r > 0:
+            sens_ms.append(a0.elapsed_time(a1))
     # forward-only adaptive solve of the same ensemble (outside the job)
     solve_ms = []
     for r in range(3):
@@ -301,6 +305,7 @@ def main():
     mean_steps = float(ns.mean().item())
     mname, rname = W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs]
     flop_step = flop_per_step(mname, rname, w.dim)
+    sens_flop = sens_flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = None if args.rhs_source else read_traffic(w.name, kernel_family(mname, rname),
@@ -326,12 +331,12 @@ def main():
                      "flop_per_step": flop_step, "populated_steps_per_launch": total_steps},
         "per_pass": {"ms": pass_ms, "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
         "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
-        "forward_mode_grad": None if not sens_ms else {
+        "forward_mode_grad": {
             "ms": float(np.mean(sens_ms)),
             "trajectory_gradients_per_s": n / (float(np.mean(sens_ms)) * 1e-3),
-            "flop_per_step": sens_flop_per_step(mname, rname),
-            "achieved_tflops": sens_flop_per_step(mname, rname) * total_steps
-            / (float(np.mean(sens_ms)) * 1e-3) / 1e12},
+            "flop_per_step": sens_flop,
+            "achieved_tflops": None if sens_flop is None
+            else sens_flop * total_steps / (float(np.mean(sens_ms)) * 1e-3) / 1e12},
         "solve_fwd": {"ms": float(np.mean(solve_ms)),
                       "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],

@@ -420,8 +420,6 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
-  if (pr.rhs == DA_RHS_LORENZ96)
-    return fail(DA_EUNSUPPORTED, "sensitivities are available for systems of dimension <= 3");
   if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
   if (pr.dense && (sens || (loss && loss->kind != DA_LOSS_SUMSQ_FINAL)) && !mesh->save_theta)
@@ -446,9 +444,11 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
     a.gu0 = grad_u0;
     a.gp = grad_p;
   }
-  const hipError_t e = user_rhs(pr)            ? dadj::launch_rtc_replay_sens(a, (hipStream_t)stream)
-                       : pr.method == DA_ROS2 ? dadj::launch_ros2_replay_sens(a, (hipStream_t)stream)
-                                              : dadj::launch_erk_replay_sens(a, (hipStream_t)stream);
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = user_rhs(pr)                   ? dadj::launch_rtc_replay_sens(a, s)
+                       : pr.rhs == DA_RHS_LORENZ96   ? dadj::launch_l96_replay_sens(a, s)
+                       : pr.method == DA_ROS2        ? dadj::launch_ros2_replay_sens(a, s)
+                                                     : dadj::launch_erk_replay_sens(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_sens launch");
   return ok();
 }

@@ -82,6 +82,7 @@ hipError_t launch_erk_replay_grad(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_l96_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_l96_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_l96_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_l96_replay_sens(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_erk_replay_sens(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_ros2_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_ros2_replay_fwd(const ReplayArgs &a, hipStream_t s);

@@ -1,5 +1,6 @@
 // Lorenz-96 ensembles (state dimension 4..64) on the wavefront-per-trajectory
-// kernels: explicit Tsit5 and Dopri5 in FP64 and FP32.
+// kernels: explicit Tsit5 and Dopri5 in FP64 and FP32; record, replay,
+// reverse sweep and forward-mode sensitivities.
 #include "wave_kernels.hpp"
 
 namespace dadj {
@@ -67,6 +68,31 @@ hipError_t wreplay_grad_t(const ReplayArgs &a, hipStream_t s) {
   return dense ? wreplay_grad_d<T, M, true>(a, s) : wreplay_grad_d<T, M, false>(a, s);
 }
 
+// Sensitivities: 4 tangent directions per lane; ceil((d + 1) / 4) direction
+// groups on the second grid dimension.
+constexpr int WSENS_G = 4;
+template <class T, class M, bool FULL, bool DENSE>
+hipError_t wreplay_sens_f(const ReplayArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)((a.n + WAVES - 1) / WAVES),
+                  (unsigned)((a.pr.dim + 1 + WSENS_G - 1) / WSENS_G));
+  hipLaunchKernelGGL((wave::k_wreplay_sens<T, M, WSENS_G, FULL, DENSE>), grid, 64 * WAVES, 0, s,
+                     a);
+  return hipGetLastError();
+}
+template <class T, class M, bool DENSE>
+hipError_t wreplay_sens_d(const ReplayArgs &a, hipStream_t s) {
+  return a.pr.dim == 64 ? wreplay_sens_f<T, M, true, DENSE>(a, s)
+                        : wreplay_sens_f<T, M, false, DENSE>(a, s);
+}
+// Without loss terms at the saves and without sensitivity output, a dense
+// problem runs the plain kernel.
+template <class T, class M>
+hipError_t wreplay_sens_t(const ReplayArgs &a, hipStream_t s) {
+  const bool at_saves = a.sens || (a.has_loss && a.loss_kind != DA_LOSS_SUMSQ_FINAL);
+  return (a.pr.dense && at_saves) ? wreplay_sens_d<T, M, true>(a, s)
+                                  : wreplay_sens_d<T, M, false>(a, s);
+}
+
 #define DADJ_L96_DISPATCH(FN, ARGS)                                                    \
   do {                                                                                 \
     const bool f64 = a.pr.dtype == DA_F64;                                             \
@@ -89,6 +115,9 @@ hipError_t launch_l96_replay_fwd(const ReplayArgs &a, hipStream_t s) {
 }
 hipError_t launch_l96_replay_grad(const ReplayArgs &a, hipStream_t s) {
   DADJ_L96_DISPATCH(wreplay_grad_t, (a, s));
+}
+hipError_t launch_l96_replay_sens(const ReplayArgs &a, hipStream_t s) {
+  DADJ_L96_DISPATCH(wreplay_sens_t, (a, s));
 }
 
 }  // namespace dadj

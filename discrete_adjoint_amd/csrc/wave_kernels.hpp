@@ -12,6 +12,8 @@
 //  k_wrecord<T, M, LOG>        adaptive solve (record / forward-only solve)
 //  k_wreplay_fwd<T, M>         fixed-step replay
 //  k_wreplay_grad<T, M, CK>    replay + reverse sweep, mesh held fixed
+//  k_wreplay_sens<T, M, G>     replay with G tangent directions per lane
+//                              (forward-mode sensitivities)
 // each also with DENSE: save times read from the cubic Hermite interpolant of
 // the accepted step that holds them, per component (lane_kernels.hpp gives
 // the interpolant); whether a step holds a save is the same for all lanes.
@@ -27,6 +29,7 @@
 
 #include "dadj_device.hpp"
 #include "dadj_internal.hpp"
+#include "dual.hpp"
 
 namespace dadj {
 namespace wave {
@@ -70,6 +73,35 @@ template <int CTRL> __device__ __forceinline__ double rot(double v) {
 }
 template <int CTRL> __device__ __forceinline__ float rot(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Tangent numbers move part by part.
+template <int CTRL, class T, int G>
+__device__ __forceinline__ DualN<T, G> rot(const DualN<T, G> &v) {
+  DualN<T, G> r;
+  r.v = rot<CTRL>(v.v);
+#pragma unroll
+  for (int m = 0; m < G; ++m) r.d[m] = rot<CTRL>(v.d[m]);
+  return r;
+}
+template <class T, int G>
+__device__ __forceinline__ DualN<T, G> take(const DualN<T, G> &v, int src) {
+  DualN<T, G> r;
+  r.v = take(v.v, src);
+#pragma unroll
+  for (int m = 0; m < G; ++m) r.d[m] = take(v.d[m], src);
+  return r;
+}
+
+// The value of lane l (a wavefront-uniform lane index), in every lane.
+__device__ __forceinline__ double lane_value(double v, int l) {
+  const long long b = __double_as_longlong(v);
+  const unsigned lo = __builtin_amdgcn_readlane((unsigned)b, l);
+  const unsigned hi = __builtin_amdgcn_readlane((unsigned)((unsigned long long)b >> 32), l);
+  return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 // The cyclic neighbours of component c in dimension d.  FULL (d = 64): the
@@ -131,26 +163,27 @@ struct L96 {
 // ---------------------------------------------------------------------------
 // Explicit RK step per component (same arithmetic schedule as the
 // lane-per-trajectory kernels: first product, then multiply-adds, left to
-// right; Y_i = fma(h, acc, y)).
+// right; Y_i = fma(h, acc, y)).  T is a real or a tangent number (the
+// coefficients and h carry no tangent); H the real type of h.
 // ---------------------------------------------------------------------------
-template <class Tab, int I, class T>
-__device__ __forceinline__ T wstage(T y, const T (&K)[7], T h) {
+template <class Tab, int I, class T, class H>
+__device__ __forceinline__ T wstage(T y, const T (&K)[7], H h) {
   T acc = T(0);
   bool first = true;
 #pragma unroll
   for (int j = 0; j < I; ++j) {
     if (Tab::a[I][j] != 0.0) {
-      if (first) { acc = T(Tab::a[I][j]) * K[j]; first = false; }
-      else acc = mac(T(Tab::a[I][j]), K[j], acc);
+      if (first) { acc = cmul(Tab::a[I][j], K[j]); first = false; }
+      else acc = cmac(Tab::a[I][j], K[j], acc);
     }
   }
-  return mac(h, acc, y);
+  return smac(h, acc, y);
 }
 
 template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
 struct WStages {
-  template <class NB>
-  __device__ static __forceinline__ void run(T y, T F, T h, const NB &nb, T (&Y)[7], T (&K)[7]) {
+  template <class H, class NB>
+  __device__ static __forceinline__ void run(T y, T F, H h, const NB &nb, T (&Y)[7], T (&K)[7]) {
     Y[I] = wstage<Tab, I>(y, K, h);
     if (I < LAST || LASTK) K[I] = Rhs::f(Y[I], F, nb);
     WStages<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, F, h, nb, Y, K);
@@ -158,8 +191,8 @@ struct WStages {
 };
 template <class Tab, class Rhs, int LAST, bool LASTK, class T>
 struct WStages<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
-  template <class NB>
-  __device__ static __forceinline__ void run(T, T, T, const NB &, T (&)[7], T (&)[7]) {}
+  template <class H, class NB>
+  __device__ static __forceinline__ void run(T, T, H, const NB &, T (&)[7], T (&)[7]) {}
 };
 
 template <class Tab, class R>
@@ -185,8 +218,9 @@ struct WErk {
     return Y[6];
   }
 
-  template <class T, class NB>
-  __device__ static __forceinline__ T fwd(T x, T F, T h, const NB &nb) {
+  // T: a real, or the tangent numbers of the sensitivity kernel
+  template <class T, class H, class NB>
+  __device__ static __forceinline__ T fwd(T x, T F, H h, const NB &nb) {
     T Y[7], K[7];
     K[0] = Rhs::f(x, F, nb);
     WStages<Tab, Rhs, 1, 6, false, T>::run(x, F, h, nb, Y, K);
@@ -231,13 +265,16 @@ struct WErk {
 };
 
 // Dense output, per component: the interpolant at fraction th of the step of
-// size h from x0 to x1, h (H11 f(x1) + H10 f(x0)) + (H01 x1 + H00 x0).
-template <class Rhs, class T, class NB>
-__device__ __forceinline__ T wdense_value(T th, T h, T x0, T x1, T F, const NB &nb) {
+// size h from x0 to x1, h (H11 f(x1) + H10 f(x0)) + (H01 x1 + H00 x0).  V is
+// a real or a tangent number (whose weights and step carry no tangent), T
+// the real type of th and h.
+template <class Rhs, class V, class T, class NB>
+__device__ __forceinline__ V wdense_value(T th, T h, V x0, V x1, V F, const NB &nb) {
   const HermiteW<T> w = hermite_w(th);
-  const T f0 = Rhs::f(x0, F, nb), f1 = Rhs::f(x1, F, nb);
-  const T sl = mac(w.h11, f1, w.h10 * f0);
-  return mac(h, sl, mac(w.h01, x1, w.h00 * x0));
+  const V w00(w.h00), w01(w.h01), w10(w.h10), w11(w.h11), hv(h);
+  const V f0 = Rhs::f(x0, F, nb), f1 = Rhs::f(x1, F, nb);
+  const V sl = mac(w11, f1, w10 * f0);
+  return mac(hv, sl, mac(w01, x1, w00 * x0));
 }
 
 template <class T> __device__ __forceinline__ T wmax(T a, T b) { return (a < b) ? b : a; }
@@ -651,6 +688,125 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   if (c == 0) {
     if (a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * L : nanv<T>();
     if (a.gp) ((T *)a.gp)[tr] = ok ? G : nanv<T>();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Forward-mode sensitivities (mesh held fixed): lane c carries component c of
+// the state with G tangent directions; the d + 1 directions (u0 components,
+// then F) are split into groups of G on the second grid dimension.  Outputs
+// as the lane-per-trajectory kernel: sens[S][d][d+1][n], and with a loss its
+// value and gradient by the chain rule.  The gradient and loss sums run in
+// save-then-component order, one component after the other (each lane's
+// terms are broadcast from that lane), so they follow the same order as the
+// per-trajectory formulas.
+// ---------------------------------------------------------------------------
+template <class T, class M, int G, bool FULL, bool DENSE>
+__global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
+  using Rhs = typename M::Rhs;
+  using DT = DualN<T, G>;
+  const int64_t n = a.n;
+  const WaveId w = wave_id(n);
+  if (!w.live) return;
+  const int64_t j = w.i;
+  const int c = w.c;
+  const int d = a.pr.dim, Q = d + 1;
+  const int q0 = (int)blockIdx.y * G;
+  const bool on = c < d;
+  Nbr<FULL> nb;
+  nb.init(c, d);
+  const int S = a.pr.S;
+  const int lk = a.loss_kind;
+  const bool saves = a.has_loss && lk != DA_LOSS_SUMSQ_FINAL;
+  const T *aux = (const T *)a.aux;
+  T *sens = (T *)a.sens;
+  const int64_t tr = uniform((int)(a.perm ? a.perm[j] : j));
+  int N = uniform(a.nsteps[tr]);
+  const int cap = a.h_rows ? a.rows : a.pr.max_steps;
+  const bool ok = a.status[tr] == LANE_OK && N >= 0 && N <= cap;
+  if (!ok) N = 0;
+  WSteps<T> src;
+  src.init(a, j, tr);
+  DT x(on ? ((const T *)a.u0)[c * n + tr] : T(0));
+  DT F(uniform(((const T *)a.p)[tr]));
+#pragma unroll
+  for (int m = 0; m < G; ++m) {
+    x.d[m] = (on && q0 + m == c) ? T(1) : T(0);
+    F.d[m] = (q0 + m == d) ? T(1) : T(0);
+  }
+  if (sens && on)
+    for (int s = 0; s < S; ++s) {
+      const int ix = a.sidx[s * n + tr];
+      if (!ok || ix < 0 || ix > N)
+#pragma unroll
+        for (int m = 0; m < G; ++m)
+          if (q0 + m < Q) sens[((int64_t)(s * d + c) * Q + q0 + m) * n + tr] = nanv<T>();
+    }
+
+  T g[G], ss = T(0);
+#pragma unroll
+  for (int m = 0; m < G; ++m) g[m] = T(0);
+  bool first = true;
+  // terms of component l for every l < d in order: seed_l . tangent_l into g,
+  // (u_l, v_l) into the loss (u v, or u u when u is v)
+  auto chain = [&](T seed, const DT &yv, T u, T v) {
+    for (int l = 0; l < d; ++l) {
+      const T sd = lane_value(seed, l), ul = lane_value(u, l), vl = lane_value(v, l);
+#pragma unroll
+      for (int m = 0; m < G; ++m) {
+        const T t = lane_value(yv.d[m], l);
+        g[m] = first ? sd * t : mac(sd, t, g[m]);
+      }
+      ss = first ? ul * vl : mac(ul, vl, ss);
+      first = false;
+    }
+  };
+  int s = 0;
+  int nxt = ok ? uniform(a.sidx[tr]) : -1;
+  auto emit = [&](const DT &ysv) {
+    if (sens && on)
+#pragma unroll
+      for (int m = 0; m < G; ++m)
+        if (q0 + m < Q) sens[((int64_t)(s * d + c) * Q + q0 + m) * n + tr] = ysv.d[m];
+    if (saves) {
+      const T av = on ? aux[((int64_t)s * d + c) * n + tr] : T(0);
+      const T yv = ysv.v;
+      if (lk == DA_LOSS_MSE_SAVE) {
+        const T r = yv - av;
+        chain(T(2.0 * a.scale) * r, ysv, r, r);
+      } else {
+        chain(T(a.scale) * av, ysv, av, yv);
+      }
+    }
+    ++s;
+    nxt = s < S ? uniform(a.sidx[s * n + tr]) : -1;
+  };
+  while (s < S && nxt == 0) emit(x);
+  const T *theta = (const T *)a.theta;
+  T hcur = src.load(0);
+  for (int k = 0; k < N; ++k) {
+    const T hnext = src.load(k + 1);
+    const DT xp = x;
+    x = M::fwd(x, F, hcur, nb);
+    while (s < S && nxt == k + 1) {
+      if constexpr (DENSE) emit(wdense_value<Rhs>(theta[(int64_t)s * n + tr], hcur, xp, x, F, nb));
+      else emit(x);
+    }
+    hcur = hnext;
+  }
+  if (a.has_loss && !saves) chain(T(2.0 * a.scale) * x.v, x, x.v, x.v);
+  if (c == 0 && a.has_loss) {
+#pragma unroll
+    for (int m = 0; m < G; ++m) {
+      const int q = q0 + m;
+      const T v = ok ? g[m] : nanv<T>();
+      if (q < d) {
+        if (a.gu0) ((T *)a.gu0)[(int64_t)q * n + tr] = v;
+      } else if (q == d) {
+        if (a.gp) ((T *)a.gp)[tr] = v;
+      }
+    }
+    if (blockIdx.y == 0 && a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * ss : nanv<T>();
   }
 }
 

@@ -306,8 +306,8 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
  * tangents (the same quantity as da_replay_grad computes in reverse).
  * Needs no workspace.  Every method (for ROS2 the tangents run through the
  * Jacobian, the LU factors with the pivots of the values, and both solves)
- * and every right-hand side except Lorenz-96 (DA_EUNSUPPORTED).
- * Trajectories whose record failed get NaN. */
+ * and every right-hand side (Lorenz-96: one wavefront per trajectory, four
+ * directions per lane).  Trajectories whose record failed get NaN. */
 int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
                    const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
                    void *grad_p, void *sens, void *stream);

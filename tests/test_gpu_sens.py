@@ -87,8 +87,8 @@ def test_sensitivities_on_oracle_mesh(da, orc, name, wid, kw, lk, n):
 
 
 def test_sensitivity_options_and_errors(da, orc):
-    """Sensitivities alone (no loss), a replay order with its table, failed
-    trajectories, and the unsupported combinations."""
+    """Sensitivities alone (no loss), a replay order with its table, and
+    failed trajectories."""
     w = W.WORKLOADS[1]
     prob = w.problem(max_steps=45)
     n = 300
@@ -111,12 +111,52 @@ def test_sensitivity_options_and_errors(da, orc):
     assert np.all(np.isnan(q1.cpu().numpy()[:, bad]))
     assert np.all(np.isnan(s1.cpu().numpy()[..., bad]))
     assert not np.any(np.isnan(q1.cpu().numpy()[:, ~bad]))
-    prob_u = W.WORKLOADS[5].problem()
-    iu = W.make_inputs(5, 4)
-    mu, _ = da.record(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch))
-    with pytest.raises(da.DadjError) as e:
-        da.replay_sens(prob_u, to_dev(iu["u0"], torch), to_dev(iu["p"], torch), mu)
-    assert e.value.code == da.DA_EUNSUPPORTED
+
+
+L96_CASES = [
+    # d = 64: neighbours by DPP rotations; 17 direction groups, the last one
+    # holding only the F direction
+    ("d64_tsit5_final", 64, W.TSIT5, W.SUMSQ_FINAL, dict(), 48),
+    ("d64_tsit5_cot_dense", 64, W.TSIT5, W.COTANGENT,
+     dict(dense=1, save_times=(0.13, 0.5, 0.77)), 32),
+    # d < 64: neighbours by cross-lane reads; d = 17 leaves a partly used group
+    ("d40_dopri5_mse", 40, W.DOPRI5, W.MSE_SAVE, dict(save_times=(0.25, 0.5, 1.0)), 40),
+    ("d17_tsit5_cot", 17, W.TSIT5, W.COTANGENT, dict(save_times=(0.1, 0.6, 1.0)), 64),
+]
+
+
+@pytest.mark.parametrize("name,dim,method,lk,kw,n", L96_CASES, ids=[c[0] for c in L96_CASES])
+def test_l96_sensitivities_on_oracle_mesh(da, orc, name, dim, method, lk, kw, n):
+    """Lorenz-96 on the wavefront kernel (one trajectory per wavefront, four
+    directions per lane): sensitivities, loss and gradient against the
+    oracle's fused mode on its mesh, and the gradient against the reverse
+    sweep."""
+    inp = W.make_inputs(5, n)
+    u0n = np.ascontiguousarray(inp["u0"][:, :dim])
+    pn = inp["p"]
+    prob = W.Problem(W.LORENZ96, dim, 1, method, 0.0, 1.0, 1e-7, 1e-7, 4096)
+    prob = prob.replace(**kw)
+    _print(f"case: Lorenz-96 sensitivities {name}, n={n}")
+    m = orc.record(prob, u0n, pn, fused=True)
+    assert np.all(m["status"] == 0)
+    S = prob.n_save_eff
+    aux = None if lk == W.SUMSQ_FINAL else np.random.default_rng(dim).standard_normal((n, S, dim))
+    so, lo, go, po = orc.replay_sens(prob, u0n, pn, m, lk, aux=aux, scale=0.4, fused=True)
+    mesh = mesh_to_dev(m, prob.max_steps, torch)
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    sg, lg, gu0, gp = da.replay_sens(prob, u0, p, mesh, lk, aux=auxd, scale=0.4)
+    la, ga, pa = da.replay_grad(prob, u0, p, mesh, lk, aux=auxd, scale=0.4)
+    torch.cuda.synchronize()
+    es = _sens_err(sg.cpu().numpy().transpose(3, 0, 1, 2), so)
+    eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+    el = np.abs(lg.cpu().numpy() - lo) / np.abs(lo)
+    ea = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, ga.cpu().numpy().T,
+                      pa.cpu().numpy().T)
+    _print(f"  sens max rel {es.max():.3e} (bitwise lanes {np.mean(es == 0):.3f}), "
+           f"grad {eg.max():.3e}, loss {el.max():.3e}, forward vs reverse {ea.max():.3e}")
+    assert es.max() <= 1e-12 and eg.max() <= 1e-12 and el.max() <= 1e-12
+    assert ea.max() <= 1e-10
 
 
 def test_ros2_sensitivities_with_row_exchanges(da, orc):
@@ -158,11 +198,12 @@ def test_ros2_sensitivities_with_row_exchanges(da, orc):
     assert es.max() <= 1e-12 and eg.max() <= 1e-12 and ea.max() <= 1e-10
 
 
-@pytest.mark.parametrize("wid", [2, 4])
+@pytest.mark.parametrize("wid", [2, 4, 5])
 def test_full_size_sensitivities_sampled(da, orc, wid):
-    """Lorenz-63 with Dopri5 (2^20 trajectories) and Robertson with ROS2
-    (65536) at full size: record, replay order with table, forward-mode
-    gradient; sampled trajectories against the oracle on the GPU's mesh."""
+    """Lorenz-63 with Dopri5 (2^20 trajectories), Robertson with ROS2 (65536)
+    and Lorenz-96 at d = 64 (16384) at full size: record, replay order with
+    table, forward-mode gradient; sampled trajectories against the oracle on
+    the GPU's mesh."""
     w = W.WORKLOADS[wid]
     prob = w.problem()
     inp = W.make_inputs(wid)
@@ -191,8 +232,9 @@ def test_full_size_sensitivities_sampled(da, orc, wid):
 
 
 @pytest.mark.parametrize("wid,kw", [(3, dict(t1=1.0, save_times=(0.5, 1.0))),
-                                    (4, dict(t1=10.0, rtol=1e-4, atol=1e-8))],
-                         ids=["lorenz63_tsit5", "robertson_ros2"])
+                                    (4, dict(t1=10.0, rtol=1e-4, atol=1e-8)),
+                                    (5, dict(t1=0.5, rtol=1e-5, atol=1e-5))],
+                         ids=["lorenz63_tsit5", "robertson_ros2", "lorenz96_tsit5"])
 def test_sensitivities_fp32(da, orc, wid, kw):
     """FP32 tangents against the FP64 oracle on the FP32 mesh (the tangent
     arithmetic in single precision)."""
