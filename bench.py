@@ -277,17 +277,24 @@ def main():
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
     pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
                              for k in range(passes)]))
-    # forward-mode gradient of the same loss on the same replay order and table
-    sens_ms = []
-    for r in range(3):
-        a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a0.record(stream)
-        da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux, scale=scale,
-                       with_sens=False)
-        a1.record(stream)
-        torch.cuda.synchronize()
-        if r > 0:
-            sens_ms.append(a0.elapsed_time(a1))
+    # forward-mode gradient of the same loss on the same replay order and
+    # table: all d + P directions, and the P parameter directions alone
+    def timed(fn):
+        out = []
+        for r in range(3):
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            fn()
+            a1.record(stream)
+            torch.cuda.synchronize()
+            if r > 0:
+                out.append(a0.elapsed_time(a1))
+        return out
+    sens_ms = timed(lambda: da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux,
+                                           scale=scale, with_sens=False))
+    sens_p_ms = timed(lambda: da.replay_sens_dirs(prob, u0, p, state["call"].mesh, prob.dim,
+                                                  prob.n_params, w.loss, aux=aux, scale=scale,
+                                                  with_sens=False))
     # forward-only adaptive solve of the same ensemble (outside the job)
     solve_ms = []
     for r in range(3):
@@ -337,6 +344,10 @@ def main():
             "flop_per_step": sens_flop,
             "achieved_tflops": None if sens_flop is None
             else sens_flop * total_steps / (float(np.mean(sens_ms)) * 1e-3) / 1e12},
+        "forward_mode_param_grad": {
+            "ms": float(np.mean(sens_p_ms)),
+            "directions": prob.n_params,
+            "trajectory_gradients_per_s": n / (float(np.mean(sens_p_ms)) * 1e-3)},
         "solve_fwd": {"ms": float(np.mean(solve_ms)),
                       "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],

@@ -46,7 +46,8 @@ MAX_SAVES = 128
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_pad",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
-           "da_replay_sens", "da_rhs_register", "da_rhs_release", "da_last_error", "da_version")
+           "da_replay_sens", "da_replay_sens_dirs", "da_rhs_register", "da_rhs_release",
+           "da_last_error", "da_version")
 
 
 class DadjError(RuntimeError):
@@ -108,11 +109,14 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp]
     lib.da_replay_sens.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, vp, vp]
+    lib.da_replay_sens_dirs.argtypes = [P, i64, vp, vp, M, i32, i32, ctypes.POINTER(_Loss), vp,
+                                        vp, vp, vp]
     lib.da_rhs_register.argtypes = [ctypes.POINTER(_RhsDef), ctypes.POINTER(ctypes.c_int32)]
     lib.da_rhs_release.argtypes = [i32]
     lib.da_last_error.restype = ctypes.c_char_p
     for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps", "da_mesh_pad",
-                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_rhs_register",
+                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_replay_sens_dirs",
+                 "da_rhs_register",
                  "da_rhs_release", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -421,3 +425,29 @@ def replay_sens(prob, u0, p, mesh: Mesh, loss_kind: Optional[int] = SUMSQ_FINAL,
     _check(_lib.da_replay_sens(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm), lp,
                                _ptr(loss), _ptr(gu0), _ptr(gp), _ptr(sens), _stream(stream)))
     return sens, loss, gu0, gp
+
+
+def replay_sens_dirs(prob, u0, p, mesh: Mesh, q_begin: int, q_count: int,
+                     loss_kind: Optional[int] = SUMSQ_FINAL, aux=None, scale: float = 1.0,
+                     with_sens: bool = True, stream=None):
+    """Forward-mode sensitivities along the unit directions q_begin ..
+    q_begin + q_count - 1 of the d + P (u0 components, then parameters):
+    (sens [S, d, q_count, n] or None, loss [n], grad [q_count, n])."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    dev = u0.device
+    if aux is not None:
+        _need(aux, (S, prob.dim, n), dt, "aux")
+    sens = torch.empty((S, prob.dim, q_count, n), dtype=dt, device=dev) if with_sens else None
+    loss = torch.empty(n, dtype=dt, device=dev)
+    grad = torch.empty((max(q_count, 0), n), dtype=dt, device=dev)
+    P, keep = cproblem(prob, dt)
+    cm = mesh.c()
+    lp = None
+    if loss_kind is not None:
+        lobj = _Loss(loss_kind, None if aux is None else aux.data_ptr(), scale)
+        lp = ctypes.byref(lobj)
+    _check(_lib.da_replay_sens_dirs(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm),
+                                    int(q_begin), int(q_count), lp, _ptr(loss), _ptr(grad),
+                                    _ptr(sens), _stream(stream)))
+    return sens, loss, grad

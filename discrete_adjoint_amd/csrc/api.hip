@@ -414,12 +414,23 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   return ok();
 }
 
-int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
-                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
-                   void *grad_p, void *sens, void *stream) {
+// Forward-mode sensitivities along directions q_begin .. q_begin + q_count - 1
+// (q_count < 0: all d + P); gq, when not null, takes the gradient of the range.
+static int replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                       const da_mesh *mesh, int32_t q_begin, int32_t q_count, const da_loss *loss,
+                       void *loss_out, void *grad_u0, void *grad_p, void *gq, void *sens,
+                       void *stream) {
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
+  const int Q = pr.dim + pr.n_params;
+  if (q_count < 0) {
+    q_begin = 0;
+    q_count = Q;
+  }
+  if (q_begin < 0 || q_count < 1 || q_begin > Q - q_count)
+    return fail(DA_EINVAL, "direction range [%d, %d + %d) outside the %d directions", q_begin,
+                q_begin, q_count, Q);
   if (n == 0) return ok();
   if ((rc = check_mesh(mesh, true, pr.max_steps))) return rc;
   if (pr.dense && (sens || (loss && loss->kind != DA_LOSS_SUMSQ_FINAL)) && !mesh->save_theta)
@@ -435,6 +446,8 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
   dadj::ReplayArgs a;
   fill_replay_args(a, pr, n, u0, p, mesh);
   a.sens = sens;
+  a.q_begin = q_begin;
+  a.q_count = q_count;
   a.has_loss = loss != nullptr;
   if (loss) {
     a.loss_kind = loss->kind;
@@ -443,6 +456,7 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
     a.loss_out = loss_out;
     a.gu0 = grad_u0;
     a.gp = grad_p;
+    a.gq = gq;
   }
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = user_rhs(pr)                   ? dadj::launch_rtc_replay_sens(a, s)
@@ -451,6 +465,22 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
                                                      : dadj::launch_erk_replay_sens(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_sens launch");
   return ok();
+}
+
+int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                   void *grad_p, void *sens, void *stream) {
+  return replay_sens(prob, n, u0, p, mesh, 0, -1, loss, loss_out, grad_u0, grad_p, nullptr, sens,
+                     stream);
+}
+
+int da_replay_sens_dirs(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                        const da_mesh *mesh, int32_t q_begin, int32_t q_count,
+                        const da_loss *loss, void *loss_out, void *grad, void *sens,
+                        void *stream) {
+  if (q_count < 1) return fail(DA_EINVAL, "q_count must be at least 1");
+  return replay_sens(prob, n, u0, p, mesh, q_begin, q_count, loss, loss_out, nullptr, nullptr,
+                     grad, sens, stream);
 }
 
 }  // extern "C"

@@ -69,8 +69,10 @@ struct ReplayArgs {
   double scale;
   void *loss_out, *gu0, *gp;   // [n], [d][n], [P][n]
   void *ws;                    // [ceil(max_n_steps / checkpoint)][d][ws_lanes]
-  void *sens;                  // sensitivity output [S][d][d+P][n] or null
+  void *sens;                  // sensitivity output [S][d][q_count][n] or null
   int32_t has_loss;            // sensitivity call: loss outputs requested
+  int32_t q_begin, q_count;    // sensitivity call: unit directions q_begin .. + q_count - 1
+  void *gq;                    // sensitivity call: gradient [q_count][n] (else gu0 / gp)
   int64_t slot0, nslots, ws_lanes;
   int32_t max_n_steps;
 };

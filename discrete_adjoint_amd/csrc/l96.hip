@@ -68,15 +68,21 @@ hipError_t wreplay_grad_t(const ReplayArgs &a, hipStream_t s) {
   return dense ? wreplay_grad_d<T, M, true>(a, s) : wreplay_grad_d<T, M, false>(a, s);
 }
 
-// Sensitivities: 4 tangent directions per lane; ceil((d + 1) / 4) direction
-// groups on the second grid dimension.
+// Sensitivities: 4 tangent directions per lane, ceil(q_count / 4) direction
+// groups on the second grid dimension; a single direction (such as F alone)
+// takes one per lane.
 constexpr int WSENS_G = 4;
 template <class T, class M, bool FULL, bool DENSE>
 hipError_t wreplay_sens_f(const ReplayArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n + WAVES - 1) / WAVES),
-                  (unsigned)((a.pr.dim + 1 + WSENS_G - 1) / WSENS_G));
-  hipLaunchKernelGGL((wave::k_wreplay_sens<T, M, WSENS_G, FULL, DENSE>), grid, 64 * WAVES, 0, s,
-                     a);
+  if (a.q_count == 1) {
+    const dim3 grid((unsigned)((a.n + WAVES - 1) / WAVES), 1);
+    hipLaunchKernelGGL((wave::k_wreplay_sens<T, M, 1, FULL, DENSE>), grid, 64 * WAVES, 0, s, a);
+  } else {
+    const dim3 grid((unsigned)((a.n + WAVES - 1) / WAVES),
+                    (unsigned)((a.q_count + WSENS_G - 1) / WSENS_G));
+    hipLaunchKernelGGL((wave::k_wreplay_sens<T, M, WSENS_G, FULL, DENSE>), grid, 64 * WAVES, 0,
+                       s, a);
+  }
   return hipGetLastError();
 }
 template <class T, class M, bool DENSE>

@@ -14,8 +14,10 @@ namespace dadj {
 
 constexpr int SENS_G = 2;  // tangent directions per lane and grid row
 
-// Gradient terms seed . dy/dtheta_q in save-then-component order (first
-// product, then multiply-adds), the seeds being
+// Directions q_begin .. q_begin + q_count - 1 of the d + P; sens and the
+// gradient hold them at q - q_begin.  Gradient terms seed . dy/dtheta_q in
+// save-then-component order (first product, then multiply-adds), the seeds
+// being
 //   final-state loss: (2 scale) y_N    MSE: (2 scale) (y_s - aux_s)
 //   cotangent:        scale aux_s.
 // DENSE: a save with index k >= 1 (and its tangents) is the interpolant of
@@ -23,12 +25,12 @@ constexpr int SENS_G = 2;  // tangent directions per lane and grid row
 template <class T, class M, int G, bool ROWS, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
   using Rhs = typename M::Rhs;
-  constexpr int D = Rhs::D, P = Rhs::P, Q = D + P;
+  constexpr int D = Rhs::D, P = Rhs::P;
   using DT = DualN<T, G>;
   const int64_t n = a.n;
   const int64_t j = (int64_t)blockIdx.x * BLOCK + threadIdx.x;
   const bool live = j < n;
-  const int q0 = (int)blockIdx.y * G;
+  const int q0 = a.q_begin + (int)blockIdx.y * G, qe = a.q_begin + a.q_count, Qo = a.q_count;
   const int S = a.pr.S;
   const int lk = a.loss_kind;
   const bool saves = a.has_loss && lk != DA_LOSS_SUMSQ_FINAL;
@@ -62,7 +64,8 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
           for (int c = 0; c < D; ++c)
 #pragma unroll
             for (int m = 0; m < G; ++m)
-              if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = nanv<T>();
+              if (q0 + m < qe)
+                sens[((int64_t)(s * D + c) * Qo + q0 + m - a.q_begin) * n + tr] = nanv<T>();
       }
   }
   const int Nw = wave_max(N);
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
       for (int c = 0; c < D; ++c)
 #pragma unroll
         for (int m = 0; m < G; ++m)
-          if (q0 + m < Q) sens[((int64_t)(s * D + c) * Q + q0 + m) * n + tr] = ysv[c].d[m];
+          if (q0 + m < qe) sens[((int64_t)(s * D + c) * Qo + q0 + m - a.q_begin) * n + tr] = ysv[c].d[m];
     if (saves) {
 #pragma unroll
       for (int c = 0; c < D; ++c) {
@@ -147,9 +150,12 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
     for (int m = 0; m < G; ++m) {
       const int q = q0 + m;
       const T v = ok ? g[m] : nanv<T>();
-      if (q < D) {
+      if (q >= qe) continue;
+      if (a.gq) {
+        ((T *)a.gq)[(int64_t)(q - a.q_begin) * n + tr] = v;
+      } else if (q < D) {
         if (a.gu0) ((T *)a.gu0)[q * n + tr] = v;
-      } else if (q < Q) {
+      } else {
         if (a.gp) ((T *)a.gp)[(q - D) * n + tr] = v;
       }
     }
@@ -158,12 +164,12 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
 }
 
 #ifndef __HIPCC_RTC__
-// Launch: one lane per trajectory, the d + P directions in groups of G on the
+// Launch: one lane per trajectory, the directions in groups of G on the
 // second grid dimension.
 template <class T, class M, bool DENSE>
 hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {
-  constexpr int Q = M::Rhs::D + M::Rhs::P;
-  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK), (unsigned)((Q + SENS_G - 1) / SENS_G));
+  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK),
+                  (unsigned)((a.q_count + SENS_G - 1) / SENS_G));
   if (a.h_rows)
     hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true, DENSE>), grid, BLOCK, 0, s, a);
   else

@@ -693,10 +693,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
 
 // ---------------------------------------------------------------------------
 // Forward-mode sensitivities (mesh held fixed): lane c carries component c of
-// the state with G tangent directions; the d + 1 directions (u0 components,
-// then F) are split into groups of G on the second grid dimension.  Outputs
-// as the lane-per-trajectory kernel: sens[S][d][d+1][n], and with a loss its
-// value and gradient by the chain rule.  The gradient and loss sums run in
+// the state with G tangent directions; the directions q_begin .. q_begin +
+// q_count - 1 of the d + 1 (u0 components, then F) are split into groups of G
+// on the second grid dimension.  Outputs as the lane-per-trajectory kernel:
+// sens[S][d][q_count][n], and with a loss its value and gradient by the chain
+// rule.  The gradient and loss sums run in
 // save-then-component order, one component after the other (each lane's
 // terms are broadcast from that lane), so they follow the same order as the
 // per-trajectory formulas.
@@ -710,8 +711,8 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
   if (!w.live) return;
   const int64_t j = w.i;
   const int c = w.c;
-  const int d = a.pr.dim, Q = d + 1;
-  const int q0 = (int)blockIdx.y * G;
+  const int d = a.pr.dim;
+  const int q0 = a.q_begin + (int)blockIdx.y * G, qe = a.q_begin + a.q_count, Qo = a.q_count;
   const bool on = c < d;
   Nbr<FULL> nb;
   nb.init(c, d);
@@ -740,7 +741,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
       if (!ok || ix < 0 || ix > N)
 #pragma unroll
         for (int m = 0; m < G; ++m)
-          if (q0 + m < Q) sens[((int64_t)(s * d + c) * Q + q0 + m) * n + tr] = nanv<T>();
+          if (q0 + m < qe) sens[((int64_t)(s * d + c) * Qo + q0 + m - a.q_begin) * n + tr] = nanv<T>();
     }
 
   T g[G], ss = T(0);
@@ -767,7 +768,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
     if (sens && on)
 #pragma unroll
       for (int m = 0; m < G; ++m)
-        if (q0 + m < Q) sens[((int64_t)(s * d + c) * Q + q0 + m) * n + tr] = ysv.d[m];
+        if (q0 + m < qe) sens[((int64_t)(s * d + c) * Qo + q0 + m - a.q_begin) * n + tr] = ysv.d[m];
     if (saves) {
       const T av = on ? aux[((int64_t)s * d + c) * n + tr] : T(0);
       const T yv = ysv.v;
@@ -800,9 +801,12 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
     for (int m = 0; m < G; ++m) {
       const int q = q0 + m;
       const T v = ok ? g[m] : nanv<T>();
-      if (q < d) {
+      if (q >= qe) continue;
+      if (a.gq) {
+        ((T *)a.gq)[(int64_t)(q - a.q_begin) * n + tr] = v;
+      } else if (q < d) {
         if (a.gu0) ((T *)a.gu0)[(int64_t)q * n + tr] = v;
-      } else if (q == d) {
+      } else {
         if (a.gp) ((T *)a.gp)[tr] = v;
       }
     }

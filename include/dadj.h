@@ -312,6 +312,23 @@ int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void
                    const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
                    void *grad_p, void *sens, void *stream);
 
+/* da_replay_sens restricted to the unit directions q_begin .. q_begin +
+ * q_count - 1 of the d + P (u0 components first, then parameters).  Forward
+ * mode costs one replay per group of directions, which is why it pays when
+ * few directions are wanted ("Differentiable astrophysics at scale",
+ * Methodology: forward sensitivities with respect to the parameters suit
+ * problems with few parameters and many outputs): the P parameter directions
+ * of a system with many state components are q_begin = d, q_count = P.
+ * Outputs (each may be NULL): sens [S][d][q_count][n] with
+ * d y(save s)[c] / d theta_q at q - q_begin; with loss not NULL, loss_out [n]
+ * and grad [q_count][n], dL / d theta_q at q - q_begin.  Each direction's
+ * values are those da_replay_sens gives for it (the directions do not
+ * interact).  DA_EINVAL when the range is empty or outside [0, d + P). */
+int da_replay_sens_dirs(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                        const da_mesh *mesh, int32_t q_begin, int32_t q_count,
+                        const da_loss *loss, void *loss_out, void *grad, void *sens,
+                        void *stream);
+
 /* Right-hand side compiled at run time ("GRADSOLVE", evolve.pub review, FAQ:
  * registered right-hand sides of small dimension run in the fused kernels,
  * hand-written or translated from the caller's function).  The caller gives

@@ -142,6 +142,24 @@ def test_dense_output_checks(da):
     assert "save_theta" in da.last_error()
 
 
+def test_sensitivity_direction_range_checks(da):
+    """da_replay_sens_dirs refuses an empty range and one outside the d + P
+    directions before it touches any buffer."""
+    lib = da.library()
+    for prob, Q in ((W.WORKLOADS[1].problem(), 6), (W.WORKLOADS[5].problem(), 65)):
+        P, keep = da.cproblem(prob, __import__("torch").float64)
+        m = da._Mesh(64, 8, 8, 8, None)          # aligned fake addresses
+        args = (ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.byref(m))
+        for qb, qc in ((0, 0), (-1, 2), (0, Q + 1), (Q - 1, 2), (Q, 1), (2, -3)):
+            rc = lib.da_replay_sens_dirs(ctypes.byref(P), 4, *args, qb, qc, None, None, None,
+                                         None, None)
+            assert rc == -1, (qb, qc)
+            assert "q_count" in da.last_error() or "direction range" in da.last_error()
+        # an empty ensemble with a valid range is a no-op
+        assert lib.da_replay_sens_dirs(ctypes.byref(P), 0, *args, Q - 1, 1, None, None, None,
+                                       None, None) == 0
+
+
 def test_rhs_registration_checks(da):
     """Argument checks of da_rhs_register, and compilation, which needs no
     GPU: a source with an error is refused with the compiler's message; a

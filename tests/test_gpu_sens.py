@@ -159,6 +159,47 @@ def test_l96_sensitivities_on_oracle_mesh(da, orc, name, dim, method, lk, kw, n)
     assert ea.max() <= 1e-10
 
 
+RANGE_CASES = [
+    ("lorenz63_dopri5", W.Problem(W.LORENZ63, 3, 3, W.DOPRI5, 0.0, 1.5, 1e-8, 1e-8, 4096,
+                                  save_times=(0.4, 1.1, 1.5)), 1, 500,
+     [(3, 3), (0, 1), (5, 1), (1, 4)]),
+    ("robertson_ros2", W.WORKLOADS[4].problem(t1=100.0), 4, 300, [(3, 3), (2, 1)]),
+    ("l96_d64_tsit5", W.Problem(W.LORENZ96, 64, 1, W.TSIT5, 0.0, 1.0, 1e-7, 1e-7, 4096,
+                                save_times=(0.3, 1.0)), 5, 96, [(64, 1), (30, 7), (0, 65)]),
+    ("l96_d40_dopri5_dense", W.Problem(W.LORENZ96, 40, 1, W.DOPRI5, 0.0, 1.0, 1e-7, 1e-7, 4096,
+                                       save_times=(0.37, 0.81), dense=1), 5, 80,
+     [(40, 1), (38, 3)]),
+]
+
+
+@pytest.mark.parametrize("name,prob,wid,n,ranges", RANGE_CASES, ids=[c[0] for c in RANGE_CASES])
+def test_direction_ranges_equal_full_call(da, name, prob, wid, n, ranges):
+    """da_replay_sens_dirs over a range of directions gives, bit for bit, that
+    range of da_replay_sens's sensitivities and gradient, and the same loss
+    (the directions do not interact; a single Lorenz-96 direction runs one
+    per lane)."""
+    inp = W.make_inputs(wid, n)
+    u0n = np.ascontiguousarray(inp["u0"][:, :prob.dim])
+    u0, p = to_dev(u0n, torch), to_dev(inp["p"], torch)
+    S = prob.n_save_eff
+    auxd = aux_to_dev(np.random.default_rng(11).standard_normal((n, S, prob.dim)), torch)
+    _print(f"case: direction ranges {name}, n={n}")
+    mesh, _ = da.record(prob, u0, p)
+    sf, lf, gu0, gp = da.replay_sens(prob, u0, p, mesh, W.COTANGENT, aux=auxd, scale=0.25)
+    torch.cuda.synchronize()
+    assert torch.all(mesh.status == 0)
+    gall = torch.cat([gu0, gp])
+    for qb, qc in ranges:
+        sr, lr, gr = da.replay_sens_dirs(prob, u0, p, mesh, qb, qc, W.COTANGENT, aux=auxd,
+                                         scale=0.25)
+        torch.cuda.synchronize()
+        assert sr.shape == (S, prob.dim, qc, n) and gr.shape == (qc, n)
+        assert torch.equal(sr, sf[:, :, qb:qb + qc]), (qb, qc)
+        assert torch.equal(gr, gall[qb:qb + qc]), (qb, qc)
+        assert torch.equal(lr, lf), (qb, qc)
+    _print(f"  {len(ranges)} ranges equal to the full call")
+
+
 def test_ros2_sensitivities_with_row_exchanges(da, orc):
     """ROS2 on Lorenz-63 over a coarse hand-made mesh (per-trajectory step
     sizes 0.02..0.2), where the LU of W = I - gamma h J exchanges rows in some

@@ -121,6 +121,10 @@ def test_source_variants_checkpoints_table_dense_sens(da, orc, rhs):
     es = rel_err(sg.cpu().numpy().transpose(3, 0, 1, 2).reshape(n, -1), so.reshape(n, -1))
     _print(f"  sensitivities max rel {es.max():.3e}")
     assert es.max() <= 1e-12
+    # the parameter directions alone
+    sq, lq, gq = da.replay_sens_dirs(prob, u0, p, mesh, 3, 3, W.COTANGENT, aux=auxd, scale=0.5)
+    torch.cuda.synchronize()
+    assert torch.equal(sq, sg[:, :, 3:]) and torch.equal(gq, sp) and torch.equal(lq, lg)
     # dense output
     dprob = prob.replace(dense=1, save_times=(0.33, 0.9, 1.21))
     md = orc.record(dprob, inp["u0"], inp["p"], fused=True)
