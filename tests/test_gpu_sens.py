@@ -200,6 +200,36 @@ def test_direction_ranges_equal_full_call(da, name, prob, wid, n, ranges):
     _print(f"  {len(ranges)} ranges equal to the full call")
 
 
+def test_l96_sensitivity_options(da):
+    """Lorenz-96 forward mode with an ensemble that does not fill its last
+    workgroup, a failed trajectory (NaN everywhere, the others finite), the
+    replay order with its table (bit-for-bit the same as the record order),
+    and sensitivities without a loss."""
+    n, dim = 97, 64
+    inp = W.make_inputs(5, n)
+    inp["p"][5, 0] = np.nan
+    prob = W.Problem(W.LORENZ96, dim, 1, W.TSIT5, 0.0, 0.6, 1e-7, 1e-7, 4096,
+                     save_times=(0.2, 0.6))
+    _print(f"case: Lorenz-96 sensitivity options, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    auxd = aux_to_dev(np.random.default_rng(2).standard_normal((n, 2, dim)), torch)
+    s1, l1, g1, q1 = da.replay_sens(prob, u0, p, mesh, W.MSE_SAVE, aux=auxd, scale=0.5)
+    s2, l2, g2, q2 = da.replay_sens(prob, u0, p, sm, W.MSE_SAVE, aux=auxd, scale=0.5)
+    s3, _, _, _ = da.replay_sens(prob, u0, p, sm, loss_kind=None)
+    torch.cuda.synchronize()
+    bad = mesh.status.cpu().numpy() != 0
+    assert bad[5] and bad.sum() == 1
+    for a, b in ((s1, s2), (s1, s3), (l1, l2), (g1, g2), (q1, q2)):
+        assert torch.equal(torch.nan_to_num(a), torch.nan_to_num(b))
+    s1n = s1.cpu().numpy()
+    assert np.all(np.isnan(s1n[..., bad])) and np.all(np.isfinite(s1n[..., ~bad]))
+    for t in (l1, g1, q1):
+        tn = t.cpu().numpy()
+        assert np.all(np.isnan(tn[..., bad])) and np.all(np.isfinite(tn[..., ~bad]))
+
+
 def test_ros2_sensitivities_with_row_exchanges(da, orc):
     """ROS2 on Lorenz-63 over a coarse hand-made mesh (per-trajectory step
     sizes 0.02..0.2), where the LU of W = I - gamma h J exchanges rows in some
