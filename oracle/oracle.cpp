@@ -55,7 +55,7 @@ namespace {
 constexpr int MAXD = 64;  // largest state dimension handled
 constexpr int MAXP = 16;  // largest parameter count
 
-enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2 };
+enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3 };
 enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3 };
 constexpr int R_USER = 1024;  /* kinds from here: the caller's right-hand side */
 enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
@@ -756,6 +756,158 @@ void ros2_step_adjoint(int kind, int d, const T *y, const T *p, T h, T *lam, T *
 }
 
 /* ------------------------------------------------------------------ */
+/* Rodas3 step                                                         */
+/* ------------------------------------------------------------------ */
+
+/* Rodas3 (Sandu, Verwer, Blom, Spee, Carmichael and Potra 1997, the
+ * Rosenbrock solvers of atmospheric chemistry): four stages, order 3,
+ * stiffly accurate and L-stable, with an embedded second-order solution.
+ * With the same W = I - gamma h J as ROS2 (gamma = 1/2) the stages are
+ *   Y_i = y + sum_{j<i} a_ij u_j,
+ *   u_i = W^-1 (gamma h f(Y_i) + sum_{j<i} gamma c_ij u_j),
+ * and y+ = y + sum m_i u_i, err = sum e_i u_i (here u_4).  The published form
+ * solves (I / (gamma h) - J) u_i = f(Y_i) + sum_j (c_ij / h) u_j, which is the
+ * same system multiplied by gamma h.  The coefficients are the published
+ * ones; a test checks that they give order 3, L-stability and a second-order
+ * embedded estimate. */
+struct RosTab {
+  int s;
+  double gamma;
+  double a[4][4], c[4][4], gc[4][4];  /* gc = gamma c */
+  double m[4], e[4];
+  int order, err_order;
+};
+
+RosTab make_rodas3() {
+  RosTab t = {};
+  t.s = 4;
+  t.gamma = 0.5;
+  t.a[2][0] = 2.0; t.a[3][0] = 2.0; t.a[3][2] = 1.0;
+  t.c[1][0] = 4.0;
+  t.c[2][0] = 1.0; t.c[2][1] = -1.0;
+  t.c[3][0] = 1.0; t.c[3][1] = -1.0; t.c[3][2] = -8.0 / 3.0;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) t.gc[i][j] = t.gamma * t.c[i][j];
+  t.m[0] = 2.0; t.m[1] = 0.0; t.m[2] = 1.0; t.m[3] = 1.0;
+  t.e[3] = 1.0;
+  t.order = 3; t.err_order = 2;
+  return t;
+}
+const RosTab RODAS3 = make_rodas3();
+
+template <class T>
+struct RodasStep {
+  T J[9], LU[9];
+  int perm[3];
+  T Y[4][3], f[4][3], r[4][3], u[4][3], ynew[3], err[3];
+};
+
+/* Stage sums: Y_i from y, adding a_ij u_j for j = 0, 1, ...; r_i the sum of
+ * gamma c_ij u_j (first a product, then multiply-adds), then gamma h f(Y_i)
+ * added last; y+ from y adding m_i u_i in stage order. */
+template <class T, bool F>
+void rodas_forward(const RosTab &tb, int kind, int d, const T *y, const T *p, T h,
+                   RodasStep<T> &s) {
+  rhs_jac<T, F>(kind, d, y, p, s.J);
+  const T gh = T(tb.gamma) * h;
+  for (int a = 0; a < d; ++a)
+    for (int b = 0; b < d; ++b)
+      s.LU[a * d + b] = (a == b) ? mac<F>(-gh, s.J[a * d + b], T(1.0)) : (-gh) * s.J[a * d + b];
+  lu_factor<T, F>(d, s.LU, s.perm);
+  for (int i = 0; i < tb.s; ++i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = y[c];
+      for (int j = 0; j < i; ++j)
+        if (tb.a[i][j] != 0.0) acc = mac<F>(T(tb.a[i][j]), s.u[j][c], acc);
+      s.Y[i][c] = acc;
+    }
+    rhs_f<T, F>(kind, d, s.Y[i], p, s.f[i]);
+    for (int c = 0; c < d; ++c) {
+      T acc = T(0.0);
+      bool first = true;
+      for (int j = 0; j < i; ++j)
+        if (tb.gc[i][j] != 0.0) {
+          acc = first ? T(tb.gc[i][j]) * s.u[j][c] : mac<F>(T(tb.gc[i][j]), s.u[j][c], acc);
+          first = false;
+        }
+      s.r[i][c] = first ? gh * s.f[i][c] : mac<F>(gh, s.f[i][c], acc);
+    }
+    lu_solve<T, F>(d, s.LU, s.perm, s.r[i], s.u[i]);
+  }
+  for (int c = 0; c < d; ++c) {
+    T acc = y[c];
+    for (int i = 0; i < tb.s; ++i)
+      if (tb.m[i] != 0.0) acc = mac<F>(T(tb.m[i]), s.u[i][c], acc);
+    s.ynew[c] = acc;
+    T e = T(0.0);
+    bool first = true;
+    for (int i = 0; i < tb.s; ++i)
+      if (tb.e[i] != 0.0) {
+        e = first ? T(tb.e[i]) * s.u[i][c] : mac<F>(T(tb.e[i]), s.u[i][c], e);
+        first = false;
+      }
+    s.err[c] = e;
+  }
+}
+
+template <class T, bool F>
+void rodas_step(const RosTab &tb, int kind, int d, T *y, const T *p, T h) {
+  RodasStep<T> s;
+  rodas_forward<T, F>(tb, kind, d, y, p, h, s);
+  for (int c = 0; c < d; ++c) y[c] = s.ynew[c];
+}
+
+/* Reverse of rodas_step (mesh fixed), stages from the last to the first:
+ *   ubar_i = m_i lam + sum_{l>i} (a_li Ybar_l + gamma c_li rbar_l)
+ *            (in that order: the m term, then l = i+1, ... with its a term
+ *            before its c term; first a product, then multiply-adds)
+ *   rbar_i = W^-T ubar_i,  Wbar -= rbar_i u_i^T,  fbar_i = gamma h rbar_i,
+ *   Ybar_i = J(Y_i)^T fbar_i,  g += J_p(Y_i)^T fbar_i,  ybar += Ybar_i;
+ * then Jbar = -gamma h Wbar contracted with the derivative of J at y. */
+template <class T, bool F>
+void rodas_step_adjoint(const RosTab &tb, int kind, int d, const T *y, const T *p, T h, T *lam,
+                        T *gp) {
+  RodasStep<T> s;
+  rodas_forward<T, F>(tb, kind, d, y, p, h, s);
+  const T gh = T(tb.gamma) * h;
+  T yb[3], ub[3], fb[3], rb[4][3], Yb[4][3], Wb[9], Jb[9];
+  for (int c = 0; c < d; ++c) yb[c] = lam[c];
+  for (int i = tb.s - 1; i >= 0; --i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = T(0.0);
+      bool first = true;
+      if (tb.m[i] != 0.0) {
+        acc = T(tb.m[i]) * lam[c];
+        first = false;
+      }
+      for (int l = i + 1; l < tb.s; ++l) {
+        if (tb.a[l][i] != 0.0) {
+          acc = first ? T(tb.a[l][i]) * Yb[l][c] : mac<F>(T(tb.a[l][i]), Yb[l][c], acc);
+          first = false;
+        }
+        if (tb.gc[l][i] != 0.0) {
+          acc = first ? T(tb.gc[l][i]) * rb[l][c] : mac<F>(T(tb.gc[l][i]), rb[l][c], acc);
+          first = false;
+        }
+      }
+      ub[c] = acc;
+    }
+    lu_solve_t<T, F>(d, s.LU, s.perm, ub, rb[i]);
+    for (int a = 0; a < d; ++a)
+      for (int b = 0; b < d; ++b)
+        Wb[a * d + b] = (i == tb.s - 1) ? (-rb[i][a]) * s.u[i][b]
+                                        : mac<F>(-rb[i][a], s.u[i][b], Wb[a * d + b]);
+    for (int c = 0; c < d; ++c) fb[c] = gh * rb[i][c];
+    rhs_vjp_y<T, F>(kind, d, s.Y[i], p, fb, Yb[i]);
+    rhs_vjp_p_acc<T, F>(kind, d, s.Y[i], p, fb, gp);
+    for (int c = 0; c < d; ++c) yb[c] = yb[c] + Yb[i][c];
+  }
+  for (int q = 0; q < d * d; ++q) Jb[q] = (-gh) * Wb[q];
+  rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);
+  for (int c = 0; c < d; ++c) lam[c] = yb[c];
+}
+
+/* ------------------------------------------------------------------ */
 /* Problem helpers                                                     */
 /* ------------------------------------------------------------------ */
 
@@ -781,12 +933,13 @@ Opts make_opts(const orc_problem *P) {
 
 int validate(const orc_problem *P) {
   if (!P) return E_INVAL;
-  if (P->method < 0 || P->method > 2) return E_INVAL;
+  if (P->method < 0 || P->method > 3) return E_INVAL;
   if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
-  if (P->method == M_ROS2 && P->dim > 3) return E_UNSUPPORTED;
+  const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
+  if (ros && P->dim > 3) return E_UNSUPPORTED;
   if (P->dense != 0 && P->dense != 1) return E_INVAL;
-  if (P->dense && P->method == M_ROS2) return E_UNSUPPORTED;
-  if (P->rhs >= R_USER && P->method == M_ROS2) return E_UNSUPPORTED;
+  if (P->dense && ros) return E_UNSUPPORTED;
+  if (P->rhs >= R_USER && ros) return E_UNSUPPORTED;
   if (!(P->t1 > P->t0)) return E_INVAL;
   if (!(P->rtol >= 0) || !(P->atol >= 0) || !(P->rtol + P->atol > 0)) return E_INVAL;
   if (P->max_steps < 1) return E_INVAL;
@@ -931,10 +1084,10 @@ template <class T, bool F>
 void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
                  const LaneOut<T> &out) {
   const int d = P->dim, kind = P->rhs;
-  const bool ros = P->method == M_ROS2;
+  const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
   const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
-  const int qerr = ros ? 1 : tb.err_order;
-  const int qord = ros ? 2 : tb.order;
+  const int qerr = P->method == M_ROS2 ? 1 : P->method == M_RODAS3 ? RODAS3.err_order : tb.err_order;
+  const int qord = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order : tb.order;
   const T atol = T(P->atol), rtol = T(P->rtol);
   const T expo = T(-1.0) / T(qerr + 1);
   const T safety = T(o.safety), fmin = T(o.fac_min), fmax = T(o.fac_max);
@@ -971,9 +1124,13 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
       if (natt >= o.max_attempts) { st = S_MAX_ATTEMPTS; break; }
       if (!(hs > T(0.0)) || t + double(hs) == t) { st = S_DT_UNDERFLOW; break; }
       ++natt;
-      if (ros) {
+      if (P->method == M_ROS2) {
         Ros2Step<T> rs;
         ros2_forward<T, F>(kind, d, y, p, hs, rs);
+        for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+      } else if (P->method == M_RODAS3) {
+        RodasStep<T> rs;
+        rodas_forward<T, F>(RODAS3, kind, d, y, p, hs, rs);
         for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
       } else {
         erk_stages<T, F>(tb, kind, d, y, p, hs, 6, true, Y, K);
@@ -1044,6 +1201,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
 template <class T, bool F>
 inline void one_step(const orc_problem *P, T *y, const T *p, T h) {
   if (P->method == M_ROS2) ros2_step<T, F>(P->rhs, P->dim, y, p, h);
+  else if (P->method == M_RODAS3) rodas_step<T, F>(RODAS3, P->rhs, P->dim, y, p, h);
   else erk_step<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p, h);
 }
 
@@ -1051,6 +1209,8 @@ template <class T, bool F>
 inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, T *lam, T *gp,
                              T *gpc = nullptr) {
   if (P->method == M_ROS2) ros2_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
+  else if (P->method == M_RODAS3)
+    rodas_step_adjoint<T, F>(RODAS3, P->rhs, P->dim, y, p, h, lam, gp);
   else erk_step_adjoint<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p,
                               h, lam, gp, gpc);
 }
@@ -1248,16 +1408,19 @@ void replay_grad_lane(const orc_problem *P, int S, const T *u0, const T *p, cons
 template <class T, bool F>
 T mesh_max_err_lane(const orc_problem *P, const T *u0, const T *p, const T *h, int N) {
   const int d = P->dim, kind = P->rhs;
-  const bool ros = P->method == M_ROS2;
   const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
   const T atol = T(P->atol), rtol = T(P->rtol);
   T y[MAXD], ynew[MAXD], err[MAXD], Y[7][MAXD], K[7][MAXD];
   for (int c = 0; c < d; ++c) y[c] = u0[c];
   T worst = T(0.0);
   for (int k = 0; k < N; ++k) {
-    if (ros) {
+    if (P->method == M_ROS2) {
       Ros2Step<T> rs;
       ros2_forward<T, F>(kind, d, y, p, h[k], rs);
+      for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+    } else if (P->method == M_RODAS3) {
+      RodasStep<T> rs;
+      rodas_forward<T, F>(RODAS3, kind, d, y, p, h[k], rs);
       for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
     } else {
       rhs_f<T, F>(kind, d, y, p, K[0]);
@@ -1683,7 +1846,7 @@ int orc_initial_step_f64(const orc_problem *P, const double *y0, const double *p
   if (rc) return rc;
   double f0[MAXD];
   rhs_f<double, false>(P->rhs, P->dim, y0, p, f0);
-  const int q = P->method == M_ROS2 ? 2 : 5;
+  const int q = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order : 5;
   *h0 = initial_step<double, false>(P->rhs, P->dim, y0, f0, p, P->atol, P->rtol, q);
   return E_OK;
 }

@@ -64,6 +64,16 @@ MUTANTS = {
                           "pd[q] = U(p[q], (wrt_p && q == 0) ? T(1) : T(0));"),
     "dense_save_in_next_step": ("out.sidx[j] = nacc;\n            if (out.theta) out.theta[j] = th;",
                                 "out.sidx[j] = nacc + 1;\n            if (out.theta) out.theta[j] = th;"),
+    "rodas3_digit": ("t.c[3][2] = -8.0 / 3.0;", "t.c[3][2] = -7.0 / 3.0;"),
+    "rodas3_weight": ("t.m[0] = 2.0; t.m[1] = 0.0;", "t.m[0] = 1.5; t.m[1] = 0.0;"),
+    "rodas3_stage_sum_misses_c_term": (
+        "        if (tb.gc[l][i] != 0.0) {\n          acc = first ? T(tb.gc[l][i]) * rb[l][c]",
+        "        if (tb.gc[l][i] != 0.0 && l > i + 1) {\n          acc = first ? T(tb.gc[l][i]) * rb[l][c]"),
+    "rodas3_wbar_from_wrong_stage": (
+        "mac<F>(-rb[i][a], s.u[i][b], Wb[a * d + b]);",
+        "mac<F>(-rb[i][a], s.u[tb.s - 1][b], Wb[a * d + b]);"),
+    "rodas3_vjp_at_step_start": ("rhs_vjp_y<T, F>(kind, d, s.Y[i], p, fb, Yb[i]);",
+                                 "rhs_vjp_y<T, F>(kind, d, y, p, fb, Yb[i]);"),
 }
 
 
@@ -73,12 +83,14 @@ def _battery():
         out.append((pins.test_tableau_order_conditions, dict(method=m)))
     out += [(pins.test_dopri5_rationals, {}), (pins.test_dopri5_stability_polynomial, {}),
             (pins.test_page5_enzyme_fixed_step_tsit5, {})]
-    for m in (W.TSIT5, W.DOPRI5, W.ROS2):
+    for m in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3):
         out.append((pins.test_linear_decay_closed_form, dict(method=m, fused=False)))
         out.append((pins.test_lorenz63_origin_linearisation, dict(method=m)))
+    out.append((pins.test_rodas3_order_stability_and_estimator, {}))
     for m in (W.TSIT5, W.DOPRI5):
         out.append((pins.test_lorenz96_fixed_point, dict(method=m)))
-    out += [(pins.test_robertson_ros2_conservation, {}),
+    out += [(pins.test_robertson_ros2_conservation, {"method": W.ROS2}),
+            (pins.test_robertson_ros2_conservation, {"method": W.RODAS3}),
             (pins.test_dopri5_record_matches_scipy_rk45, {}),
             (pins.test_loss_values_match_their_definitions, {}),
             (pins.test_rhs_vjp_against_dense_jacobian, {})]

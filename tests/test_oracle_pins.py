@@ -137,12 +137,31 @@ def _R_ros2(gamma, z):
     return 1 + 2 * z * w + 0.5 * z * z * w * w - z * w * w
 
 
+def _rodas3_matrix(Z):
+    """One Rodas3 step on y' = A y with Z = h A (any square matrix, complex
+    allowed): the published stages with gamma = 1/2 applied to the identity,
+    u_i = (I - Z/2)^-1 (Z/2 Y_i + sum_j c_ij/2 u_j)."""
+    I = np.eye(Z.shape[0], dtype=complex if np.iscomplexobj(Z) else float)
+    Wi = np.linalg.inv(I - 0.5 * Z)
+    u0 = Wi @ (0.5 * Z @ I)
+    u1 = Wi @ (0.5 * Z @ I + 2.0 * u0)
+    Y2 = I + 2.0 * u0
+    u2 = Wi @ (0.5 * Z @ Y2 + 0.5 * u0 - 0.5 * u1)
+    Y3 = Y2 + u2
+    u3 = Wi @ (0.5 * Z @ Y3 + 0.5 * u0 - 0.5 * u1 - (4.0 / 3.0) * u2)
+    return I + 2.0 * u0 + u2 + u3
+
+
+def _R_rodas3(z):
+    return _rodas3_matrix(np.array([[z]]))[0, 0]
+
+
 def _complex_step(fn, z):
     eps = 1e-30
     return (fn(z + 1j * eps)).imag / eps
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
 @pytest.mark.parametrize("fused", [False, True])
 def test_linear_decay_closed_form(orc, method, fused):
     """y' = -k y on an arbitrary mesh: y_N = y0 prod R(-k h_n); exact derivative
@@ -158,6 +177,8 @@ def test_linear_decay_closed_form(orc, method, fused):
         assert g == 1.0 + 1.0 / math.sqrt(2.0)
         assert abs(_R_ros2(g, -1e12)) < 1e-11            # L-stable: R(-inf) = 0
         R = lambda z: _R_ros2(g, z)
+    elif method == W.RODAS3:
+        R = _R_rodas3
     else:
         coef = _stability_poly(orc.tableau(method))
         R = lambda z: _R_erk(coef, z)
@@ -180,12 +201,62 @@ def test_linear_decay_closed_form(orc, method, fused):
         assert gp[i, 0] == pytest.approx(y0[i] * dprod, rel=2e-13, abs=1e-300)
 
 
+def test_rodas3_order_stability_and_estimator(orc):
+    """What identifies a correct Rodas3, from the mathematics alone:
+    - the oracle's one-step map of y' = z y is the closed form above;
+    - R(z) - e^z = O(z^4), with a nonzero z^4 term (order exactly 3);
+    - A-stable (|R| <= 1 on the imaginary axis and the negative real axis)
+      and L-stable (R(-inf) = 0);
+    - global order 3 on Lorenz-63 with fixed steps, against SciPy's DOP853 at
+      a tolerance far below the errors measured;
+    - a second-order embedded estimate: the recorded step count grows as
+      tol^(-1/3) (local error estimate O(h^3))."""
+    from scipy.integrate import solve_ivp
+    prob = W.Problem(W.LINEAR, 1, 1, W.RODAS3, 0.0, 1.0, 1e-6, 1e-6, 1)
+    one = {"h": np.ones((1, 1)), "n_steps": np.array([1]), "save_idx": np.array([[1]]),
+           "status": np.zeros(1)}
+    for z in (-50.0, -1.3, -0.01, 0.2, 1.5):
+        _, y1 = orc.replay(prob, np.ones((1, 1)), np.array([[z]]), one)
+        assert y1[0, 0] == pytest.approx(_R_rodas3(z), rel=1e-14)
+    e1, e2 = _R_rodas3(0.02) - math.exp(0.02), _R_rodas3(0.01) - math.exp(0.01)
+    assert 14.0 < e1 / e2 < 18.0 and abs(e2) > 1e-13            # C z^4, C != 0
+    assert abs(_R_rodas3(-1e12)) < 1e-11
+    assert max(abs(_R_rodas3(1j * y)) for y in np.logspace(-3, 6, 400)) <= 1.0 + 1e-12
+    assert max(abs(_R_rodas3(-x)) for x in np.logspace(-3, 12, 400)) <= 1.0 + 1e-12
+    # global order on Lorenz-63 over [0, 0.5]
+    u0 = np.array([[1.0, 1.0, 1.0]])
+    pv = np.array([[10.0, 28.0, 8.0 / 3.0]])
+    ref = solve_ivp(lambda t, y: [10 * (y[1] - y[0]), y[0] * (28 - y[2]) - y[1],
+                                  y[0] * y[1] - 8 / 3 * y[2]], (0, 0.5), u0[0],
+                    method="DOP853", rtol=1e-13, atol=1e-13).y[:, -1]
+    errs = []
+    for N in (40, 80, 160, 320):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.RODAS3, 0.0, 0.5, 1e-6, 1e-6, N)
+        mesh = {"h": np.full((1, N), 0.5 / N), "n_steps": np.array([N]),
+                "save_idx": np.array([[N]]), "status": np.zeros(1)}
+        _, yN = orc.replay(pr, u0, pv, mesh)
+        errs.append(np.abs(yN[0] - ref).max())
+    orders = [math.log2(errs[i] / errs[i + 1]) for i in range(3)]
+    assert all(2.7 < o < 3.3 for o in orders[1:]), orders
+    # step counts against the tolerance
+    inp = W.make_inputs(1, 8)
+    steps = []
+    for tol in (1e-6, 1e-9):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.RODAS3, 0.0, 1.0, tol, tol, 100000)
+        m = orc.record(pr, inp["u0"], inp["p"])
+        assert np.all(m["status"] == 0)
+        steps.append(m["n_steps"].mean())
+    assert 7.0 < steps[1] / steps[0] < 14.0, steps                # 1000^(1/3) = 10
+
+
 def _matrix_R(method, orc, Z):
     I = np.eye(Z.shape[0])
     if method == W.ROS2:
         g = orc.ros2_gamma()
         Wm = np.linalg.inv(I - g * Z)
         return I + 2 * Z @ Wm + 0.5 * Z @ Z @ Wm @ Wm - Z @ Wm @ Wm
+    if method == W.RODAS3:
+        return _rodas3_matrix(Z)
     coef = _stability_poly(orc.tableau(method))
     out = np.zeros_like(Z)
     Zp = I.copy()
@@ -195,7 +266,7 @@ def _matrix_R(method, orc, Z):
     return out
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
 def test_lorenz63_origin_linearisation(orc, method):
     """At the origin Lorenz-63 is a fixed point; the replay's Jacobian is the
     product of R(h_n A) with A = [[-s, s, 0], [r, -1, 0], [0, 0, -b]].  A
@@ -268,12 +339,14 @@ def test_lorenz96_fixed_point(orc, method):
 # Invariants
 # ---------------------------------------------------------------------------
 
-def test_robertson_ros2_conservation(orc):
-    """1^T f = 0 for Robertson, so 1^T J = 0 and ROS2 keeps y1+y2+y3 fixed for
-    any k and h; the adjoint of the linear functional 1^T y_N is 1 for u0 and
-    0 for k."""
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3])
+def test_robertson_ros2_conservation(orc, method):
+    """1^T f = 0 for Robertson, so 1^T J = 0 and a Rosenbrock step (ROS2,
+    Rodas3: every stage is W^-1 of a combination of f values and earlier
+    stages) keeps y1+y2+y3 fixed for any k and h; the adjoint of the linear
+    functional 1^T y_N is 1 for u0 and 0 for k."""
     inp = W.make_inputs(4, 64)
-    prob = W.WORKLOADS[4].problem()
+    prob = W.WORKLOADS[4].problem(method=method)
     m = orc.record(prob, inp["u0"], inp["p"])
     assert np.all(m["status"] == 0)
     ys, yN = orc.replay(prob, inp["u0"], inp["p"], m)
@@ -327,7 +400,7 @@ def test_save_times_are_mesh_points(orc):
 def test_global_error_tracks_tolerance(orc):
     """y' = -y on [0, 1]: the recorded solve's error at t=1 stays below the
     tolerance scale and shrinks as the tolerance does."""
-    for method in (W.TSIT5, W.DOPRI5, W.ROS2):
+    for method in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3):
         errs = []
         for tol in (1e-4, 1e-6, 1e-8):
             prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, tol, tol, 100000)
@@ -437,6 +510,13 @@ def _cases():
                 inp["p"], W.COTANGENT, np.random.default_rng(3).standard_normal((3, 1, 64))))
     out.append(("linear_ros2", W.Problem(W.LINEAR, 1, 1, W.ROS2, 0.0, 2.0, 1e-6, 1e-6, 20000),
                 np.array([[1.0], [2.0]]), np.array([[-0.7], [0.4]]), W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(4, 4)
+    out.append(("robertson_rodas3", W.WORKLOADS[4].problem(t1=300.0, method=W.RODAS3),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(1, 6)
+    out.append(("lorenz63_rodas3_saves", W.WORKLOADS[1].problem(
+        method=W.RODAS3, max_steps=4096, save_times=(0.3, 0.7, 1.0)), inp["u0"], inp["p"],
+        W.MSE_SAVE, np.random.default_rng(4).standard_normal((6, 3, 3))))
     return out
 
 
@@ -560,7 +640,7 @@ def test_fp32_oracle_tracks_fp64(orc):
 # Forward-mode sensitivities (tangents carried through the replay)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
 @pytest.mark.parametrize("fused", [False, True])
 def test_sensitivities_linear_closed_form(orc, method, fused):
     """y' = p y on an arbitrary mesh: dy_N/dy0 = prod R(p h_n) and
@@ -573,6 +653,8 @@ def test_sensitivities_linear_closed_form(orc, method, fused):
     if method == W.ROS2:
         g = orc.ros2_gamma()
         R = lambda z: _R_ros2(g, z)
+    elif method == W.RODAS3:
+        R = _R_rodas3
     else:
         coef = _stability_poly(orc.tableau(method))
         R = lambda z: _R_erk(coef, z)
