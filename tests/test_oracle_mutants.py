@@ -35,7 +35,12 @@ MUTANTS = {
     "dopri5_weight": ("t.a[6][3] = 125.0 / 192.0;", "t.a[6][3] = 125.0 / 191.0;"),
     "lu_transposed_solve": ("z[i] = mac<F>(-LU[j * d + i], z[j], z[i]);\n    z[i] = F ?",
                             "z[i] = mac<F>(-LU[i * d + j], z[j], z[i]);\n    z[i] = F ?"),
-    "ros2_no_jac_contraction": ("rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);", ""),
+    "ros2_no_jac_contraction": (
+        "for (int i = 0; i < d * d; ++i) Jb[i] = (-gh) * Wb[i];\n  rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);",
+        "for (int i = 0; i < d * d; ++i) Jb[i] = (-gh) * Wb[i];"),
+    "rodas3_no_jac_contraction": (
+        "for (int q = 0; q < d * d; ++q) Jb[q] = (-gh) * Wb[q];\n  rhs_jac_contract_acc<T, F>(kind, d, y, p, Jb, yb, gp);",
+        "for (int q = 0; q < d * d; ++q) Jb[q] = (-gh) * Wb[q];"),
     "ros2_wrong_weight": ("const T acc = mac<F>(T(0.5), s.k2[c], T(1.5) * s.k1[c]);",
                           "const T acc = mac<F>(T(0.5), s.k2[c], T(1.0) * s.k1[c]);"),
     "robertson_contraction_sign": ("gy[1] = mac<F>(-two_k2, Jb[4], gy[1]);",
