@@ -27,6 +27,7 @@ Printed on one JSON line, besides the driver's fields:
 --gpus N with N > 1 is not supported (this build runs on one GPU).
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -51,6 +52,11 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 #    26, two solves 30, stage and solution combinations 27) = 118; adjoint
 #    (two transposed solves 30, J^T v and J_p^T v at both stages 66, Wbar 27,
 #    cotangent combinations 36, dJ contraction 29) = 188; total 306.
+#  Rodas3 / Robertson: forward (Jacobian 9, W 13, LU 13, four right-hand
+#    sides 52, four solves 60, stage sums Y_i 18 and stage right-hand sides
+#    48, solution 18 and error 3) = 234; adjoint (stage cotangents 60, four
+#    transposed solves 60, Wbar 63, fbar 12, J^T v and J_p^T v at four stages
+#    132, ybar sums 12, Jbar 9 and dJ contraction 29) = 377; total 611.
 #  Tsit5 / Lorenz-96 (d components): forward 6 x 4d + 48d = 72d; adjoint
 #    42d + 6 x (J^T v 7d + J_p^T v d + accumulate d) = 96d; total 168d.
 # Forward-mode sensitivities (all d + P unit directions as dual numbers, the
@@ -69,7 +75,7 @@ def sens_flop_per_step(method: str, rhs: str, dim: int):
 
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
     table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
-             ("ros2", "robertson"): 306}
+             ("ros2", "robertson"): 306, ("rodas3", "robertson"): 611}
     if rhs == "lorenz96" and method == "tsit5":
         return 168 * dim
     return table[(method, rhs)]
@@ -90,7 +96,10 @@ KERNEL_SOURCES = {
     "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "erk_grad_f64_dopri5.hip",
             "erk_grad_f64_tsit5.hip", "erk_grad_f32_dopri5.hip", "erk_grad_f32_tsit5.hip",
             "dadj_device.hpp", "dadj_internal.hpp"],
-    "ros2": ["lane_kernels.hpp", "ros2.hip", "dadj_device.hpp", "dadj_internal.hpp"],
+    "ros2": ["lane_kernels.hpp", "rosenbrock.hpp", "ros2.hip", "dadj_device.hpp",
+             "dadj_internal.hpp"],
+    "rodas3": ["lane_kernels.hpp", "rosenbrock.hpp", "rodas3.hip", "dadj_device.hpp",
+               "dadj_internal.hpp"],
     "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
 }
 
@@ -98,7 +107,7 @@ KERNEL_SOURCES = {
 def kernel_family(method: str, rhs: str) -> str:
     if rhs == "lorenz96":
         return "wave"
-    return "ros2" if method == "ros2" else "erk"
+    return method if method in ("ros2", "rodas3") else "erk"
 
 
 def kernel_source_hash(family: str = "erk") -> str:
@@ -129,9 +138,10 @@ def read_traffic(workload_name: str, family: str, dense: bool = False):
 
 
 def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0,
-                 dense: int = 0):
+                 dense: int = 0, method=None):
     """Oracle as it stands, plain rounding, all OpenMP threads: record + passes
-    on the first `lanes` trajectories of the workload."""
+    on the first `lanes` trajectories of the workload (with `method` in place
+    of the workload's integrator, when given)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -139,6 +149,8 @@ def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0,
     lanes = min(lanes, w.n)
     inp = W.make_inputs(wid, lanes)
     prob = w.problem(dense=dense)
+    if method is not None:
+        prob = prob.replace(method=method)
     cores = oracle.max_threads()
     aux, scale = None, 1.0
     if w.loss == W.MSE_SAVE:
@@ -190,6 +202,9 @@ def main():
     ap.add_argument("--rhs-source", action="store_true",
                     help="Lorenz-63 workloads: run the system as a right-hand side compiled at "
                          "run time from source instead of the built-in one")
+    ap.add_argument("--method", choices=["rodas3"], default=None,
+                    help="workload 4 (Robertson): integrate with the third-order Rosenbrock "
+                         "method Rodas3 instead of ROS2, at the same tolerances")
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
@@ -209,6 +224,10 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
+    if args.method:
+        if args.workload != 4:
+            sys.exit("--method rodas3 is available for workload 4 (Robertson)")
+        w = dataclasses.replace(w, method=W.RODAS3, name=w.name.replace("ros2", "rodas3"))
     prob = w.problem(checkpoint=args.checkpoint, dense=int(args.dense))
     if args.rhs_source:
         if w.rhs != W.LORENZ63:
@@ -357,7 +376,7 @@ def main():
         out["rhs_registration_s"] = t_reg
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
-                                           dense=int(args.dense))
+                                           dense=int(args.dense), method=w.method)
     print(json.dumps(out), flush=True)
 
 

@@ -9,8 +9,7 @@
 // Jbar = -gamma h Wbar with the derivative of J.  The forward step is written
 // once for values and for the tangent numbers of the sensitivity kernel (V is
 // either; the step size and gamma carry no tangent).
-#include "lane_kernels.hpp"
-#include "sens_kernel.hpp"
+#include "rosenbrock.hpp"
 
 namespace dadj {
 namespace {
@@ -21,123 +20,6 @@ template <int D, class V> struct Ros2Step {
   bool swapped;  // some row exchange happened (perm is not the identity)
   V f1[D], k1[D], Y2[D], f2[D], r2[D], k2[D], ynew[D], err[D];
 };
-
-// In-place LU of A (row-major) with partial pivoting; perm[i] = original row
-// now in position i, swapped = some row was exchanged.  Row exchanges are
-// register selects, executed only when some lane of the wavefront needs one
-// (a uniform branch: where the pivot is already on the diagonal, as with
-// diagonally dominant W, the selects are skipped; the values are the same
-// either way).  Each pivot's reciprocal is formed once (a correctly rounded
-// 1 / u) and every division by the pivot, here and in the solves, is a
-// multiplication by it.  Pivots are chosen on values.
-template <int D, class V>
-__device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rinv)[D],
-                                          bool &swapped) {
-#pragma unroll
-  for (int i = 0; i < D; ++i) perm[i] = i;
-  swapped = false;
-#pragma unroll
-  for (int k = 0; k < D; ++k) {
-    int piv = k;
-    auto best = dabs(vpart(A[k * D + k]));
-#pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const auto v = dabs(vpart(A[i * D + k]));
-      if (v > best) { best = v; piv = i; }
-    }
-    swapped = swapped || piv != k;
-    if (__ballot(piv != k) != 0ull) {
-#pragma unroll
-      for (int r = k + 1; r < D; ++r) {
-        const bool sw = piv == r;
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-          const V top = A[k * D + j], oth = A[r * D + j];
-          A[k * D + j] = sel(sw, oth, top);
-          A[r * D + j] = sel(sw, top, oth);
-        }
-        const int pt = perm[k], po = perm[r];
-        perm[k] = sw ? po : pt;
-        perm[r] = sw ? pt : po;
-      }
-    }
-    rinv[k] = recip(A[k * D + k]);
-#pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const V l = A[i * D + k] * rinv[k];
-      A[i * D + k] = l;
-#pragma unroll
-      for (int j = k + 1; j < D; ++j) A[i * D + j] = mac(-l, A[k * D + j], A[i * D + j]);
-    }
-  }
-}
-
-// Solve A x = b from the factors (P A = L U).  The right-hand side is copied
-// into a private array first so that the permutation stays a register select
-// (a select between loads through the argument would become an indexed load
-// and keep the caller's arrays out of registers).
-template <int D, class V>
-__device__ __forceinline__ void lu_solve(const V (&LU)[D * D], const V (&rinv)[D],
-                                         const int (&perm)[D], bool swapped, const V (&b_in)[D],
-                                         V (&x)[D]) {
-  V b[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) b[i] = b_in[i];
-  if (__ballot(swapped) != 0ull) {  // uniform: some lane has a row exchange
-#pragma unroll
-    for (int i = 0; i < D; ++i) {
-      V v = b[0];
-#pragma unroll
-      for (int q = 1; q < D; ++q) v = sel(perm[i] == q, b[q], v);
-      x[i] = v;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < D; ++i) x[i] = b[i];
-  }
-#pragma unroll
-  for (int i = 0; i < D; ++i)
-#pragma unroll
-    for (int j = 0; j < i; ++j) x[i] = mac(-LU[i * D + j], x[j], x[i]);
-#pragma unroll
-  for (int i = D - 1; i >= 0; --i) {
-#pragma unroll
-    for (int j = i + 1; j < D; ++j) x[i] = mac(-LU[i * D + j], x[j], x[i]);
-    x[i] = x[i] * rinv[i];
-  }
-}
-
-// Solve A^T x = b from the factors of A (A^T = U^T L^T P).
-template <int D, class T>
-__device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)[D],
-                                           const int (&perm)[D], bool swapped, const T (&b)[D],
-                                           T (&x)[D]) {
-  T z[D];
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    z[i] = b[i];
-#pragma unroll
-    for (int j = 0; j < i; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
-    z[i] = z[i] * rinv[i];
-  }
-#pragma unroll
-  for (int i = D - 1; i >= 0; --i)
-#pragma unroll
-    for (int j = i + 1; j < D; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
-  // x[perm[i]] = z[i]
-  if (__ballot(swapped) != 0ull) {  // uniform, as in lu_solve
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      T v = z[0];
-#pragma unroll
-      for (int i = 1; i < D; ++i) v = (perm[i] == c) ? z[i] : v;
-      x[c] = v;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < D; ++c) x[c] = z[c];
-  }
-}
 
 // One ROS2 step from y with size h:
 //   k1 = W^-1 f(y);  Y2 = y + h k1;  k2 = W^-1 (f(Y2) - 2 k1);

@@ -63,10 +63,14 @@ extern "C" {
 typedef enum { DA_F64 = 0, DA_F32 = 1 } da_dtype;
 
 /* Integrators: explicit Tsitouras 5(4) and Dormand-Prince 5(4) (both 7
- * stages, first-same-as-last, 5th-order solution propagated), and the
+ * stages, first-same-as-last, 5th-order solution propagated), the
  * second-order Rosenbrock method ROS2 with gamma = 1 + 1/sqrt(2) (summary,
- * Abstract: explicit and Rosenbrock integrators). */
-typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2 } da_method;
+ * Abstract: explicit and Rosenbrock integrators), and Rodas3, a third-order,
+ * stiffly accurate, L-stable Rosenbrock method (four stages, embedded
+ * second-order estimate, gamma = 1/2; Sandu et al. 1997) for stiff problems
+ * at tight tolerances.  The Rosenbrock methods take systems of dimension
+ * <= 3 and no dense output (DA_EUNSUPPORTED). */
+typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2, DA_RODAS3 = 3 } da_method;
 
 /* Built-in right-hand sides (dimension d, parameter count P):
  *  DA_RHS_LINEAR    d=1, P=1: y' = p0 y
@@ -112,7 +116,8 @@ typedef enum {
  * Adaptive control (record and forward solve): error norm = RMS over
  * components of err / (atol + rtol max(|y_n|, |y_{n+1}|)); accept iff it is
  * <= 1; next step = used step * clamp(safety E^(-1/(q+1)), fac_min, fac_max)
- * with q the embedded order (4 for the explicit pairs, 1 for ROS2), no growth
+ * with q the embedded order (4 for the explicit pairs, 1 for ROS2, 2 for
+ * Rodas3), no growth
  * on the step after a rejection.  Steps are shortened to land exactly on each
  * save time and on t1, or, with dense = 1, on t1 only, each save time then
  * being read from the interpolant of the accepted step that contains it
@@ -154,7 +159,8 @@ typedef struct {
                           t_k < t_s <= t_k + h; th = (t_s - t_k) / h in double,
                           capped at 1, exactly 1 at the step's end.  th is part
                           of the mesh and, like h, carries no derivative.
-                          Explicit methods only (DA_EUNSUPPORTED with ROS2).  */
+                          Explicit methods only (DA_EUNSUPPORTED with ROS2
+                          and Rodas3).  */
 } da_problem;
 
 /* The record: one zero-padded step mesh per trajectory, reused by every
@@ -304,8 +310,9 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
  * not reached); with loss not NULL, loss_out [n], grad_u0 [d][n] and
  * grad_p [P][n], the gradient of that loss by the chain rule through the
  * tangents (the same quantity as da_replay_grad computes in reverse).
- * Needs no workspace.  Every method (for ROS2 the tangents run through the
- * Jacobian, the LU factors with the pivots of the values, and both solves)
+ * Needs no workspace.  Every method (for the Rosenbrock methods the tangents
+ * run through the Jacobian, the LU factors with the pivots of the values,
+ * and every solve)
  * and every right-hand side (Lorenz-96: one wavefront per trajectory, four
  * directions per lane).  Trajectories whose record failed get NaN. */
 int da_replay_sens(const da_problem *prob, int64_t n, const void *u0, const void *p,

@@ -43,7 +43,7 @@ def _call_record(da, prob, n=4, dtype_code=0, **kw):
 
 @pytest.mark.parametrize("change,code", [
     (dict(t1=0.0), -1), (dict(rtol=0.0, atol=0.0), -1), (dict(max_steps=0), -1),
-    (dict(dim=4), -1), (dict(method=7), -1), (dict(rhs=9), -1),
+    (dict(dim=4), -1), (dict(method=7), -1), (dict(method=4), -1), (dict(rhs=9), -1),
     (dict(save_times=(0.5, 0.4)), -1), (dict(save_times=(0.5, 2.0)), -1),
     (dict(rtol=-1.0), -1), (dict(safety=-0.5), -1),
 ])
@@ -54,9 +54,12 @@ def test_invalid_problems_rejected(da, change, code):
 
 
 def test_unsupported_combinations(da):
-    prob = W.Problem(W.LORENZ96, 64, 1, W.ROS2, 0.0, 1.0, 1e-6, 1e-6, 100)
-    assert _call_record(da, prob) == -2
-    assert "ROS2" in da.last_error()
+    for method in (W.ROS2, W.RODAS3):
+        prob = W.Problem(W.LORENZ96, 64, 1, method, 0.0, 1.0, 1e-6, 1e-6, 100)
+        assert _call_record(da, prob) == -2
+        assert "Rosenbrock" in da.last_error()
+        assert _call_record(da, W.WORKLOADS[4].problem(method=method, dense=1)) == -2
+        assert "dense" in da.last_error()
     for dim in (3, 65):
         prob = W.Problem(W.LORENZ96, dim, 1, W.TSIT5, 0.0, 1.0, 1e-6, 1e-6, 100)
         assert _call_record(da, prob) == -1

@@ -1,0 +1,178 @@
+"""Rodas3 (the third-order Rosenbrock method) on the GPU against the oracle.
+
+Gates: on oracle-recorded meshes (fused rounding), saves, losses and
+gradients within 1e-12 relative per trajectory in FP64 (the arithmetic
+schedule is the same on both sides), and 1e-4 in FP32 against the FP64
+oracle; the GPU's records agree with the oracle's (step counts, error
+norms, states); checkpoint intervals and the replay table give bit-for-bit
+the same gradients; forward-mode
+sensitivities against the oracle and against the reverse sweep; the
+Robertson workload at full size (65536 trajectories) sampled."""
+import numpy as np
+import pytest
+
+import workloads as W
+from helpers import aux_to_dev, grad_rel_err, mesh_to_dev, mesh_to_host, rel_err, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def da():
+    import discrete_adjoint_amd as da
+    assert torch.cuda.is_available()
+    return da
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+def _linear_inputs(n):
+    rng = np.random.default_rng(5)
+    return {"u0": 1.0 + rng.random((n, 1)), "p": -3.0 * rng.random((n, 1)) + 0.2}
+
+
+CASES = [
+    ("robertson_full", W.WORKLOADS[4].problem(method=W.RODAS3), 4, W.SUMSQ_FINAL, 300),
+    ("robertson_saves_mse", W.WORKLOADS[4].problem(method=W.RODAS3, t1=1e3,
+                                                   save_times=(1.0, 10.0, 1e3)),
+     4, W.MSE_SAVE, 200),
+    ("lorenz63_saves_cot", W.WORKLOADS[1].problem(method=W.RODAS3, max_steps=4096,
+                                                  save_times=(0.3, 0.7, 1.0)),
+     1, W.COTANGENT, 400),
+    ("linear", W.Problem(W.LINEAR, 1, 1, W.RODAS3, 0.0, 4.0, 1e-8, 1e-8, 4096,
+                         save_times=(1.0, 4.0)), None, W.COTANGENT, 300),
+]
+
+
+@pytest.mark.parametrize("name,prob,wid,lk,n", CASES, ids=[c[0] for c in CASES])
+def test_rodas3_against_oracle(da, orc, name, prob, wid, lk, n):
+    inp = _linear_inputs(n) if wid is None else W.make_inputs(wid, n)
+    u0n, pn = inp["u0"].astype(np.float64), inp["p"].astype(np.float64)
+    d = prob.dim
+    S = prob.n_save_eff
+    aux = None if lk == W.SUMSQ_FINAL else np.random.default_rng(9).standard_normal((n, S, d))
+    _print(f"case: Rodas3 {name}, n={n}")
+    m = orc.record(prob, u0n, pn, fused=True)
+    assert np.all(m["status"] == 0)
+    yo, _ = orc.replay(prob, u0n, pn, m, fused=True)
+    lo, go, po = orc.replay_grad(prob, u0n, pn, m, lk, aux=aux, scale=0.3, fused=True)
+    mesh = mesh_to_dev(m, prob.max_steps, torch)
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    yg = da.replay_fwd(prob, u0, p, mesh)
+    loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, lk, aux=auxd, scale=0.3)
+    torch.cuda.synchronize()
+    ey = rel_err(yg.cpu().numpy().transpose(2, 0, 1).reshape(n, -1), yo.reshape(n, -1))
+    eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+    el = np.abs(loss.cpu().numpy() - lo) / np.abs(lo)
+    _print(f"  mean steps {m['n_steps'].mean():.1f}; saves max rel {ey.max():.3e}, grad max rel "
+           f"{eg.max():.3e} (bitwise lanes {np.mean(eg == 0):.3f}), loss {el.max():.3e}")
+    assert ey.max() <= 1e-12 and eg.max() <= 1e-12 and el.max() <= 1e-12
+    # the GPU's record: the oracle's mesh, and the replay's states
+    mg_dev, ys = da.record(prob, u0, p)
+    yr = da.replay_fwd(prob, u0, p, mg_dev)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, yr)
+    mg = mesh_to_host(mg_dev, prob.max_steps)
+    assert np.all(mg["status"] == 0)
+    # the controller's single-precision power rounds differently in the last
+    # bit on the two sides, so the meshes are held to the same record, not to
+    # the same bits: step counts within max(2, 1%), every GPU step accepted by
+    # the oracle's error norm, and the GPU's states those of the oracle's
+    # replay of the GPU mesh
+    E = orc.mesh_max_err(prob, u0n, pn, mg, fused=True)
+    yo2, _ = orc.replay(prob, u0n, pn, mg, fused=True)
+    er = rel_err(ys.cpu().numpy().transpose(2, 0, 1).reshape(n, -1), yo2.reshape(n, -1))
+    _print(f"  GPU record: mean steps {mg['n_steps'].mean():.1f} (oracle {m['n_steps'].mean():.1f}),"
+           f" max error norm {E.max():.4f}, states vs oracle replay {er.max():.3e}")
+    assert np.all(np.abs(mg["n_steps"] - m["n_steps"]) <= np.maximum(2, 0.01 * m["n_steps"]))
+    assert np.all(E <= 1 + 1e-6) and er.max() <= 1e-12
+    # checkpoint intervals and the replay table
+    for ck in (2, 4, 8):
+        _, g2, q2 = da.replay_grad(prob.replace(checkpoint=ck), u0, p, mesh, lk, aux=auxd,
+                                   scale=0.3)
+        torch.cuda.synchronize()
+        assert torch.equal(g2, gu0) and torch.equal(q2, gp), ck
+    sm = da.mesh_sort(prob, mesh)
+    _, g3, q3 = da.replay_grad(prob, u0, p, sm, lk, aux=auxd, scale=0.3)
+    torch.cuda.synchronize()
+    assert torch.equal(g3, gu0) and torch.equal(q3, gp)
+    # forward-mode sensitivities
+    so, _, gso, pso = orc.replay_sens(prob, u0n, pn, m, lk, aux=aux, scale=0.3, fused=True)
+    sg, _, gs, ps = da.replay_sens(prob, u0, p, mesh, lk, aux=auxd, scale=0.3)
+    torch.cuda.synchronize()
+    sgn = sg.cpu().numpy().transpose(3, 0, 1, 2).reshape(n, -1)
+    es = np.max(np.abs(sgn - so.reshape(n, -1)), axis=1) / np.maximum(
+        np.max(np.abs(so.reshape(n, -1)), axis=1), 1e-300)
+    ef = grad_rel_err(gs.cpu().numpy().T, ps.cpu().numpy().T, gso, pso)
+    ea = grad_rel_err(gs.cpu().numpy().T, ps.cpu().numpy().T, gu0.cpu().numpy().T,
+                      gp.cpu().numpy().T)
+    _print(f"  sensitivities max rel {es.max():.3e}, forward-mode grad {ef.max():.3e}, "
+           f"forward vs reverse {ea.max():.3e}")
+    assert es.max() <= 1e-12 and ef.max() <= 1e-12 and ea.max() <= 1e-10
+
+
+def test_rodas3_fp32(da, orc):
+    """FP32 Rodas3 on Robertson against the FP64 oracle on the FP32 mesh."""
+    prob = W.WORKLOADS[4].problem(method=W.RODAS3, t1=100.0, rtol=1e-4, atol=1e-8)
+    n = 256
+    inp = {k: v.astype(np.float32) for k, v in W.make_inputs(4, n).items()}
+    _print(f"case: Rodas3 FP32, n={n}")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    assert np.all(m["status"] == 0)
+    m64 = dict(m)
+    m64["h"] = m["h"].astype(np.float64)
+    lo, go, po = orc.replay_grad(prob, inp["u0"].astype(np.float64),
+                                 inp["p"].astype(np.float64), m64, W.SUMSQ_FINAL, fused=True)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    loss, gu0, gp = da.replay_grad(prob, u0, p, mesh_to_dev(m, prob.max_steps, torch))
+    mg, _ = da.record(prob, u0, p)
+    torch.cuda.synchronize()
+    eg = grad_rel_err(gu0.cpu().numpy().T.astype(np.float64),
+                      gp.cpu().numpy().T.astype(np.float64), go, po)
+    ns = mg.n_steps.cpu().numpy()
+    _print(f"  grad max rel {eg.max():.3e}; steps GPU {ns.mean():.1f} oracle "
+           f"{m['n_steps'].mean():.1f}")
+    assert eg.max() <= 1e-4
+    assert np.all(mg.status.cpu().numpy() == 0)
+    assert np.all(np.abs(ns - m["n_steps"]) <= np.maximum(4, 0.05 * m["n_steps"]))
+
+
+def test_rodas3_robertson_full_size_sampled(da, orc):
+    """Robertson with Rodas3 at the workload's full size and tolerances
+    (65536 trajectories, t in [0, 1e5], rtol 1e-6, atol 1e-10): record,
+    replay order with table, one gradient pass; sampled trajectories against
+    the oracle on the GPU's mesh and against the oracle's record."""
+    w = W.WORKLOADS[4]
+    prob = w.problem(method=W.RODAS3)
+    inp = W.make_inputs(4)
+    n = w.n
+    _print(f"case: Rodas3 Robertson at full size, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p, save=False)
+    sm = da.mesh_sort(prob, mesh)
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.SUMSQ_FINAL)()
+    torch.cuda.synchronize()
+    st = sm.status.cpu().numpy()
+    assert np.all(st == 0)
+    perm = sm.perm.cpu().numpy()
+    ns_all = sm.n_steps.cpu().numpy()
+    rng = np.random.default_rng(41)
+    slots = np.unique(np.concatenate([rng.choice(n, 48, replace=False), [0, n - 1]]))
+    tr = perm[slots]
+    N = int(ns_all.max())
+    idx = torch.from_numpy(tr.astype(np.int64)).cuda()
+    h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
+    sub = {"h": np.ascontiguousarray(h), "n_steps": ns_all[tr],
+           "save_idx": sm.save_idx.cpu().numpy()[:, tr].T.copy(), "status": st[tr]}
+    pn = prob.replace(max_steps=N)
+    lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, W.SUMSQ_FINAL, fused=True)
+    err = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
+    mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
+    _print(f"  sampled {len(tr)}: max rel {err.max():.3e}; mean steps {ns_all.mean():.1f} "
+           f"(max {N}); oracle record of the sample {mo['n_steps'].mean():.1f}")
+    assert err.max() <= 1e-12
+    assert np.all(np.abs(sub["n_steps"] - mo["n_steps"]) <= np.maximum(2, 0.01 * mo["n_steps"]))
