@@ -341,13 +341,15 @@ def initial_step(prob, y0, p) -> float:
 
 
 def rhs(kind: int, y, p, v):
-    """f(y), J(y)^T v, J_p(y)^T v and (d <= 3) the Jacobian, float64."""
+    """f(y), J(y)^T v, J_p(y)^T v and the Jacobian of the systems the
+    Rosenbrock methods take (None for Lorenz-96), float64."""
     y = np.ascontiguousarray(y, dtype=np.float64)
     p = np.ascontiguousarray(p, dtype=np.float64)
     v = np.ascontiguousarray(v, dtype=np.float64)
     d = y.shape[0]
+    jac = d <= 8 and kind != 3
     f = np.zeros(d); wy = np.zeros(d); gp = np.zeros(p.shape[0]); J = np.zeros(d * d)
     _check(_load().orc_rhs_f64(ctypes.c_int32(kind), ctypes.c_int32(d), _ptr(y), _ptr(p),
                                _ptr(v), _ptr(f), _ptr(wy), _ptr(gp),
-                               _ptr(J) if d <= 3 else None), "rhs")
-    return f, wy, gp, J.reshape(d, d) if d <= 3 else None
+                               _ptr(J) if jac else None), "rhs")
+    return f, wy, gp, J.reshape(d, d) if jac else None

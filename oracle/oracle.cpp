@@ -53,10 +53,11 @@
 namespace {
 
 constexpr int MAXD = 64;  // largest state dimension handled
+constexpr int MAXR = 8;   // largest state dimension of the Rosenbrock methods
 constexpr int MAXP = 16;  // largest parameter count
 
 enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3 };
-enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3 };
+enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3, R_KINETICS8 = 4 };
 constexpr int R_USER = 1024;  /* kinds from here: the caller's right-hand side */
 enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
        S_MAX_ATTEMPTS = 4 };
@@ -346,6 +347,56 @@ void user_f(int d, const T *y, const T *p, T *o) {
  *  gp[q], each term a multiply-add into the accumulator, entries (a,b) in
  *  row-major order. */
 
+/* Eight-species reaction cycle, a synthetic stiff system of the size of the
+ * HIRES test problem (whose equations are not restated here).  Nine
+ * mass-action reactions move one unit of mass each from species src to
+ * species dst, so sum_i y_i is conserved; reaction r has rate
+ *   w_r = (c_r p_{q_r}) y_a            (one reactant a), or
+ *   w_r = ((c_r p_{q_r}) y_a) y_b      (two reactants, in that order),
+ * and f = sum_r (e_dst - e_src) w_r.  With p = (0.04, 3e7, 1e4, 1) the rates
+ * span ten orders of magnitude (the first three reactions are those of
+ * Robertson's system).  Arithmetic: sums over reactions in table order (a
+ * product, then multiply-adds / additions); the partial derivatives of w_r
+ * with respect to its reactants in reactant order. */
+struct Reaction {
+  int src, dst, q, na, a, b;
+  double c;
+};
+const Reaction KIN8[9] = {
+    {0, 1, 0, 1, 0, 0, 1.0},   /* y0 -> y1           p0 y0          */
+    {1, 2, 1, 2, 1, 1, 1.0},   /* 2 y1 -> y1 + y2    p1 y1 y1       */
+    {1, 0, 2, 2, 1, 2, 1.0},   /* y1 + y2 -> y0 + y2 p2 y1 y2       */
+    {2, 3, 3, 1, 2, 0, 1.0},   /* y2 -> y3           p3 y2          */
+    {3, 4, 3, 1, 3, 0, 10.0},  /* y3 -> y4           10 p3 y3       */
+    {4, 5, 1, 2, 4, 4, 1e-3},  /* 2 y4 -> y4 + y5    1e-3 p1 y4 y4  */
+    {5, 6, 0, 1, 5, 0, 25.0},  /* y5 -> y6           25 p0 y5       */
+    {6, 7, 2, 2, 6, 2, 0.1},   /* y6 + y2 -> y7 + y2 0.1 p2 y6 y2   */
+    {7, 0, 3, 1, 7, 0, 0.01},  /* y7 -> y0           0.01 p3 y7     */
+};
+
+/* Partial derivatives of w_r: the columns cols[0..n) and their values. */
+template <class T>
+int kin8_partials(const Reaction &r, const T *y, const T *p, int *cols, T *vals) {
+  const T k = T(r.c) * p[r.q];
+  if (r.na == 1) {
+    cols[0] = r.a; vals[0] = k;
+    return 1;
+  }
+  if (r.a == r.b) {
+    cols[0] = r.a; vals[0] = (T(2.0) * k) * y[r.a];
+    return 1;
+  }
+  cols[0] = r.a; vals[0] = k * y[r.b];
+  cols[1] = r.b; vals[1] = k * y[r.a];
+  return 2;
+}
+
+template <class T>
+T kin8_rate(const Reaction &r, const T *y, const T *p) {
+  const T w = (T(r.c) * p[r.q]) * y[r.a];
+  return r.na == 2 ? w * y[r.b] : w;
+}
+
 template <class T, bool F>
 void rhs_f(int kind, int d, const T *y, const T *p, T *out) {
   if (kind >= R_USER) {
@@ -385,6 +436,20 @@ void rhs_f(int kind, int d, const T *y, const T *p, T *out) {
       }
       break;
     }
+    case R_KINETICS8: {
+      T w[9];
+      for (int r = 0; r < 9; ++r) w[r] = kin8_rate(KIN8[r], y, p);
+      for (int a = 0; a < 8; ++a) {
+        T acc = T(0.0);
+        bool first = true;
+        for (int r = 0; r < 9; ++r) {
+          if (KIN8[r].src == a) { acc = first ? -w[r] : acc - w[r]; first = false; }
+          if (KIN8[r].dst == a) { acc = first ? w[r] : acc + w[r]; first = false; }
+        }
+        out[a] = acc;
+      }
+      break;
+    }
   }
 }
 
@@ -409,6 +474,25 @@ void rhs_jac(int kind, int d, const T *y, const T *p, T *J) {
       /* J22 = -2 k2 y2 - k3 y3 */
       J[3] = k1;   J[4] = mac<F>(-k3, y[2], -(T(2.0) * k2) * y[1]);  J[5] = -(k3 * y[1]);
       J[6] = T(0.0); J[7] = T(2.0) * k2 * y[1]; J[8] = T(0.0);
+      break;
+    }
+    case R_KINETICS8: {
+      /* J[a][b] = sum_r (e_dst - e_src)_a dw_r/dy_b, reactions in table order */
+      bool set[64] = {};
+      for (int r = 0; r < 9; ++r) {
+        int cols[2];
+        T vals[2];
+        const int m = kin8_partials(KIN8[r], y, p, cols, vals);
+        for (int e = 0; e < m; ++e) {
+          const int b = cols[e];
+          T &s = J[KIN8[r].src * 8 + b];
+          s = set[KIN8[r].src * 8 + b] ? s - vals[e] : -vals[e];
+          set[KIN8[r].src * 8 + b] = true;
+          T &t = J[KIN8[r].dst * 8 + b];
+          t = set[KIN8[r].dst * 8 + b] ? t + vals[e] : vals[e];
+          set[KIN8[r].dst * 8 + b] = true;
+        }
+      }
       break;
     }
   }
@@ -461,6 +545,24 @@ void rhs_vjp_y(int kind, int d, const T *y, const T *p, const T *v, T *w) {
       }
       break;
     }
+    case R_KINETICS8: {
+      /* w_b = sum_r dw_r/dy_b (v_dst - v_src), reactions in table order */
+      bool set[8] = {};
+      for (int r = 0; r < 9; ++r) {
+        int cols[2];
+        T vals[2];
+        const int m = kin8_partials(KIN8[r], y, p, cols, vals);
+        const T dl = v[KIN8[r].dst] - v[KIN8[r].src];
+        for (int e = 0; e < m; ++e) {
+          const int b = cols[e];
+          w[b] = set[b] ? mac<F>(vals[e], dl, w[b]) : vals[e] * dl;
+          set[b] = true;
+        }
+      }
+      for (int b = 0; b < 8; ++b)
+        if (!set[b]) w[b] = T(0.0);
+      break;
+    }
   }
 }
 
@@ -494,6 +596,15 @@ void rhs_vjp_p_acc(int kind, int d, const T *y, const T *p, const T *v, T *g) {
     }
     case R_LORENZ96:  /* df_i/dF = 1 */
       for (int i = 0; i < d; ++i) g[0] = g[0] + v[i];
+      break;
+    case R_KINETICS8:
+      /* g_q += dw_r/dp_q (v_dst - v_src), dw_r/dp_q = c_r y_a [y_b] */
+      for (int r = 0; r < 9; ++r) {
+        const Reaction &k = KIN8[r];
+        T dw = T(k.c) * y[k.a];
+        if (k.na == 2) dw = dw * y[k.b];
+        g[k.q] = mac<F>(dw, v[k.dst] - v[k.src], g[k.q]);
+      }
       break;
   }
 }
@@ -545,6 +656,30 @@ void rhs_jac_contract_acc(int kind, int d, const T *y, const T *p, const T *Jb,
       gp[1] = mac<F>(two_y2, Jb[7], gp[1]);
       break;
     }
+    case R_KINETICS8:
+      /* J = S dw/dy: for each partial dw_r/dy_b, with M = Jbar[dst][b] -
+       * Jbar[src][b], add M times its derivatives (reactions in table order,
+       * partials in reactant order, y before p) */
+      for (int r = 0; r < 9; ++r) {
+        const Reaction &k = KIN8[r];
+        const T kk = T(k.c) * p[k.q];
+        auto M = [&](int b) { return Jb[k.dst * 8 + b] - Jb[k.src * 8 + b]; };
+        if (k.na == 1) {
+          gp[k.q] = mac<F>(T(k.c), M(k.a), gp[k.q]);
+        } else if (k.a == k.b) {
+          const T m = M(k.a);
+          gy[k.a] = mac<F>(T(2.0) * kk, m, gy[k.a]);
+          gp[k.q] = mac<F>((T(2.0) * T(k.c)) * y[k.a], m, gp[k.q]);
+        } else {
+          const T ma = M(k.a);  /* partial k y_b in column a */
+          gy[k.b] = mac<F>(kk, ma, gy[k.b]);
+          gp[k.q] = mac<F>(T(k.c) * y[k.b], ma, gp[k.q]);
+          const T mb = M(k.b);  /* partial k y_a in column b */
+          gy[k.a] = mac<F>(kk, mb, gy[k.a]);
+          gp[k.q] = mac<F>(T(k.c) * y[k.a], mb, gp[k.q]);
+        }
+      }
+      break;
   }
 }
 
@@ -555,6 +690,7 @@ bool rhs_shape_ok(int kind, int d, int P) {
     case R_LORENZ63: return d == 3 && P == 3;
     case R_ROBERTSON: return d == 3 && P == 3;
     case R_LORENZ96: return d >= 4 && d <= MAXD && P == 1;
+    case R_KINETICS8: return d == 8 && P == 4;
   }
   return false;
 }
@@ -683,9 +819,9 @@ void lu_solve_t(int d, const T *LU, const int *perm, const T *b, T *x) {
 /* Everything one ROS2 step computes from (y, h). */
 template <class T>
 struct Ros2Step {
-  T J[9], LU[9];
-  int perm[3];
-  T f1[3], k1[3], Y2[3], f2[3], r2[3], k2[3], ynew[3], err[3];
+  T J[MAXR * MAXR], LU[MAXR * MAXR];
+  int perm[MAXR];
+  T f1[MAXR], k1[MAXR], Y2[MAXR], f2[MAXR], r2[MAXR], k2[MAXR], ynew[MAXR], err[MAXR];
 };
 
 /* W = I - gamma h J; k1 = W^-1 f(y); Y2 = y + h k1;
@@ -726,7 +862,8 @@ template <class T, bool F>
 void ros2_step_adjoint(int kind, int d, const T *y, const T *p, T h, T *lam, T *gp) {
   Ros2Step<T> s;
   ros2_forward<T, F>(kind, d, y, p, h, s);
-  T yb[3], kb1[3], kb2[3], rb1[3], rb2[3], Y2b[3], w[3], Wb[9], Jb[9];
+  T yb[MAXR], kb1[MAXR], kb2[MAXR], rb1[MAXR], rb2[MAXR], Y2b[MAXR], w[MAXR], Wb[MAXR * MAXR],
+      Jb[MAXR * MAXR];
   for (int c = 0; c < d; ++c) {
     const T ab = h * lam[c];      /* adjoint of the weighted stage sum */
     kb1[c] = T(1.5) * ab;
@@ -797,9 +934,9 @@ const RosTab RODAS3 = make_rodas3();
 
 template <class T>
 struct RodasStep {
-  T J[9], LU[9];
-  int perm[3];
-  T Y[4][3], f[4][3], r[4][3], u[4][3], ynew[3], err[3];
+  T J[MAXR * MAXR], LU[MAXR * MAXR];
+  int perm[MAXR];
+  T Y[4][MAXR], f[4][MAXR], r[4][MAXR], u[4][MAXR], ynew[MAXR], err[MAXR];
 };
 
 /* Stage sums: Y_i from y, adding a_ij u_j for j = 0, 1, ...; r_i the sum of
@@ -870,7 +1007,7 @@ void rodas_step_adjoint(const RosTab &tb, int kind, int d, const T *y, const T *
   RodasStep<T> s;
   rodas_forward<T, F>(tb, kind, d, y, p, h, s);
   const T gh = T(tb.gamma) * h;
-  T yb[3], ub[3], fb[3], rb[4][3], Yb[4][3], Wb[9], Jb[9];
+  T yb[MAXR], ub[MAXR], fb[MAXR], rb[4][MAXR], Yb[4][MAXR], Wb[MAXR * MAXR], Jb[MAXR * MAXR];
   for (int c = 0; c < d; ++c) yb[c] = lam[c];
   for (int i = tb.s - 1; i >= 0; --i) {
     for (int c = 0; c < d; ++c) {
@@ -936,7 +1073,8 @@ int validate(const orc_problem *P) {
   if (P->method < 0 || P->method > 3) return E_INVAL;
   if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
   const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
-  if (ros && P->dim > 3) return E_UNSUPPORTED;
+  /* the Rosenbrock methods need the explicit Jacobian of the built-in systems */
+  if (ros && (P->dim > MAXR || P->rhs == R_LORENZ96)) return E_UNSUPPORTED;
   if (P->dense != 0 && P->dense != 1) return E_INVAL;
   if (P->dense && ros) return E_UNSUPPORTED;
   if (P->rhs >= R_USER && ros) return E_UNSUPPORTED;
@@ -1854,12 +1992,12 @@ int orc_initial_step_f64(const orc_problem *P, const double *y0, const double *p
 /* One right-hand-side evaluation and its products (for direct checks). */
 int orc_rhs_f64(int32_t kind, int32_t d, const double *y, const double *p, const double *v,
                 double *f, double *wy, double *gp, double *J) {
-  if (!rhs_shape_ok(kind, d, kind == R_LORENZ96 ? 1 : (kind == R_LINEAR ? 1 : 3)))
-    return E_INVAL;
+  const int np = kind == R_LORENZ96 || kind == R_LINEAR ? 1 : kind == R_KINETICS8 ? 4 : 3;
+  if (!rhs_shape_ok(kind, d, np)) return E_INVAL;
   rhs_f<double, false>(kind, d, y, p, f);
   rhs_vjp_y<double, false>(kind, d, y, p, v, wy);
   rhs_vjp_p_acc<double, false>(kind, d, y, p, v, gp);
-  if (J && d <= 3) rhs_jac<double, false>(kind, d, y, p, J);
+  if (J && d <= MAXR && kind != R_LORENZ96) rhs_jac<double, false>(kind, d, y, p, J);
   return E_OK;
 }
 

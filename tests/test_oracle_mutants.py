@@ -79,6 +79,11 @@ MUTANTS = {
         "mac<F>(-rb[i][a], s.u[tb.s - 1][b], Wb[a * d + b]);"),
     "rodas3_vjp_at_step_start": ("rhs_vjp_y<T, F>(kind, d, s.Y[i], p, fb, Yb[i]);",
                                  "rhs_vjp_y<T, F>(kind, d, y, p, fb, Yb[i]);"),
+    "kinetics8_partial_of_wrong_reactant": ("cols[0] = r.a; vals[0] = k * y[r.b];",
+                                            "cols[0] = r.a; vals[0] = k * y[r.a];"),
+    "kinetics8_contraction_flipped": (
+        "auto M = [&](int b) { return Jb[k.dst * 8 + b] - Jb[k.src * 8 + b]; };",
+        "auto M = [&](int b) { return Jb[k.src * 8 + b] - Jb[k.dst * 8 + b]; };"),
 }
 
 
@@ -96,6 +101,7 @@ def _battery():
         out.append((pins.test_lorenz96_fixed_point, dict(method=m)))
     out += [(pins.test_robertson_ros2_conservation, {"method": W.ROS2}),
             (pins.test_robertson_ros2_conservation, {"method": W.RODAS3}),
+            (pins.test_kinetics8_conservation_and_reference, {"method": W.RODAS3}),
             (pins.test_dopri5_record_matches_scipy_rk45, {}),
             (pins.test_loss_values_match_their_definitions, {}),
             (pins.test_rhs_vjp_against_dense_jacobian, {})]

@@ -359,6 +359,46 @@ def test_robertson_ros2_conservation(orc, method):
     assert np.all(np.abs(gp * inp["p"]) < 1e-9)
 
 
+# the eight-species cycle written out from its reaction list, independently
+# of the oracle: (source, target, parameter, coefficient, reactants)
+_KIN8 = [(0, 1, 0, 1.0, (0,)), (1, 2, 1, 1.0, (1, 1)), (1, 0, 2, 1.0, (1, 2)),
+         (2, 3, 3, 1.0, (2,)), (3, 4, 3, 10.0, (3,)), (4, 5, 1, 1e-3, (4, 4)),
+         (5, 6, 0, 25.0, (5,)), (6, 7, 2, 0.1, (6, 2)), (7, 0, 3, 0.01, (7,))]
+
+
+def _kin8_f(y, p):
+    S = np.zeros((8, 9))
+    w = np.zeros(9)
+    for r, (src, dst, q, c, reac) in enumerate(_KIN8):
+        S[src, r] -= 1.0
+        S[dst, r] += 1.0
+        w[r] = c * p[q] * np.prod([y[a] for a in reac])
+    return S @ w
+
+
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3])
+def test_kinetics8_conservation_and_reference(orc, method):
+    """The eight-species cycle: every reaction moves one unit, so both
+    Rosenbrock methods keep sum y fixed and the gradient of sum y_N is 1 for
+    u0 and 0 for the rates; the recorded solution agrees with SciPy's Radau
+    on the system written out above from its reaction list."""
+    from scipy.integrate import solve_ivp
+    inp = W.make_inputs(6, 6)
+    prob = W.WORKLOADS[6].problem(method=method, t1=30.0, max_steps=20000)
+    m = orc.record(prob, inp["u0"], inp["p"])
+    assert np.all(m["status"] == 0)
+    ys, yN = orc.replay(prob, inp["u0"], inp["p"], m)
+    assert np.allclose(yN.sum(1), 1.0, rtol=0, atol=1e-13)
+    loss, gu0, gp = orc.replay_grad(prob, inp["u0"], inp["p"], m, W.COTANGENT,
+                                    aux=np.ones((6, 1, 8)))
+    assert np.allclose(gu0, 1.0, rtol=0, atol=1e-10)
+    assert np.all(np.abs(gp * inp["p"]) < 1e-8)
+    for i in range(2):
+        ref = solve_ivp(lambda t, y: _kin8_f(y, inp["p"][i]), (0, 30.0), inp["u0"][i],
+                        method="Radau", rtol=1e-11, atol=1e-15).y[:, -1]
+        assert np.allclose(yN[i], ref, rtol=1e-4, atol=2e-9), (method, i)
+
+
 def test_record_equals_replay_bitwise(orc):
     """The replay reproduces the recorded states bit for bit (both roundings)."""
     for wid, n in [(1, 64), (2, 32), (3, 32), (4, 8), (5, 8)]:
@@ -513,6 +553,12 @@ def _cases():
     inp = W.make_inputs(4, 4)
     out.append(("robertson_rodas3", W.WORKLOADS[4].problem(t1=300.0, method=W.RODAS3),
                 inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(6, 3)
+    out.append(("kinetics8_rodas3_saves", W.WORKLOADS[6].problem(t1=20.0, save_times=(0.5, 20.0)),
+                inp["u0"], inp["p"], W.COTANGENT,
+                np.random.default_rng(5).standard_normal((3, 2, 8))))
+    out.append(("kinetics8_ros2", W.WORKLOADS[6].problem(t1=0.5, method=W.ROS2, max_steps=8192),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
     inp = W.make_inputs(1, 6)
     out.append(("lorenz63_rodas3_saves", W.WORKLOADS[1].problem(
         method=W.RODAS3, max_steps=4096, save_times=(0.3, 0.7, 1.0)), inp["u0"], inp["p"],
@@ -604,7 +650,7 @@ def test_rhs_vjp_against_dense_jacobian(orc):
     """J^T v and J_p^T v of each system against finite-difference Jacobians."""
     rng = np.random.default_rng(9)
     for kind, d, P in [(W.LORENZ63, 3, 3), (W.ROBERTSON, 3, 3), (W.LORENZ96, 8, 1),
-                       (W.LINEAR, 1, 1)]:
+                       (W.LINEAR, 1, 1), (W.KINETICS8, 8, 4)]:
         y = rng.standard_normal(d)
         p = rng.uniform(0.5, 2.0, P)
         v = rng.standard_normal(d)

@@ -24,6 +24,13 @@ Five workloads, all synthetic (the pages name the systems, not data files):
    x0 = F + N(0, 0.01^2) per component, t in [0, 2], Tsit5, rtol=atol=1e-7,
    at most 4096 steps; loss = sum of squared final states.
 
+A sixth workload stands in for the HIRES test problem that the pages pair
+with higher-order stiff methods (its equations are not on the pages):
+6. The eight-species mass-action reaction cycle (d = 8, P = 4), n=65536, FP64,
+   rates p = (0.04, 3e7, 1e4, 1) * exp(0.1 N(0,1)) per component,
+   y0 = (1, 0, ..., 0), t in [0, 100], Rodas3, rtol=1e-6, atol=1e-10, at most
+   2048 steps; loss = sum of squared final states.
+
 Random draws use ``numpy.random.default_rng(seed)`` with seed = workload
 number, in this order: parameter multipliers [n, P], then initial-state noise
 [n, d] (workloads 2 and 5), then target perturbations [n, P] (workload 3).
@@ -38,12 +45,12 @@ import numpy as np
 
 # Integer codes shared by convention (not by code) with both implementations.
 TSIT5, DOPRI5, ROS2, RODAS3 = 0, 1, 2, 3
-LINEAR, LORENZ63, ROBERTSON, LORENZ96 = 0, 1, 2, 3
+LINEAR, LORENZ63, ROBERTSON, LORENZ96, KINETICS8 = 0, 1, 2, 3, 4
 SUMSQ_FINAL, MSE_SAVE, COTANGENT = 0, 1, 2
 
 METHOD_NAMES = {TSIT5: "tsit5", DOPRI5: "dopri5", ROS2: "ros2", RODAS3: "rodas3"}
 RHS_NAMES = {LINEAR: "linear", LORENZ63: "lorenz63", ROBERTSON: "robertson",
-             LORENZ96: "lorenz96"}
+             LORENZ96: "lorenz96", KINETICS8: "kinetics8"}
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,10 +137,13 @@ WORKLOADS = {
                 65536, 0.0, 1e5, 1e-6, 1e-10, 16384, SUMSQ_FINAL),
     5: Workload(5, "lorenz96_n64_tsit5_f64_n16384", LORENZ96, 64, 1, TSIT5, "f64",
                 16384, 0.0, 2.0, 1e-7, 1e-7, 4096, SUMSQ_FINAL),
+    6: Workload(6, "kinetics8_rodas3_f64_n65536", KINETICS8, 8, 4, RODAS3, "f64",
+                65536, 0.0, 100.0, 1e-6, 1e-10, 2048, SUMSQ_FINAL),
 }
 
 LORENZ_P0 = (10.0, 28.0, 8.0 / 3.0)
 ROBERTSON_K0 = (0.04, 3e7, 1e4)
+KINETICS8_K0 = (0.04, 3e7, 1e4, 1.0)
 
 
 def make_inputs(wid: int, n: Optional[int] = None) -> dict:
@@ -159,6 +169,11 @@ def make_inputs(wid: int, n: Optional[int] = None) -> dict:
         mult = np.exp(0.1 * rng.standard_normal((n, 3)))
         p = np.asarray(ROBERTSON_K0)[None, :] * mult
         u0 = np.zeros((n, 3))
+        u0[:, 0] = 1.0
+    elif w.rhs == KINETICS8:
+        mult = np.exp(0.1 * rng.standard_normal((n, 4)))
+        p = np.asarray(KINETICS8_K0)[None, :] * mult
+        u0 = np.zeros((n, 8))
         u0[:, 0] = 1.0
     elif w.rhs == LORENZ96:
         F = 8.0 * rng.uniform(0.9, 1.1, size=(n, 1))
