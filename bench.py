@@ -57,6 +57,13 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 #    48, solution 18 and error 3) = 234; adjoint (stage cotangents 60, four
 #    transposed solves 60, Wbar 63, fbar 12, J^T v and J_p^T v at four stages
 #    132, ybar sums 12, Jbar 9 and dJ contraction 29) = 377; total 611.
+#  Rodas3 / eight-species kinetics (dense 8 x 8 factors, as implemented):
+#    forward (rate partials and Jacobian 14, W 73, LU 316, four right-hand
+#    sides 112, four solves 480, stage sums Y_i 48 and stage right-hand sides
+#    128, solution 48 and error 8) = 1227; adjoint (stage cotangents 160,
+#    four transposed solves 480, Wbar 448, fbar 32, J^T v and J_p^T v at four
+#    stages 288, ybar sums 32, Jbar 64 and dJ contraction 53) = 1557; total
+#    2784.
 #  Tsit5 / Lorenz-96 (d components): forward 6 x 4d + 48d = 72d; adjoint
 #    42d + 6 x (J^T v 7d + J_p^T v d + accumulate d) = 96d; total 168d.
 # Forward-mode sensitivities (all d + P unit directions as dual numbers, the
@@ -75,7 +82,8 @@ def sens_flop_per_step(method: str, rhs: str, dim: int):
 
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
     table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
-             ("ros2", "robertson"): 306, ("rodas3", "robertson"): 611}
+             ("ros2", "robertson"): 306, ("rodas3", "robertson"): 611,
+             ("rodas3", "kinetics8"): 2784}
     if rhs == "lorenz96" and method == "tsit5":
         return 168 * dim
     return table[(method, rhs)]

@@ -39,6 +39,7 @@ bool shape_ok(int rhs, int d, int P) {
     case DA_RHS_LORENZ63: return d == 3 && P == 3;
     case DA_RHS_ROBERTSON: return d == 3 && P == 3;
     case DA_RHS_LORENZ96: return d >= 4 && d <= 64 && P == 1;
+    case DA_RHS_KINETICS8: return d == 8 && P == 4;
   }
   return false;
 }
@@ -69,7 +70,7 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
     const int rc = dadj::rtc_check(*pb, msg);
     if (rc) return fail(rc, "%s", msg.c_str());
   } else {
-    if (pb->rhs < DA_RHS_LINEAR || pb->rhs > DA_RHS_LORENZ96)
+    if (pb->rhs < DA_RHS_LINEAR || pb->rhs > DA_RHS_KINETICS8)
       return fail(DA_EINVAL, "bad rhs %d", pb->rhs);
     if (!shape_ok(pb->rhs, pb->dim, pb->n_params))
       return fail(DA_EINVAL, "rhs %d does not take dim=%d, n_params=%d", pb->rhs, pb->dim,
@@ -77,6 +78,8 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
     if (pb->rhs == DA_RHS_LORENZ96 && rosenbrock)
       return fail(DA_EUNSUPPORTED,
                   "the Rosenbrock methods are available for systems of dimension <= 3 only");
+    if (pb->rhs == DA_RHS_KINETICS8 && !rosenbrock)
+      return fail(DA_EUNSUPPORTED, "the kinetics system takes the Rosenbrock methods only");
   }
   if (!(isfinite(pb->t0) && isfinite(pb->t1) && pb->t1 > pb->t0))
     return fail(DA_EINVAL, "need finite t0 < t1");

@@ -235,6 +235,148 @@ struct Robertson {
     gp[1] = mac(two_y2, Jb[7], gp[1]);
   }
 };
+// ---------------------------------------------------------------------------
+// Eight-species reaction cycle: a synthetic stiff system of the size of the
+// HIRES test problem.  Nine mass-action reactions r0..r8 each move one unit
+// of mass from species src to species dst (sum y_i is conserved):
+//   r0 y0 -> y1            w = p0 y0            r5 2 y4 -> y4 + y5  ((1e-3 p1) y4) y4
+//   r1 2 y1 -> y1 + y2     (p1 y1) y1           r6 y5 -> y6          (25 p0) y5
+//   r2 y1 + y2 -> y0 + y2  (p2 y1) y2           r7 y6 + y2 -> y7 + y2 ((0.1 p2) y6) y2
+//   r3 y2 -> y3            p3 y2                r8 y7 -> y0          (0.01 p3) y7
+//   r4 y3 -> y4            (10 p3) y3
+// f_a = sum_r (e_dst - e_src)_a w_r.  Every sum runs over the reactions in
+// that order (a product or the first term, then multiply-adds or
+// additions); a two-reactant rate k y_a y_b has the partials k y_b (in
+// column a) and k y_a (column b), and k y_a^2 has (2k) y_a.
+// ---------------------------------------------------------------------------
+struct Kinetics8 {
+  static constexpr int D = 8, P = 4;
+  template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
+    const T w0 = (T(1.0) * p[0]) * y[0];
+    const T w1 = ((T(1.0) * p[1]) * y[1]) * y[1];
+    const T w2 = ((T(1.0) * p[2]) * y[1]) * y[2];
+    const T w3 = (T(1.0) * p[3]) * y[2];
+    const T w4 = (T(10.0) * p[3]) * y[3];
+    const T w5 = ((T(1e-3) * p[1]) * y[4]) * y[4];
+    const T w6 = (T(25.0) * p[0]) * y[5];
+    const T w7 = ((T(0.1) * p[2]) * y[6]) * y[2];
+    const T w8 = (T(0.01) * p[3]) * y[7];
+    o[0] = ((-w0) + w2) + w8;
+    o[1] = (w0 - w1) - w2;
+    o[2] = w1 - w3;
+    o[3] = w3 - w4;
+    o[4] = w4 - w5;
+    o[5] = w5 - w6;
+    o[6] = w6 - w7;
+    o[7] = w7 - w8;
+  }
+  // partials of the rates: r0..r8 in order, two-reactant ones column a then b
+  template <class T> struct Partials {
+    T d0_0, d1_1, d2_1, d2_2, d3_2, d4_3, d5_4, d6_5, d7_6, d7_2, d8_7;
+  };
+  template <class T>
+  __device__ static __forceinline__ Partials<T> partials(const T *y, const T *p) {
+    Partials<T> d;
+    const T k2 = T(1.0) * p[2], k7 = T(0.1) * p[2];
+    d.d0_0 = T(1.0) * p[0];
+    d.d1_1 = (T(2.0) * (T(1.0) * p[1])) * y[1];
+    d.d2_1 = k2 * y[2];
+    d.d2_2 = k2 * y[1];
+    d.d3_2 = T(1.0) * p[3];
+    d.d4_3 = T(10.0) * p[3];
+    d.d5_4 = (T(2.0) * (T(1e-3) * p[1])) * y[4];
+    d.d6_5 = T(25.0) * p[0];
+    d.d7_6 = k7 * y[2];
+    d.d7_2 = k7 * y[6];
+    d.d8_7 = T(0.01) * p[3];
+    return d;
+  }
+  // J^T v: w_b = sum_r dw_r/dy_b (v_dst - v_src)
+  template <class T>
+  __device__ static __forceinline__ void vjp_y(const T *y, const T *p, const T *v, T *w) {
+    const Partials<T> d = partials(y, p);
+    const T l0 = v[1] - v[0], l1 = v[2] - v[1], l2 = v[0] - v[1], l3 = v[3] - v[2];
+    const T l4 = v[4] - v[3], l5 = v[5] - v[4], l6 = v[6] - v[5], l7 = v[7] - v[6];
+    const T l8 = v[0] - v[7];
+    w[0] = d.d0_0 * l0;
+    w[1] = mac(d.d2_1, l2, d.d1_1 * l1);
+    w[2] = mac(d.d7_2, l7, mac(d.d3_2, l3, d.d2_2 * l2));
+    w[3] = d.d4_3 * l4;
+    w[4] = d.d5_4 * l5;
+    w[5] = d.d6_5 * l6;
+    w[6] = d.d7_6 * l7;
+    w[7] = d.d8_7 * l8;
+  }
+  // g_q += dw_r/dp_q (v_dst - v_src), reactions in order
+  template <class T>
+  __device__ static __forceinline__ void vjp_p_acc(const T *y, const T *p, const T *v, T *g) {
+    g[0] = mac(T(1.0) * y[0], v[1] - v[0], g[0]);
+    g[1] = mac((T(1.0) * y[1]) * y[1], v[2] - v[1], g[1]);
+    g[2] = mac((T(1.0) * y[1]) * y[2], v[0] - v[1], g[2]);
+    g[3] = mac(T(1.0) * y[2], v[3] - v[2], g[3]);
+    g[3] = mac(T(10.0) * y[3], v[4] - v[3], g[3]);
+    g[1] = mac((T(1e-3) * y[4]) * y[4], v[5] - v[4], g[1]);
+    g[0] = mac(T(25.0) * y[5], v[6] - v[5], g[0]);
+    g[2] = mac((T(0.1) * y[6]) * y[2], v[7] - v[6], g[2]);
+    g[3] = mac(T(0.01) * y[7], v[0] - v[7], g[3]);
+  }
+  template <class T> __device__ static __forceinline__ void jac(const T *y, const T *p, T *J) {
+    const Partials<T> d = partials(y, p);
+#pragma unroll
+    for (int i = 0; i < 64; ++i) J[i] = T(0.0);
+    J[0 * 8 + 0] = -d.d0_0;       J[1 * 8 + 0] = d.d0_0;
+    J[1 * 8 + 1] = -d.d1_1;       J[2 * 8 + 1] = d.d1_1;
+    J[1 * 8 + 1] = J[1 * 8 + 1] - d.d2_1;
+    J[0 * 8 + 1] = d.d2_1;
+    J[1 * 8 + 2] = -d.d2_2;       J[0 * 8 + 2] = d.d2_2;
+    J[2 * 8 + 2] = -d.d3_2;       J[3 * 8 + 2] = d.d3_2;
+    J[3 * 8 + 3] = -d.d4_3;       J[4 * 8 + 3] = d.d4_3;
+    J[4 * 8 + 4] = -d.d5_4;       J[5 * 8 + 4] = d.d5_4;
+    J[5 * 8 + 5] = -d.d6_5;       J[6 * 8 + 5] = d.d6_5;
+    J[6 * 8 + 6] = -d.d7_6;       J[7 * 8 + 6] = d.d7_6;
+    J[6 * 8 + 2] = -d.d7_2;       J[7 * 8 + 2] = d.d7_2;
+    J[7 * 8 + 7] = -d.d8_7;       J[0 * 8 + 7] = d.d8_7;
+  }
+  // sum_ab Jbar_ab dJ_ab: for each rate partial, M = Jbar[dst][col] -
+  // Jbar[src][col] times its derivatives (y before p)
+  template <class T>
+  __device__ static __forceinline__ void jac_contract_acc(const T *y, const T *p, const T *Jb,
+                                                          T *gy, T *gp) {
+    gp[0] = mac(T(1.0), Jb[1 * 8 + 0] - Jb[0 * 8 + 0], gp[0]);                  // r0
+    {
+      const T m = Jb[2 * 8 + 1] - Jb[1 * 8 + 1];                                  // r1
+      gy[1] = mac(T(2.0) * (T(1.0) * p[1]), m, gy[1]);
+      gp[1] = mac((T(2.0) * T(1.0)) * y[1], m, gp[1]);
+    }
+    {
+      const T kk = T(1.0) * p[2];                                                // r2
+      const T ma = Jb[0 * 8 + 1] - Jb[1 * 8 + 1];
+      gy[2] = mac(kk, ma, gy[2]);
+      gp[2] = mac(T(1.0) * y[2], ma, gp[2]);
+      const T mb = Jb[0 * 8 + 2] - Jb[1 * 8 + 2];
+      gy[1] = mac(kk, mb, gy[1]);
+      gp[2] = mac(T(1.0) * y[1], mb, gp[2]);
+    }
+    gp[3] = mac(T(1.0), Jb[3 * 8 + 2] - Jb[2 * 8 + 2], gp[3]);                  // r3
+    gp[3] = mac(T(10.0), Jb[4 * 8 + 3] - Jb[3 * 8 + 3], gp[3]);                 // r4
+    {
+      const T m = Jb[5 * 8 + 4] - Jb[4 * 8 + 4];                                  // r5
+      gy[4] = mac(T(2.0) * (T(1e-3) * p[1]), m, gy[4]);
+      gp[1] = mac((T(2.0) * T(1e-3)) * y[4], m, gp[1]);
+    }
+    gp[0] = mac(T(25.0), Jb[6 * 8 + 5] - Jb[5 * 8 + 5], gp[0]);                 // r6
+    {
+      const T kk = T(0.1) * p[2];                                                // r7
+      const T ma = Jb[7 * 8 + 6] - Jb[6 * 8 + 6];
+      gy[2] = mac(kk, ma, gy[2]);
+      gp[2] = mac(T(0.1) * y[2], ma, gp[2]);
+      const T mb = Jb[7 * 8 + 2] - Jb[6 * 8 + 2];
+      gy[6] = mac(kk, mb, gy[6]);
+      gp[2] = mac(T(0.1) * y[6], mb, gp[2]);
+    }
+    gp[3] = mac(T(0.01), Jb[0 * 8 + 7] - Jb[7 * 8 + 7], gp[3]);                 // r8
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Explicit RK stage machinery (one trajectory per lane, state in registers)

@@ -202,6 +202,8 @@ struct Rodas3 {
         return f64 ? FN<double, Rodas3<Lorenz63>> ARGS : FN<float, Rodas3<Lorenz63>> ARGS;  \
       case DA_RHS_ROBERTSON:                                                                \
         return f64 ? FN<double, Rodas3<Robertson>> ARGS : FN<float, Rodas3<Robertson>> ARGS; \
+      case DA_RHS_KINETICS8:                                                          \
+        return f64 ? FN<double, Rodas3<Kinetics8>> ARGS : FN<float, Rodas3<Kinetics8>> ARGS; \
       default:                                                                              \
         return hipErrorInvalidValue;                                                        \
     }                                                                                       \

@@ -149,6 +149,8 @@ struct Ros2 {
         return f64 ? FN<double, Ros2<Lorenz63>> ARGS : FN<float, Ros2<Lorenz63>> ARGS; \
       case DA_RHS_ROBERTSON:                                                          \
         return f64 ? FN<double, Ros2<Robertson>> ARGS : FN<float, Ros2<Robertson>> ARGS; \
+      case DA_RHS_KINETICS8:                                                          \
+        return f64 ? FN<double, Ros2<Kinetics8>> ARGS : FN<float, Ros2<Kinetics8>> ARGS; \
       default:                                                                        \
         return hipErrorInvalidValue;                                                  \
     }                                                                                 \

@@ -69,7 +69,8 @@ typedef enum { DA_F64 = 0, DA_F32 = 1 } da_dtype;
  * stiffly accurate, L-stable Rosenbrock method (four stages, embedded
  * second-order estimate, gamma = 1/2; Sandu et al. 1997) for stiff problems
  * at tight tolerances.  The Rosenbrock methods take systems of dimension
- * <= 3 and no dense output (DA_EUNSUPPORTED). */
+ * <= 3 and the eight-species kinetics system, and no dense output
+ * (DA_EUNSUPPORTED). */
 typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2, DA_RODAS3 = 3 } da_method;
 
 /* Built-in right-hand sides (dimension d, parameter count P):
@@ -79,12 +80,21 @@ typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2, DA_RODAS3 = 3 } da_meth
  *  DA_RHS_ROBERTSON d=3, P=3: (-k1 y1 + k3 y2 y3, k1 y1 - k2 y2^2 - k3 y2 y3,
  *                   k2 y2^2), p = (k1, k2, k3)
  *  DA_RHS_LORENZ96  4<=d<=64, P=1: x_i' = (x_{i+1} - x_{i-2}) x_{i-1} - x_i + F,
- *                   indices cyclic, p = (F).  Explicit methods only.       */
+ *                   indices cyclic, p = (F).  Explicit methods only.
+ *  DA_RHS_KINETICS8 d=8, P=4: an eight-species mass-action reaction cycle,
+ *                   a synthetic stiff system of the size of the HIRES test
+ *                   problem; nine reactions, each moving one unit of mass
+ *                   (sum y_i is conserved), with rates
+ *                   p0 y0 (y0->y1), p1 y1^2 (y1->y2), p2 y1 y2 (y1->y0),
+ *                   p3 y2 (y2->y3), 10 p3 y3 (y3->y4), 1e-3 p1 y4^2 (y4->y5),
+ *                   25 p0 y5 (y5->y6), 0.1 p2 y6 y2 (y6->y7), 0.01 p3 y7
+ *                   (y7->y0).  Rosenbrock methods only.                   */
 typedef enum {
   DA_RHS_LINEAR = 0,
   DA_RHS_LORENZ63 = 1,
   DA_RHS_ROBERTSON = 2,
-  DA_RHS_LORENZ96 = 3
+  DA_RHS_LORENZ96 = 3,
+  DA_RHS_KINETICS8 = 4
 } da_rhs;
 
 /* Identifiers of right-hand sides registered at run time (da_rhs_register)

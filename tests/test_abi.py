@@ -60,6 +60,10 @@ def test_unsupported_combinations(da):
         assert "Rosenbrock" in da.last_error()
         assert _call_record(da, W.WORKLOADS[4].problem(method=method, dense=1)) == -2
         assert "dense" in da.last_error()
+    for method in (W.TSIT5, W.DOPRI5):          # the kinetics system is stiff
+        assert _call_record(da, W.WORKLOADS[6].problem(method=method)) == -2
+        assert "Rosenbrock" in da.last_error()
+    assert _call_record(da, W.WORKLOADS[6].problem(dim=7)) == -1
     for dim in (3, 65):
         prob = W.Problem(W.LORENZ96, dim, 1, W.TSIT5, 0.0, 1.0, 1e-6, 1e-6, 100)
         assert _call_record(da, prob) == -1

@@ -7,7 +7,8 @@ oracle; the GPU's records agree with the oracle's (step counts, error
 norms, states); checkpoint intervals and the replay table give bit-for-bit
 the same gradients; forward-mode
 sensitivities against the oracle and against the reverse sweep; the
-Robertson workload at full size (65536 trajectories) sampled."""
+Robertson workload and the eight-species cycle at full size (65536
+trajectories) sampled."""
 import numpy as np
 import pytest
 
@@ -44,6 +45,11 @@ CASES = [
      1, W.COTANGENT, 400),
     ("linear", W.Problem(W.LINEAR, 1, 1, W.RODAS3, 0.0, 4.0, 1e-8, 1e-8, 4096,
                          save_times=(1.0, 4.0)), None, W.COTANGENT, 300),
+    # the eight-species cycle (8 x 8 factors per lane)
+    ("kinetics8", W.WORKLOADS[6].problem(t1=20.0), 6, W.SUMSQ_FINAL, 256),
+    ("kinetics8_ros2_saves", W.WORKLOADS[6].problem(method=W.ROS2, t1=0.5, max_steps=8192,
+                                                    save_times=(0.1, 0.5)),
+     6, W.COTANGENT, 128),
 ]
 
 
@@ -162,6 +168,45 @@ def test_rodas3_robertson_full_size_sampled(da, orc):
     ns_all = sm.n_steps.cpu().numpy()
     rng = np.random.default_rng(41)
     slots = np.unique(np.concatenate([rng.choice(n, 48, replace=False), [0, n - 1]]))
+    tr = perm[slots]
+    N = int(ns_all.max())
+    idx = torch.from_numpy(tr.astype(np.int64)).cuda()
+    h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
+    sub = {"h": np.ascontiguousarray(h), "n_steps": ns_all[tr],
+           "save_idx": sm.save_idx.cpu().numpy()[:, tr].T.copy(), "status": st[tr]}
+    pn = prob.replace(max_steps=N)
+    lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, W.SUMSQ_FINAL, fused=True)
+    err = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
+    mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
+    _print(f"  sampled {len(tr)}: max rel {err.max():.3e}; mean steps {ns_all.mean():.1f} "
+           f"(max {N}); oracle record of the sample {mo['n_steps'].mean():.1f}")
+    assert err.max() <= 1e-12
+    assert np.all(np.abs(sub["n_steps"] - mo["n_steps"]) <= np.maximum(2, 0.01 * mo["n_steps"]))
+
+
+def test_kinetics8_full_size_sampled(da, orc):
+    """The eight-species cycle at full size (65536 trajectories, Rodas3, t in
+    [0, 100]): record, replay order with table, one gradient pass; sampled
+    trajectories against the oracle on the GPU's mesh and its record; sum y
+    conserved by the GPU's record."""
+    w = W.WORKLOADS[6]
+    prob = w.problem()
+    inp = W.make_inputs(6)
+    n = w.n
+    _print(f"case: kinetics8 at full size, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, ys = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.SUMSQ_FINAL)()
+    torch.cuda.synchronize()
+    st = sm.status.cpu().numpy()
+    assert np.all(st == 0)
+    yN = ys.cpu().numpy()[-1]
+    assert np.max(np.abs(yN.sum(0) - 1.0)) < 1e-12
+    perm = sm.perm.cpu().numpy()
+    ns_all = sm.n_steps.cpu().numpy()
+    rng = np.random.default_rng(43)
+    slots = np.unique(np.concatenate([rng.choice(n, 32, replace=False), [0, n - 1]]))
     tr = perm[slots]
     N = int(ns_all.max())
     idx = torch.from_numpy(tr.astype(np.int64)).cuda()
