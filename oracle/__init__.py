@@ -179,6 +179,15 @@ def tableau(method: int) -> dict:
     return {"c": c, "a": a, "b": b, "e": e, "order": int(info[0]), "err_order": int(info[1])}
 
 
+def rk78_tableau() -> dict:
+    """The Fehlberg 7(8) coefficients as the oracle holds them: a[13, 13],
+    b (7th-order weights), e = b7 - b8."""
+    a = np.zeros((13, 13)); b = np.zeros(13); e = np.zeros(13)
+    info = np.zeros(2, dtype=np.int32)
+    _check(_load().orc_rk78_tableau(_ptr(a), _ptr(b), _ptr(e), _ptr(info)), "rk78_tableau")
+    return {"a": a, "b": b, "e": e, "order": int(info[0]), "err_order": int(info[1])}
+
+
 def record(prob, u0, p, fused: bool = False, nthreads: int = 0, with_h: bool = True) -> dict:
     """Adaptive solve per lane; returns the mesh and saved states."""
     u0 = np.ascontiguousarray(u0)

@@ -56,7 +56,7 @@ constexpr int MAXD = 64;  // largest state dimension handled
 constexpr int MAXR = 8;   // largest state dimension of the Rosenbrock methods
 constexpr int MAXP = 16;  // largest parameter count
 
-enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3 };
+enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3, M_RKF78 = 4 };
 enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3, R_KINETICS8 = 4 };
 constexpr int R_USER = 1024;  /* kinds from here: the caller's right-hand side */
 enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
@@ -759,6 +759,140 @@ void erk_step_adjoint(const Tableau &tb, int kind, int d, const T *y, const T *p
 }
 
 /* ------------------------------------------------------------------ */
+/* Fehlberg 7(8)                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Fehlberg's seventh-order pair with an eighth-order companion (Fehlberg
+ * 1968, NASA TR R-287): 13 stages, rational coefficients.  The 7th-order
+ * solution y + h sum b_j K_j uses K_1..K_11 and is propagated; the 8th-order
+ * one differs by (41/840) h (K_12 + K_13 - K_1 - K_11), and that difference
+ * is the error estimate (err = h sum e_j K_j, e = b7 - b8).  Not first same
+ * as last.  The coefficients are typed as the published fractions; a test
+ * checks them against the order conditions. */
+struct Rk78Tab {
+  double a[13][13];
+  double b[13];  /* 7th order */
+  double e[13];  /* b7 - b8 */
+};
+
+Rk78Tab make_rk78() {
+  Rk78Tab t;
+  std::memset(&t, 0, sizeof t);
+  double (&a)[13][13] = t.a;
+  a[1][0] = 2.0 / 27.0;
+  a[2][0] = 1.0 / 36.0; a[2][1] = 1.0 / 12.0;
+  a[3][0] = 1.0 / 24.0; a[3][2] = 1.0 / 8.0;
+  a[4][0] = 5.0 / 12.0; a[4][2] = -25.0 / 16.0; a[4][3] = 25.0 / 16.0;
+  a[5][0] = 1.0 / 20.0; a[5][3] = 1.0 / 4.0; a[5][4] = 1.0 / 5.0;
+  a[6][0] = -25.0 / 108.0; a[6][3] = 125.0 / 108.0; a[6][4] = -65.0 / 27.0;
+  a[6][5] = 125.0 / 54.0;
+  a[7][0] = 31.0 / 300.0; a[7][4] = 61.0 / 225.0; a[7][5] = -2.0 / 9.0; a[7][6] = 13.0 / 900.0;
+  a[8][0] = 2.0; a[8][3] = -53.0 / 6.0; a[8][4] = 704.0 / 45.0; a[8][5] = -107.0 / 9.0;
+  a[8][6] = 67.0 / 90.0; a[8][7] = 3.0;
+  a[9][0] = -91.0 / 108.0; a[9][3] = 23.0 / 108.0; a[9][4] = -976.0 / 135.0;
+  a[9][5] = 311.0 / 54.0; a[9][6] = -19.0 / 60.0; a[9][7] = 17.0 / 6.0; a[9][8] = -1.0 / 12.0;
+  a[10][0] = 2383.0 / 4100.0; a[10][3] = -341.0 / 164.0; a[10][4] = 4496.0 / 1025.0;
+  a[10][5] = -301.0 / 82.0; a[10][6] = 2133.0 / 4100.0; a[10][7] = 45.0 / 82.0;
+  a[10][8] = 45.0 / 164.0; a[10][9] = 18.0 / 41.0;
+  a[11][0] = 3.0 / 205.0; a[11][5] = -6.0 / 41.0; a[11][6] = -3.0 / 205.0;
+  a[11][7] = -3.0 / 41.0; a[11][8] = 3.0 / 41.0; a[11][9] = 6.0 / 41.0;
+  a[12][0] = -1777.0 / 4100.0; a[12][3] = -341.0 / 164.0; a[12][4] = 4496.0 / 1025.0;
+  a[12][5] = -289.0 / 82.0; a[12][6] = 2193.0 / 4100.0; a[12][7] = 51.0 / 82.0;
+  a[12][8] = 33.0 / 164.0; a[12][9] = 12.0 / 41.0; a[12][11] = 1.0;
+  double b8[13] = {};
+  t.b[0] = 41.0 / 840.0; t.b[5] = 34.0 / 105.0; t.b[6] = 9.0 / 35.0; t.b[7] = 9.0 / 35.0;
+  t.b[8] = 9.0 / 280.0; t.b[9] = 9.0 / 280.0; t.b[10] = 41.0 / 840.0;
+  b8[5] = 34.0 / 105.0; b8[6] = 9.0 / 35.0; b8[7] = 9.0 / 35.0; b8[8] = 9.0 / 280.0;
+  b8[9] = 9.0 / 280.0; b8[11] = 41.0 / 840.0; b8[12] = 41.0 / 840.0;
+  for (int j = 0; j < 13; ++j) t.e[j] = t.b[j] - b8[j];
+  return t;
+}
+const Rk78Tab RK78 = make_rk78();
+constexpr int RK78_ORDER = 7, RK78_ERR_ORDER = 7;  /* error of the 7th-order solution: h^8 */
+
+/* Stage i of a step: Y_i = fma(h, sum_{j<i} a_ij K_j, y) (a product, then
+ * multiply-adds), K_i = f(Y_i), for i = 1..last. */
+template <class T, bool F>
+void rk78_stages(int kind, int d, const T *y, const T *p, T h, int last, T (*Y)[MAXD],
+                 T (*K)[MAXD]) {
+  for (int c = 0; c < d; ++c) Y[0][c] = y[c];
+  rhs_f<T, F>(kind, d, y, p, K[0]);
+  for (int i = 1; i <= last; ++i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = T(0.0);
+      bool first = true;
+      for (int j = 0; j < i; ++j) {
+        if (RK78.a[i][j] == 0.0) continue;
+        acc = first ? T(RK78.a[i][j]) * K[j][c] : mac<F>(T(RK78.a[i][j]), K[j][c], acc);
+        first = false;
+      }
+      Y[i][c] = mac<F>(h, acc, y[c]);
+    }
+    rhs_f<T, F>(kind, d, Y[i], p, K[i]);
+  }
+}
+
+/* sum_j w_j K_j[c] over the nonzero weights (a product, then multiply-adds) */
+template <class T, bool F>
+T rk78_combine(const double *w, const T (*K)[MAXD], int c) {
+  T acc = T(0.0);
+  bool first = true;
+  for (int j = 0; j < 13; ++j) {
+    if (w[j] == 0.0) continue;
+    acc = first ? T(w[j]) * K[j][c] : mac<F>(T(w[j]), K[j][c], acc);
+    first = false;
+  }
+  return acc;
+}
+
+/* Trial step of the record: all 13 stages, the 7th-order solution and the
+ * error estimate. */
+template <class T, bool F>
+void rk78_attempt(int kind, int d, const T *y, const T *p, T h, T *ynew, T *err) {
+  T Y[13][MAXD], K[13][MAXD];
+  rk78_stages<T, F>(kind, d, y, p, h, 12, Y, K);
+  for (int c = 0; c < d; ++c) {
+    ynew[c] = mac<F>(h, rk78_combine<T, F>(RK78.b, K, c), y[c]);
+    err[c] = h * rk78_combine<T, F>(RK78.e, K, c);
+  }
+}
+
+/* Replay step: the 7th-order solution needs K_1..K_11. */
+template <class T, bool F>
+void rk78_step(int kind, int d, T *y, const T *p, T h) {
+  T Y[13][MAXD], K[13][MAXD];
+  rk78_stages<T, F>(kind, d, y, p, h, 10, Y, K);
+  for (int c = 0; c < d; ++c) y[c] = mac<F>(h, rk78_combine<T, F>(RK78.b, K, c), y[c]);
+}
+
+/* Reverse of rk78_step: kbar_i = h (b_i lam + sum_{l>i} a_li w_l) for
+ * i = 10..0 (terms in that order), w_i = J(Y_i)^T kbar_i,
+ * g += J_p(Y_i)^T kbar_i, then lam + w_10 + w_9 + ... + w_0. */
+template <class T, bool F>
+void rk78_step_adjoint(int kind, int d, const T *y, const T *p, T h, T *lam, T *gp) {
+  T Y[13][MAXD], K[13][MAXD], Wv[11][MAXD], kb[MAXD], lacc[MAXD];
+  rk78_stages<T, F>(kind, d, y, p, h, 10, Y, K);
+  for (int c = 0; c < d; ++c) lacc[c] = lam[c];
+  for (int i = 10; i >= 0; --i) {
+    for (int c = 0; c < d; ++c) {
+      T acc = T(0.0);
+      bool first = true;
+      if (RK78.b[i] != 0.0) { acc = T(RK78.b[i]) * lam[c]; first = false; }
+      for (int l = i + 1; l <= 10; ++l) {
+        if (RK78.a[l][i] == 0.0) continue;
+        acc = first ? T(RK78.a[l][i]) * Wv[l][c] : mac<F>(T(RK78.a[l][i]), Wv[l][c], acc);
+        first = false;
+      }
+      kb[c] = h * acc;
+    }
+    rhs_vjp_y<T, F>(kind, d, Y[i], p, kb, Wv[i]);
+    rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);
+    for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];
+  }
+  for (int c = 0; c < d; ++c) lam[c] = lacc[c];
+}
+
+/* ------------------------------------------------------------------ */
 /* ROS2 step                                                           */
 /* ------------------------------------------------------------------ */
 
@@ -1070,13 +1204,14 @@ Opts make_opts(const orc_problem *P) {
 
 int validate(const orc_problem *P) {
   if (!P) return E_INVAL;
-  if (P->method < 0 || P->method > 3) return E_INVAL;
+  if (P->method < 0 || P->method > 4) return E_INVAL;
   if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
   const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
   /* the Rosenbrock methods need the explicit Jacobian of the built-in systems */
   if (ros && (P->dim > MAXR || P->rhs == R_LORENZ96)) return E_UNSUPPORTED;
   if (P->dense != 0 && P->dense != 1) return E_INVAL;
-  if (P->dense && ros) return E_UNSUPPORTED;
+  if (P->dense && (ros || P->method == M_RKF78)) return E_UNSUPPORTED;
+  if (P->method == M_RKF78 && (P->rhs == R_LORENZ96 || P->rhs >= R_USER)) return E_UNSUPPORTED;
   if (P->rhs >= R_USER && ros) return E_UNSUPPORTED;
   if (!(P->t1 > P->t0)) return E_INVAL;
   if (!(P->rtol >= 0) || !(P->atol >= 0) || !(P->rtol + P->atol > 0)) return E_INVAL;
@@ -1224,8 +1359,11 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
   const int d = P->dim, kind = P->rhs;
   const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
   const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
-  const int qerr = P->method == M_ROS2 ? 1 : P->method == M_RODAS3 ? RODAS3.err_order : tb.err_order;
-  const int qord = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order : tb.order;
+  const bool rk78 = P->method == M_RKF78;
+  const int qerr = P->method == M_ROS2 ? 1 : P->method == M_RODAS3 ? RODAS3.err_order
+                 : rk78 ? RK78_ERR_ORDER : tb.err_order;
+  const int qord = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order
+                 : rk78 ? RK78_ORDER : tb.order;
   const T atol = T(P->atol), rtol = T(P->rtol);
   const T expo = T(-1.0) / T(qerr + 1);
   const T safety = T(o.safety), fmin = T(o.fac_min), fmax = T(o.fac_max);
@@ -1270,6 +1408,8 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
         RodasStep<T> rs;
         rodas_forward<T, F>(RODAS3, kind, d, y, p, hs, rs);
         for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+      } else if (rk78) {
+        rk78_attempt<T, F>(kind, d, y, p, hs, ynew, err);
       } else {
         erk_stages<T, F>(tb, kind, d, y, p, hs, 6, true, Y, K);
         const T *Kp[7];
@@ -1292,7 +1432,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
             if (out.ysave) dense_value<T, T, F>(kind, d, th, hs, y, ynew, p, &out.ysave[j * d]);
           }
         for (int c = 0; c < d; ++c) y[c] = ynew[c];
-        if (!ros)
+        if (!ros && !rk78)
           for (int c = 0; c < d; ++c) K[0][c] = K[6][c];  /* first same as last */
         t = t_new;
         T fac = (E == T(0.0)) ? fmax
@@ -1340,6 +1480,7 @@ template <class T, bool F>
 inline void one_step(const orc_problem *P, T *y, const T *p, T h) {
   if (P->method == M_ROS2) ros2_step<T, F>(P->rhs, P->dim, y, p, h);
   else if (P->method == M_RODAS3) rodas_step<T, F>(RODAS3, P->rhs, P->dim, y, p, h);
+  else if (P->method == M_RKF78) rk78_step<T, F>(P->rhs, P->dim, y, p, h);
   else erk_step<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p, h);
 }
 
@@ -1349,6 +1490,8 @@ inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, 
   if (P->method == M_ROS2) ros2_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
   else if (P->method == M_RODAS3)
     rodas_step_adjoint<T, F>(RODAS3, P->rhs, P->dim, y, p, h, lam, gp);
+  else if (P->method == M_RKF78)
+    rk78_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
   else erk_step_adjoint<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p,
                               h, lam, gp, gpc);
 }
@@ -1560,6 +1703,8 @@ T mesh_max_err_lane(const orc_problem *P, const T *u0, const T *p, const T *h, i
       RodasStep<T> rs;
       rodas_forward<T, F>(RODAS3, kind, d, y, p, h[k], rs);
       for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
+    } else if (P->method == M_RKF78) {
+      rk78_attempt<T, F>(kind, d, y, p, h[k], ynew, err);
     } else {
       rhs_f<T, F>(kind, d, y, p, K[0]);
       erk_stages<T, F>(tb, kind, d, y, p, h[k], 6, true, Y, K);
@@ -1783,6 +1928,16 @@ int orc_tableau(int method, double *c, double *a, double *b, double *e, int32_t 
 
 double orc_ros2_gamma(void) { return ROS2_GAMMA; }
 
+/* The Fehlberg 7(8) coefficients as typed: a[13][13], b (7th order), e. */
+int orc_rk78_tableau(double *a, double *b, double *e, int32_t *info) {
+  for (int i = 0; i < 13; ++i) {
+    b[i] = RK78.b[i]; e[i] = RK78.e[i];
+    for (int j = 0; j < 13; ++j) a[i * 13 + j] = RK78.a[i][j];
+  }
+  info[0] = RK78_ORDER; info[1] = RK78_ERR_ORDER;
+  return E_OK;
+}
+
 /* The caller's right-hand side from a plugin (see user_types.h): f on reals
  * (double, float) and on dual numbers (plain and fused, double and float). */
 int orc_set_user_rhs(int32_t dim, int32_t n_params, void *f64, void *f32, void *dp64, void *df64,
@@ -1984,7 +2139,8 @@ int orc_initial_step_f64(const orc_problem *P, const double *y0, const double *p
   if (rc) return rc;
   double f0[MAXD];
   rhs_f<double, false>(P->rhs, P->dim, y0, p, f0);
-  const int q = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order : 5;
+  const int q = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order
+              : P->method == M_RKF78 ? RK78_ORDER : 5;
   *h0 = initial_step<double, false>(P->rhs, P->dim, y0, f0, p, P->atol, P->rtol, q);
   return E_OK;
 }

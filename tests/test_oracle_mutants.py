@@ -79,6 +79,9 @@ MUTANTS = {
         "mac<F>(-rb[i][a], s.u[tb.s - 1][b], Wb[a * d + b]);"),
     "rodas3_vjp_at_step_start": ("rhs_vjp_y<T, F>(kind, d, s.Y[i], p, fb, Yb[i]);",
                                  "rhs_vjp_y<T, F>(kind, d, y, p, fb, Yb[i]);"),
+    "rkf78_digit": ("a[8][4] = 704.0 / 45.0;", "a[8][4] = 704.0 / 44.0;"),
+    "rkf78_adjoint_drops_last_stage": ("      for (int l = i + 1; l <= 10; ++l) {\n        if (RK78.a[l][i] == 0.0) continue;",
+                                       "      for (int l = i + 1; l <= 9; ++l) {\n        if (RK78.a[l][i] == 0.0) continue;"),
     "kinetics8_partial_of_wrong_reactant": ("cols[0] = r.a; vals[0] = k * y[r.b];",
                                             "cols[0] = r.a; vals[0] = k * y[r.a];"),
     "kinetics8_contraction_flipped": (
@@ -97,6 +100,8 @@ def _battery():
         out.append((pins.test_linear_decay_closed_form, dict(method=m, fused=False)))
         out.append((pins.test_lorenz63_origin_linearisation, dict(method=m)))
     out.append((pins.test_rodas3_order_stability_and_estimator, {}))
+    out += [(pins.test_rkf78_tableau_is_fehlberg, {}),
+            (pins.test_linear_decay_closed_form, dict(method=W.RKF78, fused=False))]
     for m in (W.TSIT5, W.DOPRI5):
         out.append((pins.test_lorenz96_fixed_point, dict(method=m)))
     out += [(pins.test_robertson_ros2_conservation, {"method": W.ROS2}),

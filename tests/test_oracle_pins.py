@@ -82,13 +82,156 @@ def test_dopri5_rationals(orc):
 def _stability_poly(t):
     """Coefficients of R(z) = 1 + z b^T (I - zA)^{-1} 1 = sum_j (b^T A^{j-1} 1) z^j."""
     A, b = t["a"], t["b"]
-    one = np.ones(7)
+    s = len(b)
+    one = np.ones(s)
     coef = [1.0]
     v = one.copy()
-    for _ in range(7):
+    for _ in range(s):
         coef.append(b @ v)
         v = A @ v
     return np.array(coef)
+
+
+# Fehlberg 7(8), typed here from the published fractions independently of the
+# oracle: rows of a (stage: {column: value}), the 7th- and 8th-order weights.
+_F = Fr
+_RK78_A = {
+    1: {0: _F(2, 27)}, 2: {0: _F(1, 36), 1: _F(1, 12)}, 3: {0: _F(1, 24), 2: _F(1, 8)},
+    4: {0: _F(5, 12), 2: _F(-25, 16), 3: _F(25, 16)}, 5: {0: _F(1, 20), 3: _F(1, 4), 4: _F(1, 5)},
+    6: {0: _F(-25, 108), 3: _F(125, 108), 4: _F(-65, 27), 5: _F(125, 54)},
+    7: {0: _F(31, 300), 4: _F(61, 225), 5: _F(-2, 9), 6: _F(13, 900)},
+    8: {0: _F(2), 3: _F(-53, 6), 4: _F(704, 45), 5: _F(-107, 9), 6: _F(67, 90), 7: _F(3)},
+    9: {0: _F(-91, 108), 3: _F(23, 108), 4: _F(-976, 135), 5: _F(311, 54), 6: _F(-19, 60),
+        7: _F(17, 6), 8: _F(-1, 12)},
+    10: {0: _F(2383, 4100), 3: _F(-341, 164), 4: _F(4496, 1025), 5: _F(-301, 82),
+         6: _F(2133, 4100), 7: _F(45, 82), 8: _F(45, 164), 9: _F(18, 41)},
+    11: {0: _F(3, 205), 5: _F(-6, 41), 6: _F(-3, 205), 7: _F(-3, 41), 8: _F(3, 41), 9: _F(6, 41)},
+    12: {0: _F(-1777, 4100), 3: _F(-341, 164), 4: _F(4496, 1025), 5: _F(-289, 82),
+         6: _F(2193, 4100), 7: _F(51, 82), 8: _F(33, 164), 9: _F(12, 41), 11: _F(1)},
+}
+_RK78_B7 = {0: _F(41, 840), 5: _F(34, 105), 6: _F(9, 35), 7: _F(9, 35), 8: _F(9, 280),
+            9: _F(9, 280), 10: _F(41, 840)}
+_RK78_B8 = {5: _F(34, 105), 6: _F(9, 35), 7: _F(9, 35), 8: _F(9, 280), 9: _F(9, 280),
+            11: _F(41, 840), 12: _F(41, 840)}
+
+
+def _rk78_float():
+    A = np.zeros((13, 13))
+    for i, row in _RK78_A.items():
+        for j, v in row.items():
+            A[i, j] = float(v)
+    b = np.zeros(13)
+    for j, v in _RK78_B7.items():
+        b[j] = float(v)
+    return {"a": A, "b": b}
+
+
+def _rooted_trees(n, memo={}):
+    """Rooted trees with n vertices, each a sorted tuple of its subtrees."""
+    if n not in memo:
+        if n == 1:
+            memo[n] = [()]
+        else:
+            out = set()
+
+            def forests(rem, maxsize, maxtree):
+                if rem == 0:
+                    yield ()
+                    return
+                for size in range(min(rem, maxsize), 0, -1):
+                    for t in _rooted_trees(size):
+                        if size == maxsize and maxtree is not None and t > maxtree:
+                            continue
+                        for rest in forests(rem - size, size, t):
+                            yield (t,) + rest
+            for f in forests(n - 1, n - 1, None):
+                out.add(tuple(sorted(f)))
+            memo[n] = sorted(out)
+    return memo[n]
+
+
+def _tree_density(t):
+    """gamma(t): the order of t times the densities of its subtrees."""
+    g = 1 + sum(_tree_order(c) for c in t)
+    for c in t:
+        g *= _tree_density(c)
+    return g
+
+
+def _tree_order(t):
+    return 1 + sum(_tree_order(c) for c in t)
+
+
+def _elementary_weight(t, A, s):
+    """Per-stage vector of the elementary differential of t: the product over
+    the subtrees u of (A Phi(u))."""
+    v = [Fr(1)] * s
+    for u in t:
+        w = _elementary_weight(u, A, s)
+        v = [v[i] * sum((A.get(i, {}).get(j, 0) * w[j] for j in range(s)), Fr(0))
+             for i in range(s)]
+    return v
+
+
+def _order_defects(b, A, s, order):
+    """Number of trees with up to ``order`` vertices whose condition
+    b^T Phi(t) = 1/gamma(t) fails (exact rational arithmetic)."""
+    bad = 0
+    for n in range(1, order + 1):
+        for t in _rooted_trees(n):
+            phi = _elementary_weight(t, A, s)
+            if sum((b.get(i, 0) * phi[i] for i in range(s)), Fr(0)) != Fr(1, _tree_density(t)):
+                bad += 1
+    return bad
+
+
+def test_rkf78_tableau_is_fehlberg(orc):
+    """The oracle holds Fehlberg's 7(8) coefficients: each equals the nearest
+    double of the published fraction, and the fractions satisfy every order
+    condition up to order 7 for the propagated weights (85 trees) and up to
+    order 8 for the companion (200 trees), the propagated weights not order 8."""
+    t = orc.rk78_tableau()
+    assert t["order"] == 7 and t["err_order"] == 7
+    A = np.zeros((13, 13))
+    for i, row in _RK78_A.items():
+        for j, v in row.items():
+            A[i, j] = float(v)
+    assert np.array_equal(t["a"], A)
+    b7 = np.array([float(_RK78_B7.get(j, 0)) for j in range(13)])
+    b8 = np.array([float(_RK78_B8.get(j, 0)) for j in range(13)])
+    assert np.array_equal(t["b"], b7) and np.array_equal(t["e"], b7 - b8)
+    assert sum(len(_rooted_trees(n)) for n in range(1, 9)) == 200
+    assert _order_defects(_RK78_B7, _RK78_A, 13, 7) == 0
+    assert _order_defects(_RK78_B8, _RK78_A, 13, 8) == 0
+    assert _order_defects(_RK78_B7, _RK78_A, 13, 8) > 0
+
+
+def test_rkf78_global_order_and_step_scaling(orc):
+    """Global order 7 on Lorenz-63 with fixed steps, against SciPy's DOP853 at
+    1e-14; recorded step counts grow as tol^(-1/8) (error estimate O(h^8))."""
+    from scipy.integrate import solve_ivp
+    u0 = np.array([[1.0, 1.0, 1.0]])
+    pv = np.array([[10.0, 28.0, 8.0 / 3.0]])
+    ref = solve_ivp(lambda t, y: [10 * (y[1] - y[0]), y[0] * (28 - y[2]) - y[1],
+                                  y[0] * y[1] - 8 / 3 * y[2]], (0, 0.5), u0[0],
+                    method="DOP853", rtol=1e-14, atol=1e-14).y[:, -1]
+    errs = []
+    for N in (10, 20, 40):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.RKF78, 0.0, 0.5, 1e-6, 1e-6, N)
+        mesh = {"h": np.full((1, N), 0.5 / N), "n_steps": np.array([N]),
+                "save_idx": np.array([[N]]), "status": np.zeros(1)}
+        _, yN = orc.replay(pr, u0, pv, mesh)
+        errs.append(np.abs(yN[0] - ref).max())
+    orders = [math.log2(errs[i] / errs[i + 1]) for i in range(2)]
+    assert all(6.5 < o < 7.6 for o in orders), (orders, errs)
+    inp = W.make_inputs(1, 8)
+    steps = []
+    for tol in (1e-6, 1e-12):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.RKF78, 0.0, 1.0, tol, tol, 100000)
+        m = orc.record(pr, inp["u0"], inp["p"])
+        assert np.all(m["status"] == 0)
+        steps.append(m["n_steps"].mean())
+    assert 4.3 < steps[1] / steps[0] < 7.3, steps                  # 1e6^(1/8) = 5.6
 
 
 def test_dopri5_stability_polynomial(orc):
@@ -161,7 +304,7 @@ def _complex_step(fn, z):
     return (fn(z + 1j * eps)).imag / eps
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
 @pytest.mark.parametrize("fused", [False, True])
 def test_linear_decay_closed_form(orc, method, fused):
     """y' = -k y on an arbitrary mesh: y_N = y0 prod R(-k h_n); exact derivative
@@ -180,7 +323,7 @@ def test_linear_decay_closed_form(orc, method, fused):
     elif method == W.RODAS3:
         R = _R_rodas3
     else:
-        coef = _stability_poly(orc.tableau(method))
+        coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
         R = lambda z: _R_erk(coef, z)
     prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, 1e-6, 1e-6, N)
     mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
@@ -257,7 +400,7 @@ def _matrix_R(method, orc, Z):
         return I + 2 * Z @ Wm + 0.5 * Z @ Z @ Wm @ Wm - Z @ Wm @ Wm
     if method == W.RODAS3:
         return _rodas3_matrix(Z)
-    coef = _stability_poly(orc.tableau(method))
+    coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
     out = np.zeros_like(Z)
     Zp = I.copy()
     for cj in coef:
@@ -266,7 +409,7 @@ def _matrix_R(method, orc, Z):
     return out
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
 def test_lorenz63_origin_linearisation(orc, method):
     """At the origin Lorenz-63 is a fixed point; the replay's Jacobian is the
     product of R(h_n A) with A = [[-s, s, 0], [r, -1, 0], [0, 0, -b]].  A
@@ -440,7 +583,7 @@ def test_save_times_are_mesh_points(orc):
 def test_global_error_tracks_tolerance(orc):
     """y' = -y on [0, 1]: the recorded solve's error at t=1 stays below the
     tolerance scale and shrinks as the tolerance does."""
-    for method in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3):
+    for method in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78):
         errs = []
         for tol in (1e-4, 1e-6, 1e-8):
             prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, tol, tol, 100000)
@@ -552,6 +695,13 @@ def _cases():
                 np.array([[1.0], [2.0]]), np.array([[-0.7], [0.4]]), W.SUMSQ_FINAL, None))
     inp = W.make_inputs(4, 4)
     out.append(("robertson_rodas3", W.WORKLOADS[4].problem(t1=300.0, method=W.RODAS3),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(1, 6)
+    out.append(("lorenz63_rkf78_saves", W.WORKLOADS[1].problem(
+        method=W.RKF78, rtol=1e-9, atol=1e-9, save_times=(0.3, 0.7, 1.0)), inp["u0"], inp["p"],
+        W.MSE_SAVE, np.random.default_rng(6).standard_normal((6, 3, 3))))
+    inp = W.make_inputs(4, 4)
+    out.append(("robertson_rkf78", W.WORKLOADS[4].problem(t1=0.3, method=W.RKF78, max_steps=8192),
                 inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
     inp = W.make_inputs(6, 3)
     out.append(("kinetics8_rodas3_saves", W.WORKLOADS[6].problem(t1=20.0, save_times=(0.5, 20.0)),
@@ -686,7 +836,7 @@ def test_fp32_oracle_tracks_fp64(orc):
 # Forward-mode sensitivities (tangents carried through the replay)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
 @pytest.mark.parametrize("fused", [False, True])
 def test_sensitivities_linear_closed_form(orc, method, fused):
     """y' = p y on an arbitrary mesh: dy_N/dy0 = prod R(p h_n) and
@@ -702,7 +852,7 @@ def test_sensitivities_linear_closed_form(orc, method, fused):
     elif method == W.RODAS3:
         R = _R_rodas3
     else:
-        coef = _stability_poly(orc.tableau(method))
+        coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
         R = lambda z: _R_erk(coef, z)
     prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, 1e-6, 1e-6, N)
     mesh = {"h": h, "n_steps": np.full(n, N), "save_idx": np.full((n, 1), N),
