@@ -21,8 +21,9 @@ SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), 
                    "oracle.cpp")
 
 MUTANTS = {
-    "drop_first_stage_adjoint": ("for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];",
-                                 "for (int c = 0; c < d; ++c) if (i > 0) lacc[c] = lacc[c] + Wv[i][c];"),
+    "drop_first_stage_adjoint": (
+        "rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);\n    for (int c = 0; c < d; ++c) lacc[c] = lacc[c] + Wv[i][c];\n  }\n  for (int c = 0; c < d; ++c) lam[c] = lacc[c];\n}\n\n/* ------------------------------------------------------------------ */\n/* Fehlberg",
+        "rhs_vjp_p_acc<T, F>(kind, d, Y[i], p, kb, gp);\n    for (int c = 0; c < d; ++c) if (i > 0) lacc[c] = lacc[c] + Wv[i][c];\n  }\n  for (int c = 0; c < d; ++c) lam[c] = lacc[c];\n}\n\n/* ------------------------------------------------------------------ */\n/* Fehlberg"),
     "lorenz_vjp_sign": ("w[2] = mac<F>(-b, v[2], (-y[0]) * v[1]);",
                         "w[2] = mac<F>(b, v[2], (-y[0]) * v[1]);"),
     "lorenz_vjp_index": ("w[1] = mac<F>(y[0], v[2], mac<F>(s, v[0], -v[1]));",
