@@ -57,6 +57,10 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 #    48, solution 18 and error 3) = 234; adjoint (stage cotangents 60, four
 #    transposed solves 60, Wbar 63, fbar 12, J^T v and J_p^T v at four stages
 #    132, ybar sums 12, Jbar 9 and dJ contraction 29) = 377; total 611.
+#  Fehlberg 7(8) / Lorenz-63: forward (11 right-hand sides of 8 flop = 88,
+#    stage sums over the nonzero a_ij and the solution over the 7 nonzero
+#    b_j: 3 x 105 = 315) = 403; adjoint (stage cotangents 3 x 94 = 282, J^T v
+#    and J_p^T v at 11 stages 220, lam sums 33) = 535; total 938.
 #  Rodas3 / eight-species kinetics (dense 8 x 8 factors, as implemented):
 #    forward (rate partials and Jacobian 14, W 73, LU 316, four right-hand
 #    sides 112, four solves 480, stage sums Y_i 48 and stage right-hand sides
@@ -83,7 +87,7 @@ def sens_flop_per_step(method: str, rhs: str, dim: int):
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
     table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
              ("ros2", "robertson"): 306, ("rodas3", "robertson"): 611,
-             ("rodas3", "kinetics8"): 2784}
+             ("rodas3", "kinetics8"): 2784, ("rkf78", "lorenz63"): 938}
     if rhs == "lorenz96" and method == "tsit5":
         return 168 * dim
     return table[(method, rhs)]
@@ -108,6 +112,7 @@ KERNEL_SOURCES = {
              "dadj_internal.hpp"],
     "rodas3": ["lane_kernels.hpp", "rosenbrock.hpp", "rodas3.hip", "dadj_device.hpp",
                "dadj_internal.hpp"],
+    "rkf78": ["lane_kernels.hpp", "rkf78.hip", "dadj_device.hpp", "dadj_internal.hpp"],
     "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
 }
 
@@ -115,7 +120,7 @@ KERNEL_SOURCES = {
 def kernel_family(method: str, rhs: str) -> str:
     if rhs == "lorenz96":
         return "wave"
-    return method if method in ("ros2", "rodas3") else "erk"
+    return method if method in ("ros2", "rodas3", "rkf78") else "erk"
 
 
 def kernel_source_hash(family: str = "erk") -> str:
@@ -210,9 +215,10 @@ def main():
     ap.add_argument("--rhs-source", action="store_true",
                     help="Lorenz-63 workloads: run the system as a right-hand side compiled at "
                          "run time from source instead of the built-in one")
-    ap.add_argument("--method", choices=["rodas3"], default=None,
-                    help="workload 4 (Robertson): integrate with the third-order Rosenbrock "
-                         "method Rodas3 instead of ROS2, at the same tolerances")
+    ap.add_argument("--method", choices=["rodas3", "rkf78"], default=None,
+                    help="rodas3: workload 4 (Robertson) with the third-order Rosenbrock "
+                         "method instead of ROS2; rkf78: workload 2 (Lorenz-63) with "
+                         "Fehlberg 7(8) instead of Dopri5; same tolerances")
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
@@ -232,10 +238,14 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
-    if args.method:
+    if args.method == "rodas3":
         if args.workload != 4:
             sys.exit("--method rodas3 is available for workload 4 (Robertson)")
         w = dataclasses.replace(w, method=W.RODAS3, name=w.name.replace("ros2", "rodas3"))
+    elif args.method == "rkf78":
+        if args.workload != 2:
+            sys.exit("--method rkf78 is available for workload 2 (Lorenz-63)")
+        w = dataclasses.replace(w, method=W.RKF78, name=w.name.replace("dopri5", "rkf78"))
     prob = w.problem(checkpoint=args.checkpoint, dense=int(args.dense))
     if args.rhs_source:
         if w.rhs != W.LORENZ63:

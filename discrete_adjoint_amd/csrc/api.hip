@@ -62,7 +62,7 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (!pb) return fail(DA_EINVAL, "problem is NULL");
   if (n < 0 || n > (int64_t)0x7fffffff) return fail(DA_EINVAL, "n = %lld out of range", (long long)n);
   if (pb->dtype != DA_F64 && pb->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", pb->dtype);
-  if (pb->method < DA_TSIT5 || pb->method > DA_RODAS3)
+  if (pb->method < DA_TSIT5 || pb->method > DA_RKF78)
     return fail(DA_EINVAL, "bad method %d", pb->method);
   const bool rosenbrock = pb->method == DA_ROS2 || pb->method == DA_RODAS3;
   if (pb->rhs >= DA_RHS_USER_BASE) {
@@ -80,6 +80,8 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
                   "the Rosenbrock methods are available for systems of dimension <= 3 only");
     if (pb->rhs == DA_RHS_KINETICS8 && !rosenbrock)
       return fail(DA_EUNSUPPORTED, "the kinetics system takes the Rosenbrock methods only");
+    if (pb->rhs == DA_RHS_LORENZ96 && pb->method == DA_RKF78)
+      return fail(DA_EUNSUPPORTED, "Lorenz-96 takes Tsit5 and Dopri5 only");
   }
   if (!(isfinite(pb->t0) && isfinite(pb->t1) && pb->t1 > pb->t0))
     return fail(DA_EINVAL, "need finite t0 < t1");
@@ -104,8 +106,8 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
       pb->checkpoint != 8)
     return fail(DA_EINVAL, "checkpoint must be 0, 1, 2, 4 or 8");
   if (pb->dense != 0 && pb->dense != 1) return fail(DA_EINVAL, "dense must be 0 or 1");
-  if (pb->dense && rosenbrock)
-    return fail(DA_EUNSUPPORTED, "dense output is available for the explicit methods");
+  if (pb->dense && (rosenbrock || pb->method == DA_RKF78))
+    return fail(DA_EUNSUPPORTED, "dense output is available for Tsit5 and Dopri5");
   pr.rhs = pb->rhs;
   pr.dim = pb->dim;
   pr.n_params = pb->n_params;
@@ -169,6 +171,7 @@ hipError_t launch_record(const dadj::RecordArgs &a, const dadj::SaveTimes &st, h
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_record(a, st, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_record(a, st, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_record(a, st, s);
+  if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_record(a, st, s);
   return dadj::launch_erk_record(a, st, s);
 }
 
@@ -177,6 +180,7 @@ hipError_t launch_replay_fwd(const dadj::ReplayArgs &a, hipStream_t s) {
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_fwd(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_fwd(a, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_replay_fwd(a, s);
+  if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_replay_fwd(a, s);
   return dadj::launch_erk_replay_fwd(a, s);
 }
 
@@ -185,6 +189,7 @@ hipError_t launch_replay_grad(const dadj::ReplayArgs &a, hipStream_t s) {
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_grad(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_grad(a, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_replay_grad(a, s);
+  if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_replay_grad(a, s);
   return dadj::launch_erk_replay_grad(a, s);
 }
 
@@ -471,6 +476,7 @@ static int replay_sens(const da_problem *prob, int64_t n, const void *u0, const 
                        : pr.rhs == DA_RHS_LORENZ96   ? dadj::launch_l96_replay_sens(a, s)
                        : pr.method == DA_ROS2        ? dadj::launch_ros2_replay_sens(a, s)
                        : pr.method == DA_RODAS3      ? dadj::launch_rodas3_replay_sens(a, s)
+                       : pr.method == DA_RKF78       ? dadj::launch_rkf78_replay_sens(a, s)
                                                      : dadj::launch_erk_replay_sens(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_sens launch");
   return ok();

@@ -70,8 +70,17 @@ typedef enum { DA_F64 = 0, DA_F32 = 1 } da_dtype;
  * second-order estimate, gamma = 1/2; Sandu et al. 1997) for stiff problems
  * at tight tolerances.  The Rosenbrock methods take systems of dimension
  * <= 3 and the eight-species kinetics system, and no dense output
- * (DA_EUNSUPPORTED). */
-typedef enum { DA_TSIT5 = 0, DA_DOPRI5 = 1, DA_ROS2 = 2, DA_RODAS3 = 3 } da_method;
+ * (DA_EUNSUPPORTED).  DA_RKF78 is Fehlberg's 7(8) pair (13 stages, the
+ * 7th-order solution propagated, its difference to the 8th-order one the
+ * error estimate; Fehlberg 1968), the higher-order explicit method for
+ * tight tolerances: linear, Lorenz-63 and Robertson, no dense output. */
+typedef enum {
+  DA_TSIT5 = 0,
+  DA_DOPRI5 = 1,
+  DA_ROS2 = 2,
+  DA_RODAS3 = 3,
+  DA_RKF78 = 4
+} da_method;
 
 /* Built-in right-hand sides (dimension d, parameter count P):
  *  DA_RHS_LINEAR    d=1, P=1: y' = p0 y
@@ -126,8 +135,8 @@ typedef enum {
  * Adaptive control (record and forward solve): error norm = RMS over
  * components of err / (atol + rtol max(|y_n|, |y_{n+1}|)); accept iff it is
  * <= 1; next step = used step * clamp(safety E^(-1/(q+1)), fac_min, fac_max)
- * with q the embedded order (4 for the explicit pairs, 1 for ROS2, 2 for
- * Rodas3), no growth
+ * with q the embedded order (4 for the 5(4) pairs, 1 for ROS2, 2 for
+ * Rodas3, 7 for Fehlberg 7(8)), no growth
  * on the step after a rejection.  Steps are shortened to land exactly on each
  * save time and on t1, or, with dense = 1, on t1 only, each save time then
  * being read from the interpolant of the accepted step that contains it

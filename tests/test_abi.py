@@ -43,7 +43,7 @@ def _call_record(da, prob, n=4, dtype_code=0, **kw):
 
 @pytest.mark.parametrize("change,code", [
     (dict(t1=0.0), -1), (dict(rtol=0.0, atol=0.0), -1), (dict(max_steps=0), -1),
-    (dict(dim=4), -1), (dict(method=7), -1), (dict(method=4), -1), (dict(rhs=9), -1),
+    (dict(dim=4), -1), (dict(method=7), -1), (dict(method=5), -1), (dict(rhs=9), -1),
     (dict(save_times=(0.5, 0.4)), -1), (dict(save_times=(0.5, 2.0)), -1),
     (dict(rtol=-1.0), -1), (dict(safety=-0.5), -1),
 ])
@@ -64,6 +64,11 @@ def test_unsupported_combinations(da):
         assert _call_record(da, W.WORKLOADS[6].problem(method=method)) == -2
         assert "Rosenbrock" in da.last_error()
     assert _call_record(da, W.WORKLOADS[6].problem(dim=7)) == -1
+    assert _call_record(da, W.WORKLOADS[6].problem(method=W.RKF78)) == -2
+    assert _call_record(da, W.WORKLOADS[1].problem(method=W.RKF78, dense=1)) == -2
+    assert "dense" in da.last_error()
+    assert _call_record(da, W.WORKLOADS[5].problem(method=W.RKF78)) == -2
+    assert "Lorenz-96" in da.last_error()
     for dim in (3, 65):
         prob = W.Problem(W.LORENZ96, dim, 1, W.TSIT5, 0.0, 1.0, 1e-6, 1e-6, 100)
         assert _call_record(da, prob) == -1

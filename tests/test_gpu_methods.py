@@ -1,4 +1,6 @@
-"""Rodas3 (the third-order Rosenbrock method) on the GPU against the oracle.
+"""The higher-order methods on the GPU against the oracle: Rodas3 (the
+third-order Rosenbrock method, also on the eight-species kinetics system with
+ROS2) and Fehlberg 7(8) (the seventh-order explicit pair).
 
 Gates: on oracle-recorded meshes (fused rounding), saves, losses and
 gradients within 1e-12 relative per trajectory in FP64 (the arithmetic
@@ -7,8 +9,8 @@ oracle; the GPU's records agree with the oracle's (step counts, error
 norms, states); checkpoint intervals and the replay table give bit-for-bit
 the same gradients; forward-mode
 sensitivities against the oracle and against the reverse sweep; the
-Robertson workload and the eight-species cycle at full size (65536
-trajectories) sampled."""
+Robertson workload and the eight-species cycle with Rodas3 (65536
+trajectories) and Lorenz-63 with Fehlberg 7(8) (2^20) at full size, sampled."""
 import numpy as np
 import pytest
 
@@ -50,17 +52,28 @@ CASES = [
     ("kinetics8_ros2_saves", W.WORKLOADS[6].problem(method=W.ROS2, t1=0.5, max_steps=8192,
                                                     save_times=(0.1, 0.5)),
      6, W.COTANGENT, 128),
+    # Fehlberg 7(8)
+    ("rkf78_lorenz63_saves_mse", W.WORKLOADS[1].problem(method=W.RKF78, rtol=1e-9, atol=1e-9,
+                                                        save_times=(0.3, 0.7, 1.0)),
+     1, W.MSE_SAVE, 400),
+    ("rkf78_lorenz63_tight", W.WORKLOADS[2].problem(method=W.RKF78, t1=2.0, rtol=1e-12,
+                                                    atol=1e-12),
+     2, W.SUMSQ_FINAL, 300),
+    ("rkf78_robertson", W.WORKLOADS[4].problem(method=W.RKF78, t1=0.3, max_steps=8192),
+     4, W.SUMSQ_FINAL, 200),
+    ("rkf78_linear", W.Problem(W.LINEAR, 1, 1, W.RKF78, 0.0, 4.0, 1e-10, 1e-10, 4096,
+                               save_times=(1.0, 4.0)), None, W.COTANGENT, 300),
 ]
 
 
 @pytest.mark.parametrize("name,prob,wid,lk,n", CASES, ids=[c[0] for c in CASES])
-def test_rodas3_against_oracle(da, orc, name, prob, wid, lk, n):
+def test_method_against_oracle(da, orc, name, prob, wid, lk, n):
     inp = _linear_inputs(n) if wid is None else W.make_inputs(wid, n)
     u0n, pn = inp["u0"].astype(np.float64), inp["p"].astype(np.float64)
     d = prob.dim
     S = prob.n_save_eff
     aux = None if lk == W.SUMSQ_FINAL else np.random.default_rng(9).standard_normal((n, S, d))
-    _print(f"case: Rodas3 {name}, n={n}")
+    _print(f"case: {W.METHOD_NAMES[prob.method]} {name}, n={n}")
     m = orc.record(prob, u0n, pn, fused=True)
     assert np.all(m["status"] == 0)
     yo, _ = orc.replay(prob, u0n, pn, m, fused=True)
@@ -207,6 +220,43 @@ def test_kinetics8_full_size_sampled(da, orc):
     ns_all = sm.n_steps.cpu().numpy()
     rng = np.random.default_rng(43)
     slots = np.unique(np.concatenate([rng.choice(n, 32, replace=False), [0, n - 1]]))
+    tr = perm[slots]
+    N = int(ns_all.max())
+    idx = torch.from_numpy(tr.astype(np.int64)).cuda()
+    h = sm.h.index_select(1, idx).permute(1, 0, 2).reshape(len(tr), -1)[:, :N].cpu().numpy()
+    sub = {"h": np.ascontiguousarray(h), "n_steps": ns_all[tr],
+           "save_idx": sm.save_idx.cpu().numpy()[:, tr].T.copy(), "status": st[tr]}
+    pn = prob.replace(max_steps=N)
+    lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, W.SUMSQ_FINAL, fused=True)
+    err = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
+    mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
+    _print(f"  sampled {len(tr)}: max rel {err.max():.3e}; mean steps {ns_all.mean():.1f} "
+           f"(max {N}); oracle record of the sample {mo['n_steps'].mean():.1f}")
+    assert err.max() <= 1e-12
+    assert np.all(np.abs(sub["n_steps"] - mo["n_steps"]) <= np.maximum(2, 0.01 * mo["n_steps"]))
+
+
+def test_rkf78_lorenz63_full_size_sampled(da, orc):
+    """Lorenz-63 with Fehlberg 7(8) at the headline workload's size and
+    tolerances (2^20 trajectories, t in [0, 10], 1e-8): record, replay order
+    with table, one gradient pass; sampled trajectories against the oracle on
+    the GPU's mesh and against the oracle's record."""
+    w = W.WORKLOADS[2]
+    prob = w.problem(method=W.RKF78)
+    inp = W.make_inputs(2)
+    n = w.n
+    _print(f"case: Fehlberg 7(8) Lorenz-63 at full size, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p, save=False)
+    sm = da.mesh_sort(prob, mesh)
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.SUMSQ_FINAL)()
+    torch.cuda.synchronize()
+    st = sm.status.cpu().numpy()
+    assert np.all(st == 0)
+    perm = sm.perm.cpu().numpy()
+    ns_all = sm.n_steps.cpu().numpy()
+    rng = np.random.default_rng(47)
+    slots = np.unique(np.concatenate([rng.choice(n, 40, replace=False), [0, n - 1]]))
     tr = perm[slots]
     N = int(ns_all.max())
     idx = torch.from_numpy(tr.astype(np.int64)).cuda()
