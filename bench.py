@@ -123,13 +123,21 @@ def kernel_family(method: str, rhs: str) -> str:
     return method if method in ("ros2", "rodas3", "rkf78") else "erk"
 
 
+# The host-side part of the internal header (launcher declarations and the
+# like) does not change any kernel: only the text before this marker counts.
+HOST_SECTION = b"#ifndef __HIPCC_RTC__  // host side"
+
+
 def kernel_source_hash(family: str = "erk") -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
         path = os.path.join(ROOT, "discrete_adjoint_amd", "csrc", f)
         if os.path.exists(path):
             with open(path, "rb") as fh:
-                h.update(fh.read())
+                text = fh.read()
+            if f == "dadj_internal.hpp" and HOST_SECTION in text:
+                text = text[:text.index(HOST_SECTION)]
+            h.update(text)
     return h.hexdigest()[:16]
 
 
