@@ -21,6 +21,15 @@ Printed on one JSON line, besides the driver's fields:
                 by what the counter reads for a copy of known size, when the
                 kernel sources match the ones the counters were taken with,
                 else null;
+  clock_adjusted  the same achieved rate against the vector peak at the
+                shader clock the counters measured while the gradient kernel
+                ran (GRBM_GUI_ACTIVE per XCD over the launch time), and the
+                executed FP64 rate (SQ_INSTS_VALU_*_F64: stage recomputation and
+                padded steps included) over the live launch time; from the
+                committed counter summary of the workload when the kernel
+                sources match it, else null;
+  record_log    bytes of the zero-padded step log the record writes, and the
+                rate over the record time;
   cpu_baseline  the CPU oracle (plain C++, OpenMP) on a bounded sample of the
                 same workload, as trajectory-gradients/s of the same job.
 
@@ -158,6 +167,36 @@ def read_traffic(workload_name: str, family: str, dense: bool = False):
     return traffic if src_hash == kernel_source_hash(family) else None
 
 
+def read_valu_clock(workload_name: str, family: str):
+    """Shader clock and executed FP64 work of the gradient kernel from the
+    committed counter summary of the workload (GRBM_GUI_ACTIVE per XCD over
+    the launch time; SQ_INSTS_VALU_{FMA,MUL,ADD,TRANS}_F64), if it was taken
+    with the current kernel sources."""
+    path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}_valu_clock.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        for key in ("kernel_source_hash", "clock_ghz", "valu_busy", "fp64_flop_executed_per_launch"):
+            if line.startswith(key + ":"):
+                vals[key] = line.split(":", 1)[1].strip()
+    if vals.get("kernel_source_hash") != kernel_source_hash(family) or len(vals) < 4:
+        return None
+    return {"clock_ghz": float(vals["clock_ghz"]), "valu_busy": float(vals["valu_busy"]),
+            "fp64_flop_executed_per_launch": float(vals["fp64_flop_executed_per_launch"]),
+            "source": os.path.relpath(path, ROOT)}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0,
                  dense: int = 0, method=None):
     """Oracle as it stands, plain rounding, all OpenMP threads: record + passes
@@ -191,7 +230,8 @@ def cpu_baseline(wid: int, lanes: int, passes: int, max_seconds: float = 25.0,
         t_pass.append(time.perf_counter() - t0)
     t_job = t_rec + passes * float(np.mean(t_pass))
     return {"value": lanes * passes / t_job, "unit": "trajectory-gradients/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "per_core": lanes * passes / t_job / cores,
+            "cpu_model": cpu_model(),
             "sample": f"first {lanes} of {w.n} trajectories of the workload: record "
                       f"{t_rec:.2f} s + {len(t_pass)} timed gradient passes (mean "
                       f"{np.mean(t_pass):.3f} s); job time = record + {passes} passes"}
@@ -320,8 +360,11 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     rec_ms = float(np.mean([e["rec0"].elapsed_time(e["rec1"]) for e in evs]))
     sort_ms = float(np.mean([e["rec1"].elapsed_time(e["sort1"]) for e in evs]))
-    pass_ms = float(np.mean([e["p0"][k].elapsed_time(e["p1"][k]) for e in evs
-                             for k in range(passes)]))
+    pass_all = [e["p0"][k].elapsed_time(e["p1"][k]) for e in evs for k in range(passes)]
+    pass_ms = float(np.mean(pass_all))
+    pass_med = float(np.median(pass_all))
+    pass_total = float(np.mean([sum(e["p0"][k].elapsed_time(e["p1"][k]) for k in range(passes))
+                                for e in evs]))
     # forward-mode gradient of the same loss on the same replay order and
     # table: all d + P directions, and the P parameter directions alone
     def timed(fn):
@@ -362,6 +405,10 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     traffic = None if args.rhs_source else read_traffic(w.name, kernel_family(mname, rname),
                                                           args.dense)
+    clk = None if (args.rhs_source or args.dense or args.checkpoint) else \
+        read_valu_clock(w.name, kernel_family(mname, rname))
+    log_bytes = (mesh.h.numel() * mesh.h.element_size() + mesh.n_steps.numel() * 4
+                 + mesh.save_idx.numel() * 4 + mesh.status.numel() * 4)
     out = {
         "metric": "trajectory-gradients/s (Lorenz FP64, 1M traj) + % of FP64 vector peak",
         "value": n * passes / (ms_per_step * 1e-3),
@@ -381,8 +428,21 @@ def main():
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "kernel": "k_replay_grad",
                      "flop_per_step": flop_step, "populated_steps_per_launch": total_steps},
-        "per_pass": {"ms": pass_ms, "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
+        "clock_adjusted": None if clk is None else {
+            "clock_ghz": clk["clock_ghz"],
+            "peak_at_clock": 256 * 128 * clk["clock_ghz"] / 1e3 * (1 if w.dtype == "f64" else 2),
+            "frac_at_clock": achieved / (256 * 128 * clk["clock_ghz"] / 1e3
+                                         * (1 if w.dtype == "f64" else 2)),
+            "valu_busy": clk["valu_busy"],
+            "executed_fp64_tflops": clk["fp64_flop_executed_per_launch"] / (pass_ms * 1e-3) / 1e12,
+            "source": clk["source"]},
+        "per_pass": {"ms": pass_ms, "median_ms": pass_med,
+                     f"total_ms_{passes}_passes": pass_total,
+                     "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
         "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
+        "record_log": {"bytes": log_bytes, "GB_per_s": log_bytes / (rec_ms * 1e-3) / 1e9,
+                       "what": "zero-padded step log written by the record kernel "
+                               "(step sizes, step counts, save indices, status)"},
         "forward_mode_grad": {
             "ms": float(np.mean(sens_ms)),
             "trajectory_gradients_per_s": n / (float(np.mean(sens_ms)) * 1e-3),
@@ -403,6 +463,7 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
                                            dense=int(args.dense), method=w.method)
+        out["cpu_baseline"]["gpu_over_cpu"] = out["value"] / out["cpu_baseline"]["value"]
     print(json.dumps(out), flush=True)
 
 
