@@ -168,10 +168,23 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // exactly on every save time and on t1 (DENSE: on t1 only; the save times
 // inside an accepted step are read from its interpolant); t accumulates in
 // double.  Accepted steps collect in a register chunk that is written when
-// full; after the last step the partial chunk and (unless the caller defers
-// them to da_mesh_pad) zero chunks up to the end
-// of the log follow.
+// full; after the last step the partial chunk follows.  The zero chunks past
+// a lane's last step (unless the caller defers them to da_mesh_pad) are
+// written from the end of the log downwards while the lane integrates: one
+// chunk row every PAD_EVERY attempts, as long as the row lies at or past the
+// chunk the next accepted step would go to (attempts >= accepted steps, so
+// the rule needs only the attempt count, which all lanes still in the loop
+// share: the wavefront writes one contiguous row).  A lane that takes more
+// steps than that overwrites the zeros later, in program order.  Spread over
+// the integration, these stores use the HBM bandwidth that the arithmetic
+// leaves free; the rows between the last step and the lowest zeroed row
+// follow the loop.
 // ---------------------------------------------------------------------------
+#ifndef DADJ_PAD_EVERY
+#define DADJ_PAD_EVERY 2
+#endif
+constexpr int PAD_EVERY = DADJ_PAD_EVERY;
+
 template <class T, class M, bool LOG, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
@@ -194,6 +207,8 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   T *theta = (T *)a.theta;
 
   int nacc = 0, natt = 0, st = LANE_OK;
+  const bool pad = LOG && !a.defer_pad && PAD_EVERY > 0;  // (uniform)
+  int zl = pr.n_chunks;  // rows [zl, n_chunks) of this lane are zero
   T hb[B];
 #pragma unroll
   for (int b = 0; b < B; ++b) hb[b] = T(0);
@@ -237,6 +252,13 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         if (natt >= pr.max_attempts) { st = LANE_MAX_ATTEMPTS; break; }
         if (!(hs > T(0)) || t + double(hs) == t) { st = LANE_DT_UNDERFLOW; break; }
         ++natt;
+        if (pad && natt % PAD_EVERY == 0 && zl - 1 >= natt / B) {
+          --zl;
+          T zb[B];
+#pragma unroll
+          for (int b = 0; b < B; ++b) zb[b] = T(0);
+          store_chunk(H + ((int64_t)zl * n + i) * B, zb);
+        }
         M::attempt(y, p, hs, cache, ynew, err);
         const T E = err_norm<D>(err, y, ynew, atol, rtol);
         if (E <= T(1)) {
@@ -306,23 +328,26 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     if (LOG && nacc % B != 0) store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
   }
   if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)
-    // zero chunks after each lane's last one, chunk row by chunk row across
-    // the wavefront (hb is all zero here except for lanes that still hold a
-    // partial chunk, which start one chunk later)
+    // the zero chunks from each lane's first chunk past its last step up to
+    // its lowest zeroed row, chunk row by chunk row across the wavefront
     const int Tn = pr.n_chunks;
     const int mine = live ? (nacc + B - 1) / B : Tn;
-    int tmin = mine;
+    const int upto = live ? zl : Tn;
+    int tmin = mine, tmax = upto;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const int o = __shfl_xor(tmin, off, 64);
+      const int u = __shfl_xor(tmax, off, 64);
       tmin = o < tmin ? o : tmin;
+      tmax = u > tmax ? u : tmax;
     }
     tmin = __builtin_amdgcn_readfirstlane(tmin);
+    tmax = __builtin_amdgcn_readfirstlane(tmax);
     T zb[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) zb[b] = T(0);
-    for (int t = tmin; t < Tn; ++t)
-      if (t >= mine) store_chunk(H + ((int64_t)t * n + i) * B, zb);
+    for (int t = tmin; t < tmax; ++t)
+      if (t >= mine && t < upto) store_chunk(H + ((int64_t)t * n + i) * B, zb);
   }
 }
 
