@@ -595,3 +595,36 @@ def test_deferred_padding(da, orc, wid, n):
     da.mesh_pad(prob, m2)
     torch.cuda.synchronize()
     assert torch.equal(m1.h, m2.h)
+
+
+@pytest.mark.parametrize("wid,n,max_steps", [(1, 1000, 40), (1, 777, 33), (3, 1000, 96),
+                                             (4, 300, 10000)])
+def test_inline_padding(da, wid, n, max_steps):
+    """Logs short enough that the zero rows written during the integration
+    reach the rows the trajectories still fill, with some trajectories running
+    out of steps: the inline-padded log equals a deferred record padded
+    afterwards (so every real chunk written after a zero row replaced it), and
+    holds nonzero step sizes up to each step count and zeros after it."""
+    w = W.WORKLOADS[wid]
+    prob = w.problem().replace(max_steps=max_steps)
+    _print(f"case: inline padding, workload {wid}, n={n}, max_steps={max_steps}")
+    inp = W.make_inputs(wid, n)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    m1, ys1 = da.record(prob, u0, p)
+    m2 = da.empty_mesh(prob, n, u0.dtype, u0.device)
+    m2.h.fill_(float("nan"))
+    m2, ys2 = da.record(prob, u0, p, mesh=m2, defer_pad=True)
+    da.mesh_pad(prob, m2)
+    torch.cuda.synchronize()
+    assert torch.equal(m1.h, m2.h)
+    assert torch.equal(m1.n_steps, m2.n_steps) and torch.equal(m1.status, m2.status)
+    assert torch.equal(torch.nan_to_num(ys1, nan=7.0), torch.nan_to_num(ys2, nan=7.0))
+    st = m1.status.cpu().numpy()
+    ns = m1.n_steps.cpu().numpy()
+    assert np.any(st == 1) and np.any(st == 0), "want lanes that run out of steps and lanes that finish"
+    B = m1.h.shape[2]
+    h = m1.h.cpu().numpy().transpose(1, 0, 2).reshape(n, -1)[:, :max_steps]  # [n, max_steps]
+    k = np.arange(max_steps)[None, :]
+    assert np.all(h[k < ns[:, None]] != 0)
+    assert np.all(h[k >= ns[:, None]] == 0)
+    assert np.all(m1.h.cpu().numpy().transpose(1, 0, 2).reshape(n, -1)[:, max_steps:] == 0)
