@@ -164,16 +164,21 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
 }
 
 #ifndef __HIPCC_RTC__
+// Directions per lane: SENS_G, or one for systems of eight or more
+// components, whose d x d factors with two tangents each would not fit the
+// registers.
+template <class M> constexpr int sens_group() { return M::D >= 8 ? 1 : SENS_G; }
+
 // Launch: one lane per trajectory, the directions in groups of G on the
 // second grid dimension.
 template <class T, class M, bool DENSE>
 hipError_t replay_sens_d(const ReplayArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK),
-                  (unsigned)((a.q_count + SENS_G - 1) / SENS_G));
+  constexpr int G = sens_group<M>();
+  const dim3 grid((unsigned)((a.n + BLOCK - 1) / BLOCK), (unsigned)((a.q_count + G - 1) / G));
   if (a.h_rows)
-    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, true, DENSE>), grid, BLOCK, 0, s, a);
+    hipLaunchKernelGGL((k_replay_sens<T, M, G, true, DENSE>), grid, BLOCK, 0, s, a);
   else
-    hipLaunchKernelGGL((k_replay_sens<T, M, SENS_G, false, DENSE>), grid, BLOCK, 0, s, a);
+    hipLaunchKernelGGL((k_replay_sens<T, M, G, false, DENSE>), grid, BLOCK, 0, s, a);
   return hipGetLastError();
 }
 
