@@ -46,8 +46,8 @@ MAX_SAVES = 128
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_pad",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
-           "da_replay_sens", "da_replay_sens_dirs", "da_rhs_register", "da_rhs_release",
-           "da_last_error", "da_version")
+           "da_replay_sens", "da_replay_sens_dirs", "da_rhs_register", "da_rhs_register_stencil",
+           "da_rhs_release", "da_last_error", "da_version")
 
 
 class DadjError(RuntimeError):
@@ -82,6 +82,12 @@ class _RhsDef(ctypes.Structure):
                 ("method", ctypes.c_int32), ("f_body", ctypes.c_char_p)]
 
 
+class _RhsStencilDef(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("n_params", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("method", ctypes.c_int32), ("n_offsets", ctypes.c_int32),
+                ("offsets", ctypes.POINTER(ctypes.c_int32)), ("f_body", ctypes.c_char_p)]
+
+
 class _Loss(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("aux", ctypes.c_void_p), ("scale", ctypes.c_double)]
 
@@ -112,11 +118,13 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_sens_dirs.argtypes = [P, i64, vp, vp, M, i32, i32, ctypes.POINTER(_Loss), vp,
                                         vp, vp, vp]
     lib.da_rhs_register.argtypes = [ctypes.POINTER(_RhsDef), ctypes.POINTER(ctypes.c_int32)]
+    lib.da_rhs_register_stencil.argtypes = [ctypes.POINTER(_RhsStencilDef),
+                                            ctypes.POINTER(ctypes.c_int32)]
     lib.da_rhs_release.argtypes = [i32]
     lib.da_last_error.restype = ctypes.c_char_p
     for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps", "da_mesh_pad",
                  "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_replay_sens_dirs",
-                 "da_rhs_register",
+                 "da_rhs_register", "da_rhs_register_stencil",
                  "da_rhs_release", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -151,6 +159,21 @@ def register_rhs(f_body: str, dim: int, n_params: int, dtype=torch.float64,
     rid = ctypes.c_int32(0)
     d = _RhsDef(dim, n_params, _dtype_code(dtype), method, f_body.encode())
     _check(_lib.da_rhs_register(ctypes.byref(d), ctypes.byref(rid)))
+    return int(rid.value)
+
+
+def register_rhs_stencil(f_body: str, dim: int, n_params: int, offsets, dtype=torch.float64,
+                         method: int = 0) -> int:
+    """Compile the wavefront kernels for a cyclic-stencil right-hand side of
+    dimension up to 64: component i of f is the C++ body of
+    ``template <class T, class Y> T f(const Y &y, const T *p)`` with y(o) the
+    component i + o (mod dim) for each o in `offsets` (see
+    da_rhs_register_stencil in include/dadj.h).  Returns the rhs identifier."""
+    offs = (ctypes.c_int32 * len(offsets))(*[int(o) for o in offsets])
+    rid = ctypes.c_int32(0)
+    d = _RhsStencilDef(dim, n_params, _dtype_code(dtype), method, len(offsets),
+                       ctypes.cast(offs, ctypes.POINTER(ctypes.c_int32)), f_body.encode())
+    _check(_lib.da_rhs_register_stencil(ctypes.byref(d), ctypes.byref(rid)))
     return int(rid.value)
 
 

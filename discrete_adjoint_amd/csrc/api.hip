@@ -46,6 +46,14 @@ bool shape_ok(int rhs, int d, int P) {
 
 size_t dsize(int dtype) { return dtype == DA_F64 ? 8 : 4; }
 
+// Values per stored state in the replay-gradient workspace: a full
+// wavefront row for the wavefront kernels (Lorenz-96 and registered
+// stencils), else the dimension.
+int ws_row_of(int rhs, int dim) {
+  if (rhs >= DA_RHS_USER_BASE) return dadj::rtc_is_stencil(rhs) ? 64 : dim;
+  return dadj::ws_row(rhs, dim);
+}
+
 // Checkpoint interval of the reverse sweep when the caller leaves it to the
 // library.
 int default_checkpoint(const da_problem &pb) {
@@ -77,7 +85,7 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
                   pb->n_params);
     if (pb->rhs == DA_RHS_LORENZ96 && rosenbrock)
       return fail(DA_EUNSUPPORTED,
-                  "the Rosenbrock methods are available for systems of dimension <= 3 only");
+                  "the Rosenbrock methods do not take Lorenz-96");
     if (pb->rhs == DA_RHS_KINETICS8 && !rosenbrock)
       return fail(DA_EUNSUPPORTED, "the kinetics system takes the Rosenbrock methods only");
     if (pb->rhs == DA_RHS_LORENZ96 && pb->method == DA_RKF78)
@@ -210,6 +218,29 @@ int da_rhs_register(const da_rhs_def *def, int32_t *rhs_id) {
   if (!def->f_body) return fail(DA_EINVAL, "f_body is NULL");
   std::string msg;
   const int rc = dadj::rtc_register(*def, rhs_id, msg);
+  if (rc) return fail(rc, "%s", msg.c_str());
+  return ok();
+}
+
+int da_rhs_register_stencil(const da_rhs_stencil_def *def, int32_t *rhs_id) {
+  if (!def || !rhs_id) return fail(DA_EINVAL, "def and rhs_id must not be NULL");
+  if (def->dim < 2 || def->dim > 64) return fail(DA_EINVAL, "dim must be in [2, 64]");
+  if (def->n_params < 1 || def->n_params > 16)
+    return fail(DA_EINVAL, "n_params must be in [1, 16]");
+  if (def->dtype != DA_F64 && def->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", def->dtype);
+  if (def->method != DA_TSIT5 && def->method != DA_DOPRI5)
+    return fail(DA_EUNSUPPORTED, "registered right-hand sides run the explicit methods");
+  if (def->n_offsets < 1 || def->n_offsets > 7 || !def->offsets)
+    return fail(DA_EINVAL, "need 1 to 7 offsets");
+  for (int i = 0; i < def->n_offsets; ++i) {
+    const int o = def->offsets[i];
+    if (o < -3 || o > 3) return fail(DA_EINVAL, "offset %d outside [-3, 3]", o);
+    for (int j = 0; j < i; ++j)
+      if (def->offsets[j] == o) return fail(DA_EINVAL, "offset %d given twice", o);
+  }
+  if (!def->f_body) return fail(DA_EINVAL, "f_body is NULL");
+  std::string msg;
+  const int rc = dadj::rtc_register_stencil(*def, rhs_id, msg);
   if (rc) return fail(rc, "%s", msg.c_str());
   return ok();
 }
@@ -369,7 +400,7 @@ size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n
   const int ck = resolved_checkpoint(*prob);
   if (ck <= 0 || ck > 8) return 0;
   return (size_t)n * (size_t)((max_n_steps + ck - 1) / ck) *
-         (size_t)dadj::ws_row(prob->rhs, prob->dim) * dsize(prob->dtype);
+         (size_t)ws_row_of(prob->rhs, prob->dim) * dsize(prob->dtype);
 }
 
 int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
@@ -394,7 +425,7 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
   if (n > 0 && (!u0 || !p)) return fail(DA_EINVAL, "u0 and p must not be NULL");
   if (n == 0) return ok();
   const size_t per_lane = (size_t)((max_n_steps + pr.checkpoint - 1) / pr.checkpoint) *
-                          dadj::ws_row(pr.rhs, pr.dim) * dsize(pr.dtype);
+                          ws_row_of(pr.rhs, pr.dim) * dsize(pr.dtype);
   int64_t C = n;
   if (per_lane > 0) {
     if (!workspace) return fail(DA_EWORKSPACE, "workspace is NULL");

@@ -113,6 +113,8 @@ hipError_t launch_max_steps(int64_t n, const int32_t *nsteps, int32_t *dev_out, 
 
 // Right-hand sides compiled at run time (rtc.hip)
 int rtc_register(const da_rhs_def &def, int32_t *id, std::string &err);
+int rtc_register_stencil(const da_rhs_stencil_def &def, int32_t *id, std::string &err);
+bool rtc_is_stencil(int32_t rhs);  // a registered stencil (wavefront kernels)
 int rtc_release(int32_t id, std::string &err);
 int rtc_check(const da_problem &pb, std::string &err);
 std::string rtc_take_error();  // message of the last failed lazy compilation on this thread

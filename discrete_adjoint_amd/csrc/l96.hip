@@ -68,10 +68,10 @@ hipError_t wreplay_grad_t(const ReplayArgs &a, hipStream_t s) {
   return dense ? wreplay_grad_d<T, M, true>(a, s) : wreplay_grad_d<T, M, false>(a, s);
 }
 
-// Sensitivities: 4 tangent directions per lane, ceil(q_count / 4) direction
-// groups on the second grid dimension; a single direction (such as F alone)
-// takes one per lane.
-constexpr int WSENS_G = 4;
+// Sensitivities: WSENS_G tangent directions per lane, ceil(q_count /
+// WSENS_G) direction groups on the second grid dimension; a single direction
+// (such as F alone) takes one per lane.
+using wave::WSENS_G;
 template <class T, class M, bool FULL, bool DENSE>
 hipError_t wreplay_sens_f(const ReplayArgs &a, hipStream_t s) {
   if (a.q_count == 1) {

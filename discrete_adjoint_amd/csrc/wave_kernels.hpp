@@ -18,14 +18,20 @@
 // the accepted step that holds them, per component (lane_kernels.hpp gives
 // the interpolant); whether a step holds a save is the same for all lanes.
 //
-// A method M provides, per lane (component) with a Nbr context for the
-// neighbours: fwd(x, F, h), attempt(x, F, h, k0, xnew, err) and
-// adj(x, F, h, lam, gF) (gF accumulates this lane's share of dL/dF).  At
-// d = 64 (FULL) the neighbours are DPP wavefront rotations; otherwise
-// cross-lane reads (ds_bpermute).
+// A method M provides, per lane (component) with the right-hand side's
+// neighbour context: fwd(x, F, h), attempt(x, F, h, k0, xnew, err) and
+// adj(x, F, h, lam, gF), where F holds the trajectory's P parameters and gF
+// accumulates this lane's share of dL/dF.  A right-hand side Rhs provides P,
+// its neighbour context Nb<FULL>, f(x, F, nb) for this lane's component, and
+// the vector-Jacobian products vjp_y(x, F, v, nb) (this lane's component of
+// J^T v), vjp_p_acc(x, F, v, nb, g) (g += this lane's terms of J_p^T v) and
+// vjp(x, F, v, nb, g) (both).  At d = 64 (FULL) the neighbours are DPP
+// wavefront rotations; otherwise cross-lane reads (ds_bpermute).
 #pragma once
 
+#ifndef __HIPCC_RTC__
 #include <math.h>
+#endif
 
 #include "dadj_device.hpp"
 #include "dadj_internal.hpp"
@@ -35,6 +41,13 @@ namespace dadj {
 namespace wave {
 
 constexpr int WAVES = 4;  // trajectories (wavefronts) per workgroup
+constexpr int WSENS_G = 4;  // tangent directions per lane of the sensitivity kernel
+
+// The parameters of one trajectory (the same in every lane), as reals or as
+// tangent numbers.
+template <class V, int P> struct WPar {
+  V v[P];
+};
 
 // ---------------------------------------------------------------------------
 // wavefront helpers
@@ -143,13 +156,15 @@ template <bool FULL> struct Nbr {
 // (rows c-1, c, c+1, c+2 of column c, in that order); df_c/dF = 1.
 // ---------------------------------------------------------------------------
 struct L96 {
-  template <class T, class NB>
-  __device__ static __forceinline__ T f(T x, T F, const NB &nb) {
+  static constexpr int P = 1;
+  template <bool FULL> using Nb = Nbr<FULL>;
+  template <class T, class PV, class NB>
+  __device__ static __forceinline__ T f(T x, const PV &F, const NB &nb) {
     const T xp1 = nb.up1(x), xm1 = nb.dn1(x), xm2 = nb.dn2(x, xm1);
-    return mac(xp1 - xm2, xm1, -x) + F;
+    return mac(xp1 - xm2, xm1, -x) + F.v[0];
   }
-  template <class T, class NB>
-  __device__ static __forceinline__ T vjp_y(T x, T v, const NB &nb) {
+  template <class T, class PV, class NB>
+  __device__ static __forceinline__ T vjp_y(T x, const PV &, T v, const NB &nb) {
     const T xp1 = nb.up1(x), xp2 = nb.up2(x, xp1), xm1 = nb.dn1(x), xm2 = nb.dn2(x, xm1);
     const T vm1 = nb.dn1(v), vp1 = nb.up1(v), vp2 = nb.up2(v, vp1);
     T s = xm2 * vm1;
@@ -157,6 +172,16 @@ struct L96 {
     s = mac(xp2 - xm1, vp1, s);
     s = mac(-xp1, vp2, s);
     return s;
+  }
+  template <class T, class PV, class GV, class NB>
+  __device__ static __forceinline__ void vjp_p_acc(T, const PV &, T v, const NB &, GV &g) {
+    g.v[0] = g.v[0] + v;
+  }
+  template <class T, class PV, class GV, class NB>
+  __device__ static __forceinline__ T vjp(T x, const PV &F, T v, const NB &nb, GV &g) {
+    const T w = vjp_y(x, F, v, nb);
+    vjp_p_acc(x, F, v, nb, g);
+    return w;
   }
 };
 
@@ -182,8 +207,9 @@ __device__ __forceinline__ T wstage(T y, const T (&K)[7], H h) {
 
 template <class Tab, class Rhs, int I, int LAST, bool LASTK, class T>
 struct WStages {
-  template <class H, class NB>
-  __device__ static __forceinline__ void run(T y, T F, H h, const NB &nb, T (&Y)[7], T (&K)[7]) {
+  template <class PV, class H, class NB>
+  __device__ static __forceinline__ void run(T y, const PV &F, H h, const NB &nb, T (&Y)[7],
+                                             T (&K)[7]) {
     Y[I] = wstage<Tab, I>(y, K, h);
     if (I < LAST || LASTK) K[I] = Rhs::f(Y[I], F, nb);
     WStages<Tab, Rhs, I + 1, LAST, LASTK, T>::run(y, F, h, nb, Y, K);
@@ -191,8 +217,8 @@ struct WStages {
 };
 template <class Tab, class Rhs, int LAST, bool LASTK, class T>
 struct WStages<Tab, Rhs, LAST + 1, LAST, LASTK, T> {
-  template <class H, class NB>
-  __device__ static __forceinline__ void run(T, T, H, const NB &, T (&)[7], T (&)[7]) {}
+  template <class PV, class H, class NB>
+  __device__ static __forceinline__ void run(T, const PV &, H, const NB &, T (&)[7], T (&)[7]) {}
 };
 
 template <class Tab, class R>
@@ -201,8 +227,9 @@ struct WErk {
   static constexpr int order = Tab::order, err_order = Tab::err_order;
 
   // trial step from x with K[0] = f(x) given; returns the 5th-order value
-  template <class T, class NB>
-  __device__ static __forceinline__ T attempt(T x, T F, T h, const NB &nb, T (&K)[7], T &err) {
+  template <class T, class PV, class NB>
+  __device__ static __forceinline__ T attempt(T x, const PV &F, T h, const NB &nb, T (&K)[7],
+                                              T &err) {
     T Y[7];
     WStages<Tab, Rhs, 1, 6, true, T>::run(x, F, h, nb, Y, K);
     T acc = T(0);
@@ -219,8 +246,8 @@ struct WErk {
   }
 
   // T: a real, or the tangent numbers of the sensitivity kernel
-  template <class T, class H, class NB>
-  __device__ static __forceinline__ T fwd(T x, T F, H h, const NB &nb) {
+  template <class T, class PV, class H, class NB>
+  __device__ static __forceinline__ T fwd(T x, const PV &F, H h, const NB &nb) {
     T Y[7], K[7];
     K[0] = Rhs::f(x, F, nb);
     WStages<Tab, Rhs, 1, 6, false, T>::run(x, F, h, nb, Y, K);
@@ -228,9 +255,10 @@ struct WErk {
   }
 
   // Reverse of fwd at x = x_k: lam (dL/dx_{k+1} -> dL/dx_k); gF += this
-  // component's share of dL/dF (the sum of its stage cotangents).
-  template <class T, class NB>
-  __device__ static __forceinline__ void adj(T x, T F, T h, const NB &nb, T &lam, T &gF) {
+  // component's share of dL/dF (its terms of J_p^T kbar at every stage).
+  template <class T, class PV, class GV, class NB>
+  __device__ static __forceinline__ void adj(T x, const PV &F, T h, const NB &nb, T &lam,
+                                             GV &gF) {
     T Y[7], Wv[7];
     {
       T K[7];
@@ -254,8 +282,7 @@ struct WErk {
         }
       }
       const T kb = h * acc;
-      Wv[i] = Rhs::vjp_y(Y[i], kb, nb);
-      gF = gF + kb;
+      Wv[i] = Rhs::vjp(Y[i], F, kb, nb, gF);
     }
     T s = lam;
 #pragma unroll
@@ -268,8 +295,8 @@ struct WErk {
 // size h from x0 to x1, h (H11 f(x1) + H10 f(x0)) + (H01 x1 + H00 x0).  V is
 // a real or a tangent number (whose weights and step carry no tangent), T
 // the real type of th and h.
-template <class Rhs, class V, class T, class NB>
-__device__ __forceinline__ V wdense_value(T th, T h, V x0, V x1, V F, const NB &nb) {
+template <class Rhs, class V, class T, class PV, class NB>
+__device__ __forceinline__ V wdense_value(T th, T h, V x0, V x1, const PV &F, const NB &nb) {
   const HermiteW<T> w = hermite_w(th);
   const V w00(w.h00), w01(w.h01), w10(w.h10), w11(w.h11), hv(h);
   const V f0 = Rhs::f(x0, F, nb), f1 = Rhs::f(x1, F, nb);
@@ -328,7 +355,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   const ProbArgs &pr = a.pr;
   const int d = pr.dim;
   const bool on = c < d;
-  Nbr<FULL> nb;
+  typename Rhs::template Nb<FULL> nb;
   nb.init(c, d);
   const int S = pr.S;
   const bool has_saves = pr.n_save > 0;
@@ -341,7 +368,13 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   T *theta = (T *)a.theta;
 
   T x = on ? ((const T *)a.u0)[c * n + i] : T(0);
-  const T F = uniform(((const T *)a.p)[i]);
+  WPar<T, Rhs::P> F;
+  bool finp = true;
+#pragma unroll
+  for (int q = 0; q < Rhs::P; ++q) {
+    F.v[q] = uniform(((const T *)a.p)[(int64_t)q * n + i]);
+    finp = finp && finite(F.v[q]);
+  }
   for (int s = 0; s < S; ++s) {
     if (a.sidx && c == 0) a.sidx[s * n + i] = -1;
     if (theta && c == 0) theta[s * n + i] = nanv<T>();
@@ -349,7 +382,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   }
   int nacc = 0, natt = 0, st = LANE_OK;
   T hb = T(0);  // lane b: step b of the current chunk
-  const bool fin = wave_all(finite(x)) && finite(F);
+  const bool fin = wave_all(finite(x)) && finp;
   if (!fin) {
     st = LANE_NONFINITE;
   } else {
@@ -501,7 +534,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
   const int c = w.c;
   const int d = a.pr.dim;
   const bool on = c < d;
-  Nbr<FULL> nb;
+  typename Rhs::template Nb<FULL> nb;
   nb.init(c, d);
   const int S = a.pr.S;
   T *ysave = (T *)a.y_save;
@@ -513,7 +546,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_fwd(ReplayArgs a) {
   WSteps<T> src;
   src.init(a, j, tr);
   T x = on ? ((const T *)a.u0)[c * n + tr] : T(0);
-  const T F = uniform(((const T *)a.p)[tr]);
+  WPar<T, Rhs::P> F;
+#pragma unroll
+  for (int q = 0; q < Rhs::P; ++q) F.v[q] = uniform(((const T *)a.p)[(int64_t)q * n + tr]);
   for (int q = 0; q < S; ++q) {
     const int ix = a.sidx[q * n + tr];
     if (on && (!ok || ix < 0 || ix > N)) ysave[(q * d + c) * n + tr] = nanv<T>();
@@ -553,7 +588,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   const int c = w.c;
   const int d = a.pr.dim;
   const bool on = c < d;
-  Nbr<FULL> nb;
+  typename Rhs::template Nb<FULL> nb;
   nb.init(c, d);
   const int64_t C = a.ws_lanes;
   const int S = a.pr.S;
@@ -569,7 +604,9 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   WSteps<T> src;
   src.init(a, j, tr);
   T x = on ? ((const T *)a.u0)[c * n + tr] : T(0);
-  const T F = uniform(((const T *)a.p)[tr]);
+  WPar<T, Rhs::P> F;
+#pragma unroll
+  for (int q = 0; q < Rhs::P; ++q) F.v[q] = uniform(((const T *)a.p)[(int64_t)q * n + tr]);
 
   // ---- forward replay, checkpoints, loss terms ----
   const T *theta = (const T *)a.theta;
@@ -608,7 +645,10 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
   }
 
   // ---- loss and seeds at the final state ----
-  T lam = T(0), gF = T(0);
+  T lam = T(0);
+  WPar<T, Rhs::P> gF;
+#pragma unroll
+  for (int q = 0; q < Rhs::P; ++q) gF.v[q] = T(0);
   if (!saves) {
     ss = on ? x * x : T(0);
     lam = on ? T(2.0 * a.scale) * x : T(0);
@@ -660,11 +700,11 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
             }
             const HermiteW<T> w = hermite_w(th);
             const T v1 = (hs[b] * w.h11) * sb, v0 = (hs[b] * w.h10) * sb;
-            const T w1 = Rhs::vjp_y(xhi, v1, nb), w0 = Rhs::vjp_y(xs[b], v0, nb);
+            const T w1 = Rhs::vjp_y(xhi, F, v1, nb), w0 = Rhs::vjp_y(xs[b], F, v0, nb);
             lam = mac(w.h01, sb, lam) + w1;
             mu = mac(w.h00, sb, mu) + w0;
-            gF = gF + v1;
-            gF = gF + v0;
+            Rhs::vjp_p_acc(xhi, F, v1, nb, gF);
+            Rhs::vjp_p_acc(xs[b], F, v0, nb, gF);
             has_mu = true;
             --sh;
             hidx = sh >= 0 ? uniform(a.sidx[(int64_t)sh * n + tr]) : -1;
@@ -683,18 +723,19 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_grad(ReplayArgs a) {
 
   // ---- outputs ----
   const T L = wave_sum(on ? ss : T(0));
-  const T G = wave_sum(on ? gF : T(0));
   if (on && a.gu0) ((T *)a.gu0)[c * n + tr] = ok ? lam : nanv<T>();
-  if (c == 0) {
-    if (a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * L : nanv<T>();
-    if (a.gp) ((T *)a.gp)[tr] = ok ? G : nanv<T>();
+  if (c == 0 && a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * L : nanv<T>();
+#pragma unroll
+  for (int q = 0; q < Rhs::P; ++q) {
+    const T G = wave_sum(on ? gF.v[q] : T(0));
+    if (c == 0 && a.gp) ((T *)a.gp)[(int64_t)q * n + tr] = ok ? G : nanv<T>();
   }
 }
 
 // ---------------------------------------------------------------------------
 // Forward-mode sensitivities (mesh held fixed): lane c carries component c of
 // the state with G tangent directions; the directions q_begin .. q_begin +
-// q_count - 1 of the d + 1 (u0 components, then F) are split into groups of G
+// q_count - 1 of the d + P (u0 components, then parameters) are split into groups of G
 // on the second grid dimension.  Outputs as the lane-per-trajectory kernel:
 // sens[S][d][q_count][n], and with a loss its value and gradient by the chain
 // rule.  The gradient and loss sums run in
@@ -714,7 +755,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
   const int d = a.pr.dim;
   const int q0 = a.q_begin + (int)blockIdx.y * G, qe = a.q_begin + a.q_count, Qo = a.q_count;
   const bool on = c < d;
-  Nbr<FULL> nb;
+  typename Rhs::template Nb<FULL> nb;
   nb.init(c, d);
   const int S = a.pr.S;
   const int lk = a.loss_kind;
@@ -729,12 +770,15 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
   WSteps<T> src;
   src.init(a, j, tr);
   DT x(on ? ((const T *)a.u0)[c * n + tr] : T(0));
-  DT F(uniform(((const T *)a.p)[tr]));
+  WPar<DT, Rhs::P> F;
 #pragma unroll
-  for (int m = 0; m < G; ++m) {
-    x.d[m] = (on && q0 + m == c) ? T(1) : T(0);
-    F.d[m] = (q0 + m == d) ? T(1) : T(0);
+  for (int q = 0; q < Rhs::P; ++q) {
+    F.v[q] = DT(uniform(((const T *)a.p)[(int64_t)q * n + tr]));
+#pragma unroll
+    for (int m = 0; m < G; ++m) F.v[q].d[m] = (q0 + m == d + q) ? T(1) : T(0);
   }
+#pragma unroll
+  for (int m = 0; m < G; ++m) x.d[m] = (on && q0 + m == c) ? T(1) : T(0);
   if (sens && on)
     for (int s = 0; s < S; ++s) {
       const int ix = a.sidx[s * n + tr];
@@ -807,7 +851,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wreplay_sens(ReplayArgs a) {
       } else if (q < d) {
         if (a.gu0) ((T *)a.gu0)[(int64_t)q * n + tr] = v;
       } else {
-        if (a.gp) ((T *)a.gp)[tr] = v;
+        if (a.gp) ((T *)a.gp)[(int64_t)(q - d) * n + tr] = v;
       }
     }
     if (blockIdx.y == 0 && a.loss_out) ((T *)a.loss_out)[tr] = ok ? T(a.scale) * ss : nanv<T>();

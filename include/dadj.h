@@ -389,6 +389,40 @@ typedef struct {
 } da_rhs_def;
 
 int da_rhs_register(const da_rhs_def *def, int32_t *rhs_id);
+
+/* A right-hand side compiled at run time for systems of dimension up to 64
+ * ("GRADSOLVE", evolve.pub review, FAQ: registered right-hand sides up to
+ * state dimension 64 run in the fused kernels) whose component i depends on
+ * the components i + o (mod dim) for a few fixed offsets o: a cyclic
+ * stencil, such as Lorenz-96 (offsets -2, -1, 0, 1).  They run on the
+ * wavefront-per-trajectory kernels (lane i of a wavefront holds component i;
+ * the neighbours move between lanes).  The caller gives component i of f as
+ * C++ statements, the body of
+ *     template <class T, class Y> T f(const Y &y, const T *p)
+ * returning dy_i, where y(o) is the component i + o (mod dim) for a declared
+ * offset o (NaN for any other), y.i is i and y.d is dim, and p holds the
+ * n_params parameters; T is a real or a tangent number, with the operations
+ * and functions listed for da_rhs_register.  The vector-Jacobian products
+ * come from one forward pass on tangent numbers with a direction per offset
+ * and per parameter: (J^T v)_i adds, in the declared offset order, the
+ * products v_j df_j/dy(o) of the components j = i - o; J_p^T v sums each
+ * component's terms over the wavefront.  Methods DA_TSIT5 and DA_DOPRI5,
+ * FP64 and FP32, dense output, every kernel (record, forward solve, replay,
+ * replay-gradient with the Lorenz-96 workspace of 64 values per stored
+ * state, sensitivities).  Registration, errors, identifiers and release as
+ * for da_rhs_register; DA_EINVAL for a dim outside 2..64, n_params outside
+ * 1..16, or offsets that are not distinct values in [-3, 3]. */
+typedef struct {
+  int32_t dim;             /* 2..64 */
+  int32_t n_params;        /* 1..16 */
+  int32_t dtype;           /* da_dtype */
+  int32_t method;          /* DA_TSIT5 or DA_DOPRI5 */
+  int32_t n_offsets;       /* 1..7 */
+  const int32_t *offsets;  /* host [n_offsets]: distinct, each in [-3, 3] */
+  const char *f_body;      /* host string, NUL-terminated */
+} da_rhs_stencil_def;
+
+int da_rhs_register_stencil(const da_rhs_stencil_def *def, int32_t *rhs_id);
 int da_rhs_release(int32_t rhs_id);
 
 /* Message of the last non-zero return on this thread ("" if none). */

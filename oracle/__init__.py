@@ -131,6 +131,43 @@ ORC_USER_F(orc_user_dp32, DP32)
 ORC_USER_F(orc_user_df32, DF32)
 }
 '''
+# A cyclic stencil (the form of the wavefront kernels' registered right-hand
+# sides): component i of f from the components i + o (mod d) of the declared
+# offsets o; the whole vector is those components in order.
+_STENCIL_PLUGIN = r'''
+#include <limits>
+#include "user_types.h"
+namespace user {
+constexpr int SD = %d, NOFF = %d;
+constexpr int OFF[NOFF] = {%s};
+template <class V> struct SY {
+  const V *yv;
+  int i, d;
+  V operator()(int o) const {
+    for (int s = 0; s < NOFF; ++s)
+      if (OFF[s] == o) return yv[((i + o) %% d + d) %% d];
+    return V(std::numeric_limits<double>::quiet_NaN());
+  }
+};
+struct Stencil {
+  template <class T, class Y> static T g(const Y &y, const T *p) {
+#line 1 "rhs"
+%s
+  }
+};
+struct Src {
+  template <class T> static void f(const T *y, const T *p, T *dy) {
+    for (int i = 0; i < SD; ++i) {
+      SY<T> acc;
+      acc.yv = y;
+      acc.i = i;
+      acc.d = SD;
+      dy[i] = Stencil::g<T>(acc, p);
+    }
+  }
+};
+}  // namespace user
+''' + _PLUGIN[_PLUGIN.index("typedef user::UDual<double, false> DP64;"):]
 _plugins = {}
 
 
@@ -140,7 +177,23 @@ def set_user_rhs(f_body: str, dim: int, n_params: int) -> None:
     source the HIP library compiles) the oracle's right-hand side for every
     problem whose rhs code is >= 1024.  It is built with g++ into a plugin
     (cached by source) and evaluated on reals and dual numbers."""
-    key = hashlib.sha256(f"{dim} {n_params}\n{f_body}".encode()).hexdigest()[:16]
+    _set_plugin(_PLUGIN % f_body, dim, n_params)
+
+
+def set_user_stencil(f_body: str, dim: int, n_params: int, offsets) -> None:
+    """As set_user_rhs for a cyclic stencil (the source of
+    da_rhs_register_stencil): the body of
+    ``template <class T, class Y> T f(const Y &y, const T *p)`` gives
+    component i from y(o) = y[(i + o) mod dim] for the declared offsets o
+    (NaN for others); the oracle's f is the vector of those components, and
+    its derivatives are the generic ones of any registered right-hand side."""
+    offs = [int(o) for o in offsets]
+    src = _STENCIL_PLUGIN % (dim, len(offs), ", ".join(map(str, offs)), f_body)
+    _set_plugin(src, dim, n_params)
+
+
+def _set_plugin(source: str, dim: int, n_params: int) -> None:
+    key = hashlib.sha256(f"{dim} {n_params}\n{source}".encode()).hexdigest()[:16]
     if key not in _plugins:
         d = os.path.join(tempfile.gettempdir(), "dadj_oracle_rhs")
         os.makedirs(d, exist_ok=True)
@@ -148,7 +201,7 @@ def set_user_rhs(f_body: str, dim: int, n_params: int) -> None:
         lib = os.path.join(d, f"rhs_{key}.so")
         if not os.path.exists(lib):
             with open(src, "w") as f:
-                f.write(_PLUGIN % f_body)
+                f.write(source)
             tmp = lib + f".{os.getpid()}.tmp"
             subprocess.run(["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math",
                             "-fPIC", "-shared", "-I", _HERE, "-o", tmp, src], check=True)

@@ -199,6 +199,33 @@ def test_rhs_registration_checks(da):
     assert lib.da_rhs_release(5) == -1
 
 
+def test_stencil_registration_checks(da):
+    """Argument checks of da_rhs_register_stencil (dimension 2..64, 1..16
+    parameters, 1..7 distinct offsets in [-3, 3], an explicit method), and a
+    source with an error refused with the compiler's message; no GPU needed."""
+    lib = da.library()
+    rid = ctypes.c_int32(-1)
+    assert lib.da_rhs_register_stencil(None, ctypes.byref(rid)) == -1
+    good = "return p[0] * (y(1) - y(-1));"
+    for dim, npar, dt, meth, offs, body, code in [
+            (1, 1, 0, 0, (-1, 1), good, -1), (65, 1, 0, 0, (-1, 1), good, -1),
+            (8, 0, 0, 0, (-1, 1), good, -1), (8, 17, 0, 0, (-1, 1), good, -1),
+            (8, 1, 2, 0, (-1, 1), good, -1), (8, 1, 0, 2, (-1, 1), good, -2),
+            (8, 1, 0, 0, (), good, -1), (8, 1, 0, 0, (-4, 1), good, -1),
+            (8, 1, 0, 0, (-1, 4), good, -1), (8, 1, 0, 0, (1, -1, 1), good, -1),
+            (8, 1, 0, 0, tuple(range(-3, 4)) + (0,), good, -1),
+            (8, 1, 0, 0, (-1, 1), None, -1)]:
+        arr = (ctypes.c_int32 * max(1, len(offs)))(*offs)
+        d = da._RhsStencilDef(dim, npar, dt, meth, len(offs),
+                              ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                              None if body is None else body.encode())
+        assert lib.da_rhs_register_stencil(ctypes.byref(d), ctypes.byref(rid)) == code, (
+            dim, npar, dt, meth, offs)
+    with pytest.raises(da.DadjError) as e:
+        da.register_rhs_stencil("return y(0) +;", 8, 1, (0,))
+    assert e.value.code == -1 and "expected expression" in str(e.value)
+
+
 @pytest.mark.parametrize("ck", [3, 5, 16, -1])
 def test_bad_checkpoint_rejected(da, ck):
     prob = W.WORKLOADS[1].problem(checkpoint=ck)
