@@ -112,6 +112,10 @@ LORENZ63_SOURCE = """
     dy[1] = y[0] * (p[1] - y[2]) - y[1];
     dy[2] = y[0] * y[1] - p[2] * y[2];
 """
+# Lorenz-96 written as a cyclic stencil for the wavefront kernels
+# (--rhs-source on workload 5): component i from y(o) = y[(i + o) mod d].
+LORENZ96_STENCIL = "return (y(1) - y(-2)) * y(-1) - y(0) + p[0];"
+LORENZ96_OFFSETS = (-2, -1, 0, 1)
 # Sources of the gradient kernel of each method family.
 KERNEL_SOURCES = {
     "erk": ["lane_kernels.hpp", "erk_method.hpp", "erk.hip", "erk_grad_f64_dopri5.hip",
@@ -261,8 +265,9 @@ def main():
     ap.add_argument("--cpu-lanes", type=int, default=262144)
     ap.add_argument("--copy-probe", action="store_true")
     ap.add_argument("--rhs-source", action="store_true",
-                    help="Lorenz-63 workloads: run the system as a right-hand side compiled at "
-                         "run time from source instead of the built-in one")
+                    help="Lorenz-63 and Lorenz-96 workloads: run the system as a right-hand "
+                         "side compiled at run time from source (Lorenz-96: as a cyclic "
+                         "stencil) instead of the built-in one")
     ap.add_argument("--method", choices=["rodas3", "rkf78"], default=None,
                     help="rodas3: workload 4 (Robertson) with the third-order Rosenbrock "
                          "method instead of ROS2; rkf78: workload 2 (Lorenz-63) with "
@@ -296,11 +301,15 @@ def main():
         w = dataclasses.replace(w, method=W.RKF78, name=w.name.replace("dopri5", "rkf78"))
     prob = w.problem(checkpoint=args.checkpoint, dense=int(args.dense))
     if args.rhs_source:
-        if w.rhs != W.LORENZ63:
-            sys.exit("--rhs-source is available for the Lorenz-63 workloads")
+        tdt = torch.float64 if w.dtype == "f64" else torch.float32
         t_reg = time.perf_counter()
-        rid = da.register_rhs(LORENZ63_SOURCE, 3, 3, torch.float64 if w.dtype == "f64"
-                              else torch.float32, w.method)
+        if w.rhs == W.LORENZ63:
+            rid = da.register_rhs(LORENZ63_SOURCE, 3, 3, tdt, w.method)
+        elif w.rhs == W.LORENZ96:
+            rid = da.register_rhs_stencil(LORENZ96_STENCIL, w.dim, 1, LORENZ96_OFFSETS, tdt,
+                                          w.method)
+        else:
+            sys.exit("--rhs-source is available for the Lorenz-63 and Lorenz-96 workloads")
         t_reg = time.perf_counter() - t_reg
         prob = prob.replace(rhs=rid)
     n = w.n
