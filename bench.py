@@ -30,6 +30,9 @@ Printed on one JSON line, besides the driver's fields:
                 sources match it, else null;
   record_log    bytes of the zero-padded step log the record writes, and the
                 rate over the record time;
+  replay_fwd    the fused fixed-step replay alone (saved states, no
+                gradient) on the job's replay order and table, with its
+                algorithmic FLOP rate (the forward part of flop_per_step);
   cpu_baseline  the CPU oracle (plain C++, OpenMP) on a bounded sample of the
                 same workload, as trajectory-gradients/s of the same job.
 
@@ -91,6 +94,16 @@ def sens_flop_per_step(method: str, rhs: str, dim: int):
     if (method, rhs) == ("tsit5", "lorenz96"):
         return 72 * dim + (dim + 1) * 84 * dim
     return {("dopri5", "lorenz63"): 1590, ("tsit5", "lorenz63"): 1632}.get((method, rhs))
+
+
+def fwd_flop_per_step(method: str, rhs: str, dim: int):
+    """The forward part of flop_per_step: one replay step (the da_replay_fwd
+    kernel), from the same counts."""
+    if rhs == "lorenz96" and method == "tsit5":
+        return 72 * dim
+    return {("dopri5", "lorenz63"): 186, ("tsit5", "lorenz63"): 192,
+            ("ros2", "robertson"): 118, ("rodas3", "robertson"): 234,
+            ("rodas3", "kinetics8"): 1227, ("rkf78", "lorenz63"): 403}.get((method, rhs))
 
 
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
@@ -392,6 +405,9 @@ def main():
     sens_p_ms = timed(lambda: da.replay_sens_dirs(prob, u0, p, state["call"].mesh, prob.dim,
                                                   prob.n_params, w.loss, aux=aux, scale=scale,
                                                   with_sens=False))
+    # the fused fixed-step replay alone (da_replay_fwd: saved states, no
+    # gradient) on the same replay order and table
+    fwd_ms = timed(lambda: da.replay_fwd(prob, u0, p, state["call"].mesh))
     # forward-only adaptive solve of the same ensemble (outside the job)
     solve_ms = []
     for r in range(3):
@@ -410,6 +426,7 @@ def main():
     mname, rname = W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs]
     flop_step = flop_per_step(mname, rname, w.dim)
     sens_flop = sens_flop_per_step(mname, rname, w.dim)
+    fwd_flop = fwd_flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
     traffic = None if args.rhs_source else read_traffic(w.name, kernel_family(mname, rname),
@@ -462,6 +479,14 @@ def main():
             "ms": float(np.mean(sens_p_ms)),
             "directions": prob.n_params,
             "trajectory_gradients_per_s": n / (float(np.mean(sens_p_ms)) * 1e-3)},
+        "replay_fwd": {
+            "ms": float(np.mean(fwd_ms)),
+            "trajectory_replays_per_s": n / (float(np.mean(fwd_ms)) * 1e-3),
+            "flop_per_step": fwd_flop,
+            "achieved_tflops": None if fwd_flop is None
+            else fwd_flop * total_steps / (float(np.mean(fwd_ms)) * 1e-3) / 1e12,
+            "frac": None if fwd_flop is None
+            else fwd_flop * total_steps / (float(np.mean(fwd_ms)) * 1e-3) / 1e12 / peak},
         "solve_fwd": {"ms": float(np.mean(solve_ms)),
                       "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],
