@@ -28,6 +28,10 @@
  *    (1980) 19-26.
  *  - ROS2: J. G. Verwer, E. J. Spee, J. G. Blom, W. Hundsdorfer, SIAM J. Sci.
  *    Comput. 20 (1999) 1456-1480, with gamma = 1 + 1/sqrt(2).
+ *  - Rodas3: A. Sandu et al., Atmos. Environ. 31 (1997) 3459-3472.
+ *  - Fehlberg 7(8): E. Fehlberg, NASA TR R-287 (1968).
+ *  - A fourth-order Rosenbrock method: L. F. Shampine, ACM TOMS 8 (1982)
+ *    93-113 (its parameter set of the four-stage scheme).
  *  - Starting step: Hairer, Norsett, Wanner, Solving ODEs I, section II.4.
  *
  * Rounding modes.  Every sum of products is evaluated left to right as a
@@ -56,7 +60,7 @@ constexpr int MAXD = 64;  // largest state dimension handled
 constexpr int MAXR = 8;   // largest state dimension of the Rosenbrock methods
 constexpr int MAXP = 16;  // largest parameter count
 
-enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3, M_RKF78 = 4 };
+enum { M_TSIT5 = 0, M_DOPRI5 = 1, M_ROS2 = 2, M_RODAS3 = 3, M_RKF78 = 4, M_ROS4 = 5 };
 enum { R_LINEAR = 0, R_LORENZ63 = 1, R_ROBERTSON = 2, R_LORENZ96 = 3, R_KINETICS8 = 4 };
 constexpr int R_USER = 1024;  /* kinds from here: the caller's right-hand side */
 enum { S_OK = 0, S_MAX_STEPS = 1, S_DT_UNDERFLOW = 2, S_NONFINITE = 3,
@@ -1066,6 +1070,39 @@ RosTab make_rodas3() {
 }
 const RosTab RODAS3 = make_rodas3();
 
+/* A fourth-order Rosenbrock method with an embedded third-order solution
+ * (Shampine 1982, "Implementation of Rosenbrock methods", ACM TOMS 8:93;
+ * four stages, A-stable, R(-inf) = 1/3), in the same transformed form:
+ * gamma = 1/2; a_21 = 2, a_31 = a_41 = 48/25, a_32 = a_42 = 6/25 (the fourth
+ * stage is evaluated at the third stage's point); c_21 = -8, c_31 = 372/25,
+ * c_32 = 12/5, c_41 = -112/125, c_42 = -54/125, c_43 = -2/5; m = (19/9,
+ * 1/2, 25/108, 125/108); e = (17/54, 7/36, 0, 125/108), the difference of
+ * the fourth- and third-order solutions.  A test checks order 4 (linear and
+ * nonlinear) and order 3 for the embedded solution. */
+RosTab make_ros4() {
+  RosTab t = {};
+  t.s = 4;
+  t.gamma = 0.5;
+  t.a[1][0] = 2.0;
+  t.a[2][0] = 48.0 / 25.0; t.a[2][1] = 6.0 / 25.0;
+  t.a[3][0] = 48.0 / 25.0; t.a[3][1] = 6.0 / 25.0;
+  t.c[1][0] = -8.0;
+  t.c[2][0] = 372.0 / 25.0; t.c[2][1] = 12.0 / 5.0;
+  t.c[3][0] = -112.0 / 125.0; t.c[3][1] = -54.0 / 125.0; t.c[3][2] = -2.0 / 5.0;
+  for (int i = 0; i < 4; ++i)
+    for (int j = 0; j < 4; ++j) t.gc[i][j] = t.gamma * t.c[i][j];
+  t.m[0] = 19.0 / 9.0; t.m[1] = 0.5; t.m[2] = 25.0 / 108.0; t.m[3] = 125.0 / 108.0;
+  t.e[0] = 17.0 / 54.0; t.e[1] = 7.0 / 36.0; t.e[2] = 0.0; t.e[3] = 125.0 / 108.0;
+  t.order = 4; t.err_order = 3;
+  return t;
+}
+const RosTab ROS4 = make_ros4();
+
+/* The four-stage Rosenbrock table of a method (null for the others). */
+const RosTab *ros_tab(int method) {
+  return method == M_RODAS3 ? &RODAS3 : method == M_ROS4 ? &ROS4 : nullptr;
+}
+
 template <class T>
 struct RodasStep {
   T J[MAXR * MAXR], LU[MAXR * MAXR];
@@ -1204,9 +1241,9 @@ Opts make_opts(const orc_problem *P) {
 
 int validate(const orc_problem *P) {
   if (!P) return E_INVAL;
-  if (P->method < 0 || P->method > 4) return E_INVAL;
+  if (P->method < 0 || P->method > 5) return E_INVAL;
   if (!rhs_shape_ok(P->rhs, P->dim, P->n_params)) return E_INVAL;
-  const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
+  const bool ros = P->method == M_ROS2 || ros_tab(P->method);
   /* the Rosenbrock methods need the explicit Jacobian of the built-in systems */
   if (ros && (P->dim > MAXR || P->rhs == R_LORENZ96)) return E_UNSUPPORTED;
   if (P->dense != 0 && P->dense != 1) return E_INVAL;
@@ -1357,12 +1394,13 @@ template <class T, bool F>
 void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
                  const LaneOut<T> &out) {
   const int d = P->dim, kind = P->rhs;
-  const bool ros = P->method == M_ROS2 || P->method == M_RODAS3;
+  const RosTab *rt = ros_tab(P->method);
+  const bool ros = P->method == M_ROS2 || rt;
   const Tableau &tb = (P->method == M_DOPRI5) ? DOPRI5 : TSIT5;
   const bool rk78 = P->method == M_RKF78;
-  const int qerr = P->method == M_ROS2 ? 1 : P->method == M_RODAS3 ? RODAS3.err_order
+  const int qerr = P->method == M_ROS2 ? 1 : rt ? rt->err_order
                  : rk78 ? RK78_ERR_ORDER : tb.err_order;
-  const int qord = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order
+  const int qord = P->method == M_ROS2 ? 2 : rt ? rt->order
                  : rk78 ? RK78_ORDER : tb.order;
   const T atol = T(P->atol), rtol = T(P->rtol);
   const T expo = T(-1.0) / T(qerr + 1);
@@ -1404,9 +1442,9 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
         Ros2Step<T> rs;
         ros2_forward<T, F>(kind, d, y, p, hs, rs);
         for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
-      } else if (P->method == M_RODAS3) {
+      } else if (rt) {
         RodasStep<T> rs;
-        rodas_forward<T, F>(RODAS3, kind, d, y, p, hs, rs);
+        rodas_forward<T, F>(*rt, kind, d, y, p, hs, rs);
         for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
       } else if (rk78) {
         rk78_attempt<T, F>(kind, d, y, p, hs, ynew, err);
@@ -1479,7 +1517,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
 template <class T, bool F>
 inline void one_step(const orc_problem *P, T *y, const T *p, T h) {
   if (P->method == M_ROS2) ros2_step<T, F>(P->rhs, P->dim, y, p, h);
-  else if (P->method == M_RODAS3) rodas_step<T, F>(RODAS3, P->rhs, P->dim, y, p, h);
+  else if (ros_tab(P->method)) rodas_step<T, F>(*ros_tab(P->method), P->rhs, P->dim, y, p, h);
   else if (P->method == M_RKF78) rk78_step<T, F>(P->rhs, P->dim, y, p, h);
   else erk_step<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p, h);
 }
@@ -1488,8 +1526,8 @@ template <class T, bool F>
 inline void one_step_adjoint(const orc_problem *P, const T *y, const T *p, T h, T *lam, T *gp,
                              T *gpc = nullptr) {
   if (P->method == M_ROS2) ros2_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
-  else if (P->method == M_RODAS3)
-    rodas_step_adjoint<T, F>(RODAS3, P->rhs, P->dim, y, p, h, lam, gp);
+  else if (ros_tab(P->method))
+    rodas_step_adjoint<T, F>(*ros_tab(P->method), P->rhs, P->dim, y, p, h, lam, gp);
   else if (P->method == M_RKF78)
     rk78_step_adjoint<T, F>(P->rhs, P->dim, y, p, h, lam, gp);
   else erk_step_adjoint<T, F>(P->method == M_DOPRI5 ? DOPRI5 : TSIT5, P->rhs, P->dim, y, p,
@@ -1699,9 +1737,9 @@ T mesh_max_err_lane(const orc_problem *P, const T *u0, const T *p, const T *h, i
       Ros2Step<T> rs;
       ros2_forward<T, F>(kind, d, y, p, h[k], rs);
       for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
-    } else if (P->method == M_RODAS3) {
+    } else if (ros_tab(P->method)) {
       RodasStep<T> rs;
-      rodas_forward<T, F>(RODAS3, kind, d, y, p, h[k], rs);
+      rodas_forward<T, F>(*ros_tab(P->method), kind, d, y, p, h[k], rs);
       for (int c = 0; c < d; ++c) { ynew[c] = rs.ynew[c]; err[c] = rs.err[c]; }
     } else if (P->method == M_RKF78) {
       rk78_attempt<T, F>(kind, d, y, p, h[k], ynew, err);
@@ -2139,7 +2177,7 @@ int orc_initial_step_f64(const orc_problem *P, const double *y0, const double *p
   if (rc) return rc;
   double f0[MAXD];
   rhs_f<double, false>(P->rhs, P->dim, y0, p, f0);
-  const int q = P->method == M_ROS2 ? 2 : P->method == M_RODAS3 ? RODAS3.order
+  const int q = P->method == M_ROS2 ? 2 : ros_tab(P->method) ? ros_tab(P->method)->order
               : P->method == M_RKF78 ? RK78_ORDER : 5;
   *h0 = initial_step<double, false>(P->rhs, P->dim, y0, f0, p, P->atol, P->rtol, q);
   return E_OK;

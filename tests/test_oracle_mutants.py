@@ -85,6 +85,10 @@ MUTANTS = {
                                        "      for (int l = i + 1; l <= 9; ++l) {\n        if (RK78.a[l][i] == 0.0) continue;"),
     "kinetics8_partial_of_wrong_reactant": ("cols[0] = r.a; vals[0] = k * y[r.b];",
                                             "cols[0] = r.a; vals[0] = k * y[r.a];"),
+    "ros4_digit": ("t.c[3][0] = -112.0 / 125.0;", "t.c[3][0] = -111.0 / 125.0;"),
+    "ros4_fourth_stage_at_wrong_point": ("t.a[3][0] = 48.0 / 25.0; t.a[3][1] = 6.0 / 25.0;",
+                                         "t.a[3][0] = 48.0 / 25.0; t.a[3][2] = 6.0 / 25.0;"),
+    "ros4_error_weight": ("t.e[0] = 17.0 / 54.0;", "t.e[0] = 19.0 / 54.0;"),
     "kinetics8_contraction_flipped": (
         "auto M = [&](int b) { return Jb[k.dst * 8 + b] - Jb[k.src * 8 + b]; };",
         "auto M = [&](int b) { return Jb[k.src * 8 + b] - Jb[k.dst * 8 + b]; };"),
@@ -101,6 +105,7 @@ def _battery():
         out.append((pins.test_linear_decay_closed_form, dict(method=m, fused=False)))
         out.append((pins.test_lorenz63_origin_linearisation, dict(method=m)))
     out.append((pins.test_rodas3_order_stability_and_estimator, {}))
+    out.append((pins.test_ros4_order_stability_and_estimator, {}))
     out += [(pins.test_rkf78_tableau_is_fehlberg, {}),
             (pins.test_linear_decay_closed_form, dict(method=W.RKF78, fused=False))]
     for m in (W.TSIT5, W.DOPRI5):

@@ -299,12 +299,43 @@ def _R_rodas3(z):
     return _rodas3_matrix(np.array([[z]]))[0, 0]
 
 
+# Shampine's fourth-order Rosenbrock parameters (ACM TOMS 8, 1982), typed here
+# from the publication as fractions, independently of the oracle's doubles:
+# transformed form with gamma = 1/2, stage points a, stage couplings c,
+# weights m and error weights e (fourth minus third order).
+ROS4_A = {(1, 0): Fr(2), (2, 0): Fr(48, 25), (2, 1): Fr(6, 25),
+          (3, 0): Fr(48, 25), (3, 1): Fr(6, 25)}
+ROS4_C = {(1, 0): Fr(-8), (2, 0): Fr(372, 25), (2, 1): Fr(12, 5),
+          (3, 0): Fr(-112, 125), (3, 1): Fr(-54, 125), (3, 2): Fr(-2, 5)}
+ROS4_M = [Fr(19, 9), Fr(1, 2), Fr(25, 108), Fr(125, 108)]
+ROS4_E = [Fr(17, 54), Fr(7, 36), Fr(0), Fr(125, 108)]
+
+
+def _ros4_matrix(Z, weights=None):
+    """One step of the four-stage scheme on y' = A y with Z = h A:
+    u_i = (I - Z/2)^-1 (Z/2 Y_i + sum_j c_ij/2 u_j), Y_i = I + sum_j a_ij u_j,
+    result I + sum_i w_i u_i (w = m by default)."""
+    w = ROS4_M if weights is None else weights
+    I = np.eye(Z.shape[0], dtype=complex if np.iscomplexobj(Z) else float)
+    Wi = np.linalg.inv(I - 0.5 * Z)
+    u = []
+    for i in range(4):
+        Y = I + sum(float(ROS4_A.get((i, j), 0)) * u[j] for j in range(i))
+        u.append(Wi @ (0.5 * Z @ Y + sum(0.5 * float(ROS4_C.get((i, j), 0)) * u[j]
+                                         for j in range(i))))
+    return I + sum(float(w[i]) * u[i] for i in range(4))
+
+
+def _R_ros4(z):
+    return _ros4_matrix(np.array([[z]]))[0, 0]
+
+
 def _complex_step(fn, z):
     eps = 1e-30
     return (fn(z + 1j * eps)).imag / eps
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78, W.ROS4])
 @pytest.mark.parametrize("fused", [False, True])
 def test_linear_decay_closed_form(orc, method, fused):
     """y' = -k y on an arbitrary mesh: y_N = y0 prod R(-k h_n); exact derivative
@@ -322,6 +353,8 @@ def test_linear_decay_closed_form(orc, method, fused):
         R = lambda z: _R_ros2(g, z)
     elif method == W.RODAS3:
         R = _R_rodas3
+    elif method == W.ROS4:
+        R = _R_ros4
     else:
         coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
         R = lambda z: _R_erk(coef, z)
@@ -392,6 +425,58 @@ def test_rodas3_order_stability_and_estimator(orc):
     assert 7.0 < steps[1] / steps[0] < 14.0, steps                # 1000^(1/3) = 10
 
 
+def test_ros4_order_stability_and_estimator(orc):
+    """What identifies a correct fourth-order Rosenbrock step with a
+    third-order companion, from the mathematics alone:
+    - the oracle's one-step map of y' = z y is the closed form of the
+      fractions above;
+    - R(z) - e^z = O(z^5) with a nonzero z^5 term (order exactly 4), and the
+      companion m - e gives O(z^4) (order 3);
+    - A-stable (|R| <= 1 on the imaginary axis and the negative real axis)
+      with R(-inf) = 1/3;
+    - global order 4 on Lorenz-63 with fixed steps (nonlinear: every order
+      condition, not only the linear ones), against SciPy's DOP853;
+    - the recorded step count grows as tol^(-1/4) (a third-order estimate)."""
+    from scipy.integrate import solve_ivp
+    prob = W.Problem(W.LINEAR, 1, 1, W.ROS4, 0.0, 1.0, 1e-6, 1e-6, 1)
+    one = {"h": np.ones((1, 1)), "n_steps": np.array([1]), "save_idx": np.array([[1]]),
+           "status": np.zeros(1)}
+    for z in (-50.0, -1.3, -0.01, 0.2, 1.5):
+        _, y1 = orc.replay(prob, np.ones((1, 1)), np.array([[z]]), one)
+        assert y1[0, 0] == pytest.approx(_R_ros4(z), rel=1e-14)
+    e1, e2 = _R_ros4(0.04) - math.exp(0.04), _R_ros4(0.02) - math.exp(0.02)
+    assert 28.0 < e1 / e2 < 36.0 and abs(e2) > 1e-13            # C z^5, C != 0
+    emb = [mi - ei for mi, ei in zip(ROS4_M, ROS4_E)]
+    Re = lambda z: _ros4_matrix(np.array([[z]]), emb)[0, 0]
+    c1, c2 = Re(0.04) - math.exp(0.04), Re(0.02) - math.exp(0.02)
+    assert 14.0 < c1 / c2 < 18.0                                 # companion: C z^4
+    assert _R_ros4(-1e12) == pytest.approx(1.0 / 3.0, abs=1e-9)
+    assert max(abs(_R_ros4(1j * y)) for y in np.logspace(-3, 6, 400)) <= 1.0 + 1e-12
+    assert max(abs(_R_ros4(-x)) for x in np.logspace(-3, 12, 400)) <= 1.0 + 1e-12
+    u0 = np.array([[1.0, 1.0, 1.0]])
+    pv = np.array([[10.0, 28.0, 8.0 / 3.0]])
+    ref = solve_ivp(lambda t, y: [10 * (y[1] - y[0]), y[0] * (28 - y[2]) - y[1],
+                                  y[0] * y[1] - 8 / 3 * y[2]], (0, 0.5), u0[0],
+                    method="DOP853", rtol=1e-13, atol=1e-13).y[:, -1]
+    errs = []
+    for N in (50, 100, 200, 400):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.ROS4, 0.0, 0.5, 1e-6, 1e-6, N)
+        mesh = {"h": np.full((1, N), 0.5 / N), "n_steps": np.array([N]),
+                "save_idx": np.array([[N]]), "status": np.zeros(1)}
+        _, yN = orc.replay(pr, u0, pv, mesh)
+        errs.append(np.abs(yN[0] - ref).max())
+    orders = [math.log2(errs[i] / errs[i + 1]) for i in range(3)]
+    assert all(3.8 < o < 4.3 for o in orders), orders
+    inp = W.make_inputs(1, 8)
+    steps = []
+    for tol in (1e-6, 1e-9):
+        pr = W.Problem(W.LORENZ63, 3, 3, W.ROS4, 0.0, 1.0, tol, tol, 100000)
+        m = orc.record(pr, inp["u0"], inp["p"])
+        assert np.all(m["status"] == 0)
+        steps.append(m["n_steps"].mean())
+    assert 4.2 < steps[1] / steps[0] < 7.5, steps               # 1000^(1/4) = 5.6
+
+
 def _matrix_R(method, orc, Z):
     I = np.eye(Z.shape[0])
     if method == W.ROS2:
@@ -400,6 +485,8 @@ def _matrix_R(method, orc, Z):
         return I + 2 * Z @ Wm + 0.5 * Z @ Z @ Wm @ Wm - Z @ Wm @ Wm
     if method == W.RODAS3:
         return _rodas3_matrix(Z)
+    if method == W.ROS4:
+        return _ros4_matrix(Z)
     coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
     out = np.zeros_like(Z)
     Zp = I.copy()
@@ -409,7 +496,7 @@ def _matrix_R(method, orc, Z):
     return out
 
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78, W.ROS4])
 def test_lorenz63_origin_linearisation(orc, method):
     """At the origin Lorenz-63 is a fixed point; the replay's Jacobian is the
     product of R(h_n A) with A = [[-s, s, 0], [r, -1, 0], [0, 0, -b]].  A
@@ -482,7 +569,7 @@ def test_lorenz96_fixed_point(orc, method):
 # Invariants
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3])
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3, W.ROS4])
 def test_robertson_ros2_conservation(orc, method):
     """1^T f = 0 for Robertson, so 1^T J = 0 and a Rosenbrock step (ROS2,
     Rodas3: every stage is W^-1 of a combination of f values and earlier
@@ -519,7 +606,7 @@ def _kin8_f(y, p):
     return S @ w
 
 
-@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3])
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3, W.ROS4])
 def test_kinetics8_conservation_and_reference(orc, method):
     """The eight-species cycle: every reaction moves one unit, so both
     Rosenbrock methods keep sum y fixed and the gradient of sum y_N is 1 for
@@ -583,7 +670,7 @@ def test_save_times_are_mesh_points(orc):
 def test_global_error_tracks_tolerance(orc):
     """y' = -y on [0, 1]: the recorded solve's error at t=1 stays below the
     tolerance scale and shrinks as the tolerance does."""
-    for method in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78):
+    for method in (W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78, W.ROS4):
         errs = []
         for tol in (1e-4, 1e-6, 1e-8):
             prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 1.0, tol, tol, 100000)
@@ -713,6 +800,16 @@ def _cases():
     out.append(("lorenz63_rodas3_saves", W.WORKLOADS[1].problem(
         method=W.RODAS3, max_steps=4096, save_times=(0.3, 0.7, 1.0)), inp["u0"], inp["p"],
         W.MSE_SAVE, np.random.default_rng(4).standard_normal((6, 3, 3))))
+    inp = W.make_inputs(4, 4)
+    out.append(("robertson_ros4", W.WORKLOADS[4].problem(t1=300.0, method=W.ROS4),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
+    inp = W.make_inputs(1, 6)
+    out.append(("lorenz63_ros4_saves", W.WORKLOADS[1].problem(
+        method=W.ROS4, max_steps=4096, save_times=(0.3, 0.7, 1.0)), inp["u0"], inp["p"],
+        W.MSE_SAVE, np.random.default_rng(8).standard_normal((6, 3, 3))))
+    inp = W.make_inputs(6, 3)
+    out.append(("kinetics8_ros4", W.WORKLOADS[6].problem(t1=5.0, method=W.ROS4),
+                inp["u0"], inp["p"], W.SUMSQ_FINAL, None))
     return out
 
 
@@ -836,7 +933,7 @@ def test_fp32_oracle_tracks_fp64(orc):
 # Forward-mode sensitivities (tangents carried through the replay)
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78])
+@pytest.mark.parametrize("method", [W.TSIT5, W.DOPRI5, W.ROS2, W.RODAS3, W.RKF78, W.ROS4])
 @pytest.mark.parametrize("fused", [False, True])
 def test_sensitivities_linear_closed_form(orc, method, fused):
     """y' = p y on an arbitrary mesh: dy_N/dy0 = prod R(p h_n) and
@@ -851,6 +948,8 @@ def test_sensitivities_linear_closed_form(orc, method, fused):
         R = lambda z: _R_ros2(g, z)
     elif method == W.RODAS3:
         R = _R_rodas3
+    elif method == W.ROS4:
+        R = _R_ros4
     else:
         coef = _stability_poly(_rk78_float() if method == W.RKF78 else orc.tableau(method))
         R = lambda z: _R_erk(coef, z)

@@ -44,12 +44,12 @@ from typing import Optional
 import numpy as np
 
 # Integer codes shared by convention (not by code) with both implementations.
-TSIT5, DOPRI5, ROS2, RODAS3, RKF78 = 0, 1, 2, 3, 4
+TSIT5, DOPRI5, ROS2, RODAS3, RKF78, ROS4 = 0, 1, 2, 3, 4, 5
 LINEAR, LORENZ63, ROBERTSON, LORENZ96, KINETICS8 = 0, 1, 2, 3, 4
 SUMSQ_FINAL, MSE_SAVE, COTANGENT = 0, 1, 2
 
 METHOD_NAMES = {TSIT5: "tsit5", DOPRI5: "dopri5", ROS2: "ros2", RODAS3: "rodas3",
-                RKF78: "rkf78"}
+                RKF78: "rkf78", ROS4: "ros4"}
 RHS_NAMES = {LINEAR: "linear", LORENZ63: "lorenz63", ROBERTSON: "robertson",
              LORENZ96: "lorenz96", KINETICS8: "kinetics8"}
 
