@@ -69,6 +69,11 @@ PEAK_TFLOPS = {"f64": 78.6, "f32": 157.3}
 #    48, solution 18 and error 3) = 234; adjoint (stage cotangents 60, four
 #    transposed solves 60, Wbar 63, fbar 12, J^T v and J_p^T v at four stages
 #    132, ybar sums 12, Jbar 9 and dJ contraction 29) = 377; total 611.
+#  Fourth-order Rosenbrock (Shampine's parameters) / Robertson: forward as
+#    Rodas3 but five nonzero a_ij (stage sums Y_i 30), four nonzero m_i
+#    (solution 24) and three nonzero e_i (error 15) = 264; adjoint as Rodas3
+#    but stage cotangents over eleven nonzero a_li and gamma c_li terms
+#    with four m_i (78) = 395; total 659.
 #  Fehlberg 7(8) / Lorenz-63: forward (11 right-hand sides of 8 flop = 88,
 #    stage sums over the nonzero a_ij and the solution over the 7 nonzero
 #    b_j: 3 x 105 = 315) = 403; adjoint (stage cotangents 3 x 94 = 282, J^T v
@@ -103,13 +108,15 @@ def fwd_flop_per_step(method: str, rhs: str, dim: int):
         return 72 * dim
     return {("dopri5", "lorenz63"): 186, ("tsit5", "lorenz63"): 192,
             ("ros2", "robertson"): 118, ("rodas3", "robertson"): 234,
-            ("rodas3", "kinetics8"): 1227, ("rkf78", "lorenz63"): 403}.get((method, rhs))
+            ("rodas3", "kinetics8"): 1227, ("rkf78", "lorenz63"): 403,
+            ("ros4", "robertson"): 264}.get((method, rhs))
 
 
 def flop_per_step(method: str, rhs: str, dim: int) -> int:
     table = {("dopri5", "lorenz63"): 444, ("tsit5", "lorenz63"): 456,
              ("ros2", "robertson"): 306, ("rodas3", "robertson"): 611,
-             ("rodas3", "kinetics8"): 2784, ("rkf78", "lorenz63"): 938}
+             ("rodas3", "kinetics8"): 2784, ("rkf78", "lorenz63"): 938,
+             ("ros4", "robertson"): 659}
     if rhs == "lorenz96" and method == "tsit5":
         return 168 * dim
     return table[(method, rhs)]
@@ -136,8 +143,10 @@ KERNEL_SOURCES = {
             "dadj_device.hpp", "dadj_internal.hpp"],
     "ros2": ["lane_kernels.hpp", "rosenbrock.hpp", "ros2.hip", "dadj_device.hpp",
              "dadj_internal.hpp"],
-    "rodas3": ["lane_kernels.hpp", "rosenbrock.hpp", "rodas3.hip", "dadj_device.hpp",
-               "dadj_internal.hpp"],
+    "rodas3": ["lane_kernels.hpp", "rosenbrock.hpp", "rosenbrock4.hpp", "rodas3.hip",
+               "dadj_device.hpp", "dadj_internal.hpp"],
+    "ros4": ["lane_kernels.hpp", "rosenbrock.hpp", "rosenbrock4.hpp", "ros4.hip",
+             "dadj_device.hpp", "dadj_internal.hpp"],
     "rkf78": ["lane_kernels.hpp", "rkf78.hip", "dadj_device.hpp", "dadj_internal.hpp"],
     "wave": ["wave_kernels.hpp", "l96.hip", "dadj_device.hpp", "dadj_internal.hpp"],
 }
@@ -146,7 +155,7 @@ KERNEL_SOURCES = {
 def kernel_family(method: str, rhs: str) -> str:
     if rhs == "lorenz96":
         return "wave"
-    return method if method in ("ros2", "rodas3", "rkf78") else "erk"
+    return method if method in ("ros2", "rodas3", "ros4", "rkf78") else "erk"
 
 
 # The host-side part of the internal header (launcher declarations and the
@@ -281,10 +290,10 @@ def main():
                     help="Lorenz-63 and Lorenz-96 workloads: run the system as a right-hand "
                          "side compiled at run time from source (Lorenz-96: as a cyclic "
                          "stencil) instead of the built-in one")
-    ap.add_argument("--method", choices=["rodas3", "rkf78"], default=None,
-                    help="rodas3: workload 4 (Robertson) with the third-order Rosenbrock "
-                         "method instead of ROS2; rkf78: workload 2 (Lorenz-63) with "
-                         "Fehlberg 7(8) instead of Dopri5; same tolerances")
+    ap.add_argument("--method", choices=["rodas3", "ros4", "rkf78"], default=None,
+                    help="rodas3 / ros4: workload 4 (Robertson) with the third- / "
+                         "fourth-order Rosenbrock method instead of ROS2; rkf78: workload 2 "
+                         "(Lorenz-63) with Fehlberg 7(8) instead of Dopri5; same tolerances")
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
@@ -304,10 +313,11 @@ def main():
     import workloads as W
 
     w = W.WORKLOADS[args.workload]
-    if args.method == "rodas3":
+    if args.method in ("rodas3", "ros4"):
         if args.workload != 4:
-            sys.exit("--method rodas3 is available for workload 4 (Robertson)")
-        w = dataclasses.replace(w, method=W.RODAS3, name=w.name.replace("ros2", "rodas3"))
+            sys.exit(f"--method {args.method} is available for workload 4 (Robertson)")
+        code = W.RODAS3 if args.method == "rodas3" else W.ROS4
+        w = dataclasses.replace(w, method=code, name=w.name.replace("ros2", args.method))
     elif args.method == "rkf78":
         if args.workload != 2:
             sys.exit("--method rkf78 is available for workload 2 (Lorenz-63)")

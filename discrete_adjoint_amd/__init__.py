@@ -36,7 +36,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DADJ_LIBRARY") or os.path.join(_HERE, "libdadj.so")
 
 DA_F64, DA_F32 = 0, 1
-TSIT5, DOPRI5, ROS2, RODAS3, RKF78 = 0, 1, 2, 3, 4
+TSIT5, DOPRI5, ROS2, RODAS3, RKF78, ROS4 = 0, 1, 2, 3, 4, 5
 LINEAR, LORENZ63, ROBERTSON, LORENZ96 = 0, 1, 2, 3
 SUMSQ_FINAL, MSE_SAVE, COTANGENT = 0, 1, 2
 LANE_OK, LANE_MAX_STEPS, LANE_DT_UNDERFLOW, LANE_NONFINITE, LANE_MAX_ATTEMPTS = range(5)

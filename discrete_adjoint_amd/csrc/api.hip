@@ -70,9 +70,10 @@ int check_problem(const da_problem *pb, int64_t n, dadj::ProbArgs &pr, dadj::Sav
   if (!pb) return fail(DA_EINVAL, "problem is NULL");
   if (n < 0 || n > (int64_t)0x7fffffff) return fail(DA_EINVAL, "n = %lld out of range", (long long)n);
   if (pb->dtype != DA_F64 && pb->dtype != DA_F32) return fail(DA_EINVAL, "bad dtype %d", pb->dtype);
-  if (pb->method < DA_TSIT5 || pb->method > DA_RKF78)
+  if (pb->method < DA_TSIT5 || pb->method > DA_ROS4)
     return fail(DA_EINVAL, "bad method %d", pb->method);
-  const bool rosenbrock = pb->method == DA_ROS2 || pb->method == DA_RODAS3;
+  const bool rosenbrock =
+      pb->method == DA_ROS2 || pb->method == DA_RODAS3 || pb->method == DA_ROS4;
   if (pb->rhs >= DA_RHS_USER_BASE) {
     std::string msg;
     const int rc = dadj::rtc_check(*pb, msg);
@@ -179,6 +180,7 @@ hipError_t launch_record(const dadj::RecordArgs &a, const dadj::SaveTimes &st, h
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_record(a, st, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_record(a, st, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_record(a, st, s);
+  if (a.pr.method == DA_ROS4) return dadj::launch_ros4_record(a, st, s);
   if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_record(a, st, s);
   return dadj::launch_erk_record(a, st, s);
 }
@@ -188,6 +190,7 @@ hipError_t launch_replay_fwd(const dadj::ReplayArgs &a, hipStream_t s) {
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_fwd(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_fwd(a, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_replay_fwd(a, s);
+  if (a.pr.method == DA_ROS4) return dadj::launch_ros4_replay_fwd(a, s);
   if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_replay_fwd(a, s);
   return dadj::launch_erk_replay_fwd(a, s);
 }
@@ -197,6 +200,7 @@ hipError_t launch_replay_grad(const dadj::ReplayArgs &a, hipStream_t s) {
   if (a.pr.rhs == DA_RHS_LORENZ96) return dadj::launch_l96_replay_grad(a, s);
   if (a.pr.method == DA_ROS2) return dadj::launch_ros2_replay_grad(a, s);
   if (a.pr.method == DA_RODAS3) return dadj::launch_rodas3_replay_grad(a, s);
+  if (a.pr.method == DA_ROS4) return dadj::launch_ros4_replay_grad(a, s);
   if (a.pr.method == DA_RKF78) return dadj::launch_rkf78_replay_grad(a, s);
   return dadj::launch_erk_replay_grad(a, s);
 }
@@ -507,6 +511,7 @@ static int replay_sens(const da_problem *prob, int64_t n, const void *u0, const 
                        : pr.rhs == DA_RHS_LORENZ96   ? dadj::launch_l96_replay_sens(a, s)
                        : pr.method == DA_ROS2        ? dadj::launch_ros2_replay_sens(a, s)
                        : pr.method == DA_RODAS3      ? dadj::launch_rodas3_replay_sens(a, s)
+                       : pr.method == DA_ROS4        ? dadj::launch_ros4_replay_sens(a, s)
                        : pr.method == DA_RKF78       ? dadj::launch_rkf78_replay_sens(a, s)
                                                      : dadj::launch_erk_replay_sens(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_sens launch");

@@ -94,6 +94,10 @@ hipError_t launch_rodas3_record(const RecordArgs &a, const SaveTimes &st, hipStr
 hipError_t launch_rodas3_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_rodas3_replay_grad(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_rodas3_replay_sens(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_ros4_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
+hipError_t launch_ros4_replay_fwd(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_ros4_replay_grad(const ReplayArgs &a, hipStream_t s);
+hipError_t launch_ros4_replay_sens(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_rkf78_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s);
 hipError_t launch_rkf78_replay_fwd(const ReplayArgs &a, hipStream_t s);
 hipError_t launch_rkf78_replay_grad(const ReplayArgs &a, hipStream_t s);

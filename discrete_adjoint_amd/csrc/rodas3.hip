@@ -1,227 +1,40 @@
 // Rodas3 (Sandu, Verwer, Blom, Spee, Carmichael and Potra 1997, the
 // Rosenbrock solvers of atmospheric chemistry) for the lane-per-trajectory
 // kernels: a third-order, stiffly accurate, L-stable Rosenbrock method with
-// four stages and an embedded second-order solution, the higher-order stiff
-// integrator beside ROS2 on the record-and-replay path.  Per lane: the d x d
-// Jacobian (d <= 3), W = I - gamma h J with gamma = 1/2, its LU factors with
-// partial pivoting, and per stage
-//   Y_i = y + sum_{j<i} a_ij u_j,
-//   u_i = W^-1 (gamma h f(Y_i) + sum_{j<i} gamma c_ij u_j),
-// then y+ = y + sum m_i u_i and err = u_4.  The published form solves
-// (I / (gamma h) - J) u_i = f(Y_i) + sum_j (c_ij / h) u_j, the same system
-// multiplied by gamma h.  The reverse sweep runs the stages backwards with
-// transposed solves on the same factors and contracts Jbar = -gamma h Wbar
-// with the derivative of J, as for ROS2.
-#include "rosenbrock.hpp"
+// four stages and an embedded second-order solution (err = u_4), the
+// higher-order stiff integrator beside ROS2 on the record-and-replay path.
+#include "rosenbrock4.hpp"
 
 namespace dadj {
 namespace {
 
-constexpr double RODAS3_GAMMA = 0.5;
-constexpr double RODAS3_A[4][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {2, 0, 0, 0}, {2, 0, 1, 0}};
-constexpr double RODAS3_C[4][4] = {
-    {0, 0, 0, 0}, {4, 0, 0, 0}, {1, -1, 0, 0}, {1, -1, -8.0 / 3.0, 0}};
-constexpr double RODAS3_M[4] = {2, 0, 1, 1};
-constexpr double RODAS3_E[4] = {0, 0, 0, 1};
-
-// gamma c_ij, the coefficient of u_j in the right-hand side of stage i
-__device__ __forceinline__ constexpr double rodas3_gc(int i, int j) {
-  return RODAS3_GAMMA * RODAS3_C[i][j];
-}
-
-template <int D, class V> struct Rodas3Step {
-  V J[D * D], LU[D * D], rinv[D];
-  int perm[D];
-  bool swapped;
-  V Y[4][D], u[4][D], ynew[D], err[D];
-};
-
-// One Rodas3 step from y with size h.  Stage sums: Y_i from y adding a_ij u_j
-// for j = 0, 1, ...; the stage right-hand side is the sum of gamma c_ij u_j
-// (a product, then multiply-adds) with gamma h f(Y_i) added last; y+ from y
-// adding m_i u_i in stage order.  V: a real or a tangent number.
-template <class Rhs, class V, class H>
-__device__ __forceinline__ void rodas3_forward(const V (&y)[Rhs::D], const V *p, H h,
-                                               Rodas3Step<Rhs::D, V> &s) {
-  constexpr int D = Rhs::D;
-  Rhs::jac(y, p, s.J);
-  const H gh = H(RODAS3_GAMMA) * h;
-#pragma unroll
-  for (int a = 0; a < D; ++a)
-#pragma unroll
-    for (int b = 0; b < D; ++b)
-      s.LU[a * D + b] = (a == b) ? smac(-gh, s.J[a * D + b], V(1)) : smul(-gh, s.J[a * D + b]);
-  lu_factor<D>(s.LU, s.perm, s.rinv, s.swapped);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      V acc = y[c];
-#pragma unroll
-      for (int j = 0; j < i; ++j)
-        if (RODAS3_A[i][j] != 0.0) acc = cmac(RODAS3_A[i][j], s.u[j][c], acc);
-      s.Y[i][c] = acc;
-    }
-    V f[D], r[D];
-    Rhs::f(s.Y[i], p, f);
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      V acc = V(0);
-      bool first = true;
-#pragma unroll
-      for (int j = 0; j < i; ++j)
-        if (rodas3_gc(i, j) != 0.0) {
-          acc = first ? cmul(rodas3_gc(i, j), s.u[j][c]) : cmac(rodas3_gc(i, j), s.u[j][c], acc);
-          first = false;
-        }
-      r[c] = first ? smul(gh, f[c]) : smac(gh, f[c], acc);
-    }
-    lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, r, s.u[i]);
-  }
-#pragma unroll
-  for (int c = 0; c < D; ++c) {
-    V acc = y[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (RODAS3_M[i] != 0.0) acc = cmac(RODAS3_M[i], s.u[i][c], acc);
-    s.ynew[c] = acc;
-    V e = V(0);
-    bool first = true;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (RODAS3_E[i] != 0.0) {
-        e = first ? cmul(RODAS3_E[i], s.u[i][c]) : cmac(RODAS3_E[i], s.u[i][c], e);
-        first = false;
-      }
-    s.err[c] = e;
-  }
-}
-
-template <class R>
-struct Rodas3 {
-  using Rhs = R;
-  static constexpr int D = R::D;
+struct Rodas3Tab {
+  static constexpr double GAMMA = 0.5;
+  static constexpr double A[4][4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {2, 0, 0, 0}, {2, 0, 1, 0}};
+  static constexpr double C[4][4] = {
+      {0, 0, 0, 0}, {4, 0, 0, 0}, {1, -1, 0, 0}, {1, -1, -8.0 / 3.0, 0}};
+  static constexpr double M[4] = {2, 0, 1, 1};
+  static constexpr double E[4] = {0, 0, 0, 1};
   static constexpr int order = 3, err_order = 2;
-  static constexpr bool dense_output = false;
-  template <class T> struct Cache {};
-
-  template <class T>
-  __device__ static __forceinline__ void begin(const T (&)[D], const T *, const T (&)[D],
-                                               Cache<T> &) {}
-
-  template <class T>
-  __device__ static __forceinline__ void attempt(const T (&y)[D], const T *p, T h, Cache<T> &,
-                                                 T (&ynew)[D], T (&err)[D]) {
-    Rodas3Step<D, T> s;
-    rodas3_forward<Rhs>(y, p, h, s);
-#pragma unroll
-    for (int c = 0; c < D; ++c) {
-      ynew[c] = s.ynew[c];
-      err[c] = s.err[c];
-    }
-  }
-
-  template <class T> __device__ static __forceinline__ void accepted(Cache<T> &) {}
-
-  // V: values, or the tangent numbers of the sensitivity kernel
-  template <class V, class H>
-  __device__ static __forceinline__ void fwd(V (&y)[D], const V *p, H h) {
-    Rodas3Step<D, V> s;
-    rodas3_forward<Rhs>(y, p, h, s);
-#pragma unroll
-    for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
-  }
-
-  // Reverse with the mesh fixed, stages from the last to the first:
-  //   ubar_i = m_i lam + sum_{l>i} (a_li Ybar_l + gamma c_li rbar_l)
-  //            (the m term, then l = i+1, ... with its a term before its c
-  //            term; a product, then multiply-adds)
-  //   rbar_i = W^-T ubar_i, Wbar -= rbar_i u_i^T, fbar_i = gamma h rbar_i,
-  //   Ybar_i = J(Y_i)^T fbar_i, g += J_p(Y_i)^T fbar_i, ybar += Ybar_i;
-  // then Jbar = -gamma h Wbar contracted with the derivative of J at y.
-  template <class T>
-  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
-    Rodas3Step<D, T> s;
-    rodas3_forward<Rhs>(y, p, h, s);
-    const T gh = T(RODAS3_GAMMA) * h;
-    T yb[D], rb[4][D], Yb[4][D], Wb[D * D], Jb[D * D];
-#pragma unroll
-    for (int c = 0; c < D; ++c) yb[c] = lam[c];
-#pragma unroll
-    for (int i = 3; i >= 0; --i) {
-      T ub[D], fb[D];
-#pragma unroll
-      for (int c = 0; c < D; ++c) {
-        T acc = T(0);
-        bool first = true;
-        if (RODAS3_M[i] != 0.0) {
-          acc = cmul(RODAS3_M[i], lam[c]);
-          first = false;
-        }
-#pragma unroll
-        for (int l = i + 1; l < 4; ++l) {
-          if (RODAS3_A[l][i] != 0.0) {
-            acc = first ? cmul(RODAS3_A[l][i], Yb[l][c]) : cmac(RODAS3_A[l][i], Yb[l][c], acc);
-            first = false;
-          }
-          if (rodas3_gc(l, i) != 0.0) {
-            acc = first ? cmul(rodas3_gc(l, i), rb[l][c]) : cmac(rodas3_gc(l, i), rb[l][c], acc);
-            first = false;
-          }
-        }
-        ub[c] = acc;
-      }
-      lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, ub, rb[i]);
-#pragma unroll
-      for (int a = 0; a < D; ++a)
-#pragma unroll
-        for (int b = 0; b < D; ++b)
-          Wb[a * D + b] = (i == 3) ? (-rb[i][a]) * s.u[i][b] : mac(-rb[i][a], s.u[i][b], Wb[a * D + b]);
-#pragma unroll
-      for (int c = 0; c < D; ++c) fb[c] = gh * rb[i][c];
-      Rhs::vjp_y(s.Y[i], p, fb, Yb[i]);
-      Rhs::vjp_p_acc(s.Y[i], p, fb, g);
-#pragma unroll
-      for (int c = 0; c < D; ++c) yb[c] = yb[c] + Yb[i][c];
-    }
-#pragma unroll
-    for (int q = 0; q < D * D; ++q) Jb[q] = (-gh) * Wb[q];
-    Rhs::jac_contract_acc(y, p, Jb, yb, g);
-#pragma unroll
-    for (int c = 0; c < D; ++c) lam[c] = yb[c];
-  }
+  // gamma c_ij, the coefficient of u_j in the right-hand side of stage i
+  __device__ static __forceinline__ constexpr double gc(int i, int j) { return GAMMA * C[i][j]; }
 };
 
-#define DADJ_RODAS3_DISPATCH(FN, ARGS)                                                      \
-  do {                                                                                      \
-    const bool f64 = a.pr.dtype == DA_F64;                                                  \
-    switch (a.pr.rhs) {                                                                     \
-      case DA_RHS_LINEAR:                                                                   \
-        return f64 ? FN<double, Rodas3<Linear>> ARGS : FN<float, Rodas3<Linear>> ARGS;      \
-      case DA_RHS_LORENZ63:                                                                 \
-        return f64 ? FN<double, Rodas3<Lorenz63>> ARGS : FN<float, Rodas3<Lorenz63>> ARGS;  \
-      case DA_RHS_ROBERTSON:                                                                \
-        return f64 ? FN<double, Rodas3<Robertson>> ARGS : FN<float, Rodas3<Robertson>> ARGS; \
-      case DA_RHS_KINETICS8:                                                          \
-        return f64 ? FN<double, Rodas3<Kinetics8>> ARGS : FN<float, Rodas3<Kinetics8>> ARGS; \
-      default:                                                                              \
-        return hipErrorInvalidValue;                                                        \
-    }                                                                                       \
-  } while (0)
+template <class R> struct Rodas3 : Rosenbrock4<Rodas3Tab, R> {};
 
 }  // namespace
 
 hipError_t launch_rodas3_record(const RecordArgs &a, const SaveTimes &st, hipStream_t s) {
-  DADJ_RODAS3_DISPATCH(record_t, (a, st, s));
+  DADJ_ROS4S_DISPATCH(Rodas3, record_t, (a, st, s));
 }
 hipError_t launch_rodas3_replay_fwd(const ReplayArgs &a, hipStream_t s) {
-  DADJ_RODAS3_DISPATCH(replay_fwd_t, (a, s));
+  DADJ_ROS4S_DISPATCH(Rodas3, replay_fwd_t, (a, s));
 }
 hipError_t launch_rodas3_replay_grad(const ReplayArgs &a, hipStream_t s) {
-  DADJ_RODAS3_DISPATCH(replay_grad_t, (a, s));
+  DADJ_ROS4S_DISPATCH(Rodas3, replay_grad_t, (a, s));
 }
 hipError_t launch_rodas3_replay_sens(const ReplayArgs &a, hipStream_t s) {
-  DADJ_RODAS3_DISPATCH(replay_sens_t, (a, s));
+  DADJ_ROS4S_DISPATCH(Rodas3, replay_sens_t, (a, s));
 }
 
 }  // namespace dadj

@@ -73,13 +73,18 @@ typedef enum { DA_F64 = 0, DA_F32 = 1 } da_dtype;
  * (DA_EUNSUPPORTED).  DA_RKF78 is Fehlberg's 7(8) pair (13 stages, the
  * 7th-order solution propagated, its difference to the 8th-order one the
  * error estimate; Fehlberg 1968), the higher-order explicit method for
- * tight tolerances: linear, Lorenz-63 and Robertson, no dense output. */
+ * tight tolerances: linear, Lorenz-63 and Robertson, no dense output.
+ * DA_ROS4 is a fourth-order Rosenbrock method with an embedded third-order
+ * solution (four stages, gamma = 1/2, A-stable, stability function 1/3 at
+ * infinity; Shampine 1982, ACM TOMS 8:93): the same systems and limits as
+ * Rodas3, and one order more for stiff problems at tight tolerances. */
 typedef enum {
   DA_TSIT5 = 0,
   DA_DOPRI5 = 1,
   DA_ROS2 = 2,
   DA_RODAS3 = 3,
-  DA_RKF78 = 4
+  DA_RKF78 = 4,
+  DA_ROS4 = 5
 } da_method;
 
 /* Built-in right-hand sides (dimension d, parameter count P):
@@ -136,7 +141,7 @@ typedef enum {
  * components of err / (atol + rtol max(|y_n|, |y_{n+1}|)); accept iff it is
  * <= 1; next step = used step * clamp(safety E^(-1/(q+1)), fac_min, fac_max)
  * with q the embedded order (4 for the 5(4) pairs, 1 for ROS2, 2 for
- * Rodas3, 7 for Fehlberg 7(8)), no growth
+ * Rodas3, 3 for DA_ROS4, 7 for Fehlberg 7(8)), no growth
  * on the step after a rejection.  Steps are shortened to land exactly on each
  * save time and on t1, or, with dense = 1, on t1 only, each save time then
  * being read from the interpolant of the accepted step that contains it
@@ -178,8 +183,8 @@ typedef struct {
                           t_k < t_s <= t_k + h; th = (t_s - t_k) / h in double,
                           capped at 1, exactly 1 at the step's end.  th is part
                           of the mesh and, like h, carries no derivative.
-                          Explicit methods only (DA_EUNSUPPORTED with ROS2
-                          and Rodas3).  */
+                          Explicit methods only (DA_EUNSUPPORTED with ROS2,
+                          Rodas3 and DA_ROS4).  */
 } da_problem;
 
 /* The record: one zero-padded step mesh per trajectory, reused by every

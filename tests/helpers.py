@@ -69,3 +69,19 @@ def mse_targets(orc, wid, n, inp):
     prob = w.problem()
     m = orc.record(prob, inp["u0"].astype(np.float64), inp["p_true"], with_h=False)
     return m["y_save"].astype(w.np_dtype), m["status"]
+
+
+def step_count_gate(orc, prob, u0, p, n_ref, eps=1e-7):
+    """Per-lane bound on |N_gpu - N_oracle| for a GPU record against the
+    oracle's: max(2, 1% of the oracle's count), widened to the largest change
+    the oracle's own record shows when its step factor is scaled by 1 +- eps.
+    The two sides round the controller's single-precision power differently
+    in the last bit (relative 6e-8), so a method whose step sequence that
+    perturbation moves cannot be held closer than this.  Returns the bound
+    and that spread."""
+    spread = 0
+    for s in (1.0 + eps, 1.0 - eps):
+        pr = prob.replace(safety=(prob.safety or 0.9) * s)
+        m = orc.record(pr, u0, p, fused=True, with_h=False)
+        spread = max(spread, int(np.max(np.abs(m["n_steps"] - n_ref))))
+    return np.maximum(np.maximum(2, 0.01 * n_ref), spread), spread

@@ -54,7 +54,7 @@ def test_invalid_problems_rejected(da, change, code):
 
 
 def test_unsupported_combinations(da):
-    for method in (W.ROS2, W.RODAS3):
+    for method in (W.ROS2, W.RODAS3, W.ROS4):
         prob = W.Problem(W.LORENZ96, 64, 1, method, 0.0, 1.0, 1e-6, 1e-6, 100)
         assert _call_record(da, prob) == -2
         assert "Rosenbrock" in da.last_error()
