@@ -297,3 +297,56 @@ def test_rkf78_lorenz63_full_size_sampled(da, orc):
            f"(max {N}); oracle record of the sample {mo['n_steps'].mean():.1f}")
     assert err.max() <= 1e-12
     assert np.all(np.abs(sub["n_steps"] - mo["n_steps"]) <= np.maximum(2, 0.01 * mo["n_steps"]))
+
+
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3, W.ROS4], ids=["ros2", "rodas3", "ros4"])
+def test_rosenbrock_failed_lanes_and_edge_sizes(da, orc, method):
+    """Robertson to t = 1000 with a NaN rate (lane 5), an overflowing start
+    (lane 7), an infinite rate (lane 9) and a step limit at the median step
+    count, so about half the trajectories stop at it.  On the oracle's mesh:
+    NaN loss and gradients exactly where the oracle's record failed, the
+    oracle's values elsewhere.  The GPU's own record: the oracle's status for
+    the three broken lanes, and for every lane whose unconstrained step
+    count is clear of the limit by more than the step-count gate.  n = 1 and
+    n = 0 run."""
+    n = 130
+    inp = W.make_inputs(4, n)
+    inp["p"][5, 0] = np.nan
+    inp["u0"][7, :] = 1e200
+    inp["p"][9, 1] = np.inf
+    base = W.WORKLOADS[4].problem(method=method, t1=1e3, max_steps=16384)
+    free = orc.record(base, inp["u0"], inp["p"], fused=True, with_h=False)
+    ok_free = free["status"] == 0
+    limit = int(np.median(free["n_steps"][ok_free]))
+    prob = base.replace(max_steps=limit)
+    _print(f"case: {W.METHOD_NAMES[method]} failed lanes, n={n}, max_steps={limit}")
+    m = orc.record(prob, inp["u0"], inp["p"], fused=True)
+    bad = m["status"] != 0
+    assert bad.sum() > 10 and (~bad).sum() > 10
+    lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, fused=True)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    loss, gu0, gp = da.replay_grad(prob, u0, p, mesh_to_dev(m, prob.max_steps, torch))
+    torch.cuda.synchronize()
+    gu0n, gpn, ln = gu0.cpu().numpy().T, gp.cpu().numpy().T, loss.cpu().numpy()
+    assert np.all(np.isnan(gpn[bad])) and np.all(np.isnan(gu0n[bad])) and np.all(np.isnan(ln[bad]))
+    assert np.all(np.isfinite(gpn[~bad])) and np.all(np.isfinite(gu0n[~bad]))
+    assert grad_rel_err(gu0n[~bad], gpn[~bad], go[~bad], po[~bad]).max() <= 1e-12
+    mesh, _ = da.record(prob, u0, p)
+    torch.cuda.synchronize()
+    st = mesh.status.cpu().numpy()
+    assert np.array_equal(st[[5, 7, 9]], m["status"][[5, 7, 9]])
+    assert st[5] == da.LANE_NONFINITE and st[7] == da.LANE_DT_UNDERFLOW
+    gate, spread = step_count_gate(orc, base, inp["u0"], inp["p"], free["n_steps"])
+    clear = ok_free & (np.abs(free["n_steps"] - limit) > gate)
+    _print(f"  oracle failed {bad.sum()}, GPU failed {(st != 0).sum()}; {clear.sum()} lanes clear "
+           f"of the limit (spread {spread})")
+    assert clear.sum() > 10 and np.array_equal(st[clear], m["status"][clear])
+    # n = 1 and n = 0
+    m1, _ = da.record(base, u0[:, :1].contiguous(), p[:, :1].contiguous())
+    l1, g1, q1 = da.replay_grad(base, u0[:, :1].contiguous(), p[:, :1].contiguous(), m1)
+    torch.cuda.synchronize()
+    assert m1.status.item() == 0 and np.isfinite(q1.cpu().numpy()).all()
+    e = torch.empty((3, 0), dtype=torch.float64, device="cuda")
+    m0, _ = da.record(base, e, e)
+    r0 = da.replay_grad(base, e, e, m0, max_n_steps=0)
+    assert r0[0].numel() == 0
