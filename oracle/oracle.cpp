@@ -37,8 +37,13 @@
  * Rounding modes.  Every sum of products is evaluated left to right as a
  * chain "first product, then multiply-add".  With fused = 0 each multiply and
  * add rounds separately (built with -ffp-contract=off); with fused = 1 each
- * multiply-add is one correctly rounded fma().  Nothing else changes between
- * the two modes.
+ * multiply-add is one correctly rounded fma().  The fused mode also follows
+ * the kernels' written schedule in three more places, each marked where it
+ * occurs: pivot reciprocals in the LU and its solves, the pairwise order of
+ * the Lorenz-96 parameter-gradient sum, and the step-size controller's power
+ * taken in single precision.  The plain mode keeps the textbook forms there:
+ * divisions by the pivot, one running sum, and the power in the state's own
+ * precision.
  *
  * Layout here is lane-major: u0[n][d], p[n][P], h[n][max_steps],
  * save_idx[n][S], y_save[n][S][d] with S = max(1, n_save).
@@ -1285,11 +1290,15 @@ T err_norm(int d, const T *err, const T *y, const T *yn, T atol, T rtol) {
   return rms<T, F>(d, err, sc);
 }
 
-/* The controller's power E^expo, in single precision: exp2(expo log2 E) with
- * E and expo rounded to float (it only scales the next trial step). */
-template <class T>
+/* The controller's power E^expo.  Plain mode: pow in the state's precision,
+ * the textbook I-controller.  Fused mode (the kernels' schedule): in single
+ * precision, exp2(expo log2 E) with E and expo rounded to float; the factor
+ * only scales the next trial step, so this changes which steps are tried, not
+ * the accept test E <= 1 or any accepted step's arithmetic. */
+template <class T, bool F>
 T ctrl_pow(T E, T expo) {
-  return T(std::exp2(float(expo) * std::log2(float(E))));
+  if (F) return T(std::exp2(float(expo) * std::log2(float(E))));
+  return std::pow(E, expo);
 }
 
 /* Starting step (HNW I, II.4) for a method of order q. */
@@ -1474,7 +1483,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
           for (int c = 0; c < d; ++c) K[0][c] = K[6][c];  /* first same as last */
         t = t_new;
         T fac = (E == T(0.0)) ? fmax
-                              : std::min(fmax, std::max(fmin, safety * ctrl_pow(E, expo)));
+                              : std::min(fmax, std::max(fmin, safety * ctrl_pow<T, F>(E, expo)));
         if (after_reject) fac = std::min(fac, T(1.0));
         h = hs * fac;
         after_reject = false;
@@ -1497,7 +1506,7 @@ void record_lane(const orc_problem *P, const Opts &o, const T *u0, const T *p,
           if (++j == n_stops) break;
         }
       } else {
-        const T fac = fin(E) ? std::max(fmin, safety * ctrl_pow(E, expo)) : fmin;
+        const T fac = fin(E) ? std::max(fmin, safety * ctrl_pow<T, F>(E, expo)) : fmin;
         h = hs * fac;
         after_reject = true;
       }

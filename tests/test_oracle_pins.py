@@ -719,10 +719,11 @@ def _lorenz(p):
 def test_dopri5_record_matches_scipy_rk45(orc):
     """SciPy's RK45 is Dormand-Prince with the same RMS error norm and
     I-controller (safety 0.9, factors in [0.2, 10], no growth right after a
-    reject).  Given the same first step, the accepted steps coincide: the same
-    number, and step sizes within 1e-4 relative (the controller's power is
-    taken in single precision here, in double precision by SciPy; the
-    difference feeds back through the error estimate but stays small)."""
+    reject).  Given the same first step, the oracle's plain mode (the
+    textbook controller, its power in double precision as in SciPy) accepts
+    the same steps: the same number, and step sizes within 1e-8 relative.
+    The fused mode takes the power in single precision, as the kernels do;
+    its step counts still equal SciPy's."""
     from scipy.integrate import solve_ivp
     inp = W.make_inputs(2, 6)
     for i in range(6):
@@ -733,8 +734,10 @@ def test_dopri5_record_matches_scipy_rk45(orc):
         hs = np.diff(sol.t)
         N = m["n_steps"][0]
         assert N == len(hs)
-        assert np.allclose(m["h"][0, :N], hs, rtol=1e-4)
+        assert np.allclose(m["h"][0, :N], hs, rtol=1e-8)
         assert np.allclose(m["y_save"][0, 0], sol.y[:, -1], rtol=1e-6, atol=1e-8)
+        mf = orc.record(prob, inp["u0"][i:i + 1], inp["p"][i:i + 1], fused=True)
+        assert mf["n_steps"][0] == N
 
 
 def test_initial_step_matches_textbook(orc):
