@@ -11,8 +11,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from helpers import (aux_to_dev, grad_rel_err, mesh_to_dev, mesh_to_host, mse_targets, rel_err,
-                     to_dev)
+from helpers import (aux_to_dev, elem_err, grad_elem_err, grad_rel_err, mesh_to_dev,
+                     mesh_to_host, mse_targets, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -93,10 +93,10 @@ def test_dense_on_oracle_mesh(da, orc, name, wid, kw, lk, n):
     torch.cuda.synchronize()
     tol = TOL[dt]
     ygn = yg.cpu().numpy().transpose(2, 0, 1)             # [n, S, d]
-    ey = rel_err(ygn.reshape(n, -1), yo.reshape(n, -1))
-    eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+    ey = elem_err(ygn.reshape(n, -1), yo.reshape(n, -1))
+    eg = grad_elem_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
     el = np.abs(loss.cpu().numpy() - lo) / np.abs(lo)
-    _print(f"  saves max rel {ey.max():.3e} (bitwise lanes {np.mean(ey == 0):.3f}), "
+    _print(f"  element-wise: saves max rel {ey.max():.3e} (bitwise lanes {np.mean(ey == 0):.3f}), "
            f"grad max rel {eg.max():.3e}, loss max rel {el.max():.3e}")
     assert ey.max() <= tol and eg.max() <= tol
     if prob.rhs == W.LORENZ96:
@@ -166,7 +166,7 @@ def test_dense_gpu_record(da, orc, name, wid, kw, lk, n):
         assert np.array_equal(mg["save_idx"][same], mo["save_idx"][same])
         assert np.array_equal(mg["save_theta"][same], mo["save_theta"][same])
         ysn = ys.cpu().numpy().transpose(2, 0, 1)
-        e = rel_err(ysn[same].reshape(same.sum(), -1), mo["y_save"][same].reshape(same.sum(), -1))
+        e = elem_err(ysn[same].reshape(same.sum(), -1), mo["y_save"][same].reshape(same.sum(), -1))
         assert e.max() <= TOL[dt]
 
 
@@ -219,8 +219,8 @@ def test_dense_sensitivities(da, orc, name, wid, kw, lk, n):
     la, ga, pa = da.replay_grad(prob, u0, p, mesh, lk, aux=auxd, scale=scale)
     torch.cuda.synchronize()
     sgn = sg.cpu().numpy().transpose(3, 0, 1, 2)
-    es = rel_err(sgn.reshape(n, -1), so.reshape(n, -1))
-    eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+    es = elem_err(sgn.reshape(n, -1), so.reshape(n, -1))
+    eg = grad_elem_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
     ea = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, ga.cpu().numpy().T,
                       pa.cpu().numpy().T)
     _print(f"  sens max rel {es.max():.3e}, grad {eg.max():.3e}, forward vs reverse {ea.max():.3e}")
@@ -251,8 +251,8 @@ def test_dense_full_size_fp32_sampled(da, orc):
     sub = {k: v[idx] for k, v in mg.items()}
     lo, go, po = orc.replay_grad(prob, inp["u0"][idx], inp["p"][idx], sub, W.MSE_SAVE,
                                  aux=aux[idx], scale=scale, fused=True)
-    eg = grad_rel_err(gu0.cpu().numpy().T[idx], gp.cpu().numpy().T[idx], go, po)
+    eg = grad_elem_err(gu0.cpu().numpy().T[idx], gp.cpu().numpy().T[idx], go, po)
     el = np.abs(loss.cpu().numpy()[idx] - lo) / np.abs(lo)
-    _print(f"  sampled grad max rel {eg.max():.3e}, loss {el.max():.3e}; "
+    _print(f"  sampled grad element-wise max rel {eg.max():.3e}, loss {el.max():.3e}; "
            f"mean steps {mg['n_steps'].mean():.1f}")
     assert eg.max() <= 1e-4 and el.max() <= 1e-4

@@ -1,22 +1,32 @@
 """GPU (HIP library, through the C ABI) against the CPU oracle.
 
-Gates (relative error per lane = max over grad_u0, grad_p of
-||g_gpu - g_orc||_inf / ||g_orc||_inf):
- - gradients on a shared (oracle-recorded) mesh: <= 1e-12 in FP64 against the
-   oracle's fused-rounding mode, <= 1e-4 in FP32 against the FP32 oracle;
- - a GPU-recorded mesh: every step's re-evaluated error norm <= 1 + 1e-6,
-   same statuses, |N_gpu - N_orc| <= max(2, 1% of N_orc) on every lane in
-   FP64 (on 90% of lanes in FP32, where chaotic growth of last-bit
-   differences in the controller moves a few lanes by up to 10%);
- - the GPU record and the GPU replay give bitwise equal states;
- - results do not depend on the slot order, the workspace chunking or the run.
+Gates on the gradients of a shared (oracle-recorded) mesh, every one element
+by element (each component of grad_u0 and grad_p against its own value, the
+smallest included; no absolute floor):
+ - against the oracle's fused-rounding mode, which evaluates the kernels'
+   written arithmetic schedule: <= 1e-12 in FP64, <= 1e-4 in FP32 (the
+   the benchmark spec's figures; they hold against this twin of the schedule);
+ - against the oracle's plain-rounding mode (every operation rounded on its
+   own, textbook controller), which shares no arithmetic order with the
+   kernels: FP64 <= PLAIN_TOL, four times the largest gap the oracle's two
+   modes show on the same inputs (measured by the oracle alone); FP32 within
+   twice the oracle's own FP32 rounding spread of the FP64 oracle, plus 1e-4
+   (helpers.fp32_against_fp64).
+Gates on a GPU-recorded mesh: every step's re-evaluated error norm
+<= 1 + 1e-6, the same statuses, and |N_gpu - N_orc| per trajectory within
+max(2, 1% of N_orc) or, where larger, the oracle's own spread under a
+last-bit change of the controller's factor (helpers.step_count_gate),
+against the fused-mode record and against the plain-mode record.  The GPU
+record and the GPU replay give bitwise equal states; results do not depend
+on the slot order, the workspace chunking or the run.
 """
 import numpy as np
 import pytest
 
 import workloads as W
-from helpers import (aux_to_dev, grad_rel_err, mesh_to_dev, mesh_to_host, mse_targets,
-                     rel_err, to_dev)
+from helpers import (aux_to_dev, elem_err, fp32_against_fp64, grad_elem_err, grad_rel_err,
+                     mesh_to_dev, mesh_to_host, mse_targets, rel_err, smallest_component,
+                     step_count_gate, to_dev)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -24,6 +34,11 @@ pytestmark = pytest.mark.gpu
 # (workload, lanes) small enough for the oracle, several tiles and a ragged tail
 SMALL = [(1, 1024), (2, 1000), (3, 1500), (4, 300), (5, 200)]
 TOL = {"f64": 1e-12, "f32": 1e-4}
+# Element-wise gate against the plain-rounding oracle on the SMALL inputs:
+# four times the largest element-wise gap between the oracle's plain and
+# fused modes on the same mesh (measured 9.5e-12, 6.3e-9, 7.8e-14 and 2.9e-8
+# for workloads 1, 2, 4 and 5; 2 and 5 are chaotic over their intervals).
+PLAIN_TOL = {1: 4e-11, 2: 3e-8, 4: 4e-13, 5: 2e-7}
 
 
 @pytest.fixture(scope="module")
@@ -50,6 +65,39 @@ def _print(*a):
     print(*a, flush=True)
 
 
+def _as64(m):
+    """A mesh with its floating fields in double (exact for FP32 values)."""
+    return {k: (v.astype(np.float64) if v.dtype == np.float32 else v) for k, v in m.items()}
+
+
+def check_independent(orc, wid, prob, inp, m, lk, aux, scale, g1, g2, go, po):
+    """The independent gates of a shared-mesh gradient (g1, g2 from the GPU;
+    go, po the fused oracle's): FP64 element-wise against the plain-rounding
+    oracle; FP32 against the FP64 oracle of the same mesh."""
+    if inp["u0"].dtype == np.float64:
+        _, gop, pop = orc.replay_grad(prob, inp["u0"], inp["p"], m, lk, aux=aux, scale=scale,
+                                      fused=False)
+        errp = grad_elem_err(g1, g2, gop, pop)
+        _print(f"  vs plain-rounding oracle: element-wise max {errp.max():.3e} "
+               f"(gate {PLAIN_TOL[wid]:.0e}), median {np.median(errp):.3e}")
+        assert errp.max() <= PLAIN_TOL[wid]
+        return
+    _, gop, pop = orc.replay_grad(prob, inp["u0"], inp["p"], m, lk, aux=aux, scale=scale,
+                                  fused=False)
+    ax64 = None if aux is None else aux.astype(np.float64)
+    _, g64, p64 = orc.replay_grad(prob, inp["u0"].astype(np.float64),
+                                  inp["p"].astype(np.float64), _as64(m), lk, aux=ax64,
+                                  scale=scale, fused=False)
+    e = np.maximum(fp32_against_fp64(g1, g64, gop, go), fp32_against_fp64(g2, p64, pop, po))
+    e_plain = grad_elem_err(g1, g2, gop, pop)
+    e64 = grad_elem_err(g1, g2, g64, p64)
+    _print(f"  FP32 vs FP64 oracle: element-wise median {np.median(e64):.3e}, p99 "
+           f"{np.percentile(e64, 99):.3e}, max {e64.max():.3e}; vs the plain FP32 oracle: "
+           f"median {np.median(e_plain):.3e}, max {e_plain.max():.3e}; "
+           f"gate ratio max {e.max():.3f} (<= 1)")
+    assert e.max() <= 1.0
+
+
 @pytest.mark.parametrize("wid,n", SMALL)
 def test_gradient_on_oracle_mesh(da, orc, wid, n):
     """Shared mesh: the GPU replays the oracle's record."""
@@ -65,47 +113,42 @@ def test_gradient_on_oracle_mesh(da, orc, wid, n):
     loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale)
     torch.cuda.synchronize()
     g1, g2, L = gu0.cpu().numpy().T, gp.cpu().numpy().T, loss.cpu().numpy()
-    err = grad_rel_err(g1, g2, go, po)
-    _print(f"  max rel err {err.max():.3e}, p99.9 {np.percentile(err, 99.9):.3e}, "
-           f"bitwise equal lanes {np.mean(err == 0):.4f}")
+    err = grad_elem_err(g1, g2, go, po)
+    errn = grad_rel_err(g1, g2, go, po)
+    _print(f"  element-wise max rel err {err.max():.3e} (norm-wise {errn.max():.3e}), "
+           f"p99.9 {np.percentile(err, 99.9):.3e}, bitwise equal lanes {np.mean(err == 0):.4f}; "
+           f"smallest component / lane's largest {smallest_component(go, po):.2e}")
     assert err.max() <= TOL[w.dtype]
     assert np.max(np.abs(L - lo) / np.abs(lo)) <= TOL[w.dtype]
-    # against the plain-rounding oracle: reported, loose gate
-    lp, gop, pop = orc.replay_grad(prob, inp["u0"], inp["p"], m, w.loss, aux=aux, scale=scale,
-                                   fused=False)
-    errp = grad_rel_err(g1, g2, gop, pop)
-    _print(f"  vs plain-rounding oracle: max {errp.max():.3e}, median {np.median(errp):.3e}")
-    assert np.median(errp) < (1e-9 if w.dtype == "f64" else 1e-3)
+    check_independent(orc, wid, prob, inp, m, w.loss, aux, scale, g1, g2, go, po)
 
 
 @pytest.mark.parametrize("wid,n", SMALL)
 def test_record_within_tolerance_of_oracle(da, orc, wid, n):
     """GPU-recorded mesh: accepted steps pass the oracle's own error test and the
-    step counts agree with the oracle's record."""
+    step counts agree with the oracle's records, in both rounding modes."""
     w, prob, inp, aux, scale = _setup(orc, wid, n)
     _print(f"case: GPU record vs oracle, workload {wid}, n={n}")
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     mesh, ys = da.record(prob, u0, p)
     torch.cuda.synchronize()
     mg = mesh_to_host(mesh, prob.max_steps)
-    mo = orc.record(prob, inp["u0"], inp["p"], fused=True)
-    assert np.array_equal(mg["status"], mo["status"])
-    ng, no = mg["n_steps"], mo["n_steps"]
-    close = np.abs(ng - no) <= np.maximum(2, 0.01 * no)
-    _print(f"  step counts within max(2, 1%): {close.mean():.4f}; "
-           f"max |dN| {np.abs(ng - no).max()}")
-    if w.dtype == "f64":
-        assert np.all(close)
-    else:
-        # single precision on a chaotic system: last-bit differences of the
-        # controller's pow/sqrt grow over the interval, so the step counts
-        # agree statistically
-        assert close.mean() >= 0.9
-        assert np.all(np.abs(ng - no) <= np.maximum(8, 0.1 * no))
-    same = np.array([np.array_equal(mg["h"][i, :ng[i]], mo["h"][i, :no[i]]) and ng[i] == no[i]
-                     for i in range(n)])
-    _print(f"  bitwise-equal meshes: {same.mean():.4f}; mean steps gpu {ng.mean():.2f} "
-           f"oracle {no.mean():.2f}")
+    ng = mg["n_steps"]
+    for fused in (True, False):
+        mo = orc.record(prob, inp["u0"], inp["p"], fused=fused)
+        assert np.array_equal(mg["status"], mo["status"])
+        no = mo["n_steps"]
+        gate, spread = step_count_gate(orc, prob, inp["u0"], inp["p"], no, fused=fused)
+        dn = np.abs(ng - no)
+        same = np.array([np.array_equal(mg["h"][i, :ng[i]], mo["h"][i, :no[i]]) and ng[i] == no[i]
+                         for i in range(n)])
+        _print(f"  vs {'fused' if fused else 'plain'} record: max |dN| {dn.max()}, within "
+               f"max(2, 1%) {np.mean(dn <= np.maximum(2, 0.01 * no)):.4f}, oracle's own spread "
+               f"{spread}; bitwise-equal meshes {same.mean():.4f}; mean steps gpu {ng.mean():.2f} "
+               f"oracle {no.mean():.2f}")
+        assert np.all(dn <= gate)
+        if fused:
+            mfused = mo
     # zero padding after the last step, to the end of the tiled log
     hg = mg["h"]
     hall = mesh.steps().cpu().numpy()
@@ -123,7 +166,7 @@ def test_record_within_tolerance_of_oracle(da, orc, wid, n):
     if wid in (1, 4):
         # short or non-chaotic: final states agree to the tolerance scale
         yg = ys.cpu().numpy()[-1].T
-        yo = mo["y_save"][:, -1, :]
+        yo = mfused["y_save"][:, -1, :]
         tol = 10 * (prob.atol + prob.rtol * np.abs(yo))
         assert np.all(np.abs(yg - yo) <= tol)
 
@@ -141,8 +184,8 @@ def test_gpu_record_equals_gpu_replay(da, orc, wid, n):
     mg = mesh_to_host(mesh, prob.max_steps)
     yo, _ = orc.replay(prob, inp["u0"], inp["p"], mg, fused=True)
     yg = ys.cpu().numpy().transpose(2, 0, 1)
-    err = rel_err(yg.reshape(n, -1), yo.reshape(n, -1))
-    _print(f"  replay of GPU mesh vs oracle: max rel {err.max():.3e}")
+    err = elem_err(yg.reshape(n, -1), yo.reshape(n, -1))
+    _print(f"  replay of GPU mesh vs oracle: element-wise max rel {err.max():.3e}")
     assert err.max() <= TOL[w.dtype]
 
 
@@ -249,7 +292,7 @@ def test_loss_kinds_and_cotangents(da, orc):
         loss, gu0, gp = da.replay_grad(prob, u0, p, mesh, lk, aux=aux_to_dev(aux, torch),
                                        scale=sc)
         torch.cuda.synchronize()
-        err = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+        err = grad_elem_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
         assert err.max() <= 1e-12, (lk, err.max())
         assert np.allclose(loss.cpu().numpy(), lo, rtol=1e-12)
 
@@ -279,8 +322,8 @@ def test_lorenz96_losses_and_dimensions(da, orc, dim):
                                            aux=None if ax is None else aux_to_dev(ax, torch),
                                            scale=sc)
             torch.cuda.synchronize()
-            err = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
-            _print(f"  method {method} loss {lk}: max rel err {err.max():.3e}")
+            err = grad_elem_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+            _print(f"  method {method} loss {lk}: element-wise max rel err {err.max():.3e}")
             assert err.max() <= 1e-12, (method, lk, err.max())
             # the loss is a sum over components that the GPU adds pairwise and
             # the oracle in sequence: both within 2 d eps of the sum of |terms|
@@ -346,6 +389,44 @@ def test_solve_fwd_matches_record(da, orc):
         assert torch.equal(ys, yf) and torch.equal(ns, mesh.n_steps) and torch.equal(st, mesh.status)
 
 
+# (workload, lanes, shortened interval): the interval over which the chaotic
+# workloads' final states can still be held to the tolerance scale
+SOLVE_CASES = [(1, 1000, None), (2, 600, 1.0), (3, 500, 1.0), (4, 200, None), (5, 70, 0.5)]
+
+
+@pytest.mark.parametrize("wid,n,t_short", SOLVE_CASES)
+def test_solve_fwd_against_oracle(da, orc, wid, n, t_short):
+    """The forward-only solve against the oracle's records directly (both
+    rounding modes): the same statuses, step counts within the record gate,
+    and saved states within 10 (atol + rtol |y|) of the oracle's on the
+    non-chaotic workloads (1, 4) and, for the chaotic ones (2, 3, 5), on a
+    shortened interval; over their full intervals the spread is reported."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    probs = [prob] + ([] if t_short is None else [prob.replace(t1=t_short, save_times=())])
+    for k, pr in enumerate(probs):
+        _print(f"case: solve_fwd against the oracle, workload {wid}, n={n}, t1={pr.t1}")
+        yf, ns, st = da.solve_fwd(pr, u0, p)
+        torch.cuda.synchronize()
+        yg = yf.cpu().numpy().transpose(2, 0, 1).astype(np.float64)   # [n, S, d]
+        ng, sg = ns.cpu().numpy(), st.cpu().numpy()
+        for fused in (True, False):
+            mo = orc.record(pr, inp["u0"], inp["p"], fused=fused, with_h=False)
+            assert np.array_equal(sg, mo["status"])
+            no = mo["n_steps"]
+            gate, spread = step_count_gate(orc, pr, inp["u0"], inp["p"], no, fused=fused)
+            dn = np.abs(ng - no)
+            yo = mo["y_save"].astype(np.float64)
+            bound = 10 * (pr.atol + pr.rtol * np.abs(yo))
+            ratio = np.abs(yg - yo) / bound
+            _print(f"  vs {'fused' if fused else 'plain'} record: max |dN| {dn.max()} (spread "
+                   f"{spread}); saves: max |dy| / (10 (atol + rtol |y|)) {ratio.max():.3e}, "
+                   f"median {np.median(ratio):.3e}")
+            assert np.all(dn <= gate)
+            if wid in (1, 4) or k == 1:
+                assert ratio.max() <= 1.0
+
+
 @pytest.mark.parametrize("wid", [3, 4, 5])
 def test_full_size_workloads_sampled(da, orc, wid):
     """Workloads 3, 4 and 5 at their full sizes in the benchmark's launch
@@ -388,19 +469,19 @@ def test_full_size_workloads_sampled(da, orc, wid):
     ax = None if aux is None else aux[tr]
     lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, w.loss, aux=ax,
                                  scale=scale, fused=True)
-    err = grad_rel_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
-    _print(f"  sampled {len(tr)} trajectories: max rel err {err.max():.3e}, max steps {N}")
+    err = grad_elem_err(gu0.cpu().numpy()[:, tr].T, gp.cpu().numpy()[:, tr].T, go, po)
+    _print(f"  sampled {len(tr)} trajectories: element-wise max rel err {err.max():.3e}, "
+           f"max steps {N}")
     assert err.max() <= TOL[w.dtype]
     E = orc.mesh_max_err(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
-    assert np.all(E <= 1 + (1e-6 if w.dtype == "f64" else 1e-3))
+    _print(f"  max re-evaluated error norm {E.max():.7f}")
+    assert np.all(E <= 1 + 1e-6)
     mo = orc.record(prob, inp["u0"][tr], inp["p"][tr], fused=True, with_h=False)
     no = mo["n_steps"]
     dn = np.abs(sub["n_steps"] - no)
-    if w.dtype == "f64":
-        assert np.all(dn <= np.maximum(2, 0.01 * no))
-    else:
-        assert np.mean(dn <= np.maximum(2, 0.01 * no)) >= 0.9
-        assert np.all(dn <= np.maximum(8, 0.1 * no))
+    gate, spread = step_count_gate(orc, prob, inp["u0"][tr], inp["p"][tr], no)
+    _print(f"  step counts: max |dN| {dn.max()}, oracle's own spread {spread}")
+    assert np.all(dn <= gate)
 
 
 def test_degenerate_trajectories(da, orc):
@@ -423,7 +504,7 @@ def test_degenerate_trajectories(da, orc):
     lo, go, po = orc.replay_grad(prob, inp["u0"], inp["p"], m, fused=True)
     l1, g1, q1 = da.replay_grad(prob, u0, p, mesh_to_dev(m, prob.max_steps, torch))
     torch.cuda.synchronize()
-    assert np.all(grad_rel_err(g1.cpu().numpy().T, q1.cpu().numpy().T, go, po)[
+    assert np.all(grad_elem_err(g1.cpu().numpy().T, q1.cpu().numpy().T, go, po)[
         np.arange(70) != 3] <= 1e-12)
     assert np.all(g1.cpu().numpy()[:, 3] == 0) and l1.cpu().numpy()[3] == 0
     # Lorenz-96 at its fixed point
@@ -478,8 +559,8 @@ def test_full_size_lorenz_dopri5_sampled(da, orc):
     lo, go, po = orc.replay_grad(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
     g1 = gu0.cpu().numpy()[:, tr].T
     g2 = gp.cpu().numpy()[:, tr].T
-    err = grad_rel_err(g1, g2, go, po)
-    _print(f"  sampled {len(slots)} lanes: max rel err {err.max():.3e}, "
+    err = grad_elem_err(g1, g2, go, po)
+    _print(f"  sampled {len(slots)} lanes: element-wise max rel err {err.max():.3e}, "
            f"max steps {N}, mean steps {sm.n_steps.float().mean().item():.1f}")
     assert err.max() <= 1e-12
     E = orc.mesh_max_err(pn, inp["u0"][tr], inp["p"][tr], sub, fused=True)
@@ -516,8 +597,8 @@ def test_lorenz96_chunked_workspace_and_fp32(da, orc):
     l, g, q = da.replay_grad(prob, to_dev(u32, torch), to_dev(p32, torch),
                              mesh_to_dev(m, prob.max_steps, torch))
     torch.cuda.synchronize()
-    err = grad_rel_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
-    _print(f"  FP32 max rel err {err.max():.3e}")
+    err = grad_elem_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
+    _print(f"  FP32 element-wise max rel err {err.max():.3e}")
     assert err.max() <= 1e-4
 
 
@@ -542,7 +623,7 @@ def test_maximum_save_times(da, orc):
     mesh, ys = da.record(prob, u0, p)
     yr = da.replay_fwd(prob, u0, p, mesh)
     torch.cuda.synchronize()
-    err = grad_rel_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
+    err = grad_elem_err(g.cpu().numpy().T, q.cpu().numpy().T, go, po)
     assert err.max() <= 1e-12
     assert torch.equal(ys, yr)
     si = mesh.save_idx.cpu().numpy().T

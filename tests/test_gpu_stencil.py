@@ -5,7 +5,11 @@ the components, differentiated by the oracle's own dual numbers).
 
 Gates: on shared (oracle-recorded) meshes, saved states, losses, gradients
 and sensitivities within 1e-12 relative per trajectory in FP64 (fused
-oracle) and 1e-4 in FP32; Lorenz-96 written as a stencil gives the built-in
+oracle) and 1e-4 in FP32, norm-wise (the largest difference over the
+vector's largest element): the two sides take the derivatives by different
+routes (the GPU from one tangent per stencil offset, the oracle from its
+Jacobian columns), so their rounding differences scale with the vector and
+an element-wise gate would measure the route, not the kernel; Lorenz-96 written as a stencil gives the built-in
 Lorenz-96's gradient to 1e-12 on the same mesh; a GPU-recorded mesh is
 within the step-count gate of the oracle's; checkpoint intervals and the
 replay table give bitwise equal gradients."""

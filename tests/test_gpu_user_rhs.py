@@ -4,7 +4,11 @@ differentiated by the oracle's own dual numbers).
 
 Gates: on shared (oracle-recorded) meshes, losses, gradients, saved states
 and sensitivities within 1e-12 relative per trajectory in FP64 (fused
-oracle) and 1e-4 in FP32; the same system written as source and built in
+oracle) and 1e-4 in FP32, norm-wise (the largest difference over the
+vector's largest element): the device's and the host's exp, sin, pow and
+the like differ in the last bits, and the derivatives come from tangent
+passes on the GPU and Jacobian columns in the oracle, so the differences
+scale with the vector rather than with each element; the same system written as source and built in
 gives the same gradient to 1e-12; checkpoint intervals, the replay table and
 dense output behave as for the built-in systems; the GPU record of a Kepler
 orbit conserves its invariants."""
