@@ -46,6 +46,7 @@ MAX_SAVES = 128
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_pad",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
+           "da_replay_grad_noalloc",
            "da_replay_sens", "da_replay_sens_dirs", "da_rhs_register", "da_rhs_register_stencil",
            "da_rhs_release", "da_last_error", "da_version")
 
@@ -114,6 +115,8 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_grad_workspace.restype = ctypes.c_size_t
     lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp]
+    lib.da_replay_grad_noalloc.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp,
+                                           i32, vp]
     lib.da_replay_sens.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, vp, vp]
     lib.da_replay_sens_dirs.argtypes = [P, i64, vp, vp, M, i32, i32, ctypes.POINTER(_Loss), vp,
                                         vp, vp, vp]
@@ -123,7 +126,8 @@ def _load_library() -> ctypes.CDLL:
     lib.da_rhs_release.argtypes = [i32]
     lib.da_last_error.restype = ctypes.c_char_p
     for name in ("da_record", "da_solve_fwd", "da_mesh_sort", "da_mesh_max_steps", "da_mesh_pad",
-                 "da_replay_fwd", "da_replay_grad", "da_replay_sens", "da_replay_sens_dirs",
+                 "da_replay_fwd", "da_replay_grad", "da_replay_grad_noalloc", "da_replay_sens",
+                 "da_replay_sens_dirs",
                  "da_rhs_register", "da_rhs_register_stencil",
                  "da_rhs_release", "da_version"):
         getattr(lib, name).restype = ctypes.c_int
@@ -423,6 +427,36 @@ def replay_grad(prob, u0, p, mesh: Mesh, loss_kind: int = SUMSQ_FINAL, aux=None,
     """Replay + reverse sweep: (loss [n], grad_u0 [d, n], grad_p [P, n])."""
     call = ReplayGrad(prob, u0, p, mesh, loss_kind, aux, scale, max_n_steps, ws_bytes)
     return call(stream)
+
+
+def replay_grad_noalloc(prob, u0, p, mesh: Mesh, max_n_steps: int, loss_kind: int = SUMSQ_FINAL,
+                        aux=None, scale: float = 1.0, out=None, stream=None):
+    """da_replay_grad_noalloc: the replay gradient with the library's static
+    device scratch as workspace (no allocation in the call).  out = (loss
+    [n], grad_u0 [d, n], grad_p [P, n]) are written when given, else
+    allocated here; returns them."""
+    n, dt = _inputs(prob, u0, p)
+    S = max(1, len(prob.save_times))
+    if aux is not None:
+        _need(aux, (S, prob.dim, n), dt, "aux")
+    if out is None:
+        out = (torch.empty(n, dtype=dt, device=u0.device),
+               torch.empty((prob.dim, n), dtype=dt, device=u0.device),
+               torch.empty((prob.n_params, n), dtype=dt, device=u0.device))
+    loss, gu0, gp = out
+    _need(loss, (n,), dt, "loss")
+    _need(gu0, (prob.dim, n), dt, "grad_u0")
+    _need(gp, (prob.n_params, n), dt, "grad_p")
+    P, keep = cproblem(prob, dt)
+    cm = mesh.c()
+    lobj = _Loss(loss_kind, None if aux is None else aux.data_ptr(), scale)
+    _check(_lib.da_replay_grad_noalloc(ctypes.byref(P), n, _ptr(u0), _ptr(p), ctypes.byref(cm),
+                                       ctypes.byref(lobj), _ptr(loss), _ptr(gu0), _ptr(gp),
+                                       int(max_n_steps), _stream(stream)))
+    return loss, gu0, gp
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def replay_sens(prob, u0, p, mesh: Mesh, loss_kind: Optional[int] = SUMSQ_FINAL, aux=None,

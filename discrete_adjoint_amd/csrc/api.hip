@@ -5,10 +5,18 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 
 #include "dadj.h"
 #include "dadj_internal.hpp"
+
+// Device scratch of da_replay_grad_noalloc, for callers that cannot allocate
+// device memory: DA_NOALLOC_SCRATCH_BYTES bytes that every GPU the library
+// runs on holds from its first use until the process ends.  Host code never
+// uses this name as an address (here it is a host-side stand-in); the device
+// address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[DA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -407,10 +415,43 @@ size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n
          (size_t)ws_row_of(prob->rhs, prob->dim) * dsize(prob->dtype);
 }
 
-int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
-                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
-                   void *grad_p, int32_t max_n_steps, void *workspace, size_t ws_bytes,
-                   void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Device address of `scratch` on each device, looked up on the device's first
+// da_replay_grad_noalloc call with that device current.
+constexpr int kScratchDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kScratchDevices] = {};
+
+int noalloc_scratch(void **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kScratchDevices)
+    return fail(DA_EUNSUPPORTED, "device %d is beyond the %d devices of the scratch table", dev,
+                kScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(DA_EHIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DA_OK;
+}
+
+// The replay gradient of da_replay_grad and da_replay_grad_noalloc.  With
+// noalloc the workspace is the static scratch, looked up after the argument
+// checks (so that they need no device), and the error raised when it holds
+// fewer than one block of trajectories names the scratch.
+int replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                void *grad_p, int32_t max_n_steps, void *workspace, size_t ws_bytes,
+                bool noalloc, void *stream) {
   dadj::ProbArgs pr;
   int rc = check_problem(prob, n, pr, nullptr);
   if (rc) return rc;
@@ -432,10 +473,21 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
                           ws_row_of(pr.rhs, pr.dim) * dsize(pr.dtype);
   int64_t C = n;
   if (per_lane > 0) {
+    if (noalloc) {
+      const int rs = noalloc_scratch(&workspace);
+      if (rs) return rs;
+      ws_bytes = DA_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace) return fail(DA_EWORKSPACE, "workspace is NULL");
     const size_t fit = ws_bytes / per_lane;
     if (fit < (size_t)n) {
       C = (int64_t)(fit / dadj::BLOCK) * dadj::BLOCK;
+      if (C < dadj::BLOCK && noalloc)
+        return fail(DA_EWORKSPACE,
+                    "da_replay_grad_noalloc: %zu bytes per trajectory (max_n_steps %d, checkpoint "
+                    "interval %d) times %d trajectories exceed the %zu-byte static scratch; call "
+                    "da_replay_grad with a workspace",
+                    per_lane, max_n_steps, pr.checkpoint, dadj::BLOCK, ws_bytes);
       if (C < dadj::BLOCK)
         return fail(DA_EWORKSPACE, "workspace %zu bytes holds fewer than %d trajectories", ws_bytes,
                     dadj::BLOCK);
@@ -460,6 +512,25 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
     if (e != hipSuccess) return hip_fail(e, "replay_grad launch");
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                   const da_mesh *mesh, const da_loss *loss, void *loss_out, void *grad_u0,
+                   void *grad_p, int32_t max_n_steps, void *workspace, size_t ws_bytes,
+                   void *stream) {
+  return replay_grad(prob, n, u0, p, mesh, loss, loss_out, grad_u0, grad_p, max_n_steps,
+                     workspace, ws_bytes, false, stream);
+}
+
+int da_replay_grad_noalloc(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                           const da_mesh *mesh, const da_loss *loss, void *loss_out,
+                           void *grad_u0, void *grad_p, int32_t max_n_steps, void *stream) {
+  return replay_grad(prob, n, u0, p, mesh, loss, loss_out, grad_u0, grad_p, max_n_steps, nullptr,
+                     0, true, stream);
 }
 
 // Forward-mode sensitivities along directions q_begin .. q_begin + q_count - 1

@@ -26,9 +26,10 @@
  *  - All array pointers are DEVICE pointers unless marked "host"; all memory is
  *    owned by the caller.  The library allocates no device memory (except the
  *    1 KiB scratch that da_mesh_max_steps allocates and frees within the
- *    call) and keeps no state apart from a thread-local error message and the
+ *    call) and keeps no state apart from a thread-local error message, the
  *    code objects of right-hand sides registered at run time
- *    (da_rhs_register).
+ *    (da_rhs_register) and the static device scratch of
+ *    da_replay_grad_noalloc (one per GPU, with its looked-up address).
  *  - Per-trajectory arrays are component-major: element (c, i) of an array
  *    with C components lives at index c * n + i (trajectory index fastest), so
  *    a wavefront reads and writes contiguous memory.
@@ -323,6 +324,28 @@ int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void
                    const da_mesh *mesh, const da_loss *loss, void *loss_out,
                    void *grad_u0, void *grad_p, int32_t max_n_steps, void *workspace,
                    size_t ws_bytes, void *stream);
+
+/* For callers that cannot allocate device memory at call time (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * da_replay_grad with its workspace taken from a static device scratch of
+ * DA_NOALLOC_SCRATCH_BYTES bytes instead of a caller buffer.  Same arguments,
+ * kernels and results as da_replay_grad (bit for bit); the call allocates
+ * nothing.  The ensemble is processed in consecutive chunks of as many
+ * trajectories as the scratch holds (a multiple of 256); when it holds fewer
+ * than 256 trajectories of max_n_steps steps (about 10900 steps of a
+ * three-component FP64 system at checkpoint interval 1) the call returns
+ * DA_EWORKSPACE before any launch.  The caller still owns and passes every
+ * input and output.
+ * Each GPU holds one copy of the scratch from the first call on it until the
+ * process ends; the first call on a device looks up its address, with that
+ * device current (make that first call outside graph capture).  All calls on
+ * one GPU share that copy: calls that overlap in time on one GPU (two
+ * streams, two threads) race and must be ordered by the caller.  Nothing in
+ * the scratch needs to start at zero. */
+#define DA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int da_replay_grad_noalloc(const da_problem *prob, int64_t n, const void *u0, const void *p,
+                           const da_mesh *mesh, const da_loss *loss, void *loss_out,
+                           void *grad_u0, void *grad_p, int32_t max_n_steps, void *stream);
 
 /* Forward-mode sensitivities of the replay, mesh held fixed: the d + P unit
  * directions (u0 components first, then parameters) are carried as tangents
