@@ -24,7 +24,7 @@ Printed on one JSON line, besides the driver's fields:
   clock_adjusted  the same achieved rate against the vector peak at the
                 shader clock the counters measured while the gradient kernel
                 ran (GRBM_GUI_ACTIVE per XCD over the launch time), and the
-                executed FP64 rate (SQ_INSTS_VALU_*_F64: stage recomputation and
+                executed rate (SQ_INSTS_VALU_*_F64, or _F32 in single precision: stage recomputation and
                 padded steps included) over the live launch time; from the
                 committed counter summary of the workload when the kernel
                 sources match it, else null;
@@ -176,13 +176,22 @@ def kernel_source_hash(family: str = "erk") -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload_name: str, family: str, dense: bool = False):
+def _summary_interval(path: str) -> int:
+    """Checkpoint interval a counter summary was taken at (1 when it does not
+    say: every summary without the line was taken at interval 1)."""
+    for line in open(path):
+        if line.startswith("checkpoint_interval:"):
+            return int(line.split(":", 1)[1].strip())
+    return 1
+
+
+def read_traffic(workload_name: str, family: str, dense: bool = False, interval: int = 1):
     """HBM bytes per gradient launch from the committed counter summary of the
     workload (its dense-output variant with `dense`), if it was taken with the
-    current kernel sources."""
+    current kernel sources at the same checkpoint interval."""
     sfx = "_dense" if dense else ""
     path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}{sfx}_counters.md")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or _summary_interval(path) != interval:
         return None
     src_hash, traffic = None, None
     for line in open(path):
@@ -193,23 +202,24 @@ def read_traffic(workload_name: str, family: str, dense: bool = False):
     return traffic if src_hash == kernel_source_hash(family) else None
 
 
-def read_valu_clock(workload_name: str, family: str):
+def read_valu_clock(workload_name: str, family: str, interval: int = 1):
     """Shader clock and executed FP64 work of the gradient kernel from the
     committed counter summary of the workload (GRBM_GUI_ACTIVE per XCD over
     the launch time; SQ_INSTS_VALU_{FMA,MUL,ADD,TRANS}_F64), if it was taken
-    with the current kernel sources."""
+    with the current kernel sources at the same checkpoint interval."""
     path = os.path.join(COUNTERS_DIR, f"replay_grad_{workload_name}_valu_clock.md")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or _summary_interval(path) != interval:
         return None
     vals = {}
     for line in open(path):
-        for key in ("kernel_source_hash", "clock_ghz", "valu_busy", "fp64_flop_executed_per_launch"):
+        for key in ("kernel_source_hash", "clock_ghz", "valu_busy", "fp64_flop_executed_per_launch",
+                    "fp32_flop_executed_per_launch"):
             if line.startswith(key + ":"):
-                vals[key] = line.split(":", 1)[1].strip()
+                vals[key.replace("fp64_", "").replace("fp32_", "")] = line.split(":", 1)[1].strip()
     if vals.get("kernel_source_hash") != kernel_source_hash(family) or len(vals) < 4:
         return None
     return {"clock_ghz": float(vals["clock_ghz"]), "valu_busy": float(vals["valu_busy"]),
-            "fp64_flop_executed_per_launch": float(vals["fp64_flop_executed_per_launch"]),
+            "flop_executed_per_launch": float(vals["flop_executed_per_launch"]),
             "source": os.path.relpath(path, ROOT)}
 
 
@@ -439,10 +449,11 @@ def main():
     fwd_flop = fwd_flop_per_step(mname, rname, w.dim)
     achieved = flop_step * total_steps / (pass_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
+    ck_used = da.checkpoint_interval(prob, dt)
     traffic = None if args.rhs_source else read_traffic(w.name, kernel_family(mname, rname),
-                                                          args.dense)
-    clk = None if (args.rhs_source or args.dense or args.checkpoint) else \
-        read_valu_clock(w.name, kernel_family(mname, rname))
+                                                          args.dense, ck_used)
+    clk = None if (args.rhs_source or args.dense) else \
+        read_valu_clock(w.name, kernel_family(mname, rname), ck_used)
     log_bytes = (mesh.h.numel() * mesh.h.element_size() + mesh.n_steps.numel() * 4
                  + mesh.save_idx.numel() * 4 + mesh.status.numel() * 4)
     out = {
@@ -454,7 +465,7 @@ def main():
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "n": n, "method": mname, "rhs": rname, "dim": w.dim,
                    "t1": w.t1, "rtol": w.rtol, "atol": w.atol, "max_steps": w.max_steps,
-                   "passes_per_record": passes, "checkpoint": args.checkpoint,
+                   "passes_per_record": passes, "checkpoint": ck_used,
                    "saves": "dense output" if args.dense else "steps land on save times",
                    "rhs_source": "compiled at run time from source, vector-Jacobian products by "
                                  "forward-mode tangents" if args.rhs_source else "built in",
@@ -470,7 +481,7 @@ def main():
             "frac_at_clock": achieved / (256 * 128 * clk["clock_ghz"] / 1e3
                                          * (1 if w.dtype == "f64" else 2)),
             "valu_busy": clk["valu_busy"],
-            "executed_fp64_tflops": clk["fp64_flop_executed_per_launch"] / (pass_ms * 1e-3) / 1e12,
+            "executed_tflops": clk["flop_executed_per_launch"] / (pass_ms * 1e-3) / 1e12,
             "source": clk["source"]},
         "per_pass": {"ms": pass_ms, "median_ms": pass_med,
                      f"total_ms_{passes}_passes": pass_total,

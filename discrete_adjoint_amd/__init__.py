@@ -46,7 +46,7 @@ MAX_SAVES = 128
 EXPORTS = ("da_record", "da_solve_fwd", "da_mesh_h_elems", "da_mesh_sort_workspace", "da_mesh_sort",
            "da_mesh_pad",
            "da_mesh_max_steps", "da_replay_fwd", "da_replay_grad_workspace", "da_replay_grad",
-           "da_replay_grad_noalloc",
+           "da_replay_grad_noalloc", "da_checkpoint_interval",
            "da_replay_sens", "da_replay_sens_dirs", "da_rhs_register", "da_rhs_register_stencil",
            "da_rhs_release", "da_last_error", "da_version")
 
@@ -113,6 +113,8 @@ def _load_library() -> ctypes.CDLL:
     lib.da_replay_fwd.argtypes = [P, i64, vp, vp, M, vp, vp]
     lib.da_replay_grad_workspace.argtypes = [P, i64, i32]
     lib.da_replay_grad_workspace.restype = ctypes.c_size_t
+    lib.da_checkpoint_interval.argtypes = [P]
+    lib.da_checkpoint_interval.restype = ctypes.c_int32
     lib.da_replay_grad.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp, i32, vp,
                                    ctypes.c_size_t, vp]
     lib.da_replay_grad_noalloc.argtypes = [P, i64, vp, vp, M, ctypes.POINTER(_Loss), vp, vp, vp,
@@ -386,6 +388,13 @@ def replay_fwd(prob, u0, p, mesh: Mesh, stream=None) -> torch.Tensor:
 def replay_grad_workspace(prob, n: int, max_n_steps: int, dtype=torch.float64) -> int:
     P, keep = cproblem(prob, dtype)
     return int(_lib.da_replay_grad_workspace(ctypes.byref(P), n, max_n_steps))
+
+
+def checkpoint_interval(prob, dtype=torch.float64) -> int:
+    """The reverse sweep's checkpoint interval for prob (its own, or the
+    library's choice when prob.checkpoint is 0)."""
+    P, keep = cproblem(prob, dtype)
+    return int(_lib.da_checkpoint_interval(ctypes.byref(P)))
 
 
 class ReplayGrad:

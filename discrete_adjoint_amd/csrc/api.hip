@@ -63,9 +63,25 @@ int ws_row_of(int rhs, int dim) {
 }
 
 // Checkpoint interval of the reverse sweep when the caller leaves it to the
-// library.
+// library.  Every kernel family stores states and recomputes the stages from
+// them (storing the stages would move 2 s d values per step through HBM
+// against about s right-hand sides of recomputation, far slower for every
+// built-in system); the interval trades stored states against recomputed
+// steps.  Measured on MI355X (gradient pass, ms, intervals 1 / 2 / 4 / 8):
+//   ROS2, Robertson (d = 3), FP64, 65536 trajectories: 16.6 / 15.4 / 15.9 / 15.8
+//   Rodas3 and the fourth-order method, Robertson:      0.76 / 0.80, 0.67 / 0.73
+//   Dopri5 / Fehlberg 7(8), Lorenz-63 (d = 3), FP64, 2^20: 10.6 / 10.6 / 10.7 / 11.5,
+//                                                         4.9 / 5.5
+//   Tsit5, Lorenz-63, FP32, 65536:                       0.203 / 0.208 / 0.217 / 0.217
+//   Rodas3, kinetics (d = 8), FP64, 65536:               4.04 / 5.40 / 7.44 (spills)
+//   Tsit5, Lorenz-96 (d = 64, wavefront kernel), 16384:  1.23 / 1.32 / 1.37 / 1.41
+// so the interval is 2 for the two-stage ROS2 on systems of up to three
+// components in double precision (the recomputed step in registers gives
+// the scheduler independent work), and 1 (every state stored) everywhere
+// else.
 int default_checkpoint(const da_problem &pb) {
-  (void)pb;
+  if (pb.method == DA_ROS2 && pb.dim <= 3 && pb.dtype == DA_F64 && pb.rhs < DA_RHS_USER_BASE)
+    return 2;
   return 1;
 }
 
@@ -405,6 +421,12 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
   const hipError_t e = launch_replay_fwd(a, s);
   if (e != hipSuccess) return hip_fail(e, "replay_fwd launch");
   return ok();
+}
+
+int32_t da_checkpoint_interval(const da_problem *prob) {
+  if (!prob || prob->checkpoint < 0 || prob->checkpoint > 8) return 0;
+  const int ck = resolved_checkpoint(*prob);
+  return (ck == 1 || ck == 2 || ck == 4 || ck == 8) ? ck : 0;
 }
 
 size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps) {

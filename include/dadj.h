@@ -165,8 +165,9 @@ typedef struct {
                           keeps every checkpoint-th state in the workspace and
                           the sweep recomputes the states in between in
                           registers; 1 = keep every state; 0 = the library's
-                          choice for the right-hand side.  1, 2, 4 or 8 (or
-                          0).  The result does not depend on it.             */
+                          choice: 2 for ROS2 on built-in systems of up to
+                          three components in FP64, else 1.  1, 2, 4 or 8
+                          (or 0).  The result does not depend on it.         */
   int32_t dense;       /* 0: steps land on the save times.  1: dense output
                           ("Differentiable astrophysics at scale",
                           Methodology: the solution is interpolated at the
@@ -320,6 +321,10 @@ int da_replay_fwd(const da_problem *prob, int64_t n, const void *u0, const void 
  * (at least enough for 256 trajectories) makes the call process the
  * ensemble in consecutive chunks; less returns DA_EWORKSPACE. */
 size_t da_replay_grad_workspace(const da_problem *prob, int64_t n, int32_t max_n_steps);
+/* The checkpoint interval da_replay_grad uses for this problem: its
+ * checkpoint field, or the library's choice when that is 0; 0 for a NULL
+ * problem or an interval other than 0, 1, 2, 4, 8. */
+int32_t da_checkpoint_interval(const da_problem *prob);
 int da_replay_grad(const da_problem *prob, int64_t n, const void *u0, const void *p,
                    const da_mesh *mesh, const da_loss *loss, void *loss_out,
                    void *grad_u0, void *grad_p, int32_t max_n_steps, void *workspace,

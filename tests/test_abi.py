@@ -245,6 +245,38 @@ def test_workspace_sizes(da):
     assert da.mesh_sort_workspace(prob, 1 << 20) >= 3 * 4 * (1 << 20)
 
 
+def test_default_checkpoint_interval(da):
+    """The library's checkpoint interval (checkpoint = 0), read from the
+    workspace it asks for: 2 for ROS2 on built-in systems of up to three
+    components in FP64, 1 for every other method, dimension and dtype."""
+    import torch
+
+    def interval(prob, dt=torch.float64, n=1000, N=700):
+        row = 64 if prob.rhs == W.LORENZ96 else prob.dim
+        size = dt.itemsize
+        ws = da.replay_grad_workspace(prob.replace(checkpoint=0), n, N, dt)
+        for ck in (1, 2, 4, 8):
+            if ws == n * ((N + ck - 1) // ck) * row * size:
+                return ck
+        raise AssertionError(ws)
+
+    assert interval(W.WORKLOADS[4].problem()) == 2                     # ROS2, Robertson
+    assert interval(W.WORKLOADS[4].problem(), torch.float32) == 1
+    assert interval(W.WORKLOADS[1].problem(method=W.ROS2)) == 2        # ROS2, Lorenz-63
+    assert interval(W.WORKLOADS[6].problem(method=W.ROS2)) == 1        # ROS2, d = 8
+    for m in (W.RODAS3, W.ROS4):
+        assert interval(W.WORKLOADS[4].problem(method=m)) == 1
+    for wid in (1, 2, 3, 5, 6):
+        assert interval(W.WORKLOADS[wid].problem()) == 1
+    assert interval(W.WORKLOADS[2].problem(method=W.RKF78)) == 1
+    # the entry point that reports it
+    assert da.checkpoint_interval(W.WORKLOADS[4].problem()) == 2
+    assert da.checkpoint_interval(W.WORKLOADS[4].problem(), torch.float32) == 1
+    assert da.checkpoint_interval(W.WORKLOADS[2].problem()) == 1
+    assert da.checkpoint_interval(W.WORKLOADS[2].problem(checkpoint=4)) == 4
+    assert da.checkpoint_interval(W.WORKLOADS[4].problem(checkpoint=3)) == 0
+
+
 def test_step_log_length(da):
     import torch
     lib = da.library()
