@@ -223,6 +223,24 @@ def read_valu_clock(workload_name: str, family: str, interval: int = 1):
             "source": os.path.relpath(path, ROOT)}
 
 
+def record_stats(mesh) -> dict:
+    """Statistics of one record (the review's Strengths quote Table 5's step
+    counts across the ensemble): accepted and rejected trial steps per
+    trajectory (mean, max) and the trajectories per lane status."""
+    import numpy as np
+    ns = mesh.n_steps.cpu().numpy().astype(np.int64)
+    na = mesh.n_attempts.cpu().numpy().astype(np.int64)
+    st = mesh.status.cpu().numpy()
+    rej = na - ns
+    names = ("ok", "max_steps", "dt_underflow", "nonfinite", "max_attempts")
+    hist = {nm: int((st == k).sum()) for k, nm in enumerate(names)}
+    return {"accepted_mean": float(ns.mean()), "accepted_max": int(ns.max()),
+            "accepted_max_over_mean": float(ns.max() / max(ns.mean(), 1e-300)),
+            "rejected_total": int(rej.sum()), "rejected_mean": float(rej.mean()),
+            "rejected_max": int(rej.max()), "reject_rate": float(rej.sum() / max(na.sum(), 1)),
+            "status": hist}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -512,6 +530,7 @@ def main():
                       "trajectory_solves_per_s": n / (float(np.mean(solve_ms)) * 1e-3)},
         "mesh": {"mean_steps": mean_steps, "max_steps": state["N"],
                  "max_over_mean": state["N"] / mean_steps, "failed_lanes": int((st != 0).sum())},
+        "record_stats": record_stats(mesh),
     }
     if args.rhs_source:
         out["rhs_registration_s"] = t_reg

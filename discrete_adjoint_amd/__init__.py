@@ -75,7 +75,7 @@ class _Mesh(ctypes.Structure):
                 ("save_idx", ctypes.c_void_p), ("status", ctypes.c_void_p),
                 ("perm", ctypes.c_void_p), ("h_rows", ctypes.c_void_p),
                 ("rows", ctypes.c_int32), ("save_theta", ctypes.c_void_p),
-                ("defer_pad", ctypes.c_int32)]
+                ("defer_pad", ctypes.c_int32), ("n_attempts", ctypes.c_void_p)]
 
 
 class _RhsDef(ctypes.Structure):
@@ -240,7 +240,8 @@ class Mesh:
     """The record: tiled step log h [T, n, B], n_steps [n], save_idx [S, n],
     status [n]; an optional replay order perm [n] (None = identity) and
     replay table h_rows [rows, n]; save fractions save_theta [S, n] (needed
-    with dense output)."""
+    with dense output); the record's trial steps n_attempts [n] (accepted
+    plus rejected; written by the record when present)."""
     h: torch.Tensor
     n_steps: torch.Tensor
     save_idx: torch.Tensor
@@ -248,6 +249,7 @@ class Mesh:
     perm: Optional[torch.Tensor] = None
     h_rows: Optional[torch.Tensor] = None
     save_theta: Optional[torch.Tensor] = None
+    n_attempts: Optional[torch.Tensor] = None
 
     @property
     def n(self) -> int:
@@ -264,7 +266,8 @@ class Mesh:
                      self.status.data_ptr(), None if self.perm is None else self.perm.data_ptr(),
                      None if self.h_rows is None else self.h_rows.data_ptr(),
                      0 if self.h_rows is None else self.h_rows.shape[0],
-                     None if self.save_theta is None else self.save_theta.data_ptr())
+                     None if self.save_theta is None else self.save_theta.data_ptr(), 0,
+                     None if self.n_attempts is None else self.n_attempts.data_ptr())
 
 
 def mesh_h_shape(prob, n: int, dtype) -> tuple:
@@ -283,7 +286,8 @@ def empty_mesh(prob, n: int, dtype, device="cuda", with_perm: bool = False) -> M
                 torch.empty(n, dtype=torch.int32, device=device),
                 torch.empty(n, dtype=torch.int32, device=device) if with_perm else None,
                 None,
-                torch.empty((S, n), dtype=dtype, device=device))
+                torch.empty((S, n), dtype=dtype, device=device),
+                torch.empty(n, dtype=torch.int32, device=device))
 
 
 def _inputs(prob, u0: torch.Tensor, p: torch.Tensor):
@@ -350,12 +354,82 @@ def mesh_sort(prob, mesh: Mesh, perm: Optional[torch.Tensor] = None, table: bool
     need = mesh_sort_workspace(prob, n, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    out = Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, perm, h_rows, mesh.save_theta)
+    out = Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, perm, h_rows, mesh.save_theta,
+               mesh.n_attempts)
     P, keep = cproblem(prob, dt)
     co = out.c()
     _check(_lib.da_mesh_sort(ctypes.byref(P), n, ctypes.byref(co), _ptr(workspace),
                              workspace.numel(), _stream(stream)))
     return out
+
+
+# Mesh files: a numpy .npz archive of plain arrays (no pickled objects).
+MESH_FORMAT = 1
+# problem fields a record depends on: a mesh is replayed only under these
+_MESH_KEYS = ("rhs", "dim", "n_params", "method", "t0", "t1", "max_steps", "dense")
+
+
+def save_mesh(path, prob, mesh: Mesh) -> None:
+    """Write the record to `path` (.npz): the tiled step log, n_steps,
+    save_idx, status, save_theta, n_attempts and the replay order when set
+    (the replay table is rebuilt on load), with the problem fields it
+    depends on (right-hand side, dimensions, method, interval, save times,
+    max_steps, dense output) and the dtype.  The record is the artefact that
+    is replayed for many gradient passes until a re-record, so it can be kept
+    across processes."""
+    import numpy as np
+    arrays = {"format": np.int64(MESH_FORMAT),
+              "dtype": np.array(str(mesh.h.dtype).replace("torch.", "")),
+              "save_times": np.asarray(prob.save_times, dtype=np.float64),
+              "h": mesh.h.cpu().numpy(), "n_steps": mesh.n_steps.cpu().numpy(),
+              "save_idx": mesh.save_idx.cpu().numpy(), "status": mesh.status.cpu().numpy()}
+    for k in _MESH_KEYS:
+        arrays["prob_" + k] = np.asarray(getattr(prob, k))
+    for k in ("save_theta", "n_attempts", "perm"):
+        t = getattr(mesh, k)
+        if t is not None:
+            arrays[k] = t.cpu().numpy()
+    with open(path, "wb") as f:
+        np.savez(f, **arrays)
+
+
+def load_mesh(path, prob, device="cuda", table: bool = True) -> Mesh:
+    """Read a record written by save_mesh and check it against `prob` (the
+    fields it depends on, the save times and the array shapes).  With a
+    stored replay order and `table`, the replay table is rebuilt on a GPU
+    device (da_mesh_sort, which recomputes the order; it must equal the
+    stored one).  Raises ValueError on any mismatch."""
+    import numpy as np
+    with np.load(path, allow_pickle=False) as z:
+        d = {k: z[k] for k in z.files}
+    if int(d.get("format", -1)) != MESH_FORMAT:
+        raise ValueError(f"{path}: not a mesh file of format {MESH_FORMAT}")
+    for k in _MESH_KEYS:
+        want, got = getattr(prob, k), d["prob_" + k].item()
+        if want != got:
+            raise ValueError(f"{path}: recorded with {k} = {got}, the problem has {want}")
+    if not np.array_equal(d["save_times"], np.asarray(prob.save_times, dtype=np.float64)):
+        raise ValueError(f"{path}: recorded with other save times")
+    dt = {"float64": torch.float64, "float32": torch.float32}[str(d["dtype"])]
+    n = d["n_steps"].shape[0]
+    S = max(1, len(prob.save_times))
+    shapes = {"h": mesh_h_shape(prob, n, dt), "save_idx": (S, n), "status": (n,),
+              "save_theta": (S, n), "n_attempts": (n,), "perm": (n,)}
+    for k, shp in shapes.items():
+        if k in d and tuple(d[k].shape) != tuple(shp):
+            raise ValueError(f"{path}: {k} has shape {d[k].shape}, expected {shp}")
+
+    def dev(k):
+        return None if k not in d else torch.from_numpy(np.ascontiguousarray(d[k])).to(device)
+    mesh = Mesh(dev("h"), dev("n_steps"), dev("save_idx"), dev("status"), dev("perm"), None,
+                dev("save_theta"), dev("n_attempts"))
+    if mesh.perm is not None and table and torch.device(device).type == "cuda":
+        sm = mesh_sort(prob, Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, None, None,
+                                  mesh.save_theta, mesh.n_attempts))
+        if not torch.equal(sm.perm, mesh.perm):
+            raise ValueError(f"{path}: the stored replay order is not the record's")
+        mesh = sm
+    return mesh
 
 
 def mesh_pad(prob, mesh: Mesh, stream=None) -> None:

@@ -306,6 +306,7 @@ int da_record(const da_problem *prob, int64_t n, const void *u0, const void *p, 
   a.status = mesh->status;
   a.y_save = y_save;
   a.defer_pad = mesh->defer_pad != 0;
+  a.natt = mesh->n_attempts;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = launch_record(a, st, s);
   if (e != hipSuccess) return hip_fail(e, "record launch");
@@ -331,6 +332,7 @@ int da_solve_fwd(const da_problem *prob, int64_t n, const void *u0, const void *
   a.theta = nullptr;
   a.status = status;
   a.defer_pad = 0;
+  a.natt = nullptr;
   a.y_save = y_save;
   hipStream_t s = (hipStream_t)stream;
   const hipError_t e = launch_record(a, st, s);

@@ -52,6 +52,7 @@ struct RecordArgs {
   int32_t *status;      // [n] or null
   void *y_save;         // [S][d][n] or null
   int32_t defer_pad;    // leave the chunks after each trajectory's last one
+  int32_t *natt;        // [n] trial steps (accepted + rejected), or null
 };
 
 struct ReplayArgs {

@@ -325,6 +325,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     }
     if (a.nsteps) a.nsteps[i] = nacc;
     if (a.status) a.status[i] = st;
+    if (a.natt) a.natt[i] = natt;
     if (LOG && nacc % B != 0) store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
   }
   if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)

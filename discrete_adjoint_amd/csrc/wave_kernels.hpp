@@ -476,6 +476,7 @@ __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes 
   if (c == 0) {
     if (a.nsteps) a.nsteps[i] = nacc;
     if (a.status) a.status[i] = st;
+    if (a.natt) a.natt[i] = natt;
   }
   if (LOG) {
     // the partial chunk, then zero chunks to the end of the log, B lanes per

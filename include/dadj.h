@@ -238,6 +238,12 @@ typedef struct {
                         da_mesh_sort read no chunk past a trajectory's last
                         step, so they need not wait for it.  0: da_record
                         writes the zeros itself.                             */
+  int32_t *n_attempts; /* [n] trial steps of the record (accepted + rejected:
+                        rejections = n_attempts - n_steps), written by
+                        da_record when not NULL; the replays do not read
+                        it.  The record statistics the review's Strengths
+                        quote (Table 5: step counts across the ensemble)
+                        come from n_steps and this.                          */
 } da_mesh;
 
 /* Elements (of the problem's dtype) of the step log of n trajectories:

@@ -33,15 +33,27 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 LANE_OK, LANE_MAX_STEPS, LANE_DT_UNDERFLOW, LANE_NONFINITE, LANE_MAX_ATTEMPTS = range(5)
 
 
-def build(force: bool = True) -> str:
-    """Compile oracle.cpp into liboracle.so (g++, -O2, no fp contraction, OpenMP)."""
-    if force or not os.path.exists(_LIB):
-        tmp = _LIB + ".tmp"
+# A library to load instead of liboracle.so (the sanitizer build, in a
+# process that preloads the sanitizer runtime).
+_ENV_LIB = "ORACLE_LIBRARY"
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build(force: bool = True, sanitize: bool = False) -> str:
+    """Compile oracle.cpp into liboracle.so (g++, -O2, no fp contraction,
+    OpenMP).  With `sanitize`, into liboracle_san.so with AddressSanitizer
+    and UndefinedBehaviorSanitizer (every report fatal); a process loads it
+    through ORACLE_LIBRARY with the ASan runtime preloaded."""
+    out = _SAN_LIB if sanitize else _LIB
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp"
         cmd = ["g++", "-O2", "-std=c++17", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
-               "-fPIC", "-shared", "-Wall", "-o", tmp, _SRC]
+               "-fPIC", "-shared", "-Wall", *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, _SRC]
         subprocess.run(cmd, check=True)
-        os.replace(tmp, _LIB)
-    return _LIB
+        os.replace(tmp, out)
+    return out
 
 
 class _Problem(ctypes.Structure):
@@ -63,9 +75,12 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build(force=True)
-        _lib = ctypes.CDLL(_LIB)
+        path = os.environ.get(_ENV_LIB)
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB):
+                build(force=True)
+        _lib = ctypes.CDLL(path)
         _lib.orc_ros2_gamma.restype = ctypes.c_double
     return _lib
 

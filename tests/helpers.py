@@ -156,3 +156,16 @@ def plain_gap_gate(orc, prob, u0, p, mesh, lk, aux, scale, g1, g2, go, po, facto
     _, gop, pop = orc.replay_grad(prob, u0, p, mesh, lk, aux=aux, scale=scale, fused=False)
     gap = grad_elem_err(go, po, gop, pop).max()
     return grad_elem_err(g1, g2, gop, pop).max(), factor * gap
+
+
+def attempt_count_gate(orc, prob, u0, p, natt_ref, eps=1e-7, fused=True):
+    """As step_count_gate, for the record's trial steps (accepted plus
+    rejected): max(2, 1% of the oracle's count), widened to the largest
+    change of any trajectory's count under the same perturbation of the
+    step factor.  Returns the bound and that spread."""
+    spread = 0
+    for s in (1.0 + eps, 1.0 - eps):
+        pr = prob.replace(safety=(prob.safety or 0.9) * s)
+        m = orc.record(pr, u0, p, fused=fused, with_h=False)
+        spread = max(spread, int(np.max(np.abs(m["n_attempts"] - natt_ref))))
+    return np.maximum(np.maximum(2, 0.01 * natt_ref), spread), spread

@@ -24,8 +24,8 @@ import numpy as np
 import pytest
 
 import workloads as W
-from helpers import (aux_to_dev, elem_err, fp32_against_fp64, grad_elem_err, grad_rel_err,
-                     mesh_to_dev, mesh_to_host, mse_targets, rel_err, smallest_component,
+from helpers import (attempt_count_gate, aux_to_dev, elem_err, fp32_against_fp64, grad_elem_err,
+                     grad_rel_err, mesh_to_dev, mesh_to_host, mse_targets, smallest_component,
                      step_count_gate, to_dev)
 
 torch = pytest.importorskip("torch")
@@ -147,6 +147,14 @@ def test_record_within_tolerance_of_oracle(da, orc, wid, n):
                f"{spread}; bitwise-equal meshes {same.mean():.4f}; mean steps gpu {ng.mean():.2f} "
                f"oracle {no.mean():.2f}")
         assert np.all(dn <= gate)
+        # trial steps: at least the accepted ones, within the same kind of gate
+        ag = mesh.n_attempts.cpu().numpy()
+        ao = mo["n_attempts"]
+        agate, aspread = attempt_count_gate(orc, prob, inp["u0"], inp["p"], ao, fused=fused)
+        _print(f"    trial steps: mean gpu {ag.mean():.2f} oracle {ao.mean():.2f}, max |dA| "
+               f"{np.abs(ag - ao).max()} (spread {aspread}); rejected per trajectory "
+               f"{(ag - ng).mean():.2f}")
+        assert np.all(ag >= ng) and np.all(np.abs(ag - ao) <= agate)
         if fused:
             mfused = mo
     # zero padding after the last step, to the end of the tiled log
@@ -425,6 +433,32 @@ def test_solve_fwd_against_oracle(da, orc, wid, n, t_short):
             assert np.all(dn <= gate)
             if wid in (1, 4) or k == 1:
                 assert ratio.max() <= 1.0
+
+
+@pytest.mark.parametrize("wid,n", [(2, 1000), (3, 777), (4, 300), (5, 120)])
+def test_saved_mesh_replays_bitwise(da, orc, wid, n, tmp_path):
+    """A record (with its replay order) written to a file and read back gives
+    the same replay table and, replayed, the same saves, loss and gradients
+    bit for bit; the attempt counts survive the round trip."""
+    w, prob, inp, aux, scale = _setup(orc, wid, n)
+    _print(f"case: saved mesh, workload {wid}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    auxd = None if aux is None else aux_to_dev(aux, torch)
+    mesh, _ = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    path = tmp_path / "mesh.npz"
+    da.save_mesh(path, prob, sm)
+    lm = da.load_mesh(path, prob)
+    a = da.replay_grad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)
+    b = da.replay_grad(prob, u0, p, lm, w.loss, aux=auxd, scale=scale)
+    fa, fb = da.replay_fwd(prob, u0, p, sm), da.replay_fwd(prob, u0, p, lm)
+    torch.cuda.synchronize()
+    assert torch.equal(lm.h_rows, sm.h_rows) and torch.equal(lm.perm, sm.perm)
+    assert torch.equal(lm.n_attempts, mesh.n_attempts)
+    for x, y in zip(a + (fa,), b + (fb,)):
+        assert torch.equal(x, y)
+    with pytest.raises(ValueError):
+        da.load_mesh(path, prob.replace(max_steps=prob.max_steps + 1))
 
 
 @pytest.mark.parametrize("wid", [3, 4, 5])
