@@ -62,22 +62,53 @@ struct Erk {
     for (int i = 0; i < D; ++i) y[i] = Y[6][i];
   }
 
+  // The reverse sweep runs on two wavefronts for small ensembles
+  // (k_replay_grad2): one recomputes the stages (pre), one runs the adjoint
+  // (adj_pre).
+  static constexpr bool two_wave_reverse = true;
+
+  // What the reverse of one step needs from its forward recomputation: the
+  // state y_k and the stage states Y_1..Y_5, in v = (y, Y_1, ..., Y_5).
+  template <class T> struct Pre {
+    static constexpr int NV = 6 * D;
+    T v[NV];
+    int bits;
+  };
+  template <class T>
+  __device__ static __forceinline__ void pre(const T (&y)[D], const T *p, T h, Pre<T> &q) {
+    T Y[7][D], K[7][D];
+    Rhs::f(y, p, K[0]);
+    erk_stages<Tab, Rhs, 5, false>(y, p, h, Y, K);
+#pragma unroll
+    for (int c = 0; c < D; ++c) q.v[c] = y[c];
+#pragma unroll
+    for (int i = 1; i <= 5; ++i)
+#pragma unroll
+      for (int c = 0; c < D; ++c) q.v[i * D + c] = Y[i][c];
+    q.bits = 0;
+  }
+
   // Reverse of fwd at y = y_k: lam (dL/dy_{k+1} -> dL/dy_k), g += dL/dp.
   //   kbar_i = h (b_i lam + sum_{l>i} a[l][i] w_l),  w_i = J(Y_i)^T kbar_i,
   //   g += J_p(Y_i)^T kbar_i,  lam <- lam + w_5 + w_4 + ... + w_0.
-  // Stage states Y_1..Y_5 are recomputed from y_k; the stage slopes are dead
-  // once the states are formed, and the w_i are summed into lam at the end
-  // in the order of the formula.
+  // Stage states Y_1..Y_5 are recomputed from y_k (pre); the stage slopes
+  // are dead once the states are formed, and the w_i are summed into lam at
+  // the end in the order of the formula.
   template <class T>
   __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
-    T Y[7][D], Wv[7][D], kb[D];
-    {
-      T K[7][D];
-      Rhs::f(y, p, K[0]);
-      erk_stages<Tab, Rhs, 5, false>(y, p, h, Y, K);
-    }
+    Pre<T> q;
+    pre(y, p, h, q);
+    adj_pre(q, p, h, lam, g);
+  }
+
+  template <class T>
+  __device__ static __forceinline__ void adj_pre(const Pre<T> &q, const T *p, T h, T (&lam)[D],
+                                                 T *g) {
+    T Y[6][D], Wv[7][D], kb[D];
 #pragma unroll
-    for (int c = 0; c < D; ++c) Y[0][c] = y[c];
+    for (int i = 0; i <= 5; ++i)
+#pragma unroll
+      for (int c = 0; c < D; ++c) Y[i][c] = q.v[i * D + c];
 #pragma unroll
     for (int i = 5; i >= 0; --i) {
 #pragma unroll

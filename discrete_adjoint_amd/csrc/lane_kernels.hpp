@@ -753,6 +753,218 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 }
 
 // ---------------------------------------------------------------------------
+// The replay gradient with two wavefronts per 64 trajectories, for ensembles
+// that give the one-wavefront kernel about one wavefront per SIMD (65536
+// trajectories), where a step's serial chain of dependent operations leaves
+// the SIMD idle most of the time.
+//  - Forward replay: each wavefront replays 32 of the 64 trajectories
+//    (storing every state), so both are busy wherever the hardware places
+//    them; the final seeds, loss sums and save cursors then pass through LDS.
+//  - Reverse sweep: the first wavefront runs the adjoint of all 64 while the
+//    second recomputes the forward stages of each step (M::pre) one step
+//    ahead and hands them over through LDS, so that the recomputation of
+//    step k - 1 runs beside the adjoint of step k (M::adj_pre).
+// Checkpoint interval 1, no dense output.  The arithmetic is that of
+// k_replay_grad<T, M, 1, ROWS, false> (M::adj is M::pre followed by
+// M::adj_pre), so the results are the same bit for bit.  Both wavefronts
+// pass the same barriers: the reverse sweep's trip count is the maximum over
+// the same 64 trajectories in both.
+// ---------------------------------------------------------------------------
+template <class T, class M, bool ROWS>
+__global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
+  using Rhs = typename M::Rhs;
+  using Q = typename M::template Pre<T>;
+  constexpr int D = Rhs::D, P = Rhs::P, NV = Q::NV;
+  __shared__ T qv[2][NV][64];
+  __shared__ T qh[2][64];
+  __shared__ int qb[2][64];
+  __shared__ T hand[D + 1][64];  // forward -> reverse: lam, loss sum
+  __shared__ int handi[2][64];   // save cursor: sh, hidx
+  const int lane = (int)(threadIdx.x & 63);
+  const int wv = (int)(threadIdx.x >> 6);
+  const bool helper = wv == 1;  // wavefront-uniform
+  const int64_t n = a.n;
+  const int64_t C = a.ws_lanes;
+  const int S = a.pr.S;
+  const int lk = a.loss_kind;
+  const bool saves = lk != DA_LOSS_SUMSQ_FINAL;
+  const T *aux = (const T *)a.aux;
+
+  // ---- forward replay: slot t = 32 wv + lane of the workgroup's 64 ----
+  {
+    const int t = 32 * wv + lane;
+    const int64_t jl = (int64_t)blockIdx.x * 64 + t;
+    const bool live = lane < 32 && jl < a.nslots;
+    const int64_t j = a.slot0 + jl;
+    T *ws = (T *)a.ws + (live ? jl : 0);
+    const LaneInfo L = lane_info(a, j, live, a.max_n_steps, true);
+    const int64_t tr = L.tr;
+    const int N = L.N;
+    const bool ok = L.ok;
+    StepSrc<T, ROWS> src;
+    src.init(a, live ? j : a.slot0, tr);
+    T y[D], p[P];
+    if (live) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) y[c] = ((const T *)a.u0)[c * n + tr];
+#pragma unroll
+      for (int q = 0; q < P; ++q) p[q] = ((const T *)a.p)[q * n + tr];
+    }
+    const int Nw = wave_max(N);
+    T ss = T(0);
+    bool first = true;
+    int s = 0;
+    int nxt = (ok && saves) ? a.sidx[tr] : -1;
+    auto terms = [&](int k) {
+      while (s < S && nxt == k) {
+        loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
+        ++s;
+        nxt = s < S ? a.sidx[s * n + tr] : -1;
+      }
+    };
+    if (saves) terms(0);
+    auto fstep = [&](int k, T hk) {
+      if (k < N) {
+        T *wk = ws + (int64_t)k * D * C;
+#pragma unroll
+        for (int c = 0; c < D; ++c) wk[c * C] = y[c];
+        M::fwd(y, p, hk);
+        if (saves) terms(k + 1);
+      }
+    };
+    T hA = src.load(0);
+    for (int k = 0; k < Nw; k += 2) {
+      const T hB = src.load(k + 1);
+      fstep(k, hA);
+      hA = src.load(k + 2);
+      if (k + 1 < Nw) fstep(k + 1, hB);
+    }
+    // loss and seeds at the final state
+    T lam[D];
+    if (!saves) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) ss = (c == 0) ? y[c] * y[c] : mac(y[c], y[c], ss);
+#pragma unroll
+      for (int c = 0; c < D; ++c) lam[c] = T(2.0 * a.scale) * y[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < D; ++c) lam[c] = T(0);
+    }
+    int sh = S - 1;
+    int hidx = (ok && saves) ? a.sidx[(int64_t)sh * n + tr] : -1;
+    if (saves) {
+      while (sh >= 0 && hidx == N) {
+        seed_terms<T, D>(lk, y, aux, n, sh, tr, a.scale, lam);
+        --sh;
+        hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+      }
+    }
+    if (lane < 32) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) hand[c][t] = lam[c];
+      hand[D][t] = ss;
+      handi[0][t] = sh;
+      handi[1][t] = hidx;
+    }
+  }
+  __syncthreads();  // every state stored (and visible to both), seeds handed over
+
+  // ---- reverse sweep: lane = slot t; the helper prepares step Nw - 1 - i
+  // while the first wavefront reverses step Nw - i (prepared the round before)
+  const int64_t jl = (int64_t)blockIdx.x * 64 + lane;
+  const bool live = jl < a.nslots;
+  const int64_t j = a.slot0 + jl;
+  T *ws = (T *)a.ws + (live ? jl : 0);
+  const LaneInfo L = lane_info(a, j, live, a.max_n_steps, true);
+  const int64_t tr = L.tr;
+  const int N = L.N;
+  const bool ok = L.ok;
+  StepSrc<T, ROWS> src;
+  src.init(a, live ? j : a.slot0, tr);
+  T p[P];
+  if (live) {
+#pragma unroll
+    for (int q = 0; q < P; ++q) p[q] = ((const T *)a.p)[q * n + tr];
+  }
+  const int Nw = wave_max(N);
+  T lam[D], g[P], ss = T(0);
+  int sh = -1, hidx = -1;
+#pragma unroll
+  for (int q = 0; q < P; ++q) g[q] = T(0);
+  if (!helper) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) lam[c] = hand[c][lane];
+    ss = hand[D][lane];
+    sh = handi[0][lane];
+    hidx = handi[1][lane];
+  }
+  T yn[D], hn = T(0);  // helper: the next step's state and size, loaded ahead
+  if (helper && Nw > 0) {
+#pragma unroll
+    for (int c = 0; c < D; ++c) yn[c] = ws[((int64_t)(Nw - 1) * D + c) * C];
+    hn = src.load(Nw - 1);
+  }
+  for (int i = 0; i <= Nw; ++i) {
+    if (helper) {
+      const int k = Nw - 1 - i;
+      if (k >= 0) {
+        T yk[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) yk[c] = yn[c];
+        const T hk = hn;
+        const int kn = k > 0 ? k - 1 : 0;
+#pragma unroll
+        for (int c = 0; c < D; ++c) yn[c] = ws[((int64_t)kn * D + c) * C];
+        hn = src.load(kn);
+        Q q;
+        if (k < N) {
+          M::pre(yk, p, hk, q);
+        } else {
+#pragma unroll
+          for (int v = 0; v < NV; ++v) q.v[v] = T(0);
+          q.bits = 0;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) qv[k & 1][v][lane] = q.v[v];
+        qh[k & 1][lane] = hk;
+        qb[k & 1][lane] = q.bits;
+      }
+    } else {
+      const int k = Nw - i;
+      if (k < Nw && k < N) {
+        Q q;
+#pragma unroll
+        for (int v = 0; v < NV; ++v) q.v[v] = qv[k & 1][v][lane];
+        q.bits = qb[k & 1][lane];
+        M::adj_pre(q, p, qh[k & 1][lane], lam, g);
+        if (saves) {
+          while (sh >= 0 && hidx == k) {
+            T yk[D];
+#pragma unroll
+            for (int c = 0; c < D; ++c) yk[c] = q.v[c];
+            seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
+            --sh;
+            hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  if (live && !helper) {
+    const T Lv = ok ? T(a.scale) * ss : nanv<T>();
+    if (a.loss_out) ((T *)a.loss_out)[tr] = Lv;
+    if (a.gu0)
+#pragma unroll
+      for (int c = 0; c < D; ++c) ((T *)a.gu0)[c * n + tr] = ok ? lam[c] : nanv<T>();
+    if (a.gp)
+#pragma unroll
+      for (int q = 0; q < P; ++q) ((T *)a.gp)[q * n + tr] = ok ? g[q] : nanv<T>();
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 #ifndef __HIPCC_RTC__
@@ -794,8 +1006,32 @@ hipError_t replay_fwd_t(const ReplayArgs &a, hipStream_t s) {
   return replay_fwd_d<T, M, false>(a, s);
 }
 
+// Methods whose reverse step is split into M::pre and M::adj_pre and that
+// take the two-wavefront gradient kernel (M::two_wave_reverse).
+template <class...> struct VoidT { typedef void type; };
+template <class M, class = void> struct TwoWave { static constexpr bool value = false; };
+template <class M>
+struct TwoWave<M, typename VoidT<decltype(M::two_wave_reverse)>::type> {
+  static constexpr bool value = M::two_wave_reverse;
+};
+
+// Ensembles of at most this many trajectories (one wavefront per SIMD for
+// the one-wavefront kernel) take the two-wavefront gradient kernel.
+// Measured (gradient pass): Tsit5 on Lorenz-63, FP32, 65536 trajectories
+// 0.189 against 0.203 ms; FP64, 1024 trajectories 0.044 against 0.047 ms;
+// Dopri5 on Lorenz-63, FP64, 2^20 trajectories 13.8 against 10.5 ms (the
+// one-wavefront kernel already runs three wavefronts per SIMD there).
+constexpr int64_t TWO_WAVE_MAX_LANES = 65536;
+
 template <class T, class M, bool ROWS, bool DENSE>
 hipError_t replay_grad_ck(const ReplayArgs &a, hipStream_t s) {
+  if constexpr (TwoWave<M>::value && !DENSE && M::D <= 4) {
+    if (a.pr.checkpoint == 1 && a.nslots <= TWO_WAVE_MAX_LANES) {
+      const unsigned grid2 = (unsigned)((a.nslots + 63) / 64);
+      hipLaunchKernelGGL((k_replay_grad2<T, M, ROWS>), grid2, 128, 0, s, a);
+      return hipGetLastError();
+    }
+  }
   const unsigned grid = (unsigned)((a.nslots + BLOCK - 1) / BLOCK);
   switch (a.pr.checkpoint) {
     case 1: hipLaunchKernelGGL((k_replay_grad<T, M, 1, ROWS, DENSE>), grid, BLOCK, 0, s, a); break;
