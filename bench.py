@@ -34,7 +34,13 @@ Printed on one JSON line, besides the driver's fields:
                 gradient) on the job's replay order and table, with its
                 algorithmic FLOP rate (the forward part of flop_per_step);
   cpu_baseline  the CPU oracle (plain C++, OpenMP) on a bounded sample of the
-                same workload, as trajectory-gradients/s of the same job.
+                same workload, as trajectory-gradients/s of the same job;
+  record_stats  accepted and rejected trial steps per trajectory and the
+                trajectories per lane status of the record;
+  other_workloads  (default run only) one job of each other gradient
+                workload at its full size, timed after the headline: job and
+                gradient-pass times, and the pass's algorithmic rate against
+                its dtype's vector peak.
 
 --gpus N with N > 1 is not supported (this build runs on one GPU).
 """
@@ -303,6 +309,71 @@ def copy_probe(gib: float = 1.0):
     print(json.dumps({"copy_probe_bytes_each_way": n * 8, "launches": 3}))
 
 
+# The other gradient workloads, timed after the headline in the default run so
+# that the driver's record holds them too: (workload, method or None).
+OTHER_WORKLOADS = ((1, None), (3, None), (4, None), (4, "rodas3"), (4, "ros4"), (5, None),
+                   (6, None), (2, "rkf78"))
+
+
+def other_workloads(da, W, torch, np, steps: int = 2, warmup: int = 1) -> list:
+    """One job each (record, lane ordering with the replay table, one
+    gradient pass) of the other workloads at their full sizes, `warmup` + `steps`
+    times: job time and gradient-pass time from HIP events on the launch
+    stream, and the pass's algorithmic rate against its dtype's vector peak."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    out = []
+    for wid, method in OTHER_WORKLOADS:
+        w = W.WORKLOADS[wid]
+        if method is not None:
+            code = {"rodas3": W.RODAS3, "ros4": W.ROS4, "rkf78": W.RKF78}[method]
+            old = W.METHOD_NAMES[w.method]
+            w = dataclasses.replace(w, method=code, name=w.name.replace(old, method))
+        prob = w.problem()
+        inp = W.make_inputs(wid)
+        u0 = torch.from_numpy(np.ascontiguousarray(inp["u0"].T)).to(dev)
+        p = torch.from_numpy(np.ascontiguousarray(inp["p"].T)).to(dev)
+        n, dt = w.n, u0.dtype
+        aux, scale = None, 1.0
+        if w.loss == W.MSE_SAVE:
+            pt = torch.from_numpy(np.ascontiguousarray(inp["p_true"].T.astype(inp["p"].dtype)))
+            aux = torch.nan_to_num(da.solve_fwd(prob, u0, pt.to(dev))[0])
+            scale = 1.0 / (n * w.n_save_eff * w.dim)
+        mesh = da.empty_mesh(prob, n, dt, dev, with_perm=True)
+        job_ms, pass_ms = [], []
+        for r in range(warmup + steps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+            e[0].record(stream)
+            da.record(prob, u0, p, mesh=mesh, save=False)
+            sm = da.mesh_sort(prob, mesh, perm=mesh.perm)
+            call = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=aux, scale=scale,
+                                 max_n_steps=sm.h_rows.shape[0])
+            e[1].record(stream)
+            call()
+            e[2].record(stream)
+            torch.cuda.synchronize()
+            if r >= warmup:
+                job_ms.append(e[0].elapsed_time(e[2]))
+                pass_ms.append(e[1].elapsed_time(e[2]))
+        ns = mesh.n_steps.double()
+        ok = torch.from_numpy(mesh.status.cpu().numpy() == 0).to(dev)
+        total_steps = float(ns[ok].sum().item())
+        mname, rname = W.METHOD_NAMES[w.method], W.RHS_NAMES[w.rhs]
+        fps = flop_per_step(mname, rname, w.dim)
+        pm = sum(pass_ms) / len(pass_ms)
+        achieved = fps * total_steps / (pm * 1e-3) / 1e12
+        out.append({"workload": w.name, "dtype": w.dtype, "n": n,
+                    "checkpoint": da.checkpoint_interval(prob, dt),
+                    "job_ms": sum(job_ms) / len(job_ms), "pass_ms": pm,
+                    "trajectory_gradients_per_s": n / (pm * 1e-3),
+                    "achieved_tflops": achieved, "peak": PEAK_TFLOPS[w.dtype],
+                    "frac": achieved / PEAK_TFLOPS[w.dtype], "flop_per_step": fps,
+                    "mean_steps": float(ns.mean().item())})
+        del mesh, sm, call, u0, p, aux
+        torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -325,6 +396,9 @@ def main():
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
+    ap.add_argument("--no-others", action="store_true",
+                    help="skip the other workloads that the default run times after the "
+                         "headline")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU mode (trajectories "
@@ -534,6 +608,10 @@ def main():
     }
     if args.rhs_source:
         out["rhs_registration_s"] = t_reg
+    default_run = (args.workload == 2 and args.method is None and not args.rhs_source
+                   and not args.dense and not args.checkpoint)
+    if default_run and not args.no_others:
+        out["other_workloads"] = other_workloads(da, W, torch, np)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
                                            dense=int(args.dense), method=w.method)
