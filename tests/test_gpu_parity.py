@@ -743,3 +743,29 @@ def test_inline_padding(da, wid, n, max_steps):
     assert np.all(h[k < ns[:, None]] != 0)
     assert np.all(h[k >= ns[:, None]] == 0)
     assert np.all(m1.h.cpu().numpy().transpose(1, 0, 2).reshape(n, -1)[:, max_steps:] == 0)
+
+
+def test_two_wavefront_kernel_boundary(da, orc):
+    """Explicit pairs with interval 1 run the two-wavefront gradient kernel
+    up to 65536 trajectories and the one-wavefront kernel above: the first
+    65536 trajectories of a 65537-trajectory ensemble give the same loss and
+    gradients bit for bit as the 65536-trajectory ensemble alone (FP32
+    calibration workload, MSE at the saves)."""
+    w = W.WORKLOADS[3]
+    n = w.n + 1
+    prob = w.problem()
+    inp = W.make_inputs(3, n)
+    aux, st = mse_targets(orc, 3, n, inp)
+    assert np.all(st == 0)
+    scale = 1.0 / (w.n * w.n_save_eff * w.dim)
+    _print(f"case: two-wavefront kernel boundary, n={w.n} and {n}")
+    outs = []
+    for m in (w.n, n):
+        u0, p = to_dev(inp["u0"][:m], torch), to_dev(inp["p"][:m], torch)
+        mesh, _ = da.record(prob, u0, p, save=False)
+        sm = da.mesh_sort(prob, mesh)
+        outs.append(da.replay_grad(prob, u0, p, sm, W.MSE_SAVE,
+                                   aux=aux_to_dev(aux[:m], torch), scale=scale))
+        torch.cuda.synchronize()
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a, b[..., :w.n])
