@@ -4,8 +4,8 @@ Gates on the gradients of a shared (oracle-recorded) mesh, every one element
 by element (each component of grad_u0 and grad_p against its own value, the
 smallest included; no absolute floor):
  - against the oracle's fused-rounding mode, which evaluates the kernels'
-   written arithmetic schedule: <= 1e-12 in FP64, <= 1e-4 in FP32 (the
-   north star's figures; they hold against this twin of the schedule);
+   written arithmetic schedule: <= 1e-12 in FP64, <= 1e-4 in FP32 (figures
+   that hold against this twin of the schedule);
  - against the oracle's plain-rounding mode (every operation rounded on its
    own, textbook controller), which shares no arithmetic order with the
    kernels: FP64 <= PLAIN_TOL, four times the largest gap the oracle's two
