@@ -176,10 +176,10 @@ def test_method_against_oracle(da, orc, name, prob, wid, lk, n):
     assert es.max() <= 1e-12 and ef.max() <= 1e-12 and ea.max() <= 1e-10
 
 
-@pytest.mark.parametrize("method", [W.RODAS3, W.ROS4], ids=["rodas3", "ros4"])
+@pytest.mark.parametrize("method", [W.ROS2, W.RODAS3, W.ROS4], ids=["ros2", "rodas3", "ros4"])
 def test_rosenbrock4_fp32(da, orc, method):
-    """FP32 four-stage Rosenbrock methods on Robertson against the FP64 oracle
-    on the FP32 mesh."""
+    """FP32 Rosenbrock methods (ROS2 and the four-stage ones) on Robertson
+    against the FP32 oracle and the FP64 oracle on the FP32 mesh."""
     prob = W.WORKLOADS[4].problem(method=method, t1=100.0, rtol=1e-4, atol=1e-8)
     n = 256
     inp = {k: v.astype(np.float32) for k, v in W.make_inputs(4, n).items()}

@@ -305,7 +305,7 @@ def test_loss_kinds_and_cotangents(da, orc):
         assert np.allclose(loss.cpu().numpy(), lo, rtol=1e-12)
 
 
-@pytest.mark.parametrize("dim", [64, 40, 5])
+@pytest.mark.parametrize("dim", [64, 40, 5, 4])
 def test_lorenz96_losses_and_dimensions(da, orc, dim):
     """Lorenz-96 on the wavefront kernels: dimensions that fill a wavefront or
     not, cotangent and MSE losses at several save times, Dopri5 as well."""
