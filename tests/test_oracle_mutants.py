@@ -89,6 +89,11 @@ MUTANTS = {
     "ros4_fourth_stage_at_wrong_point": ("t.a[3][0] = 48.0 / 25.0; t.a[3][1] = 6.0 / 25.0;",
                                          "t.a[3][0] = 48.0 / 25.0; t.a[3][2] = 6.0 / 25.0;"),
     "ros4_error_weight": ("t.e[0] = 17.0 / 54.0;", "t.e[0] = 19.0 / 54.0;"),
+    "landing_next_step_from_unshortened_proposal": (
+        "h = hs * fac;\n        after_reject = false;",
+        "h = (land ? h : hs) * fac;\n        after_reject = false;"),
+    "plain_controller_power_in_single_precision": (
+        "  return std::pow(E, expo);", "  return T(std::exp2(float(expo) * std::log2(float(E))));"),
     "kinetics8_contraction_flipped": (
         "auto M = [&](int b) { return Jb[k.dst * 8 + b] - Jb[k.src * 8 + b]; };",
         "auto M = [&](int b) { return Jb[k.src * 8 + b] - Jb[k.dst * 8 + b]; };"),
@@ -114,6 +119,7 @@ def _battery():
             (pins.test_robertson_ros2_conservation, {"method": W.RODAS3}),
             (pins.test_kinetics8_conservation_and_reference, {"method": W.RODAS3}),
             (pins.test_dopri5_record_matches_scipy_rk45, {}),
+            (pins.test_save_time_landing_matches_scipy_rk45, {}),
             (pins.test_loss_values_match_their_definitions, {}),
             (pins.test_rhs_vjp_against_dense_jacobian, {})]
     for case in pins.CASES:

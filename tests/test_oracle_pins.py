@@ -740,6 +740,45 @@ def test_dopri5_record_matches_scipy_rk45(orc):
         assert mf["n_steps"][0] == N
 
 
+def test_save_time_landing_matches_scipy_rk45(orc):
+    """The landing rule for save times (reading R6): every save time is a mesh
+    point, the step that would pass it is shortened to end on it, and the
+    next trial step comes from that shortened step's error norm.  SciPy's
+    RK45, started again at each save time with the step size it proposed at
+    the end of the previous segment (its t_bound shortens the last step of a
+    segment the same way, and its next proposal comes from that step), gives
+    the same steps: the same count per segment and step sizes within 1e-6
+    relative (the two sides' error norms differ in the last bits and the
+    differences drift over about 150 chaotic steps; a next step taken from the
+    unshortened proposal would differ at order one), and the same saved
+    states."""
+    from scipy.integrate import RK45
+    inp = W.make_inputs(2, 6)
+    saves = (0.3, 0.9, 1.5, 2.0)
+    for i in range(6):
+        prob = W.Problem(W.LORENZ63, 3, 3, W.DOPRI5, 0.0, 2.0, 1e-8, 1e-8, 4096,
+                         save_times=saves, dt0=1e-3)
+        m = orc.record(prob, inp["u0"][i:i + 1], inp["p"][i:i + 1])
+        hs, idx, ys = [], [], []
+        t, y, h0 = 0.0, inp["u0"][i].copy(), 1e-3
+        for ts in saves:
+            sol = RK45(_lorenz(inp["p"][i]), t, y, ts, rtol=1e-8, atol=1e-8, first_step=h0)
+            while sol.status == "running":
+                tp = sol.t
+                sol.step()
+                hs.append(sol.t - tp)
+            assert sol.status == "finished" and sol.t == ts
+            t, y, h0 = sol.t, sol.y.copy(), sol.h_abs
+            idx.append(len(hs))
+            ys.append(y)
+        hs = np.array(hs)
+        N = m["n_steps"][0]
+        assert N == len(hs)
+        assert np.array_equal(m["save_idx"][0], idx)
+        assert np.allclose(m["h"][0, :N], hs, rtol=1e-6, atol=0)
+        assert np.allclose(m["y_save"][0], np.array(ys), rtol=1e-10, atol=1e-12)
+
+
 def test_initial_step_matches_textbook(orc):
     """Starting step of Hairer-Norsett-Wanner I.II.4 (SciPy's select_initial_step
     implements the same algorithm), with the method order 5."""
