@@ -58,6 +58,15 @@ __device__ __forceinline__ int wave_max(int x) {
   }
   return __builtin_amdgcn_readfirstlane(x);
 }
+// Smallest value of x over the active lanes of the wavefront, broadcast to all.
+__device__ __forceinline__ int wave_min(int x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const int o = __shfl_xor(x, off, 64);
+    x = o < x ? o : x;
+  }
+  return __builtin_amdgcn_readfirstlane(x);
+}
 
 // ---------------------------------------------------------------------------
 // Explicit 7-stage first-same-as-last tableaux.  Row 6 of A equals b and
@@ -116,6 +125,7 @@ constexpr double ROS2_GAMMA = 1.7071067811865475;
 // ---------------------------------------------------------------------------
 struct Linear {
   static constexpr int D = 1, P = 1;
+  static constexpr bool built_in = true;
   template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
     o[0] = p[0] * y[0];
   }
@@ -140,6 +150,7 @@ struct Linear {
 struct Lorenz63 {
   // p = (sigma, rho, beta)
   static constexpr int D = 3, P = 3;
+  static constexpr bool built_in = true;
   template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
     o[0] = p[0] * (y[1] - y[0]);
     o[1] = mac(y[0], p[1] - y[2], -y[1]);
@@ -180,6 +191,7 @@ struct Lorenz63 {
 struct Robertson {
   // p = (k1, k2, k3)
   static constexpr int D = 3, P = 3;
+  static constexpr bool built_in = true;
   template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
     o[0] = mac(p[2] * y[1], y[2], (-p[0]) * y[0]);
     T s = p[0] * y[0];
@@ -251,6 +263,7 @@ struct Robertson {
 // ---------------------------------------------------------------------------
 struct Kinetics8 {
   static constexpr int D = 8, P = 4;
+  static constexpr bool built_in = true;
   template <class T> __device__ static __forceinline__ void f(const T *y, const T *p, T *o) {
     const T w0 = (T(1.0) * p[0]) * y[0];
     const T w1 = ((T(1.0) * p[1]) * y[1]) * y[1];

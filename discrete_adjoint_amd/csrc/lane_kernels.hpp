@@ -560,6 +560,37 @@ __device__ __forceinline__ void dense_seed(int lk, T th, T h, const T (&yk)[Rhs:
   Rhs::vjp_p_acc(yk, p, v0, g);
 }
 
+template <class...> struct VoidT { typedef void type; };
+
+// Methods whose steps exchange rows (the pivoted factorisation of the
+// Rosenbrock methods) and that also provide the steps without exchanges
+// (M::fwd_nx, M::adj_nx: the same results wherever partial pivoting keeps
+// every row in place, and `need` set where it would not).
+template <class M, class = void> struct RowX { static constexpr bool value = false; };
+template <class M>
+struct RowX<M, typename VoidT<decltype(M::row_exchanges)>::type> {
+  static constexpr bool value = M::row_exchanges;
+};
+// The built-in systems (R::built_in); the kernels of right-hand sides
+// compiled at run time do not take the branch-free path below (their
+// gradient kernels are often near the register limit already).
+template <class R, class = void> struct BuiltIn { static constexpr bool value = false; };
+template <class R>
+struct BuiltIn<R, typename VoidT<decltype(R::built_in)>::type> {
+  static constexpr bool value = R::built_in;
+};
+template <class M, class T, int D>
+__device__ __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
+  if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
+  else M::fwd(y, p, h);
+}
+template <class M, class T, int D>
+__device__ __forceinline__ void adj_nx(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g,
+                                       bool &need) {
+  if constexpr (RowX<M>::value) M::adj_nx(y, p, h, lam, g, need);
+  else M::adj(y, p, h, lam, g);
+}
+
 template <class T, class M, int CK, bool ROWS, bool DENSE>
 __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(ReplayArgs a) {
   using Rhs = typename M::Rhs;
@@ -634,9 +665,61 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
       }
     }
   };
+  // Branch-free path (built-in systems of at most 4 components, checkpoint
+  // interval 1 or 2, no loss terms at saves, no dense output; beyond these
+  // the registers of a unit spill): the steps below every lane's step count
+  // (Nmin) run U at a time with no per-lane guard and, for methods with row
+  // exchanges, without exchanges; if some lane would have exchanged rows,
+  // the unit is repeated with M::fwd.  Same arithmetic as fstep, so the same
+  // results bit for bit.
+  constexpr bool PX = RowX<M>::value;
+  constexpr bool FAST = !DENSE && CK <= 2 && D <= 4 && BuiltIn<Rhs>::value;
+  constexpr int U = CK < 2 ? 2 : CK;  // a multiple of CK
+  const bool fast = FAST && !saves;
+  const int Nmin = FAST ? wave_min(N) : 0;
+  int k0 = 0;
+  if constexpr (FAST) if (fast) {
+    T hc[U];
+#pragma unroll
+    for (int b = 0; b < U; ++b) hc[b] = src.load(b);
+    for (; k0 + U <= Nmin; k0 += U) {
+      T hn[U], ys[U + 1][D];
+#pragma unroll
+      for (int b = 0; b < U; ++b) hn[b] = src.load(k0 + U + b);
+#pragma unroll
+      for (int c = 0; c < D; ++c) ys[0][c] = y[c];
+      bool need = false;
+#pragma unroll
+      for (int b = 0; b < U; ++b) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) ys[b + 1][c] = ys[b][c];
+        fwd_nx<M>(ys[b + 1], p, hc[b], need);
+      }
+      if constexpr (PX) {
+        if (__ballot(need) != 0ull) {
+#pragma unroll
+          for (int b = 0; b < U; ++b) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) ys[b + 1][c] = ys[b][c];
+            M::fwd(ys[b + 1], p, hc[b]);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 0; b < U; b += CK) {
+        T *wk = ws + (int64_t)((k0 + b) / CK) * D * C;
+#pragma unroll
+        for (int c = 0; c < D; ++c) wk[c * C] = ys[b][c];
+      }
+#pragma unroll
+      for (int c = 0; c < D; ++c) y[c] = ys[U][c];
+#pragma unroll
+      for (int b = 0; b < U; ++b) hc[b] = hn[b];
+    }
+  }
   {
-    T hA = src.load(0);
-    for (int k = 0; k < Nw; k += 2) {
+    T hA = src.load(k0);
+    for (int k = k0; k < Nw; k += 2) {
       const T hB = src.load(k + 1);
       fstep(k, hA);
       hA = src.load(k + 2);
@@ -729,15 +812,71 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
       }
     }
   };
+  // Branch-free segment: no per-lane guard, no row exchanges (`need` set
+  // where partial pivoting would exchange rows).
+  auto rseg_nx = [&](const Seg<T, D, CK> &sg, bool &need) {
+    T ys[CK][D];
+#pragma unroll
+    for (int c = 0; c < D; ++c) ys[0][c] = sg.cp[c];
+#pragma unroll
+    for (int b = 1; b < CK; ++b) {
+#pragma unroll
+      for (int c = 0; c < D; ++c) ys[b][c] = ys[b - 1][c];
+      fwd_nx<M>(ys[b], p, sg.h[b - 1], need);
+    }
+#pragma unroll
+    for (int b = CK - 1; b >= 0; --b) adj_nx<M>(ys[b], p, sg.h[b], lam, g, need);
+  };
   if (Mw > 0) {
     Seg<T, D, CK> A, B;
     fetch(Mw - 1, A);
-    for (int m = Mw - 1; m >= 0; m -= 2) {
+    int m = Mw - 1;
+    // pairs of segments that hold some lane's last step, or everything when
+    // the branch-free path is off: guarded
+    for (; m >= 0 && !(fast && (m + 1) * CK <= Nmin); m -= 2) {
       fetch(m - 1, B);
       rseg(m, A);
       fetch(m - 2, A);
       if (m - 1 >= 0) rseg(m - 1, B);
     }
+    // segments below every lane's step count: branch-free, one segment at a
+    // time (a pair of one-step segments at checkpoint interval 1; measured
+    // faster than pairs at interval 2); with row exchanges, repeated through
+    // rseg (from the saved lam and g, the segment read again) if some lane
+    // would have exchanged rows
+    constexpr int SP = CK == 1 ? 2 : 1;  // segments per check
+    if constexpr (FAST) for (; m >= SP - 1; m -= SP) {
+      T lam0[D], g0[P];
+      if constexpr (PX) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) lam0[c] = lam[c];
+#pragma unroll
+        for (int q = 0; q < P; ++q) g0[q] = g[q];
+      }
+      bool need = false;
+      fetch(m - 1, B);
+      rseg_nx(A, need);
+      if constexpr (SP == 2) {
+        fetch(m - 2, A);
+        rseg_nx(B, need);
+      }
+      if constexpr (PX) {
+        if (__ballot(need) != 0ull) {
+#pragma unroll
+          for (int c = 0; c < D; ++c) lam[c] = lam0[c];
+#pragma unroll
+          for (int q = 0; q < P; ++q) g[q] = g0[q];
+          Seg<T, D, CK> R;
+#pragma unroll
+          for (int i = 0; i < SP; ++i) {
+            fetch(m - i, R);
+            rseg(m - i, R);
+          }
+        }
+      }
+      if constexpr (SP == 1) A = B;
+    }
+    if (m == 0) rseg(0, A);
   }
 
   if (live) {
@@ -1008,7 +1147,6 @@ hipError_t replay_fwd_t(const ReplayArgs &a, hipStream_t s) {
 
 // Methods whose reverse step is split into M::pre and M::adj_pre and that
 // take the two-wavefront gradient kernel (M::two_wave_reverse).
-template <class...> struct VoidT { typedef void type; };
 template <class M, class = void> struct TwoWave { static constexpr bool value = false; };
 template <class M>
 struct TwoWave<M, typename VoidT<decltype(M::two_wave_reverse)>::type> {

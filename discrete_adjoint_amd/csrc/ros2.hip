@@ -24,9 +24,11 @@ template <int D, class V> struct Ros2Step {
 // One ROS2 step from y with size h:
 //   k1 = W^-1 f(y);  Y2 = y + h k1;  k2 = W^-1 (f(Y2) - 2 k1);
 //   y+ = y + h (3/2 k1 + 1/2 k2);  err = h (1/2 k1 + 1/2 k2).
-template <class Rhs, class V, class H>
+// X = false: factors without row exchanges (lu_factor<D, false>); `need`
+// is set where that differs from partial pivoting.
+template <class Rhs, bool X = true, class V, class H>
 __device__ __forceinline__ void ros2_forward(const V (&y)[Rhs::D], const V *p, H h,
-                                             Ros2Step<Rhs::D, V> &s) {
+                                             Ros2Step<Rhs::D, V> &s, bool &need) {
   constexpr int D = Rhs::D;
   Rhs::jac(y, p, s.J);
   const H gh = H(ROS2_GAMMA) * h;
@@ -35,15 +37,15 @@ __device__ __forceinline__ void ros2_forward(const V (&y)[Rhs::D], const V *p, H
 #pragma unroll
     for (int b = 0; b < D; ++b)
       s.LU[a * D + b] = (a == b) ? smac(-gh, s.J[a * D + b], V(1)) : smul(-gh, s.J[a * D + b]);
-  lu_factor<D>(s.LU, s.perm, s.rinv, s.swapped);
+  lu_factor<D, X>(s.LU, s.perm, s.rinv, s.swapped, need);
   Rhs::f(y, p, s.f1);
-  lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.f1, s.k1);
+  lu_solve<D, X>(s.LU, s.rinv, s.perm, s.swapped, s.f1, s.k1);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.Y2[c] = smac(h, s.k1[c], y[c]);
   Rhs::f(s.Y2, p, s.f2);
 #pragma unroll
   for (int c = 0; c < D; ++c) s.r2[c] = cmac(-2.0, s.k1[c], s.f2[c]);
-  lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, s.r2, s.k2);
+  lu_solve<D, X>(s.LU, s.rinv, s.perm, s.swapped, s.r2, s.k2);
 #pragma unroll
   for (int c = 0; c < D; ++c) {
     const V acc = cmac(0.5, s.k2[c], cmul(1.5, s.k1[c]));
@@ -69,7 +71,8 @@ struct Ros2 {
   __device__ static __forceinline__ void attempt(const T (&y)[D], const T *p, T h, Cache<T> &,
                                                  T (&ynew)[D], T (&err)[D]) {
     Ros2Step<D, T> s;
-    ros2_forward<Rhs>(y, p, h, s);
+    bool need = false;
+    ros2_forward<Rhs>(y, p, h, s, need);
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       ynew[c] = s.ynew[c];
@@ -83,9 +86,33 @@ struct Ros2 {
   template <class V, class H>
   __device__ static __forceinline__ void fwd(V (&y)[D], const V *p, H h) {
     Ros2Step<D, V> s;
-    ros2_forward<Rhs>(y, p, h, s);
+    bool need = false;
+    ros2_forward<Rhs>(y, p, h, s, need);
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
+  }
+
+  // fwd and adj without row exchanges, for the gradient kernel's branch-free
+  // path: the results are those of fwd and adj wherever `need` stays false
+  // (partial pivoting would keep every row in place); where it is set, the
+  // caller repeats the step with fwd or adj.
+  static constexpr bool row_exchanges = true;
+  template <class T>
+  __device__ static __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
+    Ros2Step<D, T> s;
+    ros2_forward<Rhs, false>(y, p, h, s, need);
+#pragma unroll
+    for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
+  }
+  template <class T>
+  __device__ static __forceinline__ void adj_nx(const T (&y)[D], const T *p, T h, T (&lam)[D],
+                                                T *g, bool &need) {
+    adj_x<false>(y, p, h, lam, g, need);
+  }
+  template <class T>
+  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
+    bool need = false;
+    adj_x<true>(y, p, h, lam, g, need);
   }
 
   // Reverse with the mesh fixed:
@@ -96,10 +123,11 @@ struct Ros2 {
   //   rbar1 = W^-T kbar1, Wbar += -rbar1 k1^T
   //   ybar += J(y)^T rbar1, g += J_p(y)^T rbar1
   //   Jbar = -gamma h Wbar; ybar, g += contraction of Jbar with dJ
-  template <class T>
-  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
+  template <bool X, class T>
+  __device__ static __forceinline__ void adj_x(const T (&y)[D], const T *p, T h, T (&lam)[D],
+                                               T *g, bool &need) {
     Ros2Step<D, T> s;
-    ros2_forward<Rhs>(y, p, h, s);
+    ros2_forward<Rhs, X>(y, p, h, s, need);
     T yb[D], kb1[D], kb2[D], rb1[D], rb2[D], Y2b[D], w[D], Wb[D * D], Jb[D * D];
 #pragma unroll
     for (int c = 0; c < D; ++c) {
@@ -108,7 +136,7 @@ struct Ros2 {
       kb2[c] = T(0.5) * ab;
       yb[c] = lam[c];
     }
-    lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, kb2, rb2);
+    lu_solve_t<D, X>(s.LU, s.rinv, s.perm, s.swapped, kb2, rb2);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll
@@ -121,7 +149,7 @@ struct Ros2 {
       kb1[c] = mac(h, Y2b[c], kb1[c]);
       yb[c] = yb[c] + Y2b[c];
     }
-    lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, kb1, rb1);
+    lu_solve_t<D, X>(s.LU, s.rinv, s.perm, s.swapped, kb1, rb1);
 #pragma unroll
     for (int a = 0; a < D; ++a)
 #pragma unroll

@@ -19,36 +19,50 @@ namespace {
 // either way).  Each pivot's reciprocal is formed once (a correctly rounded
 // 1 / u) and every division by the pivot, here and in the solves, is a
 // multiplication by it.  Pivots are chosen on values.
-template <int D, class V>
+//
+// X = false is the same factorisation on the assumption that no row is
+// exchanged: no branch, perm the identity, swapped false, and `need` set
+// where partial pivoting would have exchanged rows at some column (some
+// entry below the diagonal larger in magnitude than the diagonal one, the
+// comparison the pivot search makes).  Where `need` stays false the factors
+// are bit for bit those of X = true; where it is set they are not, and the
+// caller recomputes with X = true.
+template <int D, bool X = true, class V>
 __device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rinv)[D],
-                                          bool &swapped) {
+                                          bool &swapped, bool &need) {
 #pragma unroll
   for (int i = 0; i < D; ++i) perm[i] = i;
   swapped = false;
 #pragma unroll
   for (int k = 0; k < D; ++k) {
-    int piv = k;
-    auto best = dabs(vpart(A[k * D + k]));
+    if constexpr (X) {
+      int piv = k;
+      auto best = dabs(vpart(A[k * D + k]));
 #pragma unroll
-    for (int i = k + 1; i < D; ++i) {
-      const auto v = dabs(vpart(A[i * D + k]));
-      if (v > best) { best = v; piv = i; }
-    }
-    swapped = swapped || piv != k;
-    if (__ballot(piv != k) != 0ull) {
-#pragma unroll
-      for (int r = k + 1; r < D; ++r) {
-        const bool sw = piv == r;
-#pragma unroll
-        for (int j = 0; j < D; ++j) {
-          const V top = A[k * D + j], oth = A[r * D + j];
-          A[k * D + j] = sel(sw, oth, top);
-          A[r * D + j] = sel(sw, top, oth);
-        }
-        const int pt = perm[k], po = perm[r];
-        perm[k] = sw ? po : pt;
-        perm[r] = sw ? pt : po;
+      for (int i = k + 1; i < D; ++i) {
+        const auto v = dabs(vpart(A[i * D + k]));
+        if (v > best) { best = v; piv = i; }
       }
+      swapped = swapped || piv != k;
+      if (__ballot(piv != k) != 0ull) {
+#pragma unroll
+        for (int r = k + 1; r < D; ++r) {
+          const bool sw = piv == r;
+#pragma unroll
+          for (int j = 0; j < D; ++j) {
+            const V top = A[k * D + j], oth = A[r * D + j];
+            A[k * D + j] = sel(sw, oth, top);
+            A[r * D + j] = sel(sw, top, oth);
+          }
+          const int pt = perm[k], po = perm[r];
+          perm[k] = sw ? po : pt;
+          perm[r] = sw ? pt : po;
+        }
+      }
+    } else {
+      const auto dk = dabs(vpart(A[k * D + k]));
+#pragma unroll
+      for (int i = k + 1; i < D; ++i) need = need || dabs(vpart(A[i * D + k])) > dk;
     }
     rinv[k] = recip(A[k * D + k]);
 #pragma unroll
@@ -60,19 +74,26 @@ __device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rin
     }
   }
 }
+template <int D, class V>
+__device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rinv)[D],
+                                          bool &swapped) {
+  bool need = false;
+  lu_factor<D, true>(A, perm, rinv, swapped, need);
+}
 
 // Solve A x = b from the factors (P A = L U).  The right-hand side is copied
 // into a private array first so that the permutation stays a register select
 // (a select between loads through the argument would become an indexed load
-// and keep the caller's arrays out of registers).
-template <int D, class V>
+// and keep the caller's arrays out of registers).  X = false: factors from
+// lu_factor<D, false> (no permutation).
+template <int D, bool X = true, class V>
 __device__ __forceinline__ void lu_solve(const V (&LU)[D * D], const V (&rinv)[D],
                                          const int (&perm)[D], bool swapped, const V (&b_in)[D],
                                          V (&x)[D]) {
   V b[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) b[i] = b_in[i];
-  if (__ballot(swapped) != 0ull) {  // uniform: some lane has a row exchange
+  if (X && __ballot(swapped) != 0ull) {  // uniform: some lane has a row exchange
 #pragma unroll
     for (int i = 0; i < D; ++i) {
       V v = b[0];
@@ -97,7 +118,7 @@ __device__ __forceinline__ void lu_solve(const V (&LU)[D * D], const V (&rinv)[D
 }
 
 // Solve A^T x = b from the factors of A (A^T = U^T L^T P).
-template <int D, class T>
+template <int D, bool X = true, class T>
 __device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)[D],
                                            const int (&perm)[D], bool swapped, const T (&b)[D],
                                            T (&x)[D]) {
@@ -114,7 +135,7 @@ __device__ __forceinline__ void lu_solve_t(const T (&LU)[D * D], const T (&rinv)
 #pragma unroll
     for (int j = i + 1; j < D; ++j) z[i] = mac(-LU[j * D + i], z[j], z[i]);
   // x[perm[i]] = z[i]
-  if (__ballot(swapped) != 0ull) {  // uniform, as in lu_solve
+  if (X && __ballot(swapped) != 0ull) {  // uniform, as in lu_solve
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       T v = z[0];

@@ -265,6 +265,60 @@ def test_checkpoint_intervals_give_identical_gradients(da, orc, wid, n):
             assert torch.equal(a, b), ck
 
 
+def test_ros2_gradient_with_row_exchanges(da, orc):
+    """ROS2 on Lorenz-63 over a hand-made mesh: the first four steps coarse
+    (0.02..0.2 per trajectory, so that the LU of W = I - gamma h J exchanges
+    rows in some lanes of each of the first four wavefronts and not in
+    others), the rest fine (1e-3), step counts 16..24 (ragged inside every
+    wavefront); the fifth wavefront takes fine steps only.  The gradient
+    kernel runs the steps below a wavefront's smallest step count without
+    per-lane guards and without row exchanges, and repeats a unit with the
+    pivoted steps where some lane would exchange rows: against the oracle's
+    fused mode at checkpoint intervals 1, 2 and 4 (the last takes the guarded
+    path throughout), with the final-state loss and with losses at saves."""
+    n = 320
+    inp = W.make_inputs(2, n)
+    u0n, pn = inp["u0"], inp["p"]
+    rng = np.random.default_rng(21)
+    coarse = 0.02 + 0.18 * rng.random(n)
+    coarse[256:] = 1e-3
+    ns = (16 + rng.integers(0, 9, n)).astype(np.int32)
+    Nmax = int(ns.max())
+    h = np.full((n, Nmax), 1e-3)
+    h[:, :4] = coarse[:, None]
+    for i in range(n):
+        h[i, ns[i]:] = 0.0
+    g = orc.ros2_gamma()
+    col0 = np.abs(np.stack([1 + g * coarse * pn[:, 0], -g * coarse * (pn[:, 1] - u0n[:, 2]),
+                            -g * coarse * u0n[:, 1]]))
+    piv = np.argmax(col0, axis=0)          # pivot row of the first column, first step
+    for w0 in range(0, 256, 64):
+        assert 0 < np.count_nonzero(piv[w0:w0 + 64]) < 64
+    assert np.count_nonzero(piv[256:]) == 0
+    save_idx = np.stack([np.full(n, 3), np.full(n, 9), ns], 1).astype(np.int32)
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    aux = np.random.default_rng(5).standard_normal((n, 3, 3))
+    for lk, st in ((W.SUMSQ_FINAL, ()), (W.MSE_SAVE, (0.1, 0.2, 0.3))):
+        prob = W.Problem(W.LORENZ63, 3, 3, W.ROS2, 0.0, 0.3, 1e-6, 1e-6, Nmax, save_times=st)
+        m = {"h": h, "n_steps": ns, "status": np.zeros(n, np.int32),
+             "save_idx": save_idx if st else ns[:, None].copy()}
+        a = aux if lk == W.MSE_SAVE else None
+        lo, go, po = orc.replay_grad(prob, u0n, pn, m, lk, aux=a, scale=0.3, fused=True)
+        mesh = mesh_to_dev(m, Nmax, torch)
+        auxd = None if a is None else aux_to_dev(a, torch)
+        for ck in (1, 2, 4):
+            _print(f"case: ROS2 gradient with row exchanges, loss {lk}, checkpoint {ck}, n={n}")
+            loss, gu0, gp = da.replay_grad(prob.replace(checkpoint=ck), u0, p, mesh, lk, aux=auxd,
+                                           scale=0.3)
+            torch.cuda.synchronize()
+            err = grad_elem_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+            L = loss.cpu().numpy()
+            _print(f"  element-wise max rel err {err.max():.3e}, bitwise equal lanes "
+                   f"{np.mean(err == 0):.4f}")
+            assert err.max() <= TOL["f64"]
+            assert np.max(np.abs(L - lo) / np.abs(lo)) <= TOL["f64"]
+
+
 def test_determinism_and_chunking(da, orc):
     w, prob, inp, aux, scale = _setup(orc, 2, 3000)
     _print("case: determinism and chunked workspace, workload 2, n=3000")

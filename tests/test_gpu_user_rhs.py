@@ -189,6 +189,39 @@ def test_source_every_function_fp64_and_fp32(da, orc, rhs):
                           W.MSE_SAVE, aux, 0.1, tol)
 
 
+def test_source_every_function_intervals_and_order(da, orc, rhs):
+    """The source that calls every allowed function (a gradient kernel near the
+    register limit) in FP64 at checkpoint intervals 1, 2, 4 and 8, on the
+    oracle's mesh in trajectory order and in replay order, with the final-state
+    loss and with losses at saves: every combination against the oracle."""
+    n = 600
+    rng = np.random.default_rng(10)
+    u0n = 0.5 * rng.standard_normal((n, 3))
+    pn = 1.0 + rng.random((n, 3))
+    rid = rhs("allfn", torch.float64, W.TSIT5)
+    orc.set_user_rhs(ALLFN, 3, 3)
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    for lk, st in ((W.SUMSQ_FINAL, ()), (W.MSE_SAVE, (0.5, 2.0))):
+        prob = W.Problem(rid, 3, 3, W.TSIT5, 0.0, 2.0, 1e-6, 1e-6, 4096, save_times=st)
+        aux = rng.standard_normal((n, len(st), 3)) if st else None
+        m = orc.record(prob, u0n, pn, fused=True)
+        assert np.all(m["status"] == 0)
+        lo, go, po = orc.replay_grad(prob, u0n, pn, m, lk, aux=aux, scale=0.1, fused=True)
+        mesh = mesh_to_dev(m, prob.max_steps, torch)
+        sm = da.mesh_sort(prob, mesh)
+        auxd = None if aux is None else aux_to_dev(aux, torch)
+        for ck in (1, 2, 4, 8):
+            for order, me in (("trajectory", mesh), ("replay", sm)):
+                _print(f"case: every function, loss {lk}, checkpoint {ck}, {order} order, n={n}")
+                loss, gu0, gp = da.replay_grad(prob.replace(checkpoint=ck), u0, p, me, lk,
+                                               aux=auxd, scale=0.1)
+                torch.cuda.synchronize()
+                eg = grad_rel_err(gu0.cpu().numpy().T, gp.cpu().numpy().T, go, po)
+                el = np.abs(loss.cpu().numpy() - lo) / np.abs(lo)
+                _print(f"  grad max rel {eg.max():.3e}, loss {el.max():.3e}")
+                assert eg.max() <= 1e-12 and el.max() <= 1e-12
+
+
 def test_registration_errors(da, rhs):
     """A source that does not compile reports the compiler's message; a
     problem that does not fit the registration is refused; a released
