@@ -11,6 +11,30 @@
 namespace dadj {
 namespace {
 
+// 1 / x for the factorisation without row exchanges, in FP64: the hardware's
+// approximate reciprocal refined by three Newton steps q <- q + q (1 - x q)
+// (the residual and the update one fma each).  The correctly rounded
+// division 1.0 / x compiles to scalings of numerator and denominator, the
+// same approximate reciprocal and two such steps, a quotient (numerator
+// times reciprocal), its residual and correction, and a fix-up of special
+// operands.  For |x| in [2^-600, 2^600] nothing is scaled or fixed up and
+// the quotient is the reciprocal itself (the numerator is 1), so the two
+// sequences are the same operations and agree bit for bit; outside that
+// range (and for non-finite x) `need` is set and the caller recomputes with
+// the division.  FP32 keeps the division.
+__device__ __forceinline__ double recip_nx(double x, bool &need) {
+  const double ax = __builtin_fabs(x);
+  need = need || !(ax >= 0x1p-600 && ax <= 0x1p600);
+  double q = __builtin_amdgcn_rcp(x);
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const double t = __builtin_fma(-x, q, 1.0);
+    q = __builtin_fma(q, t, q);
+  }
+  return q;
+}
+__device__ __forceinline__ float recip_nx(float x, bool &) { return recip(x); }
+
 // In-place LU of A (row-major) with partial pivoting; perm[i] = original row
 // now in position i, swapped = some row was exchanged.  Row exchanges are
 // register selects, executed only when some lane of the wavefront needs one
@@ -24,9 +48,10 @@ namespace {
 // exchanged: no branch, perm the identity, swapped false, and `need` set
 // where partial pivoting would have exchanged rows at some column (some
 // entry below the diagonal larger in magnitude than the diagonal one, the
-// comparison the pivot search makes).  Where `need` stays false the factors
-// are bit for bit those of X = true; where it is set they are not, and the
-// caller recomputes with X = true.
+// comparison the pivot search makes) or where a pivot lies outside the
+// range of recip_nx.  Where `need` stays false the factors are bit for bit
+// those of X = true; where it is set they are not, and the caller
+// recomputes with X = true.
 template <int D, bool X = true, class V>
 __device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rinv)[D],
                                           bool &swapped, bool &need) {
@@ -64,7 +89,8 @@ __device__ __forceinline__ void lu_factor(V (&A)[D * D], int (&perm)[D], V (&rin
 #pragma unroll
       for (int i = k + 1; i < D; ++i) need = need || dabs(vpart(A[i * D + k])) > dk;
     }
-    rinv[k] = recip(A[k * D + k]);
+    if constexpr (X) rinv[k] = recip(A[k * D + k]);
+    else rinv[k] = recip_nx(A[k * D + k], need);
 #pragma unroll
     for (int i = k + 1; i < D; ++i) {
       const V l = A[i * D + k] * rinv[k];
