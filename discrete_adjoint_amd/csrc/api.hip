@@ -67,21 +67,35 @@ int ws_row_of(int rhs, int dim) {
 // them (storing the stages would move 2 s d values per step through HBM
 // against about s right-hand sides of recomputation, far slower for every
 // built-in system); the interval trades stored states against recomputed
-// steps.  Measured on MI355X (gradient pass, ms, intervals 1 / 2 / 4 / 8):
-//   ROS2, Robertson (d = 3), FP64, 65536 trajectories: 16.6 / 15.4 / 15.9 / 15.8
-//   Rodas3 and the fourth-order method, Robertson:      0.76 / 0.80, 0.67 / 0.73
-//   Dopri5 / Fehlberg 7(8), Lorenz-63 (d = 3), FP64, 2^20: 10.6 / 10.6 / 10.7 / 11.5,
-//                                                         4.9 / 5.5
-//   Tsit5, Lorenz-63, FP32, 65536:                       0.203 / 0.208 / 0.217 / 0.217
-//   Rodas3, kinetics (d = 8), FP64, 65536:               4.04 / 5.40 / 7.44 (spills)
-//   Tsit5, Lorenz-96 (d = 64, wavefront kernel), 16384:  1.23 / 1.32 / 1.37 / 1.41
-// so the interval is 2 for the two-stage ROS2 on systems of up to three
-// components in double precision (the recomputed step in registers gives
-// the scheduler independent work), and 1 (every state stored) everywhere
-// else.
+// steps.  The lane kernels replay the steps that every trajectory of a
+// wavefront still has without per-lane guards (built-in systems of up to
+// four components, intervals 1, 2 and 4, final-state loss, no dense
+// output), and a segment of several steps is one block of independent work
+// for the scheduler there.  Measured on MI355X, gradient pass in ms at
+// intervals 1 / 2 / 4 / 8, final-state loss:
+//   ROS2, Robertson (d = 3), FP64, 65536 trajectories:  13.55 / 11.43 / 10.60 / 15.69
+//   Dopri5, Lorenz-63 (d = 3), FP64, 2^20:              10.56 / 9.75 / 10.10 / 11.95
+//   Tsit5, Lorenz-63, FP64, 1024:                       0.0438 / 0.0419 / 0.0427 / 0.0581
+//   Rodas3, Robertson:                                  0.708 / 0.760 / 0.806 / 0.955
+//   fourth-order Rosenbrock method, Robertson:          0.656 / 0.688 / 0.722 / 0.869
+//   Fehlberg 7(8), Lorenz-63, FP64, 2^20:               4.92 / 5.01 / 5.15 / 6.19
+// and with the guarded replay (losses at save times, registered or larger
+// systems):
+//   ROS2, Robertson, FP64:                              16.6 / 15.4 / 15.9 / 15.8
+//   Tsit5, Lorenz-63, FP32, 65536, MSE at 10 saves:     0.189 (two wavefronts) / 0.208
+//   Rodas3, kinetics (d = 8), FP64, 65536:              4.04 / 5.40 / 7.44 (spills)
+//   Tsit5, Lorenz-96 (d = 64, wavefront kernel), 16384: 1.23 / 1.32 / 1.37 / 1.41
+// A problem with save times is taken to be replayed with losses at them.
+// So, in FP64 on built-in systems of up to four components (not the
+// wavefront kernels' Lorenz-96), without dense output: with no save times,
+// 4 for ROS2 and 2 for Tsit5 and Dopri5; with save times, 2 for ROS2.
+// Everywhere else 1 (every state stored).
 int default_checkpoint(const da_problem &pb) {
-  if (pb.method == DA_ROS2 && pb.dim <= 3 && pb.dtype == DA_F64 && pb.rhs < DA_RHS_USER_BASE)
-    return 2;
+  const bool lane_builtin = pb.rhs < DA_RHS_USER_BASE && pb.rhs != DA_RHS_LORENZ96 &&
+                            pb.dim <= 4 && pb.dtype == DA_F64 && pb.dense == 0;
+  if (!lane_builtin) return 1;
+  if (pb.method == DA_ROS2) return pb.n_save == 0 ? 4 : 2;
+  if ((pb.method == DA_TSIT5 || pb.method == DA_DOPRI5) && pb.n_save == 0) return 2;
   return 1;
 }
 

@@ -666,15 +666,15 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
     }
   };
   // Branch-free path (built-in systems of at most 4 components, checkpoint
-  // interval 1 or 2, no loss terms at saves, no dense output; beyond these
-  // the registers of a unit spill): the steps below every lane's step count
-  // (Nmin) run U at a time with no per-lane guard and, for methods with row
-  // exchanges, without exchanges; if some lane would have exchanged rows,
-  // the unit is repeated with M::fwd.  Same arithmetic as fstep, so the same
-  // results bit for bit.
+  // interval 1, 2 or 4, no loss terms at saves, no dense output; beyond
+  // these the registers of a unit spill): the steps below every lane's step
+  // count (Nmin) run U at a time with no per-lane guard and, for methods
+  // with row exchanges, without exchanges; if some lane would have exchanged
+  // rows, the unit is repeated with M::fwd.  Same arithmetic as fstep, so
+  // the same results bit for bit.
   constexpr bool PX = RowX<M>::value;
-  constexpr bool FAST = !DENSE && CK <= 2 && D <= 4 && BuiltIn<Rhs>::value;
-  constexpr int U = CK < 2 ? 2 : CK;  // a multiple of CK
+  constexpr bool FAST = !DENSE && CK <= 4 && D <= 4 && BuiltIn<Rhs>::value;
+  constexpr int U = 4;  // a multiple of CK
   const bool fast = FAST && !saves;
   const int Nmin = FAST ? wave_min(N) : 0;
   int k0 = 0;
@@ -841,7 +841,7 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
     }
     // segments below every lane's step count: branch-free, one segment at a
     // time (a pair of one-step segments at checkpoint interval 1; measured
-    // faster than pairs at interval 2); with row exchanges, repeated through
+    // faster than pairs at intervals 2 and 4); with row exchanges, repeated through
     // rseg (from the saved lam and g, the segment read again) if some lane
     // would have exchanged rows
     constexpr int SP = CK == 1 ? 2 : 1;  // segments per check
