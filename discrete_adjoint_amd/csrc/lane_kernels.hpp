@@ -185,6 +185,51 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 #endif
 constexpr int PAD_EVERY = DADJ_PAD_EVERY;
 
+template <class...> struct VoidT { typedef void type; };
+
+// Methods whose steps exchange rows (the pivoted factorisation of the
+// Rosenbrock methods) and that also provide the steps without exchanges
+// (M::attempt_nx, M::fwd_nx, M::adj_nx: the same results wherever partial
+// pivoting keeps every row in place, and `need` set where it would not).
+template <class M, class = void> struct RowX { static constexpr bool value = false; };
+template <class M>
+struct RowX<M, typename VoidT<decltype(M::row_exchanges)>::type> {
+  static constexpr bool value = M::row_exchanges;
+};
+// The built-in systems (R::built_in); the kernels of right-hand sides
+// compiled at run time do not take the gradient kernel's branch-free path
+// (their gradient kernels are often near the register limit already).
+template <class R, class = void> struct BuiltIn { static constexpr bool value = false; };
+template <class R>
+struct BuiltIn<R, typename VoidT<decltype(R::built_in)>::type> {
+  static constexpr bool value = R::built_in;
+};
+// One trial step of the record: without row exchanges where the method
+// provides it, repeated with the pivoted step in the lanes where partial
+// pivoting would have exchanged rows (the same results bit for bit).
+template <class M, class T, int D, class Cache>
+__device__ __forceinline__ void attempt_x(const T (&y)[D], const T *p, T h, Cache &cache,
+                                          T (&ynew)[D], T (&err)[D]) {
+  if constexpr (RowX<M>::value) {
+    bool need = false;
+    M::attempt_nx(y, p, h, cache, ynew, err, need);
+    if (need) M::attempt(y, p, h, cache, ynew, err);
+  } else {
+    M::attempt(y, p, h, cache, ynew, err);
+  }
+}
+template <class M, class T, int D>
+__device__ __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
+  if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
+  else M::fwd(y, p, h);
+}
+template <class M, class T, int D>
+__device__ __forceinline__ void adj_nx(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g,
+                                       bool &need) {
+  if constexpr (RowX<M>::value) M::adj_nx(y, p, h, lam, g, need);
+  else M::adj(y, p, h, lam, g);
+}
+
 template <class T, class M, bool LOG, bool DENSE>
 __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes) {
   using Rhs = typename M::Rhs;
@@ -259,7 +304,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
           for (int b = 0; b < B; ++b) zb[b] = T(0);
           store_chunk(H + ((int64_t)zl * n + i) * B, zb);
         }
-        M::attempt(y, p, hs, cache, ynew, err);
+        attempt_x<M>(y, p, hs, cache, ynew, err);
         const T E = err_norm<D>(err, y, ynew, atol, rtol);
         if (E <= T(1)) {
           const double t_new = land ? t_stop : t + double(hs);
@@ -558,37 +603,6 @@ __device__ __forceinline__ void dense_seed(int lk, T th, T h, const T (&yk)[Rhs:
   }
   Rhs::vjp_p_acc(yk1, p, v1, g);
   Rhs::vjp_p_acc(yk, p, v0, g);
-}
-
-template <class...> struct VoidT { typedef void type; };
-
-// Methods whose steps exchange rows (the pivoted factorisation of the
-// Rosenbrock methods) and that also provide the steps without exchanges
-// (M::fwd_nx, M::adj_nx: the same results wherever partial pivoting keeps
-// every row in place, and `need` set where it would not).
-template <class M, class = void> struct RowX { static constexpr bool value = false; };
-template <class M>
-struct RowX<M, typename VoidT<decltype(M::row_exchanges)>::type> {
-  static constexpr bool value = M::row_exchanges;
-};
-// The built-in systems (R::built_in); the kernels of right-hand sides
-// compiled at run time do not take the branch-free path below (their
-// gradient kernels are often near the register limit already).
-template <class R, class = void> struct BuiltIn { static constexpr bool value = false; };
-template <class R>
-struct BuiltIn<R, typename VoidT<decltype(R::built_in)>::type> {
-  static constexpr bool value = R::built_in;
-};
-template <class M, class T, int D>
-__device__ __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
-  if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
-  else M::fwd(y, p, h);
-}
-template <class M, class T, int D>
-__device__ __forceinline__ void adj_nx(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g,
-                                       bool &need) {
-  if constexpr (RowX<M>::value) M::adj_nx(y, p, h, lam, g, need);
-  else M::adj(y, p, h, lam, g);
 }
 
 template <class T, class M, int CK, bool ROWS, bool DENSE>

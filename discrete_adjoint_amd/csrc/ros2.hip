@@ -92,11 +92,23 @@ struct Ros2 {
     for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
   }
 
-  // fwd and adj without row exchanges, for the gradient kernel's branch-free
-  // path: the results are those of fwd and adj wherever `need` stays false
-  // (partial pivoting would keep every row in place); where it is set, the
-  // caller repeats the step with fwd or adj.
+  // attempt, fwd and adj without row exchanges (the record's trial steps and
+  // the gradient kernel's branch-free path): the results are those of
+  // attempt, fwd and adj wherever `need` stays false (partial pivoting would
+  // keep every row in place, every pivot in the range of recip_nx); where it
+  // is set, the caller repeats the step with attempt, fwd or adj.
   static constexpr bool row_exchanges = true;
+  template <class T>
+  __device__ static __forceinline__ void attempt_nx(const T (&y)[D], const T *p, T h, Cache<T> &,
+                                                    T (&ynew)[D], T (&err)[D], bool &need) {
+    Ros2Step<D, T> s;
+    ros2_forward<Rhs, false>(y, p, h, s, need);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      ynew[c] = s.ynew[c];
+      err[c] = s.err[c];
+    }
+  }
   template <class T>
   __device__ static __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
     Ros2Step<D, T> s;

@@ -319,6 +319,48 @@ def test_ros2_gradient_with_row_exchanges(da, orc):
             assert np.max(np.abs(L - lo) / np.abs(lo)) <= TOL["f64"]
 
 
+@pytest.mark.parametrize("dt0", [0.05, 0.25])
+def test_ros2_record_with_row_exchanges(da, orc, dt0):
+    """The record's trial steps run without row exchanges and are repeated with
+    the pivoted step in the lanes where partial pivoting would exchange rows.
+    ROS2 on Lorenz-63 with a first trial step of 0.05 (the LU of W = I - gamma
+    h J exchanges rows in about two thirds of the lanes of every wavefront) or
+    0.25 (in every lane); the rejected first attempts decide the steps that
+    follow.  The record's states at the saves equal, bit for bit, the GPU
+    replay of its mesh (pivoted steps) and the oracle's fused-mode replay of
+    it; statuses and step counts agree with the oracle's record within the
+    gate of reading R17 (the two sides' single-precision controller powers
+    may differ in the last bit)."""
+    n = 512
+    inp = W.make_inputs(1, n)
+    u0n, pn = inp["u0"], inp["p"]
+    prob = W.WORKLOADS[1].problem(method=W.ROS2, rtol=1e-3, atol=1e-3, t1=2.0, max_steps=4096,
+                                  dt0=dt0, save_times=(0.5, 2.0))
+    g = orc.ros2_gamma()
+    col0 = np.abs(np.stack([1 + g * dt0 * pn[:, 0], -g * dt0 * (pn[:, 1] - u0n[:, 2]),
+                            -g * dt0 * u0n[:, 1]]))
+    piv = np.argmax(col0, axis=0)          # pivot row of the first column, first attempt
+    counts = [np.count_nonzero(piv[w0:w0 + 64]) for w0 in range(0, n, 64)]
+    assert all(c > 0 for c in counts) and (dt0 > 0.1 or all(c < 64 for c in counts))
+    _print(f"case: ROS2 record with row exchanges, dt0 {dt0}, n={n}")
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    mesh, ys = da.record(prob, u0, p)
+    yr = da.replay_fwd(prob, u0, p, mesh)
+    torch.cuda.synchronize()
+    assert torch.equal(ys, yr)
+    mg = mesh_to_host(mesh, prob.max_steps)
+    yo, _ = orc.replay(prob, u0n, pn, mg, fused=True)
+    yg = ys.cpu().numpy().transpose(2, 0, 1)
+    mo = orc.record(prob, u0n, pn, fused=True)
+    gate, spread = step_count_gate(orc, prob, u0n, pn, mo["n_steps"], fused=True)
+    dn = np.abs(mg["n_steps"] - mo["n_steps"])
+    _print(f"  record vs oracle replay of its mesh: max |diff| {np.max(np.abs(yg - yo)):.3e}; "
+           f"step counts vs the oracle's record: max |dN| {dn.max()} (spread {spread})")
+    assert np.array_equal(yg, yo)
+    assert np.array_equal(mg["status"], mo["status"]) and np.all(mo["status"] == 0)
+    assert np.all(dn <= gate)
+
+
 def test_determinism_and_chunking(da, orc):
     w, prob, inp, aux, scale = _setup(orc, 2, 3000)
     _print("case: determinism and chunked workspace, workload 2, n=3000")
