@@ -31,9 +31,11 @@ template <int D, class V> struct Ros4sStep {
 // for j = 0, 1, ...; the stage right-hand side is the sum of gamma c_ij u_j
 // (a product, then multiply-adds) with gamma h f(Y_i) added last; y+ from y
 // adding m_i u_i in stage order.  V: a real or a tangent number.
-template <class Tab, class Rhs, class V, class H>
+// X = false: factors without row exchanges (lu_factor<D, false>); `need` is
+// set where that differs from partial pivoting.
+template <class Tab, class Rhs, bool X = true, class V, class H>
 __device__ __forceinline__ void ros4s_forward(const V (&y)[Rhs::D], const V *p, H h,
-                                               Ros4sStep<Rhs::D, V> &s) {
+                                               Ros4sStep<Rhs::D, V> &s, bool &need) {
   constexpr int D = Rhs::D;
   Rhs::jac(y, p, s.J);
   const H gh = H(Tab::GAMMA) * h;
@@ -42,7 +44,7 @@ __device__ __forceinline__ void ros4s_forward(const V (&y)[Rhs::D], const V *p, 
 #pragma unroll
     for (int b = 0; b < D; ++b)
       s.LU[a * D + b] = (a == b) ? smac(-gh, s.J[a * D + b], V(1)) : smul(-gh, s.J[a * D + b]);
-  lu_factor<D>(s.LU, s.perm, s.rinv, s.swapped);
+  lu_factor<D, X>(s.LU, s.perm, s.rinv, s.swapped, need);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -67,7 +69,7 @@ __device__ __forceinline__ void ros4s_forward(const V (&y)[Rhs::D], const V *p, 
         }
       r[c] = first ? smul(gh, f[c]) : smac(gh, f[c], acc);
     }
-    lu_solve<D>(s.LU, s.rinv, s.perm, s.swapped, r, s.u[i]);
+    lu_solve<D, X>(s.LU, s.rinv, s.perm, s.swapped, r, s.u[i]);
   }
 #pragma unroll
   for (int c = 0; c < D; ++c) {
@@ -104,7 +106,8 @@ struct Rosenbrock4 {
   __device__ static __forceinline__ void attempt(const T (&y)[D], const T *p, T h, Cache<T> &,
                                                  T (&ynew)[D], T (&err)[D]) {
     Ros4sStep<D, T> s;
-    ros4s_forward<Tab, Rhs>(y, p, h, s);
+    bool need = false;
+    ros4s_forward<Tab, Rhs>(y, p, h, s, need);
 #pragma unroll
     for (int c = 0; c < D; ++c) {
       ynew[c] = s.ynew[c];
@@ -118,9 +121,45 @@ struct Rosenbrock4 {
   template <class V, class H>
   __device__ static __forceinline__ void fwd(V (&y)[D], const V *p, H h) {
     Ros4sStep<D, V> s;
-    ros4s_forward<Tab, Rhs>(y, p, h, s);
+    bool need = false;
+    ros4s_forward<Tab, Rhs>(y, p, h, s, need);
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
+  }
+
+  // attempt, fwd and adj without row exchanges (the record's trial steps and
+  // the gradient kernel's branch-free path): the results are those of
+  // attempt, fwd and adj wherever `need` stays false (partial pivoting would
+  // keep every row in place, every pivot in the range of recip_nx); where it
+  // is set, the caller repeats the step with attempt, fwd or adj.
+  static constexpr bool row_exchanges = true;
+  template <class T>
+  __device__ static __forceinline__ void attempt_nx(const T (&y)[D], const T *p, T h, Cache<T> &,
+                                                    T (&ynew)[D], T (&err)[D], bool &need) {
+    Ros4sStep<D, T> s;
+    ros4s_forward<Tab, Rhs, false>(y, p, h, s, need);
+#pragma unroll
+    for (int c = 0; c < D; ++c) {
+      ynew[c] = s.ynew[c];
+      err[c] = s.err[c];
+    }
+  }
+  template <class T>
+  __device__ static __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
+    Ros4sStep<D, T> s;
+    ros4s_forward<Tab, Rhs, false>(y, p, h, s, need);
+#pragma unroll
+    for (int c = 0; c < D; ++c) y[c] = s.ynew[c];
+  }
+  template <class T>
+  __device__ static __forceinline__ void adj_nx(const T (&y)[D], const T *p, T h, T (&lam)[D],
+                                                T *g, bool &need) {
+    adj_x<false>(y, p, h, lam, g, need);
+  }
+  template <class T>
+  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
+    bool need = false;
+    adj_x<true>(y, p, h, lam, g, need);
   }
 
   // Reverse with the mesh fixed, stages from the last to the first:
@@ -130,10 +169,11 @@ struct Rosenbrock4 {
   //   rbar_i = W^-T ubar_i, Wbar -= rbar_i u_i^T, fbar_i = gamma h rbar_i,
   //   Ybar_i = J(Y_i)^T fbar_i, g += J_p(Y_i)^T fbar_i, ybar += Ybar_i;
   // then Jbar = -gamma h Wbar contracted with the derivative of J at y.
-  template <class T>
-  __device__ static __forceinline__ void adj(const T (&y)[D], const T *p, T h, T (&lam)[D], T *g) {
+  template <bool X, class T>
+  __device__ static __forceinline__ void adj_x(const T (&y)[D], const T *p, T h, T (&lam)[D],
+                                               T *g, bool &need) {
     Ros4sStep<D, T> s;
-    ros4s_forward<Tab, Rhs>(y, p, h, s);
+    ros4s_forward<Tab, Rhs, X>(y, p, h, s, need);
     const T gh = T(Tab::GAMMA) * h;
     T yb[D], rb[4][D], Yb[4][D], Wb[D * D], Jb[D * D];
 #pragma unroll
@@ -162,7 +202,7 @@ struct Rosenbrock4 {
         }
         ub[c] = acc;
       }
-      lu_solve_t<D>(s.LU, s.rinv, s.perm, s.swapped, ub, rb[i]);
+      lu_solve_t<D, X>(s.LU, s.rinv, s.perm, s.swapped, ub, rb[i]);
 #pragma unroll
       for (int a = 0; a < D; ++a)
 #pragma unroll
