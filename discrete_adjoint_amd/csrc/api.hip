@@ -76,8 +76,8 @@ int ws_row_of(int rhs, int dim) {
 //   ROS2, Robertson (d = 3), FP64, 65536 trajectories:  13.55 / 11.43 / 10.60 / 15.69
 //   Dopri5, Lorenz-63 (d = 3), FP64, 2^20:              10.56 / 9.75 / 10.10 / 11.95
 //   Tsit5, Lorenz-63, FP64, 1024:                       0.0438 / 0.0419 / 0.0427 / 0.0581
-//   Rodas3, Robertson:                                  0.708 / 0.760 / 0.806 / 0.955
-//   fourth-order Rosenbrock method, Robertson:          0.656 / 0.688 / 0.722 / 0.869
+//   Rodas3, Robertson:                                  0.574 / 0.509 / 0.520
+//   fourth-order Rosenbrock method, Robertson:          0.526 / 0.470 / 0.496
 //   Fehlberg 7(8), Lorenz-63, FP64, 2^20:               4.92 / 5.01 / 5.15 / 6.19
 // and with the guarded replay (losses at save times, registered or larger
 // systems):
@@ -88,14 +88,17 @@ int ws_row_of(int rhs, int dim) {
 // A problem with save times is taken to be replayed with losses at them.
 // So, in FP64 on built-in systems of up to four components (not the
 // wavefront kernels' Lorenz-96), without dense output: with no save times,
-// 4 for ROS2 and 2 for Tsit5 and Dopri5; with save times, 2 for ROS2.
-// Everywhere else 1 (every state stored).
+// 4 for ROS2 and 2 for Tsit5, Dopri5, Rodas3 and the fourth-order method;
+// with save times, 2 for ROS2.  Everywhere else 1 (every state stored).
 int default_checkpoint(const da_problem &pb) {
   const bool lane_builtin = pb.rhs < DA_RHS_USER_BASE && pb.rhs != DA_RHS_LORENZ96 &&
                             pb.dim <= 4 && pb.dtype == DA_F64 && pb.dense == 0;
   if (!lane_builtin) return 1;
   if (pb.method == DA_ROS2) return pb.n_save == 0 ? 4 : 2;
-  if ((pb.method == DA_TSIT5 || pb.method == DA_DOPRI5) && pb.n_save == 0) return 2;
+  if ((pb.method == DA_TSIT5 || pb.method == DA_DOPRI5 || pb.method == DA_RODAS3 ||
+       pb.method == DA_ROS4) &&
+      pb.n_save == 0)
+    return 2;
   return 1;
 }
 

@@ -167,8 +167,9 @@ typedef struct {
                           registers; 1 = keep every state; 0 = the library's
                           choice: on built-in systems of up to four
                           components (not Lorenz-96) in FP64 without dense
-                          output, 4 for ROS2 and 2 for Tsit5 and Dopri5 when
-                          n_save = 0, 2 for ROS2 when n_save > 0; else 1.
+                          output, 4 for ROS2 and 2 for Tsit5, Dopri5, Rodas3
+                          and DA_ROS4 when n_save = 0, 2 for ROS2 when
+                          n_save > 0; else 1.
                           1, 2, 4 or 8 (or 0).  The result does not depend
                           on it.                                             */
   int32_t dense;       /* 0: steps land on the save times.  1: dense output

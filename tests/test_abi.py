@@ -249,8 +249,9 @@ def test_default_checkpoint_interval(da):
     """The library's checkpoint interval (checkpoint = 0), read from the
     workspace it asks for: in FP64 on built-in systems of up to four
     components other than Lorenz-96, without dense output, 4 for ROS2 and 2
-    for Tsit5 and Dopri5 with no save times, 2 for ROS2 with save times; 1 for
-    every other method, dimension, dtype and right-hand side."""
+    for Tsit5, Dopri5, Rodas3 and the fourth-order Rosenbrock method with no
+    save times, 2 for ROS2 with save times; 1 for every other method,
+    dimension, dtype and right-hand side."""
     import torch
 
     def interval(prob, dt=torch.float64, n=1000, N=700):
@@ -270,7 +271,9 @@ def test_default_checkpoint_interval(da):
     assert interval(W.WORKLOADS[1].problem(method=W.ROS2)) == 4        # ROS2, Lorenz-63
     assert interval(W.WORKLOADS[6].problem(method=W.ROS2)) == 1        # ROS2, d = 8
     for m in (W.RODAS3, W.ROS4):
-        assert interval(W.WORKLOADS[4].problem(method=m)) == 1
+        assert interval(W.WORKLOADS[4].problem(method=m)) == 2
+        assert interval(W.WORKLOADS[4].problem(method=m, save_times=(1.0, 1e5))) == 1
+        assert interval(W.WORKLOADS[6].problem(method=m)) == 1          # d = 8
     for wid in (1, 2):                                                  # Tsit5, Dopri5
         prob = W.WORKLOADS[wid].problem()
         assert prob.save_times == ()
