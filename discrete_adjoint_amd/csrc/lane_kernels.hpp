@@ -559,6 +559,65 @@ __device__ __forceinline__ void seed_terms(int lk, const T (&y)[D], const T *aux
   }
 }
 
+// loss_terms and seed_terms with the save's targets (MSE) or cotangents
+// already in registers (the same arithmetic).
+template <class T, int D>
+__device__ __forceinline__ void loss_terms_v(int lk, const T (&y)[D], const T (&av)[D], T &ss,
+                                             bool &first) {
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    if (lk == DA_LOSS_MSE_SAVE) {
+      const T r = y[c] - av[c];
+      ss = first ? r * r : mac(r, r, ss);
+    } else {
+      ss = first ? av[c] * y[c] : mac(av[c], y[c], ss);
+    }
+    first = false;
+  }
+}
+template <class T, int D>
+__device__ __forceinline__ void seed_terms_v(int lk, const T (&y)[D], const T (&av)[D],
+                                             double scale, T (&lam)[D]) {
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    if (lk == DA_LOSS_MSE_SAVE) lam[c] = mac(T(2.0 * scale), y[c] - av[c], lam[c]);
+    else lam[c] = mac(T(scale), av[c], lam[c]);
+  }
+}
+
+// The save slots of one trajectory walked forward (the loss terms of the
+// forward replay, dir = +1) or backward (the seeds of the reverse sweep,
+// dir = -1): the step index and the targets or cotangents of the current
+// slot q and of the next one, in registers.  The next slot's are loaded when
+// the current one is taken, so that taking a save (one every few steps, at
+// scattered trajectory positions in replay order) waits on no load.  Slots
+// outside [0, S) read slot 0 or S - 1 (inside the buffers, never taken).
+template <class T, int D> struct SaveWalk {
+  int q = 0, idx = -1, idx2 = -1;
+  T av[D], av2[D];
+  __device__ __forceinline__ static void load(const ReplayArgs &a, int64_t tr, int r, int &i,
+                                              T (&v)[D]) {
+    const int S = a.pr.S;
+    const int rc = r < 0 ? 0 : (r >= S ? S - 1 : r);
+    i = a.sidx[(int64_t)rc * a.n + tr];
+    const T *aux = (const T *)a.aux;
+#pragma unroll
+    for (int c = 0; c < D; ++c) v[c] = aux ? aux[((int64_t)rc * D + c) * a.n + tr] : T(0);
+  }
+  __device__ __forceinline__ void start(const ReplayArgs &a, int64_t tr, int q0, int dir) {
+    q = q0;
+    load(a, tr, q0, idx, av);
+    load(a, tr, q0 + dir, idx2, av2);
+  }
+  __device__ __forceinline__ void take(const ReplayArgs &a, int64_t tr, int dir) {
+    q += dir;
+    idx = idx2;
+#pragma unroll
+    for (int c = 0; c < D; ++c) av[c] = av2[c];
+    load(a, tr, q + dir, idx2, av2);
+  }
+};
+
 // Workspace: checkpoint m (the state before step m * CK) of local lane jl at
 // ws[(m * D + c) * ws_lanes + jl].  The forward replay writes the
 // checkpoints; the reverse sweep walks the segments of CK steps from the
@@ -637,27 +696,51 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   const int Nw = wave_max(N);
 
   // ---- forward replay, keeping every CK-th state; loss terms at the saves ----
+  // Built-in systems without dense output walk the saves with SaveWalk
+  // (targets loaded ahead); dense output and the kernels of registered right-
+  // hand sides read each save's step index and targets when they reach it,
+  // as these kernels always have (their code is kept unchanged: see BuiltIn).
+  constexpr bool PF = BuiltIn<Rhs>::value && !DENSE;
   T ss = T(0);
   bool first = true;
+  const int Sl = (ok && saves) ? S : 0;  // save slots this trajectory takes
+  SaveWalk<T, D> fw;
   int s = 0;
   int nxt = (ok && saves) ? a.sidx[tr] : -1;
-  auto terms = [&](int k) {
-    while (s < S && nxt == k) {
-      loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
-      ++s;
-      nxt = s < S ? a.sidx[s * n + tr] : -1;
+  if (PF && saves) fw.start(a, tr, 0, 1);
+  auto terms = [&](int k, const T (&yk)[D]) {
+    if constexpr (PF) {
+      while (fw.q < Sl && fw.idx == k) {
+        loss_terms_v<T, D>(lk, yk, fw.av, ss, first);
+        fw.take(a, tr, 1);
+      }
+    } else {
+      while (s < S && nxt == k) {
+        loss_terms<T, D>(lk, yk, aux, n, s, tr, ss, first);
+        ++s;
+        nxt = s < S ? a.sidx[s * n + tr] : -1;
+      }
     }
   };
-  if (saves) terms(0);
+  if (saves) terms(0, y);
   const T *theta = (const T *)a.theta;
   // DENSE: loss terms of the saves inside step k, from the state yp before it
   auto dterms = [&](int k, const T (&yp)[D], T hk) {
-    while (s < S && nxt == k + 1) {
-      T ys[D];
-      dense_value<Rhs>(theta[(int64_t)s * n + tr], hk, yp, y, p, ys);
-      loss_terms<T, D>(lk, ys, aux, n, s, tr, ss, first);
-      ++s;
-      nxt = s < S ? a.sidx[s * n + tr] : -1;
+    if constexpr (PF) {
+      while (fw.q < Sl && fw.idx == k + 1) {
+        T ys[D];
+        dense_value<Rhs>(theta[(int64_t)fw.q * n + tr], hk, yp, y, p, ys);
+        loss_terms_v<T, D>(lk, ys, fw.av, ss, first);
+        fw.take(a, tr, 1);
+      }
+    } else {
+      while (s < S && nxt == k + 1) {
+        T ys[D];
+        dense_value<Rhs>(theta[(int64_t)s * n + tr], hk, yp, y, p, ys);
+        loss_terms<T, D>(lk, ys, aux, n, s, tr, ss, first);
+        ++s;
+        nxt = s < S ? a.sidx[s * n + tr] : -1;
+      }
     }
   };
   auto fstep = [&](int k, T hk) {
@@ -675,7 +758,7 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
         dterms(k, yp, hk);
       } else {
         M::fwd(y, p, hk);
-        if (saves) terms(k + 1);
+        if (saves) terms(k + 1, y);
       }
     }
   };
@@ -754,13 +837,23 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 #pragma unroll
     for (int c = 0; c < D; ++c) lam[c] = T(0);
   }
+  SaveWalk<T, D> bw;
+  if (PF && saves) bw.start(a, tr, S - 1, -1);
+  bw.q = Sl - 1;
   int sh = S - 1;
   int hidx = (ok && saves) ? a.sidx[(int64_t)sh * n + tr] : -1;
   auto seeds = [&](int k, const T (&yk)[D]) {
-    while (sh >= 0 && hidx == k) {
-      seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
-      --sh;
-      hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+    if constexpr (PF) {
+      while (bw.q >= 0 && bw.idx == k) {
+        seed_terms_v<T, D>(lk, yk, bw.av, a.scale, lam);
+        bw.take(a, tr, -1);
+      }
+    } else {
+      while (sh >= 0 && hidx == k) {
+        seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
+        --sh;
+        hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+      }
     }
   };
   if (saves && !DENSE) seeds(N, y);
@@ -932,7 +1025,7 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
   __shared__ T qh[2][64];
   __shared__ int qb[2][64];
   __shared__ T hand[D + 1][64];  // forward -> reverse: lam, loss sum
-  __shared__ int handi[2][64];   // save cursor: sh, hidx
+  __shared__ int handi[1][64];   // save cursor: the next slot to seed
   const int lane = (int)(threadIdx.x & 63);
   const int wv = (int)(threadIdx.x >> 6);
   const bool helper = wv == 1;  // wavefront-uniform
@@ -941,7 +1034,6 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
   const int S = a.pr.S;
   const int lk = a.loss_kind;
   const bool saves = lk != DA_LOSS_SUMSQ_FINAL;
-  const T *aux = (const T *)a.aux;
 
   // ---- forward replay: slot t = 32 wv + lane of the workgroup's 64 ----
   {
@@ -966,13 +1058,13 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
     const int Nw = wave_max(N);
     T ss = T(0);
     bool first = true;
-    int s = 0;
-    int nxt = (ok && saves) ? a.sidx[tr] : -1;
+    const int Sl = (ok && saves) ? S : 0;  // save slots this trajectory takes
+    SaveWalk<T, D> fw;
+    if (saves) fw.start(a, tr, 0, 1);
     auto terms = [&](int k) {
-      while (s < S && nxt == k) {
-        loss_terms<T, D>(lk, y, aux, n, s, tr, ss, first);
-        ++s;
-        nxt = s < S ? a.sidx[s * n + tr] : -1;
+      while (fw.q < Sl && fw.idx == k) {
+        loss_terms_v<T, D>(lk, y, fw.av, ss, first);
+        fw.take(a, tr, 1);
       }
     };
     if (saves) terms(0);
@@ -1003,21 +1095,20 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
 #pragma unroll
       for (int c = 0; c < D; ++c) lam[c] = T(0);
     }
-    int sh = S - 1;
-    int hidx = (ok && saves) ? a.sidx[(int64_t)sh * n + tr] : -1;
+    SaveWalk<T, D> bw;
     if (saves) {
-      while (sh >= 0 && hidx == N) {
-        seed_terms<T, D>(lk, y, aux, n, sh, tr, a.scale, lam);
-        --sh;
-        hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+      bw.start(a, tr, S - 1, -1);
+      bw.q = Sl - 1;
+      while (bw.q >= 0 && bw.idx == N) {
+        seed_terms_v<T, D>(lk, y, bw.av, a.scale, lam);
+        bw.take(a, tr, -1);
       }
     }
     if (lane < 32) {
 #pragma unroll
       for (int c = 0; c < D; ++c) hand[c][t] = lam[c];
       hand[D][t] = ss;
-      handi[0][t] = sh;
-      handi[1][t] = hidx;
+      handi[0][t] = saves ? bw.q : -1;
     }
   }
   __syncthreads();  // every state stored (and visible to both), seeds handed over
@@ -1041,15 +1132,16 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
   }
   const int Nw = wave_max(N);
   T lam[D], g[P], ss = T(0);
-  int sh = -1, hidx = -1;
+  SaveWalk<T, D> bw;
 #pragma unroll
   for (int q = 0; q < P; ++q) g[q] = T(0);
   if (!helper) {
 #pragma unroll
     for (int c = 0; c < D; ++c) lam[c] = hand[c][lane];
     ss = hand[D][lane];
-    sh = handi[0][lane];
-    hidx = handi[1][lane];
+    const int q = handi[0][lane];
+    if (saves) bw.start(a, tr, q, -1);
+    bw.q = q;
   }
   T yn[D], hn = T(0);  // helper: the next step's state and size, loaded ahead
   if (helper && Nw > 0) {
@@ -1091,13 +1183,12 @@ __global__ __launch_bounds__(128) void k_replay_grad2(ReplayArgs a) {
         q.bits = qb[k & 1][lane];
         M::adj_pre(q, p, qh[k & 1][lane], lam, g);
         if (saves) {
-          while (sh >= 0 && hidx == k) {
+          while (bw.q >= 0 && bw.idx == k) {
             T yk[D];
 #pragma unroll
             for (int c = 0; c < D; ++c) yk[c] = q.v[c];
-            seed_terms<T, D>(lk, yk, aux, n, sh, tr, a.scale, lam);
-            --sh;
-            hidx = sh >= 0 ? a.sidx[(int64_t)sh * n + tr] : -1;
+            seed_terms_v<T, D>(lk, yk, bw.av, a.scale, lam);
+            bw.take(a, tr, -1);
           }
         }
       }
