@@ -218,6 +218,13 @@ __device__ __forceinline__ void attempt_x(const T (&y)[D], const T *p, T h, Cach
     M::attempt(y, p, h, cache, ynew, err);
   }
 }
+// Methods that opt out of the gradient kernel's branch-free path
+// (M::branch_free_replay = false).
+template <class M, class = void> struct BranchFree { static constexpr bool value = true; };
+template <class M>
+struct BranchFree<M, typename VoidT<decltype(M::branch_free_replay)>::type> {
+  static constexpr bool value = M::branch_free_replay;
+};
 template <class M, class T, int D>
 __device__ __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
   if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
@@ -696,11 +703,12 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   const int Nw = wave_max(N);
 
   // ---- forward replay, keeping every CK-th state; loss terms at the saves ----
-  // Built-in systems without dense output walk the saves with SaveWalk
-  // (targets loaded ahead); dense output and the kernels of registered right-
-  // hand sides read each save's step index and targets when they reach it,
-  // as these kernels always have (their code is kept unchanged: see BuiltIn).
-  constexpr bool PF = BuiltIn<Rhs>::value && !DENSE;
+  // Built-in systems of up to four components without dense output walk the
+  // saves with SaveWalk (targets loaded ahead); dense output, larger systems
+  // (whose registers are full) and the kernels of registered right-hand
+  // sides read each save's step index and targets when they reach it, as
+  // these kernels always have (their code is kept unchanged: see BuiltIn).
+  constexpr bool PF = BuiltIn<Rhs>::value && !DENSE && D <= 4;
   T ss = T(0);
   bool first = true;
   const int Sl = (ok && saves) ? S : 0;  // save slots this trajectory takes
@@ -770,7 +778,8 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   // rows, the unit is repeated with M::fwd.  Same arithmetic as fstep, so
   // the same results bit for bit.
   constexpr bool PX = RowX<M>::value;
-  constexpr bool FAST = !DENSE && CK <= 4 && D <= 4 && BuiltIn<Rhs>::value;
+  constexpr bool FAST =
+      !DENSE && CK <= 4 && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
   constexpr int U = 4;  // a multiple of CK
   const bool fast = FAST && !saves;
   const int Nmin = FAST ? wave_min(N) : 0;
