@@ -493,15 +493,15 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
   const int Nw = wave_max(N);
   int s = 0;
   int nxt = L.ok ? a.sidx[tr] : -1;
-  auto save = [&](int k) {
+  auto save = [&](int k, const T (&yk)[D]) {
     while (s < S && nxt == k) {
 #pragma unroll
-      for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = y[c];
+      for (int c = 0; c < D; ++c) ysave[(s * D + c) * n + tr] = yk[c];
       ++s;
       nxt = s < S ? a.sidx[s * n + tr] : -1;
     }
   };
-  save(0);
+  save(0, y);
   // DENSE: the saves inside step k, from the state yp before it
   auto dsave = [&](int k, const T (&yp)[D], T hk) {
     while (s < S && nxt == k + 1) {
@@ -523,12 +523,57 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
         dsave(k, yp, hk);
       } else {
         M::fwd(y, p, hk);
-        save(k + 1);
+        save(k + 1, y);
       }
     }
   };
-  T hA = src.load(0);
-  for (int k = 0; k < Nw; k += 2) {
+  // Branch-free units (built-in systems of up to four components, no dense
+  // output), as in the gradient kernel: below the smallest step count of
+  // the wavefront's trajectories, four steps at a time with no per-lane
+  // guard and, for methods with row exchanges, without exchanges; a unit in
+  // which some lane would have exchanged rows is repeated with M::fwd.  Same
+  // arithmetic as `step`; the saves of the unit's states follow it.
+  constexpr bool FAST = !DENSE && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
+  int k0 = 0;
+  if constexpr (FAST) {
+    constexpr int U = 4;
+    const int Nmin = wave_min(N);
+    T hc[U];
+#pragma unroll
+    for (int b = 0; b < U; ++b) hc[b] = src.load(b);
+    for (; k0 + U <= Nmin; k0 += U) {
+      T hn[U], ys[U + 1][D];
+#pragma unroll
+      for (int b = 0; b < U; ++b) hn[b] = src.load(k0 + U + b);
+#pragma unroll
+      for (int c = 0; c < D; ++c) ys[0][c] = y[c];
+      bool need = false;
+#pragma unroll
+      for (int b = 0; b < U; ++b) {
+#pragma unroll
+        for (int c = 0; c < D; ++c) ys[b + 1][c] = ys[b][c];
+        fwd_nx<M>(ys[b + 1], p, hc[b], need);
+      }
+      if constexpr (RowX<M>::value) {
+        if (__ballot(need) != 0ull) {
+#pragma unroll
+          for (int b = 0; b < U; ++b) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) ys[b + 1][c] = ys[b][c];
+            M::fwd(ys[b + 1], p, hc[b]);
+          }
+        }
+      }
+#pragma unroll
+      for (int b = 1; b <= U; ++b) save(k0 + b, ys[b]);
+#pragma unroll
+      for (int c = 0; c < D; ++c) y[c] = ys[U][c];
+#pragma unroll
+      for (int b = 0; b < U; ++b) hc[b] = hn[b];
+    }
+  }
+  T hA = src.load(k0);
+  for (int k = k0; k < Nw; k += 2) {
     const T hB = src.load(k + 1);
     step(k, hA);
     hA = src.load(k + 2);

@@ -274,8 +274,9 @@ def test_ros2_gradient_with_row_exchanges(da, orc):
     kernel runs the steps below a wavefront's smallest step count without
     per-lane guards and without row exchanges, and repeats a unit with the
     pivoted steps where some lane would exchange rows: against the oracle's
-    fused mode at checkpoint intervals 1, 2 and 4 (the last takes the guarded
-    path throughout), with the final-state loss and with losses at saves."""
+    fused mode at checkpoint intervals 1, 2 and 4, with the final-state loss
+    and with losses at saves (which take the guarded loop); the forward
+    replay's saved states bit for bit."""
     n = 320
     inp = W.make_inputs(2, n)
     u0n, pn = inp["u0"], inp["p"]
@@ -306,6 +307,12 @@ def test_ros2_gradient_with_row_exchanges(da, orc):
         lo, go, po = orc.replay_grad(prob, u0n, pn, m, lk, aux=a, scale=0.3, fused=True)
         mesh = mesh_to_dev(m, Nmax, torch)
         auxd = None if a is None else aux_to_dev(a, torch)
+        # the forward replay takes the same steps (four per unit, repeated
+        # with row exchanges where a lane needs them)
+        yo, _ = orc.replay(prob, u0n, pn, m, fused=True)
+        yg = da.replay_fwd(prob, u0, p, mesh)
+        torch.cuda.synchronize()
+        assert np.array_equal(yg.cpu().numpy().transpose(2, 0, 1), yo)
         for ck in (1, 2, 4):
             _print(f"case: ROS2 gradient with row exchanges, loss {lk}, checkpoint {ck}, n={n}")
             loss, gu0, gp = da.replay_grad(prob.replace(checkpoint=ck), u0, p, mesh, lk, aux=auxd,
