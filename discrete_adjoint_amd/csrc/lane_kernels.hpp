@@ -529,14 +529,14 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
   };
   // Branch-free units (built-in systems of up to four components, no dense
   // output), as in the gradient kernel: below the smallest step count of
-  // the wavefront's trajectories, four steps at a time with no per-lane
+  // the wavefront's trajectories, eight steps at a time with no per-lane
   // guard and, for methods with row exchanges, without exchanges; a unit in
   // which some lane would have exchanged rows is repeated with M::fwd.  Same
   // arithmetic as `step`; the saves of the unit's states follow it.
   constexpr bool FAST = !DENSE && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
   int k0 = 0;
   if constexpr (FAST) {
-    constexpr int U = 4;
+    constexpr int U = 8;
     const int Nmin = wave_min(N);
     T hc[U];
 #pragma unroll
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   constexpr bool PX = RowX<M>::value;
   constexpr bool FAST =
       !DENSE && CK <= 4 && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
-  constexpr int U = 4;  // a multiple of CK
+  constexpr int U = 8;  // a multiple of CK; measured against 4 and 16
   const bool fast = FAST && !saves;
   const int Nmin = FAST ? wave_min(N) : 0;
   int k0 = 0;
