@@ -225,8 +225,8 @@ template <class M>
 struct BranchFree<M, typename VoidT<decltype(M::branch_free_replay)>::type> {
   static constexpr bool value = M::branch_free_replay;
 };
-template <class M, class T, int D>
-__device__ __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
+template <class M, class V, class H, int D>
+__device__ __forceinline__ void fwd_nx(V (&y)[D], const V *p, H h, bool &need) {
   if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
   else M::fwd(y, p, h);
 }

@@ -34,6 +34,11 @@ __device__ __forceinline__ double recip_nx(double x, bool &need) {
   return q;
 }
 __device__ __forceinline__ float recip_nx(float x, bool &) { return recip(x); }
+// tangent numbers (the sensitivity kernel): the division of recip
+template <class T, int G>
+__device__ __forceinline__ DualN<T, G> recip_nx(const DualN<T, G> &x, bool &) {
+  return recip(x);
+}
 
 // In-place LU of A (row-major) with partial pivoting; perm[i] = original row
 // now in position i, swapped = some row was exchanged.  Row exchanges are

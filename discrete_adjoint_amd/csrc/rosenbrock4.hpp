@@ -144,9 +144,9 @@ struct Rosenbrock4 {
       err[c] = s.err[c];
     }
   }
-  template <class T>
-  __device__ static __forceinline__ void fwd_nx(T (&y)[D], const T *p, T h, bool &need) {
-    Ros4sStep<D, T> s;
+  template <class V, class H>
+  __device__ static __forceinline__ void fwd_nx(V (&y)[D], const V *p, H h, bool &need) {
+    Ros4sStep<D, V> s;
     ros4s_forward<Tab, Rhs, false>(y, p, h, s, need);
 #pragma unroll
     for (int c = 0; c < D; ++c) y[c] = s.ynew[c];

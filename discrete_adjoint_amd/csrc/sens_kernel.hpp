@@ -131,8 +131,52 @@ __global__ __launch_bounds__(BLOCK) void k_replay_sens(ReplayArgs a) {
       }
     }
   };
-  T hA = src.load(0);
-  for (int k = 0; k < Nw; k += 2) {
+  // Branch-free units (built-in systems of up to four components, no dense
+  // output) when nothing is read at the saves (no sensitivity output, a
+  // final-state loss or none): below the smallest step count of the
+  // wavefront's trajectories, U steps at a time with no per-lane guard and,
+  // for methods with row exchanges, without exchanges (the tangents follow
+  // the values' pivots); a unit in which some lane would have exchanged rows
+  // is repeated with M::fwd.  The saves passed over are taken (nothing is
+  // written for them).  Same arithmetic as `step`.
+  constexpr bool FAST = !DENSE && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
+  int k0 = 0;
+  if constexpr (FAST) {
+    if (!sens && !saves) {
+      constexpr int U = 4;
+      const int Nmin = wave_min(N);
+      T hc[U];
+#pragma unroll
+      for (int b = 0; b < U; ++b) hc[b] = src.load(b);
+      for (; k0 + U <= Nmin; k0 += U) {
+        T hn[U];
+#pragma unroll
+        for (int b = 0; b < U; ++b) hn[b] = src.load(k0 + U + b);
+        DT y0[D];
+#pragma unroll
+        for (int c = 0; c < D; ++c) y0[c] = y[c];
+        bool need = false;
+#pragma unroll
+        for (int b = 0; b < U; ++b) fwd_nx<M>(y, p, hc[b], need);
+        if constexpr (RowX<M>::value) {
+          if (__ballot(need) != 0ull) {
+#pragma unroll
+            for (int c = 0; c < D; ++c) y[c] = y0[c];
+#pragma unroll
+            for (int b = 0; b < U; ++b) M::fwd(y, p, hc[b]);
+          }
+        }
+#pragma unroll
+        for (int b = 0; b < U; ++b) hc[b] = hn[b];
+      }
+      while (s < S && nxt >= 0 && nxt <= k0) {
+        ++s;
+        nxt = s < S ? a.sidx[s * n + tr] : -1;
+      }
+    }
+  }
+  T hA = src.load(k0);
+  for (int k = k0; k < Nw; k += 2) {
     const T hB = src.load(k + 1);
     step(k, hA);
     hA = src.load(k + 2);

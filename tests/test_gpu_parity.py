@@ -276,7 +276,8 @@ def test_ros2_gradient_with_row_exchanges(da, orc):
     pivoted steps where some lane would exchange rows: against the oracle's
     fused mode at checkpoint intervals 1, 2 and 4, with the final-state loss
     and with losses at saves (which take the guarded loop); the forward
-    replay's saved states bit for bit."""
+    replay's saved states bit for bit; the forward-mode gradient of the
+    final-state loss."""
     n = 320
     inp = W.make_inputs(2, n)
     u0n, pn = inp["u0"], inp["p"]
@@ -324,6 +325,16 @@ def test_ros2_gradient_with_row_exchanges(da, orc):
                    f"{np.mean(err == 0):.4f}")
             assert err.max() <= TOL["f64"]
             assert np.max(np.abs(L - lo) / np.abs(lo)) <= TOL["f64"]
+        if lk == W.SUMSQ_FINAL:
+            # forward mode without sensitivity output takes the same units
+            _, lso, gso, pso = orc.replay_sens(prob, u0n, pn, m, lk, scale=0.3, fused=True)
+            _, ls, gs, ps = da.replay_sens(prob, u0, p, mesh, lk, scale=0.3, with_sens=False)
+            torch.cuda.synchronize()
+            es = grad_elem_err(gs.cpu().numpy().T, ps.cpu().numpy().T, gso, pso)
+            _print(f"  forward mode: element-wise max rel err {es.max():.3e}, bitwise equal lanes "
+                   f"{np.mean(es == 0):.4f}")
+            assert es.max() <= TOL["f64"]
+            assert np.max(np.abs(ls.cpu().numpy() - lso) / np.abs(lso)) <= TOL["f64"]
 
 
 @pytest.mark.parametrize("dt0", [0.05, 0.25])
