@@ -826,6 +826,7 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   constexpr bool FAST =
       !DENSE && CK <= 4 && D <= 4 && BuiltIn<Rhs>::value && BranchFree<M>::value;
   constexpr int U = 8;  // a multiple of CK; measured against 4 and 16
+  static_assert(!FAST || U % CK == 0, "a forward unit holds whole checkpoint segments");
   const bool fast = FAST && !saves;
   const int Nmin = FAST ? wave_min(N) : 0;
   int k0 = 0;
@@ -1002,9 +1003,9 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
     }
     // segments below every lane's step count: branch-free, one segment at a
     // time (a pair of one-step segments at checkpoint interval 1; measured
-    // faster than pairs at intervals 2 and 4); with row exchanges, repeated through
-    // rseg (from the saved lam and g, the segment read again) if some lane
-    // would have exchanged rows
+    // faster than pairs at intervals 2 and 4); with row exchanges, repeated
+    // through rseg (from the saved lam and g, the segment read again) if some
+    // lane would have exchanged rows
     constexpr int SP = CK == 1 ? 2 : 1;  // segments per check
     if constexpr (FAST) for (; m >= SP - 1; m -= SP) {
       T lam0[D], g0[P];
