@@ -422,7 +422,13 @@ int da_replay_sens_dirs(const da_problem *prob, int64_t n, const void *u0, const
  * method, on the same device (DA_EINVAL / DA_EUNSUPPORTED otherwise).  Unlike
  * the rest of the library, a registration is global state: its code object
  * stays loaded until da_rhs_release.  Registration and release must not race
- * with launches that use the same identifier. */
+ * with launches that use the same identifier.  A body heavy enough to fill
+ * the gradient kernel's registers (the test source that calls every allowed
+ * function, at dimension 3, is near that point) has been seen to give wrong
+ * gradients at checkpoint interval 1 in trajectory order once a build of the
+ * kernels made it spill more; the cause was not found.  For such a body,
+ * compare the gradient with another interval or the replay order before
+ * relying on it. */
 typedef struct {
   int32_t dim;         /* 1..16 */
   int32_t n_params;    /* 1..16 */
