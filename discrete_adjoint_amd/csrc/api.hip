@@ -85,20 +85,27 @@ int ws_row_of(int rhs, int dim) {
 //   Tsit5, Lorenz-63, FP32, 65536, MSE at 10 saves:     0.189 (two wavefronts) / 0.208
 //   Rodas3, kinetics (d = 8), FP64, 65536:              4.04 / 5.40 / 7.44 (spills)
 //   Tsit5, Lorenz-96 (d = 64, wavefront kernel), 16384: 1.23 / 1.32 / 1.37 / 1.41
+// In FP32, final-state loss, intervals 1 / 2 / 4:
+//   Tsit5, Lorenz-63, 65536:                            0.1066 (two wavefronts) / 0.1042 / 0.1002
+//   Dopri5, Lorenz-63, 2^20:                            5.39 / 4.84 / 4.68
+//   ROS2 / Rodas3 / fourth-order method, Robertson:     9.90 / 8.08 / 7.63, 0.490 / 0.420 / 0.397,
+//                                                       0.448 / 0.400 / 0.386
 // A problem with save times is taken to be replayed with losses at them.
-// So, in FP64 on built-in systems of up to four components (not the
-// wavefront kernels' Lorenz-96), without dense output: with no save times,
-// 4 for ROS2 and 2 for Tsit5, Dopri5, Rodas3 and the fourth-order method;
-// with save times, 2 for ROS2.  Everywhere else 1 (every state stored).
+// So, on built-in systems of up to four components (not the wavefront
+// kernels' Lorenz-96), without dense output, with no save times: in FP64 4
+// for ROS2 and 2 for Tsit5, Dopri5, Rodas3 and the fourth-order method, in
+// FP32 4 for all five; with save times, 2 for ROS2 in FP64.  Everywhere else
+// 1 (every state stored).
 int default_checkpoint(const da_problem &pb) {
   const bool lane_builtin = pb.rhs < DA_RHS_USER_BASE && pb.rhs != DA_RHS_LORENZ96 &&
-                            pb.dim <= 4 && pb.dtype == DA_F64 && pb.dense == 0;
+                            pb.dim <= 4 && pb.dense == 0;
   if (!lane_builtin) return 1;
-  if (pb.method == DA_ROS2) return pb.n_save == 0 ? 4 : 2;
-  if ((pb.method == DA_TSIT5 || pb.method == DA_DOPRI5 || pb.method == DA_RODAS3 ||
-       pb.method == DA_ROS4) &&
-      pb.n_save == 0)
-    return 2;
+  const bool f64 = pb.dtype == DA_F64;
+  const bool branch_free = pb.method == DA_ROS2 || pb.method == DA_TSIT5 ||
+                           pb.method == DA_DOPRI5 || pb.method == DA_RODAS3 ||
+                           pb.method == DA_ROS4;
+  if (pb.n_save == 0 && branch_free) return (!f64 || pb.method == DA_ROS2) ? 4 : 2;
+  if (pb.method == DA_ROS2 && f64) return 2;
   return 1;
 }
 

@@ -166,10 +166,11 @@ typedef struct {
                           the sweep recomputes the states in between in
                           registers; 1 = keep every state; 0 = the library's
                           choice: on built-in systems of up to four
-                          components (not Lorenz-96) in FP64 without dense
-                          output, 4 for ROS2 and 2 for Tsit5, Dopri5, Rodas3
-                          and DA_ROS4 when n_save = 0, 2 for ROS2 when
-                          n_save > 0; else 1.
+                          components (not Lorenz-96) without dense output,
+                          when n_save = 0: in FP64 4 for ROS2 and 2 for
+                          Tsit5, Dopri5, Rodas3 and DA_ROS4, in FP32 4 for
+                          all five; when n_save > 0, 2 for ROS2 in FP64;
+                          else 1.
                           1, 2, 4 or 8 (or 0).  The result does not depend
                           on it.                                             */
   int32_t dense;       /* 0: steps land on the save times.  1: dense output

@@ -247,11 +247,11 @@ def test_workspace_sizes(da):
 
 def test_default_checkpoint_interval(da):
     """The library's checkpoint interval (checkpoint = 0), read from the
-    workspace it asks for: in FP64 on built-in systems of up to four
-    components other than Lorenz-96, without dense output, 4 for ROS2 and 2
-    for Tsit5, Dopri5, Rodas3 and the fourth-order Rosenbrock method with no
-    save times, 2 for ROS2 with save times; 1 for every other method,
-    dimension, dtype and right-hand side."""
+    workspace it asks for: on built-in systems of up to four components other
+    than Lorenz-96, without dense output and with no save times, 4 for ROS2
+    and 2 for Tsit5, Dopri5, Rodas3 and the fourth-order Rosenbrock method in
+    FP64, 4 for all five in FP32; 2 for ROS2 in FP64 with save times; 1 for
+    every other method, dimension, save times and right-hand side."""
     import torch
 
     def interval(prob, dt=torch.float64, n=1000, N=700):
@@ -267,18 +267,20 @@ def test_default_checkpoint_interval(da):
     assert rob.save_times == ()
     assert interval(rob) == 4
     assert interval(rob.replace(save_times=(1.0, 1e5))) == 2
-    assert interval(rob, torch.float32) == 1
+    assert interval(rob, torch.float32) == 4
+    assert interval(rob.replace(save_times=(1.0, 1e5)), torch.float32) == 1
     assert interval(W.WORKLOADS[1].problem(method=W.ROS2)) == 4        # ROS2, Lorenz-63
     assert interval(W.WORKLOADS[6].problem(method=W.ROS2)) == 1        # ROS2, d = 8
     for m in (W.RODAS3, W.ROS4):
         assert interval(W.WORKLOADS[4].problem(method=m)) == 2
+        assert interval(W.WORKLOADS[4].problem(method=m), torch.float32) == 4
         assert interval(W.WORKLOADS[4].problem(method=m, save_times=(1.0, 1e5))) == 1
         assert interval(W.WORKLOADS[6].problem(method=m)) == 1          # d = 8
     for wid in (1, 2):                                                  # Tsit5, Dopri5
         prob = W.WORKLOADS[wid].problem()
         assert prob.save_times == ()
         assert interval(prob) == 2
-        assert interval(prob, torch.float32) == 1
+        assert interval(prob, torch.float32) == 4
         assert interval(prob.replace(save_times=(0.5, 1.0))) == 1
         assert interval(prob.replace(save_times=(0.5, 1.0), dense=1)) == 1
     for wid in (3, 5, 6):          # FP32 with saves, Lorenz-96, the kinetics system
@@ -287,7 +289,7 @@ def test_default_checkpoint_interval(da):
     assert interval(W.WORKLOADS[2].problem(method=W.RKF78)) == 1
     # the entry point that reports it
     assert da.checkpoint_interval(W.WORKLOADS[4].problem()) == 4
-    assert da.checkpoint_interval(W.WORKLOADS[4].problem(), torch.float32) == 1
+    assert da.checkpoint_interval(W.WORKLOADS[4].problem(), torch.float32) == 4
     assert da.checkpoint_interval(W.WORKLOADS[2].problem()) == 2
     assert da.checkpoint_interval(W.WORKLOADS[3].problem()) == 1
     assert da.checkpoint_interval(W.WORKLOADS[2].problem(checkpoint=4)) == 4
