@@ -245,6 +245,49 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
                        r1[2][:, torch.from_numpy(~longest).cuda()])
 
 
+# (dtype, trajectories, max_steps, smallest step count): the replay table's
+# chunk rows are split into ranges over a second launch dimension sized by the
+# ensemble; these give a ragged last range (188 chunk rows in 63 ranges of 3),
+# a partial workgroup with one chunk row per range and zero-step trajectories,
+# FP32's 16-step chunks with a step count that is not a multiple of them, and
+# an ensemble large enough for a single range.
+TABLE_CASES = [("f64", 65536, 1500, 1300), ("f64", 1000, 77, 0), ("f32", 70001, 301, 250),
+               ("f64", 4194304, 20, 1)]
+
+
+@pytest.mark.parametrize("dt,n,max_steps,lo", TABLE_CASES)
+def test_replay_table_is_the_log_in_replay_order(da, dt, n, max_steps, lo):
+    """The replay table is the tiled log's steps gathered in replay order, one
+    row per step and zero after each trajectory's count (whatever the log
+    holds there), for a table as long as the longest trajectory, as long as
+    the log and shorter than the longest trajectory; the order is the stable
+    one by decreasing step count."""
+    import dataclasses
+    _print(f"case: replay table, {dt}, n={n}, max_steps={max_steps}")
+    tdt = torch.float64 if dt == "f64" else torch.float32
+    B = 8 if dt == "f64" else 16
+    T = (max_steps + B - 1) // B
+    prob = dataclasses.replace(W.WORKLOADS[1].problem(), max_steps=max_steps)
+    rng = np.random.default_rng(n + max_steps)
+    logv = rng.random((T, n, B), dtype=np.float64 if dt == "f64" else np.float32) + 0.5
+    ns = rng.integers(lo, max_steps + 1, n).astype(np.int32)
+    h = torch.from_numpy(logv).cuda()
+    mesh = da.Mesh(h, torch.from_numpy(ns).cuda(), torch.zeros((1, n), dtype=torch.int32).cuda(),
+                   torch.zeros(n, dtype=torch.int32).cuda())
+    perm_ref = np.argsort(-ns, kind="stable")
+    steps = logv.transpose(1, 0, 2).reshape(n, T * B)[perm_ref]
+    steps[np.arange(T * B)[None, :] >= ns[perm_ref][:, None]] = 0
+    for rows in (int(ns.max()), max_steps, max(1, int(ns.max()) - 5)):
+        sm = da.mesh_sort(prob, mesh, rows=rows)
+        torch.cuda.synchronize()
+        assert np.array_equal(sm.perm.cpu().numpy(), perm_ref)
+        got = sm.h_rows.cpu().numpy()
+        assert got.shape == (rows, n)
+        assert np.array_equal(got, steps[:, :rows].T)
+        del sm, got
+    assert torch.equal(h.cpu(), torch.from_numpy(logv))
+
+
 @pytest.mark.parametrize("wid,n", [(2, 1000), (3, 600), (4, 300), (5, 120)])
 def test_checkpoint_intervals_give_identical_gradients(da, orc, wid, n):
     """The reverse sweep's checkpoint interval changes what is stored and what
