@@ -86,6 +86,20 @@ __device__ __forceinline__ void store_chunk(float *dst, const float (&v)[16]) {
   for (int q = 0; q < 4; ++q) d[q] = fvec4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
+// Zeros over the 4096 bytes at dst (64 consecutive 64-byte chunks), the
+// wavefront's lanes each writing four 16-byte pieces so that every store
+// covers 1 KB contiguously.
+__device__ __forceinline__ void zero_row_segment(double *dst, int lane) {
+  dvec2 *d = (dvec2 *)dst;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q * 64 + lane] = dvec2{0.0, 0.0};
+}
+__device__ __forceinline__ void zero_row_segment(float *dst, int lane) {
+  fvec4 *d = (fvec4 *)dst;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) d[q * 64 + lane] = fvec4{0.f, 0.f, 0.f, 0.f};
+}
+
 // RMS of v / sc over D components.
 template <int D, class T>
 __device__ __forceinline__ T rms(const T (&v)[D], const T (&sc)[D]) {
@@ -171,19 +185,25 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // full; after the last step the partial chunk follows.  The zero chunks past
 // a lane's last step (unless the caller defers them to da_mesh_pad) are
 // written from the end of the log downwards while the lane integrates: one
-// chunk row every PAD_EVERY attempts, as long as the row lies at or past the
+// chunk row every PadEvery<M> attempts, as long as the row lies at or past the
 // chunk the next accepted step would go to (attempts >= accepted steps, so
 // the rule needs only the attempt count, which all lanes still in the loop
-// share: the wavefront writes one contiguous row).  A lane that takes more
-// steps than that overwrites the zeros later, in program order.  Spread over
-// the integration, these stores use the HBM bandwidth that the arithmetic
-// leaves free; the rows between the last step and the lowest zeroed row
-// follow the loop.
+// share).  While every lane of the wavefront is still in the loop the row
+// is the same for all of them, and the wavefront writes its 4-KB row
+// segment with each store covering 1 KB contiguously; once a lane has left,
+// each lane writes its own chunk.  A lane that takes more steps than that
+// overwrites the zeros later: the wavefront's stores to one address take
+// effect in program order.  Spread over the integration, these stores use
+// the HBM bandwidth that the arithmetic leaves free; the rows between the
+// last step and the lowest zeroed row follow the loop (whole row segments
+// where every lane needs the row zeroed).
 // ---------------------------------------------------------------------------
+// One zero row per attempt: the headline Dopri5 record (Lorenz-63, 2^20
+// trajectories) takes 10.6 ms against 11.2 with one row per two attempts,
+// Rodas3 on Robertson 1.71 against 1.80 ms.
 #ifndef DADJ_PAD_EVERY
-#define DADJ_PAD_EVERY 2
+#define DADJ_PAD_EVERY 1
 #endif
-constexpr int PAD_EVERY = DADJ_PAD_EVERY;
 
 template <class...> struct VoidT { typedef void type; };
 
@@ -225,6 +245,13 @@ template <class M>
 struct BranchFree<M, typename VoidT<decltype(M::branch_free_replay)>::type> {
   static constexpr bool value = M::branch_free_replay;
 };
+// Attempts per zero row of the record's inline padding (M::pad_every where
+// a method sets it).
+template <class M, class = void> struct PadEvery { static constexpr int value = DADJ_PAD_EVERY; };
+template <class M>
+struct PadEvery<M, typename VoidT<decltype(M::pad_every)>::type> {
+  static constexpr int value = M::pad_every;
+};
 template <class M, class V, class H, int D>
 __device__ __forceinline__ void fwd_nx(V (&y)[D], const V *p, H h, bool &need) {
   if constexpr (RowX<M>::value) M::fwd_nx(y, p, h, need);
@@ -259,7 +286,8 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   T *theta = (T *)a.theta;
 
   int nacc = 0, natt = 0, st = LANE_OK;
-  const bool pad = LOG && !a.defer_pad && PAD_EVERY > 0;  // (uniform)
+  constexpr int PE = PadEvery<M>::value;
+  const bool pad = LOG && !a.defer_pad && PE > 0;  // (uniform)
   int zl = pr.n_chunks;  // rows [zl, n_chunks) of this lane are zero
   T hb[B];
 #pragma unroll
@@ -304,12 +332,17 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         if (natt >= pr.max_attempts) { st = LANE_MAX_ATTEMPTS; break; }
         if (!(hs > T(0)) || t + double(hs) == t) { st = LANE_DT_UNDERFLOW; break; }
         ++natt;
-        if (pad && natt % PAD_EVERY == 0 && zl - 1 >= natt / B) {
+        if (pad && natt % PE == 0 && zl - 1 >= natt / B) {
           --zl;
-          T zb[B];
+          if (__ballot(1) == ~0ull) {
+            const int lane = (int)(threadIdx.x & 63u);
+            zero_row_segment(H + ((int64_t)zl * n + (i - lane)) * B, lane);
+          } else {
+            T zb[B];
 #pragma unroll
-          for (int b = 0; b < B; ++b) zb[b] = T(0);
-          store_chunk(H + ((int64_t)zl * n + i) * B, zb);
+            for (int b = 0; b < B; ++b) zb[b] = T(0);
+            store_chunk(H + ((int64_t)zl * n + i) * B, zb);
+          }
         }
         attempt_x<M>(y, p, hs, cache, ynew, err);
         const T E = err_norm<D>(err, y, ynew, atol, rtol);
@@ -382,25 +415,45 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   }
   if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)
     // the zero chunks from each lane's first chunk past its last step up to
-    // its lowest zeroed row, chunk row by chunk row across the wavefront
+    // its lowest zeroed row, chunk row by chunk row across the wavefront.
+    // Rows [lo, hi) are zero for every lane: there the wavefront writes its
+    // 4-KB row segment with each store covering 1 KB contiguously (the data
+    // is zeros, so which lane writes which bytes does not matter); elsewhere
+    // each lane writes its own chunk.
     const int Tn = pr.n_chunks;
     const int mine = live ? (nacc + B - 1) / B : Tn;
     const int upto = live ? zl : Tn;
-    int tmin = mine, tmax = upto;
+    int tmin = mine, tmax = upto, lo = mine, hi = upto;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const int o = __shfl_xor(tmin, off, 64);
       const int u = __shfl_xor(tmax, off, 64);
+      const int ol = __shfl_xor(lo, off, 64);
+      const int oh = __shfl_xor(hi, off, 64);
       tmin = o < tmin ? o : tmin;
       tmax = u > tmax ? u : tmax;
+      lo = ol > lo ? ol : lo;
+      hi = oh < hi ? oh : hi;
     }
     tmin = __builtin_amdgcn_readfirstlane(tmin);
     tmax = __builtin_amdgcn_readfirstlane(tmax);
+    lo = __builtin_amdgcn_readfirstlane(lo);
+    hi = __builtin_amdgcn_readfirstlane(hi);
     T zb[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) zb[b] = T(0);
-    for (int t = tmin; t < tmax; ++t)
+    // a lane past n has mine = upto = Tn, so a partial wavefront has lo = Tn
+    const bool whole = lo < hi;
+    const int a1 = whole ? lo : tmax;
+    for (int t = tmin; t < a1; ++t)
       if (t >= mine && t < upto) store_chunk(H + ((int64_t)t * n + i) * B, zb);
+    if (whole) {
+      const int lane = (int)(threadIdx.x & 63u);
+      const int64_t i0 = i - lane;  // the wavefront's first trajectory
+      for (int t = lo; t < hi; ++t) zero_row_segment(H + ((int64_t)t * n + i0) * B, lane);
+      for (int t = hi; t < tmax; ++t)
+        if (t >= mine && t < upto) store_chunk(H + ((int64_t)t * n + i) * B, zb);
+    }
   }
 }
 

@@ -882,7 +882,9 @@ def test_inline_padding(da, wid, n, max_steps):
     _print(f"case: inline padding, workload {wid}, n={n}, max_steps={max_steps}")
     inp = W.make_inputs(wid, n)
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
-    m1, ys1 = da.record(prob, u0, p)
+    m1 = da.empty_mesh(prob, n, u0.dtype, u0.device)
+    m1.h.fill_(float("nan"))
+    m1, ys1 = da.record(prob, u0, p, mesh=m1)
     m2 = da.empty_mesh(prob, n, u0.dtype, u0.device)
     m2.h.fill_(float("nan"))
     m2, ys2 = da.record(prob, u0, p, mesh=m2, defer_pad=True)
@@ -900,6 +902,43 @@ def test_inline_padding(da, wid, n, max_steps):
     assert np.all(h[k < ns[:, None]] != 0)
     assert np.all(h[k >= ns[:, None]] == 0)
     assert np.all(m1.h.cpu().numpy().transpose(1, 0, 2).reshape(n, -1)[:, max_steps:] == 0)
+
+
+# (workload, method, end time, trajectories, max_steps): logs at least
+# twice as long as every trajectory, so that most chunk rows after the
+# integration are zero for every lane of a wavefront (whole row segments),
+# with a partial last wavefront; FP64 and FP32 chunks.
+WHOLE_ROW_CASES = [(4, W.RODAS3, None, 1000, 16384), (4, W.ROS2, 100.0, 200, 16384),
+                   (3, W.TSIT5, None, 1100, 4096)]
+
+
+@pytest.mark.parametrize("wid,method,t1,n,max_steps", WHOLE_ROW_CASES)
+def test_padding_of_whole_rows(da, wid, method, t1, n, max_steps):
+    """A record into a log filled with NaN holds nonzero step sizes up to
+    each trajectory's step count and zeros from there to the end of the log,
+    and equals a record with deferred padding padded afterwards."""
+    w = W.WORKLOADS[wid]
+    prob = w.problem(method=method, **({} if t1 is None else {"t1": t1}))
+    prob = prob.replace(max_steps=max_steps)
+    _print(f"case: whole zero rows, workload {wid}, {W.METHOD_NAMES[method]}, t1={prob.t1}, "
+           f"n={n}, max_steps={max_steps}")
+    inp = W.make_inputs(wid, n)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    m1 = da.empty_mesh(prob, n, u0.dtype, u0.device)
+    m1.h.fill_(float("nan"))
+    m1, _ = da.record(prob, u0, p, mesh=m1)
+    m2 = da.empty_mesh(prob, n, u0.dtype, u0.device)
+    m2.h.fill_(float("nan"))
+    m2, _ = da.record(prob, u0, p, mesh=m2, defer_pad=True)
+    da.mesh_pad(prob, m2)
+    torch.cuda.synchronize()
+    ns = m1.n_steps.cpu().numpy()
+    assert np.all(m1.status.cpu().numpy() == 0) and ns.max() * 2 < max_steps
+    assert torch.equal(m1.h, m2.h)
+    h = m1.h.cpu().numpy().transpose(1, 0, 2).reshape(n, -1)
+    k = np.arange(h.shape[1])[None, :]
+    assert np.all(h[k < ns[:, None]] > 0)
+    assert np.all(h[k >= ns[:, None]] == 0)
 
 
 def test_two_wavefront_kernel_boundary(da, orc):
