@@ -246,7 +246,7 @@ struct BranchFree<M, typename VoidT<decltype(M::branch_free_replay)>::type> {
   static constexpr bool value = M::branch_free_replay;
 };
 // Attempts per zero row of the record's inline padding (M::pad_every where
-// a method sets it).
+// a method sets it; 0: every zero row after the integration).
 template <class M, class = void> struct PadEvery { static constexpr int value = DADJ_PAD_EVERY; };
 template <class M>
 struct PadEvery<M, typename VoidT<decltype(M::pad_every)>::type> {
@@ -332,7 +332,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         if (natt >= pr.max_attempts) { st = LANE_MAX_ATTEMPTS; break; }
         if (!(hs > T(0)) || t + double(hs) == t) { st = LANE_DT_UNDERFLOW; break; }
         ++natt;
-        if (pad && natt % PE == 0 && zl - 1 >= natt / B) {
+        if (pad && natt % (PE > 0 ? PE : 1) == 0 && zl - 1 >= natt / B) {
           --zl;
           if (__ballot(1) == ~0ull) {
             const int lane = (int)(threadIdx.x & 63u);

@@ -61,6 +61,11 @@ struct Ros2 {
   static constexpr int D = R::D;
   static constexpr int order = 2, err_order = 1;
   static constexpr bool dense_output = false;
+  // The record zeroes the log's rows after the integration only: a
+  // second-order method fills much of its log (9915 of 16384 steps on the
+  // Robertson workload), and most rows zeroed while it integrates would be
+  // overwritten by its later steps.  65536 trajectories: 10.8 -> 9.7 ms.
+  static constexpr int pad_every = 0;
   template <class T> struct Cache {};
 
   template <class T>
