@@ -197,12 +197,16 @@ def _dtype_code(dt) -> int:
 
 
 def cproblem(prob, dtype) -> tuple:
-    """ctypes problem struct (and the array that backs save_times)."""
+    """ctypes problem struct (and the array that backs save_times, which the
+    caller keeps alive).  The pointer is made from the array's address: a
+    cast of the array itself ties the two in a reference cycle, and freeing
+    those by the cycle collector made each call about ten times slower."""
     st = (ctypes.c_double * max(1, len(prob.save_times)))(*prob.save_times)
     P = _Problem(prob.rhs, prob.dim, prob.n_params, prob.method, _dtype_code(dtype),
                  prob.t0, prob.t1, prob.rtol, prob.atol, prob.dt0, prob.max_steps,
                  prob.max_attempts, len(prob.save_times),
-                 ctypes.cast(st, ctypes.POINTER(ctypes.c_double)) if len(prob.save_times) else None,
+                 ctypes.cast(ctypes.addressof(st), ctypes.POINTER(ctypes.c_double))
+                 if len(prob.save_times) else None,
                  prob.safety, prob.fac_min, prob.fac_max, getattr(prob, "checkpoint", 0),
                  getattr(prob, "dense", 0))
     return P, st

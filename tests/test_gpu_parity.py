@@ -250,9 +250,12 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
 # ensemble; these give a ragged last range (188 chunk rows in 63 ranges of 3),
 # a partial workgroup with one chunk row per range and zero-step trajectories,
 # FP32's 16-step chunks with a step count that is not a multiple of them, and
-# an ensemble large enough for a single range.
+# an ensemble large enough for a single range.  The sort takes one radix
+# pass up to 255 steps, two up to 65535 and three beyond (step counts spread
+# over 17 bits in the last case); its tile counts are scanned by one
+# workgroup up to 262144 trajectories, by three launches beyond.
 TABLE_CASES = [("f64", 65536, 1500, 1300), ("f64", 1000, 77, 0), ("f32", 70001, 301, 250),
-               ("f64", 4194304, 20, 1)]
+               ("f64", 4194304, 20, 1), ("f64", 300, 70000, 0)]
 
 
 @pytest.mark.parametrize("dt,n,max_steps,lo", TABLE_CASES)
