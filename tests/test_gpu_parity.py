@@ -510,6 +510,49 @@ def test_lorenz96_losses_and_dimensions(da, orc, dim):
         assert np.array_equal(ys.cpu().numpy().transpose(2, 0, 1), yo)
 
 
+def test_largest_max_steps(da):
+    """max_steps at the library's limit, 2^24: the log spans 2^21 chunk rows
+    (8.7 GB for 65 trajectories, offsets past 2^32 bytes).  No trajectory
+    comes near either limit, so the record equals one with max_steps 512:
+    the same step counts and states, the same chunks up to the last step
+    and zeros in every chunk row after it; the replay order (four radix
+    passes over 25-bit keys), its table, and the gradients and replayed
+    states from the sorted and from the unsorted mesh are bitwise the same."""
+    w = W.WORKLOADS[1]
+    n = 65
+    small = w.problem()
+    big = small.replace(max_steps=1 << 24)
+    _print(f"case: max_steps 2^24, workload 1, n={n}")
+    inp = W.make_inputs(1, n)
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    m1, ys1 = da.record(small, u0, p)
+    m2 = da.empty_mesh(big, n, u0.dtype, u0.device)
+    assert m2.h.shape[0] == (1 << 21)
+    m2.h.fill_(float("nan"))
+    m2, ys2 = da.record(big, u0, p, mesh=m2)
+    torch.cuda.synchronize()
+    assert torch.equal(ys1, ys2)
+    for a, b in ((m1.n_steps, m2.n_steps), (m1.status, m2.status), (m1.save_idx, m2.save_idx)):
+        assert torch.equal(a, b)
+    assert int(m1.status.abs().max()) == 0
+    B = m2.h.shape[2]
+    rows = (int(m2.n_steps.max()) + B - 1) // B
+    assert torch.equal(m2.h[:rows], m1.h[:rows])
+    assert not bool(torch.any(m2.h[rows:] != 0))
+    s1, s2 = da.mesh_sort(small, m1), da.mesh_sort(big, m2)
+    torch.cuda.synchronize()
+    assert torch.equal(s1.perm, s2.perm) and torch.equal(s1.h_rows, s2.h_rows)
+    for a_mesh, b_mesh in ((s1, s2), (m1, m2)):
+        r1 = da.replay_grad(small, u0, p, a_mesh)
+        r2 = da.replay_grad(big, u0, p, b_mesh)
+        f1, f2 = da.replay_fwd(small, u0, p, a_mesh), da.replay_fwd(big, u0, p, b_mesh)
+        torch.cuda.synchronize()
+        for a, b in zip(r1 + (f1,), r2 + (f2,)):
+            assert torch.equal(a, b)
+    del m2, s2
+    torch.cuda.empty_cache()
+
+
 def test_failed_lanes_and_edge_sizes(da, orc):
     """Lanes that fail report the oracle's status and NaN gradients; n = 1 and
     n = 0 work; max_steps bounds the record."""
