@@ -10,7 +10,7 @@ One timed step is that whole job: record, lane ordering with the replay
 table, and the gradient passes.
 value = trajectories * passes / step time (trajectory-gradients/s).
 
-Printed on one JSON line, besides the driver's fields:
+Printed on one JSON line, besides the standard fields (metric, value, unit, steps, config):
   roofline      the gradient kernel (k_replay_grad) against the vector ALU
                 peak of its dtype: algorithmic FLOPs per launch (the exact
                 operation count of the replay step and its adjoint per
@@ -42,7 +42,7 @@ Printed on one JSON line, besides the driver's fields:
                 gradient-pass times, and the pass's algorithmic rate against
                 its dtype's vector peak.
 
---gpus N with N > 1 is not supported (this build runs on one GPU).
+--gpus N with N > 1 is not supported (the library runs on one GPU).
 """
 import argparse
 import dataclasses
@@ -316,7 +316,7 @@ def copy_probe(gib: float = 1.0):
 
 
 # The other gradient workloads, timed after the headline in the default run so
-# that the driver's record holds them too: (workload, method or None).
+# that its JSON line holds them too: (workload, method or None).
 OTHER_WORKLOADS = ((1, None), (3, None), (4, None), (4, "rodas3"), (4, "ros4"), (5, None),
                    (6, None), (2, "rkf78"))
 
@@ -407,7 +407,7 @@ def main():
                          "headline")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU mode (trajectories "
+        print("bench.py runs on one GPU only: the library has no multi-GPU mode (trajectories "
               "are independent, so shards of the ensemble would run on separate GPUs).",
               file=sys.stderr)
         sys.exit(2)
