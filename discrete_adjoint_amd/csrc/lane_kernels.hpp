@@ -181,7 +181,7 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // a rejection, fac_max when E == 0, fac_min when E is not finite.  Steps land
 // exactly on every save time and on t1 (DENSE: on t1 only; the save times
 // inside an accepted step are read from its interpolant); t accumulates in
-// double.  Accepted steps collect in a register chunk that is written when
+// double.  Accepted steps collect in a chunk in LDS that is written when
 // full; after the last step the partial chunk follows.  The zero chunks past
 // a lane's last step (unless the caller defers them to da_mesh_pad) are
 // written from the end of the log downwards while the lane integrates: one
@@ -289,9 +289,11 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
   constexpr int PE = PadEvery<M>::value;
   const bool pad = LOG && !a.defer_pad && PE > 0;  // (uniform)
   int zl = pr.n_chunks;  // rows [zl, n_chunks) of this lane are zero
-  T hb[B];
-#pragma unroll
-  for (int b = 0; b < B; ++b) hb[b] = T(0);
+  // The lane's chunk of accepted steps, filled one position per accepted
+  // step and written to the log when full ([position][thread]: each thread
+  // reads back only its own column).  In registers it took 16 more VGPRs
+  // and a select per position on every accepted step.
+  __shared__ T lchunk[LOG ? B : 1][BLOCK];
   if (live) {
     T y[D], p[P], ynew[D], err[D];
     typename M::template Cache<T> cache;
@@ -350,12 +352,12 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
           const double t_new = land ? t_stop : t + double(hs);
           if (LOG) {
             const int pos = nacc % B;
-#pragma unroll
-            for (int b = 0; b < B; ++b) hb[b] = (b == pos) ? hs : hb[b];
+            lchunk[pos][threadIdx.x] = hs;
             if (pos == B - 1) {
-              store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
+              T hb[B];
 #pragma unroll
-              for (int b = 0; b < B; ++b) hb[b] = T(0);
+              for (int b = 0; b < B; ++b) hb[b] = lchunk[b][threadIdx.x];
+              store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
             }
           }
           ++nacc;
@@ -411,7 +413,13 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     if (a.nsteps) a.nsteps[i] = nacc;
     if (a.status) a.status[i] = st;
     if (a.natt) a.natt[i] = natt;
-    if (LOG && nacc % B != 0) store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
+    if (LOG && nacc % B != 0) {
+      T hb[B];
+      const int pos = nacc % B;
+#pragma unroll
+      for (int b = 0; b < B; ++b) hb[b] = b < pos ? lchunk[b][threadIdx.x] : T(0);
+      store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
+    }
   }
   if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)
     // the zero chunks from each lane's first chunk past its last step up to
