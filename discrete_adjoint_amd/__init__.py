@@ -10,7 +10,7 @@ been built (``python discrete_adjoint_amd/_build.py`` or
 Layout: per-trajectory tensors are component-major, shape [C, n] (trajectory
 index last and contiguous): u0 [d, n], p [P, n], y_save [S, d, n], grad_u0
 [d, n], grad_p [P, n], with S = max(1, len(problem.save_times)).  The mesh is
-h [T, n, B] (tiled step log: B = 8 steps per 64-byte chunk in float64, 16 in
+h [T, n, B] (tiled step log: B = 16 steps per 128-byte chunk in float64, 32 in
 float32, T = ceil(max_steps / B); ``Mesh.steps()`` gives the [n, max_steps]
 view), n_steps [n], save_idx [S, n], status [n], perm [n] or None (a
 replay order), h_rows [rows, n] or None (the replay table: step k of the
@@ -235,8 +235,8 @@ def _need(t: torch.Tensor, shape, dtype, name: str):
 
 
 def chunk_steps(dtype) -> int:
-    """Steps per 64-byte chunk of the step log."""
-    return 8 if dtype == torch.float64 else 16
+    """Steps per 128-byte chunk of the step log."""
+    return 16 if dtype == torch.float64 else 32
 
 
 @dataclasses.dataclass
@@ -368,7 +368,7 @@ def mesh_sort(prob, mesh: Mesh, perm: Optional[torch.Tensor] = None, table: bool
 
 
 # Mesh files: a numpy .npz archive of plain arrays (no pickled objects).
-MESH_FORMAT = 1
+MESH_FORMAT = 2  # 2: 128-byte chunks in the step log (1: 64-byte)
 # problem fields a record depends on: a mesh is replayed only under these
 _MESH_KEYS = ("rhs", "dim", "n_params", "method", "t0", "t1", "max_steps", "dense")
 

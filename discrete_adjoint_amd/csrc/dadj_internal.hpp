@@ -13,10 +13,13 @@
 namespace dadj {
 
 constexpr int BLOCK = 256;  // threads per workgroup of the lane-per-trajectory kernels
-constexpr int CHUNK_BYTES = 64;  // step-log chunk owned by one trajectory
+// Step-log chunk owned by one trajectory: one 128-byte line, so that a
+// lane reading its trajectory's chunk in any lane order fetches no other
+// trajectory's steps.
+constexpr int CHUNK_BYTES = 128;
 
 // Steps per chunk of the tiled step log.
-constexpr int chunk_steps(int dtype) { return dtype == DA_F64 ? 8 : 16; }
+constexpr int chunk_steps(int dtype) { return dtype == DA_F64 ? 16 : 32; }
 
 // Values per trajectory and checkpoint in the replay-gradient workspace: the
 // state, padded to a whole wavefront for the wavefront-per-trajectory

@@ -28,7 +28,7 @@
 // contains it, at the step fraction the record stores in the mesh.
 //
 // Memory: per-trajectory arrays are component-major ([c][n], trajectory
-// fastest).  The step log is tiled [T][n][B]: each trajectory owns one 64-byte
+// fastest).  The step log is tiled [T][n][B]: each trajectory owns one 128-byte
 // chunk of B steps per tile, so the record writes whole chunks and a replay
 // in any lane order reads whole chunks.  The replays read step k + 1 (and the
 // reverse sweep its checkpoint) while step k computes.
@@ -74,30 +74,56 @@ template <class T> struct Log {
 typedef double dvec2 __attribute__((ext_vector_type(2)));
 typedef float fvec4 __attribute__((ext_vector_type(4)));
 
-// One 64-byte chunk from registers to memory as four 16-byte stores.
-__device__ __forceinline__ void store_chunk(double *dst, const double (&v)[8]) {
+// One chunk (CHUNK_BYTES) from registers to memory as 16-byte stores.
+constexpr int CHUNK_QUADS = CHUNK_BYTES / 16;
+__device__ __forceinline__ void store_chunk(double *dst, const double (&v)[CHUNK_BYTES / 8]) {
   dvec2 *d = (dvec2 *)dst;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = dvec2{v[2 * q], v[2 * q + 1]};
+  for (int q = 0; q < CHUNK_QUADS; ++q) d[q] = dvec2{v[2 * q], v[2 * q + 1]};
 }
-__device__ __forceinline__ void store_chunk(float *dst, const float (&v)[16]) {
+__device__ __forceinline__ void store_chunk(float *dst, const float (&v)[CHUNK_BYTES / 4]) {
   fvec4 *d = (fvec4 *)dst;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q] = fvec4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+  for (int q = 0; q < CHUNK_QUADS; ++q)
+    d[q] = fvec4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
 }
 
-// Zeros over the 4096 bytes at dst (64 consecutive 64-byte chunks), the
-// wavefront's lanes each writing four 16-byte pieces so that every store
+// Thread t's chunk from its column of an LDS array [position][BLOCK] to
+// memory, one 16-byte piece at a time; the first `keep` positions (all of
+// them by default) are copied and the rest written as zeros.
+__device__ __forceinline__ void store_chunk_lds(double *dst, const double (*l)[BLOCK], int t,
+                                                int keep = CHUNK_BYTES / 8) {
+  dvec2 *d = (dvec2 *)dst;
+#pragma unroll
+  for (int q = 0; q < CHUNK_QUADS; ++q)
+    d[q] = dvec2{2 * q < keep ? l[2 * q][t] : 0.0, 2 * q + 1 < keep ? l[2 * q + 1][t] : 0.0};
+}
+__device__ __forceinline__ void store_chunk_lds(float *dst, const float (*l)[BLOCK], int t,
+                                                int keep = CHUNK_BYTES / 4) {
+  fvec4 *d = (fvec4 *)dst;
+#pragma unroll
+  for (int q = 0; q < CHUNK_QUADS; ++q) {
+    fvec4 x;
+    x.x = 4 * q < keep ? l[4 * q][t] : 0.f;
+    x.y = 4 * q + 1 < keep ? l[4 * q + 1][t] : 0.f;
+    x.z = 4 * q + 2 < keep ? l[4 * q + 2][t] : 0.f;
+    x.w = 4 * q + 3 < keep ? l[4 * q + 3][t] : 0.f;
+    d[q] = x;
+  }
+}
+
+// Zeros over the 64 consecutive chunks at dst (a wavefront's row segment),
+// the lanes each writing CHUNK_QUADS 16-byte pieces so that every store
 // covers 1 KB contiguously.
 __device__ __forceinline__ void zero_row_segment(double *dst, int lane) {
   dvec2 *d = (dvec2 *)dst;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q * 64 + lane] = dvec2{0.0, 0.0};
+  for (int q = 0; q < CHUNK_QUADS; ++q) d[q * 64 + lane] = dvec2{0.0, 0.0};
 }
 __device__ __forceinline__ void zero_row_segment(float *dst, int lane) {
   fvec4 *d = (fvec4 *)dst;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) d[q * 64 + lane] = fvec4{0.f, 0.f, 0.f, 0.f};
+  for (int q = 0; q < CHUNK_QUADS; ++q) d[q * 64 + lane] = fvec4{0.f, 0.f, 0.f, 0.f};
 }
 
 // RMS of v / sc over D components.
@@ -189,7 +215,7 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // chunk the next accepted step would go to (attempts >= accepted steps, so
 // the rule needs only the attempt count, which all lanes still in the loop
 // share).  While every lane of the wavefront is still in the loop the row
-// is the same for all of them, and the wavefront writes its 4-KB row
+// is the same for all of them, and the wavefront writes its row
 // segment with each store covering 1 KB contiguously; once a lane has left,
 // each lane writes its own chunk.  A lane that takes more steps than that
 // overwrites the zeros later: the wavefront's stores to one address take
@@ -353,12 +379,8 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
           if (LOG) {
             const int pos = nacc % B;
             lchunk[pos][threadIdx.x] = hs;
-            if (pos == B - 1) {
-              T hb[B];
-#pragma unroll
-              for (int b = 0; b < B; ++b) hb[b] = lchunk[b][threadIdx.x];
-              store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
-            }
+            if (pos == B - 1)
+              store_chunk_lds(H + ((int64_t)(nacc / B) * n + i) * B, lchunk, threadIdx.x);
           }
           ++nacc;
           if constexpr (DENSE) {
@@ -413,19 +435,14 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
     if (a.nsteps) a.nsteps[i] = nacc;
     if (a.status) a.status[i] = st;
     if (a.natt) a.natt[i] = natt;
-    if (LOG && nacc % B != 0) {
-      T hb[B];
-      const int pos = nacc % B;
-#pragma unroll
-      for (int b = 0; b < B; ++b) hb[b] = b < pos ? lchunk[b][threadIdx.x] : T(0);
-      store_chunk(H + ((int64_t)(nacc / B) * n + i) * B, hb);
-    }
+    if (LOG && nacc % B != 0)
+      store_chunk_lds(H + ((int64_t)(nacc / B) * n + i) * B, lchunk, threadIdx.x, nacc % B);
   }
   if (LOG && !a.defer_pad) {  // (a kernel argument: uniform)
     // the zero chunks from each lane's first chunk past its last step up to
     // its lowest zeroed row, chunk row by chunk row across the wavefront.
     // Rows [lo, hi) are zero for every lane: there the wavefront writes its
-    // 4-KB row segment with each store covering 1 KB contiguously (the data
+    // row segment (64 chunks) with each store covering 1 KB contiguously (the data
     // is zeros, so which lane writes which bytes does not matter); elsewhere
     // each lane writes its own chunk.
     const int Tn = pr.n_chunks;

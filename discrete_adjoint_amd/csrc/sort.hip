@@ -8,7 +8,7 @@
 // radix sort over 8-bit digits of key = max_steps - n_steps (deterministic:
 // no atomics) of (key, trajectory) pairs; the sorted trajectories are the
 // replay order.  The mesh itself is not moved: with the tiled step log a lane
-// reads whole 64-byte chunks of its trajectory wherever they lie.
+// reads whole 128-byte chunks of its trajectory wherever they lie.
 #include "dadj_internal.hpp"
 
 namespace dadj {
@@ -166,27 +166,29 @@ __global__ __launch_bounds__(SORT_THREADS) void k_scatter(int64_t n, int shift, 
   }
 }
 
-// Replay table: lane j (trajectory perm[j]) reads its trajectory's 64-byte
-// chunks of the tiled log whole and writes them as B consecutive rows, each
-// store a contiguous row segment across the wavefront; zeros after n_steps.
-// The chunk rows are split into ranges of `tpy` over the second grid
-// dimension, so that a small ensemble still puts many wavefronts in flight.
+// Replay table: lane j (trajectory perm[j]) reads its trajectory's 128-byte
+// chunks of the tiled log whole (one line each) and writes them as B
+// consecutive rows, each store a contiguous row segment across the
+// wavefront; zeros after n_steps.  The chunk rows are split into ranges of
+// `tpy` over the second grid dimension, so that a small ensemble still puts
+// many wavefronts in flight.
 typedef double dvec2 __attribute__((ext_vector_type(2)));
 typedef float fvec4 __attribute__((ext_vector_type(4)));
+constexpr int QUADS = CHUNK_BYTES / 16;  // 16-byte pieces per chunk
 
-__device__ __forceinline__ void load_chunk(const double *src, double (&v)[8]) {
+__device__ __forceinline__ void load_chunk(const double *src, double (&v)[CHUNK_BYTES / 8]) {
   const dvec2 *s = (const dvec2 *)src;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < QUADS; ++q) {
     const dvec2 x = s[q];
     v[2 * q] = x.x;
     v[2 * q + 1] = x.y;
   }
 }
-__device__ __forceinline__ void load_chunk(const float *src, float (&v)[16]) {
+__device__ __forceinline__ void load_chunk(const float *src, float (&v)[CHUNK_BYTES / 4]) {
   const fvec4 *s = (const fvec4 *)src;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < QUADS; ++q) {
     const fvec4 x = s[q];
     v[4 * q] = x.x;
     v[4 * q + 1] = x.y;
@@ -199,7 +201,7 @@ template <class T>
 __global__ __launch_bounds__(SORT_THREADS) void k_replay_table(
     int64_t n, int32_t max_steps, const T *__restrict__ h, const int32_t *__restrict__ nsteps,
     const int32_t *__restrict__ perm, T *__restrict__ out, int32_t rows, int32_t tpy) {
-  constexpr int B = 64 / (int)sizeof(T);
+  constexpr int B = CHUNK_BYTES / (int)sizeof(T);
   const int64_t j = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
   if (j >= n) return;
   const int64_t tr = perm ? perm[j] : j;
@@ -259,14 +261,14 @@ __global__ __launch_bounds__(MAX_BLOCKS) void k_max_final(int nb, int32_t *__res
 
 // Zero chunks t >= ceil(N_i / B) of every trajectory i (the padding of a
 // record taken with deferred padding).  Thread i walks its chunk rows; a
-// wavefront writes 64 adjacent 64-byte chunks per row, as four 16-byte stores
-// per lane.
+// wavefront writes 64 adjacent chunks per row, as QUADS 16-byte stores per
+// lane.
 template <class T>
 __global__ __launch_bounds__(SORT_THREADS) void k_mesh_pad(int64_t n, int32_t n_chunks,
                                                            int32_t max_steps,
                                                            const int32_t *__restrict__ nsteps,
                                                            T *__restrict__ h) {
-  constexpr int B = 64 / (int)sizeof(T);
+  constexpr int B = CHUNK_BYTES / (int)sizeof(T);
   const int64_t i = (int64_t)blockIdx.x * SORT_THREADS + threadIdx.x;
   if (i >= n) return;
   int N = nsteps[i];
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(SORT_THREADS) void k_mesh_pad(int64_t n, int32_t n_
   for (int t = (N + B - 1) / B; t < n_chunks; ++t) {
     dvec2 *dst = (dvec2 *)(h + ((int64_t)t * n + i) * B);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) dst[q] = dvec2{0.0, 0.0};
+    for (int q = 0; q < QUADS; ++q) dst[q] = dvec2{0.0, 0.0};
   }
 }
 
@@ -342,7 +344,7 @@ hipError_t launch_replay_table(const ProbArgs &pr, int64_t n, const void *h,
                                int32_t rows, hipStream_t s) {
   if (n == 0 || rows <= 0) return hipSuccess;
   const unsigned g1 = (unsigned)((n + SORT_THREADS - 1) / SORT_THREADS);
-  const int B = pr.dtype == DA_F64 ? 8 : 16;
+  const int B = chunk_steps(pr.dtype);
   const int64_t tmax = (rows + B - 1) / B;
   const int64_t waves = (n + 63) / 64;
   int64_t ny = (TABLE_WAVES + waves - 1) / waves;

@@ -341,7 +341,7 @@ template <class T> struct WLog {
 // ---------------------------------------------------------------------------
 // Record / forward solve (same controller as the lane kernels).  Lane b of
 // the wavefront holds step b of the current chunk of the step log; a full
-// chunk is written by lanes 0..B-1 as one 64-byte store.
+// chunk is written by lanes 0..B-1 as one 128-byte store.
 // ---------------------------------------------------------------------------
 template <class T, class M, bool LOG, bool FULL, bool DENSE>
 __global__ __launch_bounds__(64 * WAVES) void k_wrecord(RecordArgs a, SaveTimes stimes) {

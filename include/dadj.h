@@ -198,12 +198,12 @@ typedef struct {
  * replay until the next record.  S = max(1, n_save) save slots.  Every array
  * is in trajectory order.
  *
- * The step log is tiled so that each trajectory owns 64-byte chunks of B
- * consecutive steps, B = 8 (F64) or 16 (F32), and a wavefront's chunks are
+ * The step log is tiled so that each trajectory owns 128-byte chunks of B
+ * consecutive steps, B = 16 (F64) or 32 (F32), and a wavefront's chunks are
  * adjacent: step k of trajectory i is element ((k / B) * n + i) * B + k % B,
  * for k < T * B with T = ceil(max_steps / B) chunks.  Steps at and after
  * n_steps[i] are zero (a zero step leaves the state unchanged).  h must be
- * 64-byte aligned; da_mesh_h_elems gives its length.
+ * 128-byte aligned; da_mesh_h_elems gives its length.
  *
  * perm is a replay order: NULL replays trajectory j on lane j; otherwise lane
  * j replays trajectory perm[j] (da_mesh_sort makes one).  It only schedules

@@ -38,7 +38,7 @@ def tile_steps(h_rows, max_steps, B):
 
 def mesh_to_dev(m, max_steps, torch, dev="cuda"):
     import discrete_adjoint_amd as da
-    B = 8 if m["h"].dtype == np.float64 else 16
+    B = 16 if m["h"].dtype == np.float64 else 32
     h = tile_steps(m["h"], max_steps, B)
     th = None
     if "save_theta" in m:

@@ -100,7 +100,7 @@ def test_null_pointers_rejected(da):
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
                               ctypes.c_void_p(8), 1 << 20, None) == -1
     loss = da._Loss(0, None, 1.0)
-    m = da._Mesh(64, 8, 8, 8, None)   # plausible (aligned) addresses; nothing is launched
+    m = da._Mesh(128, 8, 8, 8, None)   # plausible (aligned) addresses; nothing is launched
     # workspace for fewer than 256 trajectories
     assert lib.da_replay_grad(ctypes.byref(P), 4096, ctypes.c_void_p(8), ctypes.c_void_p(8),
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10,
@@ -109,22 +109,22 @@ def test_null_pointers_rejected(da):
                               ctypes.byref(m), ctypes.byref(loss), None, None, None, 10**6,
                               ctypes.c_void_p(8), 1 << 30, None) == -1
     # sorting needs a permutation array and workspace
-    mo = da._Mesh(64, 8, 8, 8, None)
+    mo = da._Mesh(128, 8, 8, 8, None)
     assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(mo), ctypes.c_void_p(8), 1 << 20,
                             None) == -1
-    mo = da._Mesh(64, 8, 8, 8, 8)
+    mo = da._Mesh(128, 8, 8, 8, 8)
     assert lib.da_mesh_sort(ctypes.byref(P), 4, ctypes.byref(mo), ctypes.c_void_p(8), 4,
                             None) == -4
     # a replay table needs 1 <= rows <= max_steps
-    mr = da._Mesh(64, 8, 8, 8, 8, 64, 0)
+    mr = da._Mesh(128, 8, 8, 8, 8, 64, 0)
     assert lib.da_replay_fwd(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
                              ctypes.byref(mr), ctypes.c_void_p(8), None) == -1
-    mr = da._Mesh(64, 8, 8, 8, 8, 64, prob.max_steps + 1)
+    mr = da._Mesh(128, 8, 8, 8, 8, 64, prob.max_steps + 1)
     assert lib.da_replay_fwd(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
                              ctypes.byref(mr), ctypes.c_void_p(8), None) == -1
     assert "rows" in da.last_error()
-    # the record writes 64-byte chunks: an unaligned step log is refused
-    mu = da._Mesh(72, 8, 8, 8, None)
+    # the record writes 128-byte chunks: a step log aligned to 64 bytes only is refused
+    mu = da._Mesh(192, 8, 8, 8, None)
     assert lib.da_record(ctypes.byref(P), 4, ctypes.c_void_p(8), ctypes.c_void_p(8),
                          ctypes.byref(mu), None, None) == -1
     assert "aligned" in da.last_error()
@@ -139,7 +139,7 @@ def test_dense_output_checks(da):
     assert _call_record(da, W.WORKLOADS[4].problem(dense=1)) == -2
     prob = W.WORKLOADS[3].problem(dense=1)
     P, keep = da.cproblem(prob, __import__("torch").float32)
-    m = da._Mesh(64, 8, 8, 8, None)          # aligned fake addresses, no save_theta
+    m = da._Mesh(128, 8, 8, 8, None)          # aligned fake addresses, no save_theta
     args = (ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.byref(m))
     assert lib.da_record(ctypes.byref(P), 4, *args, None, None) == -1
     assert "save_theta" in da.last_error()
@@ -160,7 +160,7 @@ def test_sensitivity_direction_range_checks(da):
     lib = da.library()
     for prob, Q in ((W.WORKLOADS[1].problem(), 6), (W.WORKLOADS[5].problem(), 65)):
         P, keep = da.cproblem(prob, __import__("torch").float64)
-        m = da._Mesh(64, 8, 8, 8, None)          # aligned fake addresses
+        m = da._Mesh(128, 8, 8, 8, None)          # aligned fake addresses
         args = (ctypes.c_void_p(8), ctypes.c_void_p(8), ctypes.byref(m))
         for qb, qc in ((0, 0), (-1, 2), (0, Q + 1), (Q - 1, 2), (Q, 1), (2, -3)):
             rc = lib.da_replay_sens_dirs(ctypes.byref(P), 4, *args, qb, qc, None, None, None,
@@ -299,7 +299,7 @@ def test_default_checkpoint_interval(da):
 def test_step_log_length(da):
     import torch
     lib = da.library()
-    for wid, dt, B in ((2, torch.float64, 8), (3, torch.float32, 16)):
+    for wid, dt, B in ((2, torch.float64, 16), (3, torch.float32, 32)):
         prob = W.WORKLOADS[wid].problem(max_steps=1001)
         P, keep = da.cproblem(prob, dt)
         assert lib.da_mesh_h_elems(ctypes.byref(P), 300) == ((1001 + B - 1) // B) * 300 * B

@@ -247,14 +247,13 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
 
 # (dtype, trajectories, max_steps, smallest step count): the replay table's
 # chunk rows are split into ranges over a second launch dimension sized by the
-# ensemble; these give a ragged last range (188 chunk rows in 63 ranges of 3),
+# ensemble; these give a ragged last range (95 chunk rows in 48 ranges of 2),
 # a partial workgroup with one chunk row per range and zero-step trajectories,
-# FP32's 16-step chunks with a step count that is not a multiple of them, and
+# FP32's 32-step chunks with a step count that is not a multiple of them, and
 # an ensemble large enough for a single range.  The sort takes one radix
 # pass up to 255 steps, two up to 65535 and three beyond (step counts spread
-# over 17 bits in the last case); its tile counts are scanned by one
-# workgroup up to 262144 trajectories, by three launches beyond.
-TABLE_CASES = [("f64", 65536, 1500, 1300), ("f64", 1000, 77, 0), ("f32", 70001, 301, 250),
+# over 17 bits in the last case).
+TABLE_CASES = [("f64", 65536, 1510, 1300), ("f64", 1000, 77, 0), ("f32", 70001, 301, 250),
                ("f64", 4194304, 20, 1), ("f64", 300, 70000, 0)]
 
 
@@ -268,7 +267,7 @@ def test_replay_table_is_the_log_in_replay_order(da, dt, n, max_steps, lo):
     import dataclasses
     _print(f"case: replay table, {dt}, n={n}, max_steps={max_steps}")
     tdt = torch.float64 if dt == "f64" else torch.float32
-    B = 8 if dt == "f64" else 16
+    B = 16 if dt == "f64" else 32
     T = (max_steps + B - 1) // B
     prob = dataclasses.replace(W.WORKLOADS[1].problem(), max_steps=max_steps)
     rng = np.random.default_rng(n + max_steps)
@@ -511,7 +510,7 @@ def test_lorenz96_losses_and_dimensions(da, orc, dim):
 
 
 def test_largest_max_steps(da):
-    """max_steps at the library's limit, 2^24: the log spans 2^21 chunk rows
+    """max_steps at the library's limit, 2^24: the log spans 2^20 chunk rows
     (8.7 GB for 65 trajectories, offsets past 2^32 bytes).  No trajectory
     comes near either limit, so the record equals one with max_steps 512:
     the same step counts and states, the same chunks up to the last step
@@ -527,7 +526,7 @@ def test_largest_max_steps(da):
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     m1, ys1 = da.record(small, u0, p)
     m2 = da.empty_mesh(big, n, u0.dtype, u0.device)
-    assert m2.h.shape[0] == (1 << 21)
+    assert m2.h.shape[0] * m2.h.shape[2] == (1 << 24)
     m2.h.fill_(float("nan"))
     m2, ys2 = da.record(big, u0, p, mesh=m2)
     torch.cuda.synchronize()
