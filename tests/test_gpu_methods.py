@@ -210,6 +210,38 @@ def test_rosenbrock4_fp32(da, orc, method):
     assert np.all(np.abs(ns - m["n_steps"]) <= gate)
 
 
+@pytest.mark.parametrize("wid,method", [(4, W.ROS2), (4, W.RODAS3), (4, W.ROS4), (6, W.RODAS3)],
+                         ids=["robertson-ros2", "robertson-rodas3", "robertson-ros4",
+                              "kinetics8-rodas3"])
+def test_total_concentration_full_size(da, wid, method):
+    """The Robertson system and the eight-species reaction cycle conserve the
+    sum of their concentrations, and a Rosenbrock step with the exact
+    Jacobian keeps that linear invariant of the discrete map.  So for the
+    loss L = sum of the final state (cotangent of ones) the exact discrete
+    adjoint is dL/du0 = (1, ..., 1) and dL/dk = 0.  Checked on every one of
+    the 65536 trajectories in the benchmark's launch configuration (record,
+    lane ordering with the replay table, the library's interval), at 1e-12:
+    the oracle's own deviations on the Robertson workload are below 1e-14
+    (dL/dk scaled by k; a single component's dy1/dk * k is about 0.05)."""
+    w = W.WORKLOADS[wid]
+    prob = w.problem(method=method)
+    inp = W.make_inputs(wid)
+    n = w.n
+    _print(f"case: total concentration, workload {wid}, {W.METHOD_NAMES[method]}, n={n}")
+    u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
+    mesh, _ = da.record(prob, u0, p, save=False)
+    sm = da.mesh_sort(prob, mesh)
+    ones = torch.ones((1, w.dim, n), dtype=torch.float64, device="cuda")
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.COTANGENT, aux=ones)()
+    torch.cuda.synchronize()
+    assert int(sm.status.abs().max()) == 0
+    dl = (loss - 1).abs().max().item()
+    du = (gu0 - 1).abs().max().item()
+    dk = (gp * p).abs().max().item()
+    _print(f"  max |L - 1| {dl:.2e}, max |dL/du0 - 1| {du:.2e}, max |dL/dk * k| {dk:.2e}")
+    assert dl <= 1e-12 and du <= 1e-12 and dk <= 1e-12
+
+
 @pytest.mark.parametrize("method", [W.RODAS3, W.ROS4], ids=["rodas3", "ros4"])
 def test_rosenbrock4_robertson_full_size_sampled(da, orc, method):
     """Robertson with a four-stage Rosenbrock method at the workload's full
