@@ -552,6 +552,35 @@ def test_largest_max_steps(da):
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("method", [W.DOPRI5, W.TSIT5], ids=["dopri5", "tsit5"])
+def test_linear_decay_gradient_all_lanes(da, method):
+    """y' = p y: each replayed step multiplies the state by the method's
+    stability polynomial at h p, so for L = y_N (cotangent 1) the exact
+    discrete adjoint gives dL/dy0 = y_N / y0, whatever the polynomial.
+    Checked on all 2^20 trajectories (random decay rates, record, lane
+    ordering with the replay table, the library's interval) at 1e-12; L is
+    the record's final state bit for bit."""
+    n = 1 << 20
+    prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 5.0, 1e-8, 1e-8, 4096)
+    _print(f"case: linear decay, {W.METHOD_NAMES[method]}, n={n}")
+    rng = np.random.default_rng(41)
+    u0n = rng.uniform(0.5, 2.0, (n, 1))
+    pn = rng.uniform(-2.0, -0.5, (n, 1))
+    u0, p = to_dev(u0n, torch), to_dev(pn, torch)
+    mesh, ys = da.record(prob, u0, p)
+    sm = da.mesh_sort(prob, mesh)
+    ones = torch.ones((1, 1, n), dtype=torch.float64, device="cuda")
+    loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.COTANGENT, aux=ones)()
+    torch.cuda.synchronize()
+    assert int(sm.status.abs().max()) == 0
+    assert torch.equal(loss, ys[-1, 0])
+    dev = (gu0[0] * u0[0] / loss - 1).abs().max().item()
+    ns = sm.n_steps.cpu().numpy()
+    _print(f"  steps {ns.min()}..{ns.max()}, max |dL/dy0 * y0 / y_N - 1| {dev:.2e}")
+    assert dev <= 1e-12
+    assert bool(torch.all(gp[0] > 0))  # a larger rate (slower decay) raises y_N
+
+
 def test_failed_lanes_and_edge_sizes(da, orc):
     """Lanes that fail report the oracle's status and NaN gradients; n = 1 and
     n = 0 work; max_steps bounds the record."""
