@@ -552,29 +552,39 @@ def test_largest_max_steps(da):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("method", [W.DOPRI5, W.TSIT5, W.RKF78, W.ROS2, W.RODAS3, W.ROS4],
-                         ids=["dopri5", "tsit5", "rkf78", "ros2", "rodas3", "ros4"])
-def test_linear_decay_gradient_all_lanes(da, method):
+@pytest.mark.parametrize("method,dt", [(W.DOPRI5, "f64"), (W.TSIT5, "f64"), (W.RKF78, "f64"),
+                                       (W.ROS2, "f64"), (W.RODAS3, "f64"), (W.ROS4, "f64"),
+                                       (W.TSIT5, "f32"), (W.RODAS3, "f32")],
+                         ids=["dopri5", "tsit5", "rkf78", "ros2", "rodas3", "ros4", "tsit5-f32",
+                              "rodas3-f32"])
+def test_linear_decay_gradient_all_lanes(da, orc, method, dt):
     """y' = p y: each replayed step multiplies the state by the method's
     stability function at h p (a polynomial for the explicit pairs, a
     rational function for the Rosenbrock methods), so for L = y_N
     (cotangent 1) the exact discrete adjoint gives dL/dy0 = y_N / y0,
     whatever the function.
     Checked on all 2^20 trajectories (random decay rates, record, lane
-    ordering with the replay table, the library's interval) at 1e-12; L is
-    the record's final state bit for bit."""
+    ordering with the replay table, the library's interval) at 1e-12 in
+    FP64.  In FP32 the two sides round differently where |h p| is large
+    (the stability function sums terms much larger than itself): the gate is
+    four times the largest deviation the oracle shows itself (plain rounding,
+    the first 32768 trajectories).  L is the record's final state bit for
+    bit."""
     n = 1 << 20
-    # the second-order method at a looser tolerance, so that it stays within its steps
+    # the second-order method, and FP32, at looser tolerances, so that they stay within their steps
     tol, max_steps = (1e-6, 16384) if method == W.ROS2 else (1e-8, 4096)
+    if dt == "f32":
+        tol = 1e-5
     prob = W.Problem(W.LINEAR, 1, 1, method, 0.0, 5.0, tol, tol, max_steps)
-    _print(f"case: linear decay, {W.METHOD_NAMES[method]}, n={n}")
+    _print(f"case: linear decay, {W.METHOD_NAMES[method]} {dt}, n={n}")
     rng = np.random.default_rng(41)
-    u0n = rng.uniform(0.5, 2.0, (n, 1))
-    pn = rng.uniform(-2.0, -0.5, (n, 1))
+    npt = np.float64 if dt == "f64" else np.float32
+    u0n = rng.uniform(0.5, 2.0, (n, 1)).astype(npt)
+    pn = rng.uniform(-2.0, -0.5, (n, 1)).astype(npt)
     u0, p = to_dev(u0n, torch), to_dev(pn, torch)
     mesh, ys = da.record(prob, u0, p)
     sm = da.mesh_sort(prob, mesh)
-    ones = torch.ones((1, 1, n), dtype=torch.float64, device="cuda")
+    ones = torch.ones((1, 1, n), dtype=u0.dtype, device="cuda")
     loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, W.COTANGENT, aux=ones)()
     torch.cuda.synchronize()
     assert int(sm.status.abs().max()) == 0
@@ -582,7 +592,16 @@ def test_linear_decay_gradient_all_lanes(da, method):
     dev = (gu0[0] * u0[0] / loss - 1).abs().max().item()
     ns = sm.n_steps.cpu().numpy()
     _print(f"  steps {ns.min()}..{ns.max()}, max |dL/dy0 * y0 / y_N - 1| {dev:.2e}")
-    assert dev <= 1e-12
+    gate = TOL[dt]
+    if dt == "f32":
+        k = 32768
+        mo = orc.record(prob, u0n[:k], pn[:k], fused=False)
+        lo, go, _ = orc.replay_grad(prob, u0n[:k], pn[:k], mo, W.COTANGENT,
+                                    aux=np.ones((k, 1, 1), npt), fused=False)
+        spread = float(np.max(np.abs(go[:, 0].astype(np.float64) * u0n[:k, 0] / lo - 1)))
+        gate = 4 * spread
+        _print(f"  the oracle's own deviation {spread:.2e}: gate {gate:.2e}")
+    assert dev <= gate
     assert bool(torch.all(gp[0] > 0))  # a larger rate (slower decay) raises y_N
 
 
