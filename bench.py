@@ -6,8 +6,11 @@ final states; one record then 10 replay-gradient passes against it.  Inputs
 are synthetic (seeded, see workloads/) and resident on the GPU before the
 timed region.  --workload selects one of the other ensembles.
 
-One timed step is that whole job: record, lane ordering with the replay
-table, and the gradient passes.
+One timed step is that whole job: record, lane ordering (the replay order by
+decreasing step count), and the gradient passes, which read the tiled step log
+through the replay order.  --replay-table also builds the replay table in the
+job (one contiguous row of step sizes per replay step) for the passes to read
+instead; at 10 passes it no longer pays for itself.
 value = trajectories * passes / step time (trajectory-gradients/s).
 
 Printed on one JSON line, besides the standard fields (metric, value, unit, steps, config):
@@ -321,9 +324,9 @@ OTHER_WORKLOADS = ((1, None), (3, None), (4, None), (4, "rodas3"), (4, "ros4"), 
                    (6, None), (2, "rkf78"))
 
 
-def other_workloads(da, W, torch, np, steps: int = 2, warmup: int = 1) -> list:
-    """One job each (record, lane ordering with the replay table, one
-    gradient pass) of the other workloads at their full sizes, `warmup` + `steps`
+def other_workloads(da, W, torch, np, steps: int = 2, warmup: int = 1, table: bool = False) -> list:
+    """One job each (record, lane ordering, one gradient pass; the replay
+    table too with `table`) of the other workloads at their full sizes, `warmup` + `steps`
     times: job time and gradient-pass time from HIP events on the launch
     stream, and the pass's algorithmic rate against its dtype's vector peak."""
     dev = torch.device("cuda:0")
@@ -351,9 +354,9 @@ def other_workloads(da, W, torch, np, steps: int = 2, warmup: int = 1) -> list:
             e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
             e[0].record(stream)
             da.record(prob, u0, p, mesh=mesh, save=False)
-            sm = da.mesh_sort(prob, mesh, perm=mesh.perm)
-            call = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=aux, scale=scale,
-                                 max_n_steps=sm.h_rows.shape[0])
+            N = da.mesh_max_steps(mesh)   # sizes the gradient workspace (host sync)
+            sm = da.mesh_sort(prob, mesh, perm=mesh.perm, table=table)
+            call = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=aux, scale=scale, max_n_steps=N)
             e[1].record(stream)
             call()
             e[2].record(stream)
@@ -402,10 +405,16 @@ def main():
     ap.add_argument("--dense", action="store_true",
                     help="read the save times from the step interpolant (dense output) "
                          "instead of landing steps on them")
+    ap.add_argument("--replay-table", action="store_true",
+                    help="build the replay table in each job and let the gradient passes read "
+                         "it instead of the tiled log (always on with --rhs-source)")
     ap.add_argument("--no-others", action="store_true",
                     help="skip the other workloads that the default run times after the "
                          "headline")
     args = ap.parse_args()
+    # right-hand sides compiled at run time keep the guarded replay, which reads
+    # one step size at a time: for them the table is faster at any pass count
+    args.replay_table = args.replay_table or args.rhs_source
     if args.gpus != 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU mode (trajectories "
               "are independent, so shards of the ensemble would run on separate GPUs).",
@@ -468,10 +477,11 @@ def main():
         if e: e["rec0"].record(stream)
         da.record(prob, u0, p, mesh=mesh, save=False)
         if e: e["rec1"].record(stream)
-        N = da.mesh_max_steps(mesh)           # sizes the table and workspace (host sync)
-        if N != state["N"]:
+        N = da.mesh_max_steps(mesh)           # sizes the workspace (and the table) (host sync)
+        if args.replay_table and N != state["N"]:
             state["rows"] = torch.empty((max(N, 1), n), dtype=dt, device=dev)
-        sm = da.mesh_sort(prob, mesh, perm=mesh.perm, h_rows=state["rows"], workspace=sort_ws)
+        sm = da.mesh_sort(prob, mesh, perm=mesh.perm, table=args.replay_table,
+                          h_rows=state["rows"], workspace=sort_ws)
         if e: e["sort1"].record(stream)
         if N != state["N"]:
             state["call"] = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=aux, scale=scale,
@@ -505,6 +515,10 @@ def main():
     pass_med = float(np.median(pass_all))
     pass_total = float(np.mean([sum(e["p0"][k].elapsed_time(e["p1"][k]) for k in range(passes))
                                 for e in evs]))
+    # the forward legs below read a replay table (built here, outside the
+    # timed job, when the job has none)
+    leg_mesh = state["call"].mesh if args.replay_table else \
+        da.mesh_sort(prob, mesh, perm=mesh.perm)
     # forward-mode gradient of the same loss on the same replay order and
     # table: all d + P directions, and the P parameter directions alone
     def timed(fn):
@@ -518,14 +532,14 @@ def main():
             if r > 0:
                 out.append(a0.elapsed_time(a1))
         return out
-    sens_ms = timed(lambda: da.replay_sens(prob, u0, p, state["call"].mesh, w.loss, aux=aux,
+    sens_ms = timed(lambda: da.replay_sens(prob, u0, p, leg_mesh, w.loss, aux=aux,
                                            scale=scale, with_sens=False))
-    sens_p_ms = timed(lambda: da.replay_sens_dirs(prob, u0, p, state["call"].mesh, prob.dim,
+    sens_p_ms = timed(lambda: da.replay_sens_dirs(prob, u0, p, leg_mesh, prob.dim,
                                                   prob.n_params, w.loss, aux=aux, scale=scale,
                                                   with_sens=False))
     # the fused fixed-step replay alone (da_replay_fwd: saved states, no
     # gradient) on the same replay order and table
-    fwd_ms = timed(lambda: da.replay_fwd(prob, u0, p, state["call"].mesh))
+    fwd_ms = timed(lambda: da.replay_fwd(prob, u0, p, leg_mesh))
     # forward-only adaptive solve of the same ensemble (outside the job)
     solve_ms = []
     for r in range(3):
@@ -567,8 +581,9 @@ def main():
                    "saves": "dense output" if args.dense else "steps land on save times",
                    "rhs_source": "compiled at run time from source, vector-Jacobian products by "
                                  "forward-mode tangents" if args.rhs_source else "built in",
-                   "step": f"record + lane ordering and replay table + {passes} gradient "
-                           f"pass{'es' if passes > 1 else ''}"},
+                   "replay_table": bool(args.replay_table),
+                   "step": f"record + lane ordering{' and replay table' if args.replay_table else ''}"
+                           f" + {passes} gradient pass{'es' if passes > 1 else ''}"},
         "roofline": {"bound": "alu", "achieved": achieved, "peak": peak,
                      "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic, "kernel": "k_replay_grad",
@@ -584,7 +599,7 @@ def main():
         "per_pass": {"ms": pass_ms, "median_ms": pass_med,
                      f"total_ms_{passes}_passes": pass_total,
                      "trajectory_gradients_per_s": n / (pass_ms * 1e-3)},
-        "record_ms": rec_ms, "sort_and_table_ms": sort_ms,
+        "record_ms": rec_ms, "ordering_ms": sort_ms,
         "record_log": {"bytes": log_bytes, "GB_per_s": log_bytes / (rec_ms * 1e-3) / 1e9,
                        "what": "zero-padded step log written by the record kernel "
                                "(step sizes, step counts, save indices, status)"},
@@ -617,7 +632,7 @@ def main():
     default_run = (args.workload == 2 and args.method is None and not args.rhs_source
                    and not args.dense and not args.checkpoint)
     if default_run and not args.no_others:
-        out["other_workloads"] = other_workloads(da, W, torch, np)
+        out["other_workloads"] = other_workloads(da, W, torch, np, table=args.replay_table)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(args.workload, args.cpu_lanes, passes,
                                            dense=int(args.dense), method=w.method)

@@ -509,6 +509,28 @@ template <class T, bool ROWS> struct StepSrc {
     if constexpr (ROWS) return base[(int64_t)k * n];
     else return base[Log<T>::at(k, n)];
   }
+  // Steps k .. k + V - 1 (k a multiple of V): from the tiled log, V
+  // consecutive elements of one chunk read by 16-byte loads; from the table,
+  // V row loads.  A start past the source reads its last V steps.
+  template <int V> __device__ __forceinline__ void loadv(int k, T (&out)[V]) const {
+    constexpr int PER = 16 / (int)sizeof(T);  // elements per 16-byte piece
+    if constexpr (ROWS || V % PER != 0) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) out[v] = load(k + v);
+    } else {
+      k = k < cap - V ? k : cap - V;
+      k = k < 0 ? 0 : k;
+      typedef T Piece __attribute__((ext_vector_type(PER)));
+      typedef __attribute__((address_space(1))) const Piece GP;
+      GP *q = (GP *)(base + Log<T>::at(k, n));
+#pragma unroll
+      for (int r = 0; r < V / PER; ++r) {
+        const Piece x = q[r];
+#pragma unroll
+        for (int e = 0; e < PER; ++e) out[r * PER + e] = x[e];
+      }
+    }
+  }
 };
 
 // Lane j of a replay: its trajectory, step count and whether it replays.
@@ -617,12 +639,10 @@ __global__ __launch_bounds__(BLOCK) void k_replay_fwd(ReplayArgs a) {
     constexpr int U = 8;
     const int Nmin = wave_min(N);
     T hc[U];
-#pragma unroll
-    for (int b = 0; b < U; ++b) hc[b] = src.load(b);
+    src.template loadv<U>(0, hc);
     for (; k0 + U <= Nmin; k0 += U) {
       T hn[U], ys[U + 1][D];
-#pragma unroll
-      for (int b = 0; b < U; ++b) hn[b] = src.load(k0 + U + b);
+      src.template loadv<U>(k0 + U, hn);
 #pragma unroll
       for (int c = 0; c < D; ++c) ys[0][c] = y[c];
       bool need = false;
@@ -910,12 +930,10 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
   int k0 = 0;
   if constexpr (FAST) if (fast) {
     T hc[U];
-#pragma unroll
-    for (int b = 0; b < U; ++b) hc[b] = src.load(b);
+    src.template loadv<U>(0, hc);
     for (; k0 + U <= Nmin; k0 += U) {
       T hn[U], ys[U + 1][D];
-#pragma unroll
-      for (int b = 0; b < U; ++b) hn[b] = src.load(k0 + U + b);
+      src.template loadv<U>(k0 + U, hn);
 #pragma unroll
       for (int c = 0; c < D; ++c) ys[0][c] = y[c];
       bool need = false;
@@ -1007,6 +1025,12 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
 #pragma unroll
     for (int b = 0; b < CK; ++b) sg.h[b] = src.load(m * CK + b);
   };
+  auto fetchv = [&](int m, Seg<T, D, CK> &sg) {
+    m = m < 0 ? 0 : m;
+#pragma unroll
+    for (int c = 0; c < D; ++c) sg.cp[c] = ws[((int64_t)m * D + c) * C];
+    src.template loadv<CK>(m * CK, sg.h);
+  };
   auto rseg = [&](int m, const Seg<T, D, CK> &sg) {
     T ys[CK][D];
 #pragma unroll
@@ -1094,10 +1118,10 @@ __global__ __launch_bounds__(BLOCK) DADJ_GRAD_OCCUPANCY void k_replay_grad(Repla
         for (int q = 0; q < P; ++q) g0[q] = g[q];
       }
       bool need = false;
-      fetch(m - 1, B);
+      fetchv(m - 1, B);
       rseg_nx(A, need);
       if constexpr (SP == 2) {
-        fetch(m - 2, A);
+        fetchv(m - 2, A);
         rseg_nx(B, need);
       }
       if constexpr (PX) {
