@@ -209,10 +209,13 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
     mesh, _ = da.record(prob, u0, p)
     h_before = mesh.h.clone()
     sm = da.mesh_sort(prob, mesh)
+    so = da.mesh_sort(prob, mesh, table=False)     # the replay order alone
     r1 = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale)
     r2 = da.replay_grad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)
+    r4 = da.replay_grad(prob, u0, p, so, w.loss, aux=auxd, scale=scale)
     y1 = da.replay_fwd(prob, u0, p, mesh)
     y2 = da.replay_fwd(prob, u0, p, sm)
+    y4 = da.replay_fwd(prob, u0, p, so)
     # a reversed order as well (longest trajectories last)
     rev = da.Mesh(mesh.h, mesh.n_steps, mesh.save_idx, mesh.status, sm.perm.flip(0).contiguous())
     r3 = da.replay_grad(prob, u0, p, rev, w.loss, aux=auxd, scale=scale)
@@ -227,9 +230,10 @@ def test_sorted_mesh_gives_identical_gradients(da, orc, wid, n):
     for v in np.unique(ns_sorted):
         sel = perm[ns_sorted == v]
         assert np.all(np.diff(sel) > 0)
-    for a, b, c in zip(r1, r2, r3):
-        assert torch.equal(a, b) and torch.equal(a, c)
-    assert torch.equal(y1, y2)
+    assert so.h_rows is None and torch.equal(so.perm, sm.perm)
+    for a, b, c, d in zip(r1, r2, r3, r4):
+        assert torch.equal(a, b) and torch.equal(a, c) and torch.equal(a, d)
+    assert torch.equal(y1, y2) and torch.equal(y1, y4)
     # the replay table holds the record's steps in replay order, zero padded
     rows = sm.h_rows.shape[0]
     assert rows == ns.max()
@@ -719,10 +723,11 @@ def test_saved_mesh_replays_bitwise(da, orc, wid, n, tmp_path):
 @pytest.mark.parametrize("wid", [3, 4, 5])
 def test_full_size_workloads_sampled(da, orc, wid):
     """Workloads 3, 4 and 5 at their full sizes in the benchmark's launch
-    configuration (record, lane ordering with the replay table, one gradient
-    pass); sampled trajectories are checked against the oracle on the GPU's own
-    mesh (gradients) and against the oracle's record (step counts, error
-    norms)."""
+    configuration (record, lane ordering, one gradient pass reading the step
+    log through the replay order); sampled trajectories are checked against
+    the oracle on the GPU's own mesh (gradients) and against the oracle's
+    record (step counts, error norms).  The same pass through the replay
+    table gives the same gradients bit for bit."""
     w = W.WORKLOADS[wid]
     prob = w.problem()
     inp = W.make_inputs(wid)
@@ -737,9 +742,13 @@ def test_full_size_workloads_sampled(da, orc, wid):
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     auxd = None if aux is None else aux_to_dev(aux, torch)
     mesh, _ = da.record(prob, u0, p, save=False)
-    sm = da.mesh_sort(prob, mesh)
+    sm = da.mesh_sort(prob, mesh, table=False)
     loss, gu0, gp = da.ReplayGrad(prob, u0, p, sm, w.loss, aux=auxd, scale=scale)()
+    tm = da.mesh_sort(prob, mesh, perm=sm.perm)
+    rt = da.ReplayGrad(prob, u0, p, tm, w.loss, aux=auxd, scale=scale)()
     torch.cuda.synchronize()
+    for a, b in zip((loss, gu0, gp), rt):
+        assert torch.equal(a, b)
     st = sm.status.cpu().numpy()
     assert np.all(st == 0)
     perm = sm.perm.cpu().numpy()
@@ -819,8 +828,10 @@ def test_degenerate_trajectories(da, orc):
 
 def test_full_size_lorenz_dopri5_sampled(da, orc):
     """Workload 2 at its full size (2^20 lanes), in the launch configuration of
-    the benchmark (record, lane ordering, replay gradient); a sample of lanes
-    is checked against the oracle on the GPU's own mesh and record."""
+    the benchmark (record, lane ordering, replay gradient reading the step log
+    through the replay order); a sample of lanes is checked against the oracle
+    on the GPU's own mesh and record.  The same pass through the replay table
+    gives the same gradients bit for bit."""
     w = W.WORKLOADS[2]
     prob = w.problem()
     inp = W.make_inputs(2)
@@ -828,10 +839,14 @@ def test_full_size_lorenz_dopri5_sampled(da, orc):
     _print(f"case: full size workload 2, n={n}")
     u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
     mesh, _ = da.record(prob, u0, p, save=False)
-    sm = da.mesh_sort(prob, mesh)
+    sm = da.mesh_sort(prob, mesh, table=False)
     call = da.ReplayGrad(prob, u0, p, sm)
     loss, gu0, gp = call()
+    rt = da.ReplayGrad(prob, u0, p, da.mesh_sort(prob, mesh, perm=sm.perm))()
     torch.cuda.synchronize()
+    for a, b in zip((loss, gu0, gp), rt):
+        assert torch.equal(a, b)
+    del rt
     st = sm.status.cpu().numpy()
     assert np.all(st == 0)
     perm = sm.perm.cpu().numpy()

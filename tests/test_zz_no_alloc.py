@@ -1,7 +1,8 @@
 """da_replay_grad_noalloc, the replay gradient with the library's static
 device scratch as its workspace (for callers that cannot allocate), against
-da_replay_grad with a caller workspace: the same outputs bit for bit, on two
-calls in a row with the second on a smaller ensemble, with the scratch
+da_replay_grad with a caller workspace: the same outputs bit for bit, on
+calls in a row with the later ones on a smaller ensemble (a replay order with
+the replay table, none, and the replay order alone), with the scratch
 holding the whole ensemble or only part of it (consecutive chunks), on the
 lane kernels and the wavefront kernels; sizes beyond the scratch are
 rejected before any launch."""
@@ -50,7 +51,7 @@ CASES = [(2, 4000, 700), (3, 2500, 900), (4, 600, 300), (5, 1500, 200)]
 
 @pytest.mark.parametrize("wid,n1,n2", CASES)
 def test_noalloc_equals_replay_grad(da, orc, wid, n1, n2):
-    for n, sort in ((n1, True), (n2, False)):
+    for n, sort in ((n1, "table"), (n2, "none"), (n2, "order")):
         w, inp, aux, scale = _inputs(orc, wid, n)
         prob = w.problem()
         dt = torch.float64 if w.dtype == "f64" else torch.float32
@@ -58,8 +59,8 @@ def test_noalloc_equals_replay_grad(da, orc, wid, n1, n2):
         u0, p = to_dev(inp["u0"], torch), to_dev(inp["p"], torch)
         auxd = None if aux is None else aux_to_dev(aux, torch)
         mesh, _ = da.record(prob, u0, p, save=False)
-        if sort:
-            mesh = da.mesh_sort(prob, mesh)
+        if sort != "none":
+            mesh = da.mesh_sort(prob, mesh, table=sort == "table")
         N = da.mesh_max_steps(mesh)
         ref = da.replay_grad(prob, u0, p, mesh, w.loss, aux=auxd, scale=scale, max_n_steps=N)
         ref = [t.clone() for t in ref]
