@@ -314,6 +314,60 @@ def test_checkpoint_intervals_give_identical_gradients(da, orc, wid, n):
             assert torch.equal(a, b), ck
 
 
+@pytest.mark.parametrize("wid,dt", [(2, "f64"), (2, "f32"), (4, "f64")])
+def test_mesh_filled_to_capacity(da, orc, wid, dt):
+    """A synthetic mesh of 1000 trajectories (a ragged last wavefront) taking
+    1 to exactly max_steps = 64 steps, 300 of them at the cap, so that the
+    first wavefronts of the replay order fill the log to its last chunk.  The
+    replay gradient through no order, through the replay order alone (step
+    sizes read from the tiled log, by vector loads in the branch-free units)
+    and through the replay table, at checkpoint intervals 1, 2, 4 and the
+    library's choice, is the same bit for bit, and equals the oracle's on the
+    same mesh within the gradient tolerance; the replayed states too."""
+    w = W.WORKLOADS[wid]
+    cap, n = 64, 1000
+    ndt = np.float64 if dt == "f64" else np.float32
+    span = 0.2 if w.rhs == W.LORENZ63 else 1e-3     # states stay bounded (Robertson: physical)
+    prob = w.problem(max_steps=cap, t1=span)
+    _print(f"case: mesh filled to capacity, workload {wid}, {dt}, n={n}")
+    rng = np.random.default_rng(64 + wid)
+    ns = rng.integers(1, cap + 1, n).astype(np.int32)
+    ns[rng.choice(n, 300, replace=False)] = cap
+    h = np.zeros((n, cap), dtype=ndt)
+    for i in range(n):
+        h[i, :ns[i]] = (span / ns[i]) * (0.8 + 0.4 * rng.random(ns[i]))
+    m = {"h": h, "n_steps": ns, "save_idx": ns[:, None].copy(),
+         "status": np.zeros(n, dtype=np.int32)}
+    inp = W.make_inputs(wid, n)
+    u0h, ph = inp["u0"].astype(ndt), inp["p"].astype(ndt)
+    lo, go, po = orc.replay_grad(prob, u0h, ph, m, w.loss, fused=True)
+    yo, _ = orc.replay(prob, u0h, ph, m, fused=True)
+    mesh = mesh_to_dev(m, cap, torch)
+    u0, p = to_dev(u0h, torch), to_dev(ph, torch)
+    so = da.mesh_sort(prob, mesh, table=False)
+    st = da.mesh_sort(prob, mesh)
+    assert int(st.h_rows.shape[0]) == cap
+    ref = None
+    for ck in (1, 2, 4, 0):
+        pc = prob.replace(checkpoint=ck)
+        for mm in (mesh, so, st):
+            out = [x.clone() for x in da.replay_grad(pc, u0, p, mm, w.loss)]
+            torch.cuda.synchronize()
+            if ref is None:
+                ref = out
+            for a, b in zip(ref, out):
+                assert torch.equal(a, b), ck
+    err = grad_elem_err(ref[1].cpu().numpy().T, ref[2].cpu().numpy().T, go, po)
+    _print(f"  element-wise max rel err against the oracle {err.max():.3e}")
+    assert err.max() <= TOL[dt]
+    f = [da.replay_fwd(prob, u0, p, mm) for mm in (mesh, so, st)]
+    torch.cuda.synchronize()
+    assert torch.equal(f[0], f[1]) and torch.equal(f[0], f[2])
+    yg = f[0].cpu().numpy().transpose(2, 0, 1)
+    assert np.all(np.isfinite(yg))
+    assert elem_err(yg.reshape(n, -1), yo.reshape(n, -1)).max() <= TOL[dt]
+
+
 def test_ros2_gradient_with_row_exchanges(da, orc):
     """ROS2 on Lorenz-63 over a hand-made mesh: the first four steps coarse
     (0.02..0.2 per trajectory, so that the LU of W = I - gamma h J exchanges
