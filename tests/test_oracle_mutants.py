@@ -6,8 +6,10 @@ mistyped tableau digit, a missing contraction, a wrong seed).  It is built on
 the CPU into a temporary library and the pin battery of
 ``test_oracle_pins`` is run against it; at least one pin must fail.
 """
+import concurrent.futures
 import os
 import subprocess
+import tempfile
 
 import numpy as np
 import pytest
@@ -148,19 +150,48 @@ def _killed(orc):
     return None
 
 
-@pytest.mark.parametrize("name", sorted(MUTANTS))
-def test_pins_catch_planted_mistake(orc, tmp_path, name):
+def _build_mutant(name: str, d: str) -> str:
     old, new = MUTANTS[name]
     src = open(SRC).read()
     assert src.count(old) == 1, f"mutation site of {name} not unique/found"
-    mutated = tmp_path / "oracle_mutant.cpp"
-    mutated.write_text(src.replace(old, new))
-    lib = tmp_path / "liboracle_mutant.so"
+    mutated = os.path.join(d, f"oracle_{name}.cpp")
+    with open(mutated, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(d, f"liboracle_{name}.so")
     subprocess.run(["g++", "-O1", "-std=c++17", "-ffp-contract=off", "-fopenmp", "-fPIC",
-                    "-shared", "-w", "-I", os.path.dirname(SRC), "-o", str(lib), str(mutated)],
+                    "-shared", "-w", "-I", os.path.dirname(SRC), "-o", lib, mutated],
                    check=True)
+    return lib
+
+
+_BUILT = {}
+
+
+def _mutant_lib(name: str, d: str) -> str:
+    """The mutant's library.  In a single test process every mutant is built
+    at the first request, several compilers at a time; under pytest-xdist
+    each worker builds only the mutants it runs."""
+    if os.environ.get("PYTEST_XDIST_WORKER"):
+        return _build_mutant(name, d)
+    if not _BUILT:
+        with concurrent.futures.ThreadPoolExecutor(min(8, os.cpu_count() or 1)) as ex:
+            names = sorted(MUTANTS)
+            for n, lib in zip(names, ex.map(lambda m: _build_mutant(m, d), names)):
+                _BUILT[n] = lib
+    return _BUILT[name]
+
+
+@pytest.fixture(scope="module")
+def mutant_dir():
+    with tempfile.TemporaryDirectory(prefix="oracle_mutants_") as d:
+        yield d
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(orc, mutant_dir, name):
+    lib = _mutant_lib(name, mutant_dir)
     try:
-        orc._swap_library(str(lib))
+        orc._swap_library(lib)
         killer = _killed(orc)
     finally:
         orc._swap_library(None)
