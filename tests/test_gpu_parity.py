@@ -697,6 +697,10 @@ def test_failed_lanes_and_edge_sizes(da, orc):
     m0, _ = da.record(w.problem(), e, e)
     r0 = da.replay_grad(w.problem(), e, e, m0, max_n_steps=0)
     assert r0[0].numel() == 0
+    s0 = da.mesh_sort(w.problem(), m0, table=False)
+    r0 = da.replay_grad(w.problem(), e, e, s0, max_n_steps=0)
+    torch.cuda.synchronize()
+    assert s0.perm.numel() == 0 and r0[0].numel() == 0
 
 
 def test_solve_fwd_matches_record(da, orc):
