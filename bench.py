@@ -34,8 +34,11 @@ Printed on one JSON line, besides the standard fields (metric, value, unit, step
   record_log    bytes of the zero-padded step log the record writes, and the
                 rate over the record time;
   replay_fwd    the fused fixed-step replay alone (saved states, no
-                gradient) on the job's replay order and table, with its
+                gradient) on the job's replay order and a replay table (built
+                outside the timed job when the job has none), with its
                 algorithmic FLOP rate (the forward part of flop_per_step);
+  ordering_ms   the lane ordering inside the job (and the replay table when
+                the job builds one);
   cpu_baseline  the CPU oracle (plain C++, OpenMP) on a bounded sample of the
                 same workload, as trajectory-gradients/s of the same job;
   record_stats  accepted and rejected trial steps per trajectory and the
