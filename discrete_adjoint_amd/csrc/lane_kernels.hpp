@@ -211,10 +211,10 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // full; after the last step the partial chunk follows.  The zero chunks past
 // a lane's last step (unless the caller defers them to da_mesh_pad) are
 // written from the end of the log downwards while the lane integrates: one
-// chunk row every PadEvery<M> attempts, as long as the row lies at or past the
-// chunk the next accepted step would go to (attempts >= accepted steps, so
-// the rule needs only the attempt count, which all lanes still in the loop
-// share).  While every lane of the wavefront is still in the loop the row
+// chunk row every PadEvery<M> attempts, as long as the row index is at least
+// DADJ_PAD_AHEAD times that of the chunk the next attempt would go to
+// (attempts >= accepted steps, so the rule needs only the attempt count,
+// which all lanes still in the loop share).  While every lane of the wavefront is still in the loop the row
 // is the same for all of them, and the wavefront writes its row
 // segment with each store covering 1 KB contiguously; once a lane has left,
 // each lane writes its own chunk.  A lane that takes more steps than that
@@ -229,6 +229,17 @@ __device__ T initial_step(const T (&y0)[Rhs::D], const T (&f0)[Rhs::D], const T 
 // Rodas3 on Robertson 1.71 against 1.80 ms.
 #ifndef DADJ_PAD_EVERY
 #define DADJ_PAD_EVERY 1
+#endif
+// A zero row is written during the integration only while it lies at least
+// DADJ_PAD_AHEAD times the lane's current chunk row up: a row closer than
+// that may still receive the lane's own steps, and zeroing it first writes
+// it twice (with a factor of one the headline record wrote 37.7 GB for its
+// 34.4 GB log).  Rows left over are zeroed after the loop.  Factor 4: the
+// FP32 Tsit5 record (65536 trajectories) 0.278 -> 0.258 ms, the headline
+// record 10.45 -> 10.28 ms; Rodas3 on Robertson and the kinetics system
+// unchanged (factors 2 and 3 in between).
+#ifndef DADJ_PAD_AHEAD
+#define DADJ_PAD_AHEAD 4
 #endif
 
 template <class...> struct VoidT { typedef void type; };
@@ -360,7 +371,7 @@ __global__ __launch_bounds__(BLOCK) void k_record(RecordArgs a, SaveTimes stimes
         if (natt >= pr.max_attempts) { st = LANE_MAX_ATTEMPTS; break; }
         if (!(hs > T(0)) || t + double(hs) == t) { st = LANE_DT_UNDERFLOW; break; }
         ++natt;
-        if (pad && natt % (PE > 0 ? PE : 1) == 0 && zl - 1 >= natt / B) {
+        if (pad && natt % (PE > 0 ? PE : 1) == 0 && zl - 1 >= (DADJ_PAD_AHEAD * natt) / B) {
           --zl;
           if (__ballot(1) == ~0ull) {
             const int lane = (int)(threadIdx.x & 63u);
